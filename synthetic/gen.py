@@ -1,0 +1,97 @@
+"""Seeded input generators (input bytes only; no quantization arithmetic)."""
+
+import numpy as np
+import torch
+
+# Qwen3-8B linear layers as (name, N = out features, K = in features).
+# qkv: 4096 -> 6144 (32 query heads + 2 x 8 kv heads of 128), o: 4096 -> 4096,
+# gate_up: 4096 -> 2 x 12288, down: 12288 -> 4096.
+LAYER_SHAPES_QWEN3_8B = (
+    ("qkv", 6144, 4096),
+    ("o", 4096, 4096),
+    ("gate_up", 24576, 4096),
+    ("down", 4096, 12288),
+)
+
+# Qwen3-30B-A3B MoE layer: 128 experts, top-8, hidden 2048, expert FFN 768.
+MOE_QWEN3_30B_A3B = {
+    "experts": 128,
+    "top_k": 8,
+    "hidden": 2048,
+    "ffn": 768,
+    "tokens": 4096,
+    "gate_up": (1536, 2048),  # N, K per expert
+    "down": (2048, 768),
+}
+
+
+def f32_to_bf16_bits(x):
+    """float32 numpy array -> uint16 BF16 bits (torch CPU cast, nearest-even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_normal(shape, std, seed):
+    """BF16 bits of std * N(0, 1), seeded by a tuple of ints."""
+    rng = np.random.default_rng(list(seed))
+    z = rng.standard_normal(shape, dtype=np.float32)
+    return f32_to_bf16_bits(z * np.float32(std))
+
+
+def activations(m, k, seed, n_outliers=0, outlier_mult=1.0):
+    """BF16 bits of N(0,1) activations [m][k] with ``n_outliers`` K columns x mult.
+
+    Returns ``(bits, outlier_columns)``.  The chosen columns are multiplied in
+    float32 before the single rounding to BF16.
+    """
+    rng = np.random.default_rng(list(seed))
+    z = rng.standard_normal((m, k), dtype=np.float32)
+    cols = np.sort(rng.choice(k, size=n_outliers, replace=False)) if n_outliers else np.zeros(0, np.int64)
+    if n_outliers:
+        z[:, cols] *= np.float32(outlier_mult)
+    return f32_to_bf16_bits(z), cols
+
+
+def moe_routing(tokens, experts, top_k, seed):
+    """Top-k routing from softmax(N(0,1) logits); returns (token_ids, expert_ids, offsets).
+
+    ``token_ids`` / ``expert_ids`` list the (token, expert) pairs sorted by
+    expert then token; ``offsets`` [experts+1] (int32) delimit each expert's
+    rows in that order.
+    """
+    rng = np.random.default_rng(list(seed))
+    logits = rng.standard_normal((tokens, experts), dtype=np.float32)
+    z = logits - logits.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p = p / p.sum(axis=1, keepdims=True)
+    order = np.argsort(-p, axis=1, kind="stable")[:, :top_k]  # ties -> lower index
+    tok = np.repeat(np.arange(tokens), top_k)
+    exp = order.reshape(-1)
+    perm = np.lexsort((tok, exp))  # sort by expert, then token
+    tok, exp = tok[perm], exp[perm]
+    counts = np.bincount(exp, minlength=experts)
+    offsets = np.zeros(experts + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    return tok.astype(np.int64), exp.astype(np.int64), offsets
+
+
+def gather_rows(bits, token_ids):
+    """Rows of a [tokens][K] BF16 tensor in routed order (a pure copy)."""
+    return np.ascontiguousarray(np.asarray(bits)[np.asarray(token_ids)])
+
+
+def device_bf16_normal(shape, std, seed, device="cuda", chunk_rows=4096):
+    """BF16 tensor of std * N(0,1) drawn on ``device`` with torch's seeded generator.
+
+    Used for inputs too large to draw on the host (the 36-layer sweep).
+    Rows are drawn in chunks so the float32 temporary stays small.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1, shape[-1])
+    for r0 in range(0, flat.shape[0], chunk_rows):
+        r1 = min(flat.shape[0], r0 + chunk_rows)
+        z = torch.randn((r1 - r0, shape[-1]), generator=g, dtype=torch.float32, device=device)
+        flat[r0:r1] = (z * std).to(torch.bfloat16)
+    return out
