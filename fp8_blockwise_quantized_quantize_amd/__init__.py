@@ -1,0 +1,214 @@
+"""Python binding of libfp8bq.so: blockwise W8A8 FP8 for AMD MI355X (gfx950).
+
+Thin ctypes marshalling only: every function checks tensor dtypes, shapes,
+devices and contiguity, allocates missing outputs with torch, and passes raw
+device pointers plus torch's current HIP stream to the C ABI declared in
+``include/fp8bq.h``.  All arithmetic runs in the library's HIP kernels; there
+is no CPU fallback, and importing this package fails loudly when the built
+library is missing (build it with ``python -m
+fp8_blockwise_quantized_quantize_amd.build``).
+
+The operations follow "FP8-RL: A Practical and Stable Low-Precision Stack for
+LLM Reinforcement Learning" (paper-graph-ui summary page): §3.4.1 (E4M3,
+128x128 weight blocks, 1x128 activation tiles, W^ = round(W / scale)) and
+§3.4.2 (per-step weight re-quantization; FP8 GEMM with FP32 accumulation and
+BF16 output).
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BLOCK",
+    "LIB_PATH",
+    "FP8BQError",
+    "quantize_weight_blockwise",
+    "quantize_act_per_token_group",
+    "gemm_w8a8_blockscaled",
+    "grouped_gemm_w8a8_blockscaled",
+    "encode_e4m3",
+    "status_string",
+]
+
+BLOCK = 128
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8bq.so")
+
+# exported symbols of include/fp8bq.h
+EXPORTS = (
+    "fp8bq_status_string",
+    "quantize_weight_blockwise",
+    "quantize_act_per_token_group",
+    "gemm_w8a8_blockscaled",
+    "grouped_gemm_w8a8_blockscaled",
+    "fp8bq_encode_e4m3",
+)
+
+
+class FP8BQError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m fp8_blockwise_quantized_quantize_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.fp8bq_status_string.argtypes = [i32]
+    lib.fp8bq_status_string.restype = ctypes.c_char_p
+    lib.quantize_weight_blockwise.argtypes = [p, p, p, i64, i64, i64, p]
+    lib.quantize_act_per_token_group.argtypes = [p, p, p, i64, i64, p]
+    lib.gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, p]
+    lib.grouped_gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p]
+    lib.fp8bq_encode_e4m3.argtypes = [p, p, i64, i32, p]
+    for name in EXPORTS[1:]:
+        getattr(lib, name).restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(code):
+    return _lib.fp8bq_status_string(int(code)).decode()
+
+
+def _check(name, code):
+    if code != 0:
+        raise FP8BQError(f"{name}: {status_string(code)} (status {code})")
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _require(t, name, dtype, shape, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _u16(t):
+    """BF16 tensors are passed by their bit patterns."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def quantize_weight_blockwise(w, out=None, scale=None):
+    """BF16 weights [N, K] or [B, N, K] -> (E4M3 codes uint8, same shape; float32 scales [.., N/128, K/128])."""
+    if w.dim() not in (2, 3):
+        raise ValueError("weights must be [N, K] or [B, N, K]")
+    b, n, k = (1, *w.shape) if w.dim() == 2 else tuple(w.shape)
+    _require(w, "w", _BF16, w.shape)
+    sshape = (*w.shape[:-2], _cdiv(n, BLOCK), _cdiv(k, BLOCK))
+    if out is None:
+        out = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if scale is None:
+        scale = torch.empty(sshape, dtype=torch.float32, device=w.device)
+    _require(out, "out", _U8, w.shape, w.device)
+    _require(scale, "scale", torch.float32, sshape, w.device)
+    with torch.cuda.device(w.device):
+        _check("quantize_weight_blockwise",
+               _lib.quantize_weight_blockwise(_ptr(w), _ptr(out), _ptr(scale), b, n, k, _stream(w)))
+    return out, scale
+
+
+def quantize_act_per_token_group(x, out=None, scale=None):
+    """BF16 activations [M, K] -> (E4M3 codes uint8 [M, K]; float32 scales [M, ceil(K/128)])."""
+    if x.dim() != 2:
+        raise ValueError("activations must be [M, K]")
+    m, k = x.shape
+    _require(x, "x", _BF16, x.shape)
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((m, _cdiv(k, BLOCK)), dtype=torch.float32, device=x.device)
+    _require(out, "out", _U8, (m, k), x.device)
+    _require(scale, "scale", torch.float32, (m, _cdiv(k, BLOCK)), x.device)
+    with torch.cuda.device(x.device):
+        _check("quantize_act_per_token_group",
+               _lib.quantize_act_per_token_group(_ptr(x), _ptr(out), _ptr(scale), m, k, _stream(x)))
+    return out, scale
+
+
+def gemm_w8a8_blockscaled(a, a_scale, w, w_scale, out=None):
+    """y[M, N] (bfloat16) = dequant(a) @ dequant(w).T with FP32 accumulation."""
+    m, k = a.shape
+    n = w.shape[0]
+    _require(a, "a", _U8, (m, k))
+    dev = a.device
+    _require(a_scale, "a_scale", torch.float32, (m, k // BLOCK), dev)
+    _require(w, "w", _U8, (n, k), dev)
+    _require(w_scale, "w_scale", torch.float32, (_cdiv(n, BLOCK), k // BLOCK), dev)
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", _BF16, (m, n), dev)
+    with torch.cuda.device(dev):
+        _check("gemm_w8a8_blockscaled",
+               _lib.gemm_w8a8_blockscaled(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)), m, n, k,
+                                          _stream(a)))
+    return out
+
+
+def grouped_gemm_w8a8_blockscaled(a, a_scale, w, w_scale, group_offsets, out=None):
+    """Rows [off[e], off[e+1]) of a use expert e's weights w[e]; returns bfloat16 [M_total, N]."""
+    m, k = a.shape
+    g, n, _ = w.shape
+    _require(a, "a", _U8, (m, k))
+    dev = a.device
+    _require(a_scale, "a_scale", torch.float32, (m, k // BLOCK), dev)
+    _require(w, "w", _U8, (g, n, k), dev)
+    _require(w_scale, "w_scale", torch.float32, (g, _cdiv(n, BLOCK), k // BLOCK), dev)
+    _require(group_offsets, "group_offsets", torch.int32, (g + 1,), dev)
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", _BF16, (m, n), dev)
+    with torch.cuda.device(dev):
+        _check("grouped_gemm_w8a8_blockscaled",
+               _lib.grouped_gemm_w8a8_blockscaled(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale),
+                                                  _ptr(group_offsets), _ptr(_u16(out)), m, n, k, g, _stream(a)))
+    return out
+
+
+def encode_e4m3(v, method=1, out=None):
+    """float32 [n] -> E4M3 codes uint8 [n] with the library's conversion (see fp8bq.h for methods)."""
+    if v.dim() != 1:
+        raise ValueError("encode_e4m3 takes a 1-D tensor")
+    _require(v, "v", torch.float32, v.shape)
+    if out is None:
+        out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _require(out, "out", torch.uint8, v.shape, v.device)
+    with torch.cuda.device(v.device):
+        _check("fp8bq_encode_e4m3", _lib.fp8bq_encode_e4m3(_ptr(v), _ptr(out), v.numel(), int(method), _stream(v)))
+    return out
+
+
+def raw_library():
+    """The ctypes handle, for callers that marshal pointers themselves."""
+    return _lib

@@ -1,0 +1,167 @@
+// C-ABI layer of libfp8bq.so: argument checks, device check, launches.
+// The contract of every entry point is documented in include/fp8bq.h.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/fp8bq.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// per-device cache of the architecture check: 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+fp8bq_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8BQ_ERR_DEVICE;
+  if (dev >= kMaxDevices) return FP8BQ_ERR_DEVICE;
+  int state = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8BQ_ERR_DEVICE;
+    state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? FP8BQ_OK : FP8BQ_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b without int64 overflow (both >= 0)
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a == 0 || b == 0) {
+    *out = 0;
+    return true;
+  }
+  if (a > INT64_MAX / b) return false;
+  *out = a * b;
+  return true;
+}
+
+fp8bq_status launched(hipError_t e) { return e == hipSuccess ? FP8BQ_OK : FP8BQ_ERR_LAUNCH; }
+
+// Clears a stale runtime error so that the post-launch check reports ours.
+void clear_last_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8bq_status_string(fp8bq_status s) {
+  switch (s) {
+    case FP8BQ_OK: return "ok";
+    case FP8BQ_ERR_NULL_PTR: return "null pointer for a non-empty tensor";
+    case FP8BQ_ERR_BAD_SHAPE: return "invalid shape (negative size, K not a multiple of 128, or size overflow)";
+    case FP8BQ_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
+    case FP8BQ_ERR_LAUNCH: return "kernel launch failed";
+    case FP8BQ_ERR_DEVICE: return "current device is not an AMD gfx950 GPU";
+    default: return "unknown status";
+  }
+}
+
+fp8bq_status quantize_weight_blockwise(const uint16_t* w_bf16, uint8_t* w_fp8, float* w_scale, int64_t batch,
+                                       int64_t N, int64_t K, void* stream) {
+  try {
+    if (batch < 0 || N < 0 || K < 0) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t nk, total, bytes;
+    if (!mul_ok(N, K, &nk) || !mul_ok(nk, batch, &total) || !mul_ok(total, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
+    if (total == 0) return FP8BQ_OK;
+    if (!w_bf16 || !w_fp8 || !w_scale) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(w_bf16) || !aligned16(w_fp8) || !aligned16(w_scale)) return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_quant_weight(w_bf16, w_fp8, w_scale, batch, N, K,
+                                               static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status quantize_act_per_token_group(const uint16_t* x_bf16, uint8_t* x_fp8, float* x_scale, int64_t M,
+                                          int64_t K, void* stream) {
+  try {
+    if (M < 0 || K < 0) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t total, bytes;
+    if (!mul_ok(M, K, &total) || !mul_ok(total, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
+    if (total == 0) return FP8BQ_OK;
+    if (!x_bf16 || !x_fp8 || !x_scale) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(x_bf16) || !aligned16(x_fp8) || !aligned16(x_scale)) return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_quant_act(x_bf16, x_fp8, x_scale, M, K, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                   const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                   void* stream) {
+  try {
+    if (M < 0 || N < 0 || K < 0 || (K % 128) != 0) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t mk, nk, mn, bytes;
+    if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, &mn) || !mul_ok(mn, 2, &bytes))
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (mn == 0) return FP8BQ_OK;
+    if (!y_bf16) return FP8BQ_ERR_NULL_PTR;
+    if (K > 0 && (!a_fp8 || !a_scale || !w_fp8 || !w_scale)) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(y_bf16) || (K > 0 && (!aligned16(a_fp8) || !aligned16(a_scale) || !aligned16(w_fp8) ||
+                                         !aligned16(w_scale))))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(
+        fp8bq::launch_gemm(a_fp8, a_scale, w_fp8, w_scale, y_bf16, M, N, K, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                           const float* w_scale, const int32_t* group_offsets, uint16_t* y_bf16,
+                                           int64_t M_total, int64_t N, int64_t K, int64_t G, void* stream) {
+  try {
+    if (M_total < 0 || N < 0 || K < 0 || G < 0 || (K % 128) != 0) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t mk, nk, gnk, mn, bytes;
+    if (!mul_ok(M_total, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(nk, G, &gnk) || !mul_ok(M_total, N, &mn) ||
+        !mul_ok(mn, 2, &bytes))
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (G > 0 && M_total + 128 * G > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+    if (mn == 0) return FP8BQ_OK;
+    if (G == 0) return FP8BQ_ERR_BAD_SHAPE;  // rows to produce but no expert to own them
+    if (!y_bf16 || !group_offsets) return FP8BQ_ERR_NULL_PTR;
+    if (K > 0 && (!a_fp8 || !a_scale || !w_fp8 || !w_scale)) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(y_bf16) || (K > 0 && (!aligned16(a_fp8) || !aligned16(a_scale) || !aligned16(w_fp8) ||
+                                         !aligned16(w_scale))))
+      return FP8BQ_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(group_offsets) & 3u) != 0) return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_grouped_gemm(a_fp8, a_scale, w_fp8, w_scale, group_offsets, y_bf16, M_total, N,
+                                               K, G, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status fp8bq_encode_e4m3(const float* in, uint8_t* out, int64_t n, int method, void* stream) {
+  try {
+    if (n < 0 || method < 0 || method > 2) return FP8BQ_ERR_BAD_SHAPE;
+    if (n == 0) return FP8BQ_OK;
+    if (!in || !out) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(in) || !aligned16(out)) return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_encode(in, out, n, method, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,24 @@
+// Internal launchers: one per kernel family.  Arguments are already
+// validated by the C-ABI layer (api.hip); launchers only size the grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bq {
+
+hipError_t launch_quant_weight(const uint16_t* w, uint8_t* q, float* scale, int64_t batch, int64_t N, int64_t K,
+                               hipStream_t stream);
+
+hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K, hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
+                       int64_t N, int64_t K, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                               const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
+                               hipStream_t stream);
+
+hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int method, hipStream_t stream);
+
+}  // namespace fp8bq

@@ -1,0 +1,248 @@
+// Blockwise (128x128) weight quantizer, per-token 1x128 activation quantizer
+// and the standalone E4M3 encoder, for gfx950.
+//
+// Both quantizers compute, per tile: amax -> s = fl32(amax / 448) ->
+// q = E4M3_RNE(fl32(x / s)) (FP8-RL summary page, §3.4.1 formula for W^ and
+// §3.4.2 Phase 2 step 2; 1x128 activation tiles per §3.4.1 "Static vs.
+// Dynamic Quantization").  They are HBM-bound: each BF16 element is read
+// once (2 B) and its code written once (1 B), the tile stays in registers
+// between the amax pass and the encode pass.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8bq {
+
+namespace {
+
+// 8 BF16 values (one 16-byte load) -> 8 E4M3 codes (one 8-byte store).
+template <bool kFast>
+__device__ __forceinline__ u32x2 quant8(u32x4 v, const Divisor& d) {
+  float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  float q[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) q[j] = kFast ? d.quotient_fast(x[j]) : d.quotient_ieee(x[j]);
+  return u32x2{pack4_e4m3(q[0], q[1], q[2], q[3]), pack4_e4m3(q[4], q[5], q[6], q[7])};
+}
+
+// Codes of an all-zero tile: the sign of each input zero (0x00 / 0x80).
+__device__ __forceinline__ u32x2 zero8(u32x4 v) {
+  uint32_t lo = ((v.x >> 8) & 0x80u) | ((v.x >> 16) & 0x8000u) | ((v.y << 8) & 0x800000u) | (v.y & 0x80000000u);
+  uint32_t hi = ((v.z >> 8) & 0x80u) | ((v.z >> 16) & 0x8000u) | ((v.w << 8) & 0x800000u) | (v.w & 0x80000000u);
+  return u32x2{lo, hi};
+}
+
+__device__ __forceinline__ u32x2 encode8(u32x4 v, float s) {
+  if (s == 0.0f) return zero8(v);
+  Divisor d(s);
+  return d.fast ? quant8<true>(v, d) : quant8<false>(v, d);
+}
+
+// One element, any tile: used on ragged edges only.
+__device__ __forceinline__ uint8_t encode1(uint16_t bits, float s) {
+  if (s == 0.0f) return (uint8_t)((bits >> 8) & 0x80u);
+  float x = __uint_as_float((uint32_t)bits << 16);
+  Divisor d(s);
+  float q = d.fast ? d.quotient_fast(x) : d.quotient_ieee(x);
+  return (uint8_t)(cvt_pk_e4m3<false>(q, 0.0f, 0u) & 0xffu);
+}
+
+__device__ __forceinline__ uint32_t amax8(uint32_t m, u32x4 v) {
+  m = amax_pair(m, v.x);
+  m = amax_pair(m, v.y);
+  m = amax_pair(m, v.z);
+  return amax_pair(m, v.w);
+}
+
+// ---------------------------------------------------------------------------
+// Weight blocks: one 256-thread workgroup per 128x128 block.  Thread t owns
+// the 16-byte column chunk (t % 16) of rows (t / 16) + 16 i, i = 0..7, so a
+// wave reads 4 full 256-byte block rows per load instruction and the whole
+// block (64 BF16 per thread) is held in 32 VGPRs.
+// ---------------------------------------------------------------------------
+constexpr int kQwThreads = 256;
+
+__global__ __launch_bounds__(kQwThreads) void quant_weight_kernel(const uint16_t* __restrict__ w,
+                                                                  uint8_t* __restrict__ q,
+                                                                  float* __restrict__ scale, int64_t N,
+                                                                  int64_t K, int nb, int kb) {
+  __shared__ uint32_t red[kQwThreads / 64];
+  const int64_t blk = blockIdx.x;  // == index into scale[batch][nb][kb]
+  const int bk = (int)(blk % kb);
+  const int64_t rest = blk / kb;
+  const int bn = (int)(rest % nb);
+  const int64_t b = rest / nb;
+  const uint16_t* wm = w + b * N * K;
+  uint8_t* qm = q + b * N * K;
+  const int64_t row0 = (int64_t)bn * kBlock, col0 = (int64_t)bk * kBlock;
+  const int tid = threadIdx.x;
+  const bool full = (row0 + kBlock <= N) && (col0 + kBlock <= K) && ((K & 7) == 0);
+
+  if (full) {
+    const int cc = tid & 15, rr = tid >> 4;
+    const uint16_t* src = wm + (row0 + rr) * K + col0 + cc * 8;
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)16 * i * K));
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = amax8(m, v[i]);
+    m = wave_max_u32(amax_fold(m));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int i = 1; i < kQwThreads / 64; ++i) m = m > red[i] ? m : red[i];
+    const float s = scale_from_amax_bits(m);
+    if (tid == 0) scale[blk] = s;
+    uint8_t* dst = qm + (row0 + rr) * K + col0 + cc * 8;
+    if (s != 0.0f) {
+      Divisor d(s);
+      if (d.fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          __builtin_nontemporal_store(quant8<true>(v[i], d), reinterpret_cast<u32x2*>(dst + (int64_t)16 * i * K));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<u32x2*>(dst + (int64_t)16 * i * K) = quant8<false>(v[i], d);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x2*>(dst + (int64_t)16 * i * K) = zero8(v[i]);
+    }
+    return;
+  }
+
+  // Partial block (ragged N or K) or rows not 16-byte aligned: element-wise.
+  const int rows = (int)((N - row0) < kBlock ? (N - row0) : kBlock);
+  const int cols = (int)((K - col0) < kBlock ? (K - col0) : kBlock);
+  uint32_t m = 0;
+  for (int e = tid; e < kBlock * kBlock; e += kQwThreads) {
+    const int r = e >> 7, c = e & 127;
+    if (r < rows && c < cols) {
+      uint32_t bits = wm[(row0 + r) * K + col0 + c] & 0x7fffu;
+      m = m > bits ? m : bits;
+    }
+  }
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = red[0];
+  for (int i = 1; i < kQwThreads / 64; ++i) m = m > red[i] ? m : red[i];
+  const float s = scale_from_amax_bits(m);
+  if (tid == 0) scale[blk] = s;
+  for (int e = tid; e < kBlock * kBlock; e += kQwThreads) {
+    const int r = e >> 7, c = e & 127;
+    if (r < rows && c < cols) {
+      const int64_t off = (row0 + r) * K + col0 + c;
+      qm[off] = encode1(wm[off], s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Activation groups: a 16-lane quarter wave per (token, group); each lane
+// owns 8 consecutive BF16 (16 bytes).  The group amax is a 4-step xor
+// shuffle inside the quarter wave, so a wave quantizes 4 groups at once and
+// no LDS or barrier is needed.
+// ---------------------------------------------------------------------------
+constexpr int kQaThreads = 256;
+constexpr int kQaGroupsPerBlock = kQaThreads / 16;
+
+__global__ __launch_bounds__(kQaThreads) void quant_act_kernel(const uint16_t* __restrict__ x,
+                                                               uint8_t* __restrict__ q,
+                                                               float* __restrict__ scale, int64_t M, int64_t K,
+                                                               int G) {
+  const int64_t gid = (int64_t)blockIdx.x * kQaGroupsPerBlock + (threadIdx.x >> 4);
+  const int li = threadIdx.x & 15;
+  const bool valid = gid < M * G;
+  const int64_t m = valid ? gid / G : 0;
+  const int g = valid ? (int)(gid % G) : 0;
+  const int64_t col = (int64_t)g * kBlock + li * 8;
+  const bool vec = valid && ((K & 7) == 0) && (col + 8 <= K);
+  const uint16_t* src = x + m * K + col;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (vec) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+  } else if (valid) {
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (col + j < K) ? src[j] : (uint16_t)0;
+    v = u32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+              e[6] | ((uint32_t)e[7] << 16)};
+  }
+  uint32_t a = amax_fold(amax8(0u, v));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(a, off, 16);
+    a = a > o ? a : o;
+  }
+  const float s = scale_from_amax_bits(a);
+  if (valid && li == 0) scale[m * G + g] = s;
+  uint8_t* dst = q + m * K + col;
+  if (vec) {
+    __builtin_nontemporal_store(encode8(v, s), reinterpret_cast<u32x2*>(dst));
+  } else if (valid) {
+    const uint32_t e[8] = {v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16,
+                           v.z & 0xffffu, v.z >> 16, v.w & 0xffffu, v.w >> 16};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (col + j < K) dst[j] = encode1((uint16_t)e[j], s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Standalone encoder: method 0 = the hardware conversion exactly as the
+// quantizers apply it (valid for |v| < 464), 1 = saturating encoder (clamp
+// to +-448, then the hardware conversion), 2 = integer-bit encoder.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
+                                                     int64_t n, int method) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float v = in[i];
+  uint32_t c;
+  if (method == 0) {
+    c = cvt_pk_e4m3<false>(v, 0.0f, 0u) & 0xffu;
+  } else if (method == 1) {
+    c = cvt_pk_e4m3<false>(__builtin_fminf(__builtin_fmaxf(v, -kE4M3Max), kE4M3Max), 0.0f, 0u) & 0xffu;
+  } else {
+    c = encode_e4m3_soft(v);
+  }
+  out[i] = (uint8_t)c;
+}
+
+}  // namespace
+
+hipError_t launch_quant_weight(const uint16_t* w, uint8_t* q, float* scale, int64_t batch, int64_t N, int64_t K,
+                               hipStream_t stream) {
+  const int64_t nb = (N + kBlock - 1) / kBlock, kb = (K + kBlock - 1) / kBlock;
+  const int64_t blocks = batch * nb * kb;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)blocks), dim3(kQwThreads), 0, stream, w, q, scale, N, K,
+                     (int)nb, (int)kb);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K, hipStream_t stream) {
+  const int64_t G = (K + kBlock - 1) / kBlock;
+  const int64_t groups = M * G;
+  if (groups == 0) return hipSuccess;
+  const int64_t blocks = (groups + kQaGroupsPerBlock - 1) / kQaGroupsPerBlock;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q, scale, M, K,
+                     (int)G);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int method, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(encode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, n, method);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bq

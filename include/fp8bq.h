@@ -1,0 +1,157 @@
+/*
+ * fp8bq.h -- C ABI of libfp8bq.so: blockwise W8A8 FP8 quantization and
+ * block-scaled FP8 GEMMs for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the linear-layer hot path of FP8 rollout in LLM
+ * reinforcement learning as described on the page "FP8-RL: A Practical and
+ * Stable Low-Precision Stack for LLM Reinforcement Learning" (paper-graph-ui
+ * summary; cited below as [FP8-RL summary]):
+ *   - §3.4.2 Phase 2 step 2: per RL step, every 128x128 block of each
+ *     quantized BF16 weight matrix gets a scale from its maximum absolute
+ *     value, is divided by that scale and rounded to the nearest E4M3 value;
+ *   - §3.4.1 "Static vs. Dynamic Quantization" and §3.4.2 Phase 3:
+ *     activations are quantized on the fly per token in 1x128 tiles, the
+ *     FP8 x FP8 product is accumulated in FP32 and converted back to BF16;
+ *   - §3.4.1 "Quantization Scope": MoE expert layers (fc1/fc2) use the same
+ *     scheme, which makes the expert GEMMs a ragged grouped GEMM.
+ * The [128, 128] weight / [1, 128] activation granularity is also the one of
+ * the news page "How FP8 Reinforcement Learning Accelerates LLMs Without
+ * Crashing", section "End-to-End Precision Recipes Across Generation and
+ * Training Engines".
+ *
+ * Number formats
+ *   BF16 : uint16_t bit patterns (upper half of an IEEE binary32).
+ *   E4M3 : uint8_t codes, OCP "e4m3fn": 1 sign, 4 exponent bits (bias 7),
+ *          3 mantissa bits, no infinity, 0x7F/0xFF = NaN, max +-448
+ *          ([FP8-RL summary] §3.4.1 "Quantization Format and Granularity").
+ *          Encoding is round-to-nearest-even with saturation at +-448; the
+ *          library never writes 0x7F/0xFF.
+ *   Scales: IEEE float32, one per tile: s = fl32(amax / 448.0f).  A tile
+ *          whose amax is 0 gets s = 0 and codes 0x00 / 0x80 (the sign of
+ *          each input zero).  Quantized value: q = E4M3(fl32(x / s)) with
+ *          the IEEE float32 quotient.  FP32 denormals are never flushed.
+ *
+ * Conventions (all functions)
+ *   - Every tensor pointer is a DEVICE pointer to row-major, contiguous
+ *     memory on the current HIP device, aligned to 16 bytes.  The caller
+ *     allocates and frees every buffer; the library keeps no pointer.
+ *     Outputs must not overlap inputs.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default
+ *     stream).  Calls enqueue work and return without waiting; results are
+ *     ready when the stream reaches that point.
+ *   - Arguments are checked before anything is enqueued.  On error nothing
+ *     is enqueued and a non-zero fp8bq_status is returned.  A zero-sized
+ *     problem is a successful no-op.  No C++ exception crosses the ABI.
+ *   - Inputs must be finite (NaN / Inf input gives unspecified codes).
+ *   - Functions are thread-safe; ordering follows the stream.
+ */
+#ifndef FP8BQ_H
+#define FP8BQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int fp8bq_status;
+
+enum {
+  FP8BQ_OK = 0,
+  FP8BQ_ERR_NULL_PTR = 1,   /* a required pointer is NULL while its size is > 0 */
+  FP8BQ_ERR_BAD_SHAPE = 2,  /* negative size, K % 128 != 0 for a GEMM, size overflow */
+  FP8BQ_ERR_MISALIGNED = 3, /* a tensor pointer is not 16-byte aligned */
+  FP8BQ_ERR_LAUNCH = 4,     /* the HIP runtime rejected a kernel launch */
+  FP8BQ_ERR_DEVICE = 5      /* the current device is not gfx950, or no device */
+};
+
+/* Static, human-readable text for a status code (host function). */
+const char* fp8bq_status_string(fp8bq_status s);
+
+/*
+ * quantize_weight_blockwise -- per-step re-quantization of BF16 weights.
+ * [FP8-RL summary] §3.4.1 formula W^_ij = round(W_ij / scale_ij) with one
+ * scale per 128x128 block chosen so the block maximum maps to 448, applied
+ * per RL step as in §3.4.2 Phase 2 step 2.
+ *
+ *   w_bf16  [batch][N][K]  BF16 input (N = out features, K = in features)
+ *   w_fp8   [batch][N][K]  E4M3 output
+ *   w_scale [batch][ceil(N/128)][ceil(K/128)]  float32 output
+ *   batch, N, K >= 0.  Blocks are aligned at (0, 0); edge blocks of an N or
+ *   K that is not a multiple of 128 are partial (their amax covers the
+ *   in-bounds elements).  The batch dimension quantizes `batch` matrices of
+ *   the same shape in one call (e.g. the same projection of every layer).
+ */
+fp8bq_status quantize_weight_blockwise(const uint16_t* w_bf16, uint8_t* w_fp8, float* w_scale,
+                                       int64_t batch, int64_t N, int64_t K, void* stream);
+
+/*
+ * quantize_act_per_token_group -- dynamic per-token 1x128 quantization of
+ * BF16 activations ([FP8-RL summary] §3.4.1, "1 x 128 tiles for
+ * activations", and §3.4.2 Phase 3, scales computed on the fly).
+ *
+ *   x_bf16  [M][K]  BF16 input (M tokens)
+ *   x_fp8   [M][K]  E4M3 output
+ *   x_scale [M][ceil(K/128)]  float32 output, token-major
+ *   M, K >= 0.  Group g of token m covers columns [128 g, min(K, 128 g + 128)).
+ */
+fp8bq_status quantize_act_per_token_group(const uint16_t* x_bf16, uint8_t* x_fp8, float* x_scale,
+                                          int64_t M, int64_t K, void* stream);
+
+/*
+ * gemm_w8a8_blockscaled -- y = dequant(A) * dequant(W)^T in FP32, stored as
+ * BF16 ([FP8-RL summary] §3.4.2 Phase 3: FP8 matrix multiplication,
+ * accumulated in FP32, converted back to BF16).
+ *
+ *   a_fp8   [M][K]  E4M3 activations      a_scale [M][K/128]          float32
+ *   w_fp8   [N][K]  E4M3 weights          w_scale [ceil(N/128)][K/128] float32
+ *   y_bf16  [M][N]  BF16 output (round to nearest even)
+ *   y[m][n] = sum_k (a_scale[m][k/128] * dec(a[m][k])) * (w_scale[n/128][k/128] * dec(w[n][k]))
+ *   M, N >= 0; K >= 0 and K % 128 == 0.  The summation order is
+ *   unspecified (results agree with the exact value to FP32 accumulation
+ *   error before the BF16 rounding).
+ */
+fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                   const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                   void* stream);
+
+/*
+ * grouped_gemm_w8a8_blockscaled -- the MoE expert form: rows
+ * [group_offsets[e], group_offsets[e+1]) of A are multiplied with expert
+ * e's weights ([FP8-RL summary] §3.4.1 "Quantization Scope", fc1/fc2 of
+ * each expert quantized like the dense linears).
+ *
+ *   a_fp8   [M_total][K], a_scale [M_total][K/128]
+ *   w_fp8   [G][N][K],    w_scale [G][ceil(N/128)][K/128]
+ *   group_offsets  DEVICE int32 [G+1], non-decreasing, [0] = 0, [G] = M_total
+ *   y_bf16  [M_total][N]
+ *   Empty groups are allowed.  G == 0 with M_total * N > 0 is
+ *   FP8BQ_ERR_BAD_SHAPE.  The offsets are read on the device only (no
+ *   host synchronisation); offsets that break the stated contract give
+ *   unspecified output rows but never an out-of-bounds access: every row
+ *   index is clamped to [0, M_total).  M_total + 128 * G must fit in int32.
+ */
+fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                           const float* w_scale, const int32_t* group_offsets, uint16_t* y_bf16,
+                                           int64_t M_total, int64_t N, int64_t K, int64_t G, void* stream);
+
+/*
+ * fp8bq_encode_e4m3 -- the library's float32 -> E4M3 conversion on its own
+ * ([FP8-RL summary] §3.4.1 "Quantization Format and Granularity"; round to
+ * nearest even, sign of zero kept), so that it can be checked over every
+ * float32 input:
+ *   method 0: the hardware conversion exactly as the quantizers apply it to
+ *             their quotients (defined for |v| < 464, the range every
+ *             quantizer quotient lies in);
+ *   method 1: saturating encoder: clamp to +-448, then the hardware
+ *             conversion (any finite v);
+ *   method 2: integer-bit encoder (any finite v).
+ *   in [n] float32, out [n] uint8, n >= 0.  Other methods: FP8BQ_ERR_BAD_SHAPE.
+ */
+fp8bq_status fp8bq_encode_e4m3(const float* in, uint8_t* out, int64_t n, int method, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BQ_H */

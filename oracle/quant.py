@@ -90,6 +90,15 @@ def quant_weight_blockwise(w_bits):
         raise ValueError("weights must be [N][K] or [B][N][K]")
     b, n, k = w.shape
     nb, kb = -(-n // BLOCK), -(-k // BLOCK)
+    if n % BLOCK == 0 and k % BLOCK == 0:
+        # All blocks are full: gather each block's 16384 elements into one row
+        # and hand all blocks to the tile definition at once (same result as
+        # the block loop below, which handles partial edge blocks).
+        x = bf16_bits_to_f32(w).reshape(b, nb, BLOCK, kb, BLOCK).transpose(0, 1, 3, 2, 4)
+        q, s = quantize_tiles(x.reshape(b * nb * kb, BLOCK * BLOCK))
+        codes = q.reshape(b, nb, kb, BLOCK, BLOCK).transpose(0, 1, 3, 2, 4).reshape(b, n, k)
+        scales = s.reshape(b, nb, kb)
+        return (codes[0], scales[0]) if squeeze else (np.ascontiguousarray(codes), scales)
     codes = np.empty(w.shape, np.uint8)
     scales = np.zeros((b, nb, kb), np.float32)
     for l in range(b):

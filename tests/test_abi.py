@@ -1,0 +1,107 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and rejects bad arguments before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from helpers import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fp8bq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|fp8bq_status)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["quantize_weight_blockwise", "quantize_act_per_token_group", "gemm_w8a8_blockscaled",
+              "grouped_gemm_w8a8_blockscaled", "fp8bq_status_string", "fp8bq_encode_e4m3"]:
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    import fp8_blockwise_quantized_quantize_amd as fb
+
+    lib = ctypes.CDLL(fb.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(fb.EXPORTS) == declared_functions()
+
+
+def test_status_strings():
+    import fp8_blockwise_quantized_quantize_amd as fb
+
+    assert fb.status_string(0) == "ok"
+    for code in range(1, 6):
+        assert fb.status_string(code) not in ("ok", "unknown status")
+    assert fb.status_string(99) == "unknown status"
+
+
+def _call(name, *args):
+    import fp8_blockwise_quantized_quantize_amd as fb
+
+    return getattr(fb.raw_library(), name)(*args)
+
+
+P = ctypes.c_void_p
+
+
+def test_argument_errors_are_reported_before_any_launch():
+    good = P(4096)  # never dereferenced: every call below fails its checks first
+    bad_align = P(4097)
+    null = P(0)
+    # negative sizes
+    assert _call("quantize_weight_blockwise", good, good, good, 1, -1, 128, null) == 2
+    assert _call("quantize_act_per_token_group", good, good, good, -5, 128, null) == 2
+    # K not a multiple of 128 for GEMMs
+    assert _call("gemm_w8a8_blockscaled", good, good, good, good, good, 4, 4, 100, null) == 2
+    assert _call("grouped_gemm_w8a8_blockscaled", good, good, good, good, good, good, 4, 4, 100, 2, null) == 2
+    # size overflow
+    assert _call("quantize_weight_blockwise", good, good, good, 1 << 40, 1 << 20, 1 << 20, null) == 2
+    # null pointers with non-empty sizes
+    assert _call("quantize_weight_blockwise", null, good, good, 1, 128, 128, null) == 1
+    assert _call("quantize_act_per_token_group", good, null, good, 1, 128, null) == 1
+    assert _call("gemm_w8a8_blockscaled", good, good, null, good, good, 4, 4, 128, null) == 1
+    assert _call("grouped_gemm_w8a8_blockscaled", good, good, good, good, null, good, 4, 4, 128, 2, null) == 1
+    # misaligned pointers
+    assert _call("quantize_weight_blockwise", bad_align, good, good, 1, 128, 128, null) == 3
+    assert _call("gemm_w8a8_blockscaled", good, good, good, good, bad_align, 4, 4, 128, null) == 3
+    # grouped GEMM with rows but no expert
+    assert _call("grouped_gemm_w8a8_blockscaled", good, good, good, good, good, good, 4, 4, 128, 0, null) == 2
+    # encoder: bad method
+    assert _call("fp8bq_encode_e4m3", good, good, 16, 7, null) == 2
+
+
+def test_zero_sized_problems_are_no_ops():
+    null = P(0)
+    assert _call("quantize_weight_blockwise", null, null, null, 0, 128, 128, null) == 0
+    assert _call("quantize_weight_blockwise", null, null, null, 3, 0, 128, null) == 0
+    assert _call("quantize_act_per_token_group", null, null, null, 0, 4096, null) == 0
+    assert _call("gemm_w8a8_blockscaled", null, null, null, null, null, 0, 64, 128, null) == 0
+    assert _call("grouped_gemm_w8a8_blockscaled", null, null, null, null, null, null, 0, 64, 128, 4, null) == 0
+    assert _call("fp8bq_encode_e4m3", null, null, 0, 0, null) == 0
+
+
+def test_no_device_is_reported():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    good = P(4096)
+    assert _call("quantize_weight_blockwise", good, good, good, 1, 128, 128, P(0)) == 5
+
+
+def test_binding_has_no_cpu_path():
+    """The binding rejects host tensors instead of computing on the CPU."""
+    import torch
+    import fp8_blockwise_quantized_quantize_amd as fb
+
+    w = torch.zeros((128, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        fb.quantize_weight_blockwise(w)

@@ -1,0 +1,223 @@
+"""GPU parity of the block-scaled GEMM and the grouped (MoE) GEMM.
+
+Acceptance per GEMM (and per expert): relative Frobenius error and worst
+element error (against max(|y_ref|, rms(y_ref))) both <= 1e-2 versus the
+float64 oracle, plus >= 90% of outputs equal to the oracle's own BF16
+rounding (FP32 accumulation changes only last-bit ties).
+
+Inputs to the GEMM-only cases are quantized by the oracle on the host and
+uploaded; the full-size cases run the whole GPU path (quantizers, then
+GEMM) and compare sampled outputs with the oracle's quantize-then-multiply
+of the same BF16 inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (
+    announce,
+    assert_gemm_close,
+    bf16_bits_to_device,
+    device_to_bits,
+    sample_cols,
+    sampled_gemm_ref,
+)
+from synthetic import LAYER_SHAPES_QWEN3_8B, MOE_QWEN3_30B_A3B, activations, bf16_normal, gather_rows, moe_routing
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fb():
+    import fp8_blockwise_quantized_quantize_amd as m
+
+    return m
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_gemm(fb, qa, sa, qw, sw):
+    y = fb.gemm_w8a8_blockscaled(_dev(qa), _dev(sa), _dev(qw), _dev(sw))
+    return device_to_bits(y)
+
+
+def _oracle_inputs(m, n, k, seed, n_out=0, mult=1.0):
+    x, _ = activations(m, k, (seed, 0), n_outliers=n_out, outlier_mult=mult)
+    w = bf16_normal((n, k), 0.02, (seed, 1))
+    qa, sa = oracle.quant_act_per_token_group(x)
+    qw, sw = oracle.quant_weight_blockwise(w)
+    return qa, sa, qw, sw
+
+
+def test_gemm_tiny_config(fb):
+    announce("gemm tiny 32x384x512")
+    qa, sa, qw, sw = _oracle_inputs(32, 384, 512, 30, 4, 50.0)
+    rep = assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw), oracle.gemm_ref(qa, sa, qw, sw))
+    print(rep)
+
+
+@pytest.mark.parametrize("m,n,k", [(100, 200, 256), (1, 1, 128), (130, 129, 384), (257, 130, 1024), (3, 1000, 128),
+                                   (64, 128, 2048)])
+def test_gemm_ragged(fb, m, n, k):
+    announce("gemm ragged", m, n, k)
+    qa, sa, qw, sw = _oracle_inputs(m, n, k, 31 + m)
+    assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw), oracle.gemm_ref(qa, sa, qw, sw))
+
+
+def test_gemm_k_zero_gives_zeros(fb):
+    announce("gemm K = 0")
+    y = fb.gemm_w8a8_blockscaled(torch.empty((5, 0), dtype=torch.uint8, device="cuda"),
+                                 torch.empty((5, 0), dtype=torch.float32, device="cuda"),
+                                 torch.empty((7, 0), dtype=torch.uint8, device="cuda"),
+                                 torch.empty((1, 0), dtype=torch.float32, device="cuda"))
+    assert torch.count_nonzero(y.float()) == 0 and y.shape == (5, 7)
+
+
+def test_gemm_random_codes_and_scales(fb):
+    """All finite codes, scales spread over 2^-40..2^40, zero-scale rows."""
+    announce("gemm random codes 192x256x640")
+    rng = np.random.default_rng(32)
+    m, n, k = 192, 256, 640
+    qa = rng.integers(0, 256, (m, k)).astype(np.uint8)
+    qw = rng.integers(0, 256, (n, k)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x00
+    qw[(qw & 0x7F) == 0x7F] = 0x80
+    sa = np.exp2(rng.uniform(-40, 40, (m, k // 128))).astype(np.float32)
+    sw = np.exp2(rng.uniform(-40, 40, (2, k // 128))).astype(np.float32)
+    sa[5] = 0
+    y = gpu_gemm(fb, qa, sa, qw, sw)
+    ref = oracle.gemm_ref(qa, sa, qw, sw)
+    # per-row relative check: row magnitudes differ by up to 2^80
+    for r in range(m):
+        if not np.any(ref[r]):
+            assert np.all((y[r] & 0x7FFF) == 0)
+            continue
+        assert_gemm_close(y[r:r + 1], ref[r:r + 1], min_exact=0.5)
+
+
+def test_gemm_one_hot_rows(fb):
+    announce("gemm one-hot rows")
+    rng = np.random.default_rng(33)
+    n, k = 256, 384
+    w = bf16_normal((n, k), 0.02, (33, 0))
+    qw, sw = oracle.quant_weight_blockwise(w)
+    cols = np.array([0, 127, 128, 255, 300, 383])
+    qa = np.zeros((len(cols), k), np.uint8)
+    qa[np.arange(len(cols)), cols] = 0x38
+    sa = np.ones((len(cols), 3), np.float32)
+    y = gpu_gemm(fb, qa, sa, qw, sw)
+    want = oracle.round_to_bf16_bits(oracle.dequant_weight(qw, sw)[:, cols].T)
+    assert np.array_equal(y, want)  # a single exact product: bit-exact
+    _ = rng
+
+
+@pytest.mark.parametrize("n,k", [(1024, 4096), (512, 12288)])
+def test_gemm_decode_shaped_full(fb, n, k):
+    announce("gemm decode-shaped full 256 x", n, k)
+    qa, sa, qw, sw = _oracle_inputs(256, n, k, 34)
+    assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw), oracle.gemm_ref(qa, sa, qw, sw))
+
+
+def _full_path(fb, x_bits, w_bits):
+    xq, xs = fb.quantize_act_per_token_group(bf16_bits_to_device(x_bits))
+    wq, ws = fb.quantize_weight_blockwise(bf16_bits_to_device(w_bits))
+    return fb.gemm_w8a8_blockscaled(xq, xs, wq, ws)
+
+
+@pytest.mark.parametrize("idx", range(len(LAYER_SHAPES_QWEN3_8B)))
+@pytest.mark.parametrize("m", [256, 8192])
+def test_full_path_qwen3_8b_sampled(fb, idx, m):
+    name, n, k = LAYER_SHAPES_QWEN3_8B[idx]
+    announce("full path qwen3-8b", name, m, n, k)
+    n_out = round(0.01 * k) if m == 8192 else 0
+    x, _ = activations(m, k, (40 + idx, m), n_outliers=n_out, outlier_mult=30.0)
+    w = bf16_normal((n, k), 0.02, (41, idx))
+    y = _full_path(fb, x, w)
+    rng = np.random.default_rng(idx * 7 + m)
+    rows = np.sort(rng.choice(m, 64, replace=False))
+    cols = sample_cols(rng, n)
+    ref = sampled_gemm_ref(x[rows], w, cols)
+    got = device_to_bits(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].contiguous())
+    assert_gemm_close(got, ref)
+
+
+# ------------------------------------------------------------ grouped GEMM
+
+def _grouped_oracle_inputs(counts, n, k, seed):
+    g = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    m = int(off[-1])
+    x, _ = activations(max(m, 1), k, (seed, 0))
+    x = x[:m]
+    w = bf16_normal((g, n, k), 0.02, (seed, 1))
+    qa, sa = oracle.quant_act_per_token_group(x)
+    qw, sw = oracle.quant_weight_blockwise(w)
+    return qa, sa, qw, sw, off
+
+
+def gpu_grouped(fb, qa, sa, qw, sw, off):
+    y = fb.grouped_gemm_w8a8_blockscaled(_dev(qa), _dev(sa), _dev(qw), _dev(sw), _dev(off))
+    return device_to_bits(y)
+
+
+@pytest.mark.parametrize("counts", [[3, 0, 17, 1, 0], [0, 0, 300, 0], [129], [0, 128, 0, 1, 255, 0, 0, 2],
+                                    [1] * 40])
+def test_grouped_small(fb, counts):
+    announce("grouped small", counts)
+    qa, sa, qw, sw, off = _grouped_oracle_inputs(counts, 256, 384, 50 + len(counts))
+    y = gpu_grouped(fb, qa, sa, qw, sw, off)
+    ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, off)
+    for e in range(len(counts)):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            assert_gemm_close(y[lo:hi], ref[lo:hi])
+
+
+def test_grouped_single_group_equals_dense(fb):
+    announce("grouped G=1 vs dense")
+    qa, sa, qw, sw, off = _grouped_oracle_inputs([200], 384, 512, 60)
+    yg = gpu_grouped(fb, qa, sa, qw, sw, off)
+    yd = gpu_gemm(fb, qa, sa, qw[0], sw[0])
+    assert np.array_equal(yg, yd)
+
+
+def test_grouped_ragged_n(fb):
+    announce("grouped ragged N=200")
+    qa, sa, qw, sw, off = _grouped_oracle_inputs([5, 130, 0, 7], 200, 256, 61)
+    y = gpu_grouped(fb, qa, sa, qw, sw, off)
+    ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, off)
+    assert_gemm_close(y, ref)
+
+
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_grouped_moe_full_size_sampled(fb, proj):
+    """Qwen3-30B-A3B expert layer at full size: GPU quantizers + grouped GEMM."""
+    cfg = MOE_QWEN3_30B_A3B
+    g, t = cfg["experts"], cfg["tokens"]
+    n, k = cfg[proj]
+    announce("grouped moe full", proj, g, n, k)
+    tok, exp, off = moe_routing(t, g, cfg["top_k"], (70, 0))
+    m = int(off[-1])
+    if proj == "gate_up":
+        h, _ = activations(t, k, (70, 1))
+        x = gather_rows(h, tok)
+    else:
+        x, _ = activations(m, k, (70, 2))
+    w = bf16_normal((g, n, k), 0.02, (70, 3 if proj == "gate_up" else 4))
+    xq, xs = fb.quantize_act_per_token_group(bf16_bits_to_device(x))
+    wq, ws = fb.quantize_weight_blockwise(bf16_bits_to_device(w))
+    y = fb.grouped_gemm_w8a8_blockscaled(xq, xs, wq, ws, _dev(off))
+    rng = np.random.default_rng(71)
+    for e in rng.choice(g, 6, replace=False):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rows = np.sort(rng.choice(np.arange(lo, hi), min(16, hi - lo), replace=False))
+        cols = sample_cols(rng, n, blocks=2, per_block=16)
+        ref = sampled_gemm_ref(x[rows], w[e], cols)
+        got = device_to_bits(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].contiguous())
+        assert_gemm_close(got, ref)
