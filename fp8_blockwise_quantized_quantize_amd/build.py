@@ -26,6 +26,8 @@ FLAGS = [
     # no fused multiply-add contraction beyond the explicit fmaf() calls:
     # the quantizer's quotient must be the exact IEEE one.
     "-ffp-contract=off",
+    # MFMA results go to VGPRs (the per-K-block scale FMA reads them directly)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     # packed FP32 VALU forms are kept out of the generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",

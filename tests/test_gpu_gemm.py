@@ -182,7 +182,12 @@ def test_grouped_single_group_equals_dense(fb):
     qa, sa, qw, sw, off = _grouped_oracle_inputs([200], 384, 512, 60)
     yg = gpu_grouped(fb, qa, sa, qw, sw, off)
     yd = gpu_gemm(fb, qa, sa, qw[0], sw[0])
-    assert np.array_equal(yg, yd)
+    ref = oracle.gemm_ref(qa, sa, qw[0], sw[0])
+    assert_gemm_close(yg, ref)
+    assert_gemm_close(yd, ref)
+    # the two launches may use different tilings (summation orders): they
+    # agree except for last-bit rounding of a few outputs
+    assert np.mean(yg == yd) >= 0.95
 
 
 def test_grouped_ragged_n(fb):
