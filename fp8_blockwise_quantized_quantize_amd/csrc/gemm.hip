@@ -102,12 +102,59 @@ __device__ __forceinline__ v8i frag_lds(const uint8_t* lds, int row, int g) {
   return to_v8i(lo, hi);
 }
 
+// Per-lane byte offsets of the two fragment chunks inside a 16-row group of
+// a swizzled LDS tile ((row0 + r16) & 7 == r16 & 7 for row0 % 16 == 0), so
+// a fragment read is one base register plus an immediate row offset.
+struct FragLds {
+  int lo, hi;
+  __device__ __forceinline__ FragLds(int lane) {
+    const int g = lane >> 4, r16 = lane & 15;
+    lo = r16 * kBlock + ((g ^ (r16 & 7)) << 4);
+    hi = r16 * kBlock + (((g + 4) ^ (r16 & 7)) << 4);
+  }
+  // fragment of stage rows row0 .. row0 + 15 (row0 a multiple of 16)
+  __device__ __forceinline__ v8i operator()(const uint8_t* buf, int row0) const {
+    const uint8_t* p = buf + row0 * kBlock;
+    return to_v8i(*reinterpret_cast<const u32x4*>(p + lo), *reinterpret_cast<const u32x4*>(p + hi));
+  }
+};
+
 // Fence for both the IR optimizer and the machine scheduler: loads and MFMAs
 // stay on their side, so prefetches are issued before the compute that
 // overlaps them (otherwise the compiler sinks them and then waits on them).
 __device__ __forceinline__ void order_fence() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// acc[i][j] += (P(i, j) = MFMA(fw_i, fa_j)) * c(i, j) over a TN x TM grid of
+// 16x16 tiles, software-pipelined: the FMAs of MFMA t are issued after MFMA
+// t + kDelay, with the partials in a ring of kDelay + 1 registers, so the
+// MFMA pipe need not wait for its own result (with two waves per SIMD a
+// short delay suffices: the other wave fills the gap).  sched_group_barrier pins the
+// interleave (one MFMA, then the four FMAs of an older one).
+template <int TN, int TM, int kDelay, class LoadW, class Scale>
+__device__ __forceinline__ void tile_product(v4f (&acc)[TN][TM], const v8i (&fa)[TM], LoadW load_w, Scale scale) {
+  constexpr int T = TN * TM;
+  v4f ring[kDelay + 1];
+  v8i fw = load_w(0), fw_next = fw;
+#pragma unroll
+  for (int t = 0; t < T + kDelay; ++t) {
+    if (t < T) {
+      const int i = t / TM, j = t % TM;
+      if (j == 0 && i + 1 < TN) fw_next = load_w(i + 1);
+      ring[t % (kDelay + 1)] = mfma_e4m3(fw, fa[j]);
+      if (j == TM - 1) fw = fw_next;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    }
+    if (t >= kDelay) {
+      const int u = t - kDelay, i = u / TM, j = u % TM;
+      const float c = scale(i, j);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(ring[u % (kDelay + 1)][r], c, acc[i][j][r]);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // its four FMAs
+    }
+  }
 }
 
 // Rows of one output tile: activation rows [m_lo, m_hi), weight rows
@@ -185,6 +232,7 @@ struct Skinny {
     const int gvoff = lrow * (int)K + lchunk * 16;
     const int svoff = r16 * KB * 4;  // + 16 j KB 4
     uint8_t* slice = reinterpret_cast<uint8_t*>(red) + wave * kSlice;
+    const FragLds fl(lane);
 
     v4f acc[TN][TM];
 #pragma unroll
@@ -197,11 +245,11 @@ struct Skinny {
       kb = kb < KB ? kb : kb - KB;
       const int koff = kb * kBlock;
 #pragma unroll
-      for (int q = 0; q < BN / 8; ++q) s.v[q] = bload16(wr, gvoff + 8 * q * (int)K, koff);
+      for (int q = 0; q < BN / 8; ++q) s.v[q] = bload16(wr, gvoff, koff + 8 * q * (int)K);
 #pragma unroll
-      for (int q = 0; q < BM / 8; ++q) s.v[BN / 8 + q] = bload16(ar, gvoff + 8 * q * (int)K, koff);
+      for (int q = 0; q < BM / 8; ++q) s.v[BN / 8 + q] = bload16(ar, gvoff, koff + 8 * q * (int)K);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) s.sav[j] = bload_f32(sr, svoff + j * 16 * KB * 4, kb * 4);
+      for (int j = 0; j < TM; ++j) s.sav[j] = bload_f32(sr, svoff, kb * 4 + j * 16 * KB * 4);
 #pragma unroll
       for (int i = 0; i < TN; ++i) s.swv[i] = swrow[i][kb];
     };
@@ -212,18 +260,10 @@ struct Skinny {
     auto compute = [&](const Stage& s) {
       v8i fa[TM];
 #pragma unroll
-      for (int j = 0; j < TM; ++j) fa[j] = frag_lds(slice, BN + j * 16 + r16, g);
-#pragma unroll
-      for (int i = 0; i < TN; ++i) {
-        const v8i fw = frag_lds(slice, i * 16 + r16, g);
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          const v4f p = mfma_e4m3(fw, fa[j]);
-          const float c = s.sav[j] * s.swv[i];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], c, acc[i][j][r]);
-        }
-      }
+      for (int j = 0; j < TM; ++j) fa[j] = fl(slice, BN + j * 16);
+      tile_product<TN, TM, 4>(
+          acc, fa, [&](int i) { return fl(slice, i * 16); },
+          [&](int i, int j) { return s.sav[j] * s.swv[i]; });
     };
 
     // this wave's K-blocks: wave, wave + 4, ...  Stage sX holds the
@@ -293,38 +333,48 @@ struct Skinny {
 };
 
 // ---------------------------------------------------------------------------
-// wide: 128 (n) x 256 (m) tile, W K-blocks through LDS, activations direct.
+// wide: 256 (n) x 256 (m) tile, 8 waves (2 per SIMD, so one wave's MFMAs
+// fill the other's dependency stalls) in a 2 (n) x 4 (m) grid, 128 x 64
+// each.  Both operands of a K-block (256 weight rows + 256 activation rows,
+// 64 KB) go global -> LDS directly (buffer_load ... lds, 16 bytes per lane,
+// 8 lanes per 128-byte row), double-buffered, so no VGPRs hold staging
+// data; fragments are read with ds_read_b128.
+// Phase k: wait for this wave's loads of K-block k; barrier (everyone's
+// data has landed, and everyone is done with the other buffer); issue the
+// loads of k+1 into the other buffer; compute k.
 // ---------------------------------------------------------------------------
 struct Wide {
-  static constexpr int BN = 128, BM = 256, TN = 8, TM = 4;
-  static constexpr int kLdsBytes = 2 * BN * kBlock;  // double-buffered W K-block
-  static constexpr int kWavesPerSimd = 2;             // two workgroups per CU hide MFMA latency
-
-  struct AStage {
-    v8i fa[TM];
-    float sav[TM];
-    float swv;
-  };
+  static constexpr int BN = 256, BM = 256, TN = 8, TM = 4;
+  static constexpr int kThreadsW = 512;
+  static constexpr int kRows = BN + BM;
+  static constexpr int kStage = kRows * kBlock;            // 64 KB
+  static constexpr int kLdsBytes = 2 * kStage;              // double buffer
+  static constexpr int kWavesPerSimd = 2;
 
   __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) {
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wn = wave & 1, wm = wave >> 1;                    // 2 x 4 wave grid
     const int64_t K = t.K;
     const int KB = (int)(K / kBlock);
     const int64_t n_hi = (t.n0 + BN < t.N) ? t.n0 + BN : t.N;
-    const float* swrow = t.sw + (t.n0 / kBlock) * KB;  // n0 is a multiple of 128: one scale block
+    // this wave's 128 weight rows form one scale block (n0 is a multiple of 256)
+    int64_t nb_row = t.n0 + wn * 128;
+    nb_row = nb_row < t.N ? nb_row : t.N - 1;
+    const float* swrow = t.sw + (nb_row / kBlock) * KB;
     const auto wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
-    const int64_t am_lo = t.m_lo + wave * 64;  // this wave's activation rows
+    const auto ar = make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
+    const int64_t am_lo = t.m_lo + wm * 64;  // this wave's activation rows (scales)
     const int64_t am_hi = (am_lo + 64 < t.m_hi) ? am_lo + 64 : t.m_hi;
     const int64_t arows = am_hi > am_lo ? am_hi - am_lo : 0;
-    const auto ar = make_rsrc(t.a + am_lo * K, arows * K);
     const auto sr = make_rsrc(t.sa + am_lo * KB, arows * KB * 4);
+    const int svoff = r16 * KB * 4;  // + 16 j KB 4
 
-    // W staging: thread owns chunk (tid & 7) of rows (tid >> 3) + 32 q, q = 0..3
-    const int wchunk = tid & 7;
-    const int wvoff = (tid >> 3) * (int)K + wchunk * 16;  // + 32 q K
-    const int avoff = r16 * (int)K + 16 * g;              // + 16 j K
-    const int svoff = r16 * KB * 4;                       // + 16 j KB 4
+    // DMA staging: load q (0..7) of wave w fills stage rows R0..R0+7 with
+    // R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at physical chunk
+    // l%8, so it fetches logical chunk (l%8) ^ (l/8) (the XOR swizzle).
+    const int dvoff = (lane >> 3) * (int)K + (((lane & 7) ^ (lane >> 3)) << 4);
+    const FragLds fl(lane);
 
     v4f acc[TN][TM];
 #pragma unroll
@@ -332,91 +382,82 @@ struct Wide {
 #pragma unroll
       for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 wreg[4];
     auto rotk = [&](int step) {  // rotated K-block id, step < KB
       const int kb = step + t.rot;
       return kb < KB ? kb : kb - KB;
     };
-    auto load_w = [&](int step) {
-      const int kb = rotk(step);
+    auto dma = [&](int step, uint8_t* buf) {
+      const int koff = rotk(step) * kBlock;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wreg[q] = bload16(wr, wvoff + 32 * q * (int)K, kb * kBlock);
-    };
-    auto store_w = [&](uint8_t* buf) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(buf + swz((tid >> 3) + 32 * q, wchunk)) = wreg[q];
-    };
-    auto load_a = [&](AStage& s, int step) {
-      const int kb = rotk(step);
-#pragma unroll
-      for (int j = 0; j < TM; ++j) s.fa[j] = frag_buf(ar, avoff + j * 16 * (int)K, kb * kBlock);
-#pragma unroll
-      for (int j = 0; j < TM; ++j) s.sav[j] = bload_f32(sr, svoff + j * 16 * KB * 4, kb * 4);
-      s.swv = swrow[kb];
-    };
-    auto compute = [&](const AStage& s, const uint8_t* buf) {
-      float c[TM];
-#pragma unroll
-      for (int j = 0; j < TM; ++j) c[j] = s.sav[j] * s.swv;
-#pragma unroll
-      for (int i = 0; i < TN; ++i) {
-        const v8i fw = frag_lds(buf, i * 16 + r16, g);
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          const v4f p = mfma_e4m3(fw, s.fa[j]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], c[j], acc[i][j][r]);
-        }
+      for (int q = 0; q < 8; ++q) {
+        const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
+        auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
+        if (q < 4)  // stage rows 0..255: weight rows n0 + r0 ..
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff, koff + r0 * (int)K, 0, 0);
+        else        // stage rows 256..511: activation rows m_lo + r0 - 256 ..
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff, koff + (r0 - BN) * (int)K, 0, 0);
       }
     };
+    // per-K-block scales of this wave's 64 activation rows x its weight block
+    auto load_scales = [&](float (&c)[TM], int step) {
+      const int kb = rotk(step);
+      const float sw = swrow[kb];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) c[j] = bload_f32(sr, svoff, kb * 4 + j * 16 * KB * 4) * sw;
+    };
+    auto compute = [&](const float (&c)[TM], const uint8_t* buf) {
+      v8i fa[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) fa[j] = fl(buf, BN + wm * 64 + j * 16);
+      tile_product<TN, TM, 2>(
+          acc, fa, [&](int i) { return fl(buf, wn * 128 + i * 16); },
+          [&](int, int j) { return c[j]; });
+    };
+    // The compiler does not track LDS writes by buffer_load ... lds: wait
+    // for them explicitly before the barrier that publishes the buffer.
+    auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
     uint8_t* buf0 = lds;
-    uint8_t* buf1 = lds + BN * kBlock;
-    AStage s0, s1;
+    uint8_t* buf1 = lds + kStage;
     const int kb_last = KB - 1;
-    auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };  // clamped prefetch index
+    auto nxt = [&](int step) { return step < KB ? step : kb_last; };  // clamped prefetch
+    float c0[TM], c1[TM];
     if (KB > 0) {
+      dma(0, buf0);
+      load_scales(c0, 0);
+    }
+    // Loads past the last K-block re-load it into the buffer nobody reads
+    // again, keeping the loop body free of branches.
+    int k = 0;
+    for (; k + 1 < KB; k += 2) {
+      wait_dma();
+      __syncthreads();  // buf0 holds K-block k; buf1 is free
+      dma(k + 1, buf1);
+      load_scales(c1, k + 1);
       order_fence();
-      load_w(0);
-      load_a(s0, 0);
+      compute(c0, buf0);
       order_fence();
-      store_w(buf0);
-      load_w(nxt(1));
+      wait_dma();
+      __syncthreads();  // buf1 holds K-block k+1; buf0 is free
+      dma(nxt(k + 2), buf0);
+      load_scales(c0, nxt(k + 2));
       order_fence();
-      load_a(s1, nxt(1));
+      compute(c1, buf1);
       order_fence();
     }
-    // iteration kb: W(kb) in LDS, W(kb+1) in wreg, activations of kb in stage kb&1
-    int kb = 0;
-    for (; kb + 1 < KB; kb += 2) {
-      __syncthreads();  // buf0 holds W(kb); buf1 is free
-      store_w(buf1);
-      load_w(nxt(kb + 2));
-      order_fence();
-      compute(s0, buf0);
-      order_fence();
-      load_a(s0, nxt(kb + 2));
-      order_fence();
-      __syncthreads();  // buf1 holds W(kb+1); buf0 is free
-      store_w(buf0);
-      load_w(nxt(kb + 3));
-      order_fence();
-      compute(s1, buf1);
-      order_fence();
-      load_a(s1, nxt(kb + 3));
-      order_fence();
-    }
-    if (kb < KB) {
+    if (k < KB) {
+      wait_dma();
       __syncthreads();
-      compute(s0, buf0);
+      compute(c0, buf0);
     }
+    wait_dma();  // no LDS write may be in flight when the workgroup ends
 
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      const int64_t m = t.m_lo + wave * 64 + j * 16 + r16;
+      const int64_t m = t.m_lo + wm * 64 + j * 16 + r16;
       if (m >= t.m_hi) continue;
 #pragma unroll
-      for (int i = 0; i < TN; ++i) store4(t.y, t.N, m, t.n0 + i * 16 + g * 4, acc[i][j]);
+      for (int i = 0; i < TN; ++i) store4(t.y, t.N, m, t.n0 + wn * 128 + i * 16 + g * 4, acc[i][j]);
     }
   }
 };
@@ -443,8 +484,16 @@ __device__ __forceinline__ void tile_of(int64_t L, int64_t tiles_m, int64_t tile
   *tn = idx / gsize;
 }
 
+template <class Kern>
+constexpr int threads_of() {
+  if constexpr (std::is_same<Kern, Wide>::value)
+    return Wide::kThreadsW;
+  else
+    return kThreads;
+}
+
 template <class Kern, int BN, int BM>
-__global__ __launch_bounds__(kThreads, Kern::kWavesPerSimd) void gemm_dense_kernel(const uint8_t* __restrict__ a,
+__global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_dense_kernel(const uint8_t* __restrict__ a,
                                                                  const float* __restrict__ sa,
                                                                  const uint8_t* __restrict__ w,
                                                                  const float* __restrict__ sw,
@@ -460,7 +509,7 @@ __global__ __launch_bounds__(kThreads, Kern::kWavesPerSimd) void gemm_dense_kern
   t.m_hi = (t.m_lo + BM < M) ? t.m_lo + BM : M;
   t.n0 = tn * BN;
   t.N = N; t.K = K;
-  t.rot = (int)((L * 4) % (K / kBlock > 0 ? K / kBlock : 1));
+  t.rot = std::is_same<Kern, Wide>::value ? 0 : (int)((L * 4) % (K / kBlock > 0 ? K / kBlock : 1));
   if constexpr (std::is_same<Kern, Wide>::value)
     Wide::run(t, smem);
   else
@@ -471,13 +520,14 @@ __global__ __launch_bounds__(kThreads, Kern::kWavesPerSimd) void gemm_dense_kern
 // sum over ceil(rows_e / BM) computed in the workgroup from the device
 // offsets; slots past the last tile exit.  Offsets are clamped to [0, M].
 template <class Kern, int BN, int BM>
-__global__ __launch_bounds__(kThreads, Kern::kWavesPerSimd) void gemm_grouped_kernel(
+__global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_grouped_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ w,
     const float* __restrict__ sw, const int32_t* __restrict__ offsets, uint16_t* __restrict__ y, int64_t M,
     int64_t N, int64_t K, int G, int64_t slots, int64_t tiles_n) {
   extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int NT = threads_of<Kern>();
   __shared__ int found_e, found_t;
-  __shared__ int wave_sum[kThreads / 64];
+  __shared__ int wave_sum[NT / 64];
   const int64_t L = xcd_linear(blockIdx.x, slots * tiles_n);
   // n fastest: the workgroups of one (expert, m-tile) share its activation rows
   const int64_t tn = L % tiles_n;
@@ -485,7 +535,7 @@ __global__ __launch_bounds__(kThreads, Kern::kWavesPerSimd) void gemm_grouped_ke
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) found_e = -1;
   int base = 0;  // tiles of experts before this chunk
-  for (int c0 = 0; c0 < G; c0 += kThreads) {
+  for (int c0 = 0; c0 < G; c0 += NT) {
     const int e = c0 + tid;
     int tiles = 0;
     if (e < G) {
@@ -512,7 +562,7 @@ __global__ __launch_bounds__(kThreads, Kern::kWavesPerSimd) void gemm_grouped_ke
       found_t = slot - base - excl;
     }
     int total = 0;
-    for (int i = 0; i < kThreads / 64; ++i) total += wave_sum[i];
+    for (int i = 0; i < NT / 64; ++i) total += wave_sum[i];
     base += total;
   }
   __syncthreads();
@@ -532,7 +582,7 @@ __global__ __launch_bounds__(kThreads, Kern::kWavesPerSimd) void gemm_grouped_ke
   t.m_hi = (t.m_lo + BM < hi) ? t.m_lo + BM : hi;
   t.n0 = tn * BN;
   t.N = N; t.K = K;
-  t.rot = (int)((L * 4) % (KB > 0 ? KB : 1));
+  t.rot = 0;
   if constexpr (std::is_same<Kern, Wide>::value)
     Wide::run(t, smem);
   else
@@ -568,7 +618,7 @@ hipError_t launch_dense_cfg(const uint8_t* a, const float* sa, const uint8_t* w,
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_dense_kernel<Kern, BN, BM>), dim3((unsigned)blocks), dim3(kThreads),
+  hipLaunchKernelGGL((gemm_dense_kernel<Kern, BN, BM>), dim3((unsigned)blocks), dim3(threads_of<Kern>()),
                      (size_t)Kern::kLdsBytes, stream, a, sa, w, sw, y, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -596,7 +646,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t*
   const int64_t slots = (M + Wide::BM - 1) / Wide::BM + G;  // >= sum_e ceil(rows_e / BM)
   const int64_t blocks = tiles_n * slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_grouped_kernel<Wide, Wide::BN, Wide::BM>), dim3((unsigned)blocks), dim3(kThreads),
+  hipLaunchKernelGGL((gemm_grouped_kernel<Wide, Wide::BN, Wide::BM>), dim3((unsigned)blocks), dim3(Wide::kThreadsW),
                      (size_t)Wide::kLdsBytes, stream, a, sa, w, sw, offsets, y, M, N, K, (int)G, slots, tiles_n);
   return hipGetLastError();
 }
