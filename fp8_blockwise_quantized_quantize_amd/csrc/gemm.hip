@@ -18,19 +18,16 @@
 //
 //  * skinny<BN, BM> (few activation rows, e.g. decode with M = 256): a
 //    BN x BM output tile per 4-wave workgroup; the four waves split the
-//    K-blocks (wave w takes kb = w, w+4, ...), each loading its own
-//    operands straight from global memory into MFMA fragment registers
-//    (nothing is loaded twice within the workgroup), two K-blocks ahead;
-//    the four partial tiles are summed through LDS at the end.  Per-CU
-//    operand traffic is (BN + BM) * K, which is what bounds these shapes
-//    (the activation panel is re-read from L2 by every workgroup).
+//    K-blocks (wave w takes kb = w, w+4, ...).  Each wave stages its own
+//    K-blocks through a private LDS slice (coalesced 16-byte loads into
+//    registers one K-block ahead, ds_write, fragment reads), and the four
+//    partial tiles are summed through LDS at the end.
 //
-//  * wide (many rows: prefill, MoE experts): a 128 (n) x 256 (m) tile per
-//    4-wave workgroup, waves split along m (64 rows each).  The 128 x 128
-//    weight K-block is shared by all four waves, so it is staged through
-//    LDS (register-staged, double-buffered, 16-byte XOR swizzle); each
-//    wave's activation rows are private and go straight from global memory
-//    into fragment registers.  Loads run two K-blocks ahead.
+//  * wide (many rows: prefill, MoE experts): a 256 (n) x 256 (m) tile per
+//    8-wave workgroup (two waves per SIMD), waves in a 2 (n) x 4 (m) grid of
+//    128 x 64.  Both operands of a K-block go global -> LDS directly
+//    (buffer_load ... lds), double-buffered, one barrier per K-block; the
+//    loads of the next K-block are spread over the MFMAs of the current one.
 //
 // Tiles are ordered so that the workgroups resident on one XCD at a time
 // (consecutive workgroup ids of the same id % 8) share weight and
@@ -133,19 +130,27 @@ __device__ __forceinline__ void order_fence() {
 // MFMA pipe need not wait for its own result (with two waves per SIMD a
 // short delay suffices: the other wave fills the gap).  sched_group_barrier pins the
 // interleave (one MFMA, then the four FMAs of an older one).
-template <int TN, int TM, int kDelay, class LoadW, class Scale>
-__device__ __forceinline__ void tile_product(v4f (&acc)[TN][TM], const v8i (&fa)[TM], LoadW load_w, Scale scale) {
+// fw[0 .. kAhead-1] hold the first weight fragments on entry; the rest are
+// loaded kAhead row groups ahead of their use.
+struct NoExtra {
+  __device__ __forceinline__ bool operator()(int) const { return false; }
+};
+
+// `extra(t)` may issue one more instruction after MFMA t (returns whether
+// it did, so the scheduler keeps it at that point).
+template <int TN, int TM, int kDelay, int kAhead, class LoadW, class Scale, class Extra = NoExtra>
+__device__ __forceinline__ void tile_product(v4f (&acc)[TN][TM], const v8i (&fa)[TM], v8i (&fw)[kAhead + 1],
+                                             LoadW load_w, Scale scale, Extra extra = Extra()) {
   constexpr int T = TN * TM;
   v4f ring[kDelay + 1];
-  v8i fw = load_w(0), fw_next = fw;
 #pragma unroll
   for (int t = 0; t < T + kDelay; ++t) {
     if (t < T) {
       const int i = t / TM, j = t % TM;
-      if (j == 0 && i + 1 < TN) fw_next = load_w(i + 1);
-      ring[t % (kDelay + 1)] = mfma_e4m3(fw, fa[j]);
-      if (j == TM - 1) fw = fw_next;
+      if (j == 0 && i + kAhead < TN) fw[(i + kAhead) % (kAhead + 1)] = load_w(i + kAhead);
+      ring[t % (kDelay + 1)] = mfma_e4m3(fw[i % (kAhead + 1)], fa[j]);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (extra(t)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // a VMEM read
     }
     if (t >= kDelay) {
       const int u = t - kDelay, i = u / TM, j = u % TM;
@@ -261,8 +266,10 @@ struct Skinny {
       v8i fa[TM];
 #pragma unroll
       for (int j = 0; j < TM; ++j) fa[j] = fl(slice, BN + j * 16);
-      tile_product<TN, TM, 4>(
-          acc, fa, [&](int i) { return fl(slice, i * 16); },
+      v8i fw[2];
+      fw[0] = fl(slice, 0);
+      tile_product<TN, TM, 4, 1>(
+          acc, fa, fw, [&](int i) { return fl(slice, i * 16); },
           [&](int i, int j) { return s.sav[j] * s.swv[i]; });
     };
 
@@ -340,8 +347,8 @@ struct Skinny {
 // 8 lanes per 128-byte row), double-buffered, so no VGPRs hold staging
 // data; fragments are read with ds_read_b128.
 // Phase k: wait for this wave's loads of K-block k; barrier (everyone's
-// data has landed, and everyone is done with the other buffer); issue the
-// loads of k+1 into the other buffer; compute k.
+// data has landed, and everyone is done with the other buffer); compute k
+// while issuing the loads of k+1 into the other buffer between its MFMAs.
 // ---------------------------------------------------------------------------
 struct Wide {
   static constexpr int BN = 256, BM = 256, TN = 8, TM = 4;
@@ -361,7 +368,7 @@ struct Wide {
     // this wave's 128 weight rows form one scale block (n0 is a multiple of 256)
     int64_t nb_row = t.n0 + wn * 128;
     nb_row = nb_row < t.N ? nb_row : t.N - 1;
-    const float* swrow = t.sw + (nb_row / kBlock) * KB;
+    const auto swr = make_rsrc(t.sw + (nb_row / kBlock) * KB, (int64_t)KB * 4);
     const auto wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
     const auto ar = make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
     const int64_t am_lo = t.m_lo + wm * 64;  // this wave's activation rows (scales)
@@ -386,32 +393,59 @@ struct Wide {
       const int kb = step + t.rot;
       return kb < KB ? kb : kb - KB;
     };
-    auto dma = [&](int step, uint8_t* buf) {
+    auto dma_q = [&](int q, int step, uint8_t* buf) {
       const int koff = rotk(step) * kBlock;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
-        auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
-        if (q < 4)  // stage rows 0..255: weight rows n0 + r0 ..
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff, koff + r0 * (int)K, 0, 0);
-        else        // stage rows 256..511: activation rows m_lo + r0 - 256 ..
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff, koff + (r0 - BN) * (int)K, 0, 0);
-      }
+      const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
+      auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
+      if (q < 4)  // stage rows 0..255: weight rows n0 + r0 ..
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff, koff + r0 * (int)K, 0, 0);
+      else        // stage rows 256..511: activation rows m_lo + r0 - 256 ..
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff, koff + (r0 - BN) * (int)K, 0, 0);
     };
-    // per-K-block scales of this wave's 64 activation rows x its weight block
-    auto load_scales = [&](float (&c)[TM], int step) {
+    // Per-K-block scales of this wave's 64 activation rows and of its weight
+    // block, fetched one phase ahead with vector loads (tracked by vmcnt, so
+    // using them never waits on loads issued after them) and multiplied only
+    // when the phase that needs them starts.
+    struct Scales {
+      float sa[TM], sw;
+    };
+    auto load_scales = [&](Scales& c, int step) {
       const int kb = rotk(step);
-      const float sw = swrow[kb];
+      c.sw = bload_f32(swr, 0, kb * 4);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) c[j] = bload_f32(sr, svoff, kb * 4 + j * 16 * KB * 4) * sw;
+      for (int j = 0; j < TM; ++j) c.sa[j] = bload_f32(sr, svoff, kb * 4 + j * 16 * KB * 4);
     };
-    auto compute = [&](const float (&c)[TM], const uint8_t* buf) {
-      v8i fa[TM];
+    constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
+    auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * 128 + i * 16); };
+    // The first fragments of a phase, read right after its barrier; the
+    // first MFMA's two operands go first so that it waits for them only.
+    auto first_frags = [&](v8i (&fa)[TM], v8i (&fw)[kAhead + 1], const uint8_t* buf) {
+      fw[0] = load_w(buf, 0);
+      fa[0] = fl(buf, BN + wm * 64);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) fa[j] = fl(buf, BN + wm * 64 + j * 16);
-      tile_product<TN, TM, 2>(
-          acc, fa, [&](int i) { return fl(buf, wn * 128 + i * 16); },
-          [&](int, int j) { return c[j]; });
+      for (int j = 1; j < TM; ++j) fa[j] = fl(buf, BN + wm * 64 + j * 16);
+#pragma unroll
+      for (int p = 1; p < kAhead; ++p) fw[p] = load_w(buf, p);
+    };
+    // One phase: the product of the K-block in `buf`, with the eight loads of
+    // K-block `step` into `dst` issued after every second MFMA of its first
+    // half (spreading them keeps the L2 and LDS-write traffic from arriving
+    // as one burst right after the barrier).  kLoad false: no loads.
+    auto phase = [&](auto load_tag, const Scales& sc, const uint8_t* buf, int step, uint8_t* dst) {
+      constexpr bool kLoad = decltype(load_tag)::value;
+      v8i fa[TM], fw[kAhead + 1];
+      first_frags(fa, fw, buf);
+      float c[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) c[j] = sc.sa[j] * sc.sw;
+      tile_product<TN, TM, 2, kAhead>(
+          acc, fa, fw, [&](int i) { return load_w(buf, i); }, [&](int, int j) { return c[j]; },
+          [&](int t) {
+            if (!kLoad || (t & 1) || t >= 16) return false;
+            dma_q(t >> 1, step, dst);
+            return true;
+          });
     };
     // The compiler does not track LDS writes by buffer_load ... lds: wait
     // for them explicitly before the barrier that publishes the buffer.
@@ -421,34 +455,36 @@ struct Wide {
     uint8_t* buf1 = lds + kStage;
     const int kb_last = KB - 1;
     auto nxt = [&](int step) { return step < KB ? step : kb_last; };  // clamped prefetch
-    float c0[TM], c1[TM];
+    Scales c0, c1;
     if (KB > 0) {
-      dma(0, buf0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dma_q(q, 0, buf0);
       load_scales(c0, 0);
     }
-    // Loads past the last K-block re-load it into the buffer nobody reads
-    // again, keeping the loop body free of branches.
+    // Phase k: wait for this wave's loads of K-block k, barrier (all loads of
+    // k have landed and every wave is done with the other buffer), then
+    // compute k while loading k + 1 into the other buffer.  Loads past the
+    // last K-block re-load it into the buffer nobody reads again, keeping
+    // the loop body free of branches.
     int k = 0;
     for (; k + 1 < KB; k += 2) {
       wait_dma();
       __syncthreads();  // buf0 holds K-block k; buf1 is free
-      dma(k + 1, buf1);
       load_scales(c1, k + 1);
       order_fence();
-      compute(c0, buf0);
+      phase(std::true_type{}, c0, buf0, k + 1, buf1);
       order_fence();
       wait_dma();
       __syncthreads();  // buf1 holds K-block k+1; buf0 is free
-      dma(nxt(k + 2), buf0);
       load_scales(c0, nxt(k + 2));
       order_fence();
-      compute(c1, buf1);
+      phase(std::true_type{}, c1, buf1, nxt(k + 2), buf0);
       order_fence();
     }
     if (k < KB) {
       wait_dma();
       __syncthreads();
-      compute(c0, buf0);
+      phase(std::false_type{}, c0, buf0, 0, buf1);
     }
     wait_dma();  // no LDS write may be in flight when the workgroup ends
 
