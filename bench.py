@@ -16,11 +16,23 @@ region: prefill GEMMs (M = 8192), the MoE grouped GEMMs, the 36-layer
 re-quantization sweep, and sampled parity against the oracle.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail] [--no-cpu]
+       python bench.py --rocprof-summary DIR   (summarise rocprofv3 output, see below)
+
+`roofline.traffic` is the HBM traffic per launch of the dominant kernel as
+measured by rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, scaled by what
+the same counters read for a plain copy of known size).  bench.py takes it
+from the committed profile summary under profiles/ when that summary was
+taken on the current kernel sources (same SHA-256), and reports null
+otherwise.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,6 +40,41 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "fp8_blockwise_quantized_quantize_amd", "csrc")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_layer_step_qwen3_8b.md")
+# kernel-name prefix of each phase -> the source file that defines it
+PHASE_KERNELS = {
+    "requant": ("quant_weight_kernel", "quant.hip"),
+    "act_quant": ("quant_act_kernel", "quant.hip"),
+    "gemm": ("gemm_dense_kernel", "gemm.hip"),
+}
+
+
+def source_sha(fname):
+    """SHA-256 of a kernel source plus the shared device header."""
+    h = hashlib.sha256()
+    for f in (fname, "device_common.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(phase):
+    """Measured HBM bytes per launch for `phase` from the committed profile
+    summary, or None when it is missing or was taken on other sources."""
+    try:
+        text = open(PROFILE_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"^traffic-json: (\{.*\})$", text, flags=re.M)
+    if not m:
+        return None
+    entry = json.loads(m.group(1)).get(phase)
+    if not entry or entry.get("source_sha") != source_sha(PHASE_KERNELS[phase][1]):
+        return None
+    return entry
 
 
 def parse():
@@ -39,6 +86,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (to scale HBM byte counters) and exit")
+    p.add_argument("--rocprof-summary", metavar="DIR",
+                   help="summarise rocprofv3 output under DIR (kernel trace + FETCH_SIZE / WRITE_SIZE passes "
+                        "of this benchmark and of --calibrate-copy) and exit")
     return p.parse_args()
 
 
@@ -60,6 +110,9 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -133,9 +186,9 @@ def main():
     gemm_bytes = sum(M * L["k"] + L["n"] * L["k"] + 2 * M * L["n"] + L["xs"].numel() * 4 + L["ws"].numel() * 4
                      for L in layers)
     kernels = {
-        "requant": ("quant_weight_kernel", requant_bytes, 0),
-        "act_quant": ("quant_act_kernel", act_bytes, 0),
-        "gemm": ("gemm_kernel", gemm_bytes, gemm_flops),
+        "requant": (PHASE_KERNELS["requant"][0], requant_bytes, 0),
+        "act_quant": (PHASE_KERNELS["act_quant"][0], act_bytes, 0),
+        "gemm": (PHASE_KERNELS["gemm"][0], gemm_bytes, gemm_flops),
     }
     roof_all = {}
     for p in phases:
@@ -147,8 +200,10 @@ def main():
             ach, peak, unit, bound = flops / ms / 1e9, FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
         else:
             ach, peak, unit, bound = byt / ms / 1e6, HBM_PEAK_GBPS, "GB/s", "hbm"
+        tr = committed_traffic(p)
         roof_all[p] = {"bound": bound, "kernel": name, "achieved": round(ach, 1), "peak": peak, "unit": unit,
-                       "frac": round(ach / peak, 4), "traffic": None, "avg_launch_us": round(launch_us, 2),
+                       "frac": round(ach / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
+                       "avg_launch_us": round(launch_us, 2),
                        "launches_per_step": len(layers), "algorithmic_bytes_per_launch_avg": int(byt / len(layers)),
                        "flops_per_launch_avg": int(flops / len(layers))}
         if flops:
@@ -355,3 +410,121 @@ def cpu_baseline(layers, m, gemm_flops, requant_bytes):
         par["gemm"][L["name"]] = {"rel_fro": round(rel_fro, 6), "rel_max": round(rel_max, 6),
                                   "exact_bf16_frac": round(exact, 4), "pass": rel_fro <= 1e-2 and rel_max <= 1e-2}
     return base, par
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summary (kernel trace + HBM byte counters)
+# ---------------------------------------------------------------------------
+
+def _csv_rows(pattern):
+    rows = []
+    for f in sorted(glob.glob(pattern, recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(kernel_name):
+    """Kernel name without the namespace prefix and the parameter list."""
+    n = re.sub(r"^void ", "", kernel_name)
+    n = n.replace("fp8bq::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(n):  # cut at the '(' of the parameter list (outside template brackets)
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def _phase_of(kernel_name):
+    for p, (prefix, _) in PHASE_KERNELS.items():
+        if prefix in kernel_name:
+            return p
+    return None
+
+
+def step_algorithmic_bytes(M=256):
+    """Average algorithmic HBM bytes per launch of each phase of the decode step."""
+    sys.path.insert(0, ROOT)
+    from synthetic import LAYER_SHAPES_QWEN3_8B
+
+    rq = aq = gm = 0
+    for _, n, k in LAYER_SHAPES_QWEN3_8B:
+        ws = (n // 128) * (k // 128) * 4
+        xs = M * (k // 128) * 4
+        rq += n * k * 3 + ws
+        aq += M * k * 3 + xs
+        gm += M * k + n * k + 2 * M * n + xs + ws
+    L = len(LAYER_SHAPES_QWEN3_8B)
+    return {"requant": rq / L, "act_quant": aq / L, "gemm": gm / L}
+
+
+def rocprof_summary(d):
+    """Markdown summary of the rocprofv3 runs under `d`:
+      d/kt/**/*kernel_stats.csv           --kernel-trace --stats of this benchmark
+      d/fetch/**/*counter_collection.csv  --pmc FETCH_SIZE of this benchmark
+      d/write/**/*counter_collection.csv  --pmc WRITE_SIZE of this benchmark
+      d/copy_fetch, d/copy_write          the same counters for --calibrate-copy
+    Counter values are KiB per dispatch; each is scaled by (bytes the copy
+    really moves) / (what the counter reads for the copy)."""
+    lines = []
+    stats = _csv_rows(os.path.join(d, "kt", "**", "*kernel_stats.csv"))
+    lines.append("| kernel | calls | avg duration (us) | total (ms) |")
+    lines.append("|---|---|---|---|")
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        short = _short(r["Name"])
+        lines.append("| `%s` | %s | %.2f | %.3f |" % (short[:110], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                      float(r["TotalDurationNs"]) / 1e6))
+
+    def per_dispatch(sub, counter):
+        vals = {}
+        for r in _csv_rows(os.path.join(d, sub, "**", "*counter_collection.csv")):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    copy_bytes = float(1 << 30)
+    scale = {}
+    for sub, counter in (("copy_fetch", "FETCH_SIZE"), ("copy_write", "WRITE_SIZE")):
+        v = [x for name, xs in per_dispatch(sub, counter).items() if "copyBuffer" in name for x in xs]
+        scale[counter] = copy_bytes / (sum(v) / len(v)) if v else None
+    lines.append("")
+    lines.append("Copy calibration (1 GiB read + 1 GiB written per launch): FETCH_SIZE scale %s, "
+                 "WRITE_SIZE scale %s." % tuple("%.3f" % scale[c] if scale[c] else "n/a"
+                                                  for c in ("FETCH_SIZE", "WRITE_SIZE")))
+    lines.append("")
+    lines.append("| kernel | dispatches | HBM read / launch (MB) | HBM write / launch (MB) |")
+    lines.append("|---|---|---|---|")
+    fetch = per_dispatch("fetch", "FETCH_SIZE")
+    write = per_dispatch("write", "WRITE_SIZE")
+    traffic = {}
+    for name in sorted(set(fetch) | set(write)):
+        p = _phase_of(name)
+        f = fetch.get(name, [])
+        w = write.get(name, [])
+        fr = sum(f) / len(f) * (scale["FETCH_SIZE"] or float("nan")) if f else float("nan")
+        wr = sum(w) / len(w) * (scale["WRITE_SIZE"] or float("nan")) if w else float("nan")
+        lines.append("| `%s` | %d | %.2f | %.2f |" % (_short(name)[:110], max(len(f), len(w)),
+                                                      fr / 1e6, wr / 1e6))
+        if p and f and w:
+            t = traffic.setdefault(p, {"n": 0, "bytes": 0.0})
+            t["n"] += 1
+            t["bytes"] += fr + wr
+    out = {p: {"bytes_per_launch": int(t["bytes"] / t["n"]), "source_sha": source_sha(PHASE_KERNELS[p][1])}
+           for p, t in traffic.items()}
+    algo = step_algorithmic_bytes()
+    lines.append("")
+    lines.append("| phase (decode step) | measured HBM bytes / launch (MB) | algorithmic bytes / launch (MB) | ratio |")
+    lines.append("|---|---|---|---|")
+    for p, v in sorted(out.items()):
+        a = algo[p]
+        lines.append("| %s | %.2f | %.2f | %.3f |" % (p, v["bytes_per_launch"] / 1e6, a / 1e6, v["bytes_per_launch"] / a))
+    lines.append("")
+    lines.append("traffic-json: " + json.dumps(out, sort_keys=True))
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()

@@ -28,6 +28,10 @@ fp8bq_status check_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Largest GEMM K: the GEMM kernels address an operand panel of at most 256
+// rows x K bytes with 32-bit buffer offsets.
+constexpr int64_t kMaxGemmK = int64_t(1) << 22;
+
 // a * b without int64 overflow (both >= 0)
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a == 0 || b == 0) {
@@ -52,7 +56,7 @@ const char* fp8bq_status_string(fp8bq_status s) {
   switch (s) {
     case FP8BQ_OK: return "ok";
     case FP8BQ_ERR_NULL_PTR: return "null pointer for a non-empty tensor";
-    case FP8BQ_ERR_BAD_SHAPE: return "invalid shape (negative size, K not a multiple of 128, or size overflow)";
+    case FP8BQ_ERR_BAD_SHAPE: return "invalid shape (negative size, GEMM K not a multiple of 128 or above 2^22, or size overflow)";
     case FP8BQ_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
     case FP8BQ_ERR_LAUNCH: return "kernel launch failed";
     case FP8BQ_ERR_DEVICE: return "current device is not an AMD gfx950 GPU";
@@ -101,7 +105,7 @@ fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, c
                                    const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
                                    void* stream) {
   try {
-    if (M < 0 || N < 0 || K < 0 || (K % 128) != 0) return FP8BQ_ERR_BAD_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
     int64_t mk, nk, mn, bytes;
     if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, &mn) || !mul_ok(mn, 2, &bytes))
       return FP8BQ_ERR_BAD_SHAPE;
@@ -125,7 +129,7 @@ fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_
                                            const float* w_scale, const int32_t* group_offsets, uint16_t* y_bf16,
                                            int64_t M_total, int64_t N, int64_t K, int64_t G, void* stream) {
   try {
-    if (M_total < 0 || N < 0 || K < 0 || G < 0 || (K % 128) != 0) return FP8BQ_ERR_BAD_SHAPE;
+    if (M_total < 0 || N < 0 || K < 0 || G < 0 || (K % 128) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
     int64_t mk, nk, gnk, mn, bytes;
     if (!mul_ok(M_total, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(nk, G, &gnk) || !mul_ok(M_total, N, &mn) ||
         !mul_ok(mn, 2, &bytes))

@@ -32,6 +32,7 @@
 // Tiles are ordered so that the workgroups resident on one XCD at a time
 // (consecutive workgroup ids of the same id % 8) share weight and
 // activation panels in that XCD's L2.
+#include <cmath>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -200,22 +201,26 @@ __device__ __forceinline__ void store4(uint16_t* __restrict__ y, int64_t N, int6
 // MFMA fragments read back with ds_read_b128.  Waves never share LDS data,
 // so the K loop has no workgroup barrier.
 // ---------------------------------------------------------------------------
-template <int BN, int BM>
+template <int BN, int BM, int NW>
 struct Skinny {
   static constexpr int TN = BN / 16, TM = BM / 16;
   static constexpr int kRows = BN + BM;                 // rows staged per K-block
   static constexpr int kLoads = kRows / 8;              // 16-byte loads per lane per K-block
   static constexpr int kSlice = kRows * kBlock;         // LDS bytes per wave
-  static constexpr int kRed = 4 * BN * BM * 4;          // four partial tiles, FP32
-  static constexpr int kLdsBytes = (4 * kSlice > kRed) ? 4 * kSlice : kRed;
-  static constexpr int kWavesPerSimd = 1;               // one workgroup per CU; registers to 512
+  static constexpr int kRed = NW * BN * BM * 4;         // the waves' partial tiles, FP32
+  static constexpr int kLdsBytes = (NW * kSlice > kRed) ? NW * kSlice : kRed;
+  static constexpr int kThreadsPerWg = 64 * NW;
+  static constexpr int kWavesPerSimd = NW / 4;
+  static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
+  static constexpr bool kRotate = true;
 
   struct Stage {
     u32x4 v[kLoads];
     float sav[TM], swv[TN];
   };
 
-  __device__ static __forceinline__ void run(const Tile& t, float* red) {
+  __device__ static __forceinline__ void run(const Tile& t, uint8_t* smem) {
+    float* red = reinterpret_cast<float*>(smem);
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int64_t K = t.K;
@@ -273,7 +278,7 @@ struct Skinny {
           [&](int i, int j) { return s.sav[j] * s.swv[i]; });
     };
 
-    // this wave's K-blocks: wave, wave + 4, ...  Stage sX holds the
+    // this wave's K-blocks: wave, wave + NW, ...  Stage sX holds the
     // registers of the next K-block while the LDS slice holds the current.
     // Prefetches past the last K-block re-read the last one (clamped).
     const int kb_last = KB - 1;
@@ -285,26 +290,26 @@ struct Skinny {
       load_stage(s0, kb);
       order_fence();
       store_stage(s0);
-      load_stage(s1, nxt(kb + 4));
+      load_stage(s1, nxt(kb + NW));
       order_fence();
     }
-    for (; kb + 4 < KB; kb += 8) {
+    for (; kb + NW < KB; kb += 2 * NW) {
       compute(s0);                      // K-block kb from the slice, scales from s0
       order_fence();
-      load_stage(s0, nxt(kb + 8));
+      load_stage(s0, nxt(kb + 2 * NW));
       order_fence();
-      store_stage(s1);                  // K-block kb + 4 into the slice
+      store_stage(s1);                  // K-block kb + NW into the slice
       order_fence();
       compute(s1);
       order_fence();
-      load_stage(s1, nxt(kb + 12));
+      load_stage(s1, nxt(kb + 3 * NW));
       order_fence();
-      store_stage(s0);                  // K-block kb + 8
+      store_stage(s0);                  // K-block kb + 2 NW
       order_fence();
     }
     if (kb < KB) compute(s0);
 
-    // Sum the four waves' partial tiles through LDS; thread t then owns 16
+    // Sum the waves' partial tiles through LDS; thread t then owns 16
     // consecutive floats of the tile in fragment order.
     __syncthreads();  // every wave is done with its staging slice
     float* mine = red + wave * (BN * BM);
@@ -315,8 +320,8 @@ struct Skinny {
     __syncthreads();
     constexpr int kGroups = BN * BM / 16;  // groups of 16 floats: 4 lanes x 4 values of one (i, j)
 #pragma unroll
-    for (int q = 0; q < (kGroups + kThreads - 1) / kThreads; ++q) {
-      const int gi = q * kThreads + threadIdx.x;
+    for (int q = 0; q < (kGroups + kThreadsPerWg - 1) / kThreadsPerWg; ++q) {
+      const int gi = q * kThreadsPerWg + threadIdx.x;
       if (gi >= kGroups) break;
       const int base = gi * 16;
       v4f sum[4];
@@ -324,7 +329,7 @@ struct Skinny {
       for (int u = 0; u < 4; ++u) {
         sum[u] = *reinterpret_cast<const v4f*>(red + base + 4 * u);
 #pragma unroll
-        for (int w2 = 1; w2 < 4; ++w2) sum[u] += *reinterpret_cast<const v4f*>(red + w2 * (BN * BM) + base + 4 * u);
+        for (int w2 = 1; w2 < NW; ++w2) sum[u] += *reinterpret_cast<const v4f*>(red + w2 * (BN * BM) + base + 4 * u);
       }
       const int ij = base / 256, l0 = (base / 4) % 64;
       const int i = ij / TM, j = ij % TM;
@@ -340,44 +345,67 @@ struct Skinny {
 };
 
 // ---------------------------------------------------------------------------
-// wide: 256 (n) x 256 (m) tile, 8 waves (2 per SIMD, so one wave's MFMAs
-// fill the other's dependency stalls) in a 2 (n) x 4 (m) grid, 128 x 64
-// each.  Both operands of a K-block (256 weight rows + 256 activation rows,
-// 64 KB) go global -> LDS directly (buffer_load ... lds, 16 bytes per lane,
-// 8 lanes per 128-byte row), double-buffered, so no VGPRs hold staging
-// data; fragments are read with ds_read_b128.
+// panel<BN, BM, WGN, WGM, S>: a BN (n) x BM (m) tile per 8-wave workgroup
+// (two waves per SIMD, so one wave's MFMAs fill the other's stalls), waves
+// in a WGN (n) x WGM (m) grid.  Both operands of a K-block (BN weight rows
+// + BM activation rows, 128 bytes each) go global -> LDS directly
+// (buffer_load ... lds, 16 bytes per lane, 8 lanes per 128-byte row) into
+// a ring of S stages, so no VGPRs hold staging data; fragments are read
+// with ds_read_b128.
 // Phase k: wait for this wave's loads of K-block k; barrier (everyone's
-// data has landed, and everyone is done with the other buffer); compute k
-// while issuing the loads of k+1 into the other buffer between its MFMAs.
+// data has landed, and everyone is done with the stage read in phase k-1);
+// compute k while issuing the loads of K-block k + S - 1 into that stage
+// between the MFMAs.
 // ---------------------------------------------------------------------------
-struct Wide {
-  static constexpr int BN = 256, BM = 256, TN = 8, TM = 4;
-  static constexpr int kThreadsW = 512;
+template <int BN_, int BM_, int WGN, int WGM, int S>
+struct Panel {
+  static constexpr int BN = BN_, BM = BM_;
+  static_assert(WGN * WGM == 8, "eight waves");
+  static constexpr int WNR = BN / WGN, WMR = BM / WGM;  // rows of a wave's tile
+  static constexpr int TN = WNR / 16, TM = WMR / 16;
+  static_assert(WNR % 16 == 0 && WMR % 16 == 0 && WNR <= 128, "wave tile");
+  static_assert(BN % 64 == 0 && BM % 64 == 0, "each load instruction covers 8 rows of one operand, 8 waves");
   static constexpr int kRows = BN + BM;
-  static constexpr int kStage = kRows * kBlock;            // 64 KB
-  static constexpr int kLdsBytes = 2 * kStage;              // double buffer
+  static constexpr int kLoads = kRows / 64;             // load instructions per wave per K-block
+  static constexpr int kStage = kRows * kBlock;
+  static constexpr int kLdsBytes = S * kStage;
+  static_assert(S == 2 || S == 3, "stages");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+  static constexpr int kThreadsPerWg = 512;
   static constexpr int kWavesPerSimd = 2;
+  static constexpr bool kRotate = false;
+  // a wave's weight rows lie in one 128-row scale block when tiles start at
+  // multiples of 128 and the wave's share divides 128
+  static constexpr bool kOneScaleBlock = (BN % kBlock == 0) && (kBlock % WNR == 0);
 
   __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) {
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wn = wave & 1, wm = wave >> 1;                    // 2 x 4 wave grid
+    const int wn = wave % WGN, wm = wave / WGN;
     const int64_t K = t.K;
     const int KB = (int)(K / kBlock);
     const int64_t n_hi = (t.n0 + BN < t.N) ? t.n0 + BN : t.N;
-    // this wave's 128 weight rows form one scale block (n0 is a multiple of 256)
-    int64_t nb_row = t.n0 + wn * 128;
-    nb_row = nb_row < t.N ? nb_row : t.N - 1;
-    const auto swr = make_rsrc(t.sw + (nb_row / kBlock) * KB, (int64_t)KB * 4);
+    // weight scale blocks of this wave's rows: nb0, and nb0 + 1 for the
+    // fragments in hi_mask (only when a wave's rows can straddle a block)
+    const int64_t NBm1 = (t.N - 1) / kBlock;
+    const int64_t wrow0 = t.n0 + wn * WNR;
+    const int64_t nb0 = ((wrow0 < t.N) ? wrow0 : t.N - 1) / kBlock;
+    const int64_t nb1 = nb0 + 1 < NBm1 ? nb0 + 1 : NBm1;
+    const auto swr0 = make_rsrc(t.sw + nb0 * KB, (int64_t)KB * 4);
+    const auto swr1 = make_rsrc(t.sw + nb1 * KB, (int64_t)KB * 4);
+    uint32_t hi_mask = 0;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      if ((wrow0 + i * 16) / kBlock > nb0) hi_mask |= 1u << i;
     const auto wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
     const auto ar = make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
-    const int64_t am_lo = t.m_lo + wm * 64;  // this wave's activation rows (scales)
-    const int64_t am_hi = (am_lo + 64 < t.m_hi) ? am_lo + 64 : t.m_hi;
+    const int64_t am_lo = t.m_lo + wm * WMR;  // this wave's activation rows (scales)
+    const int64_t am_hi = (am_lo + WMR < t.m_hi) ? am_lo + WMR : t.m_hi;
     const int64_t arows = am_hi > am_lo ? am_hi - am_lo : 0;
     const auto sr = make_rsrc(t.sa + am_lo * KB, arows * KB * 4);
     const int svoff = r16 * KB * 4;  // + 16 j KB 4
 
-    // DMA staging: load q (0..7) of wave w fills stage rows R0..R0+7 with
+    // DMA staging: load q of wave w fills stage rows R0..R0+7 with
     // R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at physical chunk
     // l%8, so it fetches logical chunk (l%8) ^ (l/8) (the XOR swizzle).
     const int dvoff = (lane >> 3) * (int)K + (((lane & 7) ^ (lane >> 3)) << 4);
@@ -389,114 +417,118 @@ struct Wide {
 #pragma unroll
       for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    auto rotk = [&](int step) {  // rotated K-block id, step < KB
-      const int kb = step + t.rot;
-      return kb < KB ? kb : kb - KB;
-    };
-    auto dma_q = [&](int q, int step, uint8_t* buf) {
-      const int koff = rotk(step) * kBlock;
+    auto dma_q = [&](int q, int kb, uint8_t* buf) {
+      const int koff = kb * kBlock;
       const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
       auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
-      if (q < 4)  // stage rows 0..255: weight rows n0 + r0 ..
+      if (q < BN / 64)  // stage rows 0..BN-1: weight rows n0 + r0 ..
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff, koff + r0 * (int)K, 0, 0);
-      else        // stage rows 256..511: activation rows m_lo + r0 - 256 ..
+      else              // stage rows BN..: activation rows m_lo + r0 - BN ..
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff, koff + (r0 - BN) * (int)K, 0, 0);
     };
-    // Per-K-block scales of this wave's 64 activation rows and of its weight
-    // block, fetched one phase ahead with vector loads (tracked by vmcnt, so
-    // using them never waits on loads issued after them) and multiplied only
-    // when the phase that needs them starts.
+    // Per-K-block scales of this wave's activation rows and weight block(s),
+    // fetched one phase ahead with vector loads (tracked by vmcnt, so using
+    // them never waits on loads issued after them) and multiplied only when
+    // the phase that needs them starts.
     struct Scales {
-      float sa[TM], sw;
+      float sa[TM], sw0, sw1;
     };
-    auto load_scales = [&](Scales& c, int step) {
-      const int kb = rotk(step);
-      c.sw = bload_f32(swr, 0, kb * 4);
+    auto load_scales = [&](Scales& c, int kb) {
+      c.sw0 = bload_f32(swr0, 0, kb * 4);
+      c.sw1 = kOneScaleBlock ? c.sw0 : bload_f32(swr1, 0, kb * 4);
 #pragma unroll
       for (int j = 0; j < TM; ++j) c.sa[j] = bload_f32(sr, svoff, kb * 4 + j * 16 * KB * 4);
     };
     constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
-    auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * 128 + i * 16); };
+    auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * WNR + i * 16); };
     // The first fragments of a phase, read right after its barrier; the
     // first MFMA's two operands go first so that it waits for them only.
     auto first_frags = [&](v8i (&fa)[TM], v8i (&fw)[kAhead + 1], const uint8_t* buf) {
       fw[0] = load_w(buf, 0);
-      fa[0] = fl(buf, BN + wm * 64);
+      fa[0] = fl(buf, BN + wm * WMR);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 1; j < TM; ++j) fa[j] = fl(buf, BN + wm * 64 + j * 16);
+      for (int j = 1; j < TM; ++j) fa[j] = fl(buf, BN + wm * WMR + j * 16);
 #pragma unroll
-      for (int p = 1; p < kAhead; ++p) fw[p] = load_w(buf, p);
+      for (int p = 1; p < kAhead && p < TN; ++p) fw[p] = load_w(buf, p);
     };
-    // One phase: the product of the K-block in `buf`, with the eight loads of
-    // K-block `step` into `dst` issued after every second MFMA of its first
-    // half (spreading them keeps the L2 and LDS-write traffic from arriving
-    // as one burst right after the barrier).  kLoad false: no loads.
-    auto phase = [&](auto load_tag, const Scales& sc, const uint8_t* buf, int step, uint8_t* dst) {
+    // One phase: the product of the K-block in `buf`, with the loads of
+    // K-block `kb` into `dst` issued after every second MFMA (after every
+    // MFMA when there are few), so that the L2 and LDS-write traffic does
+    // not arrive as one burst right after the barrier.  kLoad false: no loads.
+    constexpr int kT = TN * TM;
+    constexpr int kEvery = (kT >= 2 * kLoads) ? 2 : 1;
+    static_assert(kT * 1 >= kLoads, "enough MFMAs to carry the loads");
+    auto phase = [&](auto load_tag, const Scales& sc, const uint8_t* buf, int kb, uint8_t* dst) {
       constexpr bool kLoad = decltype(load_tag)::value;
       v8i fa[TM], fw[kAhead + 1];
       first_frags(fa, fw, buf);
-      float c[TM];
+      float c0[TM], c1[TM];
 #pragma unroll
-      for (int j = 0; j < TM; ++j) c[j] = sc.sa[j] * sc.sw;
+      for (int j = 0; j < TM; ++j) {
+        c0[j] = sc.sa[j] * sc.sw0;
+        c1[j] = kOneScaleBlock ? c0[j] : sc.sa[j] * sc.sw1;
+      }
       tile_product<TN, TM, 2, kAhead>(
-          acc, fa, fw, [&](int i) { return load_w(buf, i); }, [&](int, int j) { return c[j]; },
-          [&](int t) {
-            if (!kLoad || (t & 1) || t >= 16) return false;
-            dma_q(t >> 1, step, dst);
+          acc, fa, fw, [&](int i) { return load_w(buf, i); },
+          [&](int i, int j) { return (kOneScaleBlock || !((hi_mask >> i) & 1u)) ? c0[j] : c1[j]; },
+          [&](int tt) {
+            if (!kLoad || tt % kEvery != 0 || tt / kEvery >= kLoads) return false;
+            dma_q(tt / kEvery, kb, dst);
             return true;
           });
     };
     // The compiler does not track LDS writes by buffer_load ... lds: wait
-    // for them explicitly before the barrier that publishes the buffer.
-    auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    // for them explicitly before the barrier that publishes the stage.  With
+    // three stages the loads of the next K-block may stay in flight.
+    auto wait_stage = [&]() {
+      if constexpr (S == 2)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+    };
+    auto wait_all = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-    uint8_t* buf0 = lds;
-    uint8_t* buf1 = lds + kStage;
     const int kb_last = KB - 1;
-    auto nxt = [&](int step) { return step < KB ? step : kb_last; };  // clamped prefetch
-    Scales c0, c1;
+    auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };  // clamped prefetch
+    Scales sc_next;
     if (KB > 0) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dma_q(q, 0, buf0);
-      load_scales(c0, 0);
+      for (int q = 0; q < kLoads; ++q) dma_q(q, 0, lds);
+      load_scales(sc_next, 0);
+      if constexpr (S == 3) {
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) dma_q(q, nxt(1), lds + kStage);
+      }
     }
-    // Phase k: wait for this wave's loads of K-block k, barrier (all loads of
-    // k have landed and every wave is done with the other buffer), then
-    // compute k while loading k + 1 into the other buffer.  Loads past the
-    // last K-block re-load it into the buffer nobody reads again, keeping
-    // the loop body free of branches.
-    int k = 0;
-    for (; k + 1 < KB; k += 2) {
-      wait_dma();
-      __syncthreads();  // buf0 holds K-block k; buf1 is free
-      load_scales(c1, k + 1);
+    // Loads past the last K-block re-load it into a stage nobody reads
+    // again, keeping the loop body free of branches.
+    int cur = 0;  // stage of K-block k
+    for (int k = 0; k < KB; ++k) {
+      wait_stage();
+      __syncthreads();  // stage cur holds K-block k; stage cur - 1 is free
+      const Scales sc = sc_next;
+      load_scales(sc_next, nxt(k + 1));
+      const int fill = (cur == 0) ? S - 1 : cur - 1;
       order_fence();
-      phase(std::true_type{}, c0, buf0, k + 1, buf1);
+      phase(std::true_type{}, sc, lds + cur * kStage, nxt(k + S - 1), lds + fill * kStage);
       order_fence();
-      wait_dma();
-      __syncthreads();  // buf1 holds K-block k+1; buf0 is free
-      load_scales(c0, nxt(k + 2));
-      order_fence();
-      phase(std::true_type{}, c1, buf1, nxt(k + 2), buf0);
-      order_fence();
+      cur = (cur + 1 == S) ? 0 : cur + 1;
     }
-    if (k < KB) {
-      wait_dma();
-      __syncthreads();
-      phase(std::false_type{}, c0, buf0, 0, buf1);
-    }
-    wait_dma();  // no LDS write may be in flight when the workgroup ends
+    wait_all();  // no LDS write may be in flight when the workgroup ends
 
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      const int64_t m = t.m_lo + wm * 64 + j * 16 + r16;
+      const int64_t m = t.m_lo + wm * WMR + j * 16 + r16;
       if (m >= t.m_hi) continue;
 #pragma unroll
-      for (int i = 0; i < TN; ++i) store4(t.y, t.N, m, t.n0 + wn * 128 + i * 16 + g * 4, acc[i][j]);
+      for (int i = 0; i < TN; ++i) store4(t.y, t.N, m, t.n0 + wn * WNR + i * 16 + g * 4, acc[i][j]);
     }
   }
 };
+
+using Wide = Panel<256, 256, 2, 4, 2>;
+using DecodePanel = Panel<128, 256, 2, 4, 3>;
 
 // ---------------------------------------------------------------------------
 // Tile order: XCD-aware remap of the workgroup id, then groups of kGroupM
@@ -522,10 +554,7 @@ __device__ __forceinline__ void tile_of(int64_t L, int64_t tiles_m, int64_t tile
 
 template <class Kern>
 constexpr int threads_of() {
-  if constexpr (std::is_same<Kern, Wide>::value)
-    return Wide::kThreadsW;
-  else
-    return kThreads;
+  return Kern::kThreadsPerWg;
 }
 
 template <class Kern, int BN, int BM>
@@ -545,11 +574,8 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   t.m_hi = (t.m_lo + BM < M) ? t.m_lo + BM : M;
   t.n0 = tn * BN;
   t.N = N; t.K = K;
-  t.rot = std::is_same<Kern, Wide>::value ? 0 : (int)((L * 4) % (K / kBlock > 0 ? K / kBlock : 1));
-  if constexpr (std::is_same<Kern, Wide>::value)
-    Wide::run(t, smem);
-  else
-    Kern::run(t, reinterpret_cast<float*>(smem));
+  t.rot = Kern::kRotate ? (int)((L * 4) % (K / kBlock > 0 ? K / kBlock : 1)) : 0;
+  Kern::run(t, smem);
 }
 
 // Grouped form: workgroup slot s is mapped to (expert, m-tile) by a prefix
@@ -619,19 +645,16 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   t.n0 = tn * BN;
   t.N = N; t.K = K;
   t.rot = 0;
-  if constexpr (std::is_same<Kern, Wide>::value)
-    Wide::run(t, smem);
-  else
-    Kern::run(t, reinterpret_cast<float*>(smem));
+  Kern::run(t, smem);
 }
 
-enum class Cfg { kSkinny64x64, kSkinny96x64, kWide };
+enum class Cfg { kSkinny64x64, kSkinny96x64, kWide, kDecodePanel };
 
 // Per-workgroup cycle estimate: operand bytes through L1 (64 B/clk/CU) vs
 // FP8 MFMA (8192 FLOP/clk/CU), times the rounds of workgroups over 256 CUs.
 double est_cycles(int64_t M, int64_t N, int64_t K, int bn, int bm, double cus) {
   const double tiles = (double)((N + bn - 1) / bn) * (double)((M + bm - 1) / bm);
-  const double rounds = tiles / cus < 1.0 ? 1.0 : (tiles + cus - 1) / cus;
+  const double rounds = std::ceil(tiles / cus);  // waves of workgroups over the CUs
   const double l1 = (double)(bn + bm) * (double)K / 64.0;
   const double mfma = 2.0 * bn * bm * (double)K / 8192.0;
   return rounds * (l1 > mfma ? l1 : mfma);
@@ -639,6 +662,9 @@ double est_cycles(int64_t M, int64_t N, int64_t K, int bn, int bm, double cus) {
 
 Cfg choose(int64_t M, int64_t N, int64_t K) {
   const double cus = 256.0;
+  // Few activation rows but many weight rows: one 128 x 256 panel covers
+  // every row of the activation panel, so each weight row is read once.
+  if (M <= DecodePanel::BM && (N + DecodePanel::BN - 1) / DecodePanel::BN >= 160) return Cfg::kDecodePanel;
   double best = est_cycles(M, N, K, Wide::BN, Wide::BM, cus);
   Cfg c = Cfg::kWide;
   const double s64 = est_cycles(M, N, K, 64, 64, cus) * 1.05;  // partial-tile reduction overhead
@@ -666,9 +692,11 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
   if (M == 0 || N == 0) return hipSuccess;
   switch (choose(M, N, K)) {
     case Cfg::kSkinny64x64:
-      return launch_dense_cfg<Skinny<64, 64>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
+      return launch_dense_cfg<Skinny<64, 64, 4>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kSkinny96x64:
-      return launch_dense_cfg<Skinny<96, 64>, 96, 64>(a, sa, w, sw, y, M, N, K, stream);
+      return launch_dense_cfg<Skinny<96, 64, 4>, 96, 64>(a, sa, w, sw, y, M, N, K, stream);
+    case Cfg::kDecodePanel:
+      return launch_dense_cfg<DecodePanel, DecodePanel::BN, DecodePanel::BM>(a, sa, w, sw, y, M, N, K, stream);
     default:
       return launch_dense_cfg<Wide, Wide::BN, Wide::BM>(a, sa, w, sw, y, M, N, K, stream);
   }
@@ -682,7 +710,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t*
   const int64_t slots = (M + Wide::BM - 1) / Wide::BM + G;  // >= sum_e ceil(rows_e / BM)
   const int64_t blocks = tiles_n * slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_grouped_kernel<Wide, Wide::BN, Wide::BM>), dim3((unsigned)blocks), dim3(Wide::kThreadsW),
+  hipLaunchKernelGGL((gemm_grouped_kernel<Wide, Wide::BN, Wide::BM>), dim3((unsigned)blocks), dim3(Wide::kThreadsPerWg),
                      (size_t)Wide::kLdsBytes, stream, a, sa, w, sw, offsets, y, M, N, K, (int)G, slots, tiles_n);
   return hipGetLastError();
 }

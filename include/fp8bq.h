@@ -59,7 +59,7 @@ typedef int fp8bq_status;
 enum {
   FP8BQ_OK = 0,
   FP8BQ_ERR_NULL_PTR = 1,   /* a required pointer is NULL while its size is > 0 */
-  FP8BQ_ERR_BAD_SHAPE = 2,  /* negative size, K % 128 != 0 for a GEMM, size overflow */
+  FP8BQ_ERR_BAD_SHAPE = 2,  /* negative size, GEMM K % 128 != 0 or K > 2^22, size overflow */
   FP8BQ_ERR_MISALIGNED = 3, /* a tensor pointer is not 16-byte aligned */
   FP8BQ_ERR_LAUNCH = 4,     /* the HIP runtime rejected a kernel launch */
   FP8BQ_ERR_DEVICE = 5      /* the current device is not gfx950, or no device */
@@ -107,7 +107,8 @@ fp8bq_status quantize_act_per_token_group(const uint16_t* x_bf16, uint8_t* x_fp8
  *   w_fp8   [N][K]  E4M3 weights          w_scale [ceil(N/128)][K/128] float32
  *   y_bf16  [M][N]  BF16 output (round to nearest even)
  *   y[m][n] = sum_k (a_scale[m][k/128] * dec(a[m][k])) * (w_scale[n/128][k/128] * dec(w[n][k]))
- *   M, N >= 0; K >= 0 and K % 128 == 0.  The summation order is
+ *   M, N >= 0; 0 <= K <= 2^22 and K % 128 == 0 (the kernels address a
+ *   256-row operand panel with 32-bit offsets).  The summation order is
  *   unspecified (results agree with the exact value to FP32 accumulation
  *   error before the BF16 rounding).
  */
@@ -129,7 +130,8 @@ fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, c
  *   FP8BQ_ERR_BAD_SHAPE.  The offsets are read on the device only (no
  *   host synchronisation); offsets that break the stated contract give
  *   unspecified output rows but never an out-of-bounds access: every row
- *   index is clamped to [0, M_total).  M_total + 128 * G must fit in int32.
+ *   index is clamped to [0, M_total).  M_total + 128 * G must fit in int32;
+ *   K as for gemm_w8a8_blockscaled.
  */
 fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
                                            const float* w_scale, const int32_t* group_offsets, uint16_t* y_bf16,

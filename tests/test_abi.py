@@ -62,6 +62,10 @@ def test_argument_errors_are_reported_before_any_launch():
     # K not a multiple of 128 for GEMMs
     assert _call("gemm_w8a8_blockscaled", good, good, good, good, good, 4, 4, 100, null) == 2
     assert _call("grouped_gemm_w8a8_blockscaled", good, good, good, good, good, good, 4, 4, 100, 2, null) == 2
+    # GEMM K above the 2^22 limit of the kernels' 32-bit panel offsets
+    assert _call("gemm_w8a8_blockscaled", good, good, good, good, good, 4, 4, (1 << 22) + 128, null) == 2
+    assert _call("grouped_gemm_w8a8_blockscaled", good, good, good, good, good, good, 4, 4, (1 << 22) + 128, 2,
+                 null) == 2
     # size overflow
     assert _call("quantize_weight_blockwise", good, good, good, 1 << 40, 1 << 20, 1 << 20, null) == 2
     # null pointers with non-empty sizes
