@@ -33,6 +33,8 @@
 // (consecutive workgroup ids of the same id % 8) share weight and
 // activation panels in that XCD's L2.
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -45,7 +47,6 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
 // D(16x16, FP32) = A(16x128, E4M3) x B(128x16, E4M3); format selectors 0 = E4M3.
@@ -81,24 +82,11 @@ __device__ __forceinline__ float bload_f32(__amdgpu_buffer_rsrc_t r, int voff, i
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
-// Operand fragment of a 16-row x 128-K tile: lane l holds row (l & 15) and
-// the 16-byte K chunks g = l >> 4 and g + 4 of the K-block.  Every operand
-// uses this same assignment, so the MFMA pairs equal k in A and B.  `voff`
-// is row * K + 16 g within the panel, `koff` = 128 kb.
-__device__ __forceinline__ v8i frag_buf(__amdgpu_buffer_rsrc_t r, int voff, int koff) {
-  return to_v8i(bload16(r, voff, koff), bload16(r, voff + 64, koff));
-}
-
 // LDS tile of 128 rows x 128 bytes, 16-byte chunk c of row r stored at
 // chunk position c ^ (r & 7): the 8 lanes of one LDS cycle read 8 rows at
 // the same logical chunk and hit 8 distinct bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBlock + ((chunk ^ (row & 7)) << 4); }
 
-__device__ __forceinline__ v8i frag_lds(const uint8_t* lds, int row, int g) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + swz(row, g));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + swz(row, g + 4));
-  return to_v8i(lo, hi);
-}
 
 // Per-lane byte offsets of the two fragment chunks inside a 16-row group of
 // a swizzled LDS tile ((row0 + r16) & 7 == r16 & 7 for row0 % 16 == 0), so
@@ -213,6 +201,7 @@ struct Skinny {
   static constexpr int kWavesPerSimd = NW / 4;
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   static constexpr bool kRotate = true;
+  static constexpr int kRotStride = 4;  // keeps each wave's K-block residue class
 
   struct Stage {
     u32x4 v[kLoads];
@@ -221,7 +210,7 @@ struct Skinny {
 
   __device__ static __forceinline__ void run(const Tile& t, uint8_t* smem) {
     float* red = reinterpret_cast<float*>(smem);
-    const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+    const int lane = threadIdx.x & 63, r16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int64_t K = t.K;
     const int KB = (int)(K / kBlock);
@@ -365,7 +354,7 @@ struct Panel {
   static constexpr int TN = WNR / 16, TM = WMR / 16;
   static_assert(WNR % 16 == 0 && WMR % 16 == 0 && WNR <= 128, "wave tile");
   static_assert(BN % 64 == 0 && BM % 64 == 0, "each load instruction covers 8 rows of one operand, 8 waves");
-  static constexpr int kRows = BN + BM;
+  static constexpr int kRows = BN + BM;                 // rows staged per K-block
   static constexpr int kLoads = kRows / 64;             // load instructions per wave per K-block
   static constexpr int kStage = kRows * kBlock;
   static constexpr int kLdsBytes = S * kStage;
@@ -374,6 +363,7 @@ struct Panel {
   static constexpr int kThreadsPerWg = 512;
   static constexpr int kWavesPerSimd = 2;
   static constexpr bool kRotate = false;
+  static constexpr int kRotStride = 1;
   // a wave's weight rows lie in one 128-row scale block when tiles start at
   // multiples of 128 and the wave's share divides 128
   static constexpr bool kOneScaleBlock = (BN % kBlock == 0) && (kBlock % WNR == 0);
@@ -482,10 +472,11 @@ struct Panel {
     // for them explicitly before the barrier that publishes the stage.  With
     // three stages the loads of the next K-block may stay in flight.
     auto wait_stage = [&]() {
+      // the loads of K-block k + 1 have at least (S - 2) * kLoads loads issued after them
       if constexpr (S == 2)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kLoads) : "memory");
     };
     auto wait_all = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -496,10 +487,10 @@ struct Panel {
 #pragma unroll
       for (int q = 0; q < kLoads; ++q) dma_q(q, 0, lds);
       load_scales(sc_next, 0);
-      if constexpr (S == 3) {
 #pragma unroll
-        for (int q = 0; q < kLoads; ++q) dma_q(q, nxt(1), lds + kStage);
-      }
+      for (int st = 1; st < S - 1; ++st)
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) dma_q(q, nxt(st), lds + st * kStage);
     }
     // Loads past the last K-block re-load it into a stage nobody reads
     // again, keeping the loop body free of branches.
@@ -574,7 +565,7 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   t.m_hi = (t.m_lo + BM < M) ? t.m_lo + BM : M;
   t.n0 = tn * BN;
   t.N = N; t.K = K;
-  t.rot = Kern::kRotate ? (int)((L * 4) % (K / kBlock > 0 ? K / kBlock : 1)) : 0;
+  t.rot = Kern::kRotate ? (int)((L * Kern::kRotStride) % (K / kBlock > 0 ? K / kBlock : 1)) : 0;
   Kern::run(t, smem);
 }
 
@@ -687,10 +678,24 @@ hipError_t launch_dense_cfg(const uint8_t* a, const float* sa, const uint8_t* w,
 
 }  // namespace
 
+// Tile override for tests and diagnostics: FP8BQ_GEMM_TILE = skinny64 |
+// skinny96 | wide | decode_panel forces that kernel for every dense GEMM;
+// unset (the default) lets the cost model choose.  Read on every call.
+Cfg tile_for(int64_t M, int64_t N, int64_t K) {
+  const char* e = std::getenv("FP8BQ_GEMM_TILE");
+  if (e != nullptr && *e != '\0') {
+    if (std::strcmp(e, "skinny64") == 0) return Cfg::kSkinny64x64;
+    if (std::strcmp(e, "skinny96") == 0) return Cfg::kSkinny96x64;
+    if (std::strcmp(e, "wide") == 0) return Cfg::kWide;
+    if (std::strcmp(e, "decode_panel") == 0) return Cfg::kDecodePanel;
+  }
+  return choose(M, N, K);
+}
+
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  switch (choose(M, N, K)) {
+  switch (tile_for(M, N, K)) {
     case Cfg::kSkinny64x64:
       return launch_dense_cfg<Skinny<64, 64, 4>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kSkinny96x64:

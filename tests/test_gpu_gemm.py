@@ -68,6 +68,20 @@ def test_gemm_ragged(fb, m, n, k):
     assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw), oracle.gemm_ref(qa, sa, qw, sw))
 
 
+TILES = ["skinny64", "skinny96", "wide", "decode_panel"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("m,n,k", [(1, 1, 128), (37, 130, 256), (130, 300, 384), (257, 129, 1024), (300, 520, 2048)])
+def test_gemm_every_tile_kernel(fb, monkeypatch, tile, m, n, k):
+    """Each tile kernel on ragged shapes and 1..16 K-blocks (odd and even
+    trip counts of the pipelined loops), forced through FP8BQ_GEMM_TILE."""
+    announce("gemm tile", tile, m, n, k)
+    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
+    qa, sa, qw, sw = _oracle_inputs(m, n, k, 90 + m + n)
+    assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw), oracle.gemm_ref(qa, sa, qw, sw))
+
+
 def test_gemm_k_zero_gives_zeros(fb):
     announce("gemm K = 0")
     y = fb.gemm_w8a8_blockscaled(torch.empty((5, 0), dtype=torch.uint8, device="cuda"),
