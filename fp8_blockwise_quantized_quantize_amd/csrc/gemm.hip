@@ -394,6 +394,9 @@ struct Panel {
     const int64_t arows = am_hi > am_lo ? am_hi - am_lo : 0;
     const auto sr = make_rsrc(t.sa + am_lo * KB, arows * KB * 4);
     const int svoff = r16 * KB * 4;  // + 16 j KB 4
+    // a ragged last tile (e.g. an expert's rows past a multiple of BM) can
+    // leave whole waves without a valid activation row: they skip the MFMAs
+    const bool idle = arows == 0;
 
     // DMA staging: load q of wave w fills stage rows R0..R0+7 with
     // R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at physical chunk
@@ -502,7 +505,12 @@ struct Panel {
       load_scales(sc_next, nxt(k + 1));
       const int fill = (cur == 0) ? S - 1 : cur - 1;
       order_fence();
-      phase(std::true_type{}, sc, lds + cur * kStage, nxt(k + S - 1), lds + fill * kStage);
+      if (idle) {  // no valid activation row: only this wave's share of the loads
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) dma_q(q, nxt(k + S - 1), lds + fill * kStage);
+      } else {
+        phase(std::true_type{}, sc, lds + cur * kStage, nxt(k + S - 1), lds + fill * kStage);
+      }
       order_fence();
       cur = (cur + 1 == S) ? 0 : cur + 1;
     }
@@ -676,11 +684,10 @@ hipError_t launch_dense_cfg(const uint8_t* a, const float* sa, const uint8_t* w,
   return hipGetLastError();
 }
 
-}  // namespace
-
 // Tile override for tests and diagnostics: FP8BQ_GEMM_TILE = skinny64 |
-// skinny96 | wide | decode_panel forces that kernel for every dense GEMM;
-// unset (the default) lets the cost model choose.  Read on every call.
+// skinny96 | wide | decode_panel forces that kernel for every dense GEMM
+// (wide | decode_panel for the grouped GEMM); unset (the default) lets the
+// cost model choose.  Read on every call.
 Cfg tile_for(int64_t M, int64_t N, int64_t K) {
   const char* e = std::getenv("FP8BQ_GEMM_TILE");
   if (e != nullptr && *e != '\0') {
@@ -691,6 +698,22 @@ Cfg tile_for(int64_t M, int64_t N, int64_t K) {
   }
   return choose(M, N, K);
 }
+
+template <class Kern>
+hipError_t launch_grouped_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                              const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
+                              hipStream_t stream) {
+  const int64_t tiles_n = (N + Kern::BN - 1) / Kern::BN;
+  const int64_t slots = (M + Kern::BM - 1) / Kern::BM + G;  // >= sum_e ceil(rows_e / BM)
+  const int64_t blocks = tiles_n * slots;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_grouped_kernel<Kern, Kern::BN, Kern::BM>), dim3((unsigned)blocks),
+                     dim3(Kern::kThreadsPerWg), (size_t)Kern::kLdsBytes, stream, a, sa, w, sw, offsets, y, M, N, K,
+                     (int)G, slots, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
                        int64_t N, int64_t K, hipStream_t stream) {
@@ -711,13 +734,11 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t*
                                const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
                                hipStream_t stream) {
   if (M == 0 || N == 0 || G == 0) return hipSuccess;
-  const int64_t tiles_n = (N + Wide::BN - 1) / Wide::BN;
-  const int64_t slots = (M + Wide::BM - 1) / Wide::BM + G;  // >= sum_e ceil(rows_e / BM)
-  const int64_t blocks = tiles_n * slots;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_grouped_kernel<Wide, Wide::BN, Wide::BM>), dim3((unsigned)blocks), dim3(Wide::kThreadsPerWg),
-                     (size_t)Wide::kLdsBytes, stream, a, sa, w, sw, offsets, y, M, N, K, (int)G, slots, tiles_n);
-  return hipGetLastError();
+  // the expert tiles: 128 x 256 panels when the override asks for them
+  const char* e = std::getenv("FP8BQ_GEMM_TILE");
+  if (e != nullptr && std::strcmp(e, "decode_panel") == 0)
+    return launch_grouped_cfg<DecodePanel>(a, sa, w, sw, offsets, y, M, N, K, G, stream);
+  return launch_grouped_cfg<Wide>(a, sa, w, sw, offsets, y, M, N, K, G, stream);
 }
 
 }  // namespace fp8bq

@@ -178,10 +178,12 @@ def gpu_grouped(fb, qa, sa, qw, sw, off):
     return device_to_bits(y)
 
 
+@pytest.mark.parametrize("tile", ["wide", "decode_panel"])
 @pytest.mark.parametrize("counts", [[3, 0, 17, 1, 0], [0, 0, 300, 0], [129], [0, 128, 0, 1, 255, 0, 0, 2],
-                                    [1] * 40])
-def test_grouped_small(fb, counts):
-    announce("grouped small", counts)
+                                    [1] * 40, [257, 511, 70]])
+def test_grouped_small(fb, monkeypatch, tile, counts):
+    announce("grouped small", tile, counts)
+    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
     qa, sa, qw, sw, off = _grouped_oracle_inputs(counts, 256, 384, 50 + len(counts))
     y = gpu_grouped(fb, qa, sa, qw, sw, off)
     ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, off)
