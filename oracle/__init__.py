@@ -32,6 +32,8 @@ Modules
            and 1x128 per-token activation groups.
 ``gemm``   block-scaled GEMM (dequantize, exact product, one BF16 rounding)
            and its ragged grouped (MoE) form.
+``tis``    token-level importance weights of the rollout correction
+           ([FP8-RL summary] §3.4.3): TIS clipping and MIS masking.
 
 Precision readings (the pages leave these open; each is pinned by a test in
 ``tests/test_oracle_*.py``):
@@ -63,6 +65,7 @@ from .gemm import (
     gemm_ref_bf16,
     grouped_gemm_ref,
 )
+from .tis import importance_weights
 
 __all__ = [
     "E4M3_MAX",
@@ -82,4 +85,5 @@ __all__ = [
     "gemm_ref",
     "gemm_ref_bf16",
     "grouped_gemm_ref",
+    "importance_weights",
 ]
