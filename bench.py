@@ -347,7 +347,34 @@ def detail(fb, dev):
                                       "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
     del bufs
     torch.cuda.empty_cache()
+
+    # -- token-level TIS weights of one training batch (512 responses padded
+    #    to 20,000 tokens), fused with the response mask and w * advantage
+    from synthetic import ROLLOUT_TRAIN_BATCH, rollout_batch
+
+    rb = rollout_batch(ROLLOUT_TRAIN_BATCH["responses"], ROLLOUT_TRAIN_BATCH["max_len"], (31, 1))
+    lt, lr, adv = (torch.from_numpy(rb[k]).to(dev) for k in ("logp_train", "logp_rollout", "advantages"))
+    msk = torch.from_numpy(rb["mask"]).to(dev)
+    w = torch.empty_like(lt)
+    wa = torch.empty_like(lt)
+    ms, ms_min = _time_ms(lambda: fb.token_importance_weights(lt, lr, C=2.0, mode="tis", mask=msk, advantages=adv,
+                                                              out=w, out_adv=wa), reps=20)
+    slots, valid = lt.numel(), int(rb["mask"].sum())
+    byt = importance_weight_bytes(slots, valid)
+    gbps = byt / ms / 1e6
+    res["tis_weights_train_batch_512x20000"] = {"tokens": valid, "slots": slots, "bytes": byt,
+                                                "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
+                                                "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
+    del lt, lr, adv, msk, w, wa
+    torch.cuda.empty_cache()
     return res
+
+
+def importance_weight_bytes(slots, valid):
+    """Algorithmic HBM bytes of the fused importance-weight pass: the two
+    log-probs and the advantage of each generated token (12 B), the mask byte
+    and the two float32 outputs of every slot, padding included (9 B)."""
+    return 12 * valid + 9 * slots
 
 
 # ---------------------------------------------------------------------------

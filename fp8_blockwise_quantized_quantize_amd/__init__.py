@@ -29,6 +29,7 @@ __all__ = [
     "gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled",
     "encode_e4m3",
+    "token_importance_weights",
     "status_string",
 ]
 
@@ -43,6 +44,7 @@ EXPORTS = (
     "gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled",
     "fp8bq_encode_e4m3",
+    "token_importance_weights",
 )
 
 
@@ -63,6 +65,7 @@ def _load():
     lib.gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p]
     lib.fp8bq_encode_e4m3.argtypes = [p, p, i64, i32, p]
+    lib.token_importance_weights.argtypes = [p, p, p, p, p, p, i64, ctypes.c_float, i32, p]
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = i32
     return lib
@@ -207,6 +210,47 @@ def encode_e4m3(v, method=1, out=None):
     with torch.cuda.device(v.device):
         _check("fp8bq_encode_e4m3", _lib.fp8bq_encode_e4m3(_ptr(v), _ptr(out), v.numel(), int(method), _stream(v)))
     return out
+
+
+_IW_MODES = {"tis": 0, "mis": 1}
+
+
+def token_importance_weights(logp_train, logp_rollout, C=2.0, mode="tis", mask=None, advantages=None,
+                             out=None, out_adv=None):
+    """Per-token rollout-correction weights w = exp(logp_train - logp_rollout).
+
+    ``mode="tis"`` limits w to [1/C, C]; ``mode="mis"`` sets w = 0 outside
+    that band.  float32 log-probabilities of any one shape (e.g. [responses,
+    max_len]); ``mask`` (bool / uint8, same shape, 0 = padding) zeroes
+    padding; with ``advantages`` the call also returns w * A.  Returns ``w``
+    or ``(w, w * A)``.
+    """
+    if mode not in _IW_MODES:
+        raise ValueError(f"mode must be one of {sorted(_IW_MODES)}")
+    shape = tuple(logp_train.shape)
+    _require(logp_train, "logp_train", torch.float32, shape)
+    dev = logp_train.device
+    _require(logp_rollout, "logp_rollout", torch.float32, shape, dev)
+    if mask is not None:
+        _require(mask, "mask", (torch.bool, torch.uint8), shape, dev)
+        mask = mask.view(torch.uint8)
+    if advantages is not None:
+        _require(advantages, "advantages", torch.float32, shape, dev)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, shape, dev)
+    if advantages is not None:
+        if out_adv is None:
+            out_adv = torch.empty(shape, dtype=torch.float32, device=dev)
+        _require(out_adv, "out_adv", torch.float32, shape, dev)
+    elif out_adv is not None:
+        raise ValueError("out_adv given without advantages")
+    with torch.cuda.device(dev):
+        _check("token_importance_weights",
+               _lib.token_importance_weights(_ptr(logp_train), _ptr(logp_rollout), _ptr(mask), _ptr(advantages),
+                                             _ptr(out), _ptr(out_adv), logp_train.numel(), float(C),
+                                             _IW_MODES[mode], _stream(logp_train)))
+    return out if advantages is None else (out, out_adv)
 
 
 def raw_library():

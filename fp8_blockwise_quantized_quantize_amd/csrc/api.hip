@@ -1,6 +1,7 @@
 // C-ABI layer of libfp8bq.so: argument checks, device check, launches.
 // The contract of every entry point is documented in include/fp8bq.h.
 #include <atomic>
+#include <cmath>
 #include <cstring>
 
 #include "../../include/fp8bq.h"
@@ -32,6 +33,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // rows x K bytes with 32-bit buffer offsets.
 constexpr int64_t kMaxGemmK = int64_t(1) << 22;
 
+// Largest elementwise problem: its one-dimensional grid of 256-lane
+// workgroups, four elements per lane, must stay below 2^31 workgroups.
+constexpr int64_t kMaxElementwise = int64_t(1) << 40;
+
 // a * b without int64 overflow (both >= 0)
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a == 0 || b == 0) {
@@ -60,6 +65,7 @@ const char* fp8bq_status_string(fp8bq_status s) {
     case FP8BQ_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
     case FP8BQ_ERR_LAUNCH: return "kernel launch failed";
     case FP8BQ_ERR_DEVICE: return "current device is not an AMD gfx950 GPU";
+    case FP8BQ_ERR_BAD_ARG: return "invalid scalar argument or option combination";
     default: return "unknown status";
   }
 }
@@ -163,6 +169,32 @@ fp8bq_status fp8bq_encode_e4m3(const float* in, uint8_t* out, int64_t n, int met
     if (st != FP8BQ_OK) return st;
     clear_last_error();
     return launched(fp8bq::launch_encode(in, out, n, method, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status token_importance_weights(const float* logp_train, const float* logp_rollout, const uint8_t* mask,
+                                      const float* advantages, float* weights, float* weighted_adv, int64_t n,
+                                      float C, int mode, void* stream) {
+  try {
+    if (!(C >= 1.0f) || (mode != FP8BQ_IW_TIS && mode != FP8BQ_IW_MIS)) return FP8BQ_ERR_BAD_ARG;
+    if ((advantages == nullptr) != (weighted_adv == nullptr)) return FP8BQ_ERR_BAD_ARG;
+    if (n < 0 || n > kMaxElementwise) return FP8BQ_ERR_BAD_SHAPE;
+    if (n == 0) return FP8BQ_OK;
+    if (!logp_train || !logp_rollout || !weights) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(logp_train) || !aligned16(logp_rollout) || !aligned16(weights) ||
+        (mask && !aligned16(mask)) || (advantages && (!aligned16(advantages) || !aligned16(weighted_adv))))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    // clip bounds and the MIS band edge, each rounded once to float32
+    const float lo = 1.0f / C;
+    const float log_c = static_cast<float>(std::log(static_cast<double>(C)));
+    clear_last_error();
+    return launched(fp8bq::launch_importance_weights(logp_train, logp_rollout, mask, advantages, weights,
+                                                     weighted_adv, n, lo, C, log_c, mode == FP8BQ_IW_MIS,
+                                                     static_cast<hipStream_t>(stream)));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }

@@ -21,4 +21,8 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t*
 
 hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int method, hipStream_t stream);
 
+hipError_t launch_importance_weights(const float* logp_train, const float* logp_rollout, const uint8_t* mask,
+                                     const float* advantages, float* weights, float* weighted_adv, int64_t n,
+                                     float lo, float hi, float log_c, bool mis, hipStream_t stream);
+
 }  // namespace fp8bq

@@ -42,7 +42,8 @@
  *   - Arguments are checked before anything is enqueued.  On error nothing
  *     is enqueued and a non-zero fp8bq_status is returned.  A zero-sized
  *     problem is a successful no-op.  No C++ exception crosses the ABI.
- *   - Inputs must be finite (NaN / Inf input gives unspecified codes).
+ *   - Quantizer and GEMM inputs must be finite (NaN / Inf input gives
+ *     unspecified codes).
  *   - Functions are thread-safe; ordering follows the stream.
  */
 #ifndef FP8BQ_H
@@ -62,7 +63,8 @@ enum {
   FP8BQ_ERR_BAD_SHAPE = 2,  /* negative size, GEMM K % 128 != 0 or K > 2^22, size overflow */
   FP8BQ_ERR_MISALIGNED = 3, /* a tensor pointer is not 16-byte aligned */
   FP8BQ_ERR_LAUNCH = 4,     /* the HIP runtime rejected a kernel launch */
-  FP8BQ_ERR_DEVICE = 5      /* the current device is not gfx950, or no device */
+  FP8BQ_ERR_DEVICE = 5,     /* the current device is not gfx950, or no device */
+  FP8BQ_ERR_BAD_ARG = 6     /* an invalid scalar argument or option combination */
 };
 
 /* Static, human-readable text for a status code (host function). */
@@ -154,6 +156,44 @@ fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_
  *   in [n] float32, out [n] uint8, n >= 0.  Other methods: FP8BQ_ERR_BAD_SHAPE.
  */
 fp8bq_status fp8bq_encode_e4m3(const float* in, uint8_t* out, int64_t n, int method, void* stream);
+
+/*
+ * token_importance_weights -- per-token rollout-correction weights of FP8
+ * rollouts ([FP8-RL summary] §3.4.3 "Train-Inference Mismatch and
+ * Importance-Sampling Correction").  The weight of a sampled token is the
+ * ratio of the training policy's probability to the FP8 rollout policy's,
+ *     w = exp(logp_train - logp_rollout),
+ * and it multiplies the token's advantage in the policy loss.
+ *   mode FP8BQ_IW_TIS: truncated importance sampling, w limited to [1/C, C]
+ *                      (C = 2 in the page's experiments);
+ *   mode FP8BQ_IW_MIS: masked importance sampling (only named on the page;
+ *                      this library's reading): a token whose weight lies
+ *                      outside [1/C, C] gets 0, the others keep w limited to
+ *                      [1/C, C].  The in/out decision is exact in float32:
+ *                      kept iff |fl32(logp_train - logp_rollout)| <= fl32(ln C).
+ *
+ *   logp_train    [n] float32  log-probability of each sampled token under
+ *                              the training (full-precision) policy
+ *   logp_rollout  [n] float32  the same under the FP8 rollout policy
+ *   mask          [n] uint8 or NULL: 0 = padding (w = 0, and w * A = 0),
+ *                 non-zero = a generated token.  NULL: every token counts.
+ *   advantages    [n] float32 or NULL: per-token advantage A
+ *   weights       [n] float32 output w
+ *   weighted_adv  [n] float32 output w * A (+0 wherever w == 0); must be
+ *                 non-NULL exactly when `advantages` is.
+ *   0 <= n <= 2^40 (a [responses][max_len] batch is n = responses * max_len).
+ *   C >= 1 (C = +inf gives untruncated weights); a NaN C, C < 1, another
+ *   mode, or only one of advantages / weighted_adv: FP8BQ_ERR_BAD_ARG.
+ * Error: w carries the error of one float32 exp (the difference of the log
+ * probabilities is kept exactly), then the clip; a NaN log-probability gives
+ * NaN under TIS and 0 under MIS; logp_train = -inf gives 1/C under TIS.
+ * Unlike the quantizers, infinite and NaN inputs are defined here.
+ */
+enum { FP8BQ_IW_TIS = 0, FP8BQ_IW_MIS = 1 };
+
+fp8bq_status token_importance_weights(const float* logp_train, const float* logp_rollout, const uint8_t* mask,
+                                      const float* advantages, float* weights, float* weighted_adv, int64_t n,
+                                      float C, int mode, void* stream);
 
 #ifdef __cplusplus
 }

@@ -88,7 +88,8 @@ def importance_weights(logp_train, logp_rollout, C=2.0, mode=TIS, mask=None, adv
         if m.shape != lt.shape:
             raise ValueError("mask differs in shape")
         w = np.where(m != 0, w, 0.0)
-    w32 = w.astype(np.float32)
+    with np.errstate(over="ignore"):
+        w32 = w.astype(np.float32)                           # beyond the float32 range: inf
     if advantages is None:
         return w32
     a = np.asarray(advantages, dtype=np.float32)

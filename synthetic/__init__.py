@@ -14,6 +14,10 @@ those models' linear-layer shapes stand in for them:
 * MoE routing: logits ~ N(0, 1) [tokens][experts] -> float32 softmax ->
   top-k experts per token (ties to the lower expert index) -> (expert,
   token) pairs sorted by expert then token -> ragged row offsets.
+* rollout batches for the importance weights: padded [responses][max_len]
+  log-probabilities of sampled tokens under the rollout and training
+  policies, a response mask and per-response advantages
+  (``rollout_batch``; see its docstring for the distributions).
 
 Host tensors use numpy's PCG64 (``default_rng([config, tensor, layer])``)
 and torch's CPU BF16 conversion (round to nearest even).  Very large
@@ -31,6 +35,8 @@ from .gen import (
     gather_rows,
     device_bf16_normal,
     f32_to_bf16_bits,
+    ROLLOUT_TRAIN_BATCH,
+    rollout_batch,
 )
 
 __all__ = [
@@ -42,4 +48,6 @@ __all__ = [
     "gather_rows",
     "device_bf16_normal",
     "f32_to_bf16_bits",
+    "ROLLOUT_TRAIN_BATCH",
+    "rollout_batch",
 ]

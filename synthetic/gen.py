@@ -95,3 +95,40 @@ def device_bf16_normal(shape, std, seed, device="cuda", chunk_rows=4096):
         z = torch.randn((r1 - r0, shape[-1]), generator=g, dtype=torch.float32, device=device)
         flat[r0:r1] = (z * std).to(torch.bfloat16)
     return out
+
+
+# Rollout batch of the FP8-RL experiments: 32 prompts x 16 responses per
+# training step, responses of up to 20,000 tokens.
+ROLLOUT_TRAIN_BATCH = {"responses": 32 * 16, "max_len": 20000}
+
+
+def rollout_batch(responses, max_len, seed, mismatch_std=0.08, outlier_frac=0.01, outlier_std=1.0,
+                  pad_value=0.0):
+    """Padded per-token log-probabilities of one batch of sampled responses.
+
+    Returns float32 ``logp_rollout``, ``logp_train``, ``advantages`` and a
+    uint8 ``mask``, each [responses][max_len]:
+
+    * response lengths ~ uniform integers in [max_len // 10, max_len]; the
+      mask is 1 on each response's prefix and 0 on its padding;
+    * rollout log-probs of the sampled tokens -Exp(0.6) (mostly likely
+      tokens, a long tail of unlikely ones);
+    * training log-probs = rollout log-probs + a policy mismatch drawn from
+      N(0, mismatch_std), with a fraction ``outlier_frac`` of tokens drawn
+      from N(0, outlier_std) instead, capped at 0;
+    * one advantage per response ~ N(0, 1), repeated over its tokens;
+    * padding positions hold ``pad_value`` in all three float tensors.
+    """
+    rng = np.random.default_rng(list(seed))
+    lengths = rng.integers(max(1, max_len // 10), max_len + 1, size=responses)
+    mask = (np.arange(max_len)[None, :] < lengths[:, None]).astype(np.uint8)
+    lr = -rng.exponential(0.6, size=(responses, max_len)).astype(np.float32)
+    delta = rng.normal(0.0, mismatch_std, size=(responses, max_len)).astype(np.float32)
+    out = rng.random((responses, max_len)) < outlier_frac
+    delta[out] = rng.normal(0.0, outlier_std, size=int(out.sum())).astype(np.float32)
+    lt = np.minimum(lr + delta, np.float32(0.0)).astype(np.float32)
+    adv = np.repeat(rng.standard_normal(responses).astype(np.float32)[:, None], max_len, axis=1)
+    pad = mask == 0
+    for t in (lr, lt, adv):
+        t[pad] = np.float32(pad_value)
+    return {"logp_rollout": lr, "logp_train": lt, "advantages": adv, "mask": mask, "lengths": lengths}

@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["quantize_weight_blockwise", "quantize_act_per_token_group", "gemm_w8a8_blockscaled",
-              "grouped_gemm_w8a8_blockscaled", "fp8bq_status_string", "fp8bq_encode_e4m3"]:
+              "grouped_gemm_w8a8_blockscaled", "fp8bq_status_string", "fp8bq_encode_e4m3",
+              "token_importance_weights"]:
         assert n in names, names
 
 
@@ -38,7 +39,7 @@ def test_status_strings():
     import fp8_blockwise_quantized_quantize_amd as fb
 
     assert fb.status_string(0) == "ok"
-    for code in range(1, 6):
+    for code in range(1, 7):
         assert fb.status_string(code) not in ("ok", "unknown status")
     assert fb.status_string(99) == "unknown status"
 
@@ -80,6 +81,19 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call("grouped_gemm_w8a8_blockscaled", good, good, good, good, good, good, 4, 4, 128, 0, null) == 2
     # encoder: bad method
     assert _call("fp8bq_encode_e4m3", good, good, 16, 7, null) == 2
+    # importance weights: C < 1, NaN C, bad mode, advantages without output
+    F = ctypes.c_float
+    iw = "token_importance_weights"
+    assert _call(iw, good, good, null, null, good, null, 16, F(0.5), 0, null) == 6
+    assert _call(iw, good, good, null, null, good, null, 16, F(float("nan")), 0, null) == 6
+    assert _call(iw, good, good, null, null, good, null, 16, F(2.0), 2, null) == 6
+    assert _call(iw, good, good, null, good, good, null, 16, F(2.0), 0, null) == 6
+    assert _call(iw, good, good, null, null, good, good, 16, F(2.0), 1, null) == 6
+    assert _call(iw, good, good, null, null, good, null, -1, F(2.0), 0, null) == 2
+    assert _call(iw, good, good, null, null, good, null, (1 << 40) + 1, F(2.0), 0, null) == 2
+    assert _call(iw, null, good, null, null, good, null, 16, F(2.0), 0, null) == 1
+    assert _call(iw, good, good, bad_align, null, good, null, 16, F(2.0), 0, null) == 3
+    assert _call(iw, good, good, null, good, good, bad_align, 16, F(2.0), 0, null) == 3
 
 
 def test_zero_sized_problems_are_no_ops():
@@ -90,6 +104,8 @@ def test_zero_sized_problems_are_no_ops():
     assert _call("gemm_w8a8_blockscaled", null, null, null, null, null, 0, 64, 128, null) == 0
     assert _call("grouped_gemm_w8a8_blockscaled", null, null, null, null, null, null, 0, 64, 128, 4, null) == 0
     assert _call("fp8bq_encode_e4m3", null, null, 0, 0, null) == 0
+    assert _call("token_importance_weights", null, null, null, null, null, null, 0, ctypes.c_float(2.0), 1,
+                 null) == 0
 
 
 def test_no_device_is_reported():
