@@ -32,6 +32,8 @@ Modules
            and 1x128 per-token activation groups.
 ``gemm``   block-scaled GEMM (dequantize, exact product, one BF16 rounding)
            and its ragged grouped (MoE) form.
+``moe``    MoE expert-FFN glue: pairs sorted by expert, gathered FP8 rows,
+           SiLU(gate) * up -> BF16 -> 1x128 groups, the weighted combine.
 ``tis``    token-level importance weights of the rollout correction
            ([FP8-RL summary] §3.4.3): TIS clipping and MIS masking.
 
@@ -66,6 +68,7 @@ from .gemm import (
     grouped_gemm_ref,
 )
 from .tis import importance_weights
+from .moe import sort_by_expert, gather_quantize_act, silu_mul_bf16, silu_mul_quantize, combine
 
 __all__ = [
     "E4M3_MAX",
@@ -86,4 +89,9 @@ __all__ = [
     "gemm_ref_bf16",
     "grouped_gemm_ref",
     "importance_weights",
+    "sort_by_expert",
+    "gather_quantize_act",
+    "silu_mul_bf16",
+    "silu_mul_quantize",
+    "combine",
 ]

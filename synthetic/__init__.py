@@ -13,7 +13,9 @@ those models' linear-layer shapes stand in for them:
   channels" (whole K columns) multiplied by a constant
 * MoE routing: logits ~ N(0, 1) [tokens][experts] -> float32 softmax ->
   top-k experts per token (ties to the lower expert index) -> (expert,
-  token) pairs sorted by expert then token -> ragged row offsets.
+  token) pairs sorted by expert then token -> ragged row offsets;
+  ``moe_topk`` gives the same top-k ids per token and their probabilities
+  renormalized over the k chosen experts (the combine weights).
 * rollout batches for the importance weights: padded [responses][max_len]
   log-probabilities of sampled tokens under the rollout and training
   policies, a response mask and per-response advantages
@@ -32,6 +34,7 @@ from .gen import (
     bf16_normal,
     activations,
     moe_routing,
+    moe_topk,
     gather_rows,
     device_bf16_normal,
     f32_to_bf16_bits,
@@ -45,6 +48,7 @@ __all__ = [
     "bf16_normal",
     "activations",
     "moe_routing",
+    "moe_topk",
     "gather_rows",
     "device_bf16_normal",
     "f32_to_bf16_bits",

@@ -59,12 +59,7 @@ def moe_routing(tokens, experts, top_k, seed):
     expert then token; ``offsets`` [experts+1] (int32) delimit each expert's
     rows in that order.
     """
-    rng = np.random.default_rng(list(seed))
-    logits = rng.standard_normal((tokens, experts), dtype=np.float32)
-    z = logits - logits.max(axis=1, keepdims=True)
-    p = np.exp(z)
-    p = p / p.sum(axis=1, keepdims=True)
-    order = np.argsort(-p, axis=1, kind="stable")[:, :top_k]  # ties -> lower index
+    order, _ = moe_topk(tokens, experts, top_k, seed)
     tok = np.repeat(np.arange(tokens), top_k)
     exp = order.reshape(-1)
     perm = np.lexsort((tok, exp))  # sort by expert, then token
@@ -73,6 +68,21 @@ def moe_routing(tokens, experts, top_k, seed):
     offsets = np.zeros(experts + 1, np.int32)
     offsets[1:] = np.cumsum(counts)
     return tok.astype(np.int64), exp.astype(np.int64), offsets
+
+
+def moe_topk(tokens, experts, top_k, seed):
+    """Router output: top-k expert ids [tokens][top_k] (int32, most probable
+    first, ties to the lower index) and their probabilities renormalized over
+    the k chosen experts (float32 [tokens][top_k]), from softmax(N(0,1) logits)."""
+    rng = np.random.default_rng(list(seed))
+    logits = rng.standard_normal((tokens, experts), dtype=np.float32)
+    z = logits - logits.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p = p / p.sum(axis=1, keepdims=True)
+    order = np.argsort(-p, axis=1, kind="stable")[:, :top_k]  # ties -> lower index
+    w = np.take_along_axis(p, order, axis=1)
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    return order.astype(np.int32), w
 
 
 def gather_rows(bits, token_ids):

@@ -1,0 +1,157 @@
+"""Pins of the MoE glue oracle (oracle/moe.py): brute force on tiny inputs,
+an independent sorting of the synthetic router, textbook SiLU values and the
+logistic function of scipy, and a matrix form of the combine."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+from oracle import quant_act_per_token_group, round_to_bf16_bits
+from oracle.bf16 import bf16_bits_to_f64
+from oracle.moe import combine, gather_quantize_act, silu_mul_bf16, silu_mul_f64, silu_mul_quantize, sort_by_expert
+from synthetic import f32_to_bf16_bits, moe_routing, moe_topk
+
+
+def brute_sort(ids, E):
+    flat = [int(v) for v in np.asarray(ids).reshape(-1)]
+    rows, offsets = [], [0]
+    for e in range(E):
+        for p, v in enumerate(flat):
+            if v == e:
+                rows.append(p)
+        offsets.append(len(rows))
+    pair_row = [-1] * len(flat)
+    for r, p in enumerate(rows):
+        pair_row[p] = r
+    return offsets, rows, pair_row
+
+
+@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (5, 2, 3, 1), (17, 4, 9, 2), (40, 8, 16, 3), (0, 8, 4, 4)])
+def test_sort_brute_force(T, k, E, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-2, E + 2, size=(T, k)).astype(np.int32)   # duplicates and invalid ids included
+    off, rows, pr = sort_by_expert(ids, E)
+    boff, brows, bpr = brute_sort(ids, E)
+    assert list(off) == boff and list(rows) == brows and list(pr) == bpr
+
+
+def test_sort_matches_router_order_and_invariants():
+    T, E, k = 512, 128, 8
+    ids, _ = moe_topk(T, E, k, (70, 0))
+    off, rows, pr = sort_by_expert(ids, E)
+    tok, exp, roff = moe_routing(T, E, k, (70, 0))
+    assert np.array_equal(off, roff)
+    assert np.array_equal(rows // k, tok)
+    assert np.array_equal(ids.reshape(-1)[rows], exp)
+    assert np.array_equal(pr[rows], np.arange(T * k))
+    for e in range(E):
+        seg = rows[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+def test_gather_quantize_is_quantize_then_gather():
+    rng = np.random.default_rng(5)
+    T, K, k = 9, 384, 3
+    x = f32_to_bf16_bits(rng.normal(0, 1, (T, K)).astype(np.float32) * np.float32(3.0))
+    ids = np.stack([rng.permutation(6)[:k] for _ in range(T)]).astype(np.int32)
+    _, rows, _ = sort_by_expert(ids, 6)
+    q, s = gather_quantize_act(x, rows, k)
+    q0, s0 = quant_act_per_token_group(x)
+    assert np.array_equal(q, q0[rows // k]) and np.array_equal(s, s0[rows // k])
+
+
+def bf16(v):
+    return f32_to_bf16_bits(np.asarray(v, np.float32))
+
+
+def test_silu_textbook_values():
+    # SiLU(1) = 1 / (1 + 1/e), SiLU(-1) = -1 / (1 + e), SiLU(0) = 0
+    g = np.array([1.0, -1.0, 0.0, 2.0], np.float32)
+    u = np.array([1.0, 1.0, 5.0, -0.5], np.float32)
+    y = np.concatenate([bf16(g), bf16(u)])[None, :]
+    h = silu_mul_f64(y, 4)[0]
+    assert abs(h[0] - 0.7310585786300049) < 1e-15
+    assert abs(h[1] + 0.2689414213699951) < 1e-15
+    assert h[2] == 0.0
+    assert abs(h[3] - (-0.5 * 1.7615941559557649)) < 1e-15
+    bits = silu_mul_bf16(y, 4)[0]
+    assert list(bits) == list(round_to_bf16_bits(np.array([0.7310585786300049, -0.2689414213699951, 0.0,
+                                                           -0.8807970779778824])))
+
+
+def test_silu_against_scipy_logistic_and_identities():
+    rng = np.random.default_rng(6)
+    M, F = 64, 256
+    y = bf16(rng.normal(0, 2.5, (M, 2 * F)).astype(np.float32))
+    g = bf16_bits_to_f64(y[:, :F])
+    u = bf16_bits_to_f64(y[:, F:])
+    h = silu_mul_f64(y, F)
+    ref = g * expit(g) * u
+    assert np.all(np.abs(h - ref) <= 1e-15 * np.abs(ref) + 1e-300)   # a few float64 roundings apart
+    assert np.array_equal(silu_mul_bf16(y, F), round_to_bf16_bits(ref))
+    # SiLU(g) - SiLU(-g) = g (u = 1)
+    ones = np.ones_like(y[:, F:])
+    hp = silu_mul_f64(np.concatenate([y[:, :F], ones * 0 + bf16(1.0)], axis=1), F)
+    yn = y[:, :F] ^ np.uint16(0x8000)
+    hn = silu_mul_f64(np.concatenate([yn, ones * 0 + bf16(1.0)], axis=1), F)
+    assert np.all(np.abs(hp - hn - g) <= 1e-14 * (np.abs(g) + 1))
+
+
+def test_silu_layout_gate_first():
+    # up = 0 gives h = 0 whatever the gate; a large gate g gives h = g * up
+    F = 128
+    g = bf16(np.full(F, 40.0))
+    u = bf16(np.linspace(-3, 3, F))
+    h = silu_mul_bf16(np.concatenate([g, u])[None, :], F)[0]
+    assert np.array_equal(h, round_to_bf16_bits(40.0 * bf16_bits_to_f64(u)))
+    h0 = silu_mul_bf16(np.concatenate([u, bf16(np.zeros(F))])[None, :], F)[0]
+    assert np.all((h0 & 0x7FFF) == 0)
+
+
+def test_silu_quantize_is_quant_of_bf16_h():
+    rng = np.random.default_rng(7)
+    y = bf16(rng.normal(0, 1, (8, 2 * 384)).astype(np.float32))
+    q, s = silu_mul_quantize(y, 384)
+    q0, s0 = quant_act_per_token_group(silu_mul_bf16(y, 384))
+    assert np.array_equal(q, q0) and np.array_equal(s, s0)
+    assert q.shape == (8, 384) and s.shape == (8, 3)
+
+
+def test_combine_brute_force_exact():
+    rng = np.random.default_rng(8)
+    T, k, H, M = 6, 3, 5, 20
+    y = bf16(rng.normal(0, 1, (M, H)).astype(np.float32))
+    w = rng.random((T, k)).astype(np.float32)
+    pr = rng.integers(-1, M, size=T * k).astype(np.int32)
+    out, mag, bits = combine(y, pr, w)
+    yv = bf16_bits_to_f64(y)
+    for t in range(T):
+        for h in range(H):
+            exact = Fraction(0)
+            for j in range(k):
+                r = pr[t * k + j]
+                if r >= 0:
+                    exact += Fraction(float(w[t, j])) * Fraction(float(yv[r, h]))
+            assert abs(Fraction(out[t, h]) - exact) <= Fraction(2.0 ** -50) * (abs(exact) + 1)
+    assert np.array_equal(bits, round_to_bf16_bits(out))
+
+
+def test_combine_matrix_form_and_special_weights():
+    rng = np.random.default_rng(9)
+    T, k, H, E = 32, 4, 64, 8
+    ids, w = moe_topk(T, E, k, (71, 0))
+    _, rows, pr = sort_by_expert(ids, E)
+    y = bf16(rng.normal(0, 1, (T * k, H)).astype(np.float32))
+    out, _, _ = combine(y, pr, w)
+    S = np.zeros((T, T * k))
+    for t in range(T):
+        for j in range(k):
+            S[t, pr[t * k + j]] += float(w[t, j])
+    assert np.allclose(out, S @ bf16_bits_to_f64(y), rtol=1e-13, atol=1e-13)
+    # one-hot weights copy the chosen row
+    onehot = np.zeros((T, k), np.float32)
+    onehot[:, 1] = 1.0
+    _, _, bits = combine(y, pr, onehot)
+    assert np.array_equal(bits, y[pr.reshape(T, k)[:, 1]])
