@@ -26,14 +26,19 @@ Readings of what the pages leave open:
 * fc1's output row is [gate | up]: columns [0, F) are the gate projection,
   [F, 2F) the up projection (one fused fc1 GEMM of width 2F).
 * The gated activation is SiLU(g) = g / (1 + exp(-g)) (Qwen3's MLP, the
-  model family of the pages' experiments).  h = SiLU(g) * u is evaluated in
-  float64 from the BF16 inputs and rounded once to BF16 (the precision in
-  which the nonlinearity stays), then quantized like any activation.
+  model family of the pages' experiments).  h = SiLU(g) * u of the BF16
+  inputs is rounded once, to nearest even, to BF16 (the precision in which
+  the nonlinearity stays), then quantized like any activation.  The
+  rounding is that of the exact real value: float64 decides it except near
+  a BF16 midpoint, where an exact comparison does.
 * The combine weights are float32 [T][k]; the sum is formed in float64 and
   rounded once to BF16.  Pairs without a row contribute nothing.
 
 Pinned in ``tests/test_oracle_moe.py``.
 """
+
+from decimal import Decimal, localcontext
+from fractions import Fraction
 
 import numpy as np
 
@@ -77,9 +82,56 @@ def silu_mul_f64(y_bits, F):
         return g / (1.0 + np.exp(-g)) * u
 
 
+def _exceeds_midpoint(g, u, mid):
+    """|SiLU(g) * u| > |mid| for a BF16 midpoint mid of the same sign, decided exactly.
+
+    With P = g * u (exact) and r = mid / P > 0 (rationals):
+        |h| > |mid|  <=>  sigma(g) > r,  sigma(g) = 1 / (1 + e^-g),
+    which is false for r >= 1 (sigma < 1) and otherwise, with s = 1/r - 1 > 0,
+        <=>  e^-g < s  <=>  g > -ln(s).
+    ln(s) of the rational s is taken to 100 significant digits; g is a BF16
+    value and -ln(s) is transcendental unless s = 1 (then the test is g > 0).
+    """
+    P = Fraction(g) * Fraction(u)
+    r = mid / P
+    if r >= 1:
+        return False
+    s = 1 / r - 1
+    if s == 1:
+        return g > 0
+    with localcontext() as ctx:
+        ctx.prec = 100
+        ln_s = (Decimal(s.numerator) / Decimal(s.denominator)).ln()
+        return Decimal(g) > -ln_s
+
+
 def silu_mul_bf16(y_bits, F):
-    """h = SiLU(gate) * up rounded once to BF16 (bits, [M][F])."""
-    return round_to_bf16_bits(silu_mul_f64(y_bits, F))
+    """h = SiLU(gate) * up correctly rounded (nearest even) to BF16 (bits, [M][F]).
+
+    The float64 value decides the rounding unless it lies within 2^-40
+    (relative) of a BF16 midpoint; there the side of the midpoint is decided
+    exactly (``_exceeds_midpoint``).  Such near-ties are structural: for a
+    tiny gate SiLU(g) * u = g u / 2 + O(g^2), and for a large gate
+    SiLU(g) * u = g u (1 - e^-g + ...), where g u / 2 or g u (16-bit
+    products of two BF16 values) can be exactly a midpoint.
+    """
+    y = np.asarray(y_bits, dtype=np.uint16)
+    h = silu_mul_f64(y, F)
+    bits = round_to_bf16_bits(h)
+    _, ex = np.frexp(h)
+    q = np.exp2((np.maximum(ex.astype(np.int64) - 1, -126) - 7).astype(np.float64))   # BF16 spacing at h
+    m = h / q                                   # exact: the BF16 grid becomes the integers
+    fl = np.floor(m)
+    near = (h != 0) & (np.abs(m - fl - 0.5) <= np.abs(m) * 2.0 ** -40)
+    g_all = bf16_bits_to_f64(y[:, :F])
+    u_all = bf16_bits_to_f64(y[:, F:2 * F])
+    for i, j in zip(*np.nonzero(near)):
+        mid = (Fraction(float(fl[i, j])) + Fraction(1, 2)) * Fraction(float(q[i, j]))
+        up = _exceeds_midpoint(float(g_all[i, j]), float(u_all[i, j]), mid)
+        lo, hi = float(fl[i, j]) * q[i, j], (float(fl[i, j]) + 1.0) * q[i, j]
+        val = (hi if up else lo) if m[i, j] > 0 else (lo if up else hi)
+        bits[i, j] = round_to_bf16_bits(np.array([val]))[0]     # exact: val is on the BF16 grid
+    return bits
 
 
 def silu_mul_quantize(y_bits, F):

@@ -2,6 +2,7 @@
 an independent sorting of the synthetic router, textbook SiLU values and the
 logistic function of scipy, and a matrix form of the combine."""
 
+from decimal import Decimal, localcontext
 from fractions import Fraction
 
 import numpy as np
@@ -99,13 +100,34 @@ def test_silu_against_scipy_logistic_and_identities():
     assert np.all(np.abs(hp - hn - g) <= 1e-14 * (np.abs(g) + 1))
 
 
+def decimal_silu_bf16(g, u, prec=60):
+    """BF16 bits nearest to SiLU(g) * u evaluated with `prec` significant digits
+    (an independent high-precision evaluation; ties cannot occur for g != 0)."""
+    with localcontext() as ctx:
+        ctx.prec = prec
+        G, U = Decimal(float(g)), Decimal(float(u))
+        h = G / (1 + (-G).exp()) * U
+        hf = float(h)
+        if hf == 0.0:
+            return round_to_bf16_bits(np.array([hf]))[0]
+        _, ex = np.frexp(hf)
+        q = 2.0 ** (max(ex - 1, -126) - 7)
+        lo = np.floor(hf / q) * q
+        cands = [lo - q, lo, lo + q, lo + 2 * q]
+        best = min(cands, key=lambda c: abs(Decimal(c) - h))
+        if best == 0.0:
+            best = np.copysign(0.0, hf)  # a tiny value rounds to the zero of its sign
+        return round_to_bf16_bits(np.array([best]))[0]
+
+
 def test_silu_layout_gate_first():
-    # up = 0 gives h = 0 whatever the gate; a large gate g gives h = g * up
+    # up = 0 gives h = 0 whatever the gate; a large gate g gives h ~ g * up
     F = 128
     g = bf16(np.full(F, 40.0))
     u = bf16(np.linspace(-3, 3, F))
     h = silu_mul_bf16(np.concatenate([g, u])[None, :], F)[0]
-    assert np.array_equal(h, round_to_bf16_bits(40.0 * bf16_bits_to_f64(u)))
+    uv = bf16_bits_to_f64(u)
+    assert [int(b) for b in h] == [int(decimal_silu_bf16(40.0, v)) for v in uv]
     h0 = silu_mul_bf16(np.concatenate([u, bf16(np.zeros(F))])[None, :], F)[0]
     assert np.all((h0 & 0x7FFF) == 0)
 
@@ -155,3 +177,42 @@ def test_combine_matrix_form_and_special_weights():
     onehot[:, 1] = 1.0
     _, _, bits = combine(y, pr, onehot)
     assert np.array_equal(bits, y[pr.reshape(T, k)[:, 1]])
+
+
+def test_silu_rounding_matches_high_precision():
+    # random gates over a wide range against a 60-digit evaluation
+    rng = np.random.default_rng(10)
+    g = np.concatenate([rng.normal(0, 3, 300), rng.uniform(-100, 100, 100), rng.normal(0, 1e-6, 50)])
+    u = rng.normal(0, 2, g.size)
+    y = bf16(np.concatenate([g, u]))[None, :]
+    gv, uv = bf16_bits_to_f64(y[0, :g.size]), bf16_bits_to_f64(y[0, g.size:])
+    h = silu_mul_bf16(y, g.size)[0]
+    assert [int(b) for b in h] == [int(decimal_silu_bf16(a, b)) for a, b in zip(gv, uv)]
+
+
+def test_silu_structural_near_ties():
+    # tiny gate: g u / 2 exactly a BF16 midpoint; the exact h lies beyond it
+    # in magnitude for g > 0 (sigma(g) > 1/2) and short of it for g < 0
+    g = 0.75 * 2.0 ** -52
+    u = -0.7109375
+    assert (Fraction(g) * Fraction(u) / 2) == Fraction(-273, 4) * Fraction(2) ** -60
+    for gs, expect_up in ((g, True), (-g, False)):
+        y = bf16(np.array([gs, u]))[None, :]
+        h = silu_mul_bf16(y, 1)[0, 0]
+        mid = gs * u / 2
+        hv = float(bf16_bits_to_f64(np.array([h]))[0])
+        assert (abs(hv) > abs(mid)) == expect_up
+        assert h == decimal_silu_bf16(gs, u, prec=80)
+    # large gate: g u exactly a midpoint; sigma(g) < 1 puts h short of it
+    found = 0
+    for ub in range(0x3f80, 0x4000):
+        uv = float(bf16_bits_to_f64(np.array([ub], np.uint16))[0])
+        p = 40.0 * uv
+        _, ex = np.frexp(p)
+        q = 2.0 ** (ex - 1 - 7)
+        if (p / q) % 1 == 0.5:
+            y = np.array([[bf16([40.0])[0], ub]], np.uint16)
+            hv = float(bf16_bits_to_f64(silu_mul_bf16(y, 1))[0, 0])
+            assert abs(hv) < abs(p)
+            found += 1
+    assert found > 0
