@@ -130,6 +130,7 @@ def silu_mul_bf16(y_bits, F):
         up = _exceeds_midpoint(float(g_all[i, j]), float(u_all[i, j]), mid)
         lo, hi = float(fl[i, j]) * q[i, j], (float(fl[i, j]) + 1.0) * q[i, j]
         val = (hi if up else lo) if m[i, j] > 0 else (lo if up else hi)
+        val = np.copysign(val, h[i, j]) if val == 0 else val        # rounding to zero keeps the sign
         bits[i, j] = round_to_bf16_bits(np.array([val]))[0]     # exact: val is on the BF16 grid
     return bits
 

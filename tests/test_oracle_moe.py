@@ -203,6 +203,11 @@ def test_silu_structural_near_ties():
         hv = float(bf16_bits_to_f64(np.array([h]))[0])
         assert (abs(hv) > abs(mid)) == expect_up
         assert h == decimal_silu_bf16(gs, u, prec=80)
+    # g = -2^-133 (smallest BF16 denormal), u = 1: h is just short of half the
+    # smallest denormal in magnitude, so it rounds to -0
+    y = np.array([[0x8001, bf16([1.0])[0]]], np.uint16)
+    assert silu_mul_bf16(y, 1)[0, 0] == 0x8000
+    assert silu_mul_bf16(np.array([[0x0001, bf16([1.0])[0]]], np.uint16), 1)[0, 0] == 0x0001
     # large gate: g u exactly a midpoint; sigma(g) < 1 puts h short of it
     found = 0
     for ub in range(0x3f80, 0x4000):
