@@ -53,9 +53,10 @@ PHASE_KERNELS = {
 
 
 def source_sha(fname):
-    """SHA-256 of a kernel source plus the shared device header."""
+    """SHA-256 of a kernel source plus every shared device header."""
     h = hashlib.sha256()
-    for f in (fname, "device_common.hpp"):
+    headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
+    for f in (fname, *headers):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -303,27 +304,10 @@ def detail(fb, dev):
     res["prefill_gemm_M8192"] = pre
     torch.cuda.empty_cache()
 
-    # -- MoE grouped GEMMs (Qwen3-30B-A3B layer, 4096 tokens, top-8 of 128)
-    cfg = MOE_QWEN3_30B_A3B
-    tok, _, off = moe_routing(cfg["tokens"], cfg["experts"], cfg["top_k"], (70, 0))
-    offd = torch.from_numpy(off).to(dev)
-    mt = int(off[-1])
-    moe = {}
-    for j, proj in enumerate(("gate_up", "down")):
-        n, k = cfg[proj]
-        w = device_bf16_normal((cfg["experts"], n, k), 0.02, seed=600 + j)
-        x = device_bf16_normal((mt, k), 1.0, seed=700 + j)
-        wq, ws = fb.quantize_weight_blockwise(w)
-        xq, xs = fb.quantize_act_per_token_group(x)
-        y = torch.empty((mt, n), dtype=torch.bfloat16, device=dev)
-        ms, _ = _time_ms(lambda: fb.grouped_gemm_w8a8_blockscaled(xq, xs, wq, ws, offd, y), reps=10)
-        f = 2 * mt * n * k
-        byt = mt * k + cfg["experts"] * n * k + 2 * mt * n + xs.numel() * 4 + ws.numel() * 4
-        roof = min(FP8_PEAK_TFLOPS, f / byt * HBM_PEAK_GBPS / 1e3)
-        moe[proj] = {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(f / ms / 1e9, 1),
-                     "roofline_TFLOPs": round(roof, 1), "frac_roofline": round(f / ms / 1e9 / roof, 4)}
-        del w, x, wq, ws, xq, xs, y
-    res["moe_grouped"] = moe
+    # -- one MoE expert-FFN layer (Qwen3-30B-A3B: 4096 tokens, top-8 of 128
+    #    experts, hidden 2048, expert FFN 768), every step on the GPU:
+    #    sort -> gather + 1x128 quant -> fc1 -> SiLU*up + 1x128 quant -> fc2 -> combine
+    res["moe_layer_qwen3_30b_a3b"] = moe_layer(fb, dev)
     torch.cuda.empty_cache()
 
     # -- 36-layer re-quantization sweep (4 calls, batch = 36 each)
@@ -367,6 +351,62 @@ def detail(fb, dev):
                                                 "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
     del lt, lr, adv, msk, w, wa
     torch.cuda.empty_cache()
+    return res
+
+
+def moe_layer(fb, dev):
+    import torch
+
+    from synthetic import MOE_QWEN3_30B_A3B, device_bf16_normal, moe_topk
+
+    cfg = MOE_QWEN3_30B_A3B
+    T, E, k, H, F = cfg["tokens"], cfg["experts"], cfg["top_k"], cfg["hidden"], cfg["ffn"]
+    R = T * k
+    ids_h, tw_h = moe_topk(T, E, k, (70, 0))
+    ids, tw = torch.from_numpy(ids_h).to(dev), torch.from_numpy(tw_h).to(dev)
+    x = device_bf16_normal((T, H), 1.0, seed=700)
+    w1q, w1s = fb.quantize_weight_blockwise(device_bf16_normal((E, 2 * F, H), 0.02, seed=600))
+    w2q, w2s = fb.quantize_weight_blockwise(device_bf16_normal((E, H, F), 0.02, seed=601))
+    off, sp, pr = fb.moe_sort_by_expert(ids, E)
+    a, a_s = fb.moe_gather_quantize_act(x, sp, k)
+    y1 = torch.empty((R, 2 * F), dtype=torch.bfloat16, device=dev)
+    h, h_s = torch.empty((R, F), dtype=torch.uint8, device=dev), torch.empty((R, F // 128), dtype=torch.float32,
+                                                                               device=dev)
+    y2 = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    steps = {
+        "sort": (lambda: fb.moe_sort_by_expert(ids, E, off, sp, pr), None, None),
+        "gather_quant": (lambda: fb.moe_gather_quantize_act(x, sp, k, a, a_s), T * H * 2 + R * H + R * (H // 128) * 4,
+                         None),
+        "fc1_gate_up": (lambda: fb.grouped_gemm_w8a8_blockscaled(a, a_s, w1q, w1s, off, y1), None, 2 * R * 2 * F * H),
+        "silu_mul_quant": (lambda: fb.silu_mul_quantize_act(y1, h, h_s), R * 2 * F * 2 + R * F + R * (F // 128) * 4,
+                           None),
+        "fc2_down": (lambda: fb.grouped_gemm_w8a8_blockscaled(h, h_s, w2q, w2s, off, y2), None, 2 * R * H * F),
+        "combine": (lambda: fb.moe_combine(y2, pr, tw, out), R * H * 2 + R * 8 + T * H * 2, None),
+    }
+    res, total = {}, 0.0
+    for name, (fn, byt, flops) in steps.items():
+        ms, _ = _time_ms(fn, reps=10)
+        total += ms
+        e = {"us": round(ms * 1e3, 1)}
+        if byt is not None:
+            e.update({"bytes": byt, "GBps": round(byt / ms / 1e6, 1), "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)})
+        if flops is not None:
+            n_out = 2 * F if name == "fc1_gate_up" else H
+            k_in = H if name == "fc1_gate_up" else F
+            byt_g = R * k_in + E * n_out * k_in + 2 * R * n_out + R * (k_in // 128) * 4
+            roof = min(FP8_PEAK_TFLOPS, flops / byt_g * HBM_PEAK_GBPS / 1e3)
+            e.update({"TFLOPs": round(flops / ms / 1e9, 1), "roofline_TFLOPs": round(roof, 1),
+                      "frac_roofline": round(flops / ms / 1e9 / roof, 4)})
+        res[name] = e
+
+    def layer():
+        fb.moe_expert_ffn(x, ids, tw, w1q, w1s, w2q, w2s)
+
+    layer_ms, _ = _time_ms(layer, reps=10)
+    res["sum_of_kernels_us"] = round(total * 1e3, 1)
+    res["layer_us"] = round(layer_ms * 1e3, 1)
+    res["layer_TFLOPs"] = round((2 * R * 2 * F * H + 2 * R * H * F) / layer_ms / 1e9, 1)
     return res
 
 

@@ -30,6 +30,11 @@ __all__ = [
     "grouped_gemm_w8a8_blockscaled",
     "encode_e4m3",
     "token_importance_weights",
+    "moe_sort_by_expert",
+    "moe_gather_quantize_act",
+    "silu_mul_quantize_act",
+    "moe_combine",
+    "moe_expert_ffn",
     "status_string",
 ]
 
@@ -45,6 +50,10 @@ EXPORTS = (
     "grouped_gemm_w8a8_blockscaled",
     "fp8bq_encode_e4m3",
     "token_importance_weights",
+    "moe_sort_by_expert",
+    "moe_gather_quantize_act",
+    "silu_mul_quantize_act",
+    "moe_combine",
 )
 
 
@@ -66,6 +75,10 @@ def _load():
     lib.grouped_gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p]
     lib.fp8bq_encode_e4m3.argtypes = [p, p, i64, i32, p]
     lib.token_importance_weights.argtypes = [p, p, p, p, p, p, i64, ctypes.c_float, i32, p]
+    lib.moe_sort_by_expert.argtypes = [p, i64, i64, i64, p, p, p, p]
+    lib.moe_gather_quantize_act.argtypes = [p, p, i64, i64, i64, i64, p, p, p]
+    lib.silu_mul_quantize_act.argtypes = [p, i64, i64, p, p, p, p]
+    lib.moe_combine.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = i32
     return lib
@@ -251,6 +264,111 @@ def token_importance_weights(logp_train, logp_rollout, C=2.0, mode="tis", mask=N
                                              _ptr(out), _ptr(out_adv), logp_train.numel(), float(C),
                                              _IW_MODES[mode], _stream(logp_train)))
     return out if advantages is None else (out, out_adv)
+
+
+def moe_sort_by_expert(topk_ids, num_experts, offsets=None, sorted_pair=None, pair_row=None):
+    """Routing ids int32 [T, k] -> (group_offsets int32 [E+1], sorted_pair int32 [T*k], pair_row int32 [T*k])."""
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [tokens, k]")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    _require(topk_ids, "topk_ids", torch.int32, (T, k))
+    E = int(num_experts)
+    if offsets is None:
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if sorted_pair is None:
+        sorted_pair = torch.empty(T * k, dtype=torch.int32, device=dev)
+    if pair_row is None:
+        pair_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    _require(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _require(sorted_pair, "sorted_pair", torch.int32, (T * k,), dev)
+    _require(pair_row, "pair_row", torch.int32, (T * k,), dev)
+    with torch.cuda.device(dev):
+        _check("moe_sort_by_expert", _lib.moe_sort_by_expert(_ptr(topk_ids), T, k, E, _ptr(offsets), _ptr(sorted_pair),
+                                                             _ptr(pair_row), _stream(topk_ids)))
+    return offsets, sorted_pair, pair_row
+
+
+def moe_gather_quantize_act(x, sorted_pair, k, out=None, scale=None):
+    """BF16 x [T, K] and sorted pairs [R] -> (E4M3 rows [R, K] of tokens sorted_pair // k, scales [R, K/128])."""
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, K]")
+    T, K = x.shape
+    dev = x.device
+    _require(x, "x", _BF16, (T, K))
+    R = sorted_pair.numel()
+    _require(sorted_pair, "sorted_pair", torch.int32, (R,), dev)
+    if out is None:
+        out = torch.empty((R, K), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((R, K // BLOCK), dtype=torch.float32, device=dev)
+    _require(out, "out", _U8, (R, K), dev)
+    _require(scale, "scale", torch.float32, (R, K // BLOCK), dev)
+    with torch.cuda.device(dev):
+        _check("moe_gather_quantize_act",
+               _lib.moe_gather_quantize_act(_ptr(_u16(x)), _ptr(sorted_pair), R, T, int(k), K, _ptr(out), _ptr(scale),
+                                            _stream(x)))
+    return out, scale
+
+
+def silu_mul_quantize_act(y, out=None, scale=None, h_out=None):
+    """fc1 output BF16 [M, 2F] = [gate | up] -> (E4M3 codes of BF16(SiLU(gate) * up) [M, F], scales [M, F/128]).
+
+    With ``h_out`` (BF16 [M, F]) the BF16 h is stored as well."""
+    if y.dim() != 2 or y.shape[1] % 2:
+        raise ValueError("y must be [rows, 2F]")
+    M, F = y.shape[0], y.shape[1] // 2
+    dev = y.device
+    _require(y, "y", _BF16, (M, 2 * F))
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((M, _cdiv(F, BLOCK)), dtype=torch.float32, device=dev)
+    _require(out, "out", _U8, (M, F), dev)
+    _require(scale, "scale", torch.float32, (M, _cdiv(F, BLOCK)), dev)
+    if h_out is not None:
+        _require(h_out, "h_out", _BF16, (M, F), dev)
+    with torch.cuda.device(dev):
+        _check("silu_mul_quantize_act",
+               _lib.silu_mul_quantize_act(_ptr(_u16(y)), M, F, _ptr(out), _ptr(scale),
+                                          _ptr(None if h_out is None else _u16(h_out)), _stream(y)))
+    return out, scale
+
+
+def moe_combine(y, pair_row, topk_weights, out=None):
+    """fc2 output BF16 [M, H], pair_row [T*k], weights float32 [T, k] -> BF16 [T, H] weighted sums."""
+    if y.dim() != 2 or topk_weights.dim() != 2:
+        raise ValueError("y must be [rows, H] and topk_weights [tokens, k]")
+    M, H = y.shape
+    T, k = topk_weights.shape
+    dev = y.device
+    _require(y, "y", _BF16, (M, H))
+    _require(pair_row, "pair_row", torch.int32, (T * k,), dev)
+    _require(topk_weights, "topk_weights", torch.float32, (T, k), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", _BF16, (T, H), dev)
+    with torch.cuda.device(dev):
+        _check("moe_combine", _lib.moe_combine(_ptr(_u16(y)), _ptr(pair_row), _ptr(topk_weights), T, k, H, M,
+                                               _ptr(_u16(out)), _stream(y)))
+    return out
+
+
+def moe_expert_ffn(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale):
+    """One MoE expert FFN layer through the library's kernels only.
+
+    x BF16 [T, H]; topk_ids int32 [T, k]; topk_weights float32 [T, k];
+    w1 E4M3 [E, 2F, H] (fc1 = [gate; up]) with scales [E, 2F/128, H/128];
+    w2 E4M3 [E, H, F] (fc2) with scales [E, H/128, F/128].  Returns BF16 [T, H].
+    """
+    E, H = w1.shape[0], x.shape[1]
+    k = topk_ids.shape[1]
+    offsets, sorted_pair, pair_row = moe_sort_by_expert(topk_ids, E)
+    a, a_s = moe_gather_quantize_act(x, sorted_pair, k)
+    y1 = grouped_gemm_w8a8_blockscaled(a, a_s, w1, w1_scale, offsets)
+    h, h_s = silu_mul_quantize_act(y1)
+    y2 = grouped_gemm_w8a8_blockscaled(h, h_s, w2, w2_scale, offsets)
+    return moe_combine(y2, pair_row, topk_weights)
 
 
 def raw_library():

@@ -200,4 +200,88 @@ fp8bq_status token_importance_weights(const float* logp_train, const float* logp
   }
 }
 
+fp8bq_status moe_sort_by_expert(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int32_t* group_offsets,
+                                int32_t* sorted_pair, int32_t* pair_row, void* stream) {
+  try {
+    if (T < 0 || k < 0 || E < 1 || E > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t P;
+    if (!mul_ok(T, k, &P) || P > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+    if (!group_offsets || (P > 0 && (!topk_ids || !sorted_pair || !pair_row))) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(group_offsets) || (P > 0 && (!aligned16(topk_ids) || !aligned16(sorted_pair) ||
+                                                !aligned16(pair_row))))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_moe_sort(topk_ids, P, E, group_offsets, sorted_pair, pair_row,
+                                           static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status moe_gather_quantize_act(const uint16_t* x_bf16, const int32_t* sorted_pair, int64_t rows, int64_t T,
+                                     int64_t k, int64_t K, uint8_t* a_fp8, float* a_scale, void* stream) {
+  try {
+    if (rows < 0 || T < 0 || k < 1 || K < 0 || (K % 128) != 0) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t rk, tk, bytes;
+    if (!mul_ok(rows, K, &rk) || !mul_ok(T, K, &tk) || !mul_ok(tk, 2, &bytes) || k > 0x7fffffffLL)
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (rk == 0) return FP8BQ_OK;
+    if (!sorted_pair || !a_fp8 || !a_scale || (T > 0 && !x_bf16)) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(sorted_pair) || !aligned16(a_fp8) || !aligned16(a_scale) || (T > 0 && !aligned16(x_bf16)))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_gather_quant_act(x_bf16, sorted_pair, rows, T, k, K, a_fp8, a_scale,
+                                                   static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status silu_mul_quantize_act(const uint16_t* y_bf16, int64_t M, int64_t F, uint8_t* h_fp8, float* h_scale,
+                                   uint16_t* h_bf16, void* stream) {
+  try {
+    if (M < 0 || F < 0 || (F % 8) != 0) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t mf, bytes;
+    if (!mul_ok(M, F, &mf) || !mul_ok(mf, 4, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
+    if (mf == 0) return FP8BQ_OK;
+    if (!y_bf16 || !h_fp8 || !h_scale) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(y_bf16) || !aligned16(h_fp8) || !aligned16(h_scale) || (h_bf16 && !aligned16(h_bf16)))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(
+        fp8bq::launch_silu_mul_quant(y_bf16, M, F, h_fp8, h_scale, h_bf16, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status moe_combine(const uint16_t* y_bf16, const int32_t* pair_row, const float* topk_weights, int64_t T,
+                         int64_t k, int64_t H, int64_t M_rows, uint16_t* out_bf16, void* stream) {
+  try {
+    if (T < 0 || k < 0 || H < 0 || M_rows < 0 || (H % 8) != 0 || T > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t tk, th, mh, bytes;
+    if (!mul_ok(T, k, &tk) || tk > 0x7fffffffLL || !mul_ok(T, H, &th) || !mul_ok(M_rows, H, &mh) ||
+        !mul_ok(mh > th ? mh : th, 2, &bytes))
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (th == 0) return FP8BQ_OK;
+    if (!out_bf16 || (tk > 0 && (!pair_row || !topk_weights)) || (mh > 0 && !y_bf16)) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(out_bf16) || (tk > 0 && (!aligned16(pair_row) || !aligned16(topk_weights))) ||
+        (mh > 0 && !aligned16(y_bf16)))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_moe_combine(y_bf16, pair_row, topk_weights, T, k, H, M_rows, out_bf16,
+                                              static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
 }  // extern "C"

@@ -25,4 +25,16 @@ hipError_t launch_importance_weights(const float* logp_train, const float* logp_
                                      const float* advantages, float* weights, float* weighted_adv, int64_t n,
                                      float lo, float hi, float log_c, bool mis, hipStream_t stream);
 
+hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int64_t E, int32_t* offsets, int32_t* sorted_pair,
+                           int32_t* pair_row, hipStream_t stream);
+
+hipError_t launch_gather_quant_act(const uint16_t* x, const int32_t* sorted_pair, int64_t R, int64_t T, int64_t k,
+                                   int64_t K, uint8_t* q, float* scale, hipStream_t stream);
+
+hipError_t launch_silu_mul_quant(const uint16_t* y, int64_t M, int64_t F, uint8_t* q, float* scale, uint16_t* h,
+                                 hipStream_t stream);
+
+hipError_t launch_moe_combine(const uint16_t* y, const int32_t* pair_row, const float* w, int64_t T, int64_t k,
+                              int64_t H, int64_t M, uint16_t* out, hipStream_t stream);
+
 }  // namespace fp8bq

@@ -1,0 +1,321 @@
+// MoE expert-FFN glue around the grouped block-scaled GEMMs (gfx950).
+//
+// "FP8-RL: A Practical and Stable Low-Precision Stack for LLM Reinforcement
+// Learning" (paper-graph-ui summary), §3.4.1 "Quantization Scope": the
+// expert layers fc1 / fc2 are FP8 W8A8 linears; the gated MLP multiplies
+// the gate and up activations element-wise before the down projection;
+// §3.4.1 "Static vs. Dynamic Quantization": activations are quantized on
+// the fly in 1x128 tiles while the nonlinearity stays in higher precision.
+//
+//   moe_sort_kernel          routing pairs -> rows grouped by expert
+//   gather_quant_act_kernel  FP8 rows of the sorted pairs (1x128 groups)
+//   silu_mul_quant_kernel    h = SiLU(gate) * up -> BF16 -> 1x128 groups
+//   combine_kernel           routing-weighted sum of each token's k rows
+#include <math.h>
+
+#include "device_common.hpp"
+#include "group_quant.hpp"
+#include "launch.hpp"
+
+namespace fp8bq {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Sort by expert.  One workgroup per expert e, no atomics, deterministic:
+//   first row of e = number of pairs routed to experts below e;
+//   row of pair p   = first row + number of pairs q < p routed to e.
+// Pass 1 counts the first; pass 2 ranks e's pairs with a wave ballot and a
+// cross-wave prefix, chunk by chunk in pair order (so rows keep pair order).
+// Every workgroup reads the whole id list, which stays in L2.
+// ---------------------------------------------------------------------------
+constexpr int kSortThreads = 1024;
+constexpr int kSortWaves = kSortThreads / 64;
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+__global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* __restrict__ ids, int32_t P, int32_t E,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ sorted_pair,
+                                                                int32_t* __restrict__ pair_row) {
+  __shared__ int32_t part[kSortWaves];
+  const int32_t e = static_cast<int32_t>(blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  int below = 0;
+  for (int32_t p = tid; p < P; p += kSortThreads) {
+    const int32_t id = ids[p];
+    below += (id >= 0 && id < e) ? 1 : 0;
+  }
+  below = wave_sum_i32(below);
+  if (lane == 0) part[wave] = below;
+  __syncthreads();
+  int32_t first = 0;
+#pragma unroll
+  for (int w = 0; w < kSortWaves; ++w) first += part[w];
+  __syncthreads();
+
+  int32_t running = 0;
+  for (int32_t base = 0; base < P; base += kSortThreads) {
+    const int32_t p = base + tid;
+    const int32_t id = p < P ? ids[p] : -1;
+    const bool mine = id == e;
+    const uint64_t mask = __ballot(mine);
+    if (lane == 0) part[wave] = __popcll(mask);
+    __syncthreads();
+    int32_t before = 0, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) {
+      before += (w < wave) ? part[w] : 0;
+      chunk += part[w];
+    }
+    if (mine) {
+      const int32_t r = first + running + before + static_cast<int32_t>(lanes_below(mask));
+      sorted_pair[r] = p;
+      pair_row[p] = r;
+    }
+    if (e == 0 && p < P && (id < 0 || id >= E)) pair_row[p] = -1;  // no expert, no row
+    running += chunk;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    offsets[e] = first;
+    if (e == E - 1) offsets[E] = first + running;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 groups, one 16-lane quarter wave per (row, group), each lane owning
+// 8 consecutive values, as in the activation quantizer: the group amax is a
+// 4-step xor shuffle inside the quarter wave.
+// ---------------------------------------------------------------------------
+constexpr int kGroupThreads = 256;
+constexpr int kGroupsPerBlock = kGroupThreads / 16;
+
+__device__ __forceinline__ float quarter_wave_scale(u32x4 v) {
+  uint32_t a = amax_fold(amax8(0u, v));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(a, off, 16);
+    a = a > o ? a : o;
+  }
+  return scale_from_amax_bits(a);
+}
+
+// Gathered activation rows: row r of the output is token sorted_pair[r] / k
+// of x, quantized in 1x128 groups (the same codes as quantizing x and then
+// copying rows).  Rows whose pair names no token are written as zeros.
+__global__ __launch_bounds__(kGroupThreads) void gather_quant_act_kernel(const uint16_t* __restrict__ x,
+                                                                         const int32_t* __restrict__ sorted_pair,
+                                                                         uint8_t* __restrict__ q,
+                                                                         float* __restrict__ scale, int64_t R,
+                                                                         int64_t T, int32_t k, int64_t K, int G) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4);
+  if (gid >= R * G) return;  // the 16 lanes of a group leave together
+  const int li = threadIdx.x & 15;
+  const int64_t r = gid / G;
+  const int g = static_cast<int>(gid % G);
+  const int32_t pair = sorted_pair[r];
+  const int64_t t = pair >= 0 ? pair / k : -1;
+  const int64_t col = static_cast<int64_t>(g) * kBlock + li * 8;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (t >= 0 && t < T) v = *reinterpret_cast<const u32x4*>(x + t * K + col);
+  const float s = quarter_wave_scale(v);
+  if (li == 0) scale[r * G + g] = s;
+  *reinterpret_cast<u32x2*>(q + r * K + col) = encode8(v, s);
+}
+
+// h = SiLU(g) * u rounded to BF16, correctly rounded from the exact value.
+// Fast path in float32: with |g| <= 80 and no underflow or overflow, the
+// computed h32 = fl(fl(g / fl(1 + expf(-g))) * u) is within 2^-21 relative of
+// the exact value (expf within 2 ulp, three correctly rounded operations), so
+// its BF16 rounding is the exact value's whenever h32 is more than 32 float32
+// ulps away from a BF16 midpoint (low 16 bits 0x8000).  Otherwise (about one
+// value in a thousand, and every value outside the fast range) the product
+// is formed in float64 and rounded straight to BF16.
+//
+// Two regimes put the exact value structurally close to a midpoint, closer
+// than float64 resolves: for |g| < 2^-20, SiLU(g) u = a (1 + g/2 + O(g^2))
+// with a = g u / 2, and for g > 20, SiLU(g) u = a (1 - e^-g + ...) with
+// a = g u; a is a product of two BF16 values (16 significant bits, exact in
+// float64) and can be exactly a midpoint.  There the correction decides:
+// beyond the midpoint in magnitude for a tiny positive g, short of it
+// otherwise.  When a is not a midpoint it is at least 2^-16 (relative) away
+// from every midpoint and the correction (below 2^-21) cannot cross one.
+// Elsewhere SiLU(g) u is transcendental and has no such structure.
+__device__ __noinline__ uint32_t silu_mul_bf16_f64(float g, float u) {
+  const double gd = g, ud = u;
+  double h;
+  int tie = 0;  // for an exact midpoint: +1 rounds up in magnitude, -1 down
+  if (fabs(gd) < 0x1p-20) {
+    h = gd * ud * 0.5;
+    tie = gd > 0.0 ? 1 : -1;
+  } else if (gd > 20.0) {
+    h = gd * ud;
+    tie = -1;
+  } else {
+    h = gd / (1.0 + exp(-gd)) * ud;
+  }
+  if (h == 0.0 || !isfinite(h)) return __float_as_uint(static_cast<float>(h)) >> 16;
+  int ex;
+  (void)frexp(h, &ex);                                 // |h| in [2^(ex-1), 2^ex)
+  const int q = (ex - 1 > -126 ? ex - 1 : -126) - 7;  // BF16 spacing 2^q
+  const double m = ldexp(h, -q);                       // exact; |m| < 2^9
+  const double fl = floor(m);
+  double r;
+  if (tie != 0 && m - fl == 0.5)
+    r = ((tie > 0) == (m > 0.0)) ? fl + 1.0 : fl;      // away from / toward zero
+  else
+    r = rint(m);                                       // nearest even
+  const double v = ldexp(r, q);
+  if (fabs(v) > 3.3895313892515355e38) return (h < 0 ? 0xff80u : 0x7f80u);  // beyond BF16 max
+  if (v == 0.0) return h < 0.0 ? 0x8000u : 0u;
+  return __float_as_uint(static_cast<float>(v)) >> 16;  // exact conversion
+}
+
+__device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
+  if (fabsf(g) <= 80.0f) {
+    const float h = (g / (1.0f + expf(-g))) * u;
+    const uint32_t b = __float_as_uint(h);
+    const float ah = fabsf(h);
+    const uint32_t low = b & 0xffffu;
+    const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;
+    if (h == 0.0f) return b >> 16;
+    if (ah >= 0x1p-100f && ah <= 0x1p120f && dist > 32u) return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+  }
+  return silu_mul_bf16_f64(g, u);
+}
+
+// fc1 output rows [M][2F] = [gate | up] -> h codes [M][F] and scales
+// [M][ceil(F/128)] (and, if asked, the BF16 h itself).  F % 8 == 0; a
+// partial last group has idle lanes.
+template <bool kStoreH>
+__global__ __launch_bounds__(kGroupThreads) void silu_mul_quant_kernel(const uint16_t* __restrict__ y,
+                                                                       uint8_t* __restrict__ q,
+                                                                       float* __restrict__ scale,
+                                                                       uint16_t* __restrict__ hb, int64_t M,
+                                                                       int64_t F, int G) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4);
+  if (gid >= M * G) return;
+  const int li = threadIdx.x & 15;
+  const int64_t m = gid / G;
+  const int g = static_cast<int>(gid % G);
+  const int64_t col = static_cast<int64_t>(g) * kBlock + li * 8;
+  const bool in = col < F;  // F % 8 == 0: a lane is wholly in or out
+  u32x4 h = u32x4{0u, 0u, 0u, 0u};
+  if (in) {
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(y + m * 2 * F + col);
+    const u32x4 uv = *reinterpret_cast<const u32x4*>(y + m * 2 * F + F + col);
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    uint32_t hw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      hw[j] = silu_mul_bf16(bf16_lo(gw[j]), bf16_lo(uw[j])) | (silu_mul_bf16(bf16_hi(gw[j]), bf16_hi(uw[j])) << 16);
+    h = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    if (kStoreH) *reinterpret_cast<u32x4*>(hb + m * F + col) = h;
+  }
+  const float s = quarter_wave_scale(h);
+  if (li == 0) scale[m * G + g] = s;
+  if (in) *reinterpret_cast<u32x2*>(q + m * F + col) = encode8(h, s);
+}
+
+// ---------------------------------------------------------------------------
+// Combine: out[t] = sum_j w[t][j] * y[pair_row[t k + j]], float32 fma chain in
+// slot order, rounded once to BF16.  One workgroup per token, each lane owns
+// 8 columns (16-byte loads of each routed row).  Rows outside [0, M) are
+// skipped.
+// ---------------------------------------------------------------------------
+constexpr int kCombineThreads = 256;
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // NaN stays NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
+                                                                  const int32_t* __restrict__ pair_row,
+                                                                  const float* __restrict__ w,
+                                                                  uint16_t* __restrict__ out, int32_t k, int64_t H,
+                                                                  int64_t M) {
+  const int64_t t = blockIdx.x;
+  for (int64_t c = static_cast<int64_t>(threadIdx.x) * 8; c < H; c += kCombineThreads * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t r = pair_row[t * k + j];
+      if (r < 0 || r >= M) continue;
+      const float wj = w[t * k + j];
+      const u32x4 v = *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(r) * H + c);
+      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(wj, bf16_lo(vw[i]), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wj, bf16_hi(vw[i]), acc[2 * i + 1]);
+      }
+    }
+    u32x4 o;
+    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+    o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    *reinterpret_cast<u32x4*>(out + t * H + c) = o;
+  }
+}
+
+int64_t group_blocks(int64_t groups) { return (groups + kGroupsPerBlock - 1) / kGroupsPerBlock; }
+
+}  // namespace
+
+hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int64_t E, int32_t* offsets, int32_t* sorted_pair,
+                           int32_t* pair_row, hipStream_t stream) {
+  hipLaunchKernelGGL(moe_sort_kernel, dim3(static_cast<uint32_t>(E)), dim3(kSortThreads), 0, stream, ids,
+                     static_cast<int32_t>(P), static_cast<int32_t>(E), offsets, sorted_pair, pair_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_quant_act(const uint16_t* x, const int32_t* sorted_pair, int64_t R, int64_t T, int64_t k,
+                                   int64_t K, uint8_t* q, float* scale, hipStream_t stream) {
+  const int64_t G = K / kBlock;
+  const int64_t blocks = group_blocks(R * G);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_quant_act_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kGroupThreads), 0, stream, x,
+                     sorted_pair, q, scale, R, T, static_cast<int32_t>(k), K, static_cast<int>(G));
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_quant(const uint16_t* y, int64_t M, int64_t F, uint8_t* q, float* scale, uint16_t* h,
+                                 hipStream_t stream) {
+  const int64_t G = (F + kBlock - 1) / kBlock;
+  const int64_t blocks = group_blocks(M * G);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (h)
+    hipLaunchKernelGGL(silu_mul_quant_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kGroupThreads), 0,
+                       stream, y, q, scale, h, M, F, static_cast<int>(G));
+  else
+    hipLaunchKernelGGL(silu_mul_quant_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kGroupThreads), 0,
+                       stream, y, q, scale, h, M, F, static_cast<int>(G));
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_combine(const uint16_t* y, const int32_t* pair_row, const float* w, int64_t T, int64_t k,
+                              int64_t H, int64_t M, uint16_t* out, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if (T > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(T)), dim3(kCombineThreads), 0, stream, y, pair_row, w,
+                     out, static_cast<int32_t>(k), H, M);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bq

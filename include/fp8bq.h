@@ -195,6 +195,76 @@ fp8bq_status token_importance_weights(const float* logp_train, const float* logp
                                       const float* advantages, float* weights, float* weighted_adv, int64_t n,
                                       float C, int mode, void* stream);
 
+/*
+ * MoE expert-FFN glue around grouped_gemm_w8a8_blockscaled ([FP8-RL
+ * summary] §3.4.1 "Quantization Scope": the MoE expert layers fc1 / fc2 are
+ * FP8 W8A8 linears like the dense ones, and the gated MLP multiplies the gate
+ * and up activations element-wise before the down projection; §3.4.1
+ * "Static vs. Dynamic Quantization": activations are quantized on the fly in
+ * 1x128 tiles, the nonlinearity stays in higher precision).  One MoE layer:
+ *   moe_sort_by_expert -> moe_gather_quantize_act -> grouped GEMM (fc1)
+ *   -> silu_mul_quantize_act -> grouped GEMM (fc2) -> moe_combine.
+ * A routing "pair" p = t * k + j is slot j of token t.
+ */
+
+/*
+ * moe_sort_by_expert -- rows grouped by expert for the grouped GEMM.
+ *   topk_ids       [T][k] int32, the experts each token is routed to
+ *   group_offsets  [E+1] int32 output: expert e owns rows
+ *                  [group_offsets[e], group_offsets[e+1]); [0] = 0 and
+ *                  [E] = the number of pairs whose id is in [0, E)
+ *   sorted_pair    [T*k] int32 output: row r holds pair sorted_pair[r];
+ *                  entries from [E] on are left untouched
+ *   pair_row       [T*k] int32 output: the row of pair p, or -1 when its id
+ *                  is outside [0, E)
+ * Rows of one expert keep pair order (by token, for distinct ids per
+ * token).  Deterministic, no atomics.  T, k >= 0, T * k < 2^31, E >= 1
+ * (group_offsets is written even when T * k == 0).
+ */
+fp8bq_status moe_sort_by_expert(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int32_t* group_offsets,
+                                int32_t* sorted_pair, int32_t* pair_row, void* stream);
+
+/*
+ * moe_gather_quantize_act -- the fc1 input rows: row r is token
+ * sorted_pair[r] / k of x, quantized in 1x128 per-token groups exactly as
+ * quantize_act_per_token_group quantizes that token (so the codes equal
+ * quantizing x and copying rows).  Rows whose pair is negative or names a
+ * token >= T are written as zero codes with scale 0.
+ *   x_bf16  [T][K] BF16, sorted_pair [rows] int32 (moe_sort_by_expert)
+ *   a_fp8   [rows][K] E4M3 output, a_scale [rows][K/128] float32 output
+ *   rows, T >= 0, k >= 1, K >= 0 and K % 128 == 0.
+ */
+fp8bq_status moe_gather_quantize_act(const uint16_t* x_bf16, const int32_t* sorted_pair, int64_t rows, int64_t T,
+                                     int64_t k, int64_t K, uint8_t* a_fp8, float* a_scale, void* stream);
+
+/*
+ * silu_mul_quantize_act -- the fc2 input from the fc1 output: per row, with
+ * gate = columns [0, F) and up = columns [F, 2F),
+ *   h = BF16( SiLU(gate) * up ),  SiLU(g) = g / (1 + exp(-g)),
+ * correctly rounded (round to nearest even) from the exact value, then
+ * quantized in 1x128 groups exactly as quantize_act_per_token_group
+ * quantizes a BF16 [M][F] tensor.
+ *   y_bf16 [M][2F] BF16; h_fp8 [M][F] E4M3 output; h_scale [M][ceil(F/128)]
+ *   float32 output; h_bf16 [M][F] BF16 output of h itself, or NULL.
+ *   M >= 0, F >= 0, F % 8 == 0.  Inputs must be finite and every h must be
+ *   finite (below the BF16 maximum).
+ */
+fp8bq_status silu_mul_quantize_act(const uint16_t* y_bf16, int64_t M, int64_t F, uint8_t* h_fp8, float* h_scale,
+                                   uint16_t* h_bf16, void* stream);
+
+/*
+ * moe_combine -- each token's output is the routing-weighted sum of its
+ * expert rows: out[t] = sum_j topk_weights[t][j] * y[pair_row[t*k + j]],
+ * accumulated in float32 (fused multiply-add in slot order j = 0..k-1) and
+ * rounded once to BF16 (nearest even).  Slots whose row is outside
+ * [0, M_rows) contribute nothing.
+ *   y_bf16 [M_rows][H] BF16 (the fc2 output), pair_row [T*k] int32,
+ *   topk_weights [T][k] float32, out_bf16 [T][H] BF16 output.
+ *   T, k, M_rows >= 0, H >= 0, H % 8 == 0, T * k < 2^31.
+ */
+fp8bq_status moe_combine(const uint16_t* y_bf16, const int32_t* pair_row, const float* topk_weights, int64_t T,
+                         int64_t k, int64_t H, int64_t M_rows, uint16_t* out_bf16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["quantize_weight_blockwise", "quantize_act_per_token_group", "gemm_w8a8_blockscaled",
               "grouped_gemm_w8a8_blockscaled", "fp8bq_status_string", "fp8bq_encode_e4m3",
-              "token_importance_weights"]:
+              "token_importance_weights", "moe_sort_by_expert", "moe_gather_quantize_act",
+              "silu_mul_quantize_act", "moe_combine"]:
         assert n in names, names
 
 
@@ -94,6 +95,20 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call(iw, null, good, null, null, good, null, 16, F(2.0), 0, null) == 1
     assert _call(iw, good, good, bad_align, null, good, null, 16, F(2.0), 0, null) == 3
     assert _call(iw, good, good, null, good, good, bad_align, 16, F(2.0), 0, null) == 3
+    # MoE glue
+    assert _call("moe_sort_by_expert", good, 4, 2, 0, good, good, good, null) == 2      # no expert
+    assert _call("moe_sort_by_expert", good, 1 << 20, 1 << 12, 8, good, good, good, null) == 2  # > 2^31 pairs
+    assert _call("moe_sort_by_expert", null, 4, 2, 8, good, good, good, null) == 1
+    assert _call("moe_sort_by_expert", good, 4, 2, 8, bad_align, good, good, null) == 3
+    assert _call("moe_gather_quantize_act", good, good, 8, 4, 2, 100, good, good, null) == 2  # K % 128
+    assert _call("moe_gather_quantize_act", good, good, 8, 4, 0, 128, good, good, null) == 2  # k < 1
+    assert _call("moe_gather_quantize_act", good, null, 8, 4, 2, 128, good, good, null) == 1
+    assert _call("silu_mul_quantize_act", good, 4, 12, good, good, null, null) == 2  # F % 8
+    assert _call("silu_mul_quantize_act", good, 4, 16, good, null, null, null) == 1
+    assert _call("silu_mul_quantize_act", good, 4, 16, good, good, bad_align, null) == 3
+    assert _call("moe_combine", good, good, good, 4, 2, 12, 8, good, null) == 2  # H % 8
+    assert _call("moe_combine", good, null, good, 4, 2, 16, 8, good, null) == 1
+    assert _call("moe_combine", good, good, good, 4, 2, 16, 8, bad_align, null) == 3
 
 
 def test_zero_sized_problems_are_no_ops():
@@ -106,6 +121,9 @@ def test_zero_sized_problems_are_no_ops():
     assert _call("fp8bq_encode_e4m3", null, null, 0, 0, null) == 0
     assert _call("token_importance_weights", null, null, null, null, null, null, 0, ctypes.c_float(2.0), 1,
                  null) == 0
+    assert _call("moe_gather_quantize_act", null, null, 0, 5, 2, 256, null, null, null) == 0
+    assert _call("silu_mul_quantize_act", null, 0, 768, null, null, null, null) == 0
+    assert _call("moe_combine", null, null, null, 0, 8, 2048, 0, null, null) == 0
 
 
 def test_no_device_is_reported():
