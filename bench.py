@@ -306,7 +306,8 @@ def detail(fb, dev):
 
     # -- one MoE expert-FFN layer (Qwen3-30B-A3B: 4096 tokens, top-8 of 128
     #    experts, hidden 2048, expert FFN 768), every step on the GPU:
-    #    sort -> gather + 1x128 quant -> fc1 -> SiLU*up + 1x128 quant -> fc2 -> combine
+    #    sort -> 1x128 quant of the tokens -> fc1 (rows gathered by routed pair)
+    #    -> SiLU*up + 1x128 quant -> fc2 -> combine
     res["moe_layer_qwen3_30b_a3b"] = moe_layer(fb, dev)
     torch.cuda.empty_cache()
 
@@ -368,7 +369,7 @@ def moe_layer(fb, dev):
     w1q, w1s = fb.quantize_weight_blockwise(device_bf16_normal((E, 2 * F, H), 0.02, seed=600))
     w2q, w2s = fb.quantize_weight_blockwise(device_bf16_normal((E, H, F), 0.02, seed=601))
     off, sp, pr = fb.moe_sort_by_expert(ids, E)
-    a, a_s = fb.moe_gather_quantize_act(x, sp, k)
+    a, a_s = fb.quantize_act_per_token_group(x)
     y1 = torch.empty((R, 2 * F), dtype=torch.bfloat16, device=dev)
     h, h_s = torch.empty((R, F), dtype=torch.uint8, device=dev), torch.empty((R, F // 128), dtype=torch.float32,
                                                                                device=dev)
@@ -376,9 +377,9 @@ def moe_layer(fb, dev):
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     steps = {
         "sort": (lambda: fb.moe_sort_by_expert(ids, E, off, sp, pr), None, None),
-        "gather_quant": (lambda: fb.moe_gather_quantize_act(x, sp, k, a, a_s), T * H * 2 + R * H + R * (H // 128) * 4,
-                         None),
-        "fc1_gate_up": (lambda: fb.grouped_gemm_w8a8_blockscaled(a, a_s, w1q, w1s, off, y1), None, 2 * R * 2 * F * H),
+        "act_quant": (lambda: fb.quantize_act_per_token_group(x, a, a_s), T * H * 3 + T * (H // 128) * 4, None),
+        "fc1_gate_up": (lambda: fb.grouped_gemm_w8a8_blockscaled_gather(a, a_s, sp, k, w1q, w1s, off, y1), None,
+                        2 * R * 2 * F * H),
         "silu_mul_quant": (lambda: fb.silu_mul_quantize_act(y1, h, h_s), R * 2 * F * 2 + R * F + R * (F // 128) * 4,
                            None),
         "fc2_down": (lambda: fb.grouped_gemm_w8a8_blockscaled(h, h_s, w2q, w2s, off, y2), None, 2 * R * H * F),
@@ -394,7 +395,8 @@ def moe_layer(fb, dev):
         if flops is not None:
             n_out = 2 * F if name == "fc1_gate_up" else H
             k_in = H if name == "fc1_gate_up" else F
-            byt_g = R * k_in + E * n_out * k_in + 2 * R * n_out + R * (k_in // 128) * 4
+            a_rows = T if name == "fc1_gate_up" else R  # fc1 reads each token's row once (gathered)
+            byt_g = a_rows * k_in + E * n_out * k_in + 2 * R * n_out + a_rows * (k_in // 128) * 4
             roof = min(FP8_PEAK_TFLOPS, flops / byt_g * HBM_PEAK_GBPS / 1e3)
             e.update({"TFLOPs": round(flops / ms / 1e9, 1), "roofline_TFLOPs": round(roof, 1),
                       "frac_roofline": round(flops / ms / 1e9 / roof, 4)})

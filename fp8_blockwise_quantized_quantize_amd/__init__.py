@@ -5,8 +5,8 @@ devices and contiguity, allocates missing outputs with torch, and passes raw
 device pointers plus torch's current HIP stream to the C ABI declared in
 ``include/fp8bq.h``.  All arithmetic runs in the library's HIP kernels; there
 is no CPU fallback, and importing this package fails loudly when the built
-library is missing (build it with ``python -m
-fp8_blockwise_quantized_quantize_amd.build``).
+library is missing (build it with ``python
+fp8_blockwise_quantized_quantize_amd/build.py``).
 
 The operations follow "FP8-RL: A Practical and Stable Low-Precision Stack for
 LLM Reinforcement Learning" (paper-graph-ui summary page): §3.4.1 (E4M3,
@@ -28,6 +28,7 @@ __all__ = [
     "quantize_act_per_token_group",
     "gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled",
+    "grouped_gemm_w8a8_blockscaled_gather",
     "encode_e4m3",
     "token_importance_weights",
     "moe_sort_by_expert",
@@ -48,6 +49,7 @@ EXPORTS = (
     "quantize_act_per_token_group",
     "gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled",
+    "grouped_gemm_w8a8_blockscaled_gather",
     "fp8bq_encode_e4m3",
     "token_importance_weights",
     "moe_sort_by_expert",
@@ -64,7 +66,7 @@ class FP8BQError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m fp8_blockwise_quantized_quantize_amd.build`")
+            f"{LIB_PATH} is not built; run `python fp8_blockwise_quantized_quantize_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.fp8bq_status_string.argtypes = [i32]
@@ -73,6 +75,7 @@ def _load():
     lib.quantize_act_per_token_group.argtypes = [p, p, p, i64, i64, p]
     lib.gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p]
+    lib.grouped_gemm_w8a8_blockscaled_gather.argtypes = [p, p, i64, p, i64, p, p, p, p, i64, i64, i64, i64, p]
     lib.fp8bq_encode_e4m3.argtypes = [p, p, i64, i32, p]
     lib.token_importance_weights.argtypes = [p, p, p, p, p, p, i64, ctypes.c_float, i32, p]
     lib.moe_sort_by_expert.argtypes = [p, i64, i64, i64, p, p, p, p]
@@ -209,6 +212,32 @@ def grouped_gemm_w8a8_blockscaled(a, a_scale, w, w_scale, group_offsets, out=Non
         _check("grouped_gemm_w8a8_blockscaled",
                _lib.grouped_gemm_w8a8_blockscaled(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale),
                                                   _ptr(group_offsets), _ptr(_u16(out)), m, n, k, g, _stream(a)))
+    return out
+
+
+def grouped_gemm_w8a8_blockscaled_gather(a, a_scale, a_rows, a_row_div, w, w_scale, group_offsets, out=None):
+    """Output row m uses row a_rows[m] // a_row_div of a [M_a, K] and expert e's
+    weights for m in [off[e], off[e+1]); returns bfloat16 [len(a_rows), N]."""
+    m_a, k = a.shape
+    g, n, _ = w.shape
+    _require(a, "a", _U8, (m_a, k))
+    dev = a.device
+    m = a_rows.numel()
+    _require(a_scale, "a_scale", torch.float32, (m_a, k // BLOCK), dev)
+    _require(a_rows, "a_rows", torch.int32, (m,), dev)
+    _require(w, "w", _U8, (g, n, k), dev)
+    _require(w_scale, "w_scale", torch.float32, (g, _cdiv(n, BLOCK), k // BLOCK), dev)
+    _require(group_offsets, "group_offsets", torch.int32, (g + 1,), dev)
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", _BF16, (m, n), dev)
+    with torch.cuda.device(dev):
+        _check("grouped_gemm_w8a8_blockscaled_gather",
+               _lib.grouped_gemm_w8a8_blockscaled_gather(_ptr(a), _ptr(a_scale), m_a, _ptr(a_rows), int(a_row_div),
+                                                         _ptr(w), _ptr(w_scale), _ptr(group_offsets),
+                                                         _ptr(_u16(out)), m, n, k, g, _stream(a)))
     return out
 
 
@@ -364,8 +393,8 @@ def moe_expert_ffn(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale):
     E, H = w1.shape[0], x.shape[1]
     k = topk_ids.shape[1]
     offsets, sorted_pair, pair_row = moe_sort_by_expert(topk_ids, E)
-    a, a_s = moe_gather_quantize_act(x, sorted_pair, k)
-    y1 = grouped_gemm_w8a8_blockscaled(a, a_s, w1, w1_scale, offsets)
+    a, a_s = quantize_act_per_token_group(x)   # once per token; fc1 gathers the rows
+    y1 = grouped_gemm_w8a8_blockscaled_gather(a, a_s, sorted_pair, k, w1, w1_scale, offsets)
     h, h_s = silu_mul_quantize_act(y1)
     y2 = grouped_gemm_w8a8_blockscaled(h, h_s, w2, w2_scale, offsets)
     return moe_combine(y2, pair_row, topk_weights)

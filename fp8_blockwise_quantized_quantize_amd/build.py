@@ -1,7 +1,8 @@
 """Build libfp8bq.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: ``python -m fp8_blockwise_quantized_quantize_amd.build`` or
-``build_library()``.  The library is written next to this file.
+Usage: ``python fp8_blockwise_quantized_quantize_amd/build.py`` (this file
+is self-contained: running it does not import the package, whose import
+loads the library).  The library is written next to this file.
 """
 
 import glob

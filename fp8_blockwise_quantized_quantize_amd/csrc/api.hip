@@ -159,6 +159,38 @@ fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_
   }
 }
 
+fp8bq_status grouped_gemm_w8a8_blockscaled_gather(const uint8_t* a_fp8, const float* a_scale, int64_t M_a,
+                                                  const int32_t* a_rows, int64_t a_row_div, const uint8_t* w_fp8,
+                                                  const float* w_scale, const int32_t* group_offsets,
+                                                  uint16_t* y_bf16, int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                                  void* stream) {
+  try {
+    if (M_a < 0 || M_total < 0 || N < 0 || K < 0 || G < 0 || (K % 128) != 0 || K > kMaxGemmK)
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (a_row_div < 1 || a_row_div > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t ak, nk, gnk, mn, bytes;
+    if (!mul_ok(M_a, K, &ak) || ak >= (int64_t(1) << 31) || !mul_ok(N, K, &nk) || !mul_ok(nk, G, &gnk) ||
+        !mul_ok(M_total, N, &mn) || !mul_ok(mn, 2, &bytes))
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (G > 0 && M_total + 128 * G > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+    if (mn == 0) return FP8BQ_OK;
+    if (G == 0) return FP8BQ_ERR_BAD_SHAPE;
+    if (!y_bf16 || !group_offsets || !a_rows) return FP8BQ_ERR_NULL_PTR;
+    if (K > 0 && (!w_fp8 || !w_scale || (M_a > 0 && (!a_fp8 || !a_scale)))) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(y_bf16) || !aligned16(a_rows) || !aligned16(group_offsets) ||
+        (K > 0 && (!aligned16(w_fp8) || !aligned16(w_scale) || (M_a > 0 && (!aligned16(a_fp8) || !aligned16(a_scale))))))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_grouped_gemm_gather(a_fp8, a_scale, a_rows, a_row_div, M_a, w_fp8, w_scale,
+                                                      group_offsets, y_bf16, M_total, N, K, G,
+                                                      static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
 fp8bq_status fp8bq_encode_e4m3(const float* in, uint8_t* out, int64_t n, int method, void* stream) {
   try {
     if (n < 0 || method < 0 || method > 2) return FP8BQ_ERR_BAD_SHAPE;

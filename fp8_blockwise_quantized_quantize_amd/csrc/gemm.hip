@@ -164,7 +164,16 @@ struct Tile {
   // Rows of one K-block column are K bytes apart and land on few L2
   // channels; spreading the workgroups' K positions spreads the channels.
   int rot;
+  // Gathered activations (grouped GEMM only): output row m reads row
+  // a_rows[m] / a_div of a (of a_nrows rows); others read zeros.
+  const int32_t* a_rows;
+  int a_div;
+  int64_t a_nrows;
 };
+
+// A buffer offset past every record: the load returns zeros.  Buffers that
+// use it hold fewer than 2^31 bytes.
+constexpr int kOob = (int)0x80000000u;
 
 // Store four consecutive n of output row m (BF16, RNE).
 __device__ __forceinline__ void store4(uint16_t* __restrict__ y, int64_t N, int64_t m, int64_t n, v4f v) {
@@ -226,7 +235,9 @@ struct Skinny {
       swrow[i] = t.sw + (nt / kBlock) * KB;
     }
     // staging: lane owns chunk (lane & 7) of rows (lane >> 3) + 8 q; slice
-    // rows 0..BN-1 are weight rows, BN..BN+BM-1 activation rows
+    // rows 0..BN-1 are weight rows, BN..BN+BM-1 activation rows.  The row
+    // offset is part of the per-lane offset, which the buffer range check
+    // covers: rows past the tile's last row read zeros, never memory.
     const int lrow = lane >> 3, lchunk = lane & 7;
     const int gvoff = lrow * (int)K + lchunk * 16;
     const int svoff = r16 * KB * 4;  // + 16 j KB 4
@@ -244,11 +255,11 @@ struct Skinny {
       kb = kb < KB ? kb : kb - KB;
       const int koff = kb * kBlock;
 #pragma unroll
-      for (int q = 0; q < BN / 8; ++q) s.v[q] = bload16(wr, gvoff, koff + 8 * q * (int)K);
+      for (int q = 0; q < BN / 8; ++q) s.v[q] = bload16(wr, gvoff + 8 * q * (int)K, koff);
 #pragma unroll
-      for (int q = 0; q < BM / 8; ++q) s.v[BN / 8 + q] = bload16(ar, gvoff, koff + 8 * q * (int)K);
+      for (int q = 0; q < BM / 8; ++q) s.v[BN / 8 + q] = bload16(ar, gvoff + 8 * q * (int)K, koff);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) s.sav[j] = bload_f32(sr, svoff, kb * 4 + j * 16 * KB * 4);
+      for (int j = 0; j < TM; ++j) s.sav[j] = bload_f32(sr, svoff + j * 16 * KB * 4, kb * 4);
 #pragma unroll
       for (int i = 0; i < TN; ++i) s.swv[i] = swrow[i][kb];
     };
@@ -368,7 +379,12 @@ struct Panel {
   // multiples of 128 and the wave's share divides 128
   static constexpr bool kOneScaleBlock = (BN % kBlock == 0) && (kBlock % WNR == 0);
 
-  __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) {
+  __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) { run_impl<false>(t, lds); }
+  // activation rows gathered through t.a_rows (grouped GEMM)
+  __device__ static __forceinline__ void run_gather(const Tile& t, uint8_t* lds) { run_impl<true>(t, lds); }
+
+  template <bool kGather>
+  __device__ static __forceinline__ void run_impl(const Tile& t, uint8_t* lds) {
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wn = wave % WGN, wm = wave / WGN;
@@ -388,12 +404,29 @@ struct Panel {
     for (int i = 0; i < TN; ++i)
       if ((wrow0 + i * 16) / kBlock > nb0) hi_mask |= 1u << i;
     const auto wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
-    const auto ar = make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
+    const auto ar = kGather ? make_rsrc(t.a, t.a_nrows * K) : make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
     const int64_t am_lo = t.m_lo + wm * WMR;  // this wave's activation rows (scales)
     const int64_t am_hi = (am_lo + WMR < t.m_hi) ? am_lo + WMR : t.m_hi;
     const int64_t arows = am_hi > am_lo ? am_hi - am_lo : 0;
-    const auto sr = make_rsrc(t.sa + am_lo * KB, arows * KB * 4);
-    const int svoff = r16 * KB * 4;  // + 16 j KB 4
+    const auto sr = kGather ? make_rsrc(t.sa, t.a_nrows * KB * 4) : make_rsrc(t.sa + am_lo * KB, arows * KB * 4);
+    // Source row of output row m: itself, or the gathered row (-1: none).
+    auto src_row = [&](int64_t m) -> int64_t {
+      if (m >= t.m_hi) return -1;
+      if (!kGather) return m - t.m_lo;  // relative to the tile's buffer
+      const int32_t p = t.a_rows[m];
+      const int64_t r = p >= 0 ? p / t.a_div : -1;
+      return r < t.a_nrows ? r : -1;
+    };
+    // per-lane scale offsets of this wave's activation rows j * 16 + r16
+    const int svoff = r16 * KB * 4;
+    int svoff_g[kGather ? TM : 1];
+    if constexpr (kGather) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int64_t r = src_row(am_lo + j * 16 + r16);
+        svoff_g[j] = r >= 0 ? (int)(r * KB * 4) : kOob;
+      }
+    }
     // a ragged last tile (e.g. an expert's rows past a multiple of BM) can
     // leave whole waves without a valid activation row: they skip the MFMAs
     const bool idle = arows == 0;
@@ -401,7 +434,19 @@ struct Panel {
     // DMA staging: load q of wave w fills stage rows R0..R0+7 with
     // R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at physical chunk
     // l%8, so it fetches logical chunk (l%8) ^ (l/8) (the XOR swizzle).
-    const int dvoff = (lane >> 3) * (int)K + (((lane & 7) ^ (lane >> 3)) << 4);
+    // The row offset is part of the per-lane offset, which the buffer range
+    // check covers: rows past the tile's last row read zeros, never memory.
+    const int chunk_off = ((lane & 7) ^ (lane >> 3)) << 4;
+    const int dvoff = (lane >> 3) * (int)K + chunk_off;
+    // gathered activations: the offset of this lane's row in each A load
+    int aoff[kGather ? BM / 64 : 1];
+    if constexpr (kGather) {
+#pragma unroll
+      for (int qa = 0; qa < BM / 64; ++qa) {
+        const int64_t r = src_row(t.m_lo + 8 * (8 * (BN / 64 + qa) + wave) - BN + (lane >> 3));
+        aoff[qa] = r >= 0 ? (int)(r * K) + chunk_off : kOob;
+      }
+    }
     const FragLds fl(lane);
 
     v4f acc[TN][TM];
@@ -415,9 +460,11 @@ struct Panel {
       const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
       auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
       if (q < BN / 64)  // stage rows 0..BN-1: weight rows n0 + r0 ..
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff, koff + r0 * (int)K, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, koff, 0, 0);
+      else if (kGather)  // stage rows BN..: the gathered activation rows
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, aoff[kGather ? q - BN / 64 : 0], koff, 0, 0);
       else              // stage rows BN..: activation rows m_lo + r0 - BN ..
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff, koff + (r0 - BN) * (int)K, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff + (r0 - BN) * (int)K, koff, 0, 0);
     };
     // Per-K-block scales of this wave's activation rows and weight block(s),
     // fetched one phase ahead with vector loads (tracked by vmcnt, so using
@@ -430,7 +477,8 @@ struct Panel {
       c.sw0 = bload_f32(swr0, 0, kb * 4);
       c.sw1 = kOneScaleBlock ? c.sw0 : bload_f32(swr1, 0, kb * 4);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) c.sa[j] = bload_f32(sr, svoff, kb * 4 + j * 16 * KB * 4);
+      for (int j = 0; j < TM; ++j)
+        c.sa[j] = bload_f32(sr, kGather ? svoff_g[kGather ? j : 0] : svoff + j * 16 * KB * 4, kb * 4);
     };
     constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
     auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * WNR + i * 16); };
@@ -574,17 +622,21 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   t.n0 = tn * BN;
   t.N = N; t.K = K;
   t.rot = Kern::kRotate ? (int)((L * Kern::kRotStride) % (K / kBlock > 0 ? K / kBlock : 1)) : 0;
+  t.a_rows = nullptr; t.a_div = 1; t.a_nrows = 0;
   Kern::run(t, smem);
 }
 
 // Grouped form: workgroup slot s is mapped to (expert, m-tile) by a prefix
 // sum over ceil(rows_e / BM) computed in the workgroup from the device
 // offsets; slots past the last tile exit.  Offsets are clamped to [0, M].
-template <class Kern, int BN, int BM>
+// kGather: activation row m is row a_rows[m] / a_div of a (the MoE token
+// of a routed pair), read straight from the token-major buffer.
+template <class Kern, int BN, int BM, bool kGather>
 __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_grouped_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ w,
     const float* __restrict__ sw, const int32_t* __restrict__ offsets, uint16_t* __restrict__ y, int64_t M,
-    int64_t N, int64_t K, int G, int64_t slots, int64_t tiles_n) {
+    int64_t N, int64_t K, int G, int64_t slots, int64_t tiles_n, const int32_t* __restrict__ a_rows, int a_div,
+    int64_t a_nrows) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int NT = threads_of<Kern>();
   __shared__ int found_e, found_t;
@@ -644,7 +696,11 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   t.n0 = tn * BN;
   t.N = N; t.K = K;
   t.rot = 0;
-  Kern::run(t, smem);
+  t.a_rows = a_rows; t.a_div = a_div; t.a_nrows = a_nrows;
+  if constexpr (kGather)
+    Kern::run_gather(t, smem);
+  else
+    Kern::run(t, smem);
 }
 
 enum class Cfg { kSkinny64x64, kSkinny96x64, kWide, kDecodePanel };
@@ -699,18 +755,31 @@ Cfg tile_for(int64_t M, int64_t N, int64_t K) {
   return choose(M, N, K);
 }
 
-template <class Kern>
+template <class Kern, bool kGather>
 hipError_t launch_grouped_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                               const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
-                              hipStream_t stream) {
+                              const int32_t* a_rows, int a_div, int64_t a_nrows, hipStream_t stream) {
   const int64_t tiles_n = (N + Kern::BN - 1) / Kern::BN;
   const int64_t slots = (M + Kern::BM - 1) / Kern::BM + G;  // >= sum_e ceil(rows_e / BM)
   const int64_t blocks = tiles_n * slots;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_grouped_kernel<Kern, Kern::BN, Kern::BM>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_grouped_kernel<Kern, Kern::BN, Kern::BM, kGather>), dim3((unsigned)blocks),
                      dim3(Kern::kThreadsPerWg), (size_t)Kern::kLdsBytes, stream, a, sa, w, sw, offsets, y, M, N, K,
-                     (int)G, slots, tiles_n);
+                     (int)G, slots, tiles_n, a_rows, a_div, a_nrows);
   return hipGetLastError();
+}
+
+template <bool kGather>
+hipError_t launch_grouped_any(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                              const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
+                              const int32_t* a_rows, int a_div, int64_t a_nrows, hipStream_t stream) {
+  if (M == 0 || N == 0 || G == 0) return hipSuccess;
+  // the expert tiles: 128 x 256 panels when the override asks for them
+  const char* e = std::getenv("FP8BQ_GEMM_TILE");
+  if (e != nullptr && std::strcmp(e, "decode_panel") == 0)
+    return launch_grouped_cfg<DecodePanel, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows,
+                                                    stream);
+  return launch_grouped_cfg<Wide, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows, stream);
 }
 
 }  // namespace
@@ -733,12 +802,13 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                                const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
                                hipStream_t stream) {
-  if (M == 0 || N == 0 || G == 0) return hipSuccess;
-  // the expert tiles: 128 x 256 panels when the override asks for them
-  const char* e = std::getenv("FP8BQ_GEMM_TILE");
-  if (e != nullptr && std::strcmp(e, "decode_panel") == 0)
-    return launch_grouped_cfg<DecodePanel>(a, sa, w, sw, offsets, y, M, N, K, G, stream);
-  return launch_grouped_cfg<Wide>(a, sa, w, sw, offsets, y, M, N, K, G, stream);
+  return launch_grouped_any<false>(a, sa, w, sw, offsets, y, M, N, K, G, nullptr, 1, 0, stream);
+}
+
+hipError_t launch_grouped_gemm_gather(const uint8_t* a, const float* sa, const int32_t* a_rows, int64_t a_div,
+                                      int64_t a_nrows, const uint8_t* w, const float* sw, const int32_t* offsets,
+                                      uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G, hipStream_t stream) {
+  return launch_grouped_any<true>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, (int)a_div, a_nrows, stream);
 }
 
 }  // namespace fp8bq

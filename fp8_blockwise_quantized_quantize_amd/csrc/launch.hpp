@@ -19,6 +19,10 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t*
                                const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
                                hipStream_t stream);
 
+hipError_t launch_grouped_gemm_gather(const uint8_t* a, const float* sa, const int32_t* a_rows, int64_t a_div,
+                                      int64_t a_nrows, const uint8_t* w, const float* sw, const int32_t* offsets,
+                                      uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G, hipStream_t stream);
+
 hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int method, hipStream_t stream);
 
 hipError_t launch_importance_weights(const float* logp_train, const float* logp_rollout, const uint8_t* mask,

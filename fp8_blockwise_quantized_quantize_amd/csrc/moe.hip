@@ -25,12 +25,16 @@ namespace {
 // Sort by expert.  One workgroup per expert e, no atomics, deterministic:
 //   first row of e = number of pairs routed to experts below e;
 //   row of pair p   = first row + number of pairs q < p routed to e.
-// Pass 1 counts the first; pass 2 ranks e's pairs with a wave ballot and a
-// cross-wave prefix, chunk by chunk in pair order (so rows keep pair order).
-// Every workgroup reads the whole id list, which stays in L2.
+// The pairs are taken in rounds of kSortThreads * kSortRun; in a round each
+// thread owns kSortRun consecutive pairs, loaded at once.  Pass 1 counts the
+// pairs below e; pass 2 ranks e's pairs with one block-wide exclusive scan of
+// the per-thread counts per round, so rows keep pair order.  Every
+// workgroup reads the whole id list, which stays in L2.
 // ---------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
+constexpr int kSortRun = 32;
+constexpr int32_t kSortRound = kSortThreads * kSortRun;
 
 __device__ __forceinline__ int wave_sum_i32(int v) {
 #pragma unroll
@@ -38,9 +42,32 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan_i32(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    v += lane >= off ? o : 0;
+  }
+  return v;
+}
+
+// The kSortRun ids from p0 (16-byte loads when the run is whole; -1 past P).
+__device__ __forceinline__ void load_run(const int32_t* __restrict__ ids, int32_t p0, int32_t P,
+                                         int32_t (&id)[kSortRun]) {
+  if (p0 + kSortRun <= P) {
+#pragma unroll
+    for (int i = 0; i < kSortRun; i += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(ids + p0 + i);
+      id[i] = v.x;
+      id[i + 1] = v.y;
+      id[i + 2] = v.z;
+      id[i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSortRun; ++i) id[i] = (p0 + i < P) ? ids[p0 + i] : -1;
+  }
 }
 
 __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* __restrict__ ids, int32_t P, int32_t E,
@@ -52,9 +79,12 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* _
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   int below = 0;
-  for (int32_t p = tid; p < P; p += kSortThreads) {
-    const int32_t id = ids[p];
-    below += (id >= 0 && id < e) ? 1 : 0;
+  for (int32_t base = 0; base < P; base += kSortRound) {
+    const int32_t p0 = base + tid * kSortRun;
+    int32_t id[kSortRun];
+    load_run(ids, p0, P, id);
+#pragma unroll
+    for (int i = 0; i < kSortRun; ++i) below += (id[i] >= 0 && id[i] < e) ? 1 : 0;
   }
   below = wave_sum_i32(below);
   if (lane == 0) part[wave] = below;
@@ -64,32 +94,39 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* _
   for (int w = 0; w < kSortWaves; ++w) first += part[w];
   __syncthreads();
 
-  int32_t running = 0;
-  for (int32_t base = 0; base < P; base += kSortThreads) {
-    const int32_t p = base + tid;
-    const int32_t id = p < P ? ids[p] : -1;
-    const bool mine = id == e;
-    const uint64_t mask = __ballot(mine);
-    if (lane == 0) part[wave] = __popcll(mask);
+  int32_t running = first;
+  for (int32_t base = 0; base < P; base += kSortRound) {
+    const int32_t p0 = base + tid * kSortRun;
+    int32_t id[kSortRun];
+    load_run(ids, p0, P, id);
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < kSortRun; ++i) mine += id[i] == e ? 1 : 0;
+    const int incl = wave_scan_i32(mine, lane);
+    if (lane == 63) part[wave] = incl;
     __syncthreads();
-    int32_t before = 0, chunk = 0;
+    int32_t before = 0, round_total = 0;
 #pragma unroll
     for (int w = 0; w < kSortWaves; ++w) {
       before += (w < wave) ? part[w] : 0;
-      chunk += part[w];
+      round_total += part[w];
     }
-    if (mine) {
-      const int32_t r = first + running + before + static_cast<int32_t>(lanes_below(mask));
-      sorted_pair[r] = p;
-      pair_row[p] = r;
+    int32_t r = running + before + (incl - mine);
+#pragma unroll
+    for (int i = 0; i < kSortRun; ++i) {
+      if (id[i] == e) {
+        sorted_pair[r] = p0 + i;
+        pair_row[p0 + i] = r;
+        ++r;
+      }
+      if (e == 0 && p0 + i < P && (id[i] < 0 || id[i] >= E)) pair_row[p0 + i] = -1;  // no expert, no row
     }
-    if (e == 0 && p < P && (id < 0 || id >= E)) pair_row[p] = -1;  // no expert, no row
-    running += chunk;
+    running += round_total;
     __syncthreads();
   }
   if (tid == 0) {
     offsets[e] = first;
-    if (e == E - 1) offsets[E] = first + running;
+    if (e == E - 1) offsets[E] = running;
   }
 }
 
@@ -114,34 +151,60 @@ __device__ __forceinline__ float quarter_wave_scale(u32x4 v) {
 // Gathered activation rows: row r of the output is token sorted_pair[r] / k
 // of x, quantized in 1x128 groups (the same codes as quantizing x and then
 // copying rows).  Rows whose pair names no token are written as zeros.
+// One wave per row: the row's token is a scalar load, and each lane issues
+// its 16-byte loads for all groups of the row before any of them is used;
+// in pass i the quarter wave q handles group 4 i + q.
+constexpr int kGatherRowsPerBlock = kGroupThreads / 64;
+
 __global__ __launch_bounds__(kGroupThreads) void gather_quant_act_kernel(const uint16_t* __restrict__ x,
                                                                          const int32_t* __restrict__ sorted_pair,
                                                                          uint8_t* __restrict__ q,
                                                                          float* __restrict__ scale, int64_t R,
                                                                          int64_t T, int32_t k, int64_t K, int G) {
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4);
-  if (gid >= R * G) return;  // the 16 lanes of a group leave together
-  const int li = threadIdx.x & 15;
-  const int64_t r = gid / G;
-  const int g = static_cast<int>(gid % G);
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kGatherRowsPerBlock +
+                    __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (r >= R) return;  // whole waves leave
+  const int lane = threadIdx.x & 63, li = lane & 15, quarter = lane >> 4;
   const int32_t pair = sorted_pair[r];
   const int64_t t = pair >= 0 ? pair / k : -1;
-  const int64_t col = static_cast<int64_t>(g) * kBlock + li * 8;
-  u32x4 v = u32x4{0u, 0u, 0u, 0u};
-  if (t >= 0 && t < T) v = *reinterpret_cast<const u32x4*>(x + t * K + col);
-  const float s = quarter_wave_scale(v);
-  if (li == 0) scale[r * G + g] = s;
-  *reinterpret_cast<u32x2*>(q + r * K + col) = encode8(v, s);
+  const bool ok = t >= 0 && t < T;
+  const uint16_t* src = x + (ok ? t : 0) * K;
+  uint8_t* dst = q + r * K;
+  constexpr int kPassesMax = 8;  // rows of up to 32 groups (K <= 4096) in registers
+  for (int g0 = 0; g0 < G; g0 += 4 * kPassesMax) {
+    u32x4 v[kPassesMax];
+#pragma unroll
+    for (int i = 0; i < kPassesMax; ++i) {
+      const int g = g0 + 4 * i + quarter;
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (ok && g < G) v[i] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(g) * kBlock + li * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kPassesMax; ++i) {
+      const int g = g0 + 4 * i + quarter;
+      if (g0 + 4 * i >= G) break;  // uniform: no group of this pass exists
+      const float s = quarter_wave_scale(v[i]);
+      if (g < G) {
+        if (li == 0) scale[r * G + g] = s;
+        *reinterpret_cast<u32x2*>(dst + static_cast<int64_t>(g) * kBlock + li * 8) = encode8(v[i], s);
+      }
+    }
+  }
 }
 
 // h = SiLU(g) * u rounded to BF16, correctly rounded from the exact value.
-// Fast path in float32: with |g| <= 80 and no underflow or overflow, the
-// computed h32 = fl(fl(g / fl(1 + expf(-g))) * u) is within 2^-21 relative of
-// the exact value (expf within 2 ulp, three correctly rounded operations), so
-// its BF16 rounding is the exact value's whenever h32 is more than 32 float32
-// ulps away from a BF16 midpoint (low 16 bits 0x8000).  Otherwise (about one
-// value in a thousand, and every value outside the fast range) the product
-// is formed in float64 and rounded straight to BF16.
+// Fast path in float32 for |g| <= 80:
+//   e^-g = 2^x, x = -g log2(e), split exactly as x = xh + xl (xh = fl(-g L)
+//   with L = fl32(log2 e), xl = the product's rounding error by fma plus
+//   -g (log2 e - L)); t = v_exp_f32(xh) * (1 + xl ln 2) (|xl| < 2^-17, the
+//   dropped terms are below 2^-33); h32 = fl(fl(g * rcp(fl(1 + t))) * u).
+// With v_exp_f32 and v_rcp_f32 within 2 ulp each, h32 is within 3 * 2^-22
+// (relative) of the exact value, i.e. within 12 float32 ulps, so its BF16
+// rounding is the exact value's whenever h32 is more than 48 float32 ulps
+// away from a BF16 midpoint (low 16 bits 0x8000), and |h32| is in the
+// normal range.  Otherwise (about one value in 700, and every value outside
+// the fast range) the product is formed in float64 and rounded straight to
+// BF16.
 //
 // Two regimes put the exact value structurally close to a midpoint, closer
 // than float64 resolves: for |g| < 2^-20, SiLU(g) u = a (1 + g/2 + O(g^2))
@@ -184,13 +247,20 @@ __device__ __noinline__ uint32_t silu_mul_bf16_f64(float g, float u) {
 
 __device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
   if (fabsf(g) <= 80.0f) {
-    const float h = (g / (1.0f + expf(-g))) * u;
+    constexpr float kLog2e = 1.44269502162933349609375f;      // fl32(log2 e)
+    constexpr float kLog2eLo = 1.925963033500011079e-8f;      // log2 e - kLog2e
+    constexpr float kLn2 = 0.693147180559945309f;
+    const float xh = -g * kLog2e;
+    const float xl = fmaf(-g, kLog2e, -xh) + (-g) * kLog2eLo;
+    const float p = __builtin_amdgcn_exp2f(xh);
+    const float t = fmaf(p, xl * kLn2, p);
+    const float h = (g * __builtin_amdgcn_rcpf(1.0f + t)) * u;
     const uint32_t b = __float_as_uint(h);
     const float ah = fabsf(h);
     const uint32_t low = b & 0xffffu;
     const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;
     if (h == 0.0f) return b >> 16;
-    if (ah >= 0x1p-100f && ah <= 0x1p120f && dist > 32u) return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+    if (ah >= 0x1p-100f && ah <= 0x1p120f && dist > 48u) return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
   }
   return silu_mul_bf16_f64(g, u);
 }
@@ -286,8 +356,8 @@ hipError_t launch_moe_sort(const int32_t* ids, int64_t P, int64_t E, int32_t* of
 hipError_t launch_gather_quant_act(const uint16_t* x, const int32_t* sorted_pair, int64_t R, int64_t T, int64_t k,
                                    int64_t K, uint8_t* q, float* scale, hipStream_t stream) {
   const int64_t G = K / kBlock;
-  const int64_t blocks = group_blocks(R * G);
-  if (blocks == 0) return hipSuccess;
+  if (R == 0 || G == 0) return hipSuccess;
+  const int64_t blocks = (R + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gather_quant_act_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kGroupThreads), 0, stream, x,
                      sorted_pair, q, scale, R, T, static_cast<int32_t>(k), K, static_cast<int>(G));

@@ -143,6 +143,27 @@ fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_
                                            int64_t M_total, int64_t N, int64_t K, int64_t G, void* stream);
 
 /*
+ * grouped_gemm_w8a8_blockscaled_gather -- the grouped GEMM with its
+ * activation rows gathered: output row m (expert e owns rows
+ * [group_offsets[e], group_offsets[e+1]) as above) multiplies row
+ * a_rows[m] / a_row_div of a_fp8 with expert e's weights.  With a_rows the
+ * sorted_pair of moe_sort_by_expert and a_row_div = k, the MoE fc1 reads the
+ * token-major FP8 activations (quantize_act_per_token_group of the tokens)
+ * directly, and no per-pair copy of them is made ([FP8-RL summary] §3.4.1
+ * "Quantization Scope", MoE fc1 / fc2).
+ *   a_fp8 [M_a][K], a_scale [M_a][K/128]; a_rows [M_total] int32 (entries
+ *   that are negative or name a row >= M_a give a zero activation row);
+ *   a_row_div >= 1; w_fp8, w_scale, group_offsets and y_bf16 [M_total][N]
+ *   as in grouped_gemm_w8a8_blockscaled.  M_a * K < 2^31; K as for
+ *   gemm_w8a8_blockscaled.
+ */
+fp8bq_status grouped_gemm_w8a8_blockscaled_gather(const uint8_t* a_fp8, const float* a_scale, int64_t M_a,
+                                                  const int32_t* a_rows, int64_t a_row_div, const uint8_t* w_fp8,
+                                                  const float* w_scale, const int32_t* group_offsets,
+                                                  uint16_t* y_bf16, int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                                  void* stream);
+
+/*
  * fp8bq_encode_e4m3 -- the library's float32 -> E4M3 conversion on its own
  * ([FP8-RL summary] §3.4.1 "Quantization Format and Granularity"; round to
  * nearest even, sign of zero kept), so that it can be checked over every

@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     for n in ["quantize_weight_blockwise", "quantize_act_per_token_group", "gemm_w8a8_blockscaled",
               "grouped_gemm_w8a8_blockscaled", "fp8bq_status_string", "fp8bq_encode_e4m3",
               "token_importance_weights", "moe_sort_by_expert", "moe_gather_quantize_act",
-              "silu_mul_quantize_act", "moe_combine"]:
+              "silu_mul_quantize_act", "moe_combine", "grouped_gemm_w8a8_blockscaled_gather"]:
         assert n in names, names
 
 
@@ -95,6 +95,13 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call(iw, null, good, null, null, good, null, 16, F(2.0), 0, null) == 1
     assert _call(iw, good, good, bad_align, null, good, null, 16, F(2.0), 0, null) == 3
     assert _call(iw, good, good, null, good, good, bad_align, 16, F(2.0), 0, null) == 3
+    # gathered grouped GEMM: K % 128, row divisor, M_a * K >= 2^31, null row map
+    gg = "grouped_gemm_w8a8_blockscaled_gather"
+    assert _call(gg, good, good, 4, good, 1, good, good, good, good, 4, 4, 100, 2, null) == 2
+    assert _call(gg, good, good, 4, good, 0, good, good, good, good, 4, 4, 128, 2, null) == 2
+    assert _call(gg, good, good, 1 << 20, good, 1, good, good, good, good, 4, 4, 4096, 2, null) == 2
+    assert _call(gg, good, good, 4, null, 1, good, good, good, good, 4, 4, 128, 2, null) == 1
+    assert _call(gg, good, good, 4, good, 1, good, good, good, bad_align, 4, 4, 128, 2, null) == 3
     # MoE glue
     assert _call("moe_sort_by_expert", good, 4, 2, 0, good, good, good, null) == 2      # no expert
     assert _call("moe_sort_by_expert", good, 1 << 20, 1 << 12, 8, good, good, good, null) == 2  # > 2^31 pairs

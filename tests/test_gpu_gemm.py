@@ -193,6 +193,42 @@ def test_grouped_small(fb, monkeypatch, tile, counts):
             assert_gemm_close(y[lo:hi], ref[lo:hi])
 
 
+@pytest.mark.parametrize("tile", ["wide", "decode_panel"])
+@pytest.mark.parametrize("counts,div", [([3, 0, 17, 1, 0], 1), ([0, 128, 0, 1, 255, 0, 0, 2], 8), ([257, 511, 70], 3),
+                                        ([1] * 40, 2)])
+def test_grouped_gather(fb, monkeypatch, tile, counts, div):
+    """Row m of the output uses row a_rows[m] // div of a (MoE tokens read
+    through their routed pairs); rows naming no row of a give zeros."""
+    announce("grouped gather", tile, counts, div)
+    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
+    n, k = 256, 384
+    g = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    m = int(off[-1])
+    m_a = max(7, m // 3)
+    x, _ = activations(m_a, k, (70 + g, 0))
+    w = bf16_normal((g, n, k), 0.02, (70 + g, 1))
+    qa, sa = oracle.quant_act_per_token_group(x)
+    qw, sw = oracle.quant_weight_blockwise(w)
+    rng = np.random.default_rng(71 + g)
+    rows = rng.integers(0, m_a * div, size=m).astype(np.int32)
+    if m > 4:
+        rows[1] = -5               # no row
+        rows[m // 2] = m_a * div   # one past the last row
+    y = device_to_bits(fb.grouped_gemm_w8a8_blockscaled_gather(_dev(qa), _dev(sa), _dev(rows), div, _dev(qw),
+                                                                _dev(sw), _dev(off)))
+    src = rows // div
+    valid = (rows >= 0) & (src < m_a)
+    qg = np.where(valid[:, None], qa[np.clip(src, 0, m_a - 1)], 0).astype(np.uint8)
+    sg = np.where(valid[:, None], sa[np.clip(src, 0, m_a - 1)], 0).astype(np.float32)
+    ref = oracle.grouped_gemm_ref(qg, sg, qw, sw, off)
+    for e in range(g):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            assert_gemm_close(y[lo:hi], ref[lo:hi])
+    assert np.all(y[~valid] == 0)
+
+
 def test_grouped_single_group_equals_dense(fb):
     announce("grouped G=1 vs dense")
     qa, sa, qw, sw, off = _grouped_oracle_inputs([200], 384, 512, 60)
