@@ -34,6 +34,8 @@ Modules
            and its ragged grouped (MoE) form.
 ``moe``    MoE expert-FFN glue: pairs sorted by expert, gathered FP8 rows,
            SiLU(gate) * up -> BF16 -> 1x128 groups, the weighted combine.
+``kv``     FP8 KV cache: per-step K/V scale calibration, quantizing cache
+           write into token slots ([FP8-RL summary] §3.4.4).
 ``tis``    token-level importance weights of the rollout correction
            ([FP8-RL summary] §3.4.3): TIS clipping and MIS masking.
 
@@ -68,6 +70,7 @@ from .gemm import (
     grouped_gemm_ref,
 )
 from .tis import importance_weights
+from .kv import kv_calibrate, kv_quantize, kv_cache_write
 from .moe import sort_by_expert, gather_quantize_act, silu_mul_bf16, silu_mul_quantize, combine
 
 __all__ = [
@@ -94,4 +97,7 @@ __all__ = [
     "silu_mul_bf16",
     "silu_mul_quantize",
     "combine",
+    "kv_calibrate",
+    "kv_quantize",
+    "kv_cache_write",
 ]
