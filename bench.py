@@ -271,6 +271,41 @@ def _time_ms(fn, reps, warm=2):
     return v[len(v) // 2], v[0]
 
 
+def _time_graph_ms(fn, calls=10, reps=5):
+    """Median GPU time per call of `fn`, from replays of a HIP graph holding
+    `calls` back-to-back calls (host call overhead excluded: small kernels
+    would otherwise be timed at the speed of their Python wrapper).  Falls
+    back to per-call events when the calls cannot be captured."""
+    import torch
+
+    try:
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(calls):
+                    fn()
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) / calls)
+        times.sort()
+        return times[len(times) // 2], times[0]
+    except RuntimeError:
+        return _time_ms(fn, reps=10)
+
+
 def detail(fb, dev):
     import torch
 
@@ -290,8 +325,8 @@ def detail(fb, dev):
         wq, ws = fb.quantize_weight_blockwise(w)
         xq, xs = fb.quantize_act_per_token_group(x)
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        ms, ms_min = _time_ms(lambda: fb.gemm_w8a8_blockscaled(xq, xs, wq, ws, y), reps=10)
-        aq_ms, _ = _time_ms(lambda: fb.quantize_act_per_token_group(x, xq, xs), reps=10)
+        ms, ms_min = _time_graph_ms(lambda: fb.gemm_w8a8_blockscaled(xq, xs, wq, ws, y), calls=4)
+        aq_ms, _ = _time_graph_ms(lambda: fb.quantize_act_per_token_group(x, xq, xs))
         f = 2 * m * n * k
         tot_f += f
         tot_ms += ms
@@ -333,6 +368,12 @@ def detail(fb, dev):
     del bufs
     torch.cuda.empty_cache()
 
+    # -- FP8 KV cache, one Qwen3-8B layer (8 KV heads x 128): a rollout's first
+    #    forward calibrates the per-head scales on a 16384-token prefill chunk
+    #    and writes it to the cache; a decode step then writes 1536 tokens
+    res["kv_cache_qwen3_8b_layer"] = kv_cache(fb, dev)
+    torch.cuda.empty_cache()
+
     # -- token-level TIS weights of one training batch (512 responses padded
     #    to 20,000 tokens), fused with the response mask and w * advantage
     from synthetic import ROLLOUT_TRAIN_BATCH, rollout_batch
@@ -342,8 +383,8 @@ def detail(fb, dev):
     msk = torch.from_numpy(rb["mask"]).to(dev)
     w = torch.empty_like(lt)
     wa = torch.empty_like(lt)
-    ms, ms_min = _time_ms(lambda: fb.token_importance_weights(lt, lr, C=2.0, mode="tis", mask=msk, advantages=adv,
-                                                              out=w, out_adv=wa), reps=20)
+    ms, ms_min = _time_graph_ms(lambda: fb.token_importance_weights(lt, lr, C=2.0, mode="tis", mask=msk,
+                                                                    advantages=adv, out=w, out_adv=wa))
     slots, valid = lt.numel(), int(rb["mask"].sum())
     byt = importance_weight_bytes(slots, valid)
     gbps = byt / ms / 1e6
@@ -387,7 +428,7 @@ def moe_layer(fb, dev):
     }
     res, total = {}, 0.0
     for name, (fn, byt, flops) in steps.items():
-        ms, _ = _time_ms(fn, reps=10)
+        ms, _ = _time_graph_ms(fn)
         total += ms
         e = {"us": round(ms * 1e3, 1)}
         if byt is not None:
@@ -405,10 +446,40 @@ def moe_layer(fb, dev):
     def layer():
         fb.moe_expert_ffn(x, ids, tw, w1q, w1s, w2q, w2s)
 
-    layer_ms, _ = _time_ms(layer, reps=10)
+    layer_ms, _ = _time_graph_ms(layer, calls=4)
     res["sum_of_kernels_us"] = round(total * 1e3, 1)
     res["layer_us"] = round(layer_ms * 1e3, 1)
     res["layer_TFLOPs"] = round((2 * R * 2 * F * H + 2 * R * H * F) / layer_ms / 1e9, 1)
+    return res
+
+
+def kv_cache(fb, dev):
+    import torch
+
+    from synthetic import device_bf16_normal
+
+    H, D, T, B = 8, 128, 16384, 1536
+    S = T + B
+    k = device_bf16_normal((T, H, D), 1.0, seed=900)
+    v = device_bf16_normal((T, H, D), 1.0, seed=901)
+    kn = device_bf16_normal((B, H, D), 1.0, seed=902)
+    vn = device_bf16_normal((B, H, D), 1.0, seed=903)
+    ks = torch.empty(H, dtype=torch.float32, device=dev)
+    vs = torch.empty(H, dtype=torch.float32, device=dev)
+    kc = torch.empty((S, H, D), dtype=torch.uint8, device=dev)
+    vc = torch.empty((S, H, D), dtype=torch.uint8, device=dev)
+    slots = torch.arange(T, dtype=torch.int32, device=dev)
+    dslots = torch.arange(T, S, dtype=torch.int32, device=dev)
+    res = {}
+    cal_ms, _ = _time_graph_ms(lambda: fb.kv_scale_calibrate(k, v, True, ks, vs))
+    cal_b = 2 * T * H * D * 2
+    wr_ms, _ = _time_graph_ms(lambda: fb.kv_cache_write_fp8(k, v, slots, ks, vs, kc, vc))
+    wr_b = 2 * T * H * D * 3 + T * 4
+    dec_ms, _ = _time_graph_ms(lambda: fb.kv_cache_write_fp8(kn, vn, dslots, ks, vs, kc, vc))
+    for name, ms, byt in (("calibrate_16384", cal_ms, cal_b), ("write_16384", wr_ms, wr_b),
+                          ("decode_write_1536", dec_ms, 2 * B * H * D * 3 + B * 4)):
+        res[name] = {"us": round(ms * 1e3, 1), "bytes": byt, "GBps": round(byt / ms / 1e6, 1),
+                     "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)}
     return res
 
 

@@ -36,6 +36,8 @@ __all__ = [
     "silu_mul_quantize_act",
     "moe_combine",
     "moe_expert_ffn",
+    "kv_scale_calibrate",
+    "kv_cache_write_fp8",
     "status_string",
 ]
 
@@ -56,6 +58,8 @@ EXPORTS = (
     "moe_gather_quantize_act",
     "silu_mul_quantize_act",
     "moe_combine",
+    "kv_scale_calibrate",
+    "kv_cache_write_fp8",
 )
 
 
@@ -82,6 +86,8 @@ def _load():
     lib.moe_gather_quantize_act.argtypes = [p, p, i64, i64, i64, i64, p, p, p]
     lib.silu_mul_quantize_act.argtypes = [p, i64, i64, p, p, p, p]
     lib.moe_combine.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
+    lib.kv_scale_calibrate.argtypes = [p, p, i64, i64, i64, i32, p, p, p]
+    lib.kv_cache_write_fp8.argtypes = [p, p, p, p, p, i32, p, p, i64, i64, i64, i64, p]
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = i32
     return lib
@@ -398,6 +404,60 @@ def moe_expert_ffn(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale):
     h, h_s = silu_mul_quantize_act(y1)
     y2 = grouped_gemm_w8a8_blockscaled(h, h_s, w2, w2_scale, offsets)
     return moe_combine(y2, pair_row, topk_weights)
+
+
+def kv_scale_calibrate(k, v=None, per_head=True, k_scale=None, v_scale=None):
+    """K (and V) BF16 [T, H, D] of a rollout's first forward -> float32 scales
+    [H] (per_head) or [1]: s = fl32(max |x| / 448).  Returns (k_scale, v_scale)."""
+    if k.dim() != 3:
+        raise ValueError("k must be [tokens, heads, head_dim]")
+    T, H, D = k.shape
+    dev = k.device
+    _require(k, "k", _BF16, (T, H, D))
+    if v is not None:
+        _require(v, "v", _BF16, (T, H, D), dev)
+    n = H if per_head else 1
+    if k_scale is None:
+        k_scale = torch.empty(n, dtype=torch.float32, device=dev)
+    _require(k_scale, "k_scale", torch.float32, (n,), dev)
+    if v is not None:
+        if v_scale is None:
+            v_scale = torch.empty(n, dtype=torch.float32, device=dev)
+        _require(v_scale, "v_scale", torch.float32, (n,), dev)
+    else:
+        v_scale = None
+    with torch.cuda.device(dev):
+        _check("kv_scale_calibrate",
+               _lib.kv_scale_calibrate(_ptr(_u16(k)), _ptr(None if v is None else _u16(v)), T, H, D, int(bool(per_head)),
+                                       _ptr(k_scale), _ptr(v_scale), _stream(k)))
+    return k_scale, v_scale
+
+
+def kv_cache_write_fp8(k, v, slot_mapping, k_scale, v_scale, k_cache, v_cache=None):
+    """Quantize K (and V) BF16 [T, H, D] with fixed scales and store token t in
+    slot slot_mapping[t] (int32 [T]; out of range = padding) of the E4M3
+    caches [S, H, D] (uint8).  Per-head scales have H entries, per-layer 1."""
+    T, H, D = k.shape
+    dev = k.device
+    _require(k, "k", _BF16, (T, H, D))
+    _require(slot_mapping, "slot_mapping", torch.int32, (T,), dev)
+    n = k_scale.numel()
+    if n not in (1, H):
+        raise ValueError("k_scale must have 1 or H entries")
+    per_head = n == H and H > 1
+    _require(k_scale, "k_scale", torch.float32, (n,), dev)
+    S = k_cache.shape[0]
+    _require(k_cache, "k_cache", _U8, (S, H, D), dev)
+    if v is not None:
+        _require(v, "v", _BF16, (T, H, D), dev)
+        _require(v_scale, "v_scale", torch.float32, (n,), dev)
+        _require(v_cache, "v_cache", _U8, (S, H, D), dev)
+    with torch.cuda.device(dev):
+        _check("kv_cache_write_fp8",
+               _lib.kv_cache_write_fp8(_ptr(_u16(k)), _ptr(None if v is None else _u16(v)), _ptr(slot_mapping),
+                                       _ptr(k_scale), _ptr(None if v is None else v_scale), int(per_head),
+                                       _ptr(k_cache), _ptr(None if v is None else v_cache), T, H, D, S, _stream(k)))
+    return k_cache, v_cache
 
 
 def raw_library():

@@ -316,4 +316,61 @@ fp8bq_status moe_combine(const uint16_t* y_bf16, const int32_t* pair_row, const 
   }
 }
 
+// K / V layout checks shared by the two KV-cache entry points.
+fp8bq_status kv_shape(int64_t T, int64_t H, int64_t D) {
+  if (T < 0 || H < 1 || D < 8 || (D % 8) != 0 || H * D > 8192) return FP8BQ_ERR_BAD_SHAPE;
+  int64_t thd, bytes;
+  if (!mul_ok(T, H * D, &thd) || !mul_ok(thd, 2, &bytes) || thd > (int64_t(1) << 40)) return FP8BQ_ERR_BAD_SHAPE;
+  return FP8BQ_OK;
+}
+
+fp8bq_status kv_scale_calibrate(const uint16_t* k_bf16, const uint16_t* v_bf16, int64_t T, int64_t H, int64_t D,
+                                int per_head, float* k_scale, float* v_scale, void* stream) {
+  try {
+    if (per_head != 0 && per_head != 1) return FP8BQ_ERR_BAD_ARG;
+    fp8bq_status st = kv_shape(T, H, D);
+    if (st != FP8BQ_OK) return st;
+    // V takes part when v_scale is given
+    if (!v_scale && v_bf16) return FP8BQ_ERR_BAD_ARG;
+    if (!k_scale || (T > 0 && (!k_bf16 || (v_scale && !v_bf16)))) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(k_scale) || (v_scale && !aligned16(v_scale)) ||
+        (T > 0 && (!aligned16(k_bf16) || (v_bf16 && !aligned16(v_bf16)))))
+      return FP8BQ_ERR_MISALIGNED;
+    st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_kv_calibrate(k_bf16, v_bf16, T, H, D, per_head == 1, k_scale, v_scale,
+                                               static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status kv_cache_write_fp8(const uint16_t* k_bf16, const uint16_t* v_bf16, const int32_t* slot_mapping,
+                                const float* k_scale, const float* v_scale, int per_head, uint8_t* k_cache,
+                                uint8_t* v_cache, int64_t T, int64_t H, int64_t D, int64_t S, void* stream) {
+  try {
+    if (per_head != 0 && per_head != 1) return FP8BQ_ERR_BAD_ARG;
+    // V takes part when v_scale is given
+    if (!v_scale && (v_bf16 || v_cache)) return FP8BQ_ERR_BAD_ARG;
+    fp8bq_status st = kv_shape(T, H, D);
+    if (st != FP8BQ_OK) return st;
+    int64_t shd;
+    if (S < 0 || S > 0x7fffffffLL || !mul_ok(S, H * D, &shd)) return FP8BQ_ERR_BAD_SHAPE;
+    if (T == 0) return FP8BQ_OK;
+    if (!k_bf16 || !slot_mapping || !k_scale || (S > 0 && !k_cache)) return FP8BQ_ERR_NULL_PTR;
+    if (v_scale && (!v_bf16 || (S > 0 && !v_cache))) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(k_bf16) || !aligned16(slot_mapping) || !aligned16(k_scale) || (S > 0 && !aligned16(k_cache)) ||
+        (v_bf16 && (!aligned16(v_bf16) || !aligned16(v_scale) || (S > 0 && !aligned16(v_cache)))))
+      return FP8BQ_ERR_MISALIGNED;
+    st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_kv_write(k_bf16, v_bf16, slot_mapping, k_scale, v_scale, per_head == 1, k_cache,
+                                           v_cache, T, H, D, S, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
 }  // extern "C"

@@ -41,4 +41,11 @@ hipError_t launch_silu_mul_quant(const uint16_t* y, int64_t M, int64_t F, uint8_
 hipError_t launch_moe_combine(const uint16_t* y, const int32_t* pair_row, const float* w, int64_t T, int64_t k,
                               int64_t H, int64_t M, uint16_t* out, hipStream_t stream);
 
+hipError_t launch_kv_calibrate(const uint16_t* k, const uint16_t* v, int64_t T, int64_t H, int64_t D, bool per_head,
+                               float* ks, float* vs, hipStream_t stream);
+
+hipError_t launch_kv_write(const uint16_t* k, const uint16_t* v, const int32_t* slots, const float* ks,
+                           const float* vs, bool per_head, uint8_t* kc, uint8_t* vc, int64_t T, int64_t H, int64_t D,
+                           int64_t S, hipStream_t stream);
+
 }  // namespace fp8bq

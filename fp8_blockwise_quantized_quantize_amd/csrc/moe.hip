@@ -25,16 +25,19 @@ namespace {
 // Sort by expert.  One workgroup per expert e, no atomics, deterministic:
 //   first row of e = number of pairs routed to experts below e;
 //   row of pair p   = first row + number of pairs q < p routed to e.
-// The pairs are taken in rounds of kSortThreads * kSortRun; in a round each
-// thread owns kSortRun consecutive pairs, loaded at once.  Pass 1 counts the
-// pairs below e; pass 2 ranks e's pairs with one block-wide exclusive scan of
-// the per-thread counts per round, so rows keep pair order.  Every
-// workgroup reads the whole id list, which stays in L2.
+// The pairs are taken in rounds of kSortWaves * kSortRun * 64; in a round
+// wave w owns the contiguous segment of kSortRun * 64 pairs starting at
+// w * kSortRun * 64 and reads it with coalesced loads (load i, lane l: pair
+// i * 64 + l of the segment).  Pass 1 counts the pairs below e; pass 2
+// ranks e's pairs inside the segment from one ballot per load (pair order
+// is (i, l) order) and across segments from the waves' totals, so rows keep
+// pair order.  Every workgroup reads the whole id list, which stays in L2.
 // ---------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kSortRun = 32;
-constexpr int32_t kSortRound = kSortThreads * kSortRun;
+constexpr int32_t kSortSegment = kSortRun * 64;
+constexpr int32_t kSortRound = kSortWaves * kSortSegment;
 
 __device__ __forceinline__ int wave_sum_i32(int v) {
 #pragma unroll
@@ -42,31 +45,18 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_scan_i32(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
-    v += lane >= off ? o : 0;
-  }
-  return v;
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-// The kSortRun ids from p0 (16-byte loads when the run is whole; -1 past P).
-__device__ __forceinline__ void load_run(const int32_t* __restrict__ ids, int32_t p0, int32_t P,
-                                         int32_t (&id)[kSortRun]) {
-  if (p0 + kSortRun <= P) {
+// The kSortRun ids of this lane in the segment at `seg` (-1 past P).
+__device__ __forceinline__ void load_segment(const int32_t* __restrict__ ids, int32_t seg, int lane, int32_t P,
+                                             int32_t (&id)[kSortRun]) {
 #pragma unroll
-    for (int i = 0; i < kSortRun; i += 4) {
-      const int4 v = *reinterpret_cast<const int4*>(ids + p0 + i);
-      id[i] = v.x;
-      id[i + 1] = v.y;
-      id[i + 2] = v.z;
-      id[i + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kSortRun; ++i) id[i] = (p0 + i < P) ? ids[p0 + i] : -1;
+  for (int i = 0; i < kSortRun; ++i) {
+    const int32_t p = seg + i * 64 + lane;
+    id[i] = p < P ? ids[p] : -1;
   }
 }
 
@@ -76,13 +66,13 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* _
                                                                 int32_t* __restrict__ pair_row) {
   __shared__ int32_t part[kSortWaves];
   const int32_t e = static_cast<int32_t>(blockIdx.x);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int below = 0;
   for (int32_t base = 0; base < P; base += kSortRound) {
-    const int32_t p0 = base + tid * kSortRun;
     int32_t id[kSortRun];
-    load_run(ids, p0, P, id);
+    load_segment(ids, base + wave * kSortSegment, lane, P, id);
 #pragma unroll
     for (int i = 0; i < kSortRun; ++i) below += (id[i] >= 0 && id[i] < e) ? 1 : 0;
   }
@@ -96,14 +86,17 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* _
 
   int32_t running = first;
   for (int32_t base = 0; base < P; base += kSortRound) {
-    const int32_t p0 = base + tid * kSortRun;
+    const int32_t seg = base + wave * kSortSegment;
     int32_t id[kSortRun];
-    load_run(ids, p0, P, id);
-    int mine = 0;
+    load_segment(ids, seg, lane, P, id);
+    uint64_t mask[kSortRun];
+    int32_t count = 0;  // e's pairs in this wave's segment (wave-uniform)
 #pragma unroll
-    for (int i = 0; i < kSortRun; ++i) mine += id[i] == e ? 1 : 0;
-    const int incl = wave_scan_i32(mine, lane);
-    if (lane == 63) part[wave] = incl;
+    for (int i = 0; i < kSortRun; ++i) {
+      mask[i] = __ballot(id[i] == e);
+      count += __popcll(mask[i]);
+    }
+    if (lane == 0) part[wave] = count;
     __syncthreads();
     int32_t before = 0, round_total = 0;
 #pragma unroll
@@ -111,15 +104,17 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* _
       before += (w < wave) ? part[w] : 0;
       round_total += part[w];
     }
-    int32_t r = running + before + (incl - mine);
+    int32_t r = running + before;
 #pragma unroll
     for (int i = 0; i < kSortRun; ++i) {
+      const int32_t p = seg + i * 64 + lane;
       if (id[i] == e) {
-        sorted_pair[r] = p0 + i;
-        pair_row[p0 + i] = r;
-        ++r;
+        const int32_t row = r + static_cast<int32_t>(lanes_below(mask[i]));
+        sorted_pair[row] = p;
+        pair_row[p] = row;
       }
-      if (e == 0 && p0 + i < P && (id[i] < 0 || id[i] >= E)) pair_row[p0 + i] = -1;  // no expert, no row
+      if (e == 0 && p < P && (id[i] < 0 || id[i] >= E)) pair_row[p] = -1;  // no expert, no row
+      r += __popcll(mask[i]);
     }
     running += round_total;
     __syncthreads();

@@ -286,6 +286,40 @@ fp8bq_status silu_mul_quantize_act(const uint16_t* y_bf16, int64_t M, int64_t F,
 fp8bq_status moe_combine(const uint16_t* y_bf16, const int32_t* pair_row, const float* topk_weights, int64_t T,
                          int64_t k, int64_t H, int64_t M_rows, uint16_t* out_bf16, void* stream);
 
+/*
+ * FP8 KV cache ([FP8-RL summary] §3.4.4 "KV-Cache Quantization"): K and V are
+ * stored as 1-byte E4M3 values.  The weights change every RL step, so at the
+ * start of each rollout the per-layer or per-head scales are recomputed from
+ * the K and V of its first forward pass (kv_scale_calibrate) and then used
+ * for every cache write of the rollout (kv_cache_write_fp8).
+ * Layouts: K / V of T tokens [T][H][D] BF16 (H KV heads of D elements); the
+ * caches [S][H][D] E4M3 (S token slots); scales float32 [H] (per_head = 1)
+ * or [1] (per_head = 0).  D % 8 == 0, H * D <= 8192.  V takes part when
+ * v_scale is non-NULL (then its other pointers are required as for K);
+ * otherwise its pointers must all be NULL.
+ */
+
+/*
+ * kv_scale_calibrate -- s = fl32(amax / 448) per KV head (or per layer), with
+ * amax = max |x| over all T tokens, for K and for V (the tile rule of the
+ * linear layers, §3.4.1).  T == 0 gives s = 0.  Deterministic.
+ */
+fp8bq_status kv_scale_calibrate(const uint16_t* k_bf16, const uint16_t* v_bf16, int64_t T, int64_t H, int64_t D,
+                                int per_head, float* k_scale, float* v_scale, void* stream);
+
+/*
+ * kv_cache_write_fp8 -- token t's K and V, quantized with the fixed scales
+ * as q = E4M3(fl32(x / s)) (round to nearest even), are stored in slot
+ * slot_mapping[t] of the caches.  Quotients beyond the E4M3 range (values
+ * above the calibrated amax) saturate to +-448; with s = 0 non-zero values
+ * give +-448 and zeros keep their sign.  Tokens whose slot is outside
+ * [0, S) (padding) store nothing; slots of the other tokens must differ.
+ *   slot_mapping [T] int32; 0 <= S < 2^31.
+ */
+fp8bq_status kv_cache_write_fp8(const uint16_t* k_bf16, const uint16_t* v_bf16, const int32_t* slot_mapping,
+                                const float* k_scale, const float* v_scale, int per_head, uint8_t* k_cache,
+                                uint8_t* v_cache, int64_t T, int64_t H, int64_t D, int64_t S, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

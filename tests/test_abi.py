@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     for n in ["quantize_weight_blockwise", "quantize_act_per_token_group", "gemm_w8a8_blockscaled",
               "grouped_gemm_w8a8_blockscaled", "fp8bq_status_string", "fp8bq_encode_e4m3",
               "token_importance_weights", "moe_sort_by_expert", "moe_gather_quantize_act",
-              "silu_mul_quantize_act", "moe_combine", "grouped_gemm_w8a8_blockscaled_gather"]:
+              "silu_mul_quantize_act", "moe_combine", "grouped_gemm_w8a8_blockscaled_gather",
+              "kv_scale_calibrate", "kv_cache_write_fp8"]:
         assert n in names, names
 
 
@@ -102,6 +103,20 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call(gg, good, good, 1 << 20, good, 1, good, good, good, good, 4, 4, 4096, 2, null) == 2
     assert _call(gg, good, good, 4, null, 1, good, good, good, good, 4, 4, 128, 2, null) == 1
     assert _call(gg, good, good, 4, good, 1, good, good, good, bad_align, 4, 4, 128, 2, null) == 3
+    # KV cache: D % 8, H * D > 8192, per_head flag, V pointers all or none, slot count
+    assert _call("kv_scale_calibrate", good, good, 4, 8, 12, 1, good, good, null) == 2
+    assert _call("kv_scale_calibrate", good, good, 4, 128, 128, 1, good, good, null) == 2
+    assert _call("kv_scale_calibrate", good, good, 4, 8, 128, 2, good, good, null) == 6
+    assert _call("kv_scale_calibrate", good, good, 4, 8, 128, 1, good, null, null) == 6
+    assert _call("kv_scale_calibrate", good, null, 4, 8, 128, 1, good, good, null) == 1
+    assert _call("kv_scale_calibrate", good, good, 4, 8, 128, 1, null, good, null) == 1
+    assert _call("kv_scale_calibrate", bad_align, good, 4, 8, 128, 1, good, good, null) == 3
+    kw = "kv_cache_write_fp8"
+    assert _call(kw, good, good, good, good, null, 1, good, null, 4, 8, 128, 16, null) == 6
+    assert _call(kw, good, good, good, good, good, 1, good, null, 4, 8, 128, 16, null) == 1
+    assert _call(kw, good, good, good, good, good, 1, good, good, 4, 8, 128, 1 << 31, null) == 2
+    assert _call(kw, good, good, null, good, good, 1, good, good, 4, 8, 128, 16, null) == 1
+    assert _call(kw, good, good, good, good, good, 1, bad_align, good, 4, 8, 128, 16, null) == 3
     # MoE glue
     assert _call("moe_sort_by_expert", good, 4, 2, 0, good, good, good, null) == 2      # no expert
     assert _call("moe_sort_by_expert", good, 1 << 20, 1 << 12, 8, good, good, good, null) == 2  # > 2^31 pairs
@@ -131,6 +146,7 @@ def test_zero_sized_problems_are_no_ops():
     assert _call("moe_gather_quantize_act", null, null, 0, 5, 2, 256, null, null, null) == 0
     assert _call("silu_mul_quantize_act", null, 0, 768, null, null, null, null) == 0
     assert _call("moe_combine", null, null, null, 0, 8, 2048, 0, null, null) == 0
+    assert _call("kv_cache_write_fp8", null, null, null, null, null, 1, null, null, 0, 8, 128, 0, null) == 0
 
 
 def test_no_device_is_reported():
