@@ -36,6 +36,9 @@ Modules
            SiLU(gate) * up -> BF16 -> 1x128 groups, the weighted combine.
 ``kv``     FP8 KV cache: per-step K/V scale calibration, quantizing cache
            write into token slots ([FP8-RL summary] §3.4.4).
+``train``  FP8 training operands: W and W^T in 128x128 blocks, x in groups
+           along K and x^T in groups along the tokens ([FP8-RL summary]
+           §3.4.5).
 ``tis``    token-level importance weights of the rollout correction
            ([FP8-RL summary] §3.4.3): TIS clipping and MIS masking.
 
@@ -70,6 +73,7 @@ from .gemm import (
     grouped_gemm_ref,
 )
 from .tis import importance_weights
+from .train import quant_weight_blockwise_dual, quant_act_dual
 from .kv import kv_calibrate, kv_quantize, kv_cache_write
 from .moe import sort_by_expert, gather_quantize_act, silu_mul_bf16, silu_mul_quantize, combine
 
@@ -100,4 +104,6 @@ __all__ = [
     "kv_calibrate",
     "kv_quantize",
     "kv_cache_write",
+    "quant_weight_blockwise_dual",
+    "quant_act_dual",
 ]
