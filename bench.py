@@ -368,6 +368,11 @@ def detail(fb, dev):
     del bufs
     torch.cuda.empty_cache()
 
+    # -- FP8 training operands (Qwen3-8B): W and W^T of all 36 layers' four
+    #    projections, and x / x^T of an 8192-token micro-batch's layer inputs
+    res["train_operands_qwen3_8b"] = train_operands(fb, dev)
+    torch.cuda.empty_cache()
+
     # -- FP8 KV cache, one Qwen3-8B layer (8 KV heads x 128): a rollout's first
     #    forward calibrates the per-head scales on a 16384-token prefill chunk
     #    and writes it to the cache; a decode step then writes 1536 tokens
@@ -450,6 +455,39 @@ def moe_layer(fb, dev):
     res["sum_of_kernels_us"] = round(total * 1e3, 1)
     res["layer_us"] = round(layer_ms * 1e3, 1)
     res["layer_TFLOPs"] = round((2 * R * 2 * F * H + 2 * R * H * F) / layer_ms / 1e9, 1)
+    return res
+
+
+def train_operands(fb, dev):
+    import torch
+
+    from synthetic import LAYER_SHAPES_QWEN3_8B, device_bf16_normal
+
+    res = {}
+    bufs = []
+    wbytes = 0
+    for p, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
+        w = device_bf16_normal((36, n, k), 0.02, seed=950 + p)
+        bufs.append(w)
+        wbytes += 36 * n * k * 4 + 2 * 36 * (n // 128) * (k // 128) * 4
+
+    def sweep():
+        for w in bufs:
+            fb.quantize_weight_blockwise_dual(w)
+
+    ms, _ = _time_ms(sweep, reps=3, warm=1)
+    res["weight_dual_sweep_36_layers"] = {"bytes": wbytes, "ms": round(ms, 3), "GBps": round(wbytes / ms / 1e6, 1),
+                                          "frac_hbm": round(wbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+    del bufs
+    torch.cuda.empty_cache()
+    M = 8192
+    for k in (4096, 12288):
+        x = device_bf16_normal((M, k), 1.0, seed=960 + k)
+        ms, _ = _time_graph_ms(lambda: fb.quantize_act_dual(x), calls=5)
+        byt = M * k * 4 + M * (k // 128) * 4 + k * (M // 128) * 4
+        res[f"act_dual_{M}x{k}"] = {"us": round(ms * 1e3, 1), "bytes": byt, "GBps": round(byt / ms / 1e6, 1),
+                                    "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        del x
     return res
 
 

@@ -38,6 +38,8 @@ __all__ = [
     "moe_expert_ffn",
     "kv_scale_calibrate",
     "kv_cache_write_fp8",
+    "quantize_weight_blockwise_dual",
+    "quantize_act_dual",
     "status_string",
 ]
 
@@ -60,6 +62,8 @@ EXPORTS = (
     "moe_combine",
     "kv_scale_calibrate",
     "kv_cache_write_fp8",
+    "quantize_weight_blockwise_dual",
+    "quantize_act_dual",
 )
 
 
@@ -88,6 +92,8 @@ def _load():
     lib.moe_combine.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
     lib.kv_scale_calibrate.argtypes = [p, p, i64, i64, i64, i32, p, p, p]
     lib.kv_cache_write_fp8.argtypes = [p, p, p, p, p, i32, p, p, i64, i64, i64, i64, p]
+    lib.quantize_weight_blockwise_dual.argtypes = [p, p, p, p, p, i64, i64, i64, p]
+    lib.quantize_act_dual.argtypes = [p, p, p, p, p, i64, i64, p]
     for name in EXPORTS[1:]:
         getattr(lib, name).restype = i32
     return lib
@@ -458,6 +464,42 @@ def kv_cache_write_fp8(k, v, slot_mapping, k_scale, v_scale, k_cache, v_cache=No
                                        _ptr(k_scale), _ptr(None if v is None else v_scale), int(per_head),
                                        _ptr(k_cache), _ptr(None if v is None else v_cache), T, H, D, S, _stream(k)))
     return k_cache, v_cache
+
+
+def quantize_weight_blockwise_dual(w, forward=True):
+    """BF16 W [N, K] or [B, N, K] -> ((W codes, scales) or (None, None), (W^T codes [.., K, N], scales))."""
+    batched = w.dim() == 3
+    wb = w if batched else w.unsqueeze(0)
+    b, n, k = wb.shape
+    _require(wb, "w", _BF16, (b, n, k))
+    dev = w.device
+    nb, kb = _cdiv(n, BLOCK), _cdiv(k, BLOCK)
+    q = torch.empty((b, n, k), dtype=torch.uint8, device=dev) if forward else None
+    s = torch.empty((b, nb, kb), dtype=torch.float32, device=dev) if forward else None
+    qt = torch.empty((b, k, n), dtype=torch.uint8, device=dev)
+    st = torch.empty((b, kb, nb), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("quantize_weight_blockwise_dual",
+               _lib.quantize_weight_blockwise_dual(_ptr(_u16(wb)), _ptr(q), _ptr(s), _ptr(qt), _ptr(st), b, n, k,
+                                                   _stream(w)))
+    sq = (lambda t: t) if batched else (lambda t: None if t is None else t[0])
+    return (sq(q), sq(s)), (sq(qt), sq(st))
+
+
+def quantize_act_dual(x, forward=True):
+    """BF16 x [M, K] -> ((codes [M, K], scales [M, K/128]) or (None, None),
+    (x^T codes [K, M], scales [K, ceil(M/128)]) in groups along the tokens)."""
+    m, k = x.shape
+    _require(x, "x", _BF16, (m, k))
+    dev = x.device
+    q = torch.empty((m, k), dtype=torch.uint8, device=dev) if forward else None
+    s = torch.empty((m, _cdiv(k, BLOCK)), dtype=torch.float32, device=dev) if forward else None
+    qt = torch.empty((k, m), dtype=torch.uint8, device=dev)
+    st = torch.empty((k, _cdiv(m, BLOCK)), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("quantize_act_dual",
+               _lib.quantize_act_dual(_ptr(_u16(x)), _ptr(q), _ptr(s), _ptr(qt), _ptr(st), m, k, _stream(x)))
+    return (q, s), (qt, st)
 
 
 def raw_library():

@@ -316,6 +316,50 @@ fp8bq_status moe_combine(const uint16_t* y_bf16, const int32_t* pair_row, const 
   }
 }
 
+fp8bq_status quantize_weight_blockwise_dual(const uint16_t* w_bf16, uint8_t* w_fp8, float* w_scale, uint8_t* wt_fp8,
+                                            float* wt_scale, int64_t batch, int64_t N, int64_t K, void* stream) {
+  try {
+    if (batch < 0 || N < 0 || K < 0 || (K % 8) != 0 || batch > 65535) return FP8BQ_ERR_BAD_SHAPE;
+    if ((w_fp8 == nullptr) != (w_scale == nullptr)) return FP8BQ_ERR_BAD_ARG;
+    int64_t nk, total, bytes;
+    if (!mul_ok(N, K, &nk) || !mul_ok(nk, batch, &total) || !mul_ok(total, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
+    if (total == 0) return FP8BQ_OK;
+    if (!w_bf16 || !wt_fp8 || !wt_scale) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(w_bf16) || !aligned16(wt_fp8) || !aligned16(wt_scale) ||
+        (w_fp8 && (!aligned16(w_fp8) || !aligned16(w_scale))))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_quant_weight_dual(w_bf16, w_fp8, w_scale, wt_fp8, wt_scale, batch, N, K,
+                                                    static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status quantize_act_dual(const uint16_t* x_bf16, uint8_t* x_fp8, float* x_scale, uint8_t* xt_fp8,
+                               float* xt_scale, int64_t M, int64_t K, void* stream) {
+  try {
+    if (M < 0 || K < 0 || (K % 8) != 0) return FP8BQ_ERR_BAD_SHAPE;
+    if ((x_fp8 == nullptr) != (x_scale == nullptr)) return FP8BQ_ERR_BAD_ARG;
+    int64_t mk, bytes;
+    if (!mul_ok(M, K, &mk) || !mul_ok(mk, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
+    if (mk == 0) return FP8BQ_OK;
+    if (!x_bf16 || !xt_fp8 || !xt_scale) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(x_bf16) || !aligned16(xt_fp8) || !aligned16(xt_scale) ||
+        (x_fp8 && (!aligned16(x_fp8) || !aligned16(x_scale))))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(
+        fp8bq::launch_quant_act_dual(x_bf16, x_fp8, x_scale, xt_fp8, xt_scale, M, K, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
 // K / V layout checks shared by the two KV-cache entry points.
 fp8bq_status kv_shape(int64_t T, int64_t H, int64_t D) {
   if (T < 0 || H < 1 || D < 8 || (D % 8) != 0 || H * D > 8192) return FP8BQ_ERR_BAD_SHAPE;

@@ -48,4 +48,10 @@ hipError_t launch_kv_write(const uint16_t* k, const uint16_t* v, const int32_t* 
                            const float* vs, bool per_head, uint8_t* kc, uint8_t* vc, int64_t T, int64_t H, int64_t D,
                            int64_t S, hipStream_t stream);
 
+hipError_t launch_quant_weight_dual(const uint16_t* w, uint8_t* q, float* s, uint8_t* qt, float* st, int64_t batch,
+                                    int64_t N, int64_t K, hipStream_t stream);
+
+hipError_t launch_quant_act_dual(const uint16_t* x, uint8_t* q, float* s, uint8_t* qt, float* st, int64_t M,
+                                 int64_t K, hipStream_t stream);
+
 }  // namespace fp8bq

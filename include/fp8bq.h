@@ -217,6 +217,38 @@ fp8bq_status token_importance_weights(const float* logp_train, const float* logp
                                       float C, int mode, void* stream);
 
 /*
+ * FP8 training operands ([FP8-RL summary] §3.4.5 "End-to-End FP8 RL": the
+ * trainer's forward and backward GEMMs also run in FP8).  With the §3.4.1
+ * rule applied in the layout each GEMM reduces over: forward x W^T takes x
+ * in 1x128 groups along K and W in 128x128 blocks; dgrad dy W takes W^T
+ * ([K][N]) in 128x128 blocks; wgrad dy^T x takes x^T and dy^T in 1x128
+ * groups along the tokens.  Both layouts come from one read of the BF16
+ * tensor.
+ */
+
+/*
+ * quantize_weight_blockwise_dual -- W and W^T in 128x128 blocks.  W^T's
+ * blocks are W's blocks transposed: wt_fp8 is w_fp8 transposed, wt_scale is
+ * w_scale transposed (the codes of quantize_weight_blockwise).
+ *   w_bf16 [batch][N][K]; w_fp8 [batch][N][K] and w_scale
+ *   [batch][ceil(N/128)][ceil(K/128)], or both NULL (W^T only);
+ *   wt_fp8 [batch][K][N], wt_scale [batch][ceil(K/128)][ceil(N/128)].
+ *   K % 8 == 0, batch <= 65535.
+ */
+fp8bq_status quantize_weight_blockwise_dual(const uint16_t* w_bf16, uint8_t* w_fp8, float* w_scale, uint8_t* wt_fp8,
+                                            float* wt_scale, int64_t batch, int64_t N, int64_t K, void* stream);
+
+/*
+ * quantize_act_dual -- x in 1x128 groups along K (exactly
+ * quantize_act_per_token_group) and x^T in 1x128 groups along M: row k of
+ * xt_fp8 is channel k of x quantized in groups of 128 consecutive tokens.
+ *   x_bf16 [M][K]; x_fp8 [M][K] and x_scale [M][ceil(K/128)], or both NULL
+ *   (x^T only); xt_fp8 [K][M], xt_scale [K][ceil(M/128)].  K % 8 == 0.
+ */
+fp8bq_status quantize_act_dual(const uint16_t* x_bf16, uint8_t* x_fp8, float* x_scale, uint8_t* xt_fp8,
+                               float* xt_scale, int64_t M, int64_t K, void* stream);
+
+/*
  * MoE expert-FFN glue around grouped_gemm_w8a8_blockscaled ([FP8-RL
  * summary] §3.4.1 "Quantization Scope": the MoE expert layers fc1 / fc2 are
  * FP8 W8A8 linears like the dense ones, and the gated MLP multiplies the gate

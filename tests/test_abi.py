@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
               "grouped_gemm_w8a8_blockscaled", "fp8bq_status_string", "fp8bq_encode_e4m3",
               "token_importance_weights", "moe_sort_by_expert", "moe_gather_quantize_act",
               "silu_mul_quantize_act", "moe_combine", "grouped_gemm_w8a8_blockscaled_gather",
-              "kv_scale_calibrate", "kv_cache_write_fp8"]:
+              "kv_scale_calibrate", "kv_cache_write_fp8", "quantize_weight_blockwise_dual", "quantize_act_dual"]:
         assert n in names, names
 
 
@@ -103,6 +103,13 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call(gg, good, good, 1 << 20, good, 1, good, good, good, good, 4, 4, 4096, 2, null) == 2
     assert _call(gg, good, good, 4, null, 1, good, good, good, good, 4, 4, 128, 2, null) == 1
     assert _call(gg, good, good, 4, good, 1, good, good, good, bad_align, 4, 4, 128, 2, null) == 3
+    # training operands: K % 8, forward outputs both or none, null transposed outputs
+    assert _call("quantize_weight_blockwise_dual", good, good, good, good, good, 1, 128, 100, null) == 2
+    assert _call("quantize_weight_blockwise_dual", good, good, null, good, good, 1, 128, 128, null) == 6
+    assert _call("quantize_weight_blockwise_dual", good, good, good, null, good, 1, 128, 128, null) == 1
+    assert _call("quantize_act_dual", good, good, good, good, good, 16, 100, null) == 2
+    assert _call("quantize_act_dual", good, null, good, good, good, 16, 128, null) == 6
+    assert _call("quantize_act_dual", good, good, good, good, bad_align, 16, 128, null) == 3
     # KV cache: D % 8, H * D > 8192, per_head flag, V pointers all or none, slot count
     assert _call("kv_scale_calibrate", good, good, 4, 8, 12, 1, good, good, null) == 2
     assert _call("kv_scale_calibrate", good, good, 4, 128, 128, 1, good, good, null) == 2
