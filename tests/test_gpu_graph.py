@@ -1,0 +1,77 @@
+"""The library's kernels under HIP graph capture: a decode-layer step
+(re-quant, activation quant, GEMMs) and a KV-cache calibration + write are
+captured once and replayed several times, with eager work and
+synchronizations between replays; every replay's outputs must equal the
+eager outputs bit for bit (the kernels are deterministic and no memset is
+captured)."""
+
+import numpy as np
+import pytest
+
+from helpers import announce
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def fb():
+    import fp8_blockwise_quantized_quantize_amd as m
+
+    return m
+
+
+def snapshot(ts):
+    torch.cuda.synchronize()
+    return [t.clone() for t in ts]
+
+
+def test_graph_replays_match_eager():
+    from synthetic import LAYER_SHAPES_QWEN3_8B, device_bf16_normal
+
+    M = 256
+    layers = []
+    for i, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B[:2]):
+        layers.append(dict(w=device_bf16_normal((n, k), 0.02, seed=40 + i), x=device_bf16_normal((M, k), 1.0, seed=50 + i),
+                           wq=torch.empty((n, k), dtype=torch.uint8, device=DEV),
+                           ws=torch.empty((n // 128, k // 128), dtype=torch.float32, device=DEV),
+                           xq=torch.empty((M, k), dtype=torch.uint8, device=DEV),
+                           xs=torch.empty((M, k // 128), dtype=torch.float32, device=DEV),
+                           y=torch.empty((M, n), dtype=torch.bfloat16, device=DEV)))
+    H, D, T = 8, 128, 1000
+    kv = dict(k=device_bf16_normal((T, H, D), 1.0, seed=60), v=device_bf16_normal((T, H, D), 1.0, seed=61),
+              ks=torch.empty(H, dtype=torch.float32, device=DEV), vs=torch.empty(H, dtype=torch.float32, device=DEV),
+              kc=torch.zeros((T, H, D), dtype=torch.uint8, device=DEV),
+              vc=torch.zeros((T, H, D), dtype=torch.uint8, device=DEV),
+              slots=torch.arange(T, dtype=torch.int32, device=DEV))
+
+    def work():
+        for L in layers:
+            fb().quantize_weight_blockwise(L["w"], L["wq"], L["ws"])
+            fb().quantize_act_per_token_group(L["x"], L["xq"], L["xs"])
+            fb().gemm_w8a8_blockscaled(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
+        fb().kv_scale_calibrate(kv["k"], kv["v"], True, kv["ks"], kv["vs"])
+        fb().kv_cache_write_fp8(kv["k"], kv["v"], kv["slots"], kv["ks"], kv["vs"], kv["kc"], kv["vc"])
+
+    outs = ([t for L in layers for t in (L["wq"], L["ws"], L["xq"], L["xs"], L["y"])] +
+            [kv["ks"], kv["vs"], kv["kc"], kv["vc"]])
+    announce("graph eager reference")
+    work()
+    ref = snapshot(outs)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:  # clobber the outputs eagerly between replays
+            t.view(torch.uint8).fill_(0x5A)
+        torch.cuda.synchronize()
+        announce("graph replay", rep)
+        g.replay()
+        got = snapshot(outs)
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
