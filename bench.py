@@ -271,23 +271,36 @@ def _time_ms(fn, reps, warm=2):
     return v[len(v) // 2], v[0]
 
 
+ROTATE_BYTES = 1 << 30  # a rotation of buffer sets larger than the 256 MB Infinity Cache
+
+
+def rotations(bytes_per_set, cap=16):
+    """Buffer sets to cycle through so that a call's working set has left the
+    256 MB Infinity Cache before the same set comes round again."""
+    return max(1, min(cap, -(-ROTATE_BYTES // max(1, bytes_per_set))))
+
+
 def _time_graph_ms(fn, calls=10, reps=5):
-    """Median GPU time per call of `fn`, from replays of a HIP graph holding
-    `calls` back-to-back calls (host call overhead excluded: small kernels
-    would otherwise be timed at the speed of their Python wrapper).  Falls
-    back to per-call events when the calls cannot be captured."""
+    """Median GPU time per call, from replays of a HIP graph holding `calls`
+    back-to-back calls (host call overhead excluded: small kernels would
+    otherwise be timed at the speed of their Python wrapper).  `fn` is one
+    callable or a list of callables on different buffer sets, used in turn.
+    Falls back to per-call events when the calls cannot be captured."""
     import torch
 
+    fns = fn if isinstance(fn, (list, tuple)) else [fn]
+    calls = max(calls, len(fns))
     try:
-        fn()
+        for f in fns:
+            f()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
-                for _ in range(calls):
-                    fn()
+                for i in range(calls):
+                    fns[i % len(fns)]()
         torch.cuda.current_stream().wait_stream(s)
         g.replay()
         torch.cuda.synchronize()
@@ -303,7 +316,7 @@ def _time_graph_ms(fn, calls=10, reps=5):
         times.sort()
         return times[len(times) // 2], times[0]
     except RuntimeError:
-        return _time_ms(fn, reps=10)
+        return _time_ms(fns[0], reps=10)
 
 
 def detail(fb, dev):
@@ -326,7 +339,10 @@ def detail(fb, dev):
         xq, xs = fb.quantize_act_per_token_group(x)
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ms, ms_min = _time_graph_ms(lambda: fb.gemm_w8a8_blockscaled(xq, xs, wq, ws, y), calls=4)
-        aq_ms, _ = _time_graph_ms(lambda: fb.quantize_act_per_token_group(x, xq, xs))
+        sets = [(x, xq, xs)] + [(x.clone(), torch.empty_like(xq), torch.empty_like(xs))
+                                for _ in range(rotations(m * k * 3) - 1)]
+        aq_ms, _ = _time_graph_ms([lambda t=t: fb.quantize_act_per_token_group(*t) for t in sets])
+        del sets
         f = 2 * m * n * k
         tot_f += f
         tot_ms += ms
@@ -386,17 +402,19 @@ def detail(fb, dev):
     rb = rollout_batch(ROLLOUT_TRAIN_BATCH["responses"], ROLLOUT_TRAIN_BATCH["max_len"], (31, 1))
     lt, lr, adv = (torch.from_numpy(rb[k]).to(dev) for k in ("logp_train", "logp_rollout", "advantages"))
     msk = torch.from_numpy(rb["mask"]).to(dev)
-    w = torch.empty_like(lt)
-    wa = torch.empty_like(lt)
-    ms, ms_min = _time_graph_ms(lambda: fb.token_importance_weights(lt, lr, C=2.0, mode="tis", mask=msk,
-                                                                    advantages=adv, out=w, out_adv=wa))
     slots, valid = lt.numel(), int(rb["mask"].sum())
     byt = importance_weight_bytes(slots, valid)
+    sets = [(t.clone() for t in (lt, lr, msk, adv)) for _ in range(rotations(21 * slots))]
+    sets = [tuple(g) + (torch.empty_like(lt), torch.empty_like(lt)) for g in sets]
+    ms, ms_min = _time_graph_ms([lambda t=t: fb.token_importance_weights(t[0], t[1], C=2.0, mode="tis", mask=t[2],
+                                                                         advantages=t[3], out=t[4], out_adv=t[5])
+                                 for t in sets])
+    del sets
     gbps = byt / ms / 1e6
     res["tis_weights_train_batch_512x20000"] = {"tokens": valid, "slots": slots, "bytes": byt,
                                                 "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
                                                 "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
-    del lt, lr, adv, msk, w, wa
+    del lt, lr, adv, msk
     torch.cuda.empty_cache()
     return res
 
@@ -421,21 +439,40 @@ def moe_layer(fb, dev):
                                                                                device=dev)
     y2 = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    # Each step cycles through copies of its inputs and outputs sized so that
+    # a copy has left the 256 MB Infinity Cache before it is used again.
+    fb.grouped_gemm_w8a8_blockscaled_gather(a, a_s, sp, k, w1q, w1s, off, y1)
+    fb.silu_mul_quantize_act(y1, h, h_s)
+    fb.grouped_gemm_w8a8_blockscaled(h, h_s, w2q, w2s, off, y2)
+
+    def copies(n, *ts):
+        return [ts] + [tuple(t.clone() for t in ts) for _ in range(n - 1)]
+
+    aq_b = T * H * 3 + T * (H // 128) * 4
+    silu_b = R * 2 * F * 2 + R * F + R * (F // 128) * 4
+    comb_b = R * H * 2 + R * 8 + T * H * 2
+    w1_b, w2_b = w1q.numel() + w1s.numel() * 4, w2q.numel() + w2s.numel() * 4
+    aq_sets = copies(rotations(aq_b), x, a, a_s)
+    w1_sets = copies(rotations(w1_b), w1q, w1s, y1)
+    silu_sets = copies(rotations(silu_b), y1, h, h_s)
+    w2_sets = copies(rotations(w2_b), w2q, w2s, y2)
+    comb_sets = copies(rotations(comb_b), y2, out)
     steps = {
-        "sort": (lambda: fb.moe_sort_by_expert(ids, E, off, sp, pr), None, None),
-        "act_quant": (lambda: fb.quantize_act_per_token_group(x, a, a_s), T * H * 3 + T * (H // 128) * 4, None),
-        "fc1_gate_up": (lambda: fb.grouped_gemm_w8a8_blockscaled_gather(a, a_s, sp, k, w1q, w1s, off, y1), None,
-                        2 * R * 2 * F * H),
-        "silu_mul_quant": (lambda: fb.silu_mul_quantize_act(y1, h, h_s), R * 2 * F * 2 + R * F + R * (F // 128) * 4,
-                           None),
-        "fc2_down": (lambda: fb.grouped_gemm_w8a8_blockscaled(h, h_s, w2q, w2s, off, y2), None, 2 * R * H * F),
-        "combine": (lambda: fb.moe_combine(y2, pr, tw, out), R * H * 2 + R * 8 + T * H * 2, None),
+        "sort": ([lambda: fb.moe_sort_by_expert(ids, E, off, sp, pr)], None, None),
+        "act_quant": ([lambda t=t: fb.quantize_act_per_token_group(*t) for t in aq_sets], aq_b, None),
+        "fc1_gate_up": ([lambda t=t: fb.grouped_gemm_w8a8_blockscaled_gather(a, a_s, sp, k, t[0], t[1], off, t[2])
+                         for t in w1_sets], None, 2 * R * 2 * F * H),
+        "silu_mul_quant": ([lambda t=t: fb.silu_mul_quantize_act(*t) for t in silu_sets], silu_b, None),
+        "fc2_down": ([lambda t=t: fb.grouped_gemm_w8a8_blockscaled(h, h_s, t[0], t[1], off, t[2]) for t in w2_sets],
+                     None, 2 * R * H * F),
+        "combine": ([lambda t=t: fb.moe_combine(t[0], pr, tw, t[1]) for t in comb_sets], comb_b, None),
     }
     res, total = {}, 0.0
     for name, (fn, byt, flops) in steps.items():
         ms, _ = _time_graph_ms(fn)
+        e_rot = len(fn)
         total += ms
-        e = {"us": round(ms * 1e3, 1)}
+        e = {"us": round(ms * 1e3, 1), "buffer_sets": e_rot}
         if byt is not None:
             e.update({"bytes": byt, "GBps": round(byt / ms / 1e6, 1), "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)})
         if flops is not None:
@@ -452,6 +489,7 @@ def moe_layer(fb, dev):
         fb.moe_expert_ffn(x, ids, tw, w1q, w1s, w2q, w2s)
 
     layer_ms, _ = _time_graph_ms(layer, calls=4)
+    del aq_sets, w1_sets, silu_sets, w2_sets, comb_sets
     res["sum_of_kernels_us"] = round(total * 1e3, 1)
     res["layer_us"] = round(layer_ms * 1e3, 1)
     res["layer_TFLOPs"] = round((2 * R * 2 * F * H + 2 * R * H * F) / layer_ms / 1e9, 1)
@@ -483,8 +521,10 @@ def train_operands(fb, dev):
     M = 8192
     for k in (4096, 12288):
         x = device_bf16_normal((M, k), 1.0, seed=960 + k)
-        ms, _ = _time_graph_ms(lambda: fb.quantize_act_dual(x), calls=5)
         byt = M * k * 4 + M * (k // 128) * 4 + k * (M // 128) * 4
+        xs = [x] + [x.clone() for _ in range(rotations(byt) - 1)]
+        ms, _ = _time_graph_ms([lambda t=t: fb.quantize_act_dual(t) for t in xs], calls=max(5, len(xs)))
+        del xs
         res[f"act_dual_{M}x{k}"] = {"us": round(ms * 1e3, 1), "bytes": byt, "GBps": round(byt / ms / 1e6, 1),
                                     "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)}
         del x
@@ -509,15 +549,20 @@ def kv_cache(fb, dev):
     slots = torch.arange(T, dtype=torch.int32, device=dev)
     dslots = torch.arange(T, S, dtype=torch.int32, device=dev)
     res = {}
-    cal_ms, _ = _time_graph_ms(lambda: fb.kv_scale_calibrate(k, v, True, ks, vs))
     cal_b = 2 * T * H * D * 2
-    wr_ms, _ = _time_graph_ms(lambda: fb.kv_cache_write_fp8(k, v, slots, ks, vs, kc, vc))
+    sets = [(k, v)] + [(k.clone(), v.clone()) for _ in range(rotations(cal_b) - 1)]
+    cal_ms, _ = _time_graph_ms([lambda t=t: fb.kv_scale_calibrate(t[0], t[1], True, ks, vs) for t in sets])
     wr_b = 2 * T * H * D * 3 + T * 4
+    wsets = [(t[0], t[1], torch.empty_like(kc), torch.empty_like(vc)) for t in sets[:rotations(wr_b)]]
+    wr_ms, _ = _time_graph_ms([lambda t=t: fb.kv_cache_write_fp8(t[0], t[1], slots, ks, vs, t[2], t[3])
+                               for t in wsets])
+    del sets, wsets
     dec_ms, _ = _time_graph_ms(lambda: fb.kv_cache_write_fp8(kn, vn, dslots, ks, vs, kc, vc))
-    for name, ms, byt in (("calibrate_16384", cal_ms, cal_b), ("write_16384", wr_ms, wr_b),
-                          ("decode_write_1536", dec_ms, 2 * B * H * D * 3 + B * 4)):
+    for name, ms, byt in (("calibrate_16384", cal_ms, cal_b), ("write_16384", wr_ms, wr_b)):
         res[name] = {"us": round(ms * 1e3, 1), "bytes": byt, "GBps": round(byt / ms / 1e6, 1),
                      "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+    # 9.4 MB per call: latency-bound, reported in microseconds only
+    res["decode_write_1536"] = {"us": round(dec_ms * 1e3, 1), "bytes": 2 * B * H * D * 3 + B * 4}
     return res
 
 

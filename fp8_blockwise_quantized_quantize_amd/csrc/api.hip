@@ -2,7 +2,9 @@
 // The contract of every entry point is documented in include/fp8bq.h.
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "../../include/fp8bq.h"
 #include "launch.hpp"
@@ -49,6 +51,24 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 }
 
 fp8bq_status launched(hipError_t e) { return e == hipSuccess ? FP8BQ_OK : FP8BQ_ERR_LAUNCH; }
+
+// Debug mode for the grouped GEMMs' device-side precondition: with
+// FP8BQ_CHECK_OFFSETS=1 in the environment (read on every call) the offsets
+// are copied to the host on the call's stream, which waits for them, and
+// checked: [0] = 0, non-decreasing, [G] = M_total.  A violation returns
+// FP8BQ_ERR_BAD_SHAPE before anything is launched.
+fp8bq_status check_offsets_if_asked(const int32_t* offsets, int64_t G, int64_t M_total, hipStream_t stream) {
+  const char* e = std::getenv("FP8BQ_CHECK_OFFSETS");
+  if (e == nullptr || std::strcmp(e, "1") != 0) return FP8BQ_OK;
+  std::vector<int32_t> h(static_cast<size_t>(G + 1));
+  if (hipMemcpyAsync(h.data(), offsets, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return FP8BQ_ERR_LAUNCH;
+  if (h[0] != 0 || h[static_cast<size_t>(G)] != M_total) return FP8BQ_ERR_BAD_SHAPE;
+  for (int64_t g = 0; g < G; ++g)
+    if (h[static_cast<size_t>(g + 1)] < h[static_cast<size_t>(g)]) return FP8BQ_ERR_BAD_SHAPE;
+  return FP8BQ_OK;
+}
 
 // Clears a stale runtime error so that the post-launch check reports ours.
 void clear_last_error() { (void)hipGetLastError(); }
@@ -151,6 +171,8 @@ fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_
     if ((reinterpret_cast<uintptr_t>(group_offsets) & 3u) != 0) return FP8BQ_ERR_MISALIGNED;
     fp8bq_status st = check_device();
     if (st != FP8BQ_OK) return st;
+    st = check_offsets_if_asked(group_offsets, G, M_total, static_cast<hipStream_t>(stream));
+    if (st != FP8BQ_OK) return st;
     clear_last_error();
     return launched(fp8bq::launch_grouped_gemm(a_fp8, a_scale, w_fp8, w_scale, group_offsets, y_bf16, M_total, N,
                                                K, G, static_cast<hipStream_t>(stream)));
@@ -181,6 +203,8 @@ fp8bq_status grouped_gemm_w8a8_blockscaled_gather(const uint8_t* a_fp8, const fl
         (K > 0 && (!aligned16(w_fp8) || !aligned16(w_scale) || (M_a > 0 && (!aligned16(a_fp8) || !aligned16(a_scale))))))
       return FP8BQ_ERR_MISALIGNED;
     fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    st = check_offsets_if_asked(group_offsets, G, M_total, static_cast<hipStream_t>(stream));
     if (st != FP8BQ_OK) return st;
     clear_last_error();
     return launched(fp8bq::launch_grouped_gemm_gather(a_fp8, a_scale, a_rows, a_row_div, M_a, w_fp8, w_scale,

@@ -308,6 +308,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Up to kCombineAhead routed rows are loaded before the first of them is
+// summed, so a lane keeps that many 16-byte loads in flight.
+constexpr int kCombineAhead = 8;
+
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
                                                                   const int32_t* __restrict__ pair_row,
                                                                   const float* __restrict__ w,
@@ -316,16 +320,28 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
   const int64_t t = blockIdx.x;
   for (int64_t c = static_cast<int64_t>(threadIdx.x) * 8; c < H; c += kCombineThreads * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int32_t j = 0; j < k; ++j) {
-      const int32_t r = pair_row[t * k + j];
-      if (r < 0 || r >= M) continue;
-      const float wj = w[t * k + j];
-      const u32x4 v = *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(r) * H + c);
-      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+    for (int32_t j0 = 0; j0 < k; j0 += kCombineAhead) {
+      u32x4 v[kCombineAhead];
+      float wj[kCombineAhead];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(wj, bf16_lo(vw[i]), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(wj, bf16_hi(vw[i]), acc[2 * i + 1]);
+      for (int jj = 0; jj < kCombineAhead; ++jj) {
+        const int32_t j = j0 + jj;
+        const int32_t r = j < k ? pair_row[t * k + j] : -1;
+        const bool ok = r >= 0 && r < M;
+        wj[jj] = ok ? w[t * k + j] : 0.0f;
+        v[jj] = ok ? *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(r) * H + c) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int jj = 0; jj < kCombineAhead; ++jj) {
+        if (j0 + jj >= k) break;
+        const int32_t r = pair_row[t * k + j0 + jj];
+        if (r < 0 || r >= M) continue;  // rows outside [0, M) contribute nothing
+        const uint32_t vw[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wj[jj], bf16_lo(vw[i]), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wj[jj], bf16_hi(vw[i]), acc[2 * i + 1]);
+        }
       }
     }
     u32x4 o;

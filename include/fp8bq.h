@@ -137,6 +137,11 @@ fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, c
  *   unspecified output rows but never an out-of-bounds access: every row
  *   index is clamped to [0, M_total).  M_total + 128 * G must fit in int32;
  *   K as for gemm_w8a8_blockscaled.
+ *   Debug mode: with FP8BQ_CHECK_OFFSETS=1 in the environment (read on every
+ *   call) the call copies the offsets to the host, waits for them on
+ *   `stream`, and returns FP8BQ_ERR_BAD_SHAPE, launching nothing, unless
+ *   [0] = 0, they are non-decreasing and [G] = M_total.  This applies to
+ *   grouped_gemm_w8a8_blockscaled_gather too.
  */
 fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
                                            const float* w_scale, const int32_t* group_offsets, uint16_t* y_bf16,

@@ -278,3 +278,20 @@ def test_grouped_moe_full_size_sampled(fb, proj):
         ref = sampled_gemm_ref(x[rows], w[e], cols)
         got = device_to_bits(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].contiguous())
         assert_gemm_close(got, ref)
+
+
+def test_offsets_debug_mode(fb, monkeypatch):
+    """FP8BQ_CHECK_OFFSETS=1 rejects offsets that break the contract before
+    launching anything; valid offsets run as usual."""
+    announce("offsets debug mode")
+    qa, sa, qw, sw, off = _grouped_oracle_inputs([5, 0, 9], 128, 256, 80)
+    monkeypatch.setenv("FP8BQ_CHECK_OFFSETS", "1")
+    y = gpu_grouped(fb, qa, sa, qw, sw, off)   # valid: runs
+    assert_gemm_close(y, oracle.grouped_gemm_ref(qa, sa, qw, sw, off))
+    for bad in ([0, 9, 5, 14], [1, 5, 5, 14], [0, 5, 5, 13]):
+        with pytest.raises(fb.FP8BQError, match="invalid shape"):
+            gpu_grouped(fb, qa, sa, qw, sw, np.array(bad, np.int32))
+    rows = np.arange(14, dtype=np.int32)
+    with pytest.raises(fb.FP8BQError, match="invalid shape"):
+        fb.grouped_gemm_w8a8_blockscaled_gather(_dev(qa), _dev(sa), _dev(rows), 1, _dev(qw), _dev(sw),
+                                                _dev(np.array([0, 9, 5, 14], np.int32)))
