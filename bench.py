@@ -45,8 +45,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "fp8_blockwise_quantized_quantize_amd", "csrc")
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_layer_step_qwen3_8b.md")
 # kernel-name prefix of each phase -> the source file that defines it
+# launches per decode step: the four matrices are re-quantized by one launch
+PHASE_LAUNCHES = {"requant": 1, "act_quant": 4, "gemm": 4}
 PHASE_KERNELS = {
-    "requant": ("quant_weight_kernel", "quant.hip"),
+    "requant": ("quant_weight_multi_kernel", "quant.hip"),
     "act_quant": ("quant_act_kernel", "quant.hip"),
     "gemm": ("gemm_dense_kernel", "gemm.hip"),
 }
@@ -165,8 +167,8 @@ def main():
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
         if record:
             e[0].record(stream)
-        for L in ls:
-            fb.quantize_weight_blockwise(L["w"], L["wq"], L["ws"])
+        # the layer's four matrices re-quantized by one launch
+        fb.quantize_weights_blockwise_multi([L["w"] for L in ls], [(L["wq"], L["ws"]) for L in ls])
         if record:
             e[1].record(stream)
         for L in ls:
@@ -206,7 +208,8 @@ def main():
     for p in phases:
         name, byt, flops = kernels[p]
         ms = phase_ms[p]
-        launch_us = ms * 1e3 / len(layers)
+        nl = PHASE_LAUNCHES[p]
+        launch_us = ms * 1e3 / nl
         # bound: HBM unless the arithmetic intensity passes the ridge point
         if flops and flops / byt > FP8_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3:
             ach, peak, unit, bound = flops / ms / 1e9, FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
@@ -216,8 +219,8 @@ def main():
         roof_all[p] = {"bound": bound, "kernel": name, "achieved": round(ach, 1), "peak": peak, "unit": unit,
                        "frac": round(ach / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
                        "avg_launch_us": round(launch_us, 2),
-                       "launches_per_step": len(layers), "algorithmic_bytes_per_launch_avg": int(byt / len(layers)),
-                       "flops_per_launch_avg": int(flops / len(layers))}
+                       "launches_per_step": nl, "algorithmic_bytes_per_launch_avg": int(byt / nl),
+                       "flops_per_launch_avg": int(flops / nl)}
         if flops:
             roof_all[p]["TFLOPs"] = round(flops / ms / 1e9, 1)
     dominant = max(phases, key=lambda p: phase_ms[p])
@@ -691,8 +694,8 @@ def step_algorithmic_bytes(M=256):
         rq += n * k * 3 + ws
         aq += M * k * 3 + xs
         gm += M * k + n * k + 2 * M * n + xs + ws
-    L = len(LAYER_SHAPES_QWEN3_8B)
-    return {"requant": rq / L, "act_quant": aq / L, "gemm": gm / L}
+    return {"requant": rq / PHASE_LAUNCHES["requant"], "act_quant": aq / PHASE_LAUNCHES["act_quant"],
+            "gemm": gm / PHASE_LAUNCHES["gemm"]}
 
 
 def rocprof_summary(d):

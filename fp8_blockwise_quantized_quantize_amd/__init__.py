@@ -25,6 +25,7 @@ __all__ = [
     "LIB_PATH",
     "FP8BQError",
     "quantize_weight_blockwise",
+    "quantize_weights_blockwise_multi",
     "quantize_act_per_token_group",
     "gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled",
@@ -50,6 +51,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8bq.so
 EXPORTS = (
     "fp8bq_status_string",
     "quantize_weight_blockwise",
+    "quantize_weights_blockwise_multi",
     "quantize_act_per_token_group",
     "gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled",
@@ -71,6 +73,14 @@ class FP8BQError(RuntimeError):
     pass
 
 
+MAX_WEIGHT_DESCS = 48  # FP8BQ_MAX_WEIGHT_DESCS
+
+
+class _WeightDesc(ctypes.Structure):
+    _fields_ = [("w_bf16", ctypes.c_void_p), ("w_fp8", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -81,6 +91,7 @@ def _load():
     lib.fp8bq_status_string.restype = ctypes.c_char_p
     lib.quantize_weight_blockwise.argtypes = [p, p, p, i64, i64, i64, p]
     lib.quantize_act_per_token_group.argtypes = [p, p, p, i64, i64, p]
+    lib.quantize_weights_blockwise_multi.argtypes = [ctypes.POINTER(_WeightDesc), i64, p]
     lib.gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled_gather.argtypes = [p, p, i64, p, i64, p, p, p, p, i64, i64, i64, i64, p]
@@ -164,6 +175,38 @@ def quantize_weight_blockwise(w, out=None, scale=None):
         _check("quantize_weight_blockwise",
                _lib.quantize_weight_blockwise(_ptr(w), _ptr(out), _ptr(scale), b, n, k, _stream(w)))
     return out, scale
+
+
+def quantize_weights_blockwise_multi(ws, outs=None):
+    """Several BF16 matrices [N, K] (any shapes) in one launch -> list of (codes, scales),
+    each exactly what quantize_weight_blockwise gives it.  ``outs``: optional list
+    of (codes, scales) to fill."""
+    ws = list(ws)
+    if len(ws) > MAX_WEIGHT_DESCS:
+        raise ValueError(f"at most {MAX_WEIGHT_DESCS} matrices per call")
+    if not ws:
+        return []
+    dev = ws[0].device
+    res = []
+    descs = (_WeightDesc * len(ws))()
+    for i, w in enumerate(ws):
+        if w.dim() != 2:
+            raise ValueError("each weight must be [N, K]")
+        n, k = w.shape
+        _require(w, f"w[{i}]", _BF16, (n, k), dev)
+        if outs is None:
+            q = torch.empty((n, k), dtype=torch.uint8, device=dev)
+            s = torch.empty((_cdiv(n, BLOCK), _cdiv(k, BLOCK)), dtype=torch.float32, device=dev)
+        else:
+            q, s = outs[i]
+        _require(q, f"out[{i}]", _U8, (n, k), dev)
+        _require(s, f"scale[{i}]", torch.float32, (_cdiv(n, BLOCK), _cdiv(k, BLOCK)), dev)
+        descs[i] = _WeightDesc(_ptr(_u16(w)).value, _ptr(q).value, _ptr(s).value, n, k)
+        res.append((q, s))
+    with torch.cuda.device(dev):
+        _check("quantize_weights_blockwise_multi",
+               _lib.quantize_weights_blockwise_multi(descs, len(ws), _stream(ws[0])))
+    return res
 
 
 def quantize_act_per_token_group(x, out=None, scale=None):

@@ -1,5 +1,6 @@
 // C-ABI layer of libfp8bq.so: argument checks, device check, launches.
 // The contract of every entry point is documented in include/fp8bq.h.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdlib>
@@ -104,6 +105,48 @@ fp8bq_status quantize_weight_blockwise(const uint16_t* w_bf16, uint8_t* w_fp8, f
     clear_last_error();
     return launched(fp8bq::launch_quant_weight(w_bf16, w_fp8, w_scale, batch, N, K,
                                                static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status quantize_weights_blockwise_multi(const fp8bq_weight_desc* descs, int64_t count, void* stream) {
+  try {
+    if (count < 0 || count > FP8BQ_MAX_WEIGHT_DESCS) return FP8BQ_ERR_BAD_SHAPE;
+    if (count == 0) return FP8BQ_OK;
+    if (!descs) return FP8BQ_ERR_NULL_PTR;
+    // validate each matrix as quantize_weight_blockwise would, keep the non-empty ones
+    std::vector<int> idx;
+    std::vector<int64_t> nblk(static_cast<size_t>(count), 0);
+    for (int64_t i = 0; i < count; ++i) {
+      const fp8bq_weight_desc& d = descs[i];
+      if (d.N < 0 || d.K < 0) return FP8BQ_ERR_BAD_SHAPE;
+      int64_t nk, bytes;
+      if (!mul_ok(d.N, d.K, &nk) || !mul_ok(nk, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
+      if (nk == 0) continue;
+      if (!d.w_bf16 || !d.w_fp8 || !d.w_scale) return FP8BQ_ERR_NULL_PTR;
+      if (!aligned16(d.w_bf16) || !aligned16(d.w_fp8) || !aligned16(d.w_scale)) return FP8BQ_ERR_MISALIGNED;
+      nblk[static_cast<size_t>(i)] = ((d.N + 127) / 128) * ((d.K + 127) / 128);
+      idx.push_back(static_cast<int>(i));
+    }
+    if (idx.empty()) return FP8BQ_OK;
+    // largest matrices first: the small ones fill in at the end of the launch
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return nblk[a] > nblk[b]; });
+    fp8bq::WeightBatch batch{};
+    batch.count = static_cast<int>(idx.size());
+    int64_t blocks = 0;
+    for (int t = 0; t < batch.count; ++t) {
+      const fp8bq_weight_desc& d = descs[idx[static_cast<size_t>(t)]];
+      batch.desc[t] = fp8bq::WeightDesc{d.w_bf16, d.w_fp8, d.w_scale, d.N, d.K};
+      batch.first[t] = blocks;
+      blocks += nblk[static_cast<size_t>(idx[static_cast<size_t>(t)])];
+    }
+    batch.first[batch.count] = blocks;
+    if (blocks > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_quant_weight_multi(batch, blocks, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }

@@ -7,8 +7,26 @@
 
 namespace fp8bq {
 
+// Matrices re-quantized by one launch (passed by value in the kernel
+// arguments): desc[t] is an [N][K] BF16 matrix with its outputs; its blocks
+// are workgroups first[t] .. first[t + 1] - 1.
+constexpr int kMaxWeightDescs = 48;  // FP8BQ_MAX_WEIGHT_DESCS of the C ABI
+struct WeightDesc {
+  const uint16_t* w;
+  uint8_t* q;
+  float* s;
+  int64_t N, K;
+};
+struct WeightBatch {
+  WeightDesc desc[kMaxWeightDescs];
+  int64_t first[kMaxWeightDescs + 1];
+  int count;
+};
+
 hipError_t launch_quant_weight(const uint16_t* w, uint8_t* q, float* scale, int64_t batch, int64_t N, int64_t K,
                                hipStream_t stream);
+
+hipError_t launch_quant_weight_multi(const WeightBatch& batch, int64_t blocks, hipStream_t stream);
 
 hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K, hipStream_t stream);
 

@@ -23,18 +23,11 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kQwThreads = 256;
 
-__global__ __launch_bounds__(kQwThreads) void quant_weight_kernel(const uint16_t* __restrict__ w,
-                                                                  uint8_t* __restrict__ q,
-                                                                  float* __restrict__ scale, int64_t N,
-                                                                  int64_t K, int nb, int kb) {
-  __shared__ uint32_t red[kQwThreads / 64];
-  const int64_t blk = blockIdx.x;  // == index into scale[batch][nb][kb]
-  const int bk = (int)(blk % kb);
-  const int64_t rest = blk / kb;
-  const int bn = (int)(rest % nb);
-  const int64_t b = rest / nb;
-  const uint16_t* wm = w + b * N * K;
-  uint8_t* qm = q + b * N * K;
+// Block (bn, bk) of one [N][K] matrix; its scale goes to *sslot.  `red`:
+// kQwThreads / 64 words of LDS.
+__device__ __forceinline__ void quant_weight_block(const uint16_t* __restrict__ wm, uint8_t* __restrict__ qm,
+                                                   float* __restrict__ sslot, int64_t N, int64_t K, int bn, int bk,
+                                                   uint32_t* red) {
   const int64_t row0 = (int64_t)bn * kBlock, col0 = (int64_t)bk * kBlock;
   const int tid = threadIdx.x;
   const bool full = (row0 + kBlock <= N) && (col0 + kBlock <= K) && ((K & 7) == 0);
@@ -55,7 +48,7 @@ __global__ __launch_bounds__(kQwThreads) void quant_weight_kernel(const uint16_t
 #pragma unroll
     for (int i = 1; i < kQwThreads / 64; ++i) m = m > red[i] ? m : red[i];
     const float s = scale_from_amax_bits(m);
-    if (tid == 0) scale[blk] = s;
+    if (tid == 0) *sslot = s;
     uint8_t* dst = qm + (row0 + rr) * K + col0 + cc * 8;
     if (s != 0.0f) {
       Divisor d(s);
@@ -92,7 +85,7 @@ __global__ __launch_bounds__(kQwThreads) void quant_weight_kernel(const uint16_t
   m = red[0];
   for (int i = 1; i < kQwThreads / 64; ++i) m = m > red[i] ? m : red[i];
   const float s = scale_from_amax_bits(m);
-  if (tid == 0) scale[blk] = s;
+  if (tid == 0) *sslot = s;
   for (int e = tid; e < kBlock * kBlock; e += kQwThreads) {
     const int r = e >> 7, c = e & 127;
     if (r < rows && c < cols) {
@@ -100,6 +93,35 @@ __global__ __launch_bounds__(kQwThreads) void quant_weight_kernel(const uint16_t
       qm[off] = encode1(wm[off], s);
     }
   }
+}
+
+
+__global__ __launch_bounds__(kQwThreads) void quant_weight_kernel(const uint16_t* __restrict__ w,
+                                                                  uint8_t* __restrict__ q,
+                                                                  float* __restrict__ scale, int64_t N,
+                                                                  int64_t K, int nb, int kb) {
+  __shared__ uint32_t red[kQwThreads / 64];
+  const int64_t blk = blockIdx.x;  // == index into scale[batch][nb][kb]
+  const int bk = (int)(blk % kb);
+  const int64_t rest = blk / kb;
+  const int bn = (int)(rest % nb);
+  const int64_t b = rest / nb;
+  quant_weight_block(w + b * N * K, q + b * N * K, scale + blk, N, K, bn, bk, red);
+}
+
+// Several matrices in one launch: workgroup g takes block g - first[t] of
+// the matrix t with first[t] <= g < first[t + 1] (descriptors in the kernel
+// arguments, largest matrices first).
+__global__ __launch_bounds__(kQwThreads) void quant_weight_multi_kernel(const WeightBatch batch) {
+  __shared__ uint32_t red[kQwThreads / 64];
+  const int64_t g = blockIdx.x;
+  int t = 0;
+  while (t + 1 < batch.count && g >= batch.first[t + 1]) ++t;  // uniform scan over <= 64 entries
+  const WeightDesc& d = batch.desc[t];
+  const int kb = (int)((d.K + kBlock - 1) / kBlock);
+  const int64_t local = g - batch.first[t];
+  const int bk = (int)(local % kb), bn = (int)(local / kb);
+  quant_weight_block(d.w, d.q, d.s + local, d.N, d.K, bn, bk, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -184,6 +206,13 @@ hipError_t launch_quant_weight(const uint16_t* w, uint8_t* q, float* scale, int6
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)blocks), dim3(kQwThreads), 0, stream, w, q, scale, N, K,
                      (int)nb, (int)kb);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_multi(const WeightBatch& batch, int64_t blocks, hipStream_t stream) {
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_weight_multi_kernel, dim3((unsigned)blocks), dim3(kQwThreads), 0, stream, batch);
   return hipGetLastError();
 }
 

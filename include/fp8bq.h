@@ -88,6 +88,29 @@ fp8bq_status quantize_weight_blockwise(const uint16_t* w_bf16, uint8_t* w_fp8, f
                                        int64_t batch, int64_t N, int64_t K, void* stream);
 
 /*
+ * quantize_weights_blockwise_multi -- quantize_weight_blockwise of several
+ * matrices of any shapes in one launch (a weight sync re-quantizes many
+ * parameter tensors per RL step; one launch avoids a ramp and a tail per
+ * tensor).  Each matrix gets exactly the codes and scales
+ * quantize_weight_blockwise gives it.
+ *   descs  HOST array of `count` descriptors (read during the call only):
+ *          w_bf16 [N][K] BF16, w_fp8 [N][K] E4M3, w_scale
+ *          [ceil(N/128)][ceil(K/128)] float32, N, K >= 0, each validated as
+ *          in quantize_weight_blockwise (empty matrices are skipped).
+ *   0 <= count <= FP8BQ_MAX_WEIGHT_DESCS; the matrices must not overlap.
+ */
+#define FP8BQ_MAX_WEIGHT_DESCS 48
+typedef struct {
+  const uint16_t* w_bf16;
+  uint8_t* w_fp8;
+  float* w_scale;
+  int64_t N;
+  int64_t K;
+} fp8bq_weight_desc;
+
+fp8bq_status quantize_weights_blockwise_multi(const fp8bq_weight_desc* descs, int64_t count, void* stream);
+
+/*
  * quantize_act_per_token_group -- dynamic per-token 1x128 quantization of
  * BF16 activations ([FP8-RL summary] §3.4.1, "1 x 128 tiles for
  * activations", and §3.4.2 Phase 3, scales computed on the fly).

@@ -14,6 +14,7 @@ HEADER = os.path.join(ROOT, "include", "fp8bq.h")
 
 def declared_functions():
     text = open(HEADER).read()
+    text = re.sub(r"typedef struct \{.*?\} \w+;", "", text, flags=re.S)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|fp8bq_status)\s+(\w+)\s*\(", text, flags=re.M)))
 
@@ -24,7 +25,8 @@ def test_header_declares_the_entry_points():
               "grouped_gemm_w8a8_blockscaled", "fp8bq_status_string", "fp8bq_encode_e4m3",
               "token_importance_weights", "moe_sort_by_expert", "moe_gather_quantize_act",
               "silu_mul_quantize_act", "moe_combine", "grouped_gemm_w8a8_blockscaled_gather",
-              "kv_scale_calibrate", "kv_cache_write_fp8", "quantize_weight_blockwise_dual", "quantize_act_dual"]:
+              "kv_scale_calibrate", "kv_cache_write_fp8", "quantize_weight_blockwise_dual", "quantize_act_dual",
+              "quantize_weights_blockwise_multi"]:
         assert n in names, names
 
 
@@ -103,6 +105,17 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call(gg, good, good, 1 << 20, good, 1, good, good, good, good, 4, 4, 4096, 2, null) == 2
     assert _call(gg, good, good, 4, null, 1, good, good, good, good, 4, 4, 128, 2, null) == 1
     assert _call(gg, good, good, 4, good, 1, good, good, good, bad_align, 4, 4, 128, 2, null) == 3
+    # multi-matrix re-quant: too many descriptors, null array, bad shape, null / misaligned pointers
+    import fp8_blockwise_quantized_quantize_amd as fbm
+
+    D = fbm._WeightDesc
+    mq = "quantize_weights_blockwise_multi"
+    assert _call(mq, (D * 1)(), 49, null) == 2
+    assert _call(mq, None, 2, null) == 1
+    assert _call(mq, (D * 1)(D(4096, 4096, 4096, -1, 128)), 1, null) == 2
+    assert _call(mq, (D * 2)(D(4096, 4096, 4096, 128, 128), D(0, 4096, 4096, 128, 128)), 2, null) == 1
+    assert _call(mq, (D * 1)(D(4096, 4097, 4096, 128, 128)), 1, null) == 3
+    assert _call(mq, (D * 1)(D(0, 0, 0, 0, 128)), 1, null) == 0   # empty matrices are skipped
     # training operands: K % 8, forward outputs both or none, null transposed outputs
     assert _call("quantize_weight_blockwise_dual", good, good, good, good, good, 1, 128, 100, null) == 2
     assert _call("quantize_weight_blockwise_dual", good, good, null, good, good, 1, 128, 128, null) == 6

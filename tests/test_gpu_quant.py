@@ -205,3 +205,24 @@ def test_act_empty(fb):
     assert q.shape == (0, 256) and s.shape == (0, 2)
     q, s = fb.quantize_weight_blockwise(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"))
     assert q.shape == (0, 256) and s.shape == (0, 2)
+
+
+def test_weights_multi_matches_single():
+    """quantize_weights_blockwise_multi: one launch over matrices of any shapes
+    (full Qwen3-8B layer shapes, ragged edges, K % 8 != 0, empty) gives each
+    one the oracle's codes and scales."""
+    import fp8_blockwise_quantized_quantize_amd as fb
+
+    shapes = [(n, k) for _, n, k in LAYER_SHAPES_QWEN3_8B] + [(200, 136), (37, 300), (1, 8), (0, 128), (130, 129)]
+    announce("weights multi", shapes)
+    ws_bits = [bf16_normal(sh, 0.02, (140 + i, 0, 0)) if sh[0] * sh[1] else np.zeros(sh, np.uint16)
+               for i, sh in enumerate(shapes)]
+    ws = [torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16) for b in ws_bits]
+    res = fb.quantize_weights_blockwise_multi(ws)
+    torch.cuda.synchronize()
+    for (q, s), b, sh in zip(res, ws_bits, shapes):
+        if sh[0] * sh[1] == 0:
+            continue
+        rq, rs = oracle.quant_weight_blockwise(b)
+        assert np.array_equal(q.cpu().numpy(), rq), sh
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32)), sh
