@@ -131,48 +131,80 @@ __global__ __launch_bounds__(kQwThreads) void quant_weight_multi_kernel(const We
 // no LDS or barrier is needed.
 // ---------------------------------------------------------------------------
 constexpr int kQaThreads = 256;
-constexpr int kQaGroupsPerBlock = kQaThreads / 16;
+// Groups per quarter wave, loaded before any is reduced: 4 for large
+// problems (more bytes in flight per lane), 1 when that would leave too few
+// workgroups to fill the 256 CUs (decode-sized activations).
+constexpr int kQaPassesLarge = 4;
+constexpr int64_t kQaLargeGroups = 65536;
 
+struct ActGroup {
+  int64_t m, col;
+  int g;
+  bool valid, vec;
+  u32x4 v;
+};
+
+__device__ __forceinline__ ActGroup act_group_load(const uint16_t* __restrict__ x, int64_t M, int64_t K, int G,
+                                                   int64_t gid, int li) {
+  ActGroup a;
+  a.valid = gid < M * G;
+  a.m = a.valid ? gid / G : 0;
+  a.g = a.valid ? (int)(gid % G) : 0;
+  a.col = (int64_t)a.g * kBlock + li * 8;
+  a.vec = a.valid && ((K & 7) == 0) && (a.col + 8 <= K);
+  const uint16_t* src = x + a.m * K + a.col;
+  a.v = u32x4{0u, 0u, 0u, 0u};
+  if (a.vec) {
+    a.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+  } else if (a.valid) {
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (a.col + j < K) ? src[j] : (uint16_t)0;
+    a.v = u32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+                e[6] | ((uint32_t)e[7] << 16)};
+  }
+  return a;
+}
+
+// Group amax over the quarter wave (every lane of the wave takes part), then
+// the scale and the codes.
+__device__ __forceinline__ void act_group_store(const ActGroup& a, uint8_t* __restrict__ q,
+                                                float* __restrict__ scale, int64_t K, int G, int li) {
+  uint32_t am = amax_fold(amax8(0u, a.v));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(am, off, 16);
+    am = am > o ? am : o;
+  }
+  const float s = scale_from_amax_bits(am);
+  if (a.valid && li == 0) scale[a.m * G + a.g] = s;
+  uint8_t* dst = q + a.m * K + a.col;
+  if (a.vec) {
+    __builtin_nontemporal_store(encode8(a.v, s), reinterpret_cast<u32x2*>(dst));
+  } else if (a.valid) {
+    const uint32_t e[8] = {a.v.x & 0xffffu, a.v.x >> 16, a.v.y & 0xffffu, a.v.y >> 16,
+                           a.v.z & 0xffffu, a.v.z >> 16, a.v.w & 0xffffu, a.v.w >> 16};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (a.col + j < K) dst[j] = encode1((uint16_t)e[j], s);
+  }
+}
+
+// Pass p of quarter wave w (w = threadIdx / 16) takes group
+// blockIdx * 16 * kPasses + 16 p + w, so each pass is one coalesced sweep
+// over 16 consecutive groups.
+template <int kPasses>
 __global__ __launch_bounds__(kQaThreads) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                                uint8_t* __restrict__ q,
                                                                float* __restrict__ scale, int64_t M, int64_t K,
                                                                int G) {
-  const int64_t gid = (int64_t)blockIdx.x * kQaGroupsPerBlock + (threadIdx.x >> 4);
   const int li = threadIdx.x & 15;
-  const bool valid = gid < M * G;
-  const int64_t m = valid ? gid / G : 0;
-  const int g = valid ? (int)(gid % G) : 0;
-  const int64_t col = (int64_t)g * kBlock + li * 8;
-  const bool vec = valid && ((K & 7) == 0) && (col + 8 <= K);
-  const uint16_t* src = x + m * K + col;
-  u32x4 v = u32x4{0u, 0u, 0u, 0u};
-  if (vec) {
-    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-  } else if (valid) {
-    uint16_t e[8];
+  const int64_t g0 = (int64_t)blockIdx.x * (kQaThreads / 16) * kPasses + (threadIdx.x >> 4);
+  ActGroup grp[kPasses];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = (col + j < K) ? src[j] : (uint16_t)0;
-    v = u32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
-              e[6] | ((uint32_t)e[7] << 16)};
-  }
-  uint32_t a = amax_fold(amax8(0u, v));
+  for (int p = 0; p < kPasses; ++p) grp[p] = act_group_load(x, M, K, G, g0 + 16 * p, li);
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) {
-    uint32_t o = __shfl_xor(a, off, 16);
-    a = a > o ? a : o;
-  }
-  const float s = scale_from_amax_bits(a);
-  if (valid && li == 0) scale[m * G + g] = s;
-  uint8_t* dst = q + m * K + col;
-  if (vec) {
-    __builtin_nontemporal_store(encode8(v, s), reinterpret_cast<u32x2*>(dst));
-  } else if (valid) {
-    const uint32_t e[8] = {v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16,
-                           v.z & 0xffffu, v.z >> 16, v.w & 0xffffu, v.w >> 16};
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (col + j < K) dst[j] = encode1((uint16_t)e[j], s);
-  }
+  for (int p = 0; p < kPasses; ++p) act_group_store(grp[p], q, scale, K, G, li);
 }
 
 // ---------------------------------------------------------------------------
@@ -220,10 +252,16 @@ hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t
   const int64_t G = (K + kBlock - 1) / kBlock;
   const int64_t groups = M * G;
   if (groups == 0) return hipSuccess;
-  const int64_t blocks = (groups + kQaGroupsPerBlock - 1) / kQaGroupsPerBlock;
+  const bool large = groups >= kQaLargeGroups;
+  const int64_t per_block = (kQaThreads / 16) * (large ? kQaPassesLarge : 1);
+  const int64_t blocks = (groups + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q, scale, M, K,
-                     (int)G);
+  if (large)
+    hipLaunchKernelGGL(quant_act_kernel<kQaPassesLarge>, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q,
+                       scale, M, K, (int)G);
+  else
+    hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q, scale, M, K,
+                       (int)G);
   return hipGetLastError();
 }
 
