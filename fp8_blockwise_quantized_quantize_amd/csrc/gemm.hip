@@ -368,7 +368,12 @@ struct Panel {
   static constexpr int kRows = BN + BM;                 // rows staged per K-block
   static constexpr int kLoads = kRows / 64;             // load instructions per wave per K-block
   static constexpr int kStage = kRows * kBlock;
-  static constexpr int kLdsBytes = S * kStage;
+  // Each stage also holds that K-block's scales, staged like the operands:
+  // 64 dwords per wave (activation scales of the tile's rows 0..BM-1, then
+  // the tile's weight scale blocks), after the S operand stages.
+  static constexpr int kScaleBytes = 8 * 64 * 4;
+  static_assert(BM / 64 < 8, "a wave left over for the weight scales");
+  static constexpr int kLdsBytes = S * (kStage + kScaleBytes);
   static_assert(S == 2 || S == 3, "stages");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
   static constexpr int kThreadsPerWg = 512;
@@ -392,23 +397,21 @@ struct Panel {
     const int KB = (int)(K / kBlock);
     const int64_t n_hi = (t.n0 + BN < t.N) ? t.n0 + BN : t.N;
     // weight scale blocks of this wave's rows: nb0, and nb0 + 1 for the
-    // fragments in hi_mask (only when a wave's rows can straddle a block)
+    // fragments in hi_mask (only when a wave's rows can straddle a block);
+    // wsl0 / wsl1 are their positions among the tile's blocks nbt, nbt + 1, ..
     const int64_t NBm1 = (t.N - 1) / kBlock;
+    const int64_t nbt = t.n0 / kBlock;
     const int64_t wrow0 = t.n0 + wn * WNR;
     const int64_t nb0 = ((wrow0 < t.N) ? wrow0 : t.N - 1) / kBlock;
     const int64_t nb1 = nb0 + 1 < NBm1 ? nb0 + 1 : NBm1;
-    const auto swr0 = make_rsrc(t.sw + nb0 * KB, (int64_t)KB * 4);
-    const auto swr1 = make_rsrc(t.sw + nb1 * KB, (int64_t)KB * 4);
+    const int wsl0 = (int)(nb0 - nbt), wsl1 = (int)(nb1 - nbt);
     uint32_t hi_mask = 0;
 #pragma unroll
     for (int i = 0; i < TN; ++i)
       if ((wrow0 + i * 16) / kBlock > nb0) hi_mask |= 1u << i;
     const auto wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
     const auto ar = kGather ? make_rsrc(t.a, t.a_nrows * K) : make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
-    const int64_t am_lo = t.m_lo + wm * WMR;  // this wave's activation rows (scales)
-    const int64_t am_hi = (am_lo + WMR < t.m_hi) ? am_lo + WMR : t.m_hi;
-    const int64_t arows = am_hi > am_lo ? am_hi - am_lo : 0;
-    const auto sr = kGather ? make_rsrc(t.sa, t.a_nrows * KB * 4) : make_rsrc(t.sa + am_lo * KB, arows * KB * 4);
+    const int64_t am_lo = t.m_lo + wm * WMR;  // this wave's first activation row
     // Source row of output row m: itself, or the gathered row (-1: none).
     auto src_row = [&](int64_t m) -> int64_t {
       if (m >= t.m_hi) return -1;
@@ -417,19 +420,23 @@ struct Panel {
       const int64_t r = p >= 0 ? p / t.a_div : -1;
       return r < t.a_nrows ? r : -1;
     };
-    // per-lane scale offsets of this wave's activation rows j * 16 + r16
-    const int svoff = r16 * KB * 4;
-    int svoff_g[kGather ? TM : 1];
-    if constexpr (kGather) {
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const int64_t r = src_row(am_lo + j * 16 + r16);
-        svoff_g[j] = r >= 0 ? (int)(r * KB * 4) : kOob;
-      }
-    }
     // a ragged last tile (e.g. an expert's rows past a multiple of BM) can
     // leave whole waves without a valid activation row: they skip the MFMAs
-    const bool idle = arows == 0;
+    const bool idle = am_lo >= t.m_hi;
+    // Scale staging, one buffer_load_dword ... lds per wave and K-block into
+    // the wave's 64 dwords of the stage's scale area: waves w < BM/64 load
+    // the activation scales of tile rows 64 w + lane, the others the
+    // weight scale blocks nbt + lane.  As for the operands, rows and blocks
+    // past the end sit outside the buffer range and read zeros.
+    const bool act_scales = wave < BM / 64;
+    const auto scr = act_scales ? (kGather ? make_rsrc(t.sa, t.a_nrows * KB * 4)
+                                           : make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4))
+                                : make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
+    int scvoff = lane * KB * 4;
+    if (act_scales) {
+      const int64_t r = src_row(t.m_lo + 64 * wave + lane);
+      scvoff = kGather ? (r >= 0 ? (int)(r * KB * 4) : kOob) : (64 * wave + lane) * KB * 4;
+    }
 
     // DMA staging: load q of wave w fills stage rows R0..R0+7 with
     // R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at physical chunk
@@ -455,6 +462,10 @@ struct Panel {
 #pragma unroll
       for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    auto dma_scales = [&](int kb, int stage) {
+      auto* dst = (__attribute__((address_space(3))) void*)(lds + S * kStage + stage * kScaleBytes + wave * 256);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, dst, 4, scvoff, kb * 4, 0, 0);
+    };
     auto dma_q = [&](int q, int kb, uint8_t* buf) {
       const int koff = kb * kBlock;
       const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
@@ -466,19 +477,11 @@ struct Panel {
       else              // stage rows BN..: activation rows m_lo + r0 - BN ..
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff + (r0 - BN) * (int)K, koff, 0, 0);
     };
-    // Per-K-block scales of this wave's activation rows and weight block(s),
-    // fetched one phase ahead with vector loads (tracked by vmcnt, so using
-    // them never waits on loads issued after them) and multiplied only when
-    // the phase that needs them starts.
-    struct Scales {
-      float sa[TM], sw0, sw1;
-    };
-    auto load_scales = [&](Scales& c, int kb) {
-      c.sw0 = bload_f32(swr0, 0, kb * 4);
-      c.sw1 = kOneScaleBlock ? c.sw0 : bload_f32(swr1, 0, kb * 4);
+    // all loads of one K-block: the operand rows, then the scales
+    auto dma_kblock = [&](int kb, int stage) {
 #pragma unroll
-      for (int j = 0; j < TM; ++j)
-        c.sa[j] = bload_f32(sr, kGather ? svoff_g[kGather ? j : 0] : svoff + j * 16 * KB * 4, kb * 4);
+      for (int q = 0; q < kLoads; ++q) dma_q(q, kb, lds + stage * kStage);
+      dma_scales(kb, stage);
     };
     constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
     auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * WNR + i * 16); };
@@ -493,29 +496,40 @@ struct Panel {
 #pragma unroll
       for (int p = 1; p < kAhead && p < TN; ++p) fw[p] = load_w(buf, p);
     };
-    // One phase: the product of the K-block in `buf`, with the loads of
-    // K-block `kb` into `dst` issued after every second MFMA (after every
-    // MFMA when there are few), so that the L2 and LDS-write traffic does
-    // not arrive as one burst right after the barrier.  kLoad false: no loads.
+    // One phase: the product of the K-block in stage `cur`, with the loads
+    // of K-block `kb` into stage `fill` issued after every second MFMA
+    // (after every MFMA when there are few), so that the L2 and LDS-write
+    // traffic does not arrive as one burst right after the barrier.  The
+    // scales come from the stage's scale area; their products are formed
+    // while the first MFMAs run.
     constexpr int kT = TN * TM;
-    constexpr int kEvery = (kT >= 2 * kLoads) ? 2 : 1;
-    static_assert(kT * 1 >= kLoads, "enough MFMAs to carry the loads");
-    auto phase = [&](auto load_tag, const Scales& sc, const uint8_t* buf, int kb, uint8_t* dst) {
-      constexpr bool kLoad = decltype(load_tag)::value;
+    constexpr int kPhaseLoads = kLoads + 1;
+    constexpr int kEvery = (kT >= 2 * kPhaseLoads) ? 2 : 1;
+    static_assert(kT >= kPhaseLoads, "enough MFMAs to carry the loads");
+    auto phase = [&](int cur, int kb, int fill) {
+      const uint8_t* buf = lds + cur * kStage;
       v8i fa[TM], fw[kAhead + 1];
       first_frags(fa, fw, buf);
+      const float* scl = reinterpret_cast<const float*>(lds + S * kStage + cur * kScaleBytes);
+      const float sw0 = scl[BM + wsl0];
+      const float sw1 = kOneScaleBlock ? sw0 : scl[BM + wsl1];
       float c0[TM], c1[TM];
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
-        c0[j] = sc.sa[j] * sc.sw0;
-        c1[j] = kOneScaleBlock ? c0[j] : sc.sa[j] * sc.sw1;
+        const float sa = scl[wm * WMR + j * 16 + r16];
+        c0[j] = sa * sw0;
+        c1[j] = kOneScaleBlock ? c0[j] : sa * sw1;
       }
       tile_product<TN, TM, 2, kAhead>(
           acc, fa, fw, [&](int i) { return load_w(buf, i); },
           [&](int i, int j) { return (kOneScaleBlock || !((hi_mask >> i) & 1u)) ? c0[j] : c1[j]; },
           [&](int tt) {
-            if (!kLoad || tt % kEvery != 0 || tt / kEvery >= kLoads) return false;
-            dma_q(tt / kEvery, kb, dst);
+            if (tt % kEvery != 0 || tt / kEvery >= kPhaseLoads) return false;
+            const int q = tt / kEvery;
+            if (q < kLoads)
+              dma_q(q, kb, lds + fill * kStage);
+            else
+              dma_scales(kb, fill);
             return true;
           });
     };
@@ -523,41 +537,42 @@ struct Panel {
     // for them explicitly before the barrier that publishes the stage.  With
     // three stages the loads of the next K-block may stay in flight.
     auto wait_stage = [&]() {
-      // the loads of K-block k + 1 have at least (S - 2) * kLoads loads issued after them
+      // the loads of K-block k + 1 have (S - 2) * kPhaseLoads loads issued after them
       if constexpr (S == 2)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kLoads) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kPhaseLoads) : "memory");
+    };
+    // The workgroup barrier of a phase.  Not __syncthreads(): its fence
+    // would wait for every load in flight (vmcnt(0)), including the later
+    // K-blocks' prefetches that the ring keeps in flight on purpose.  The
+    // LDS writes this barrier publishes were waited for by wait_stage();
+    // the LDS reads of the previous phase are waited for here, so no wave
+    // refills a stage that another is still reading.
+    auto barrier = [&]() {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      order_fence();
     };
     auto wait_all = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
     const int kb_last = KB - 1;
     auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };  // clamped prefetch
-    Scales sc_next;
     if (KB > 0) {
 #pragma unroll
-      for (int q = 0; q < kLoads; ++q) dma_q(q, 0, lds);
-      load_scales(sc_next, 0);
-#pragma unroll
-      for (int st = 1; st < S - 1; ++st)
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q) dma_q(q, nxt(st), lds + st * kStage);
+      for (int st = 0; st < S - 1; ++st) dma_kblock(nxt(st), st);
     }
     // Loads past the last K-block re-load it into a stage nobody reads
     // again, keeping the loop body free of branches.
     int cur = 0;  // stage of K-block k
     for (int k = 0; k < KB; ++k) {
       wait_stage();
-      __syncthreads();  // stage cur holds K-block k; stage cur - 1 is free
-      const Scales sc = sc_next;
-      load_scales(sc_next, nxt(k + 1));
+      barrier();  // stage cur holds K-block k; stage cur - 1 is free
       const int fill = (cur == 0) ? S - 1 : cur - 1;
-      order_fence();
       if (idle) {  // no valid activation row: only this wave's share of the loads
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q) dma_q(q, nxt(k + S - 1), lds + fill * kStage);
+        dma_kblock(nxt(k + S - 1), fill);
       } else {
-        phase(std::true_type{}, sc, lds + cur * kStage, nxt(k + S - 1), lds + fill * kStage);
+        phase(cur, nxt(k + S - 1), fill);
       }
       order_fence();
       cur = (cur + 1 == S) ? 0 : cur + 1;
