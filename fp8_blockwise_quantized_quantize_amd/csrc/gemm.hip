@@ -196,7 +196,10 @@ __device__ __forceinline__ void store4(uint16_t* __restrict__ y, int64_t N, int6
 // own LDS slice: coalesced 16-byte global loads (8 lanes per 128-byte row)
 // into registers one K-block ahead, ds_write into the swizzled slice, and
 // MFMA fragments read back with ds_read_b128.  Waves never share LDS data,
-// so the K loop has no workgroup barrier.
+// so the K loop has no workgroup barrier.  The activation scales of four
+// steps arrive in one load per 16-row group (one K-block per lane group):
+// per-lane scale loads touch a cache line per row, and one per step made
+// the scale loads a fifth of the kernel's vector-memory work.
 // ---------------------------------------------------------------------------
 template <int BN, int BM, int NW>
 struct Skinny {
@@ -207,14 +210,23 @@ struct Skinny {
   static constexpr int kRed = NW * BN * BM * 4;         // the waves' partial tiles, FP32
   static constexpr int kLdsBytes = (NW * kSlice > kRed) ? NW * kSlice : kRed;
   static constexpr int kThreadsPerWg = 64 * NW;
-  static constexpr int kWavesPerSimd = NW / 4;
+  // register budget: the waves of every workgroup that fits a CU's LDS
+  static constexpr int kWavesPerSimd = (NW / 4) * (2 * kLdsBytes <= 160 * 1024 ? 2 : 1);
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
   static constexpr bool kRotate = true;
   static constexpr int kRotStride = 4;  // keeps each wave's K-block residue class
 
+  // swa / swb: the K-block's scales of the tile's first and (if its rows
+  // straddle two) second weight scale block (wave-uniform: scalar loads)
   struct Stage {
     u32x4 v[kLoads];
-    float sav[TM], swv[TN];
+    float swa, swb;
+  };
+  // The activation scales of four consecutive steps of a wave, rows
+  // 16 j + r16: lane group g (lanes 16 g .. 16 g + 15) holds those of step
+  // 4 q + g; a step takes its values from its lane group with ds_bpermute.
+  struct Group {
+    float sa[TM];
   };
 
   __device__ static __forceinline__ void run(const Tile& t, uint8_t* smem) {
@@ -227,12 +239,18 @@ struct Skinny {
     const auto wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
     const auto ar = make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
     const auto sr = make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4);
-    const float* swrow[TN];  // a 16-row n-tile lies in one 128-row scale block
+    // BN <= 128: the tile's rows lie in weight scale blocks nba and nbb =
+    // nba or nba + 1; a 16-row n-tile lies in one of them (b_mask: in nbb)
+    static_assert(BN <= kBlock, "two weight scale blocks at most");
+    const int64_t nba = t.n0 / kBlock, nbb = (n_hi - 1) / kBlock;
+    const float* swa_row = t.sw + nba * KB;
+    const float* swb_row = t.sw + nbb * KB;
+    uint32_t b_mask = 0;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       int64_t nt = t.n0 + i * 16;
       nt = nt < t.N ? nt : t.N - 1;
-      swrow[i] = t.sw + (nt / kBlock) * KB;
+      if (nt / kBlock > nba) b_mask |= 1u << i;
     }
     // staging: lane owns chunk (lane & 7) of rows (lane >> 3) + 8 q; slice
     // rows 0..BN-1 are weight rows, BN..BN+BM-1 activation rows.  The row
@@ -241,6 +259,7 @@ struct Skinny {
     const int lrow = lane >> 3, lchunk = lane & 7;
     const int gvoff = lrow * (int)K + lchunk * 16;
     const int svoff = r16 * KB * 4;  // + 16 j KB 4
+    const int grp = lane >> 4;
     uint8_t* slice = reinterpret_cast<uint8_t*>(red) + wave * kSlice;
     const FragLds fl(lane);
 
@@ -258,16 +277,30 @@ struct Skinny {
       for (int q = 0; q < BN / 8; ++q) s.v[q] = bload16(wr, gvoff + 8 * q * (int)K, koff);
 #pragma unroll
       for (int q = 0; q < BM / 8; ++q) s.v[BN / 8 + q] = bload16(ar, gvoff + 8 * q * (int)K, koff);
+      s.swa = swa_row[kb];
+      s.swb = swb_row[kb];
+    };
+    const int kb_last = KB - 1;
+    auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };
+    // scales of steps 4 q .. 4 q + 3 (steps past the last re-read the last K-block)
+    auto load_group = [&](Group& G, int q) {
+      int kb = nxt(wave + NW * (4 * q + grp)) + t.rot;
+      kb = kb < KB ? kb : kb - KB;
 #pragma unroll
-      for (int j = 0; j < TM; ++j) s.sav[j] = bload_f32(sr, svoff + j * 16 * KB * 4, kb * 4);
-#pragma unroll
-      for (int i = 0; i < TN; ++i) s.swv[i] = swrow[i][kb];
+      for (int j = 0; j < TM; ++j) G.sa[j] = bload_f32(sr, svoff + j * 16 * KB * 4 + kb * 4, 0);
     };
     auto store_stage = [&](const Stage& s) {
 #pragma unroll
       for (int q = 0; q < kLoads; ++q) *reinterpret_cast<u32x4*>(slice + swz(lrow + 8 * q, lchunk)) = s.v[q];
     };
-    auto compute = [&](const Stage& s) {
+    auto bperm = [](float v, int addr) {
+      return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
+    };
+    auto compute = [&](const Stage& s, const Group& G, int step) {
+      const int addr = ((((step & 3) << 4) | r16) << 2);
+      float sa[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) sa[j] = bperm(G.sa[j], addr);
       v8i fa[TM];
 #pragma unroll
       for (int j = 0; j < TM; ++j) fa[j] = fl(slice, BN + j * 16);
@@ -275,39 +308,57 @@ struct Skinny {
       fw[0] = fl(slice, 0);
       tile_product<TN, TM, 4, 1>(
           acc, fa, fw, [&](int i) { return fl(slice, i * 16); },
-          [&](int i, int j) { return s.sav[j] * s.swv[i]; });
+          [&](int i, int j) { return sa[j] * (((b_mask >> i) & 1u) ? s.swb : s.swa); });
     };
 
-    // this wave's K-blocks: wave, wave + NW, ...  Stage sX holds the
-    // registers of the next K-block while the LDS slice holds the current.
-    // Prefetches past the last K-block re-read the last one (clamped).
-    const int kb_last = KB - 1;
-    auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };
+    // this wave's K-blocks: wave, wave + NW, ... (step 0, 1, ...).  Stage sX
+    // holds the registers of the next K-block while the LDS slice holds the
+    // current.  Prefetches past the last K-block re-read the last one
+    // (clamped).
     Stage s0, s1;
-    int kb = wave;
+    Group ga;
+    int kb = wave, step = 0;
     if (kb < KB) {
       order_fence();
+      load_group(ga, 0);
       load_stage(s0, kb);
       order_fence();
       store_stage(s0);
       load_stage(s1, nxt(kb + NW));
       order_fence();
     }
-    for (; kb + NW < KB; kb += 2 * NW) {
-      compute(s0);                      // K-block kb from the slice, scales from s0
+    // Steps step2 and step2 + 1 (K-blocks kb2 and kb2 + NW), each followed
+    // by the prefetch of the K-block two steps on and the move of the next
+    // one into the slice.
+    auto two_steps = [&](int kb2, int step2, bool next_group) {
+      compute(s0, ga, step2);           // K-block kb2 from the slice
       order_fence();
-      load_stage(s0, nxt(kb + 2 * NW));
+      load_stage(s0, nxt(kb2 + 2 * NW));
       order_fence();
-      store_stage(s1);                  // K-block kb + NW into the slice
+      store_stage(s1);                  // K-block kb2 + NW into the slice
       order_fence();
-      compute(s1);
+      compute(s1, ga, step2 + 1);
       order_fence();
-      load_stage(s1, nxt(kb + 3 * NW));
+      // after the last step of a group has read its scales, the next group
+      // is fetched into the same registers (a step ahead of its first use)
+      if (next_group) load_group(ga, (step2 >> 2) + 1);
+      load_stage(s1, nxt(kb2 + 3 * NW));
       order_fence();
-      store_stage(s0);                  // K-block kb + 2 NW
+      store_stage(s0);                  // K-block kb2 + 2 NW
       order_fence();
+    };
+    // whole groups of four steps (no branch inside: the group load has a
+    // fixed place), then at most three steps of the last group
+    for (; kb + 3 * NW < KB; kb += 4 * NW, step += 4) {
+      two_steps(kb, step, false);
+      two_steps(kb + 2 * NW, step + 2, true);
     }
-    if (kb < KB) compute(s0);
+    if (kb + NW < KB) {
+      two_steps(kb, step, false);
+      kb += 2 * NW;
+      step += 2;
+    }
+    if (kb < KB) compute(s0, ga, step);
 
     // Sum the waves' partial tiles through LDS; thread t then owns 16
     // consecutive floats of the tile in fragment order.
@@ -718,7 +769,7 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
     Kern::run(t, smem);
 }
 
-enum class Cfg { kSkinny64x64, kSkinny96x64, kWide, kDecodePanel };
+enum class Cfg { kSkinny64x64, kWide, kDecodePanel };
 
 // Per-workgroup cycle estimate: operand bytes through L1 (64 B/clk/CU) vs
 // FP8 MFMA (8192 FLOP/clk/CU), times the rounds of workgroups over 256 CUs.
@@ -738,9 +789,7 @@ Cfg choose(int64_t M, int64_t N, int64_t K) {
   double best = est_cycles(M, N, K, Wide::BN, Wide::BM, cus);
   Cfg c = Cfg::kWide;
   const double s64 = est_cycles(M, N, K, 64, 64, cus) * 1.05;  // partial-tile reduction overhead
-  if (s64 < best) { best = s64; c = Cfg::kSkinny64x64; }
-  const double s96 = est_cycles(M, N, K, 96, 64, cus) * 1.05;
-  if (s96 < best) { best = s96; c = Cfg::kSkinny96x64; }
+  if (s64 < best) c = Cfg::kSkinny64x64;
   return c;
 }
 
@@ -756,14 +805,13 @@ hipError_t launch_dense_cfg(const uint8_t* a, const float* sa, const uint8_t* w,
 }
 
 // Tile override for tests and diagnostics: FP8BQ_GEMM_TILE = skinny64 |
-// skinny96 | wide | decode_panel forces that kernel for every dense GEMM
+// wide | decode_panel forces that kernel for every dense GEMM
 // (wide | decode_panel for the grouped GEMM); unset (the default) lets the
 // cost model choose.  Read on every call.
 Cfg tile_for(int64_t M, int64_t N, int64_t K) {
   const char* e = std::getenv("FP8BQ_GEMM_TILE");
   if (e != nullptr && *e != '\0') {
     if (std::strcmp(e, "skinny64") == 0) return Cfg::kSkinny64x64;
-    if (std::strcmp(e, "skinny96") == 0) return Cfg::kSkinny96x64;
     if (std::strcmp(e, "wide") == 0) return Cfg::kWide;
     if (std::strcmp(e, "decode_panel") == 0) return Cfg::kDecodePanel;
   }
@@ -805,8 +853,6 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
   switch (tile_for(M, N, K)) {
     case Cfg::kSkinny64x64:
       return launch_dense_cfg<Skinny<64, 64, 4>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
-    case Cfg::kSkinny96x64:
-      return launch_dense_cfg<Skinny<96, 64, 4>, 96, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kDecodePanel:
       return launch_dense_cfg<DecodePanel, DecodePanel::BN, DecodePanel::BM>(a, sa, w, sw, y, M, N, K, stream);
     default:
