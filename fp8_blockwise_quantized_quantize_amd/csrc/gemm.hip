@@ -160,10 +160,6 @@ struct Tile {
   const float* sw;
   uint16_t* y;
   int64_t m_lo, m_hi, n0, N, K;
-  // K-block rotation: the tile visits K-blocks starting at `rot` (mod KB).
-  // Rows of one K-block column are K bytes apart and land on few L2
-  // channels; spreading the workgroups' K positions spreads the channels.
-  int rot;
   // Gathered activations (grouped GEMM only): output row m reads row
   // a_rows[m] / a_div of a (of a_nrows rows); others read zeros.
   const int32_t* a_rows;
@@ -213,8 +209,6 @@ struct Skinny {
   // register budget: the waves of every workgroup that fits a CU's LDS
   static constexpr int kWavesPerSimd = (NW / 4) * (2 * kLdsBytes <= 160 * 1024 ? 2 : 1);
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
-  static constexpr bool kRotate = true;
-  static constexpr int kRotStride = 4;  // keeps each wave's K-block residue class
 
   // swa / swb: the K-block's scales of the tile's first and (if its rows
   // straddle two) second weight scale block (wave-uniform: scalar loads)
@@ -269,9 +263,7 @@ struct Skinny {
 #pragma unroll
       for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    auto load_stage = [&](Stage& s, int step) {
-      int kb = step + t.rot;  // rotated K-block id, step < KB
-      kb = kb < KB ? kb : kb - KB;
+    auto load_stage = [&](Stage& s, int kb) {
       const int koff = kb * kBlock;
 #pragma unroll
       for (int q = 0; q < BN / 8; ++q) s.v[q] = bload16(wr, gvoff + 8 * q * (int)K, koff);
@@ -284,8 +276,7 @@ struct Skinny {
     auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };
     // scales of steps 4 q .. 4 q + 3 (steps past the last re-read the last K-block)
     auto load_group = [&](Group& G, int q) {
-      int kb = nxt(wave + NW * (4 * q + grp)) + t.rot;
-      kb = kb < KB ? kb : kb - KB;
+      const int kb = nxt(wave + NW * (4 * q + grp));
 #pragma unroll
       for (int j = 0; j < TM; ++j) G.sa[j] = bload_f32(sr, svoff + j * 16 * KB * 4 + kb * 4, 0);
     };
@@ -429,8 +420,6 @@ struct Panel {
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
   static constexpr int kThreadsPerWg = 512;
   static constexpr int kWavesPerSimd = 2;
-  static constexpr bool kRotate = false;
-  static constexpr int kRotStride = 1;
   // a wave's weight rows lie in one 128-row scale block when tiles start at
   // multiples of 128 and the wave's share divides 128
   static constexpr bool kOneScaleBlock = (BN % kBlock == 0) && (kBlock % WNR == 0);
@@ -687,7 +676,6 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   t.m_hi = (t.m_lo + BM < M) ? t.m_lo + BM : M;
   t.n0 = tn * BN;
   t.N = N; t.K = K;
-  t.rot = Kern::kRotate ? (int)((L * Kern::kRotStride) % (K / kBlock > 0 ? K / kBlock : 1)) : 0;
   t.a_rows = nullptr; t.a_div = 1; t.a_nrows = 0;
   Kern::run(t, smem);
 }
@@ -761,7 +749,6 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   t.m_hi = (t.m_lo + BM < hi) ? t.m_lo + BM : hi;
   t.n0 = tn * BN;
   t.N = N; t.K = K;
-  t.rot = 0;
   t.a_rows = a_rows; t.a_div = a_div; t.a_nrows = a_nrows;
   if constexpr (kGather)
     Kern::run_gather(t, smem);
