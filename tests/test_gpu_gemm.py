@@ -82,6 +82,36 @@ def test_gemm_every_tile_kernel(fb, monkeypatch, tile, m, n, k):
     assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw), oracle.gemm_ref(qa, sa, qw, sw))
 
 
+@pytest.mark.parametrize("tile", TILES)
+def test_gemm_every_tile_random_scales(fb, monkeypatch, tile):
+    """Each tile kernel with a different scale in every weight block,
+    activation row and K-block (tiles that straddle scale blocks, a partial
+    last block, zero-scale rows).  The spread (2^-3..2^3) keeps every
+    K-block's term visible in the sum, and each (row, 128-column block)
+    is checked on its own, so a scale applied to the wrong rows, block or
+    K-block fails."""
+    announce("gemm tile random scales", tile)
+    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
+    rng = np.random.default_rng(35)
+    m, n, k = 300, 520, 640
+    qa = rng.integers(0, 256, (m, k)).astype(np.uint8)
+    qw = rng.integers(0, 256, (n, k)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x00
+    qw[(qw & 0x7F) == 0x7F] = 0x80
+    sa = np.exp2(rng.uniform(-3, 3, (m, k // 128))).astype(np.float32)
+    sw = np.exp2(rng.uniform(-3, 3, ((n + 127) // 128, k // 128))).astype(np.float32)
+    zero_rows = [0, 63, 64, 257]
+    sa[zero_rows] = 0
+    y = gpu_gemm(fb, qa, sa, qw, sw)
+    ref = oracle.gemm_ref(qa, sa, qw, sw)
+    assert np.all((y[zero_rows] & 0x7FFF) == 0)
+    for r in range(m):
+        if r in zero_rows:
+            continue
+        for c0 in range(0, n, 128):
+            assert_gemm_close(y[r:r + 1, c0:c0 + 128], ref[r:r + 1, c0:c0 + 128], min_exact=0.5)
+
+
 def test_gemm_k_zero_gives_zeros(fb):
     announce("gemm K = 0")
     y = fb.gemm_w8a8_blockscaled(torch.empty((5, 0), dtype=torch.uint8, device="cuda"),
