@@ -16,18 +16,20 @@
 //
 // Two tile kernels share that inner step:
 //
-//  * skinny<BN, BM> (few activation rows, e.g. decode with M = 256): a
-//    BN x BM output tile per 4-wave workgroup; the four waves split the
+//  * skinny<64, 64> (few activation rows, e.g. decode with M = 256): a
+//    64 x 64 output tile per 4-wave workgroup; the four waves split the
 //    K-blocks (wave w takes kb = w, w+4, ...).  Each wave stages its own
 //    K-blocks through a private LDS slice (coalesced 16-byte loads into
 //    registers one K-block ahead, ds_write, fragment reads), and the four
 //    partial tiles are summed through LDS at the end.
 //
-//  * wide (many rows: prefill, MoE experts): a 256 (n) x 256 (m) tile per
-//    8-wave workgroup (two waves per SIMD), waves in a 2 (n) x 4 (m) grid of
-//    128 x 64.  Both operands of a K-block go global -> LDS directly
-//    (buffer_load ... lds), double-buffered, one barrier per K-block; the
-//    loads of the next K-block are spread over the MFMAs of the current one.
+//  * panel<BN, BM, ..., S> (many rows: prefill and MoE experts with a
+//    256 x 256 tile, two stages; decode with many weight rows with a
+//    128 x 256 tile, three stages): eight waves (two per SIMD).  Both
+//    operands of a K-block and its scales go global -> LDS directly
+//    (buffer_load ... lds) into a ring of S stages, one barrier per
+//    K-block; the loads of K-block k + S - 1 are spread over the MFMAs of
+//    K-block k.
 //
 // Tiles are ordered so that the workgroups resident on one XCD at a time
 // (consecutive workgroup ids of the same id % 8) share weight and
@@ -392,8 +394,9 @@ struct Skinny {
 // in a WGN (n) x WGM (m) grid.  Both operands of a K-block (BN weight rows
 // + BM activation rows, 128 bytes each) go global -> LDS directly
 // (buffer_load ... lds, 16 bytes per lane, 8 lanes per 128-byte row) into
-// a ring of S stages, so no VGPRs hold staging data; fragments are read
-// with ds_read_b128.
+// a ring of S stages, and so do the K-block's scales (one dword per lane),
+// so no load in the K loop writes a VGPR; fragments are read with
+// ds_read_b128 and scales with ds_read.
 // Phase k: wait for this wave's loads of K-block k; barrier (everyone's
 // data has landed, and everyone is done with the stage read in phase k-1);
 // compute k while issuing the loads of K-block k + S - 1 into that stage
