@@ -639,6 +639,10 @@ using DecodePanel = Panel<128, 256, 2, 4, 3>;
 // per workgroup instead of the wide tile's one, for weights streamed from
 // HBM once (MoE experts, whose weights no other tile reads).
 using Deep = Panel<256, 128, 2, 4, 3>;
+// Decode with exactly one round of tiles: at M = 256 and N = 24576 the
+// 192 x 128 panel gives 256 tiles (one per CU), where the 128 x 256 panel
+// leaves 64 CUs idle (48.4 vs 52.6 us on the Qwen3-8B gate_up at M = 256).
+using Panel192 = Panel<192, 128, 2, 4, 3>;
 
 // ---------------------------------------------------------------------------
 // Tile order: XCD-aware remap of the workgroup id, then groups of kGroupM
@@ -764,7 +768,7 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
     Kern::run(t, smem);
 }
 
-enum class Cfg { kSkinny64x64, kWide, kDecodePanel, kDeep };
+enum class Cfg { kSkinny64x64, kWide, kDecodePanel, kDeep, kPanel192 };
 
 // Per-workgroup cycle estimate: operand bytes through L1 (64 B/clk/CU) vs
 // FP8 MFMA (8192 FLOP/clk/CU), times the rounds of workgroups over 256 CUs.
@@ -780,7 +784,12 @@ Cfg choose(int64_t M, int64_t N, int64_t K) {
   const double cus = 256.0;
   // Few activation rows but many weight rows: one 128 x 256 panel covers
   // every row of the activation panel, so each weight row is read once.
-  if (M <= DecodePanel::BM && (N + DecodePanel::BN - 1) / DecodePanel::BN >= 160) return Cfg::kDecodePanel;
+  if (M <= DecodePanel::BM && (N + DecodePanel::BN - 1) / DecodePanel::BN >= 160) {
+    // the 192 x 128 panel when its tiles fill 224..256 CUs in one round
+    const int64_t t192 = ((N + Panel192::BN - 1) / Panel192::BN) * ((M + Panel192::BM - 1) / Panel192::BM);
+    if (t192 >= 224 && t192 <= (int64_t)cus) return Cfg::kPanel192;
+    return Cfg::kDecodePanel;
+  }
   double best = est_cycles(M, N, K, Wide::BN, Wide::BM, cus);
   Cfg c = Cfg::kWide;
   const double s64 = est_cycles(M, N, K, 64, 64, cus) * 1.05;  // partial-tile reduction overhead
@@ -800,7 +809,7 @@ hipError_t launch_dense_cfg(const uint8_t* a, const float* sa, const uint8_t* w,
 }
 
 // Tile override for tests and diagnostics: FP8BQ_GEMM_TILE = skinny64 |
-// wide | decode_panel | deep forces that kernel for every dense GEMM
+// wide | decode_panel | deep | panel192 forces that kernel for every dense GEMM
 // (wide | decode_panel | deep for the grouped GEMM); unset (the default)
 // lets the cost model choose.  Read on every call.
 Cfg tile_for(int64_t M, int64_t N, int64_t K) {
@@ -810,6 +819,7 @@ Cfg tile_for(int64_t M, int64_t N, int64_t K) {
     if (std::strcmp(e, "wide") == 0) return Cfg::kWide;
     if (std::strcmp(e, "decode_panel") == 0) return Cfg::kDecodePanel;
     if (std::strcmp(e, "deep") == 0) return Cfg::kDeep;
+    if (std::strcmp(e, "panel192") == 0) return Cfg::kPanel192;
   }
   return choose(M, N, K);
 }
@@ -857,6 +867,8 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
       return launch_dense_cfg<Skinny<64, 64, 4>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kDecodePanel:
       return launch_dense_cfg<DecodePanel, DecodePanel::BN, DecodePanel::BM>(a, sa, w, sw, y, M, N, K, stream);
+    case Cfg::kPanel192:
+      return launch_dense_cfg<Panel192, Panel192::BN, Panel192::BM>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kDeep:
       return launch_dense_cfg<Deep, Deep::BN, Deep::BM>(a, sa, w, sw, y, M, N, K, stream);
     default:
