@@ -17,6 +17,7 @@
 //                       bits, an order-independent exact max)
 //   kv_scale_kernel     amax bits -> s in place
 //   kv_write_kernel     quantize each token's K / V and store it in its slot
+//                       (up to four 16-byte chunks per lane, loads issued first)
 #include "device_common.hpp"
 #include "group_quant.hpp"
 #include "launch.hpp"
@@ -119,7 +120,16 @@ __device__ __forceinline__ u32x2 encode8_sat(u32x4 v, float s) {
   return u32x2{pack4_e4m3(q[0], q[1], q[2], q[3]), pack4_e4m3(q[4], q[5], q[6], q[7])};
 }
 
-// grid (ceil(T * C / 256), 1 or 2): one 16-byte chunk per lane.
+// grid (ceil(T * C / (256 kPer)), 1 or 2): lane l of workgroup b handles
+// the 16-byte chunks 256 (b kPer + u) + l, u = 0..kPer-1 (consecutive lanes,
+// consecutive chunks).  All the chunks' loads (value, slot, scale) are
+// issued before any of them is used, and before the slot decides whether
+// anything is stored: with one chunk per lane the value load waited for the
+// slot, and too few bytes were in flight to keep HBM busy.  Lanes past the
+// last chunk re-load the last one and store nothing.  kPer = 4 for large
+// writes (a prefill chunk); 1 for small ones (decode steps), which need the
+// workgroups more than the bytes in flight per lane.
+template <int kKvWritePer>
 __global__ __launch_bounds__(kKvThreads) void kv_write_kernel(const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               const int32_t* __restrict__ slots,
@@ -128,20 +138,43 @@ __global__ __launch_bounds__(kKvThreads) void kv_write_kernel(const uint16_t* __
                                                               uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                                                               int64_t T, int H, int D, int per_head, int64_t S) {
   const int C = H * D / 8;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kKvThreads + threadIdx.x;
-  if (i >= T * C) return;
-  const int64_t t = i / C;
-  const int col = static_cast<int>(i - t * C);
-  const int32_t slot = slots[t];
-  if (slot < 0 || slot >= S) return;  // padding: nothing stored
+  const int64_t n = T * C;
   const bool is_v = blockIdx.y == 1;
   const uint16_t* x = is_v ? v : k;
   const float* sc = is_v ? vs : ks;
   uint8_t* cache = is_v ? vc : kc;
   const int64_t HD = static_cast<int64_t>(H) * D;
-  const float s = sc[per_head ? (col * 8) / D : 0];
-  const u32x4 val = *reinterpret_cast<const u32x4*>(x + t * HD + col * 8);
-  *reinterpret_cast<u32x2*>(cache + static_cast<int64_t>(slot) * HD + col * 8) = encode8_sat(val, s);
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * (kKvThreads * kKvWritePer) + threadIdx.x;
+  int64_t t[kKvWritePer];
+  int col[kKvWritePer];
+#pragma unroll
+  for (int u = 0; u < kKvWritePer; ++u) {
+    int64_t i = i0 + u * kKvThreads;
+    i = i < n ? i : n - 1;
+    if (n <= 0x7fffffffLL) {  // uniform: 32-bit division
+      const uint32_t tt = static_cast<uint32_t>(i) / static_cast<uint32_t>(C);
+      t[u] = tt;
+      col[u] = static_cast<int>(static_cast<uint32_t>(i) - tt * static_cast<uint32_t>(C));
+    } else {
+      t[u] = i / C;
+      col[u] = static_cast<int>(i - t[u] * C);
+    }
+  }
+  int32_t slot[kKvWritePer];
+  float s[kKvWritePer];
+  u32x4 val[kKvWritePer];
+#pragma unroll
+  for (int u = 0; u < kKvWritePer; ++u) {
+    slot[u] = slots[t[u]];
+    s[u] = sc[per_head ? (col[u] * 8) / D : 0];
+    val[u] = *reinterpret_cast<const u32x4*>(x + t[u] * HD + col[u] * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < kKvWritePer; ++u) {
+    const bool mine = i0 + u * kKvThreads < n;
+    if (!mine || slot[u] < 0 || slot[u] >= S) continue;  // past the end, or padding: nothing stored
+    *reinterpret_cast<u32x2*>(cache + static_cast<int64_t>(slot[u]) * HD + col[u] * 8) = encode8_sat(val[u], s[u]);
+  }
 }
 
 }  // namespace
@@ -170,10 +203,18 @@ hipError_t launch_kv_write(const uint16_t* k, const uint16_t* v, const int32_t* 
                            int64_t S, hipStream_t stream) {
   const int64_t chunks = T * (H * D / 8);
   if (chunks == 0) return hipSuccess;
-  const int64_t blocks = (chunks + kKvThreads - 1) / kKvThreads;
+  // four chunks per lane while that still leaves >= 512 workgroups per tensor
+  const bool wide = chunks >= 512LL * kKvThreads * 4;
+  const int per = wide ? 4 : 1;
+  const int64_t blocks = (chunks + kKvThreads * per - 1) / (kKvThreads * per);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kv_write_kernel, dim3(static_cast<unsigned>(blocks), vs ? 2u : 1u), dim3(kKvThreads), 0, stream,
-                     k, v, slots, ks, vs, kc, vc, T, static_cast<int>(H), static_cast<int>(D), per_head ? 1 : 0, S);
+  const dim3 grid(static_cast<unsigned>(blocks), vs ? 2u : 1u);
+  if (wide)
+    hipLaunchKernelGGL(kv_write_kernel<4>, grid, dim3(kKvThreads), 0, stream, k, v, slots, ks, vs, kc, vc, T,
+                       static_cast<int>(H), static_cast<int>(D), per_head ? 1 : 0, S);
+  else
+    hipLaunchKernelGGL(kv_write_kernel<1>, grid, dim3(kKvThreads), 0, stream, k, v, slots, ks, vs, kc, vc, T,
+                       static_cast<int>(H), static_cast<int>(D), per_head ? 1 : 0, S);
   return hipGetLastError();
 }
 

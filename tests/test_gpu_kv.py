@@ -61,9 +61,13 @@ def test_calibrate(T, H, D, per_head):
     assert vs2 is None and np.array_equal(host(ks2), host(ks))
 
 
-@pytest.mark.parametrize("T,H,D,S", [(1, 1, 8, 4), (9, 2, 16, 20), (1000, 8, 128, 1500), (77, 64, 128, 100)])
+@pytest.mark.parametrize("T,H,D,S", [(1, 1, 8, 4), (9, 2, 16, 20), (1000, 8, 128, 1500), (77, 64, 128, 100),
+                                     (4099, 8, 128, 5000)])
 @pytest.mark.parametrize("per_head", [True, False])
 def test_cache_write(T, H, D, S, per_head):
+    """Random slots with padding (-1 and S); the last shape is large enough
+    for the four-chunks-per-lane kernel (524,672 chunks) with a ragged last
+    workgroup."""
     announce("kv write", T, H, D, S, per_head)
     rng = np.random.default_rng([111, T])
     k, v = kv_bits(T, H, D, 3), kv_bits(T, H, D, 4)
