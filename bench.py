@@ -92,6 +92,12 @@ def parse():
     p.add_argument("--rocprof-summary", metavar="DIR",
                    help="summarise rocprofv3 output under DIR (kernel trace + FETCH_SIZE / WRITE_SIZE passes "
                         "of this benchmark and of --calibrate-copy) and exit")
+    p.add_argument("--gemm-profile", action="store_true",
+                   help="only run each GEMM of GEMM_PROFILE_CASES a few times (a target for rocprofv3 "
+                        "counter passes) and exit")
+    p.add_argument("--gemm-counter-summary", metavar="DIR",
+                   help="summarise rocprofv3 passes of --gemm-profile under DIR (kt, mfma, lds, l2, fetch, "
+                        "write, copy_fetch, copy_write) and exit")
     return p.parse_args()
 
 
@@ -116,6 +122,12 @@ def main():
         return
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
+        return
+    if args.gemm_profile:
+        gemm_profile()
+        return
+    if args.gemm_counter_summary:
+        gemm_counter_summary(args.gemm_counter_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -761,6 +773,148 @@ def rocprof_summary(d):
         lines.append("| %s | %.2f | %.2f | %.3f |" % (p, v["bytes_per_launch"] / 1e6, a / 1e6, v["bytes_per_launch"] / a))
     lines.append("")
     lines.append("traffic-json: " + json.dumps(out, sort_keys=True))
+    print("\n".join(lines))
+
+
+# ---------------------------------------------------------------------------
+# GEMM counter profile: each GEMM of the decode (M = 256), prefill (M = 8192)
+# and MoE expert configurations, GEMM_PROFILE_REPS launches in a row, in
+# this order; the summary matches GEMM dispatches to cases by that order.
+# ---------------------------------------------------------------------------
+
+GEMM_PROFILE_REPS = 3
+
+
+def gemm_profile_cases():
+    """(label, M_total, N, K, experts or 0) of every GEMM profiled, in launch order."""
+    sys.path.insert(0, ROOT)
+    from synthetic import LAYER_SHAPES_QWEN3_8B, MOE_QWEN3_30B_A3B
+
+    cases = [("decode %s" % nm, 256, n, k, 0) for nm, n, k in LAYER_SHAPES_QWEN3_8B]
+    cases += [("prefill %s" % nm, 8192, n, k, 0) for nm, n, k in LAYER_SHAPES_QWEN3_8B]
+    moe = MOE_QWEN3_30B_A3B
+    mt = moe["tokens"] * moe["top_k"]
+    cases.append(("MoE fc1 gate_up", mt, moe["gate_up"][0], moe["gate_up"][1], moe["experts"]))
+    cases.append(("MoE fc2 down", mt, moe["down"][0], moe["down"][1], moe["experts"]))
+    return cases
+
+
+def gemm_profile():
+    """Run each case GEMM_PROFILE_REPS times on freshly quantized synthetic inputs."""
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import fp8_blockwise_quantized_quantize_amd as fb
+    from synthetic import MOE_QWEN3_30B_A3B, device_bf16_normal, moe_routing
+
+    moe = MOE_QWEN3_30B_A3B
+    _, _, off = moe_routing(moe["tokens"], moe["experts"], moe["top_k"], (4, 0))
+    offsets = torch.from_numpy(off).to("cuda:0")
+    for i, (label, m, n, k, g) in enumerate(gemm_profile_cases()):
+        w = device_bf16_normal((g, n, k) if g else (n, k), 0.02, seed=700 + i)
+        x = device_bf16_normal((m, k), 1.0, seed=800 + i)
+        wq, ws = fb.quantize_weight_blockwise(w)
+        xq, xs = fb.quantize_act_per_token_group(x)
+        del w, x
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+        torch.cuda.synchronize()
+        for _ in range(GEMM_PROFILE_REPS):
+            if g:
+                fb.grouped_gemm_w8a8_blockscaled(xq, xs, wq, ws, offsets, y)
+            else:
+                fb.gemm_w8a8_blockscaled(xq, xs, wq, ws, y)
+        torch.cuda.synchronize()
+        print("gemm profile case done:", label, flush=True)
+        del wq, ws, xq, xs, y
+        torch.cuda.empty_cache()
+
+
+def gemm_counter_summary(d):
+    """Markdown summary of the rocprofv3 passes of --gemm-profile under `d`:
+      kt     --kernel-trace            durations per dispatch
+      mfma   SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE
+      lds    SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_LDS_ADDR_CONFLICT
+      l2     TCC_HIT_sum TCC_MISS_sum
+      fetch / write, copy_fetch / copy_write   as for the decode-step summary
+    MOPS_F8 counts FP8 MFMA work in units of 512 FLOPs (it equals 2MNK on
+    dense shapes).  GRBM_GUI_ACTIVE reads 8 x the kernel's cycles (it sums
+    over the 8 XCDs: / 8 / duration gives 2.0-2.2 GHz on the long prefill
+    kernels), so the clock is GRBM_GUI_ACTIVE / 8 / duration (meaningful for
+    long kernels only: the counter window also covers launch overhead).
+    MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs); it equals
+    the FLOP rate over the FP8 peak at the measured clock."""
+    cases = gemm_profile_cases()
+
+    def gemm_dispatches(rows, key):
+        out = {}
+        for r in rows:
+            if "gemm_dense_kernel" in r["Kernel_Name"] or "gemm_grouped_kernel" in r["Kernel_Name"]:
+                out.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]}).update(key(r))
+        return [out[i] for i in sorted(out)]
+
+    def counters(sub):
+        rows = _csv_rows(os.path.join(d, sub, "**", "*counter_collection.csv"))
+        return gemm_dispatches(rows, lambda r: {r["Counter_Name"]: float(r["Counter_Value"])})
+
+    kt = gemm_dispatches(_csv_rows(os.path.join(d, "kt", "**", "*kernel_trace.csv")),
+                         lambda r: {"ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+    passes = {sub: counters(sub) for sub in ("mfma", "lds", "l2", "fetch", "write")}
+    n_expected = len(cases) * GEMM_PROFILE_REPS
+
+    def per_case(disp, key):
+        if len(disp) != n_expected:
+            return [None] * len(cases)
+        vals = []
+        for c in range(len(cases)):
+            xs = [x.get(key) for x in disp[c * GEMM_PROFILE_REPS:(c + 1) * GEMM_PROFILE_REPS]]
+            xs = [x for x in xs if x is not None]
+            vals.append(sum(xs) / len(xs) if xs else None)
+        return vals
+
+    copy = {}
+    for sub, counter in (("copy_fetch", "FETCH_SIZE"), ("copy_write", "WRITE_SIZE")):
+        v = [float(r["Counter_Value"]) * 1024.0
+             for r in _csv_rows(os.path.join(d, sub, "**", "*counter_collection.csv"))
+             if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+        copy[counter] = float(1 << 30) / (sum(v) / len(v)) if v else None
+    ns = per_case(kt, "ns")
+    mops = per_case(passes["mfma"], "SQ_INSTS_VALU_MFMA_MOPS_F8")
+    busy = per_case(passes["mfma"], "SQ_VALU_MFMA_BUSY_CYCLES")
+    grbm = per_case(passes["mfma"], "GRBM_GUI_ACTIVE")
+    bank = per_case(passes["lds"], "SQ_LDS_BANK_CONFLICT")
+    ldsact = per_case(passes["lds"], "SQ_LDS_IDX_ACTIVE")
+    hit = per_case(passes["l2"], "TCC_HIT_sum")
+    miss = per_case(passes["l2"], "TCC_MISS_sum")
+    fetch = per_case(passes["fetch"], "FETCH_SIZE")
+    write = per_case(passes["write"], "WRITE_SIZE")
+    names = [_short(kt[c * GEMM_PROFILE_REPS]["name"]) if len(kt) == n_expected else "?" for c in range(len(cases))]
+
+    def f(v, fmt):
+        return fmt % v if v is not None else "n/a"
+
+    lines = ["Dispatches matched: kernel trace %d, mfma %d, lds %d, l2 %d, fetch %d, write %d (expected %d)."
+             % (len(kt), *(len(passes[s]) for s in ("mfma", "lds", "l2", "fetch", "write")), n_expected), "",
+             "| GEMM | kernel | us | TFLOP/s (2MNK) | % of FP8 peak | counter FLOPs / 2MNK | clock GHz "
+             "| MFMA busy | LDS bank-conflict / active cycles | L2 hit | L2-miss MB / algorithmic MB |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for c, (label, m, n, k, g) in enumerate(cases):
+        flops = 2.0 * m * n * k
+        nb = -(-n // 128)
+        algo = m * k + (g or 1) * n * k + 2 * m * n + 4 * m * (k // 128) + 4 * (g or 1) * nb * (k // 128)
+        tf = flops / ns[c] / 1e3 if ns[c] else None
+        ghz = grbm[c] / 8.0 / ns[c] if grbm[c] and ns[c] else None
+        mb = busy[c] / (grbm[c] / 8.0 * 1024.0) if busy[c] is not None and grbm[c] else None
+        hbm = None
+        if fetch[c] is not None and write[c] is not None and copy["FETCH_SIZE"] and copy["WRITE_SIZE"]:
+            hbm = (fetch[c] * 1024.0 * copy["FETCH_SIZE"] + write[c] * 1024.0 * copy["WRITE_SIZE"]) / 1e6
+        lines.append("| %s (M=%d N=%d K=%d%s) | `%s` | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            label, m, n, k, ", %d experts" % g if g else "", names[c][:60], f(ns[c] and ns[c] / 1e3, "%.1f"),
+            f(tf, "%.0f"), f(tf and 100.0 * tf / FP8_PEAK_TFLOPS, "%.1f%%"),
+            f(mops[c] and mops[c] * 512.0 / flops, "%.3f"), f(ghz, "%.2f"), f(mb and 100.0 * mb, "%.1f%%"),
+            f(bank[c] / ldsact[c] if bank[c] is not None and ldsact[c] else None, "%.3f"),
+            f(hit[c] / (hit[c] + miss[c]) if hit[c] is not None and miss[c] is not None and hit[c] + miss[c] else None,
+              "%.3f"),
+            f(hbm and "%.1f / %.1f" % (hbm, algo / 1e6), "%s")))
     print("\n".join(lines))
 
 

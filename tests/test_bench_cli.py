@@ -29,3 +29,57 @@ def test_rocprof_summary_of_nothing(tmp_path):
     r = _run("--rocprof-summary", str(tmp_path))
     assert r.returncode == 0, r.stderr
     assert "traffic-json: {}" in r.stdout
+
+
+def test_gemm_counter_summary_of_synthetic_csvs(tmp_path):
+    """The GEMM counter summary matches dispatches to cases in launch order
+    and derives its columns as documented: a case with 2MNK FLOPs in MOPS
+    units, a 1 ms duration, GRBM = 8 x 2e6 cycles (2.0 GHz) and MFMA busy
+    cycles of half of 1024 SIMDs x 2e6 reads 1.000, 2.00 GHz and 50.0%."""
+    import csv
+
+    sys.path.insert(0, ROOT)
+    import bench
+
+    cases = bench.gemm_profile_cases()
+    reps = bench.GEMM_PROFILE_REPS
+    name = "void fp8bq::(anonymous namespace)::gemm_dense_kernel<Wide, 256, 256>(args)"
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+    def write_pass(sub, values):
+        d = tmp_path / sub
+        d.mkdir()
+        with open(d / "p_counter_collection.csv", "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=cols)
+            w.writeheader()
+            w.writerow({"Dispatch_Id": 1, "Kernel_Name": "other_kernel", "Counter_Name": "X", "Counter_Value": 1})
+            for i in range(len(cases) * reps):
+                m, n, k, _ = cases[i // reps][1:]
+                for cname, v in values(m, n, k).items():
+                    w.writerow({"Dispatch_Id": 10 + i, "Kernel_Name": name, "Counter_Name": cname,
+                                "Counter_Value": v})
+
+    (tmp_path / "kt").mkdir()
+    with open(tmp_path / "kt" / "kt_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i in range(len(cases) * reps):
+            w.writerow({"Dispatch_Id": 10 + i, "Kernel_Name": name, "Start_Timestamp": 1000,
+                        "End_Timestamp": 1000 + 1_000_000})
+    write_pass("mfma", lambda m, n, k: {"SQ_INSTS_VALU_MFMA_MOPS_F8": 2.0 * m * n * k / 512,
+                                        "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 1024 * 2e6,
+                                        "GRBM_GUI_ACTIVE": 8 * 2e6, "SQ_BUSY_CYCLES": 1})
+    write_pass("lds", lambda m, n, k: {"SQ_LDS_BANK_CONFLICT": 1, "SQ_LDS_IDX_ACTIVE": 4})
+    write_pass("l2", lambda m, n, k: {"TCC_HIT_sum": 3, "TCC_MISS_sum": 1})
+    r = _run("--gemm-counter-summary", str(tmp_path))
+    assert r.returncode == 0, r.stderr
+    assert "kernel trace %d, mfma %d" % (len(cases) * reps, len(cases) * reps) in r.stdout
+    rows = [line for line in r.stdout.splitlines() if line.startswith("| decode qkv")]
+    assert len(rows) == 1
+    cells = [c.strip() for c in rows[0].strip("|").split("|")]
+    # us, TFLOP/s, % peak, counter ratio, GHz, MFMA busy, LDS conflicts, L2 hit, bytes
+    m, n, k = 256, 6144, 4096
+    assert cells[2] == "1000.0"
+    assert cells[3] == "%.0f" % (2.0 * m * n * k / 1e-3 / 1e12)
+    assert cells[5:10] == ["1.000", "2.00", "50.0%", "0.250", "0.750"]
+    assert cells[10] == "n/a"  # no fetch / write passes
