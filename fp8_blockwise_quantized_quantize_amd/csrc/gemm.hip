@@ -354,8 +354,10 @@ struct Skinny {
     }
     if (kb < KB) compute(s0, ga, step);
 
-    // Sum the waves' partial tiles through LDS; thread t then owns 16
-    // consecutive floats of the tile in fragment order.
+    // Sum the waves' partial tiles through LDS.  Each wave stores its tile
+    // in fragment order (unit (i TM + j) 64 + lane = that lane's four
+    // values of MFMA tile (i, j)); thread t then sums units q 256 + t over
+    // the waves, so a wave's reads are 1 KB contiguous (no bank conflicts).
     __syncthreads();  // every wave is done with its staging slice
     float* mine = red + wave * (BN * BM);
 #pragma unroll
@@ -363,28 +365,19 @@ struct Skinny {
 #pragma unroll
       for (int j = 0; j < TM; ++j) *reinterpret_cast<v4f*>(mine + ((i * TM + j) * 64 + lane) * 4) = acc[i][j];
     __syncthreads();
-    constexpr int kGroups = BN * BM / 16;  // groups of 16 floats: 4 lanes x 4 values of one (i, j)
+    constexpr int kUnits = BN * BM / 4;
+    static_assert(kUnits % kThreadsPerWg == 0, "whole rounds of units");
 #pragma unroll
-    for (int q = 0; q < (kGroups + kThreadsPerWg - 1) / kThreadsPerWg; ++q) {
-      const int gi = q * kThreadsPerWg + threadIdx.x;
-      if (gi >= kGroups) break;
-      const int base = gi * 16;
-      v4f sum[4];
+    for (int q = 0; q < kUnits / kThreadsPerWg; ++q) {
+      const int unit = q * kThreadsPerWg + threadIdx.x;
+      v4f sum = *reinterpret_cast<const v4f*>(red + 4 * unit);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sum[u] = *reinterpret_cast<const v4f*>(red + base + 4 * u);
-#pragma unroll
-        for (int w2 = 1; w2 < NW; ++w2) sum[u] += *reinterpret_cast<const v4f*>(red + w2 * (BN * BM) + base + 4 * u);
-      }
-      const int ij = base / 256, l0 = (base / 4) % 64;
+      for (int w2 = 1; w2 < NW; ++w2) sum += *reinterpret_cast<const v4f*>(red + w2 * (BN * BM) + 4 * unit);
+      const int ij = unit / 64, l = unit % 64;
       const int i = ij / TM, j = ij % TM;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int l = l0 + u;
-        const int64_t m = t.m_lo + j * 16 + (l & 15);
-        const int64_t n = t.n0 + i * 16 + (l >> 4) * 4;
-        if (m < t.m_hi) store4(t.y, t.N, m, n, sum[u]);
-      }
+      const int64_t m = t.m_lo + j * 16 + (l & 15);
+      const int64_t n = t.n0 + i * 16 + (l >> 4) * 4;
+      if (m < t.m_hi) store4(t.y, t.N, m, n, sum);
     }
   }
 };
