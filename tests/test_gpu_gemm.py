@@ -325,3 +325,36 @@ def test_offsets_debug_mode(fb, monkeypatch):
     with pytest.raises(fb.FP8BQError, match="invalid shape"):
         fb.grouped_gemm_w8a8_blockscaled_gather(_dev(qa), _dev(sa), _dev(rows), 1, _dev(qw), _dev(sw),
                                                 _dev(np.array([0, 9, 5, 14], np.int32)))
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_gemm_largest_k(fb, monkeypatch, tile):
+    """K = 2^22, the largest K the boundary accepts: a 256-row activation
+    panel then spans 2^30 bytes, still addressed with 32-bit buffer offsets
+    (the 256-row tiles read rows up to 255 * 2^22 bytes in), over 32768
+    K-blocks.  Random E4M3 codes (NaN codes replaced by zero) and random
+    scales, drawn on the GPU; rows 0, 1, 128 and 255 are checked against the
+    oracle on the host.  One K-block more is rejected before anything runs."""
+    k = 1 << 22
+    m, n = 256, 3
+    announce("gemm largest K", tile, m, n, k)
+    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
+    g = torch.Generator(device="cuda").manual_seed(2201)
+    qa = torch.randint(0, 256, (m, k), generator=g, dtype=torch.uint8, device="cuda")
+    qa[(qa & 0x7F) == 0x7F] = 0
+    qw = torch.randint(0, 256, (n, k), generator=g, dtype=torch.uint8, device="cuda")
+    qw[(qw & 0x7F) == 0x7F] = 0
+    sa = torch.rand((m, k // 128), generator=g, device="cuda") + 0.5
+    sw = torch.rand((1, k // 128), generator=g, device="cuda") + 0.5
+    y = fb.gemm_w8a8_blockscaled(qa, sa, qw, sw)
+    torch.cuda.synchronize()
+    rows = [0, 1, 128, 255]
+    ref = oracle.gemm_ref(qa[rows].cpu().numpy(), sa[rows].cpu().numpy(), qw.cpu().numpy(), sw.cpu().numpy())
+    got = device_to_bits(y)[rows]
+    print(assert_gemm_close(got, ref))
+    del qa, y
+    over = k + 128
+    a1 = torch.zeros((1, over), dtype=torch.uint8, device="cuda")
+    s1 = torch.ones((1, over // 128), device="cuda")
+    with pytest.raises(fb.FP8BQError, match="shape"):
+        fb.gemm_w8a8_blockscaled(a1, s1, a1, s1)
