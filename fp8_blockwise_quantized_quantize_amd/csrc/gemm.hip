@@ -624,6 +624,219 @@ struct Panel {
       for (int i = 0; i < TN; ++i) store4(t.y, t.N, m, t.n0 + wn * WNR + i * 16 + g * 4, acc[i][j]);
     }
   }
+
+  // Several tiles per workgroup: tile r = 0 .. ntiles-1 comes from
+  // tile_at(r), and the K-blocks of consecutive tiles stream through the
+  // one ring of S stages, so the first loads of tile r + 1 are in flight
+  // while tile r finishes and stores its outputs (no per-tile pipeline
+  // fill).  The loads follow the tile of the step being prefetched ("load
+  // side"), the MFMAs, scales and stores the tile being computed ("compute
+  // side").  Prefetches past the last step re-load the last K-block into a
+  // stage nobody reads again.
+  template <bool kGather, class TileAt>
+  __device__ static __forceinline__ void run_persistent(int ntiles, TileAt tile_at, uint8_t* lds) {
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wn = wave % WGN, wm = wave / WGN;
+    const bool act_scales = wave < BM / 64;
+    const int chunk_off = ((lane & 7) ^ (lane >> 3)) << 4;
+    const FragLds fl(lane);
+
+    // ---- load side: operand and scale buffers of the tile being prefetched
+    Tile lt = tile_at(0);
+    const int64_t K = lt.K;
+    const int KB = (int)(K / kBlock);
+    const int dvoff = (lane >> 3) * (int)K + chunk_off;
+    __amdgpu_buffer_rsrc_t wr, ar, scr;
+    int scvoff = 0;
+    int aoff[kGather ? BM / 64 : 1];
+    auto src_row = [&](const Tile& t, int64_t m) -> int64_t {
+      if (m >= t.m_hi) return -1;
+      if (!kGather) return m - t.m_lo;
+      const int32_t pr = t.a_rows[m];
+      const int64_t r = pr >= 0 ? pr / t.a_div : -1;
+      return r < t.a_nrows ? r : -1;
+    };
+    auto setup_load = [&](const Tile& t) {
+      const int64_t n_hi = (t.n0 + BN < t.N) ? t.n0 + BN : t.N;
+      const int64_t NBm1 = (t.N - 1) / kBlock, nbt = t.n0 / kBlock;
+      wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
+      ar = kGather ? make_rsrc(t.a, t.a_nrows * K) : make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
+      scr = act_scales ? (kGather ? make_rsrc(t.sa, t.a_nrows * KB * 4)
+                                  : make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4))
+                       : make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
+      scvoff = lane * KB * 4;
+      if (act_scales) {
+        const int64_t r = src_row(t, t.m_lo + 64 * wave + lane);
+        scvoff = kGather ? (r >= 0 ? (int)(r * KB * 4) : kOob) : (64 * wave + lane) * KB * 4;
+      }
+      if constexpr (kGather) {
+#pragma unroll
+        for (int qa = 0; qa < BM / 64; ++qa) {
+          const int64_t r = src_row(t, t.m_lo + 8 * (8 * (BN / 64 + qa) + wave) - BN + (lane >> 3));
+          aoff[qa] = r >= 0 ? (int)(r * K) + chunk_off : kOob;
+        }
+      }
+    };
+    setup_load(lt);
+    int lt_r = 0, lt_kb = 0;
+    // the next step to prefetch (clamped to the last K-block of the last tile)
+    auto advance_load = [&]() {
+      if (lt_kb + 1 < KB) {
+        ++lt_kb;
+      } else if (lt_r + 1 < ntiles) {
+        ++lt_r;
+        lt_kb = 0;
+        lt = tile_at(lt_r);
+        setup_load(lt);
+      }
+    };
+
+    // ---- compute side: scales, MFMAs and stores of the tile being computed
+    Tile ct = lt;
+    int wsl0 = 0, wsl1 = 0;
+    uint32_t hi_mask = 0;
+    bool idle = false;
+    auto setup_compute = [&](const Tile& t) {
+      const int64_t NBm1 = (t.N - 1) / kBlock, nbt = t.n0 / kBlock;
+      const int64_t wrow0 = t.n0 + wn * WNR;
+      const int64_t nb0 = ((wrow0 < t.N) ? wrow0 : t.N - 1) / kBlock;
+      const int64_t nb1 = nb0 + 1 < NBm1 ? nb0 + 1 : NBm1;
+      wsl0 = (int)(nb0 - nbt);
+      wsl1 = (int)(nb1 - nbt);
+      hi_mask = 0;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        if ((wrow0 + i * 16) / kBlock > nb0) hi_mask |= 1u << i;
+      idle = t.m_lo + wm * WMR >= t.m_hi;
+    };
+    setup_compute(ct);
+    int ct_r = 0, ct_kb = 0;
+
+    v4f acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    auto dma_scales = [&](int kb, int stage) {
+      auto* dst = (__attribute__((address_space(3))) void*)(lds + S * kStage + stage * kScaleBytes + wave * 256);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, dst, 4, scvoff, kb * 4, 0, 0);
+    };
+    auto dma_q = [&](int q, int kb, uint8_t* buf) {
+      const int koff = kb * kBlock;
+      const int r0 = 8 * (8 * q + wave);
+      auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
+      if (q < BN / 64)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, koff, 0, 0);
+      else if (kGather)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, aoff[kGather ? q - BN / 64 : 0], koff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff + (r0 - BN) * (int)K, koff, 0, 0);
+    };
+    auto dma_kblock = [&](int kb, int stage) {
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) dma_q(q, kb, lds + stage * kStage);
+      dma_scales(kb, stage);
+    };
+    constexpr int kAhead = 2;
+    auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * WNR + i * 16); };
+    auto first_frags = [&](v8i (&fa)[TM], v8i (&fw)[kAhead + 1], const uint8_t* buf) {
+      fw[0] = load_w(buf, 0);
+      fa[0] = fl(buf, BN + wm * WMR);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 1; j < TM; ++j) fa[j] = fl(buf, BN + wm * WMR + j * 16);
+#pragma unroll
+      for (int pp = 1; pp < kAhead && pp < TN; ++pp) fw[pp] = load_w(buf, pp);
+    };
+    constexpr int kT = TN * TM;
+    constexpr int kPhaseLoads = kLoads + 1;
+    constexpr int kEvery = (kT >= 2 * kPhaseLoads) ? 2 : 1;
+    static_assert(kT >= kPhaseLoads, "enough MFMAs to carry the loads");
+    auto phase = [&](int cur, int kb, int fill) {
+      const uint8_t* buf = lds + cur * kStage;
+      v8i fa[TM], fw[kAhead + 1];
+      first_frags(fa, fw, buf);
+      const float* scl = reinterpret_cast<const float*>(lds + S * kStage + cur * kScaleBytes);
+      const float sw0 = scl[BM + wsl0];
+      const float sw1 = kOneScaleBlock ? sw0 : scl[BM + wsl1];
+      float c0[TM], c1[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const float sa = scl[wm * WMR + j * 16 + r16];
+        c0[j] = sa * sw0;
+        c1[j] = kOneScaleBlock ? c0[j] : sa * sw1;
+      }
+      tile_product<TN, TM, 2, kAhead>(
+          acc, fa, fw, [&](int i) { return load_w(buf, i); },
+          [&](int i, int j) { return (kOneScaleBlock || !((hi_mask >> i) & 1u)) ? c0[j] : c1[j]; },
+          [&](int tt) {
+            if (tt % kEvery != 0 || tt / kEvery >= kPhaseLoads) return false;
+            const int q = tt / kEvery;
+            if (q < kLoads)
+              dma_q(q, kb, lds + fill * kStage);
+            else
+              dma_scales(kb, fill);
+            return true;
+          });
+    };
+    // The same waits and barrier as run_impl.  After a tile's stores the
+    // vmcnt wait also covers them (stores count in vmcnt): it waits longer
+    // then, never too little.
+    auto wait_stage = [&]() {
+      if constexpr (S == 2)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kPhaseLoads) : "memory");
+    };
+    auto barrier = [&]() {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      order_fence();
+    };
+
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) {
+      dma_kblock(lt_kb, st);
+      advance_load();
+    }
+    const int64_t steps = (int64_t)ntiles * KB;
+    int cur = 0;
+    for (int64_t step = 0; step < steps; ++step) {
+      wait_stage();
+      barrier();
+      const int fill = (cur == 0) ? S - 1 : cur - 1;
+      if (idle) {
+        dma_kblock(lt_kb, fill);
+      } else {
+        phase(cur, lt_kb, fill);
+      }
+      order_fence();
+      advance_load();
+      cur = (cur + 1 == S) ? 0 : cur + 1;
+      if (++ct_kb == KB) {  // the compute tile's last K-block: store it, start the next
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const int64_t m = ct.m_lo + wm * WMR + j * 16 + r16;
+          if (m >= ct.m_hi) continue;
+#pragma unroll
+          for (int i = 0; i < TN; ++i) store4(ct.y, ct.N, m, ct.n0 + wn * WNR + i * 16 + g * 4, acc[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        ct_kb = 0;
+        if (++ct_r < ntiles) {
+          ct = tile_at(ct_r);
+          setup_compute(ct);
+        }
+        order_fence();
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may be in flight when the workgroup ends
+  }
 };
 
 using Wide = Panel<256, 256, 2, 4, 2>;
@@ -761,6 +974,95 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
     Kern::run(t, smem);
 }
 
+// Persistent grouped form: `gridDim.x` workgroups (at most one per CU)
+// each take tiles pos, pos + P, pos + 2P, .. of the (expert, m-tile, n-tile)
+// list, where P = gridDim.x and pos is the XCD-aware rank of the workgroup,
+// so that the workgroups of one XCD run consecutive tiles (the n-tiles of
+// one expert's rows) at the same time.  The workgroup first builds the
+// prefix of ceil(rows_e / BM) over the experts in LDS; a tile's expert is
+// then a binary search in it.  Offsets are clamped to [0, M] as in the
+// per-tile kernel.
+constexpr int kMaxPersistentExperts = 1024;
+
+template <class Kern, bool kGather>
+__global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_grouped_persistent_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ w,
+    const float* __restrict__ sw, const int32_t* __restrict__ offsets, uint16_t* __restrict__ y, int64_t M,
+    int64_t N, int64_t K, int G, int64_t tiles_n, const int32_t* __restrict__ a_rows, int a_div, int64_t a_nrows) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int NT = threads_of<Kern>();
+  constexpr int BM = Kern::BM, BN = Kern::BN;
+  __shared__ int pre[kMaxPersistentExperts + 1];
+  __shared__ int wave_sum[NT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto clamped = [&](int e, int* lo, int* hi) {
+    int l = offsets[e], h = offsets[e + 1];
+    l = l < 0 ? 0 : (l > M ? (int)M : l);
+    h = h < l ? l : (h > M ? (int)M : h);
+    *lo = l;
+    *hi = h;
+  };
+  if (tid == 0) pre[0] = 0;
+  int base = 0;
+  for (int c0 = 0; c0 < G; c0 += NT) {
+    const int e = c0 + tid;
+    int tiles = 0;
+    if (e < G) {
+      int lo, hi;
+      clamped(e, &lo, &hi);
+      tiles = (hi - lo + BM - 1) / BM;
+    }
+    int incl = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    __syncthreads();
+    if (lane == 63) wave_sum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < wave; ++i) before += wave_sum[i];
+    if (e < G) pre[e + 1] = base + before + incl;
+    int total = 0;
+    for (int i = 0; i < NT / 64; ++i) total += wave_sum[i];
+    base += total;
+  }
+  __syncthreads();
+  const int64_t tiles = (int64_t)pre[G] * tiles_n;
+  const int64_t P = gridDim.x;
+  const int64_t pos = xcd_linear(blockIdx.x, P);
+  if (pos >= tiles) return;  // uniform
+  const int ntiles = (int)((tiles - pos + P - 1) / P);
+  const int64_t KB = K / kBlock;
+  const int64_t NB = (N + kBlock - 1) / kBlock;
+  auto tile_at = [&](int r) {
+    const int64_t L = pos + (int64_t)r * P;
+    const int64_t tn = L % tiles_n;
+    const int slot = (int)(L / tiles_n);
+    int lo_e = 0, hi_e = G - 1;  // the largest e with pre[e] <= slot
+    while (lo_e < hi_e) {
+      const int mid = (lo_e + hi_e + 1) >> 1;
+      if (pre[mid] <= slot) lo_e = mid; else hi_e = mid - 1;
+    }
+    const int e = lo_e;
+    int lo, hi;
+    clamped(e, &lo, &hi);
+    Tile t;
+    t.a = a; t.sa = sa;
+    t.w = w + (int64_t)e * N * K;
+    t.sw = sw + (int64_t)e * NB * KB;
+    t.y = y;
+    t.m_lo = (int64_t)lo + (int64_t)(slot - pre[e]) * BM;
+    t.m_hi = (t.m_lo + BM < hi) ? t.m_lo + BM : hi;
+    t.n0 = tn * BN;
+    t.N = N; t.K = K;
+    t.a_rows = a_rows; t.a_div = a_div; t.a_nrows = a_nrows;
+    return t;
+  };
+  Kern::template run_persistent<kGather>(ntiles, tile_at, smem);
+}
+
 enum class Cfg { kSkinny64x64, kWide, kDecodePanel, kDeep, kPanel192 };
 
 // Per-workgroup cycle estimate: operand bytes through L1 (64 B/clk/CU) vs
@@ -803,8 +1105,9 @@ hipError_t launch_dense_cfg(const uint8_t* a, const float* sa, const uint8_t* w,
 
 // Tile override for tests and diagnostics: FP8BQ_GEMM_TILE = skinny64 |
 // wide | decode_panel | deep | panel192 forces that kernel for every dense GEMM
-// (wide | decode_panel | deep for the grouped GEMM); unset (the default)
-// lets the cost model choose.  Read on every call.
+// (wide | decode_panel | deep (one tile per workgroup) | deep_persistent for
+// the grouped GEMM); unset (the default) lets the cost model choose.  Read
+// on every call.
 Cfg tile_for(int64_t M, int64_t N, int64_t K) {
   const char* e = std::getenv("FP8BQ_GEMM_TILE");
   if (e != nullptr && *e != '\0') {
@@ -831,6 +1134,19 @@ hipError_t launch_grouped_cfg(const uint8_t* a, const float* sa, const uint8_t* 
   return hipGetLastError();
 }
 
+template <class Kern, bool kGather>
+hipError_t launch_grouped_persistent(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                                     const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
+                                     const int32_t* a_rows, int a_div, int64_t a_nrows, hipStream_t stream) {
+  const int64_t tiles_n = (N + Kern::BN - 1) / Kern::BN;
+  const int64_t bound = tiles_n * ((M + Kern::BM - 1) / Kern::BM + G);  // >= the tiles there are
+  const int64_t P = bound < 256 ? bound : 256;  // one workgroup per CU (the tile's LDS allows one)
+  hipLaunchKernelGGL((gemm_grouped_persistent_kernel<Kern, kGather>), dim3((unsigned)P), dim3(Kern::kThreadsPerWg),
+                     (size_t)Kern::kLdsBytes, stream, a, sa, w, sw, offsets, y, M, N, K, (int)G, tiles_n, a_rows,
+                     a_div, a_nrows);
+  return hipGetLastError();
+}
+
 template <bool kGather>
 hipError_t launch_grouped_any(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                               const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
@@ -840,14 +1156,21 @@ hipError_t launch_grouped_any(const uint8_t* a, const float* sa, const uint8_t* 
   // only, so they stream from HBM, and the deep (three-stage) panel keeps
   // more of them in flight.  Measured on the Qwen3-30B-A3B expert layer
   // (128 experts, ~256 rows each): fc1 234 vs 263 us, fc2 168 vs 178 us
-  // for the 256 x 256 two-stage tile.  The others on override.
+  // for the 256 x 256 two-stage tile.  Run persistent (one workgroup per
+  // CU, the ring carried across tiles) while the expert table fits in LDS:
+  // fc1 224-228 vs 240 us, fc2 131 vs 167 us (its tiles have 6 K-blocks,
+  // so the per-tile pipeline fill weighed most).  The others on override.
   const char* e = std::getenv("FP8BQ_GEMM_TILE");
   if (e != nullptr && std::strcmp(e, "decode_panel") == 0)
     return launch_grouped_cfg<DecodePanel, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows,
                                                     stream);
   if (e != nullptr && std::strcmp(e, "wide") == 0)
     return launch_grouped_cfg<Wide, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows, stream);
-  return launch_grouped_cfg<Deep, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows, stream);
+  const bool per_tile = e != nullptr && std::strcmp(e, "deep") == 0;
+  if (per_tile || G > kMaxPersistentExperts)
+    return launch_grouped_cfg<Deep, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows, stream);
+  return launch_grouped_persistent<Deep, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows,
+                                                  stream);
 }
 
 }  // namespace

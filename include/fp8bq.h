@@ -160,6 +160,11 @@ fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, c
  *   unspecified output rows but never an out-of-bounds access: every row
  *   index is clamped to [0, M_total).  M_total + 128 * G must fit in int32;
  *   K as for gemm_w8a8_blockscaled.
+ *   For G <= 1024 one workgroup per CU runs the expert tiles in turn (the
+ *   launch does not depend on how the rows are spread); for more experts,
+ *   one workgroup per tile.  FP8BQ_GEMM_TILE (wide, decode_panel, deep,
+ *   deep_persistent), read on every call, forces a tile kernel for tests
+ *   and diagnostics.
  *   Debug mode: with FP8BQ_CHECK_OFFSETS=1 in the environment (read on every
  *   call) the call copies the offsets to the host, waits for them on
  *   `stream`, and returns FP8BQ_ERR_BAD_SHAPE, launching nothing, unless

@@ -208,7 +208,7 @@ def gpu_grouped(fb, qa, sa, qw, sw, off):
     return device_to_bits(y)
 
 
-@pytest.mark.parametrize("tile", ["wide", "decode_panel", "deep"])
+@pytest.mark.parametrize("tile", ["wide", "decode_panel", "deep", "deep_persistent"])
 @pytest.mark.parametrize("counts", [[3, 0, 17, 1, 0], [0, 0, 300, 0], [129], [0, 128, 0, 1, 255, 0, 0, 2],
                                     [1] * 40, [257, 511, 70]])
 def test_grouped_small(fb, monkeypatch, tile, counts):
@@ -223,7 +223,7 @@ def test_grouped_small(fb, monkeypatch, tile, counts):
             assert_gemm_close(y[lo:hi], ref[lo:hi])
 
 
-@pytest.mark.parametrize("tile", ["wide", "decode_panel", "deep"])
+@pytest.mark.parametrize("tile", ["wide", "decode_panel", "deep", "deep_persistent"])
 @pytest.mark.parametrize("counts,div", [([3, 0, 17, 1, 0], 1), ([0, 128, 0, 1, 255, 0, 0, 2], 8), ([257, 511, 70], 3),
                                         ([1] * 40, 2)])
 def test_grouped_gather(fb, monkeypatch, tile, counts, div):
