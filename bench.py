@@ -848,7 +848,7 @@ def gemm_counter_summary(d):
     def gemm_dispatches(rows, key):
         out = {}
         for r in rows:
-            if "gemm_dense_kernel" in r["Kernel_Name"] or "gemm_grouped_kernel" in r["Kernel_Name"]:
+            if "gemm_dense_kernel" in r["Kernel_Name"] or "gemm_grouped" in r["Kernel_Name"]:
                 out.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]}).update(key(r))
         return [out[i] for i in sorted(out)]
 
