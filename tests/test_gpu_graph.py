@@ -1,5 +1,7 @@
 """The library's kernels under HIP graph capture: a decode-layer step
-(re-quant, activation quant, GEMMs) and a KV-cache calibration + write are
+(re-quant, activation quant, GEMMs), a ragged MoE grouped GEMM (plain and
+with gathered rows; the persistent expert-tile kernel by default) and a
+KV-cache calibration + write are
 captured once and replayed several times, with eager work and
 synchronizations between replays; every replay's outputs must equal the
 eager outputs bit for bit (the kernels are deterministic and no memset is
@@ -45,7 +47,24 @@ def test_graph_replays_match_eager():
               vc=torch.zeros((T, H, D), dtype=torch.uint8, device=DEV),
               slots=torch.arange(T, dtype=torch.int32, device=DEV))
 
+    G, NE, KE = 16, 256, 384
+    counts = np.array([0, 37, 300, 1, 0, 129, 256, 3, 0, 90, 17, 400, 2, 0, 64, 5], np.int64)
+    Me = int(counts.sum())
+    moe = dict(wq=torch.empty((G, NE, KE), dtype=torch.uint8, device=DEV),
+               ws=torch.empty((G, NE // 128, KE // 128), dtype=torch.float32, device=DEV),
+               xq=torch.empty((Me, KE), dtype=torch.uint8, device=DEV),
+               xs=torch.empty((Me, KE // 128), dtype=torch.float32, device=DEV),
+               off=torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device=DEV),
+               rows=torch.tensor(np.random.default_rng(7).integers(-1, 2 * Me, Me).astype(np.int32), device=DEV),
+               y=torch.empty((Me, NE), dtype=torch.bfloat16, device=DEV),
+               yg=torch.empty((Me, NE), dtype=torch.bfloat16, device=DEV))
+    fb().quantize_weight_blockwise(device_bf16_normal((G, NE, KE), 0.02, seed=70), moe["wq"], moe["ws"])
+    fb().quantize_act_per_token_group(device_bf16_normal((Me, KE), 1.0, seed=71), moe["xq"], moe["xs"])
+
     def work():
+        fb().grouped_gemm_w8a8_blockscaled(moe["xq"], moe["xs"], moe["wq"], moe["ws"], moe["off"], moe["y"])
+        fb().grouped_gemm_w8a8_blockscaled_gather(moe["xq"], moe["xs"], moe["rows"], 2, moe["wq"], moe["ws"],
+                                                  moe["off"], moe["yg"])
         for L in layers:
             fb().quantize_weight_blockwise(L["w"], L["wq"], L["ws"])
             fb().quantize_act_per_token_group(L["x"], L["xq"], L["xs"])
@@ -54,7 +73,7 @@ def test_graph_replays_match_eager():
         fb().kv_cache_write_fp8(kv["k"], kv["v"], kv["slots"], kv["ks"], kv["vs"], kv["kc"], kv["vc"])
 
     outs = ([t for L in layers for t in (L["wq"], L["ws"], L["xq"], L["xs"], L["y"])] +
-            [kv["ks"], kv["vs"], kv["kc"], kv["vc"]])
+            [kv["ks"], kv["vs"], kv["kc"], kv["vc"], moe["y"], moe["yg"]])
     announce("graph eager reference")
     work()
     ref = snapshot(outs)
