@@ -358,3 +358,28 @@ def test_gemm_largest_k(fb, monkeypatch, tile):
     s1 = torch.ones((1, over // 128), device="cuda")
     with pytest.raises(fb.FP8BQError, match="shape"):
         fb.gemm_w8a8_blockscaled(a1, s1, a1, s1)
+
+
+@pytest.mark.parametrize("tile", [None, "deep_persistent"])
+def test_grouped_more_experts_than_the_persistent_table(fb, monkeypatch, tile):
+    """1100 experts, most of them empty: above the 1024 experts whose tile
+    prefix the persistent kernel keeps in LDS, so the default (and even a
+    forced deep_persistent) runs the per-tile kernel; 1024 experts exactly
+    still run persistent."""
+    for g_total in (1100, 1024):
+        announce("grouped many experts", tile, g_total)
+        if tile:
+            monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
+        else:
+            monkeypatch.delenv("FP8BQ_GEMM_TILE", raising=False)
+        rng = np.random.default_rng(g_total)
+        counts = np.zeros(g_total, np.int64)
+        busy = rng.choice(g_total, 24, replace=False)
+        counts[busy] = rng.integers(1, 300, 24)
+        counts[-1] = 5  # the last expert's rows end the offsets
+        qa, sa, qw, sw, off = _grouped_oracle_inputs(counts, 128, 256, 90 + g_total)
+        y = gpu_grouped(fb, qa, sa, qw, sw, off)
+        ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, off)
+        for e in np.nonzero(counts)[0]:
+            lo, hi = off[e], off[e + 1]
+            assert_gemm_close(y[lo:hi], ref[lo:hi])
