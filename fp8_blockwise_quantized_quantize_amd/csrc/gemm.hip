@@ -25,12 +25,15 @@
 //
 //  * panel<BN, BM, ..., S> (many rows: prefill with a 256 x 256 tile, two
 //    stages; MoE experts with a 256 x 128 tile, three stages; decode with
-//    many weight rows with a 128 x 256 tile, three stages): eight waves
-//    (two per SIMD).  Both
-//    operands of a K-block and its scales go global -> LDS directly
-//    (buffer_load ... lds) into a ring of S stages, one barrier per
-//    K-block; the loads of K-block k + S - 1 are spread over the MFMAs of
-//    K-block k.
+//    many weight rows with a 128 x 256 or 192 x 128 tile, three stages):
+//    eight waves (two per SIMD).  Both operands of a K-block and its scales
+//    go global -> LDS directly (buffer_load ... lds) into a ring of S
+//    stages, one barrier per K-block; the loads of K-block k + S - 1 are
+//    spread over the MFMAs of K-block k.
+//
+// The grouped GEMM runs the panel persistently: one workgroup per CU takes
+// expert tiles in turn, and the ring runs on from one tile's K-blocks into
+// the next tile's, so no tile waits for its pipeline to fill.
 //
 // Tiles are ordered so that the workgroups resident on one XCD at a time
 // (consecutive workgroup ids of the same id % 8) share weight and
