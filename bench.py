@@ -835,6 +835,9 @@ def gemm_counter_summary(d):
       mfma   SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE
       lds    SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_LDS_ADDR_CONFLICT
       l2     TCC_HIT_sum TCC_MISS_sum
+      wave   SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS
+             SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_ANY
+      ta     TA_BUSY_avr GRBM_GUI_ACTIVE
       fetch / write, copy_fetch / copy_write   as for the decode-step summary
     MOPS_F8 counts FP8 MFMA work in units of 512 FLOPs (it equals 2MNK on
     dense shapes).  GRBM_GUI_ACTIVE reads 8 x the kernel's cycles (it sums
@@ -858,7 +861,7 @@ def gemm_counter_summary(d):
 
     kt = gemm_dispatches(_csv_rows(os.path.join(d, "kt", "**", "*kernel_trace.csv")),
                          lambda r: {"ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
-    passes = {sub: counters(sub) for sub in ("mfma", "lds", "l2", "fetch", "write")}
+    passes = {sub: counters(sub) for sub in ("mfma", "lds", "l2", "fetch", "write", "wave", "ta")}
     n_expected = len(cases) * GEMM_PROFILE_REPS
 
     def per_case(disp, key):
@@ -915,6 +918,23 @@ def gemm_counter_summary(d):
             f(hit[c] / (hit[c] + miss[c]) if hit[c] is not None and miss[c] is not None and hit[c] + miss[c] else None,
               "%.3f"),
             f(hbm and "%.1f / %.1f" % (hbm, algo / 1e6), "%s")))
+    # where the waves' time goes: each counter over SQ_WAVE_CYCLES (wave-cycles
+    # summed over waves); TA busy over the kernel's cycles (ta pass)
+    wc = per_case(passes["wave"], "SQ_WAVE_CYCLES")
+    wave_cols = ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                 "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM")
+    wv = {c: per_case(passes["wave"], c) for c in wave_cols}
+    ta = per_case(passes["ta"], "TA_BUSY_avr")
+    ta_grbm = per_case(passes["ta"], "GRBM_GUI_ACTIVE")
+    lines += ["", "Dispatches matched: wave %d, ta %d (expected %d).  Fractions of the waves' cycles "
+              "(SQ_WAVE_CYCLES), and TA busy over the kernel's cycles:" % (len(passes["wave"]), len(passes["ta"]),
+                                                                          n_expected), "",
+              "| GEMM | " + " | ".join(c.replace("SQ_", "") for c in wave_cols) + " | TA busy |",
+              "|---" * (len(wave_cols) + 2) + "|"]
+    for c, (label, m, n, k, g) in enumerate(cases):
+        cells = [f(wv[col][c] / wc[c] if wv[col][c] is not None and wc[c] else None, "%.3f") for col in wave_cols]
+        tb = ta[c] / (ta_grbm[c] / 8.0) if ta[c] is not None and ta_grbm[c] else None
+        lines.append("| %s | %s | %s |" % (label, " | ".join(cells), f(tb, "%.3f")))
     print("\n".join(lines))
 
 

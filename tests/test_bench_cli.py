@@ -71,10 +71,14 @@ def test_gemm_counter_summary_of_synthetic_csvs(tmp_path):
                                         "GRBM_GUI_ACTIVE": 8 * 2e6, "SQ_BUSY_CYCLES": 1})
     write_pass("lds", lambda m, n, k: {"SQ_LDS_BANK_CONFLICT": 1, "SQ_LDS_IDX_ACTIVE": 4})
     write_pass("l2", lambda m, n, k: {"TCC_HIT_sum": 3, "TCC_MISS_sum": 1})
+    write_pass("wave", lambda m, n, k: {"SQ_WAVE_CYCLES": 100, "SQ_WAIT_ANY": 40, "SQ_WAIT_INST_ANY": 30,
+                                        "SQ_WAIT_INST_LDS": 5, "SQ_ACTIVE_INST_ANY": 60, "SQ_ACTIVE_INST_VALU": 20,
+                                        "SQ_ACTIVE_INST_LDS": 10, "SQ_ACTIVE_INST_VMEM": 2})
+    write_pass("ta", lambda m, n, k: {"TA_BUSY_avr": 1e6, "GRBM_GUI_ACTIVE": 8 * 2e6})
     r = _run("--gemm-counter-summary", str(tmp_path))
     assert r.returncode == 0, r.stderr
     assert "kernel trace %d, mfma %d" % (len(cases) * reps, len(cases) * reps) in r.stdout
-    rows = [line for line in r.stdout.splitlines() if line.startswith("| decode qkv")]
+    rows = [line for line in r.stdout.splitlines() if line.startswith("| decode qkv (")]
     assert len(rows) == 1
     cells = [c.strip() for c in rows[0].strip("|").split("|")]
     # us, TFLOP/s, % peak, counter ratio, GHz, MFMA busy, LDS conflicts, L2 hit, bytes
@@ -83,3 +87,7 @@ def test_gemm_counter_summary_of_synthetic_csvs(tmp_path):
     assert cells[3] == "%.0f" % (2.0 * m * n * k / 1e-3 / 1e12)
     assert cells[5:10] == ["1.000", "2.00", "50.0%", "0.250", "0.750"]
     assert cells[10] == "n/a"  # no fetch / write passes
+    wave = [line for line in r.stdout.splitlines() if line.startswith("| decode qkv |")]
+    assert len(wave) == 1
+    assert [c.strip() for c in wave[0].strip("|").split("|")][1:] == [
+        "0.400", "0.300", "0.050", "0.600", "0.200", "0.100", "0.020", "0.500"]
