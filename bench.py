@@ -130,8 +130,9 @@ def main():
         gemm_counter_summary(args.gemm_counter_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the kernels run on one GPU's share of the work; see DESIGN.md for how it would shard).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path.  Its kernels run on "
+              "one GPU's share of the work: whole 128x128 weight blocks for re-quantization, column- or "
+              "row-parallel GEMM slices at multiples of 128, or whole experts.",
               file=sys.stderr)
         sys.exit(2)
 
