@@ -16,8 +16,8 @@
 //
 // Two tile kernels share that inner step:
 //
-//  * skinny<64, 64> (few activation rows, e.g. decode with M = 256): a
-//    64 x 64 output tile per 4-wave workgroup; the four waves split the
+//  * skinny<64 or 48, 64> (few activation rows, e.g. decode with M = 256):
+//    a 64 (or 48) x 64 output tile per 4-wave workgroup; the four waves split the
 //    K-blocks (wave w takes kb = w, w+4, ...).  Each wave stages its own
 //    K-blocks through a private LDS slice (coalesced 16-byte loads into
 //    registers one K-block ahead, ds_write, fragment reads), and the four
@@ -1068,7 +1068,7 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   Kern::template run_persistent<kGather>(ntiles, tile_at, smem);
 }
 
-enum class Cfg { kSkinny64x64, kWide, kDecodePanel, kDeep, kPanel192 };
+enum class Cfg { kSkinny64x64, kSkinny48x64, kWide, kDecodePanel, kDeep, kPanel192 };
 
 // Per-workgroup cycle estimate: operand bytes through L1 (64 B/clk/CU) vs
 // FP8 MFMA (8192 FLOP/clk/CU), times the rounds of workgroups over 256 CUs.
@@ -1093,7 +1093,18 @@ Cfg choose(int64_t M, int64_t N, int64_t K) {
   double best = est_cycles(M, N, K, Wide::BN, Wide::BM, cus);
   Cfg c = Cfg::kWide;
   const double s64 = est_cycles(M, N, K, 64, 64, cus) * 1.05;  // partial-tile reduction overhead
-  if (s64 < best) c = Cfg::kSkinny64x64;
+  if (s64 < best) {
+    // Skinny tiles 64 or 48 weight rows wide: whichever fills its rounds of
+    // 256 workgroups more evenly (tiles / (rounds * 256)); ties keep 64.
+    // At M = 256 the 48-row tile gives qkv (N = 6144) 512 tiles, two per CU,
+    // where the 64-row one gives 384 (19.7 vs 21.7 us); o and down (N =
+    // 4096) stay at 256 tiles of 64 rows.
+    auto fill = [&](int bn) {
+      const double t = (double)((N + bn - 1) / bn) * (double)((M + 63) / 64);
+      return t / (std::ceil(t / cus) * cus);
+    };
+    c = fill(48) > fill(64) ? Cfg::kSkinny48x64 : Cfg::kSkinny64x64;
+  }
   return c;
 }
 
@@ -1109,7 +1120,7 @@ hipError_t launch_dense_cfg(const uint8_t* a, const float* sa, const uint8_t* w,
 }
 
 // Tile override for tests and diagnostics: FP8BQ_GEMM_TILE = skinny64 |
-// wide | decode_panel | deep | panel192 forces that kernel for every dense GEMM
+// skinny48 | wide | decode_panel | deep | panel192 forces that kernel for every dense GEMM
 // (wide | decode_panel | deep (one tile per workgroup) | deep_persistent for
 // the grouped GEMM); unset (the default) lets the cost model choose.  Read
 // on every call.
@@ -1117,6 +1128,7 @@ Cfg tile_for(int64_t M, int64_t N, int64_t K) {
   const char* e = std::getenv("FP8BQ_GEMM_TILE");
   if (e != nullptr && *e != '\0') {
     if (std::strcmp(e, "skinny64") == 0) return Cfg::kSkinny64x64;
+    if (std::strcmp(e, "skinny48") == 0) return Cfg::kSkinny48x64;
     if (std::strcmp(e, "wide") == 0) return Cfg::kWide;
     if (std::strcmp(e, "decode_panel") == 0) return Cfg::kDecodePanel;
     if (std::strcmp(e, "deep") == 0) return Cfg::kDeep;
@@ -1186,6 +1198,8 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
   switch (tile_for(M, N, K)) {
     case Cfg::kSkinny64x64:
       return launch_dense_cfg<Skinny<64, 64, 4>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
+    case Cfg::kSkinny48x64:
+      return launch_dense_cfg<Skinny<48, 64, 4>, 48, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kDecodePanel:
       return launch_dense_cfg<DecodePanel, DecodePanel::BN, DecodePanel::BM>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kPanel192:

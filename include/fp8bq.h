@@ -137,8 +137,8 @@ fp8bq_status quantize_act_per_token_group(const uint16_t* x_bf16, uint8_t* x_fp8
  *   unspecified (results agree with the exact value to FP32 accumulation
  *   error before the BF16 rounding).
  *   The tile kernel is chosen per shape.  For tests and diagnostics the
- *   environment variable FP8BQ_GEMM_TILE (skinny64, wide, decode_panel,
- *   deep, panel192), read on every call, forces one of them.
+ *   environment variable FP8BQ_GEMM_TILE (skinny64, skinny48, wide,
+ *   decode_panel, deep, panel192), read on every call, forces one of them.
  */
 fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
                                    const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
