@@ -101,6 +101,15 @@ def parse():
     return p.parse_args()
 
 
+def device_info():
+    """GPU name and architecture, CU count and the HIP / torch versions of the run."""
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__}
+
+
 def calibrate_copy():
     """A plain device-to-device copy of known size: 1 GiB read + 1 GiB written per launch."""
     import torch
@@ -266,6 +275,7 @@ def main():
         "phase_ms": {p: round(v, 4) for p, v in phase_ms.items()},
         "requant_GBps": round(requant_gbps, 1),
         "requant_frac_hbm": round(requant_gbps / HBM_PEAK_GBPS, 4),
+        "device": device_info(),
     }
 
     if not args.no_detail:
