@@ -366,7 +366,7 @@ def detail(fb, dev):
     # -- prefill GEMMs, M = 8192, activations with 1% outlier channels x30
     m = 8192
     pre = {}
-    tot_f = tot_ms = 0.0
+    tot_f = tot_ms = tot_fr_ms = 0.0
     for i, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
         w = device_bf16_normal((n, k), 0.02, seed=300 + i)
         x = device_bf16_normal((m, k), 1.0, seed=400 + i)
@@ -377,6 +377,10 @@ def detail(fb, dev):
         xq, xs = fb.quantize_act_per_token_group(x)
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ms, ms_min = _time_graph_ms(lambda: fb.gemm_w8a8_blockscaled(xq, xs, wq, ws, y), calls=4)
+        # the same GEMM on fragment-order activation codes (same result bits)
+        xf, _ = fb.quantize_act_per_token_group_frag(x)
+        fr_ms, _ = _time_graph_ms(lambda: fb.gemm_w8a8_blockscaled_afrag(xf, xs, wq, ws, y), calls=4)
+        del xf
         sets = [(x, xq, xs)] + [(x.clone(), torch.empty_like(xq), torch.empty_like(xs))
                                 for _ in range(rotations(m * k * 3) - 1)]
         aq_ms, _ = _time_graph_ms([lambda t=t: fb.quantize_act_per_token_group(*t) for t in sets])
@@ -384,12 +388,17 @@ def detail(fb, dev):
         f = 2 * m * n * k
         tot_f += f
         tot_ms += ms
+        tot_fr_ms += fr_ms
         pre[name] = {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(f / ms / 1e9, 1),
                      "frac_fp8_peak": round(f / ms / 1e9 / FP8_PEAK_TFLOPS, 4),
+                     "afrag_gemm_us": round(fr_ms * 1e3, 1), "afrag_TFLOPs": round(f / fr_ms / 1e9, 1),
+                     "afrag_frac_fp8_peak": round(f / fr_ms / 1e9 / FP8_PEAK_TFLOPS, 4),
                      "act_quant_us": round(aq_ms * 1e3, 1),
                      "act_quant_GBps": round((m * k * 3 + m * (k // 128) * 4) / aq_ms / 1e6, 1)}
         del w, x, wq, ws, xq, xs, y
-    pre["all4"] = {"TFLOPs": round(tot_f / tot_ms / 1e9, 1), "frac_fp8_peak": round(tot_f / tot_ms / 1e9 / FP8_PEAK_TFLOPS, 4)}
+    pre["all4"] = {"TFLOPs": round(tot_f / tot_ms / 1e9, 1), "frac_fp8_peak": round(tot_f / tot_ms / 1e9 / FP8_PEAK_TFLOPS, 4),
+                   "afrag_TFLOPs": round(tot_f / tot_fr_ms / 1e9, 1),
+                   "afrag_frac_fp8_peak": round(tot_f / tot_fr_ms / 1e9 / FP8_PEAK_TFLOPS, 4)}
     res["prefill_gemm_M8192"] = pre
     torch.cuda.empty_cache()
 

@@ -27,7 +27,9 @@ __all__ = [
     "quantize_weight_blockwise",
     "quantize_weights_blockwise_multi",
     "quantize_act_per_token_group",
+    "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
+    "gemm_w8a8_blockscaled_afrag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
     "encode_e4m3",
@@ -53,7 +55,9 @@ EXPORTS = (
     "quantize_weight_blockwise",
     "quantize_weights_blockwise_multi",
     "quantize_act_per_token_group",
+    "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
+    "gemm_w8a8_blockscaled_afrag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
     "fp8bq_encode_e4m3",
@@ -93,6 +97,8 @@ def _load():
     lib.quantize_act_per_token_group.argtypes = [p, p, p, i64, i64, p]
     lib.quantize_weights_blockwise_multi.argtypes = [ctypes.POINTER(_WeightDesc), i64, p]
     lib.gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, p]
+    lib.quantize_act_per_token_group_frag.argtypes = [p, p, p, i64, i64, p]
+    lib.gemm_w8a8_blockscaled_afrag.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled_gather.argtypes = [p, p, i64, p, i64, p, p, p, p, i64, i64, i64, i64, p]
     lib.fp8bq_encode_e4m3.argtypes = [p, p, i64, i32, p]
@@ -225,6 +231,47 @@ def quantize_act_per_token_group(x, out=None, scale=None):
         _check("quantize_act_per_token_group",
                _lib.quantize_act_per_token_group(_ptr(x), _ptr(out), _ptr(scale), m, k, _stream(x)))
     return out, scale
+
+
+def quantize_act_per_token_group_frag(x, out=None, scale=None):
+    """BF16 activations [M, K] (M % 16 == 0, K % 128 == 0) -> (E4M3 codes uint8 [M, K] in the MFMA
+    fragment order of gemm_w8a8_blockscaled_afrag; float32 scales [M, K/128])."""
+    if x.dim() != 2:
+        raise ValueError("activations must be [M, K]")
+    m, k = x.shape
+    if m % 16 or k % BLOCK:
+        raise ValueError("fragment order needs M % 16 == 0 and K % 128 == 0")
+    _require(x, "x", _BF16, x.shape)
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((m, k // BLOCK), dtype=torch.float32, device=x.device)
+    _require(out, "out", _U8, (m, k), x.device)
+    _require(scale, "scale", torch.float32, (m, k // BLOCK), x.device)
+    with torch.cuda.device(x.device):
+        _check("quantize_act_per_token_group_frag",
+               _lib.quantize_act_per_token_group_frag(_ptr(x), _ptr(out), _ptr(scale), m, k, _stream(x)))
+    return out, scale
+
+
+def gemm_w8a8_blockscaled_afrag(a_frag, a_scale, w, w_scale, out=None):
+    """gemm_w8a8_blockscaled with the activation codes in fragment order (quantize_act_per_token_group_frag);
+    M % 16 == 0 and K % 256 == 0."""
+    m, k = a_frag.shape
+    n = w.shape[0]
+    _require(a_frag, "a_frag", _U8, (m, k))
+    dev = a_frag.device
+    _require(a_scale, "a_scale", torch.float32, (m, k // BLOCK), dev)
+    _require(w, "w", _U8, (n, k), dev)
+    _require(w_scale, "w_scale", torch.float32, (_cdiv(n, BLOCK), k // BLOCK), dev)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", _BF16, (m, n), dev)
+    with torch.cuda.device(dev):
+        _check("gemm_w8a8_blockscaled_afrag",
+               _lib.gemm_w8a8_blockscaled_afrag(_ptr(a_frag), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)),
+                                                m, n, k, _stream(a_frag)))
+    return out
 
 
 def gemm_w8a8_blockscaled(a, a_scale, w, w_scale, out=None):

@@ -194,6 +194,49 @@ fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, c
   }
 }
 
+fp8bq_status quantize_act_per_token_group_frag(const uint16_t* x_bf16, uint8_t* x_fp8_frag, float* x_scale,
+                                               int64_t M, int64_t K, void* stream) {
+  try {
+    if (M < 0 || K < 0 || (M % 16) != 0 || (K % 128) != 0) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t total, bytes;
+    if (!mul_ok(M, K, &total) || !mul_ok(total, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
+    if (total == 0) return FP8BQ_OK;
+    if (!x_bf16 || !x_fp8_frag || !x_scale) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(x_bf16) || !aligned16(x_fp8_frag) || !aligned16(x_scale)) return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(
+        fp8bq::launch_quant_act_frag(x_bf16, x_fp8_frag, x_scale, M, K, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8,
+                                         const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                         void* stream) {
+  try {
+    if (M < 0 || N < 0 || K < 0 || (M % 16) != 0 || (K % 256) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t mk, nk, mn, bytes;
+    if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, &mn) || !mul_ok(mn, 2, &bytes))
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (mn == 0) return FP8BQ_OK;
+    if (!y_bf16) return FP8BQ_ERR_NULL_PTR;
+    if (K > 0 && (!a_fp8_frag || !a_scale || !w_fp8 || !w_scale)) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(y_bf16) || (K > 0 && (!aligned16(a_fp8_frag) || !aligned16(a_scale) || !aligned16(w_fp8) ||
+                                         !aligned16(w_scale))))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_gemm_afrag(a_fp8_frag, a_scale, w_fp8, w_scale, y_bf16, M, N, K,
+                                             static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
 fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
                                            const float* w_scale, const int32_t* group_offsets, uint16_t* y_bf16,
                                            int64_t M_total, int64_t N, int64_t K, int64_t G, void* stream) {

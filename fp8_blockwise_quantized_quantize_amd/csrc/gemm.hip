@@ -844,6 +844,267 @@ struct Panel {
   }
 };
 
+// ---------------------------------------------------------------------------
+// panel_afrag<BN, BM, ...>: the panel tile for activations stored in the MFMA
+// fragment order (launch_quant_act_frag): each wave loads its activation
+// fragments straight into VGPRs, one K-block ahead (two contiguous 16-byte
+// loads per lane per fragment), and only the weight rows and the scales go
+// through LDS.  That leaves room for four one-K-block weight stages in two
+// alternating pairs: the waves meet at one barrier per two K-blocks (K % 256
+// == 0).  Same per-element arithmetic and order as panel<>: bit-identical
+// outputs.  Qwen3-8B prefill (M = 8192): qkv 204-211 vs 239-249 us, o
+// 138-148 vs 153-156, down 347 vs 371-379, gate_up 882-885 vs 888-892.
+// ---------------------------------------------------------------------------
+template <int BN_, int BM_, int WGN, int WGM, int S>
+struct PanelAfrag {
+  static constexpr int BN = BN_, BM = BM_;
+  static_assert(WGN * WGM == 8, "eight waves");
+  static constexpr int WNR = BN / WGN, WMR = BM / WGM;  // rows of a wave's tile
+  static constexpr int TN = WNR / 16, TM = WMR / 16;
+  static_assert(WNR % 16 == 0 && WMR % 16 == 0 && WNR <= 128, "wave tile");
+  static_assert(BN % 64 == 0 && BM % 64 == 0, "each load instruction covers 8 rows of one operand, 8 waves");
+  static constexpr int kRows = BN;                      // weight rows staged per K-block (activations direct)
+  static constexpr int kLoads = kRows / 64;             // load instructions per wave per K-block
+  static constexpr int kStage = kRows * kBlock;
+  // Each stage also holds that K-block's scales, staged like the operands:
+  // 64 dwords per wave (activation scales of the tile's rows 0..BM-1, then
+  // the tile's weight scale blocks), after the S operand stages.
+  static constexpr int kScaleBytes = 8 * 64 * 4;
+  static_assert(BM / 64 < 8, "a wave left over for the weight scales");
+  static constexpr int kLdsBytes = S * (kStage + kScaleBytes);
+  static_assert(S >= 2 && S <= 4, "stages");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+  static constexpr int kThreadsPerWg = 512;
+  static constexpr int kWavesPerSimd = 2;
+  // a wave's weight rows lie in one 128-row scale block when tiles start at
+  // multiples of 128 and the wave's share divides 128
+  static constexpr bool kOneScaleBlock = (BN % kBlock == 0) && (kBlock % WNR == 0);
+
+  __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) { run_impl<false>(t, lds); }
+
+  template <bool kGather>
+  __device__ static __forceinline__ void run_impl(const Tile& t, uint8_t* lds) {
+    static_assert(!kGather, "fragment-order activations are not gathered");
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wn = wave % WGN, wm = wave / WGN;
+    const int64_t K = t.K;
+    const int KB = (int)(K / kBlock);
+    const int64_t n_hi = (t.n0 + BN < t.N) ? t.n0 + BN : t.N;
+    // weight scale blocks of this wave's rows: nb0, and nb0 + 1 for the
+    // fragments in hi_mask (only when a wave's rows can straddle a block);
+    // wsl0 / wsl1 are their positions among the tile's blocks nbt, nbt + 1, ..
+    const int64_t NBm1 = (t.N - 1) / kBlock;
+    const int64_t nbt = t.n0 / kBlock;
+    const int64_t wrow0 = t.n0 + wn * WNR;
+    const int64_t nb0 = ((wrow0 < t.N) ? wrow0 : t.N - 1) / kBlock;
+    const int64_t nb1 = nb0 + 1 < NBm1 ? nb0 + 1 : NBm1;
+    const int wsl0 = (int)(nb0 - nbt), wsl1 = (int)(nb1 - nbt);
+    uint32_t hi_mask = 0;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      if ((wrow0 + i * 16) / kBlock > nb0) hi_mask |= 1u << i;
+    const auto wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
+    const auto ar = kGather ? make_rsrc(t.a, t.a_nrows * K) : make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
+    const int64_t am_lo = t.m_lo + wm * WMR;  // this wave's first activation row
+    // Source row of output row m: itself, or the gathered row (-1: none).
+    auto src_row = [&](int64_t m) -> int64_t {
+      if (m >= t.m_hi) return -1;
+      if (!kGather) return m - t.m_lo;  // relative to the tile's buffer
+      const int32_t p = t.a_rows[m];
+      const int64_t r = p >= 0 ? p / t.a_div : -1;
+      return r < t.a_nrows ? r : -1;
+    };
+    // a ragged last tile (e.g. an expert's rows past a multiple of BM) can
+    // leave whole waves without a valid activation row: they skip the MFMAs
+    const bool idle = am_lo >= t.m_hi;
+    // Scale staging, one buffer_load_dword ... lds per wave and K-block into
+    // the wave's 64 dwords of the stage's scale area: waves w < BM/64 load
+    // the activation scales of tile rows 64 w + lane, the others the
+    // weight scale blocks nbt + lane.  As for the operands, rows and blocks
+    // past the end sit outside the buffer range and read zeros.
+    const bool act_scales = wave < BM / 64;
+    const auto scr = act_scales ? (kGather ? make_rsrc(t.sa, t.a_nrows * KB * 4)
+                                           : make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4))
+                                : make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
+    int scvoff = lane * KB * 4;
+    if (act_scales) {
+      const int64_t r = src_row(t.m_lo + 64 * wave + lane);
+      scvoff = kGather ? (r >= 0 ? (int)(r * KB * 4) : kOob) : (64 * wave + lane) * KB * 4;
+    }
+
+    // DMA staging: load q of wave w fills stage rows R0..R0+7 with
+    // R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at physical chunk
+    // l%8, so it fetches logical chunk (l%8) ^ (l/8) (the XOR swizzle).
+    // The row offset is part of the per-lane offset, which the buffer range
+    // check covers: rows past the tile's last row read zeros, never memory.
+    const int chunk_off = ((lane & 7) ^ (lane >> 3)) << 4;
+    const int dvoff = (lane >> 3) * (int)K + chunk_off;
+    // gathered activations: the offset of this lane's row in each A load
+    int aoff[kGather ? BM / 64 : 1];
+    if constexpr (kGather) {
+#pragma unroll
+      for (int qa = 0; qa < BM / 64; ++qa) {
+        const int64_t r = src_row(t.m_lo + 8 * (8 * (BN / 64 + qa) + wave) - BN + (lane >> 3));
+        aoff[qa] = r >= 0 ? (int)(r * K) + chunk_off : kOob;
+      }
+    }
+    const FragLds fl(lane);
+
+    v4f acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    auto dma_scales = [&](int kb, int stage) {
+      auto* dst = (__attribute__((address_space(3))) void*)(lds + S * kStage + stage * kScaleBytes + wave * 256);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, dst, 4, scvoff, kb * 4, 0, 0);
+    };
+    auto dma_q = [&](int q, int kb, uint8_t* buf) {
+      const int koff = kb * kBlock;
+      const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
+      auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
+      if (q < BN / 64)  // stage rows 0..BN-1: weight rows n0 + r0 ..
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, koff, 0, 0);
+      else if (kGather)  // stage rows BN..: the gathered activation rows
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, aoff[kGather ? q - BN / 64 : 0], koff, 0, 0);
+      else              // stage rows BN..: activation rows m_lo + r0 - BN ..
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff + (r0 - BN) * (int)K, koff, 0, 0);
+    };
+    // all loads of one K-block: the operand rows, then the scales
+    auto dma_kblock = [&](int kb, int stage) {
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) dma_q(q, kb, lds + stage * kStage);
+      dma_scales(kb, stage);
+    };
+    constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
+    auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * WNR + i * 16); };
+    // The first fragments of a phase, read right after its barrier; the
+    // first MFMA's two operands go first so that it waits for them only.
+    // activation fragments in MFMA order: 2 KB per (16-row group, K-block),
+    // lane l's two 16-byte halves at l * 16 and 1024 + l * 16
+    u32x4 an_lo[TM], an_hi[TM];
+    auto afrag_off = [&](int j, int h) { return (wm * WMR + 16 * j) * (int)K + h * 1024 + lane * 16; };
+    auto load_a = [&](int j, int h, int kb) {
+      const u32x4 v = bload16(ar, afrag_off(j, h), kb * 2048);
+      if (h == 0) an_lo[j] = v; else an_hi[j] = v;
+    };
+    auto first_frags = [&](v8i (&fa)[TM], v8i (&fw)[kAhead + 1], const uint8_t* buf) {
+      fw[0] = load_w(buf, 0);
+#pragma unroll
+      for (int j = 0; j < TM; ++j) fa[j] = to_v8i(an_lo[j], an_hi[j]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int p = 1; p < kAhead && p < TN; ++p) fw[p] = load_w(buf, p);
+    };
+    // One phase: the product of the K-block in stage `cur`, with the loads
+    // of K-block `kb` into stage `fill` issued after every second MFMA
+    // (after every MFMA when there are few), so that the L2 and LDS-write
+    // traffic does not arrive as one burst right after the barrier.  The
+    // scales come from the stage's scale area; their products are formed
+    // while the first MFMAs run.
+    constexpr int kT = TN * TM;
+    constexpr int kPhaseLoads = kLoads + 1 + 2 * TM;
+    constexpr int kEvery = (kT >= 2 * kPhaseLoads) ? 2 : 1;
+    static_assert(kT >= kPhaseLoads, "enough MFMAs to carry the loads");
+    auto phase = [&](int cur, int kb, int fill, int kb_a) {
+      const uint8_t* buf = lds + cur * kStage;
+      v8i fa[TM], fw[kAhead + 1];
+      first_frags(fa, fw, buf);
+      const float* scl = reinterpret_cast<const float*>(lds + S * kStage + cur * kScaleBytes);
+      const float sw0 = scl[BM + wsl0];
+      const float sw1 = kOneScaleBlock ? sw0 : scl[BM + wsl1];
+      float c0[TM], c1[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const float sa = scl[wm * WMR + j * 16 + r16];
+        c0[j] = sa * sw0;
+        c1[j] = kOneScaleBlock ? c0[j] : sa * sw1;
+      }
+      tile_product<TN, TM, 2, kAhead>(
+          acc, fa, fw, [&](int i) { return load_w(buf, i); },
+          [&](int i, int j) { return (kOneScaleBlock || !((hi_mask >> i) & 1u)) ? c0[j] : c1[j]; },
+          [&](int tt) {
+            if (tt % kEvery != 0 || tt / kEvery >= kPhaseLoads) return false;
+            // activation fragments first: the end-of-phase wait leaves the
+            // newest (S - 2) phases' weight and scale loads in flight, and
+            // loads complete in issue order
+            const int q = tt / kEvery;
+            if (q < 2 * TM)
+              load_a(q / 2, q % 2, kb_a);
+            else if (q < 2 * TM + kLoads)
+              dma_q(q - 2 * TM, kb, lds + fill * kStage);
+            else
+              dma_scales(kb, fill);
+            return true;
+          });
+    };
+    // The compiler does not track LDS writes by buffer_load ... lds: wait
+    // for them explicitly before the barrier that publishes the stage.  With
+    // three stages the loads of the next K-block may stay in flight.
+    auto wait_stage = [&]() {
+      // weight + scale loads of the newest S - 2 phases may stay in flight
+      if constexpr (S == 2)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * (kLoads + 1)) : "memory");
+    };
+    // The workgroup barrier of a phase.  Not __syncthreads(): its fence
+    // would wait for every load in flight (vmcnt(0)), including the later
+    // K-blocks' prefetches that the ring keeps in flight on purpose.  The
+    // LDS writes this barrier publishes were waited for by wait_stage();
+    // the LDS reads of the previous phase are waited for here, so no wave
+    // refills a stage that another is still reading.
+    auto barrier = [&]() {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      order_fence();
+    };
+    auto wait_all = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+    const int kb_last = KB - 1;
+    auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };  // clamped prefetch
+    static_assert(S == 4, "two pairs of K-block sub-stages");
+    if (KB > 0) {
+      dma_kblock(0, 0);
+#pragma unroll
+      for (int j = 0; j < TM; ++j) { load_a(j, 0, 0); load_a(j, 1, 0); }
+      dma_kblock(nxt(1), 1);
+    }
+    // Loads past the last K-block re-load it into a stage nobody reads
+    // again, keeping the loop body free of branches.
+    // K-blocks in pairs, one barrier per pair (KB even: the host uses this
+    // tile only for K % 256 == 0); sub-stages 0,1 and 2,3 alternate.
+    for (int kp = 0; kp < KB; kp += 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      barrier();
+      const int c0 = ((kp >> 1) & 1) ? 2 : 0, f0 = 2 - c0;
+      if (idle) {
+        dma_kblock(nxt(kp + 2), f0);
+        dma_kblock(nxt(kp + 3), f0 + 1);
+      } else {
+        phase(c0, nxt(kp + 2), f0, nxt(kp + 1));
+        order_fence();
+        phase(c0 + 1, nxt(kp + 3), f0 + 1, nxt(kp + 2));
+      }
+      order_fence();
+    }
+    wait_all();  // no LDS write may be in flight when the workgroup ends
+
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int64_t m = t.m_lo + wm * WMR + j * 16 + r16;
+      if (m >= t.m_hi) continue;
+#pragma unroll
+      for (int i = 0; i < TN; ++i) store4(t.y, t.N, m, t.n0 + wn * WNR + i * 16 + g * 4, acc[i][j]);
+    }
+  }
+
+};
+
+using WideAfrag = PanelAfrag<256, 256, 2, 4, 4>;
+
 using Wide = Panel<256, 256, 2, 4, 2>;
 using DecodePanel = Panel<128, 256, 2, 4, 3>;
 // Three stages of 256 weight rows: two K-blocks of weights (64 KB) in flight
@@ -1209,6 +1470,13 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
     default:
       return launch_dense_cfg<Wide, Wide::BN, Wide::BM>(a, sa, w, sw, y, M, N, K, stream);
   }
+}
+
+hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (M % 16 != 0 || K % (2 * kBlock) != 0) return hipErrorInvalidValue;
+  return launch_dense_cfg<WideAfrag, WideAfrag::BN, WideAfrag::BM>(a, sa, w, sw, y, M, N, K, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,

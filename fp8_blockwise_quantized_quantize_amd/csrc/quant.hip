@@ -168,6 +168,21 @@ __device__ __forceinline__ ActGroup act_group_load(const uint16_t* __restrict__ 
 
 // Group amax over the quarter wave (every lane of the wave takes part), then
 // the scale and the codes.
+// Byte offset of lane li's 8 codes (row m, group g) in the MFMA fragment
+// order of the activation operand: per 16-row group R and K-block g a 2 KB
+// block in which lane l = 16 c + r (r = row within the group) holds bytes
+// [16 c, 16 c + 16) of its row's K-block at l * 16 and bytes [64 + 16 c,
+// 80 + 16 c) at 1024 + l * 16 -- the two halves of its 16x16x128 MFMA
+// operand, so a wave reads each half with one contiguous 1 KB load.
+__device__ __forceinline__ int64_t act_frag_offset(int64_t m, int g, int li, int G) {
+  const int64_t R = m >> 4;
+  const int r16 = (int)(m & 15), h = li >> 3, c = (li & 7) >> 1;
+  return ((R * G + g) * 2 + h) * 1024 + (c * 16 + r16) * 16 + (li & 1) * 8;
+}
+
+// kFrag: codes in the fragment order above (M % 16 == 0, K % 128 == 0, so
+// every group is whole); otherwise row-major [M][K].
+template <bool kFrag>
 __device__ __forceinline__ void act_group_store(const ActGroup& a, uint8_t* __restrict__ q,
                                                 float* __restrict__ scale, int64_t K, int G, int li) {
   uint32_t am = amax_fold(amax8(0u, a.v));
@@ -178,7 +193,7 @@ __device__ __forceinline__ void act_group_store(const ActGroup& a, uint8_t* __re
   }
   const float s = scale_from_amax_bits(am);
   if (a.valid && li == 0) scale[a.m * G + a.g] = s;
-  uint8_t* dst = q + a.m * K + a.col;
+  uint8_t* dst = q + (kFrag ? act_frag_offset(a.m, a.g, li, G) : a.m * K + a.col);
   if (a.vec) {
     __builtin_nontemporal_store(encode8(a.v, s), reinterpret_cast<u32x2*>(dst));
   } else if (a.valid) {
@@ -193,7 +208,7 @@ __device__ __forceinline__ void act_group_store(const ActGroup& a, uint8_t* __re
 // Pass p of quarter wave w (w = threadIdx / 16) takes group
 // blockIdx * 16 * kPasses + 16 p + w, so each pass is one coalesced sweep
 // over 16 consecutive groups.
-template <int kPasses>
+template <int kPasses, bool kFrag>
 __global__ __launch_bounds__(kQaThreads) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                                uint8_t* __restrict__ q,
                                                                float* __restrict__ scale, int64_t M, int64_t K,
@@ -204,7 +219,7 @@ __global__ __launch_bounds__(kQaThreads) void quant_act_kernel(const uint16_t* _
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) grp[p] = act_group_load(x, M, K, G, g0 + 16 * p, li);
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) act_group_store(grp[p], q, scale, K, G, li);
+  for (int p = 0; p < kPasses; ++p) act_group_store<kFrag>(grp[p], q, scale, K, G, li);
 }
 
 // ---------------------------------------------------------------------------
@@ -248,7 +263,9 @@ hipError_t launch_quant_weight_multi(const WeightBatch& batch, int64_t blocks, h
   return hipGetLastError();
 }
 
-hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K, hipStream_t stream) {
+template <bool kFrag>
+hipError_t launch_quant_act_any(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K,
+                                hipStream_t stream) {
   const int64_t G = (K + kBlock - 1) / kBlock;
   const int64_t groups = M * G;
   if (groups == 0) return hipSuccess;
@@ -257,12 +274,21 @@ hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t
   const int64_t blocks = (groups + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (large)
-    hipLaunchKernelGGL(quant_act_kernel<kQaPassesLarge>, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q,
-                       scale, M, K, (int)G);
+    hipLaunchKernelGGL((quant_act_kernel<kQaPassesLarge, kFrag>), dim3((unsigned)blocks), dim3(kQaThreads), 0,
+                       stream, x, q, scale, M, K, (int)G);
   else
-    hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q, scale, M, K,
-                       (int)G);
+    hipLaunchKernelGGL((quant_act_kernel<1, kFrag>), dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q,
+                       scale, M, K, (int)G);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K, hipStream_t stream) {
+  return launch_quant_act_any<false>(x, q, scale, M, K, stream);
+}
+
+hipError_t launch_quant_act_frag(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K,
+                                 hipStream_t stream) {
+  return launch_quant_act_any<true>(x, q, scale, M, K, stream);
 }
 
 hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int method, hipStream_t stream) {

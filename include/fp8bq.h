@@ -145,6 +145,43 @@ fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, c
                                    void* stream);
 
 /*
+ * quantize_act_per_token_group_frag -- quantize_act_per_token_group with
+ * the codes written in the MFMA fragment order that
+ * gemm_w8a8_blockscaled_afrag reads ([FP8-RL summary] §3.4.1 "1 × 128 tiles
+ * for activations"; §3.4.2 Phase 3).  Same codes and scales, another byte
+ * order:
+ *   x_bf16      [M][K] BF16, row-major (as for quantize_act_per_token_group)
+ *   x_fp8_frag  M * K bytes: code (m, k) at
+ *               ((m/16 * K/128 + k/128) * 2 + (k%128)/64) * 1024
+ *               + (((k%64)/16) * 16 + m%16) * 16 + k%16
+ *               (per 16 rows and K-block, 2 KB: the two 16-byte halves of
+ *               each lane's 16x16x128 MFMA operand, lane-major)
+ *   x_scale     [M][K/128] float32, token-major (as for the row-major form)
+ *   Requires M % 16 == 0 and K % 128 == 0 (FP8BQ_ERR_BAD_SHAPE otherwise);
+ *   the other conventions are those of quantize_act_per_token_group.
+ */
+fp8bq_status quantize_act_per_token_group_frag(const uint16_t* x_bf16, uint8_t* x_fp8_frag, float* x_scale,
+                                               int64_t M, int64_t K, void* stream);
+
+/*
+ * gemm_w8a8_blockscaled_afrag -- gemm_w8a8_blockscaled on activation codes
+ * in the fragment order of quantize_act_per_token_group_frag
+ * ([FP8-RL summary] §3.4.2 Phase 3).  The activation fragments go straight
+ * to registers and only the weights are staged in LDS, which leaves room for
+ * one workgroup barrier per two K-blocks.  Same result bits as
+ * gemm_w8a8_blockscaled on the row-major codes (same per-element order).
+ *   a_fp8_frag  M * K bytes in fragment order; a_scale [M][K/128]
+ *   w_fp8 [N][K], w_scale [ceil(N/128)][K/128], y_bf16 [M][N] as for
+ *   gemm_w8a8_blockscaled.
+ *   Requires M % 16 == 0 and K % 256 == 0 (K <= 2^22); FP8BQ_ERR_BAD_SHAPE
+ *   otherwise.  Meant for many activation rows (prefill): it always runs the
+ *   256 x 256 tile.
+ */
+fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8,
+                                         const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                         void* stream);
+
+/*
  * grouped_gemm_w8a8_blockscaled -- the MoE expert form: rows
  * [group_offsets[e], group_offsets[e+1]) of A are multiplied with expert
  * e's weights ([FP8-RL summary] §3.4.1 "Quantization Scope", fc1/fc2 of

@@ -64,6 +64,7 @@ from .quant import (
     quant_weight_blockwise,
     quant_weight_block,
     quant_act_per_token_group,
+    act_fragment_order,
 )
 from .gemm import (
     dequant_act,

@@ -134,3 +134,22 @@ def quant_act_per_token_group(x_bits):
         codes[:, cols] = q
         scales[:, j] = s
     return codes, scales
+
+
+def act_fragment_order(codes):
+    """Byte order of activation codes [M][K] (M % 16 == 0, K % 128 == 0) as
+    the 16x16x128 FP8 MFMA reads its activation operand: per 16-row group and
+    128-wide K-block one 2 KB block; in it, lane l = 16 c + r (r = row within
+    the group, c = 0..3) holds bytes 16 c .. 16 c + 15 of its row's K-block
+    at l * 16 and bytes 64 + 16 c .. 79 + 16 c at 1024 + l * 16.  A pure
+    permutation of the row-major codes (what the block-scaled GEMM computes
+    is unchanged; the pages leave the byte layout of the quantized operand
+    open).
+    """
+    q = np.asarray(codes, np.uint8)
+    m, k = q.shape
+    if m % 16 or k % BLOCK:
+        raise ValueError("fragment order needs M % 16 == 0 and K % 128 == 0")
+    # axes: row group, row in group, K-block, half, 16-byte chunk c, byte
+    t = q.reshape(m // 16, 16, k // BLOCK, 2, 4, 16)
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 4, 1, 5)).reshape(m, k)

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
               "token_importance_weights", "moe_sort_by_expert", "moe_gather_quantize_act",
               "silu_mul_quantize_act", "moe_combine", "grouped_gemm_w8a8_blockscaled_gather",
               "kv_scale_calibrate", "kv_cache_write_fp8", "quantize_weight_blockwise_dual", "quantize_act_dual",
-              "quantize_weights_blockwise_multi"]:
+              "quantize_weights_blockwise_multi", "quantize_act_per_token_group_frag",
+              "gemm_w8a8_blockscaled_afrag"]:
         assert n in names, names
 
 
@@ -71,6 +72,13 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call("gemm_w8a8_blockscaled", good, good, good, good, good, 4, 4, (1 << 22) + 128, null) == 2
     assert _call("grouped_gemm_w8a8_blockscaled", good, good, good, good, good, good, 4, 4, (1 << 22) + 128, 2,
                  null) == 2
+    # fragment order: M % 16, K % 128 (quantizer) and K % 256 (GEMM)
+    assert _call("quantize_act_per_token_group_frag", good, good, good, 24, 128, null) == 2
+    assert _call("quantize_act_per_token_group_frag", good, good, good, 32, 200, null) == 2
+    assert _call("gemm_w8a8_blockscaled_afrag", good, good, good, good, good, 24, 4, 256, null) == 2
+    assert _call("gemm_w8a8_blockscaled_afrag", good, good, good, good, good, 32, 4, 384, null) == 2
+    assert _call("gemm_w8a8_blockscaled_afrag", good, good, good, good, good, 32, 4, (1 << 22) + 256, null) == 2
+    assert _call("gemm_w8a8_blockscaled_afrag", good, good, null, good, good, 32, 4, 256, null) == 1
     # size overflow
     assert _call("quantize_weight_blockwise", good, good, good, 1 << 40, 1 << 20, 1 << 20, null) == 2
     # null pointers with non-empty sizes

@@ -1,0 +1,106 @@
+"""GPU parity of the fragment-order activation path: the quantizer writing
+the codes in MFMA fragment order, and the GEMM that reads them.
+
+The quantizer must give the oracle's codes, permuted by the oracle's
+fragment order, and the oracle's scales, bit for bit.  The GEMM must meet
+the GEMM bar against the exact oracle and give the same bits as the
+row-major GEMM's 256 x 256 tile (same per-element arithmetic and order).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import announce, assert_gemm_close, bf16_bits_to_device, device_to_bits
+from synthetic import activations, bf16_normal, device_bf16_normal
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fb():
+    import fp8_blockwise_quantized_quantize_amd as m
+
+    return m
+
+
+@pytest.mark.parametrize("m,k", [(16, 128), (48, 384), (272, 2048), (256, 12288)])
+def test_quantizer_fragment_order(fb, m, k):
+    announce("afrag quant", m, k)
+    x, _ = activations(m, k, (m, k), n_outliers=max(1, k // 100), outlier_mult=30.0)
+    q, s = fb.quantize_act_per_token_group_frag(bf16_bits_to_device(x))
+    oq, os_ = oracle.quant_act_per_token_group(x)
+    assert np.array_equal(q.cpu().numpy(), oracle.act_fragment_order(oq))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
+def test_quantizer_fragment_order_matches_row_major_prefill(fb):
+    """At the prefill size: the fragment codes are the row-major GPU codes
+    permuted (the row-major quantizer is itself checked against the oracle)."""
+    m, k = 8192, 4096
+    announce("afrag quant prefill", m, k)
+    x = device_bf16_normal((m, k), 1.0, seed=9)
+    q, s = fb.quantize_act_per_token_group(x)
+    qf, sf = fb.quantize_act_per_token_group_frag(x)
+    perm = q.view(m // 16, 16, k // 128, 2, 4, 16).permute(0, 2, 3, 4, 1, 5).contiguous().view(m, k)
+    assert torch.equal(qf, perm) and torch.equal(sf, s)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 130, 256), (48, 384, 768), (272, 520, 512), (256, 256, 2048)])
+def test_gemm_afrag_against_oracle_and_row_major(fb, monkeypatch, m, n, k):
+    announce("afrag gemm", m, n, k)
+    x, _ = activations(m, k, (m, n, k, 0))
+    w = bf16_normal((n, k), 0.02, (m, n, k, 1))
+    qa, sa = oracle.quant_act_per_token_group(x)
+    qw, sw = oracle.quant_weight_blockwise(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    y = fb.gemm_w8a8_blockscaled_afrag(dev(oracle.act_fragment_order(qa)), dev(sa), dev(qw), dev(sw))
+    got = device_to_bits(y)
+    assert_gemm_close(got, oracle.gemm_ref(qa, sa, qw, sw))
+    monkeypatch.setenv("FP8BQ_GEMM_TILE", "wide")
+    ref = device_to_bits(fb.gemm_w8a8_blockscaled(dev(qa), dev(sa), dev(qw), dev(sw)))
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("n,k", [(6144, 4096), (4096, 12288)])
+def test_gemm_afrag_prefill_bit_identical(fb, monkeypatch, n, k):
+    """Qwen3-8B prefill shapes (M = 8192): same bits as the row-major tile."""
+    m = 8192
+    announce("afrag gemm prefill", m, n, k)
+    x = device_bf16_normal((m, k), 1.0, seed=11)
+    wq, ws = fb.quantize_weight_blockwise(device_bf16_normal((n, k), 0.02, seed=12))
+    q, s = fb.quantize_act_per_token_group(x)
+    qf, _ = fb.quantize_act_per_token_group_frag(x)
+    monkeypatch.setenv("FP8BQ_GEMM_TILE", "wide")
+    y0 = fb.gemm_w8a8_blockscaled(q, s, wq, ws)
+    y1 = fb.gemm_w8a8_blockscaled_afrag(qf, s, wq, ws)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
+def test_gemm_afrag_largest_k(fb, monkeypatch):
+    """K = 2^22: 256 rows of fragment-order codes span 2^30 bytes."""
+    m, n, k = 256, 3, 1 << 22
+    announce("afrag gemm largest K", m, n, k)
+    g = torch.Generator(device="cuda").manual_seed(2202)
+    qa = torch.randint(0, 256, (m, k), generator=g, dtype=torch.uint8, device="cuda")
+    qa[(qa & 0x7F) == 0x7F] = 0
+    qw = torch.randint(0, 256, (n, k), generator=g, dtype=torch.uint8, device="cuda")
+    qw[(qw & 0x7F) == 0x7F] = 0
+    sa = torch.rand((m, k // 128), generator=g, device="cuda") + 0.5
+    sw = torch.rand((1, k // 128), generator=g, device="cuda") + 0.5
+    qf = qa.view(m // 16, 16, k // 128, 2, 4, 16).permute(0, 2, 3, 4, 1, 5).contiguous().view(m, k)
+    monkeypatch.setenv("FP8BQ_GEMM_TILE", "wide")
+    y0 = fb.gemm_w8a8_blockscaled(qa, sa, qw, sw)
+    del qa
+    y1 = fb.gemm_w8a8_blockscaled_afrag(qf, sa, qw, sw)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
+def test_afrag_shape_errors(fb):
+    a = torch.zeros((24, 256), dtype=torch.uint8, device="cuda")
+    s = torch.ones((24, 2), device="cuda")
+    with pytest.raises(fb.FP8BQError, match="shape"):
+        fb.gemm_w8a8_blockscaled_afrag(a, s, a, torch.ones((1, 2), device="cuda"))
+    with pytest.raises(ValueError):
+        fb.quantize_act_per_token_group_frag(torch.zeros((24, 128), dtype=torch.bfloat16, device="cuda"))

@@ -21,6 +21,7 @@ import pytest
 
 from oracle import (
     BLOCK,
+    act_fragment_order,
     decode_e4m3,
     e4m3_finite_magnitudes,
     quant_act_per_token_group,
@@ -260,3 +261,23 @@ def test_planted_mistake_is_caught():
             r = np.float32(1) / s[i, j]
             wrong[blk] = encode_e4m3(x[blk] * r)
     assert not np.array_equal(wrong, q)
+
+
+def test_act_fragment_order_element_mapping():
+    """Every code lands where the MFMA operand layout puts it: checked one
+    element at a time against the offset formula written out in scalars, and
+    the permutation is a bijection (every byte moved exactly once)."""
+    rng = np.random.default_rng(123)
+    m, k = 32, 384
+    codes = rng.integers(0, 256, (m, k)).astype(np.uint8)
+    frag = act_fragment_order(codes).reshape(-1)
+    kb = k // 128
+    seen = np.zeros(m * k, bool)
+    for r in range(m):
+        for c in range(k):
+            off = ((r // 16 * kb + c // 128) * 2 + (c % 128) // 64) * 1024 + (((c % 64) // 16) * 16 + r % 16) * 16 + c % 16
+            assert frag[off] == codes[r, c]
+            seen[off] = True
+    assert seen.all()
+    with pytest.raises(ValueError):
+        act_fragment_order(codes[:24])
