@@ -384,6 +384,7 @@ def detail(fb, dev):
         sets = [(x, xq, xs)] + [(x.clone(), torch.empty_like(xq), torch.empty_like(xs))
                                 for _ in range(rotations(m * k * 3) - 1)]
         aq_ms, _ = _time_graph_ms([lambda t=t: fb.quantize_act_per_token_group(*t) for t in sets])
+        aqf_ms, _ = _time_graph_ms([lambda t=t: fb.quantize_act_per_token_group_frag(*t) for t in sets])
         del sets
         f = 2 * m * n * k
         tot_f += f
@@ -393,7 +394,7 @@ def detail(fb, dev):
                      "frac_fp8_peak": round(f / ms / 1e9 / FP8_PEAK_TFLOPS, 4),
                      "afrag_gemm_us": round(fr_ms * 1e3, 1), "afrag_TFLOPs": round(f / fr_ms / 1e9, 1),
                      "afrag_frac_fp8_peak": round(f / fr_ms / 1e9 / FP8_PEAK_TFLOPS, 4),
-                     "act_quant_us": round(aq_ms * 1e3, 1),
+                     "act_quant_us": round(aq_ms * 1e3, 1), "afrag_act_quant_us": round(aqf_ms * 1e3, 1),
                      "act_quant_GBps": round((m * k * 3 + m * (k // 128) * 4) / aq_ms / 1e6, 1)}
         del w, x, wq, ws, xq, xs, y
     pre["all4"] = {"TFLOPs": round(tot_f / tot_ms / 1e9, 1), "frac_fp8_peak": round(tot_f / tot_ms / 1e9 / FP8_PEAK_TFLOPS, 4),

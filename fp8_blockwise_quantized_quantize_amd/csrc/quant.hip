@@ -168,21 +168,6 @@ __device__ __forceinline__ ActGroup act_group_load(const uint16_t* __restrict__ 
 
 // Group amax over the quarter wave (every lane of the wave takes part), then
 // the scale and the codes.
-// Byte offset of lane li's 8 codes (row m, group g) in the MFMA fragment
-// order of the activation operand: per 16-row group R and K-block g a 2 KB
-// block in which lane l = 16 c + r (r = row within the group) holds bytes
-// [16 c, 16 c + 16) of its row's K-block at l * 16 and bytes [64 + 16 c,
-// 80 + 16 c) at 1024 + l * 16 -- the two halves of its 16x16x128 MFMA
-// operand, so a wave reads each half with one contiguous 1 KB load.
-__device__ __forceinline__ int64_t act_frag_offset(int64_t m, int g, int li, int G) {
-  const int64_t R = m >> 4;
-  const int r16 = (int)(m & 15), h = li >> 3, c = (li & 7) >> 1;
-  return ((R * G + g) * 2 + h) * 1024 + (c * 16 + r16) * 16 + (li & 1) * 8;
-}
-
-// kFrag: codes in the fragment order above (M % 16 == 0, K % 128 == 0, so
-// every group is whole); otherwise row-major [M][K].
-template <bool kFrag>
 __device__ __forceinline__ void act_group_store(const ActGroup& a, uint8_t* __restrict__ q,
                                                 float* __restrict__ scale, int64_t K, int G, int li) {
   uint32_t am = amax_fold(amax8(0u, a.v));
@@ -193,7 +178,7 @@ __device__ __forceinline__ void act_group_store(const ActGroup& a, uint8_t* __re
   }
   const float s = scale_from_amax_bits(am);
   if (a.valid && li == 0) scale[a.m * G + a.g] = s;
-  uint8_t* dst = q + (kFrag ? act_frag_offset(a.m, a.g, li, G) : a.m * K + a.col);
+  uint8_t* dst = q + a.m * K + a.col;
   if (a.vec) {
     __builtin_nontemporal_store(encode8(a.v, s), reinterpret_cast<u32x2*>(dst));
   } else if (a.valid) {
@@ -208,7 +193,7 @@ __device__ __forceinline__ void act_group_store(const ActGroup& a, uint8_t* __re
 // Pass p of quarter wave w (w = threadIdx / 16) takes group
 // blockIdx * 16 * kPasses + 16 p + w, so each pass is one coalesced sweep
 // over 16 consecutive groups.
-template <int kPasses, bool kFrag>
+template <int kPasses>
 __global__ __launch_bounds__(kQaThreads) void quant_act_kernel(const uint16_t* __restrict__ x,
                                                                uint8_t* __restrict__ q,
                                                                float* __restrict__ scale, int64_t M, int64_t K,
@@ -219,7 +204,7 @@ __global__ __launch_bounds__(kQaThreads) void quant_act_kernel(const uint16_t* _
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) grp[p] = act_group_load(x, M, K, G, g0 + 16 * p, li);
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) act_group_store<kFrag>(grp[p], q, scale, K, G, li);
+  for (int p = 0; p < kPasses; ++p) act_group_store(grp[p], q, scale, K, G, li);
 }
 
 // ---------------------------------------------------------------------------
@@ -243,6 +228,49 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ i
   out[i] = (uint8_t)c;
 }
 
+// ---------------------------------------------------------------------------
+// Activation codes in the MFMA fragment order of the GEMM's activation
+// operand: per 16-row group R and K-block g a 2 KB block in which lane
+// l = 16 c + r (r = row within the group) holds bytes 16 c .. 16 c + 15 of
+// row 16 R + r's K-block at l * 16 and bytes 64 + 16 c .. 79 + 16 c at
+// 1024 + l * 16.  One wave per (R, g): lane l loads exactly the 32 BF16
+// values whose codes it stores, the four lanes of a row (r, r + 16, r + 32,
+// r + 48) combine their amax with two shuffles, and the two 1 KB halves are
+// stored contiguously.  Same scale and codes as quant_act_kernel (M % 16 ==
+// 0, K % 128 == 0).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kQaThreads) void quant_act_frag_kernel(const uint16_t* __restrict__ x,
+                                                                    uint8_t* __restrict__ q,
+                                                                    float* __restrict__ scale, int64_t M,
+                                                                    int64_t K, int G) {
+  const int64_t unit = (int64_t)blockIdx.x * (kQaThreads / 64) + (threadIdx.x >> 6);
+  if (unit >= (M / 16) * G) return;  // whole waves
+  const int lane = threadIdx.x & 63, r = lane & 15, c = lane >> 4;
+  const int64_t R = unit / G;
+  const int g = (int)(unit % G);
+  const int64_t m = R * 16 + r;
+  const uint16_t* src = x + m * K + (int64_t)g * kBlock + 16 * c;
+  u32x4 v[4];
+  v[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+  v[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 8));
+  v[2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 64));
+  v[3] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 72));
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) am = amax8(am, v[i]);
+  am = amax_fold(am);
+  uint32_t o = __shfl_xor(am, 16, 64);
+  am = am > o ? am : o;
+  o = __shfl_xor(am, 32, 64);
+  am = am > o ? am : o;
+  const float s = scale_from_amax_bits(am);
+  if (c == 0) scale[m * G + g] = s;
+  const u32x2 a0 = encode8(v[0], s), a1 = encode8(v[1], s), b0 = encode8(v[2], s), b1 = encode8(v[3], s);
+  uint8_t* dst = q + (R * G + g) * 2048 + lane * 16;
+  __builtin_nontemporal_store(u32x4{a0.x, a0.y, a1.x, a1.y}, reinterpret_cast<u32x4*>(dst));
+  __builtin_nontemporal_store(u32x4{b0.x, b0.y, b1.x, b1.y}, reinterpret_cast<u32x4*>(dst + 1024));
+}
+
 }  // namespace
 
 hipError_t launch_quant_weight(const uint16_t* w, uint8_t* q, float* scale, int64_t batch, int64_t N, int64_t K,
@@ -263,9 +291,20 @@ hipError_t launch_quant_weight_multi(const WeightBatch& batch, int64_t blocks, h
   return hipGetLastError();
 }
 
-template <bool kFrag>
-hipError_t launch_quant_act_any(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K,
-                                hipStream_t stream) {
+hipError_t launch_quant_act_frag(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K,
+                                 hipStream_t stream) {
+  const int64_t G = K / kBlock;
+  const int64_t units = (M / 16) * G;
+  if (units == 0) return hipSuccess;
+  if (M % 16 != 0 || K % kBlock != 0) return hipErrorInvalidValue;
+  const int64_t blocks = (units + kQaThreads / 64 - 1) / (kQaThreads / 64);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_act_frag_kernel, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q, scale, M, K,
+                     (int)G);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K, hipStream_t stream) {
   const int64_t G = (K + kBlock - 1) / kBlock;
   const int64_t groups = M * G;
   if (groups == 0) return hipSuccess;
@@ -274,21 +313,12 @@ hipError_t launch_quant_act_any(const uint16_t* x, uint8_t* q, float* scale, int
   const int64_t blocks = (groups + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (large)
-    hipLaunchKernelGGL((quant_act_kernel<kQaPassesLarge, kFrag>), dim3((unsigned)blocks), dim3(kQaThreads), 0,
-                       stream, x, q, scale, M, K, (int)G);
-  else
-    hipLaunchKernelGGL((quant_act_kernel<1, kFrag>), dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q,
+    hipLaunchKernelGGL(quant_act_kernel<kQaPassesLarge>, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q,
                        scale, M, K, (int)G);
+  else
+    hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q, scale, M, K,
+                       (int)G);
   return hipGetLastError();
-}
-
-hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K, hipStream_t stream) {
-  return launch_quant_act_any<false>(x, q, scale, M, K, stream);
-}
-
-hipError_t launch_quant_act_frag(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K,
-                                 hipStream_t stream) {
-  return launch_quant_act_any<true>(x, q, scale, M, K, stream);
 }
 
 hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int method, hipStream_t stream) {
