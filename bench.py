@@ -813,6 +813,7 @@ def gemm_profile_cases():
 
     cases = [("decode %s" % nm, 256, n, k, 0) for nm, n, k in LAYER_SHAPES_QWEN3_8B]
     cases += [("prefill %s" % nm, 8192, n, k, 0) for nm, n, k in LAYER_SHAPES_QWEN3_8B]
+    cases += [("prefill afrag %s" % nm, 8192, n, k, 0) for nm, n, k in LAYER_SHAPES_QWEN3_8B]
     moe = MOE_QWEN3_30B_A3B
     mt = moe["tokens"] * moe["top_k"]
     cases.append(("MoE fc1 gate_up", mt, moe["gate_up"][0], moe["gate_up"][1], moe["experts"]))
@@ -835,12 +836,18 @@ def gemm_profile():
         w = device_bf16_normal((g, n, k) if g else (n, k), 0.02, seed=700 + i)
         x = device_bf16_normal((m, k), 1.0, seed=800 + i)
         wq, ws = fb.quantize_weight_blockwise(w)
-        xq, xs = fb.quantize_act_per_token_group(x)
+        afrag = label.startswith("prefill afrag")
+        if afrag:
+            xq, xs = fb.quantize_act_per_token_group_frag(x)
+        else:
+            xq, xs = fb.quantize_act_per_token_group(x)
         del w, x
         y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
         torch.cuda.synchronize()
         for _ in range(GEMM_PROFILE_REPS):
-            if g:
+            if afrag:
+                fb.gemm_w8a8_blockscaled_afrag(xq, xs, wq, ws, y)
+            elif g:
                 fb.grouped_gemm_w8a8_blockscaled(xq, xs, wq, ws, offsets, y)
             else:
                 fb.gemm_w8a8_blockscaled(xq, xs, wq, ws, y)
