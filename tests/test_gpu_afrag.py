@@ -35,10 +35,12 @@ def test_quantizer_fragment_order(fb, m, k):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
-def test_quantizer_fragment_order_matches_row_major_prefill(fb):
-    """At the prefill size: the fragment codes are the row-major GPU codes
-    permuted (the row-major quantizer is itself checked against the oracle)."""
-    m, k = 8192, 4096
+@pytest.mark.parametrize("m,k", [(8192, 4096), (4112, 2176), (8208, 2176)])
+def test_quantizer_fragment_order_matches_row_major_prefill(fb, m, k):
+    """At the prefill size, and at odd unit counts with a ragged last
+    workgroup (4369 and 8721 units of 16 rows x 128): the fragment codes are
+    the row-major GPU codes permuted (the row-major quantizer is itself
+    checked against the oracle)."""
     announce("afrag quant prefill", m, k)
     x = device_bf16_normal((m, k), 1.0, seed=9)
     q, s = fb.quantize_act_per_token_group(x)

@@ -1,6 +1,7 @@
 """The library's kernels under HIP graph capture: a decode-layer step
 (re-quant, activation quant, GEMMs), a ragged MoE grouped GEMM (plain and
-with gathered rows; the persistent expert-tile kernel by default) and a
+with gathered rows; the persistent expert-tile kernel by default), the
+fragment-order activation quantizer and GEMM, and a
 KV-cache calibration + write are
 captured once and replayed several times, with eager work and
 synchronizations between replays; every replay's outputs must equal the
@@ -61,6 +62,9 @@ def test_graph_replays_match_eager():
     fb().quantize_weight_blockwise(device_bf16_normal((G, NE, KE), 0.02, seed=70), moe["wq"], moe["ws"])
     fb().quantize_act_per_token_group(device_bf16_normal((Me, KE), 1.0, seed=71), moe["xq"], moe["xs"])
 
+    L0 = layers[0]
+    af = dict(xq=torch.empty_like(L0["xq"]), xs=torch.empty_like(L0["xs"]), y=torch.empty_like(L0["y"]))
+
     def work():
         fb().grouped_gemm_w8a8_blockscaled(moe["xq"], moe["xs"], moe["wq"], moe["ws"], moe["off"], moe["y"])
         fb().grouped_gemm_w8a8_blockscaled_gather(moe["xq"], moe["xs"], moe["rows"], 2, moe["wq"], moe["ws"],
@@ -69,11 +73,13 @@ def test_graph_replays_match_eager():
             fb().quantize_weight_blockwise(L["w"], L["wq"], L["ws"])
             fb().quantize_act_per_token_group(L["x"], L["xq"], L["xs"])
             fb().gemm_w8a8_blockscaled(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
+        fb().quantize_act_per_token_group_frag(L0["x"], af["xq"], af["xs"])
+        fb().gemm_w8a8_blockscaled_afrag(af["xq"], af["xs"], L0["wq"], L0["ws"], af["y"])
         fb().kv_scale_calibrate(kv["k"], kv["v"], True, kv["ks"], kv["vs"])
         fb().kv_cache_write_fp8(kv["k"], kv["v"], kv["slots"], kv["ks"], kv["vs"], kv["kc"], kv["vc"])
 
     outs = ([t for L in layers for t in (L["wq"], L["ws"], L["xq"], L["xs"], L["y"])] +
-            [kv["ks"], kv["vs"], kv["kc"], kv["vc"], moe["y"], moe["yg"]])
+            [kv["ks"], kv["vs"], kv["kc"], kv["vc"], moe["y"], moe["yg"], af["xq"], af["xs"], af["y"]])
     announce("graph eager reference")
     work()
     ref = snapshot(outs)
@@ -94,3 +100,7 @@ def test_graph_replays_match_eager():
         got = snapshot(outs)
         for a, b in zip(got, ref):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
+    # the fragment-order GEMM agrees with the row-major GEMM (whose default
+    # tile at M = 256 sums in another order, so to the GEMM tolerance)
+    y_af, y_rm = ref[-1].float(), ref[4].float()
+    assert float((y_af - y_rm).norm() / y_rm.norm()) <= 1e-2
