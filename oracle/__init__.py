@@ -30,8 +30,8 @@ Modules
 ``bf16``   BF16 bit patterns <-> float, and round-to-nearest-even into BF16.
 ``quant``  per-tile amax -> scale -> divide -> round; 128x128 weight blocks
            and 1x128 per-token activation groups.
-``gemm``   block-scaled GEMM (dequantize, exact product, one BF16 rounding)
-           and its ragged grouped (MoE) form.
+``gemm``   block-scaled GEMM (dequantize, exact product, one BF16 rounding),
+           its FP32-accumulated form and its ragged grouped (MoE) form.
 ``moe``    MoE expert-FFN glue: pairs sorted by expert, gathered FP8 rows,
            SiLU(gate) * up -> BF16 -> 1x128 groups, the weighted combine.
 ``kv``     FP8 KV cache: per-step K/V scale calibration, quantizing cache
@@ -71,6 +71,7 @@ from .gemm import (
     dequant_weight,
     gemm_ref,
     gemm_ref_bf16,
+    gemm_ref_fp32,
     grouped_gemm_ref,
 )
 from .tis import importance_weights
@@ -95,6 +96,7 @@ __all__ = [
     "dequant_weight",
     "gemm_ref",
     "gemm_ref_bf16",
+    "gemm_ref_fp32",
     "grouped_gemm_ref",
     "importance_weights",
     "sort_by_expert",

@@ -9,11 +9,11 @@ exponent bits with bias 7, three mantissa bits.
 * exponent field 0: subnormal, value = m * 2^-9 (m = 0..7);
 * exponent field 1..15: normal, value = (1 + m/8) * 2^(e-7);
 * the pattern S.1111.111 (0x7F / 0xFF) is NaN; there is no infinity, so the
-  largest finite magnitude is 1.75 * 2^8 = 448 (the "approximately 448" of
-  §3.4.1) and the smallest normal is 2^-6.
+  largest finite magnitude is 1.75 * 2^8 = 448 (the FP8 maximum that §3.4.1
+  maps each block maximum to) and the smallest normal is 2^-6.
 
-Encoding rounds to the nearest representable value (§3.4.2 Phase 2 step 2:
-"round to the nearest E4M3 FP8 value"), ties to the even code (the IEEE
+Encoding rounds to the nearest representable value (§3.4.2 Phase 2 step 2
+rounds each quotient to the nearest E4M3 value), ties to the even code (the IEEE
 default; the pages give no tie rule), and saturates to +-448 instead of
 producing NaN (the format has no infinity and the pages give no overflow
 rule; the scale rule of §3.4.1 keeps in-range inputs at |v| <= 448 anyway).

@@ -18,6 +18,12 @@ operands are exact in float64: a float32 scale times a 4-bit significand)
 with one library matmul, and rounds once into BF16.  The summation order of
 a real kernel is free, so GPU results are compared with a tolerance.
 
+``gemm_ref_fp32`` is the same product evaluated with FP32 accumulation, as
+§3.4.2 Phase 3 describes the arithmetic: per 128-wide K-block the float32
+product of the decoded codes, times the two block scales, added into a
+float32 accumulator.  It is the fast form used for CPU timing; its distance
+from the exact value is bounded by float32 rounding (pinned in the tests).
+
 MoE expert layers (fc1/fc2, §3.4.1 "Quantization Scope") use the same
 scheme per expert: expert e owns rows [off[e], off[e+1]) of the stacked
 activations and its own weight and scale grid.
@@ -75,6 +81,37 @@ def gemm_ref(a_codes, a_scales, w_codes, w_scales, rows=None, cols=None):
 def gemm_ref_bf16(a_codes, a_scales, w_codes, w_scales, rows=None, cols=None):
     """BF16 bit patterns of the GEMM output (one RNE rounding of the float64 result)."""
     return round_to_bf16_bits(gemm_ref(a_codes, a_scales, w_codes, w_scales, rows, cols))
+
+
+def gemm_ref_fp32(a_codes, a_scales, w_codes, w_scales, rows=None):
+    """y = sum_kb (s_a[m,kb] * s_w[n//128,kb]) * P_kb[m,n] with float32 arithmetic.
+
+    P_kb is the float32 product of the decoded (unscaled) codes of K-block kb
+    (one library matmul per K-block; the decoded codes are exact in float32),
+    the scale product is a float32 multiply, and the K-blocks are summed in a
+    float32 accumulator in K order.  ``rows`` restricts the output to those
+    activation rows.  Returns float32 [M][N] (before the BF16 rounding).
+    """
+    qa = np.asarray(a_codes, np.uint8)
+    qw = np.asarray(w_codes, np.uint8)
+    m_all, k = qa.shape
+    n = qw.shape[0]
+    _check_k(k)
+    r = np.arange(m_all) if rows is None else np.asarray(rows)
+    sa = np.asarray(a_scales, np.float32)[r]
+    sw = np.asarray(w_scales, np.float32)
+    if sa.shape != (len(r), k // BLOCK) or sw.shape != (-(-n // BLOCK), k // BLOCK):
+        raise ValueError("scales must be [M][K/128] and [ceil(N/128)][K/128]")
+    da = decode_e4m3(qa[r]).astype(np.float32)
+    dw = decode_e4m3(qw).astype(np.float32)
+    block_of_n = np.arange(n) // BLOCK
+    y = np.zeros((len(r), n), np.float32)
+    for kb in range(k // BLOCK):
+        cols = slice(kb * BLOCK, (kb + 1) * BLOCK)
+        p = da[:, cols] @ dw[:, cols].T
+        c = sa[:, kb][:, None] * sw[block_of_n, kb][None, :]
+        y += p * c
+    return y
 
 
 def grouped_gemm_ref(a_codes, a_scales, w_codes, w_scales, offsets):

@@ -1,7 +1,8 @@
 """Pins of the oracle's block-scaled GEMM and grouped GEMM (CPU only).
 
 Pins: an exact-rational triple loop on tiny shapes (every product and sum in
-Fractions, one rounding to BF16 by exhaustive search), one-hot and all-ones
+Fractions, one rounding to BF16 by exhaustive search), the FP32-accumulated
+form against that exact sum within its float32 error bound, one-hot and all-ones
 activation rows that reproduce dequantized weight rows and row sums, exact
 doubling under a power-of-two activation scale, and the grouped form against
 per-expert dense calls (G = 1, empty experts, a single hot expert).
@@ -17,6 +18,7 @@ from oracle import (
     dequant_weight,
     gemm_ref,
     gemm_ref_bf16,
+    gemm_ref_fp32,
     grouped_gemm_ref,
     quant_act_per_token_group,
     quant_weight_blockwise,
@@ -161,3 +163,69 @@ def test_planted_mistake_is_caught():
     wrong_w = decode_e4m3(qw) * sw[np.arange(256) % 2]
     wrong = decode_e4m3(qa) @ wrong_w.T
     assert not np.allclose(wrong, y)
+
+
+def _exact_sum(da, sa, dw, sw, i, j):
+    acc, mag = Fraction(0), Fraction(0)
+    for t in range(da.shape[1]):
+        term = (Fraction(float(da[i, t])) * Fraction(float(sa[i, t // 128]))
+                * Fraction(float(dw[j, t])) * Fraction(float(sw[j // 128, t // 128])))
+        acc += term
+        mag += abs(term)
+    return acc, mag
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_fp32_accumulated_form_within_float32_bound_of_exact_sum(seed):
+    """gemm_ref_fp32 vs the exact rational sum: each K-block's float32 product
+    (<= 128 roundings in any order), the scale product and its multiply (2),
+    and KB accumulator additions give |y - exact| <= (128 + KB + 2) u sum|terms|
+    (u = 2^-24, first order; the factor is generous)."""
+    rng = np.random.default_rng(40 + seed)
+    m, n, k = 3, 5 + 128 * (seed == 1), 128 * (2 + seed)
+    qa, qw = _codes(rng, (m, k)), _codes(rng, (n, k))
+    sa = rng.uniform(0.001, 2.0, (m, k // 128)).astype(np.float32)
+    sw = rng.uniform(0.001, 2.0, (-(-n // 128), k // 128)).astype(np.float32)
+    y = gemm_ref_fp32(qa, sa, qw, sw)
+    assert y.dtype == np.float32 and y.shape == (m, n)
+    da, dw = decode_e4m3(qa), decode_e4m3(qw)
+    kb = k // 128
+    for i in range(m):
+        for j in range(n):
+            acc, mag = _exact_sum(da, sa, dw, sw, i, j)
+            bound = mag * Fraction(128 + kb + 3, 2 ** 24)
+            assert abs(Fraction(float(y[i, j])) - acc) <= bound, (i, j)
+    # the sampled-rows form computes the same rows
+    rows = np.array([2, 0])
+    assert np.array_equal(gemm_ref_fp32(qa, sa, qw, sw, rows=rows), y[rows])
+
+
+def test_fp32_accumulated_form_exact_on_one_hot_rows():
+    """One non-zero product per output: the product of the codes and the scale
+    product are exact, so y is the exact dequantized weight rounded once to
+    float32."""
+    rng = np.random.default_rng(44)
+    n, k = 256, 384
+    qw = _codes(rng, (n, k))
+    sw = rng.uniform(0.01, 1.0, (2, 3)).astype(np.float32)
+    cols = np.array([0, 127, 128, 300, 383])
+    qa = np.zeros((len(cols), k), np.uint8)
+    qa[np.arange(len(cols)), cols] = 0x38  # E4M3 1.0
+    sa = np.ones((len(cols), 3), np.float32)
+    y = gemm_ref_fp32(qa, sa, qw, sw)
+    w = dequant_weight(qw, sw)
+    assert np.array_equal(y, w[:, cols].T.astype(np.float32))
+
+
+def test_fp32_accumulated_form_catches_a_transposed_scale_grid():
+    """A planted mistake in the fp32 form's recipe (weight scales indexed
+    [kb][n//128]) moves the result far outside the float32 bound."""
+    rng = np.random.default_rng(45)
+    qa, qw = _codes(rng, (4, 256)), _codes(rng, (256, 256))
+    sa = rng.uniform(0.5, 1, (4, 2)).astype(np.float32)
+    sw = np.array([[1.0, 4.0], [0.25, 2.0]], np.float32)
+    y = gemm_ref_fp32(qa, sa, qw, sw)
+    wrong = gemm_ref_fp32(qa, sa, qw, np.ascontiguousarray(sw.T))
+    exact = gemm_ref(qa, sa, qw, sw)
+    assert np.max(np.abs(y - exact)) < 1e-4 * np.max(np.abs(exact))
+    assert np.max(np.abs(wrong - exact)) > 0.1 * np.max(np.abs(exact))
