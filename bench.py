@@ -1,22 +1,33 @@
 """Benchmark of the blockwise W8A8 FP8 hot path on one MI355X.
 
-One step = the whole linear-layer hot path for a Qwen3-8B-shaped decode
-layer (M = 256 tokens): re-quantize the four BF16 weight matrices (qkv
-4096->6144, o 4096->4096, gate_up 4096->24576, down 12288->4096) into E4M3
-with 128x128-block FP32 scales, quantize the four BF16 activations per token
-in 1x128 groups, and run the four block-scaled FP8 GEMMs (FP32 accumulation,
-BF16 output).  Inputs are seeded synthetic tensors already resident in HBM.
+One step = the linear-layer forward of one Qwen3-8B-shaped layer at prefill
+(M = 8192 tokens, activations N(0,1) with 1% outlier channels x30): quantize
+the four BF16 activations (qkv 4096, o 4096, gate_up 4096, down 12288 input
+features) per token in 1x128 groups, and run the four block-scaled FP8
+GEMMs (qkv 4096->6144, o 4096->4096, gate_up 4096->24576, down
+12288->4096; FP32 accumulation, BF16 output) on E4M3 weights with
+128x128-block scales quantized beforehand (once per RL step).  The
+activation codes are written in the MFMA fragment order that the library's
+prefill GEMM reads (quantize_act_per_token_group_frag +
+gemm_w8a8_blockscaled_afrag, its path for M % 16 == 0 and K % 256 == 0).
+Steps cycle through four copies of every buffer (1.4 GB each), so a copy
+has left the 256 MB Infinity Cache before it is used again.  Inputs are
+seeded synthetic tensors already resident in HBM.
 
-`value` = W8A8 GEMM FLOPs of the step / step time (TFLOP/s, the re-quant
-and activation quantization inside the timed step).  The JSON line adds the
-roofline of the dominant kernel (the weight re-quantizer, timed with HIP
-events on its stream inside the timed region), the CPU oracle timed on a
-bounded sample, and per-configuration details measured after the timed
-region: prefill GEMMs (M = 8192), the MoE grouped GEMMs, the 36-layer
-re-quantization sweep, and sampled parity against the oracle.
+`value` = GEMM FLOPs of the step / step time (TFLOP/s, the activation
+quantization inside the timed step).  The same run measures the per-step
+weight re-quantization of all 36 layers of the model (6.95 G parameters,
+20.84 GB algorithmic traffic; `requant_GBps`, `roofline_per_kernel.requant`),
+checks sampled outputs of both against the CPU oracle (`parity`), times the
+oracle on the host's cores (`cpu_baseline`), and adds per-configuration
+measurements (`detail`: the decode layer step at M = 256, the prefill
+GEMMs on both activation layouts, the Qwen3-30B-A3B MoE layer, and the
+widened operations).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail] [--no-cpu]
-       python bench.py --rocprof-summary DIR   (summarise rocprofv3 output, see below)
+       python bench.py --rocprof-summary DIR      summarise rocprofv3 runs of this benchmark
+       python bench.py --gemm-profile | --gemm-counter-summary DIR
+       python bench.py --bw-profile | --bw-counter-summary DIR
 
 `roofline.traffic` is the HBM traffic per launch of the dominant kernel as
 measured by rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, scaled by what
@@ -43,15 +54,20 @@ FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "fp8_blockwise_quantized_quantize_amd", "csrc")
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_layer_step_qwen3_8b.md")
-# kernel-name prefix of each phase -> the source file that defines it
-# launches per decode step: the four matrices are re-quantized by one launch
-PHASE_LAUNCHES = {"requant": 1, "act_quant": 4, "gemm": 4}
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "prefill_layer_step_qwen3_8b.md")
+
+PREFILL_M = 8192
+OUTLIER_FRAC, OUTLIER_MULT = 0.01, 30.0
+SWEEP_LAYERS = 36
+SWEEP_REPS = 20
+# kernel-name prefix and source file of each measured phase; launches per
+# step (headline phases) or per sweep (requant: four calls with batch = 36)
 PHASE_KERNELS = {
-    "requant": ("quant_weight_multi_kernel", "quant.hip"),
-    "act_quant": ("quant_act_kernel", "quant.hip"),
+    "act_quant": ("quant_act_frag_kernel", "quant.hip"),
     "gemm": ("gemm_dense_kernel", "gemm.hip"),
+    "requant": ("quant_weight_kernel", "quant.hip"),
 }
+PHASE_LAUNCHES = {"act_quant": 4, "gemm": 4, "requant": 4}
 
 
 def source_sha(fname):
@@ -83,21 +99,27 @@ def committed_traffic(phase):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-detail", action="store_true", help="skip the per-configuration measurements")
-    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and the parity check")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (to scale HBM byte counters) and exit")
     p.add_argument("--rocprof-summary", metavar="DIR",
                    help="summarise rocprofv3 output under DIR (kernel trace + FETCH_SIZE / WRITE_SIZE passes "
                         "of this benchmark and of --calibrate-copy) and exit")
     p.add_argument("--gemm-profile", action="store_true",
-                   help="only run each GEMM of GEMM_PROFILE_CASES a few times (a target for rocprofv3 "
+                   help="only run each GEMM of gemm_profile_cases() a few times (a target for rocprofv3 "
                         "counter passes) and exit")
     p.add_argument("--gemm-counter-summary", metavar="DIR",
                    help="summarise rocprofv3 passes of --gemm-profile under DIR (kt, mfma, lds, l2, fetch, "
                         "write, copy_fetch, copy_write) and exit")
+    p.add_argument("--bw-profile", action="store_true",
+                   help="only run each bandwidth-bound kernel of bw_profile_cases() a few times (a target for "
+                        "FETCH_SIZE / WRITE_SIZE passes) and exit")
+    p.add_argument("--bw-counter-summary", metavar="DIR",
+                   help="summarise rocprofv3 passes of --bw-profile under DIR (kt, fetch, write, copy_fetch, "
+                        "copy_write) and exit")
     return p.parse_args()
 
 
@@ -124,6 +146,12 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
+def host_threads():
+    """Worker threads for the CPU oracle: the host cores this process may
+    use, at most 16 (the host share of one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -138,6 +166,12 @@ def main():
     if args.gemm_counter_summary:
         gemm_counter_summary(args.gemm_counter_summary)
         return
+    if args.bw_profile:
+        bw_profile()
+        return
+    if args.bw_counter_summary:
+        bw_counter_summary(args.bw_counter_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path.  Its kernels run on "
               "one GPU's share of the work: whole 128x128 weight blocks for re-quantization, column- or "
@@ -147,60 +181,64 @@ def main():
 
     import torch
 
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, ROOT)
     import fp8_blockwise_quantized_quantize_amd as fb
-    from synthetic import LAYER_SHAPES_QWEN3_8B, device_bf16_normal
+    from synthetic import LAYER_SHAPES_QWEN3_8B, device_activations, device_bf16_normal
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    M = 256
+    M = PREFILL_M
 
     # ---------------------------------------------------------------- inputs
-    # Step s uses buffer set s % SETS (copies of the same inputs): one set is
-    # ~0.6 GB, so a set has left the 256 MB Infinity Cache before it is used
-    # again and the step's weight bytes come from HBM.
+    # Step s uses buffer set s % SETS (copies of the same inputs, 1.4 GB per
+    # set): a set's bytes have left the 256 MB Infinity Cache before it is
+    # used again.  The weights are quantized once, before the timed steps.
     SETS = 4
+    base = []
+    for i, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
+        w = device_bf16_normal((n, k), 0.02, seed=300 + i)
+        x, _ = device_activations(M, k, seed=400 + 2 * i, outlier_frac=OUTLIER_FRAC, outlier_mult=OUTLIER_MULT)
+        base.append((name, n, k, w, x))
     sets = []
     for c in range(SETS):
         layers = []
-        for i, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
-            w = device_bf16_normal((n, k), 0.02, seed=100 + i) if c == 0 else sets[0][i]["w"].clone()
-            x = device_bf16_normal((M, k), 1.0, seed=200 + i) if c == 0 else sets[0][i]["x"].clone()
+        for name, n, k, w, x in base:
             layers.append({
-                "name": name, "n": n, "k": k, "w": w, "x": x,
+                "name": name, "n": n, "k": k, "x": x if c == 0 else x.clone(),
                 "wq": torch.empty((n, k), dtype=torch.uint8, device=dev),
                 "ws": torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev),
                 "xq": torch.empty((M, k), dtype=torch.uint8, device=dev),
                 "xs": torch.empty((M, k // 128), dtype=torch.float32, device=dev),
                 "y": torch.empty((M, n), dtype=torch.bfloat16, device=dev),
             })
+        fb.quantize_weights_blockwise_multi([b[3] for b in base], [(L["wq"], L["ws"]) for L in layers])
         sets.append(layers)
+    w_bf16 = {name: w for name, _, _, w, _ in base}
+    del base
     layers = sets[0]
     gemm_flops = sum(2 * M * L["n"] * L["k"] for L in layers)
-    requant_bytes = sum(L["n"] * L["k"] * 3 + L["ws"].numel() * 4 for L in layers)
+    act_bytes = sum(M * L["k"] * 3 + M * (L["k"] // 128) * 4 for L in layers)
+    gemm_bytes = sum(M * L["k"] + L["n"] * L["k"] + 2 * M * L["n"] + M * (L["k"] // 128) * 4
+                     + (L["n"] // 128) * (L["k"] // 128) * 4 for L in layers)
 
-    # HIP events between the three phases of a step, on the launch stream
-    phases = ("requant", "act_quant", "gemm")
+    # HIP events between the two phases of a step, on the launch stream
+    phases = ("act_quant", "gemm")
     ev = []
 
     def step(record, s):
         ls = sets[s % SETS]
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if record else None
         if record:
             e[0].record(stream)
-        # the layer's four matrices re-quantized by one launch
-        fb.quantize_weights_blockwise_multi([L["w"] for L in ls], [(L["wq"], L["ws"]) for L in ls])
+        for L in ls:
+            fb.quantize_act_per_token_group_frag(L["x"], L["xq"], L["xs"])
         if record:
             e[1].record(stream)
         for L in ls:
-            fb.quantize_act_per_token_group(L["x"], L["xq"], L["xs"])
+            fb.gemm_w8a8_blockscaled_afrag(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
         if record:
             e[2].record(stream)
-        for L in ls:
-            fb.gemm_w8a8_blockscaled(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
-        if record:
-            e[3].record(stream)
             ev.append(e)
 
     for s in range(args.warmup):
@@ -211,43 +249,23 @@ def main():
         step(True, s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    step(False, 0)  # set 0 holds this step's outputs for the parity check below
-    torch.cuda.synchronize()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
-
-    # per-phase time (ms per step) and algorithmic bytes / FLOPs per step
+    step(False, 0)  # set 0 holds this step's outputs for the parity check
+    torch.cuda.synchronize()
     phase_ms = {p: sum(e[i].elapsed_time(e[i + 1]) for e in ev) / len(ev) for i, p in enumerate(phases)}
-    act_bytes = sum(M * L["k"] * 3 + L["xs"].numel() * 4 for L in layers)
-    gemm_bytes = sum(M * L["k"] + L["n"] * L["k"] + 2 * M * L["n"] + L["xs"].numel() * 4 + L["ws"].numel() * 4
-                     for L in layers)
-    kernels = {
-        "requant": (PHASE_KERNELS["requant"][0], requant_bytes, 0),
-        "act_quant": (PHASE_KERNELS["act_quant"][0], act_bytes, 0),
-        "gemm": (PHASE_KERNELS["gemm"][0], gemm_bytes, gemm_flops),
+
+    # ------------------------------------------- the 36-layer re-quant sweep
+    sweep = requant_sweep(fb, dev)
+
+    roof_all = {
+        "gemm": roof_entry("gemm", phase_ms["gemm"], gemm_bytes, gemm_flops),
+        "act_quant": roof_entry("act_quant", phase_ms["act_quant"], act_bytes, 0),
+        "requant": roof_entry("requant", sweep["ms"], sweep["bytes"], 0),
     }
-    roof_all = {}
-    for p in phases:
-        name, byt, flops = kernels[p]
-        ms = phase_ms[p]
-        nl = PHASE_LAUNCHES[p]
-        launch_us = ms * 1e3 / nl
-        # bound: HBM unless the arithmetic intensity passes the ridge point
-        if flops and flops / byt > FP8_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3:
-            ach, peak, unit, bound = flops / ms / 1e9, FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
-        else:
-            ach, peak, unit, bound = byt / ms / 1e6, HBM_PEAK_GBPS, "GB/s", "hbm"
-        tr = committed_traffic(p)
-        roof_all[p] = {"bound": bound, "kernel": name, "achieved": round(ach, 1), "peak": peak, "unit": unit,
-                       "frac": round(ach / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
-                       "avg_launch_us": round(launch_us, 2),
-                       "launches_per_step": nl, "algorithmic_bytes_per_launch_avg": int(byt / nl),
-                       "flops_per_launch_avg": int(flops / nl)}
-        if flops:
-            roof_all[p]["TFLOPs"] = round(flops / ms / 1e9, 1)
+    roof_all["requant"].update({"reps": sweep["reps"], "median_ms": sweep["median_ms"], "min_ms": sweep["min_ms"]})
     dominant = max(phases, key=lambda p: phase_ms[p])
     roofline = dict(roof_all[dominant])
-    requant_gbps = requant_bytes / phase_ms["requant"] / 1e6
 
     out = {
         "metric": "W8A8 block-scaled GEMM TFLOP/s + weight re-quant GB/s (% of roofline)",
@@ -261,32 +279,92 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; Qwen3-8B layer shapes; "
-                "4 buffer sets rotated across steps)",
+        "data": "synthetic (seeded N(0,0.02) weights; N(0,1) activations with 1% outlier channels x30; "
+                "Qwen3-8B layer shapes; 4 buffer sets rotated across steps)",
         "config": {
-            "workload": "qwen3-8b-decode-layer: requant qkv/o/gate_up/down + 1x128 act quant + 4 W8A8 GEMMs, M=256",
+            "workload": "qwen3-8b-prefill-layer: 1x128 act quant (fragment order) + 4 W8A8 block-scaled GEMMs "
+                        "(qkv/o/gate_up/down), M=8192",
             "tokens": M,
             "gemm_flops_per_step": gemm_flops,
-            "requant_bytes_per_step": requant_bytes,
+            "requant_workload": "qwen3-8b 36-layer weight re-quant sweep: 6.95 G params, 4 calls with batch=36",
             "parallelism": "1 GPU",
         },
         "roofline": roofline,
         "roofline_per_kernel": roof_all,
         "phase_ms": {p: round(v, 4) for p, v in phase_ms.items()},
-        "requant_GBps": round(requant_gbps, 1),
-        "requant_frac_hbm": round(requant_gbps / HBM_PEAK_GBPS, 4),
+        "requant_GBps": roof_all["requant"]["achieved"],
+        "requant_frac_hbm": roof_all["requant"]["frac"],
         "device": device_info(),
     }
 
-    if not args.no_detail:
-        out["detail"] = detail(fb, dev)
     if not args.no_cpu:
-        out["cpu_baseline"], out["parity"] = cpu_baseline(layers, M, gemm_flops, requant_bytes)
+        out["cpu_baseline"], out["parity"] = cpu_baseline_and_parity(fb, layers, w_bf16, sweep, gemm_flops)
+    sweep.pop("tensors")
+    torch.cuda.empty_cache()
+    if not args.no_detail:
+        out["detail"] = detail(fb, dev, with_cpu=not args.no_cpu)
     print(json.dumps(out), flush=True)
 
 
+def roof_entry(phase, ms, byt, flops):
+    """Roofline of one measured phase: the FP8 MFMA peak when its arithmetic
+    intensity passes the ridge point, HBM bandwidth otherwise."""
+    name = PHASE_KERNELS[phase][0]
+    nl = PHASE_LAUNCHES[phase]
+    if flops and flops / byt > FP8_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3:
+        ach, peak, unit, bound = flops / ms / 1e9, FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = byt / ms / 1e6, HBM_PEAK_GBPS, "GB/s", "hbm"
+    tr = committed_traffic(phase)
+    e = {"bound": bound, "kernel": name, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+         "frac": round(ach / peak, 4), "traffic": tr["bytes_per_launch"] if tr else None,
+         "avg_launch_us": round(ms * 1e3 / nl, 2), "launches": nl,
+         "algorithmic_bytes_per_launch_avg": int(byt / nl), "flops_per_launch_avg": int(flops / nl)}
+    if flops:
+        e["TFLOPs"] = round(flops / ms / 1e9, 1)
+    return e
+
+
+def requant_sweep(fb, dev):
+    """The per-step re-quantization of every quantized linear weight of the
+    model: 36 layers x {qkv, o, gate_up, down} (6.95 G BF16 parameters),
+    four calls with batch = 36.  SWEEP_REPS timed sweeps (HIP events around
+    each) after two untimed ones; 21 GB per sweep, far past the Infinity
+    Cache, so no rotation is needed."""
+    import torch
+
+    from synthetic import LAYER_SHAPES_QWEN3_8B, device_bf16_normal
+
+    bufs, byt = [], 0
+    for p, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
+        w = device_bf16_normal((SWEEP_LAYERS, n, k), 0.02, seed=800 + p)
+        q = torch.empty((SWEEP_LAYERS, n, k), dtype=torch.uint8, device=dev)
+        s = torch.empty((SWEEP_LAYERS, n // 128, k // 128), dtype=torch.float32, device=dev)
+        bufs.append((name, w, q, s))
+        byt += SWEEP_LAYERS * n * k * 3 + s.numel() * 4
+
+    def run():
+        for _, w, q, s in bufs:
+            fb.quantize_weight_blockwise(w, q, s)
+
+    for _ in range(2):
+        run()
+    st = torch.cuda.current_stream()
+    evs = []
+    for _ in range(SWEEP_REPS):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        run()
+        b.record(st)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"ms": sum(t) / len(t), "median_ms": t[len(t) // 2], "min_ms": t[0], "reps": len(t), "bytes": byt,
+            "params": sum(w.numel() for _, w, _, _ in bufs), "tensors": bufs}
+
+
 # ---------------------------------------------------------------------------
-# Per-configuration measurements (after the timed region)
+# Timing helpers for the per-configuration measurements
 # ---------------------------------------------------------------------------
 
 def _time_ms(fn, reps, warm=2):
@@ -357,114 +435,166 @@ def _time_graph_ms(fn, calls=10, reps=5):
         return _time_ms(fns[0], reps=10)
 
 
-def detail(fb, dev):
+# ---------------------------------------------------------------------------
+# Per-configuration measurements (after the timed region)
+# ---------------------------------------------------------------------------
+
+def detail(fb, dev, with_cpu=True):
     import torch
 
-    from synthetic import LAYER_SHAPES_QWEN3_8B, MOE_QWEN3_30B_A3B, device_bf16_normal, moe_routing
-
     res = {}
-    # -- prefill GEMMs, M = 8192, activations with 1% outlier channels x30
-    m = 8192
-    pre = {}
-    tot_f = tot_ms = tot_fr_ms = 0.0
+    # -- the Qwen3-8B decode layer step (M = 256): re-quantize the layer's four
+    #    weights, quantize its four activations, four GEMMs
+    res["decode_layer_qwen3_8b_M256"] = decode_step(fb, dev, with_cpu)
+    torch.cuda.empty_cache()
+    # -- prefill GEMMs one by one, both activation layouts, rotated buffers
+    res["prefill_gemm_M8192"] = prefill_gemms(fb, dev)
+    torch.cuda.empty_cache()
+    # -- one MoE expert-FFN layer (Qwen3-30B-A3B: 4096 tokens, top-8 of 128
+    #    experts, hidden 2048, expert FFN 768), every step on the GPU
+    res["moe_layer_qwen3_30b_a3b"] = moe_layer(fb, dev)
+    torch.cuda.empty_cache()
+    # -- FP8 training operands (Qwen3-8B)
+    res["train_operands_qwen3_8b"] = train_operands(fb, dev)
+    torch.cuda.empty_cache()
+    # -- FP8 KV cache, one Qwen3-8B layer (8 KV heads x 128)
+    res["kv_cache_qwen3_8b_layer"] = kv_cache(fb, dev)
+    torch.cuda.empty_cache()
+    # -- token-level TIS weights of one training batch (512 responses padded
+    #    to 20,000 tokens), fused with the response mask and w * advantage
+    res["tis_weights_train_batch_512x20000"] = tis_weights(fb, dev)
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_step(fb, dev, with_cpu):
+    """The Qwen3-8B decode layer step at M = 256: one launch re-quantizes the
+    four weight matrices, one launch quantizes the four activations, then
+    the four GEMMs.  Steps cycle through four copies of the layer's buffers
+    (0.6 GB each).  Phases timed with HIP events; the oracle runs the same
+    step on the same input bytes (parity and a CPU time on all its threads)."""
+    import torch
+
+    from synthetic import LAYER_SHAPES_QWEN3_8B, device_bf16_normal
+
+    M, SETS, STEPS, WARM = 256, 4, 50, 5
+    sets = []
+    for c in range(SETS):
+        layers = []
+        for i, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
+            w = device_bf16_normal((n, k), 0.02, seed=100 + i) if c == 0 else sets[0][i]["w"].clone()
+            x = device_bf16_normal((M, k), 1.0, seed=200 + i) if c == 0 else sets[0][i]["x"].clone()
+            layers.append({
+                "name": name, "n": n, "k": k, "w": w, "x": x,
+                "wq": torch.empty((n, k), dtype=torch.uint8, device=dev),
+                "ws": torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev),
+                "xq": torch.empty((M, k), dtype=torch.uint8, device=dev),
+                "xs": torch.empty((M, k // 128), dtype=torch.float32, device=dev),
+                "y": torch.empty((M, n), dtype=torch.bfloat16, device=dev),
+            })
+        sets.append(layers)
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record, s):
+        ls = sets[s % SETS]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record(stream)
+        fb.quantize_weights_blockwise_multi([L["w"] for L in ls], [(L["wq"], L["ws"]) for L in ls])
+        if record:
+            e[1].record(stream)
+        fb.quantize_acts_per_token_group_multi([L["x"] for L in ls], [(L["xq"], L["xs"]) for L in ls])
+        if record:
+            e[2].record(stream)
+        for L in ls:
+            fb.gemm_w8a8_blockscaled(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
+        if record:
+            e[3].record(stream)
+            ev.append(e)
+
+    for s in range(WARM):
+        step(False, s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(STEPS):
+        step(True, s)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / STEPS
+    step(False, 0)
+    torch.cuda.synchronize()
+    layers = sets[0]
+    flops = sum(2 * M * L["n"] * L["k"] for L in layers)
+    rq_b = sum(L["n"] * L["k"] * 3 + L["ws"].numel() * 4 for L in layers)
+    aq_b = sum(M * L["k"] * 3 + L["xs"].numel() * 4 for L in layers)
+    gm_b = sum(M * L["k"] + L["n"] * L["k"] + 2 * M * L["n"] + L["xs"].numel() * 4 + L["ws"].numel() * 4
+               for L in layers)
+    ph = {p: sum(e[i].elapsed_time(e[i + 1]) for e in ev) / len(ev)
+          for i, p in enumerate(("requant", "act_quant", "gemm"))}
+    res = {"ms_per_step": round(ms, 4), "TFLOPs": round(flops / ms / 1e9, 1), "steps": STEPS, "buffer_sets": SETS,
+           "phase_us": {p: round(v * 1e3, 2) for p, v in ph.items()},
+           "requant": {"launches": 1, "bytes": rq_b, "GBps": round(rq_b / ph["requant"] / 1e6, 1),
+                       "frac_hbm": round(rq_b / ph["requant"] / 1e6 / HBM_PEAK_GBPS, 4)},
+           "act_quant": {"launches": 1, "bytes": aq_b, "GBps": round(aq_b / ph["act_quant"] / 1e6, 1)},
+           "gemm": {"launches": 4, "bytes": gm_b, "TFLOPs": round(flops / ph["gemm"] / 1e9, 1),
+                    "GBps": round(gm_b / ph["gemm"] / 1e6, 1),
+                    "frac_hbm": round(gm_b / ph["gemm"] / 1e6 / HBM_PEAK_GBPS, 4)}}
+    if with_cpu:
+        res["cpu_baseline"], res["parity"] = decode_cpu_and_parity(layers, M, flops)
+    return res
+
+
+def prefill_gemms(fb, dev):
+    """Each prefill GEMM (M = 8192) on its own, row-major and fragment-order
+    activations, timed from graph replays over enough buffer copies (input
+    codes, weights, output) that a copy has left the Infinity Cache before
+    it comes round again; the two layouts' outputs compared bit for bit."""
+    import torch
+
+    from synthetic import LAYER_SHAPES_QWEN3_8B, device_activations, device_bf16_normal
+
+    m = PREFILL_M
+    pre, tot_f, tot_ms, tot_fr_ms = {}, 0.0, 0.0, 0.0
     for i, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
-        w = device_bf16_normal((n, k), 0.02, seed=300 + i)
-        x = device_bf16_normal((m, k), 1.0, seed=400 + i)
-        g = torch.Generator().manual_seed(500 + i)
-        cols = torch.randperm(k, generator=g)[: round(0.01 * k)].to(dev)
-        x[:, cols] = (x[:, cols].float() * 30.0).to(torch.bfloat16)
-        wq, ws = fb.quantize_weight_blockwise(w)
+        wq, ws = fb.quantize_weight_blockwise(device_bf16_normal((n, k), 0.02, seed=300 + i))
+        x, _ = device_activations(m, k, seed=400 + 2 * i, outlier_frac=OUTLIER_FRAC, outlier_mult=OUTLIER_MULT)
         xq, xs = fb.quantize_act_per_token_group(x)
-        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        ms, ms_min = _time_graph_ms(lambda: fb.gemm_w8a8_blockscaled(xq, xs, wq, ws, y), calls=4)
-        # the same GEMM on fragment-order activation codes (same result bits)
         xf, _ = fb.quantize_act_per_token_group_frag(x)
-        fr_ms, _ = _time_graph_ms(lambda: fb.gemm_w8a8_blockscaled_afrag(xf, xs, wq, ws, y), calls=4)
-        del xf
-        sets = [(x, xq, xs)] + [(x.clone(), torch.empty_like(xq), torch.empty_like(xs))
-                                for _ in range(rotations(m * k * 3) - 1)]
-        aq_ms, _ = _time_graph_ms([lambda t=t: fb.quantize_act_per_token_group(*t) for t in sets])
-        aqf_ms, _ = _time_graph_ms([lambda t=t: fb.quantize_act_per_token_group_frag(*t) for t in sets])
-        del sets
+        nsets = rotations(m * k + n * k + 2 * m * n)
+        sets = [(xq, xf, xs, wq, ws, torch.empty((m, n), dtype=torch.bfloat16, device=dev))]
+        sets += [(xq.clone(), xf.clone(), xs.clone(), wq.clone(), ws.clone(),
+                  torch.empty((m, n), dtype=torch.bfloat16, device=dev)) for _ in range(nsets - 1)]
+        ms, _ = _time_graph_ms([lambda t=t: fb.gemm_w8a8_blockscaled(t[0], t[2], t[3], t[4], t[5]) for t in sets],
+                               calls=max(4, nsets))
+        y_row = sets[0][5].clone()
+        fr_ms, _ = _time_graph_ms([lambda t=t: fb.gemm_w8a8_blockscaled_afrag(t[1], t[2], t[3], t[4], t[5])
+                                   for t in sets], calls=max(4, nsets))
+        same = bool(torch.equal(y_row.view(torch.int16), sets[0][5].view(torch.int16)))
+        del sets, y_row
+        xsets = [(x, torch.empty_like(xq), torch.empty_like(xs))]
+        xsets += [(x.clone(), torch.empty_like(xq), torch.empty_like(xs)) for _ in range(rotations(m * k * 3) - 1)]
+        aq_ms, _ = _time_graph_ms([lambda t=t: fb.quantize_act_per_token_group(*t) for t in xsets])
+        aqf_ms, _ = _time_graph_ms([lambda t=t: fb.quantize_act_per_token_group_frag(*t) for t in xsets])
+        del xsets
         f = 2 * m * n * k
         tot_f += f
         tot_ms += ms
         tot_fr_ms += fr_ms
-        pre[name] = {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(f / ms / 1e9, 1),
+        aq_b = m * k * 3 + m * (k // 128) * 4
+        pre[name] = {"buffer_sets": nsets, "gemm_us": round(ms * 1e3, 1), "TFLOPs": round(f / ms / 1e9, 1),
                      "frac_fp8_peak": round(f / ms / 1e9 / FP8_PEAK_TFLOPS, 4),
                      "afrag_gemm_us": round(fr_ms * 1e3, 1), "afrag_TFLOPs": round(f / fr_ms / 1e9, 1),
                      "afrag_frac_fp8_peak": round(f / fr_ms / 1e9 / FP8_PEAK_TFLOPS, 4),
+                     "afrag_bit_identical": same,
                      "act_quant_us": round(aq_ms * 1e3, 1), "afrag_act_quant_us": round(aqf_ms * 1e3, 1),
-                     "act_quant_GBps": round((m * k * 3 + m * (k // 128) * 4) / aq_ms / 1e6, 1)}
-        del w, x, wq, ws, xq, xs, y
-    pre["all4"] = {"TFLOPs": round(tot_f / tot_ms / 1e9, 1), "frac_fp8_peak": round(tot_f / tot_ms / 1e9 / FP8_PEAK_TFLOPS, 4),
+                     "act_quant_GBps": round(aq_b / aq_ms / 1e6, 1), "afrag_act_quant_GBps": round(aq_b / aqf_ms / 1e6, 1)}
+        del wq, ws, x, xq, xs, xf
+        torch.cuda.empty_cache()
+    pre["all4"] = {"TFLOPs": round(tot_f / tot_ms / 1e9, 1),
+                   "frac_fp8_peak": round(tot_f / tot_ms / 1e9 / FP8_PEAK_TFLOPS, 4),
                    "afrag_TFLOPs": round(tot_f / tot_fr_ms / 1e9, 1),
                    "afrag_frac_fp8_peak": round(tot_f / tot_fr_ms / 1e9 / FP8_PEAK_TFLOPS, 4)}
-    res["prefill_gemm_M8192"] = pre
-    torch.cuda.empty_cache()
-
-    # -- one MoE expert-FFN layer (Qwen3-30B-A3B: 4096 tokens, top-8 of 128
-    #    experts, hidden 2048, expert FFN 768), every step on the GPU:
-    #    sort -> 1x128 quant of the tokens -> fc1 (rows gathered by routed pair)
-    #    -> SiLU*up + 1x128 quant -> fc2 -> combine
-    res["moe_layer_qwen3_30b_a3b"] = moe_layer(fb, dev)
-    torch.cuda.empty_cache()
-
-    # -- 36-layer re-quantization sweep (4 calls, batch = 36 each)
-    sweep_bytes = 0
-    bufs = []
-    for p, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
-        w = device_bf16_normal((36, n, k), 0.02, seed=800 + p)
-        q = torch.empty((36, n, k), dtype=torch.uint8, device=dev)
-        s = torch.empty((36, n // 128, k // 128), dtype=torch.float32, device=dev)
-        bufs.append((w, q, s))
-        sweep_bytes += 36 * n * k * 3 + s.numel() * 4
-
-    def sweep():
-        for w, q, s in bufs:
-            fb.quantize_weight_blockwise(w, q, s)
-
-    ms, ms_min = _time_ms(sweep, reps=5, warm=1)
-    gbps = sweep_bytes / ms / 1e6
-    res["requant_sweep_36_layers"] = {"params": sum(w.numel() for w, _, _ in bufs), "bytes": sweep_bytes,
-                                      "ms": round(ms, 3), "GBps": round(gbps, 1),
-                                      "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
-    del bufs
-    torch.cuda.empty_cache()
-
-    # -- FP8 training operands (Qwen3-8B): W and W^T of all 36 layers' four
-    #    projections, and x / x^T of an 8192-token micro-batch's layer inputs
-    res["train_operands_qwen3_8b"] = train_operands(fb, dev)
-    torch.cuda.empty_cache()
-
-    # -- FP8 KV cache, one Qwen3-8B layer (8 KV heads x 128): a rollout's first
-    #    forward calibrates the per-head scales on a 16384-token prefill chunk
-    #    and writes it to the cache; a decode step then writes 1536 tokens
-    res["kv_cache_qwen3_8b_layer"] = kv_cache(fb, dev)
-    torch.cuda.empty_cache()
-
-    # -- token-level TIS weights of one training batch (512 responses padded
-    #    to 20,000 tokens), fused with the response mask and w * advantage
-    from synthetic import ROLLOUT_TRAIN_BATCH, rollout_batch
-
-    rb = rollout_batch(ROLLOUT_TRAIN_BATCH["responses"], ROLLOUT_TRAIN_BATCH["max_len"], (31, 1))
-    lt, lr, adv = (torch.from_numpy(rb[k]).to(dev) for k in ("logp_train", "logp_rollout", "advantages"))
-    msk = torch.from_numpy(rb["mask"]).to(dev)
-    slots, valid = lt.numel(), int(rb["mask"].sum())
-    byt = importance_weight_bytes(slots, valid)
-    sets = [(t.clone() for t in (lt, lr, msk, adv)) for _ in range(rotations(21 * slots))]
-    sets = [tuple(g) + (torch.empty_like(lt), torch.empty_like(lt)) for g in sets]
-    ms, ms_min = _time_graph_ms([lambda t=t: fb.token_importance_weights(t[0], t[1], C=2.0, mode="tis", mask=t[2],
-                                                                         advantages=t[3], out=t[4], out_adv=t[5])
-                                 for t in sets])
-    del sets
-    gbps = byt / ms / 1e6
-    res["tis_weights_train_batch_512x20000"] = {"tokens": valid, "slots": slots, "bytes": byt,
-                                                "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
-                                                "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
-    del lt, lr, adv, msk
-    torch.cuda.empty_cache()
-    return res
+    return pre
 
 
 def moe_layer(fb, dev):
@@ -518,9 +648,8 @@ def moe_layer(fb, dev):
     res, total = {}, 0.0
     for name, (fn, byt, flops) in steps.items():
         ms, _ = _time_graph_ms(fn)
-        e_rot = len(fn)
         total += ms
-        e = {"us": round(ms * 1e3, 1), "buffer_sets": e_rot}
+        e = {"us": round(ms * 1e3, 1), "buffer_sets": len(fn)}
         if byt is not None:
             e.update({"bytes": byt, "GBps": round(byt / ms / 1e6, 1), "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)})
         if flops is not None:
@@ -561,7 +690,7 @@ def train_operands(fb, dev):
         for w in bufs:
             fb.quantize_weight_blockwise_dual(w)
 
-    ms, _ = _time_ms(sweep, reps=3, warm=1)
+    ms, _ = _time_ms(sweep, reps=5, warm=1)
     res["weight_dual_sweep_36_layers"] = {"bytes": wbytes, "ms": round(ms, 3), "GBps": round(wbytes / ms / 1e6, 1),
                                           "frac_hbm": round(wbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}
     del bufs
@@ -621,70 +750,219 @@ def importance_weight_bytes(slots, valid):
     return 12 * valid + 9 * slots
 
 
+def tis_weights(fb, dev):
+    import torch
+
+    from synthetic import ROLLOUT_TRAIN_BATCH, rollout_batch
+
+    rb = rollout_batch(ROLLOUT_TRAIN_BATCH["responses"], ROLLOUT_TRAIN_BATCH["max_len"], (31, 1))
+    lt, lr, adv = (torch.from_numpy(rb[k]).to(dev) for k in ("logp_train", "logp_rollout", "advantages"))
+    msk = torch.from_numpy(rb["mask"]).to(dev)
+    slots, valid = lt.numel(), int(rb["mask"].sum())
+    byt = importance_weight_bytes(slots, valid)
+    sets = [(t.clone() for t in (lt, lr, msk, adv)) for _ in range(rotations(21 * slots))]
+    sets = [tuple(g) + (torch.empty_like(lt), torch.empty_like(lt)) for g in sets]
+    ms, _ = _time_graph_ms([lambda t=t: fb.token_importance_weights(t[0], t[1], C=2.0, mode="tis", mask=t[2],
+                                                                    advantages=t[3], out=t[4], out_adv=t[5])
+                            for t in sets])
+    gbps = byt / ms / 1e6
+    return {"tokens": valid, "slots": slots, "bytes": byt, "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
+            "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 # ---------------------------------------------------------------------------
-# CPU oracle baseline on a bounded sample, with parity of that sample
+# CPU oracle: parity of the timed runs and the CPU baseline, on the host's
+# cores.  The oracle runs as it stands; the thread pool only splits it over
+# independent pieces (128-row blocks of a weight, row chunks of activations),
+# and its GEMM uses numpy's BLAS threads.
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(layers, m, gemm_flops, requant_bytes):
-    """Time the oracle on one whole decode-layer step and check the GPU's
-    results of the timed run against it.
+def _bits(t):
+    import torch
 
-    The oracle runs the same step on the same input bytes: re-quantization
-    of the four weight matrices (193M parameters, numpy), the four per-token
-    activation quantizations, and the four GEMMs through its float64 path
-    (BLAS matmul).  It is untuned test infrastructure; the figure is a
-    reported baseline, not a target.
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _pool_map(fn, items, threads):
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(fn, items))
+
+
+def _row_chunks(rows, step):
+    return [(r, min(rows, r + step)) for r in range(0, rows, step)]
+
+
+def oracle_quant_weight(w_bits, threads):
+    """oracle.quant_weight_blockwise of [N][K] BF16 bits, one 128-row block
+    row per task (blocks are independent)."""
+    from oracle import quant_weight_blockwise
+
+    res = _pool_map(lambda c: quant_weight_blockwise(w_bits[c[0]:c[1]]), _row_chunks(w_bits.shape[0], 128), threads)
+    return np.concatenate([q for q, _ in res]), np.concatenate([s for _, s in res])
+
+
+def oracle_quant_act(x_bits, threads):
+    """oracle.quant_act_per_token_group in row chunks (tokens are independent)."""
+    from oracle import quant_act_per_token_group
+
+    res = _pool_map(lambda c: quant_act_per_token_group(x_bits[c[0]:c[1]]), _row_chunks(x_bits.shape[0], 16), threads)
+    return np.concatenate([q for q, _ in res]), np.concatenate([s for _, s in res])
+
+
+def _r14(y_bits, y_ref):
+    """The 1e-2 acceptance of a GEMM output (relative Frobenius and worst
+    element against max(|ref|, rms(ref))), with the BF16-exact fraction."""
+    import oracle
+
+    yf = (y_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = np.asarray(y_ref, np.float64)
+    rel_fro = float(np.linalg.norm(yf - ref) / np.linalg.norm(ref))
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    rel_max = float(np.max(np.abs(yf - ref) / np.maximum(np.abs(ref), rms)))
+    exact = float(np.mean(y_bits == oracle.round_to_bf16_bits(ref)))
+    return {"rel_fro": round(rel_fro, 6), "rel_max": round(rel_max, 6), "exact_bf16_frac": round(exact, 4),
+            "pass": rel_fro <= 1e-2 and rel_max <= 1e-2}
+
+
+def cpu_baseline_and_parity(fb, layers, w_bf16, sweep, gemm_flops):
+    """Parity of the timed prefill step and of the re-quant sweep against the
+    oracle, and the oracle's time for the same work on the host's cores.
+
+    Prefill (the headline): per projection, 192 consecutive token rows (12
+    groups of 16, at a seeded offset) are quantized by the oracle (codes
+    compared bit for bit with the GPU's fragment-order codes after the
+    oracle's permutation, scales bit for bit) and multiplied by the
+    FP32-accumulated oracle GEMM with the oracle's own weight codes (which
+    are compared bit for bit with the GPU's).  The GPU rows meet R14
+    against it.  The oracle GEMM is timed at 64 and 192 rows; its time for
+    all 8192 rows is the linear fit (a fixed part that decodes the weights,
+    a per-row part), plus the per-row time of its activation quantizer.
+
+    Re-quant sweep: the oracle quantizes the last layer's four matrices
+    (batch index 35, byte offsets past 2^31 in the batched call) and layer 0
+    in full, bit for bit against the GPU; its rate on those 386 M
+    parameters gives the CPU time of the 36-layer sweep.
     """
     import torch
 
-    import oracle
-    from oracle import gemm_ref, quant_act_per_token_group, quant_weight_blockwise
+    from oracle import act_fragment_order, gemm_ref_fp32, quant_act_per_token_group
 
-    def bits(t):
-        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    threads = host_threads()
+    M = PREFILL_M
+    rng = np.random.default_rng(2024)
+    r0 = int(rng.integers(0, (M - 192) // 16)) * 16
+    par = {"prefill_qwen3_8b_layer": {"rows": [r0, r0 + 192], "weights_bitexact": True, "act_quant_bitexact": True,
+                                      "gemm": {}}}
+    pp = par["prefill_qwen3_8b_layer"]
+    t_aq = t_fix = t_row = 0.0
+    for L in layers:
+        n, k = L["n"], L["k"]
+        gq, gs = L["wq"].cpu().numpy(), L["ws"].cpu().numpy()
+        qw, sw = oracle_quant_weight(_bits(w_bf16[L["name"]]), threads)
+        pp["weights_bitexact"] &= bool(np.array_equal(gq, qw) and np.array_equal(gs.view(np.uint32), sw.view(np.uint32)))
+        xb = _bits(L["x"][r0:r0 + 192])
+        t = time.perf_counter()
+        qa, sa = quant_act_per_token_group(xb)
+        t_aq += (time.perf_counter() - t) / 192 * M
+        frag = L["xq"].view(-1)[r0 * k:(r0 + 192) * k].cpu().numpy().reshape(192, k)
+        pp["act_quant_bitexact"] &= bool(np.array_equal(frag, act_fragment_order(qa)) and np.array_equal(
+            L["xs"][r0:r0 + 192].cpu().numpy().view(np.uint32), sa.view(np.uint32)))
+        t = time.perf_counter()
+        gemm_ref_fp32(qa[:64], sa[:64], qw, sw)
+        t64 = time.perf_counter() - t
+        t = time.perf_counter()
+        ref = gemm_ref_fp32(qa, sa, qw, sw)
+        t192 = time.perf_counter() - t
+        per_row = max(0.0, (t192 - t64) / 128)
+        t_row += per_row * M
+        t_fix += max(0.0, t192 - 192 * per_row)
+        pp["gemm"][L["name"]] = _r14(_bits(L["y"][r0:r0 + 192]), ref)
+    pp["pass"] = pp["weights_bitexact"] and pp["act_quant_bitexact"] and all(g["pass"] for g in pp["gemm"].values())
+    prefill_s = t_aq + t_fix + t_row
 
-    host = [(bits(L["w"]), bits(L["x"])) for L in layers]
+    # re-quant sweep: layers 35 and 0 of every projection, in full
+    ps = {"layers_checked": [SWEEP_LAYERS - 1, 0], "bitexact": True}
+    t_rq, params = 0.0, 0
+    for name, w, q, s in sweep["tensors"]:
+        for layer in (SWEEP_LAYERS - 1, 0):
+            wb = _bits(w[layer])
+            t = time.perf_counter()
+            oq, os_ = oracle_quant_weight(wb, threads)
+            t_rq += time.perf_counter() - t
+            params += wb.size
+            ps["bitexact"] &= bool(np.array_equal(q[layer].cpu().numpy(), oq) and np.array_equal(
+                s[layer].cpu().numpy().view(np.uint32), os_.view(np.uint32)))
+    ps["pass"] = ps["bitexact"]
+    par["requant_sweep_36_layers"] = ps
+    sweep_s = t_rq * sweep["params"] / params
+    import threadpoolctl
+
+    blas = [i.get("num_threads") for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    base = {
+        "value": round(gemm_flops / prefill_s / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": ("prefill layer step: per projection 192 of the 8192 token rows (oracle act quant of those rows, "
+                   "its FP32-accumulated GEMM timed at 64 and 192 rows), extrapolated to 8192 rows by a linear fit; "
+                   "weights quantized beforehand as on the GPU; same input bytes as the GPU run"),
+        "legs": {
+            "prefill_layer_step": {"seconds_extrapolated": round(prefill_s, 3),
+                                   "act_quant_s": round(t_aq, 3), "gemm_fixed_s": round(t_fix, 3),
+                                   "gemm_rows_s": round(t_row, 3),
+                                   "TFLOPs": round(gemm_flops / prefill_s / 1e12, 6),
+                                   "threads": {"act_quant": 1, "gemm_blas": blas[0] if blas else None}},
+            "requant_sweep_36_layers": {"sample": "layers 35 and 0 of the four projections (386 M params), "
+                                                  "extrapolated to 6.95 G", "seconds_sample": round(t_rq, 3),
+                                        "seconds_extrapolated": round(sweep_s, 3),
+                                        "GBps": round(sweep["bytes"] / sweep_s / 1e9, 3),
+                                        "threads": threads},
+        },
+        "host": {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+                 "blas": [i.get("internal_api") for i in threadpoolctl.threadpool_info()
+                          if i.get("user_api") == "blas"]},
+    }
+    par["pass"] = pp["pass"] and ps["pass"]
+    return base, par
+
+
+def decode_cpu_and_parity(layers, m, flops):
+    """The oracle runs the whole decode step on the same input bytes: weight
+    re-quant (thread pool over block rows), act quant, FP32-accumulated GEMM
+    (BLAS threads); its outputs check the GPU's bit for bit (quantizers) and
+    by R14 (GEMMs)."""
+    from oracle import gemm_ref_fp32, quant_act_per_token_group
+
+    threads = host_threads()
+    host = [(_bits(L["w"]), _bits(L["x"])) for L in layers]
     t0 = time.perf_counter()
-    wres = [quant_weight_blockwise(w) for w, _ in host]
+    wres = [oracle_quant_weight(w, threads) for w, _ in host]
     t_rq = time.perf_counter() - t0
     t0 = time.perf_counter()
     ares = [quant_act_per_token_group(x) for _, x in host]
     t_aq = time.perf_counter() - t0
     t0 = time.perf_counter()
-    yres = [gemm_ref(qa, sa, qw, sw) for (qa, sa), (qw, sw) in zip(ares, wres)]
+    yres = [gemm_ref_fp32(qa, sa, qw, sw) for (qa, sa), (qw, sw) in zip(ares, wres)]
     t_gm = time.perf_counter() - t0
     total = t_rq + t_aq + t_gm
-    cores = len(os.sched_getaffinity(0))
-    base = {
-        "value": round(gemm_flops / total / 1e12, 6),
-        "unit": "TFLOP/s",
-        "cores": cores,
-        "kind": "oracle",
-        "sample": ("one full decode-layer step (4 weight re-quants, 193M params, numpy single-threaded; 4 activation "
-                   "quants; 4 GEMMs as float64 BLAS matmuls on %d threads), same input bytes as the GPU run" % cores),
-        "seconds": {"requant": round(t_rq, 3), "act_quant": round(t_aq, 3), "gemm": round(t_gm, 3)},
-        "requant_GBps": round(requant_bytes / t_rq / 1e9, 3),
-    }
-
+    base = {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "threads": threads, "kind": "oracle",
+            "sample": "the whole decode layer step, same input bytes",
+            "seconds": {"requant": round(t_rq, 3), "act_quant": round(t_aq, 3), "gemm": round(t_gm, 3)}}
     par = {"requant_bitexact": True, "act_quant_bitexact": True, "gemm": {}}
     for L, (qw, sw), (qa, sa), y_ref in zip(layers, wres, ares, yres):
         par["requant_bitexact"] &= bool(np.array_equal(L["wq"].cpu().numpy(), qw) and np.array_equal(
             L["ws"].cpu().numpy().view(np.uint32), sw.view(np.uint32)))
         par["act_quant_bitexact"] &= bool(np.array_equal(L["xq"].cpu().numpy(), qa) and np.array_equal(
             L["xs"].cpu().numpy().view(np.uint32), sa.view(np.uint32)))
-        y = L["y"].view(torch.int16).cpu().numpy().view(np.uint16)
-        yf = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        rel_fro = float(np.linalg.norm(yf - y_ref) / np.linalg.norm(y_ref))
-        rms = float(np.sqrt(np.mean(y_ref ** 2)))
-        rel_max = float(np.max(np.abs(yf - y_ref) / np.maximum(np.abs(y_ref), rms)))
-        exact = float(np.mean(y == oracle.round_to_bf16_bits(y_ref)))
-        par["gemm"][L["name"]] = {"rel_fro": round(rel_fro, 6), "rel_max": round(rel_max, 6),
-                                  "exact_bf16_frac": round(exact, 4), "pass": rel_fro <= 1e-2 and rel_max <= 1e-2}
+        par["gemm"][L["name"]] = _r14(_bits(L["y"]), y_ref)
+    par["pass"] = par["requant_bitexact"] and par["act_quant_bitexact"] and all(g["pass"] for g in par["gemm"].values())
     return base, par
 
 
 # ---------------------------------------------------------------------------
-# rocprofv3 summary (kernel trace + HBM byte counters)
+# rocprofv3 summary of this benchmark (kernel trace + HBM byte counters)
 # ---------------------------------------------------------------------------
 
 def _csv_rows(pattern):
@@ -710,25 +988,32 @@ def _short(kernel_name):
 
 def _phase_of(kernel_name):
     for p, (prefix, _) in PHASE_KERNELS.items():
-        if prefix in kernel_name:
+        if prefix in kernel_name and not (p == "requant" and "quant_weight_multi" in kernel_name):
             return p
     return None
 
 
-def step_algorithmic_bytes(M=256):
-    """Average algorithmic HBM bytes per launch of each phase of the decode step."""
+def step_algorithmic_bytes():
+    """Average algorithmic HBM bytes per launch of each measured phase."""
     sys.path.insert(0, ROOT)
     from synthetic import LAYER_SHAPES_QWEN3_8B
 
-    rq = aq = gm = 0
+    M = PREFILL_M
+    aq = gm = rq = 0
     for _, n, k in LAYER_SHAPES_QWEN3_8B:
         ws = (n // 128) * (k // 128) * 4
         xs = M * (k // 128) * 4
-        rq += n * k * 3 + ws
         aq += M * k * 3 + xs
         gm += M * k + n * k + 2 * M * n + xs + ws
-    return {"requant": rq / PHASE_LAUNCHES["requant"], "act_quant": aq / PHASE_LAUNCHES["act_quant"],
-            "gemm": gm / PHASE_LAUNCHES["gemm"]}
+        rq += SWEEP_LAYERS * (n * k * 3 + ws)
+    return {"act_quant": aq / PHASE_LAUNCHES["act_quant"], "gemm": gm / PHASE_LAUNCHES["gemm"],
+            "requant": rq / PHASE_LAUNCHES["requant"]}
+
+
+def _copy_scale(d, sub, counter):
+    v = [float(r["Counter_Value"]) * 1024.0 for r in _csv_rows(os.path.join(d, sub, "**", "*counter_collection.csv"))
+         if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+    return float(1 << 30) / (sum(v) / len(v)) if v else None
 
 
 def rocprof_summary(d):
@@ -756,11 +1041,8 @@ def rocprof_summary(d):
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
         return vals
 
-    copy_bytes = float(1 << 30)
-    scale = {}
-    for sub, counter in (("copy_fetch", "FETCH_SIZE"), ("copy_write", "WRITE_SIZE")):
-        v = [x for name, xs in per_dispatch(sub, counter).items() if "copyBuffer" in name for x in xs]
-        scale[counter] = copy_bytes / (sum(v) / len(v)) if v else None
+    scale = {"FETCH_SIZE": _copy_scale(d, "copy_fetch", "FETCH_SIZE"),
+             "WRITE_SIZE": _copy_scale(d, "copy_write", "WRITE_SIZE")}
     lines.append("")
     lines.append("Copy calibration (1 GiB read + 1 GiB written per launch): FETCH_SIZE scale %s, "
                  "WRITE_SIZE scale %s." % tuple("%.3f" % scale[c] if scale[c] else "n/a"
@@ -787,7 +1069,7 @@ def rocprof_summary(d):
            for p, t in traffic.items()}
     algo = step_algorithmic_bytes()
     lines.append("")
-    lines.append("| phase (decode step) | measured HBM bytes / launch (MB) | algorithmic bytes / launch (MB) | ratio |")
+    lines.append("| phase | measured HBM bytes / launch (MB) | algorithmic bytes / launch (MB) | ratio |")
     lines.append("|---|---|---|---|")
     for p, v in sorted(out.items()):
         a = algo[p]
@@ -866,7 +1148,7 @@ def gemm_counter_summary(d):
       wave   SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS
              SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_ANY
       ta     TA_BUSY_avr GRBM_GUI_ACTIVE
-      fetch / write, copy_fetch / copy_write   as for the decode-step summary
+      fetch / write, copy_fetch / copy_write   as for the benchmark summary
     MOPS_F8 counts FP8 MFMA work in units of 512 FLOPs (it equals 2MNK on
     dense shapes).  GRBM_GUI_ACTIVE reads 8 x the kernel's cycles (it sums
     over the 8 XCDs: / 8 / duration gives 2.0-2.2 GHz on the long prefill
@@ -902,12 +1184,8 @@ def gemm_counter_summary(d):
             vals.append(sum(xs) / len(xs) if xs else None)
         return vals
 
-    copy = {}
-    for sub, counter in (("copy_fetch", "FETCH_SIZE"), ("copy_write", "WRITE_SIZE")):
-        v = [float(r["Counter_Value"]) * 1024.0
-             for r in _csv_rows(os.path.join(d, sub, "**", "*counter_collection.csv"))
-             if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
-        copy[counter] = float(1 << 30) / (sum(v) / len(v)) if v else None
+    copy = {"FETCH_SIZE": _copy_scale(d, "copy_fetch", "FETCH_SIZE"),
+            "WRITE_SIZE": _copy_scale(d, "copy_write", "WRITE_SIZE")}
     ns = per_case(kt, "ns")
     mops = per_case(passes["mfma"], "SQ_INSTS_VALU_MFMA_MOPS_F8")
     busy = per_case(passes["mfma"], "SQ_VALU_MFMA_BUSY_CYCLES")
@@ -963,6 +1241,212 @@ def gemm_counter_summary(d):
         cells = [f(wv[col][c] / wc[c] if wv[col][c] is not None and wc[c] else None, "%.3f") for col in wave_cols]
         tb = ta[c] / (ta_grbm[c] / 8.0) if ta[c] is not None and ta_grbm[c] else None
         lines.append("| %s | %s | %s |" % (label, " | ".join(cells), f(tb, "%.3f")))
+    print("\n".join(lines))
+
+
+# ---------------------------------------------------------------------------
+# Bandwidth-bound kernels: each runs BW_PROFILE_REPS times on its
+# configuration's shape, in the order of bw_profile_cases(); the summary
+# matches dispatches to cases by that order and compares the HBM bytes the
+# counters measure with the algorithmic bytes of each case.
+# ---------------------------------------------------------------------------
+
+BW_PROFILE_REPS = 3
+
+
+def bw_profile_cases():
+    """(label, kernel-name prefix, algorithmic bytes per launch) in launch order."""
+    sys.path.insert(0, ROOT)
+    from synthetic import LAYER_SHAPES_QWEN3_8B, MOE_QWEN3_30B_A3B
+
+    cases = []
+    for nm, n, k in LAYER_SHAPES_QWEN3_8B:  # 36-layer sweep: one call per projection
+        cases.append(("requant sweep %s (batch 36)" % nm, "quant_weight_kernel",
+                      SWEEP_LAYERS * (n * k * 3 + (n // 128) * (k // 128) * 4)))
+    for k in (4096, 12288):
+        ab = PREFILL_M * k * 3 + PREFILL_M * (k // 128) * 4
+        cases.append(("prefill act quant 8192x%d" % k, "quant_act_kernel", ab))
+        cases.append(("prefill act quant frag 8192x%d" % k, "quant_act_frag_kernel", ab))
+    cases.append(("decode act quant, 4 activations (one launch)", "quant_act_multi_kernel",
+                  sum(256 * k * 3 + 256 * (k // 128) * 4 for _, _, k in LAYER_SHAPES_QWEN3_8B)))
+    cases.append(("decode requant, 4 matrices (one launch)", "quant_weight_multi_kernel",
+                  sum(n * k * 3 + (n // 128) * (k // 128) * 4 for _, n, k in LAYER_SHAPES_QWEN3_8B)))
+    moe = MOE_QWEN3_30B_A3B
+    T, k, H, F = moe["tokens"], moe["top_k"], moe["hidden"], moe["ffn"]
+    R = T * k
+    cases.append(("MoE token act quant 4096x2048", "quant_act_kernel", T * H * 3 + T * (H // 128) * 4))
+    cases.append(("MoE SiLU*up quant 32768x768", "silu_mul_quant_kernel", R * 2 * F * 2 + R * F + R * (F // 128) * 4))
+    cases.append(("MoE combine 4096x2048 (top-8)", "combine_kernel", R * H * 2 + R * 8 + T * H * 2))
+    Tk, Hk, D = 16384, 8, 128
+    cases.append(("KV calibrate 16384 tokens", "kv_amax_kernel", 2 * Tk * Hk * D * 2))
+    cases.append(("KV write 16384 tokens", "kv_write_kernel", 2 * Tk * Hk * D * 3 + Tk * 4))
+    cases.append(("TIS weights 512x20000", "importance_weight_kernel", None))
+    cases.append(("W/W^T dual quant gate_up (batch 36)", "dual_quant_kernel",
+                  SWEEP_LAYERS * (24576 * 4096 * 4 + 2 * (24576 // 128) * (4096 // 128) * 4)))
+    cases.append(("x/x^T dual quant 8192x4096", "dual_quant_kernel",
+                  PREFILL_M * 4096 * 4 + PREFILL_M * 32 * 4 + 4096 * (PREFILL_M // 128) * 4))
+    return cases
+
+
+def bw_profile():
+    """Run each bandwidth-bound case BW_PROFILE_REPS times (freshly generated inputs)."""
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import fp8_blockwise_quantized_quantize_amd as fb
+    from synthetic import (LAYER_SHAPES_QWEN3_8B, MOE_QWEN3_30B_A3B, ROLLOUT_TRAIN_BATCH, device_bf16_normal,
+                           moe_topk, rollout_batch)
+
+    dev = torch.device("cuda:0")
+    R = BW_PROFILE_REPS
+
+    def done(label):
+        torch.cuda.synchronize()
+        print("bw profile case done:", label, flush=True)
+        torch.cuda.empty_cache()
+
+    for p, (nm, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
+        w = device_bf16_normal((SWEEP_LAYERS, n, k), 0.02, seed=800 + p)
+        q = torch.empty((SWEEP_LAYERS, n, k), dtype=torch.uint8, device=dev)
+        s = torch.empty((SWEEP_LAYERS, n // 128, k // 128), dtype=torch.float32, device=dev)
+        for _ in range(R):
+            fb.quantize_weight_blockwise(w, q, s)
+        del w, q, s
+        done("requant sweep " + nm)
+    for k in (4096, 12288):
+        x = device_bf16_normal((PREFILL_M, k), 1.0, seed=960 + k)
+        q = torch.empty((PREFILL_M, k), dtype=torch.uint8, device=dev)
+        s = torch.empty((PREFILL_M, k // 128), dtype=torch.float32, device=dev)
+        for _ in range(R):
+            fb.quantize_act_per_token_group(x, q, s)
+        torch.cuda.synchronize()
+        for _ in range(R):
+            fb.quantize_act_per_token_group_frag(x, q, s)
+        del x, q, s
+        done("prefill act quant %d" % k)
+    xs = [device_bf16_normal((256, k), 1.0, seed=200 + i) for i, (_, _, k) in enumerate(LAYER_SHAPES_QWEN3_8B)]
+    for _ in range(R):
+        fb.quantize_acts_per_token_group_multi(xs)
+    ws = [device_bf16_normal((n, k), 0.02, seed=100 + i) for i, (_, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B)]
+    torch.cuda.synchronize()
+    for _ in range(R):
+        fb.quantize_weights_blockwise_multi(ws)
+    del xs, ws
+    done("decode multi")
+    moe = MOE_QWEN3_30B_A3B
+    T, E, k, H, F = moe["tokens"], moe["experts"], moe["top_k"], moe["hidden"], moe["ffn"]
+    x = device_bf16_normal((T, H), 1.0, seed=700)
+    for _ in range(R):
+        fb.quantize_act_per_token_group(x)
+    y1 = device_bf16_normal((T * k, 2 * F), 1.0, seed=701)
+    torch.cuda.synchronize()
+    for _ in range(R):
+        fb.silu_mul_quantize_act(y1)
+    ids_h, tw_h = moe_topk(T, E, k, (70, 0))
+    ids, tw = torch.from_numpy(ids_h).to(dev), torch.from_numpy(tw_h).to(dev)
+    _, _, pr = fb.moe_sort_by_expert(ids, E)
+    y2 = device_bf16_normal((T * k, H), 1.0, seed=702)
+    torch.cuda.synchronize()
+    for _ in range(R):
+        fb.moe_combine(y2, pr, tw)
+    del x, y1, y2
+    done("moe glue")
+    Tk, Hk, D = 16384, 8, 128
+    kk = device_bf16_normal((Tk, Hk, D), 1.0, seed=900)
+    vv = device_bf16_normal((Tk, Hk, D), 1.0, seed=901)
+    ks = torch.empty(Hk, dtype=torch.float32, device=dev)
+    vs = torch.empty(Hk, dtype=torch.float32, device=dev)
+    kc = torch.empty((Tk, Hk, D), dtype=torch.uint8, device=dev)
+    vc = torch.empty((Tk, Hk, D), dtype=torch.uint8, device=dev)
+    slots = torch.arange(Tk, dtype=torch.int32, device=dev)
+    for _ in range(R):
+        fb.kv_scale_calibrate(kk, vv, True, ks, vs)
+    torch.cuda.synchronize()
+    for _ in range(R):
+        fb.kv_cache_write_fp8(kk, vv, slots, ks, vs, kc, vc)
+    del kk, vv, kc, vc
+    done("kv")
+    rb = rollout_batch(ROLLOUT_TRAIN_BATCH["responses"], ROLLOUT_TRAIN_BATCH["max_len"], (31, 1))
+    lt, lr, adv = (torch.from_numpy(rb[key]).to(dev) for key in ("logp_train", "logp_rollout", "advantages"))
+    msk = torch.from_numpy(rb["mask"]).to(dev)
+    for _ in range(R):
+        fb.token_importance_weights(lt, lr, C=2.0, mode="tis", mask=msk, advantages=adv)
+    del lt, lr, adv, msk
+    done("tis")
+    w = device_bf16_normal((SWEEP_LAYERS, 24576, 4096), 0.02, seed=952)
+    for _ in range(R):
+        fb.quantize_weight_blockwise_dual(w)
+    del w
+    torch.cuda.synchronize()
+    x = device_bf16_normal((PREFILL_M, 4096), 1.0, seed=960 + 4096)
+    for _ in range(R):
+        fb.quantize_act_dual(x)
+    del x
+    done("dual")
+
+
+def bw_counter_summary(d):
+    """Markdown table of the --bw-profile passes under `d` (kt, fetch, write,
+    copy_fetch, copy_write): per case, the kernel's average duration, the HBM
+    bytes per launch from FETCH_SIZE / WRITE_SIZE (copy-calibrated), the
+    algorithmic bytes and their ratio, and the achieved fraction of 8 TB/s.
+    Dispatches of the library's own kernels are matched to the cases in
+    launch order (helper kernels such as the KV scale init are skipped)."""
+    sys.path.insert(0, ROOT)
+    from synthetic import ROLLOUT_TRAIN_BATCH, rollout_batch
+
+    cases = bw_profile_cases()
+    prefixes = {c[1] for c in cases}
+
+    def ours(name):
+        return any(re.search(r"\b%s\b" % re.escape(p), _short(name)) for p in prefixes)
+
+    def dispatches(sub, key):
+        out = {}
+        pattern = "*kernel_trace.csv" if sub == "kt" else "*counter_collection.csv"
+        for r in _csv_rows(os.path.join(d, sub, "**", pattern)):
+            if ours(r["Kernel_Name"]):
+                out.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]}).update(key(r))
+        return [out[i] for i in sorted(out)]
+
+    kt = dispatches("kt", lambda r: {"ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+    fetch = dispatches("fetch", lambda r: {r["Counter_Name"]: float(r["Counter_Value"])})
+    write = dispatches("write", lambda r: {r["Counter_Name"]: float(r["Counter_Value"])})
+    scale = {"FETCH_SIZE": _copy_scale(d, "copy_fetch", "FETCH_SIZE"),
+             "WRITE_SIZE": _copy_scale(d, "copy_write", "WRITE_SIZE")}
+    rb = rollout_batch(ROLLOUT_TRAIN_BATCH["responses"], ROLLOUT_TRAIN_BATCH["max_len"], (31, 1))
+    tis_bytes = importance_weight_bytes(rb["mask"].size, int(rb["mask"].sum()))
+    n_expected = len(cases) * BW_PROFILE_REPS
+    lines = ["Dispatches matched: kernel trace %d, fetch %d, write %d (expected %d).  Copy calibration: "
+             "FETCH_SIZE x%s, WRITE_SIZE x%s." % (len(kt), len(fetch), len(write), n_expected,
+                                                  "%.3f" % scale["FETCH_SIZE"] if scale["FETCH_SIZE"] else "n/a",
+                                                  "%.3f" % scale["WRITE_SIZE"] if scale["WRITE_SIZE"] else "n/a"), "",
+             "| case | kernel | us | HBM read / launch (MB) | HBM write / launch (MB) | measured / algorithmic MB "
+             "| ratio | achieved GB/s (algorithmic) | frac of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
+
+    def avg(disp, c, key):
+        if len(disp) != n_expected:
+            return None
+        xs = [x.get(key) for x in disp[c * BW_PROFILE_REPS:(c + 1) * BW_PROFILE_REPS]]
+        xs = [x for x in xs if x is not None]
+        return sum(xs) / len(xs) if xs else None
+
+    for c, (label, prefix, algo) in enumerate(cases):
+        algo = tis_bytes if algo is None else algo
+        ns = avg(kt, c, "ns")
+        fr = avg(fetch, c, "FETCH_SIZE")
+        wr = avg(write, c, "WRITE_SIZE")
+        name = _short(kt[c * BW_PROFILE_REPS]["name"]) if len(kt) == n_expected else "?"
+        fb_ = fr * 1024.0 * scale["FETCH_SIZE"] if fr is not None and scale["FETCH_SIZE"] else None
+        wb_ = wr * 1024.0 * scale["WRITE_SIZE"] if wr is not None and scale["WRITE_SIZE"] else None
+        meas = fb_ + wb_ if fb_ is not None and wb_ is not None else None
+        gbps = algo / ns if ns else None
+        lines.append("| %s | `%s` | %s | %s | %s | %s | %s | %s | %s |" % (
+            label, name[:70], "%.1f" % (ns / 1e3) if ns else "n/a",
+            "%.1f" % (fb_ / 1e6) if fb_ is not None else "n/a", "%.1f" % (wb_ / 1e6) if wb_ is not None else "n/a",
+            "%.1f / %.1f" % (meas / 1e6, algo / 1e6) if meas is not None else "n/a / %.1f" % (algo / 1e6),
+            "%.3f" % (meas / algo) if meas is not None else "n/a", "%.0f" % gbps if gbps else "n/a",
+            "%.3f" % (gbps / HBM_PEAK_GBPS) if gbps else "n/a"))
     print("\n".join(lines))
 
 

@@ -27,11 +27,14 @@ __all__ = [
     "quantize_weight_blockwise",
     "quantize_weights_blockwise_multi",
     "quantize_act_per_token_group",
+    "quantize_acts_per_token_group_multi",
     "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
     "gemm_w8a8_blockscaled_afrag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
+    "check_group_offsets",
+    "TILES",
     "encode_e4m3",
     "token_importance_weights",
     "moe_sort_by_expert",
@@ -55,11 +58,15 @@ EXPORTS = (
     "quantize_weight_blockwise",
     "quantize_weights_blockwise_multi",
     "quantize_act_per_token_group",
+    "quantize_acts_per_token_group_multi",
     "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
     "gemm_w8a8_blockscaled_afrag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
+    "gemm_w8a8_blockscaled_tile",
+    "grouped_gemm_w8a8_blockscaled_tile",
+    "fp8bq_check_group_offsets",
     "fp8bq_encode_e4m3",
     "token_importance_weights",
     "moe_sort_by_expert",
@@ -78,11 +85,17 @@ class FP8BQError(RuntimeError):
 
 
 MAX_WEIGHT_DESCS = 48  # FP8BQ_MAX_WEIGHT_DESCS
+MAX_ACT_DESCS = 16  # FP8BQ_MAX_ACT_DESCS
 
 
 class _WeightDesc(ctypes.Structure):
     _fields_ = [("w_bf16", ctypes.c_void_p), ("w_fp8", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class _ActDesc(ctypes.Structure):
+    _fields_ = [("x_bf16", ctypes.c_void_p), ("x_fp8", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 def _load():
@@ -96,11 +109,15 @@ def _load():
     lib.quantize_weight_blockwise.argtypes = [p, p, p, i64, i64, i64, p]
     lib.quantize_act_per_token_group.argtypes = [p, p, p, i64, i64, p]
     lib.quantize_weights_blockwise_multi.argtypes = [ctypes.POINTER(_WeightDesc), i64, p]
+    lib.quantize_acts_per_token_group_multi.argtypes = [ctypes.POINTER(_ActDesc), i64, p]
     lib.gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.quantize_act_per_token_group_frag.argtypes = [p, p, p, i64, i64, p]
     lib.gemm_w8a8_blockscaled_afrag.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled_gather.argtypes = [p, p, i64, p, i64, p, p, p, p, i64, i64, i64, i64, p]
+    lib.gemm_w8a8_blockscaled_tile.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
+    lib.grouped_gemm_w8a8_blockscaled_tile.argtypes = [p, p, i64, p, i64, p, p, p, p, i64, i64, i64, i64, i32, p]
+    lib.fp8bq_check_group_offsets.argtypes = [p, i64, i64, p]
     lib.fp8bq_encode_e4m3.argtypes = [p, p, i64, i32, p]
     lib.token_importance_weights.argtypes = [p, p, p, p, p, p, i64, ctypes.c_float, i32, p]
     lib.moe_sort_by_expert.argtypes = [p, i64, i64, i64, p, p, p, p]
@@ -162,6 +179,20 @@ _U8 = (torch.uint8, torch.float8_e4m3fn)
 
 def _cdiv(a, b):
     return -(-a // b)
+
+
+# Tile kernels of the GEMMs by name (FP8BQ_TILE_* of the C ABI), for tests
+# and diagnostics; None (or "auto") is the library's own choice.
+TILES = {"auto": 0, "skinny64": 1, "skinny48": 2, "wide": 3, "decode_panel": 4, "deep": 5, "panel192": 6,
+         "deep_persistent": 7}
+
+
+def _tile_id(tile):
+    if tile is None:
+        return 0
+    if tile not in TILES:
+        raise ValueError(f"unknown tile {tile!r}; one of {sorted(TILES)}")
+    return TILES[tile]
 
 
 def quantize_weight_blockwise(w, out=None, scale=None):
@@ -233,6 +264,38 @@ def quantize_act_per_token_group(x, out=None, scale=None):
     return out, scale
 
 
+def quantize_acts_per_token_group_multi(xs, outs=None):
+    """Several BF16 activations [M, K] (any shapes) in one launch -> list of
+    (codes, scales), each exactly what quantize_act_per_token_group gives it.
+    ``outs``: optional list of (codes, scales) to fill."""
+    xs = list(xs)
+    if len(xs) > MAX_ACT_DESCS:
+        raise ValueError(f"at most {MAX_ACT_DESCS} activations per call")
+    if not xs:
+        return []
+    dev = xs[0].device
+    res = []
+    descs = (_ActDesc * len(xs))()
+    for i, x in enumerate(xs):
+        if x.dim() != 2:
+            raise ValueError("each activation must be [M, K]")
+        m, k = x.shape
+        _require(x, f"x[{i}]", _BF16, (m, k), dev)
+        if outs is None:
+            q = torch.empty((m, k), dtype=torch.uint8, device=dev)
+            s = torch.empty((m, _cdiv(k, BLOCK)), dtype=torch.float32, device=dev)
+        else:
+            q, s = outs[i]
+        _require(q, f"out[{i}]", _U8, (m, k), dev)
+        _require(s, f"scale[{i}]", torch.float32, (m, _cdiv(k, BLOCK)), dev)
+        descs[i] = _ActDesc(_ptr(_u16(x)).value, _ptr(q).value, _ptr(s).value, m, k)
+        res.append((q, s))
+    with torch.cuda.device(dev):
+        _check("quantize_acts_per_token_group_multi",
+               _lib.quantize_acts_per_token_group_multi(descs, len(xs), _stream(xs[0])))
+    return res
+
+
 def quantize_act_per_token_group_frag(x, out=None, scale=None):
     """BF16 activations [M, K] (M % 16 == 0, K % 128 == 0) -> (E4M3 codes uint8 [M, K] in the MFMA
     fragment order of gemm_w8a8_blockscaled_afrag; float32 scales [M, K/128])."""
@@ -274,8 +337,11 @@ def gemm_w8a8_blockscaled_afrag(a_frag, a_scale, w, w_scale, out=None):
     return out
 
 
-def gemm_w8a8_blockscaled(a, a_scale, w, w_scale, out=None):
-    """y[M, N] (bfloat16) = dequant(a) @ dequant(w).T with FP32 accumulation."""
+def gemm_w8a8_blockscaled(a, a_scale, w, w_scale, out=None, tile=None):
+    """y[M, N] (bfloat16) = dequant(a) @ dequant(w).T with FP32 accumulation.
+
+    ``tile`` (a name of TILES) runs that tile kernel instead of the library's
+    choice (gemm_w8a8_blockscaled_tile)."""
     m, k = a.shape
     n = w.shape[0]
     _require(a, "a", _U8, (m, k))
@@ -289,14 +355,20 @@ def gemm_w8a8_blockscaled(a, a_scale, w, w_scale, out=None):
         out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     _require(out, "out", _BF16, (m, n), dev)
     with torch.cuda.device(dev):
-        _check("gemm_w8a8_blockscaled",
-               _lib.gemm_w8a8_blockscaled(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)), m, n, k,
-                                          _stream(a)))
+        if tile is None:
+            _check("gemm_w8a8_blockscaled",
+                   _lib.gemm_w8a8_blockscaled(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)), m, n,
+                                              k, _stream(a)))
+        else:
+            _check("gemm_w8a8_blockscaled_tile",
+                   _lib.gemm_w8a8_blockscaled_tile(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)), m,
+                                                   n, k, _tile_id(tile), _stream(a)))
     return out
 
 
-def grouped_gemm_w8a8_blockscaled(a, a_scale, w, w_scale, group_offsets, out=None):
-    """Rows [off[e], off[e+1]) of a use expert e's weights w[e]; returns bfloat16 [M_total, N]."""
+def grouped_gemm_w8a8_blockscaled(a, a_scale, w, w_scale, group_offsets, out=None, tile=None):
+    """Rows [off[e], off[e+1]) of a use expert e's weights w[e]; returns bfloat16 [M_total, N].
+    ``tile``: a grouped tile kernel of TILES (grouped_gemm_w8a8_blockscaled_tile)."""
     m, k = a.shape
     g, n, _ = w.shape
     _require(a, "a", _U8, (m, k))
@@ -311,15 +383,23 @@ def grouped_gemm_w8a8_blockscaled(a, a_scale, w, w_scale, group_offsets, out=Non
         out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     _require(out, "out", _BF16, (m, n), dev)
     with torch.cuda.device(dev):
-        _check("grouped_gemm_w8a8_blockscaled",
-               _lib.grouped_gemm_w8a8_blockscaled(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale),
-                                                  _ptr(group_offsets), _ptr(_u16(out)), m, n, k, g, _stream(a)))
+        if tile is None:
+            _check("grouped_gemm_w8a8_blockscaled",
+                   _lib.grouped_gemm_w8a8_blockscaled(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale),
+                                                      _ptr(group_offsets), _ptr(_u16(out)), m, n, k, g, _stream(a)))
+        else:
+            _check("grouped_gemm_w8a8_blockscaled_tile",
+                   _lib.grouped_gemm_w8a8_blockscaled_tile(_ptr(a), _ptr(a_scale), m, None, 1, _ptr(w), _ptr(w_scale),
+                                                           _ptr(group_offsets), _ptr(_u16(out)), m, n, k, g,
+                                                           _tile_id(tile), _stream(a)))
     return out
 
 
-def grouped_gemm_w8a8_blockscaled_gather(a, a_scale, a_rows, a_row_div, w, w_scale, group_offsets, out=None):
+def grouped_gemm_w8a8_blockscaled_gather(a, a_scale, a_rows, a_row_div, w, w_scale, group_offsets, out=None,
+                                         tile=None):
     """Output row m uses row a_rows[m] // a_row_div of a [M_a, K] and expert e's
-    weights for m in [off[e], off[e+1]); returns bfloat16 [len(a_rows), N]."""
+    weights for m in [off[e], off[e+1]); returns bfloat16 [len(a_rows), N].
+    ``tile``: a grouped tile kernel of TILES (grouped_gemm_w8a8_blockscaled_tile)."""
     m_a, k = a.shape
     g, n, _ = w.shape
     _require(a, "a", _U8, (m_a, k))
@@ -336,11 +416,29 @@ def grouped_gemm_w8a8_blockscaled_gather(a, a_scale, a_rows, a_row_div, w, w_sca
         out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     _require(out, "out", _BF16, (m, n), dev)
     with torch.cuda.device(dev):
-        _check("grouped_gemm_w8a8_blockscaled_gather",
-               _lib.grouped_gemm_w8a8_blockscaled_gather(_ptr(a), _ptr(a_scale), m_a, _ptr(a_rows), int(a_row_div),
-                                                         _ptr(w), _ptr(w_scale), _ptr(group_offsets),
-                                                         _ptr(_u16(out)), m, n, k, g, _stream(a)))
+        if tile is None:
+            _check("grouped_gemm_w8a8_blockscaled_gather",
+                   _lib.grouped_gemm_w8a8_blockscaled_gather(_ptr(a), _ptr(a_scale), m_a, _ptr(a_rows),
+                                                             int(a_row_div), _ptr(w), _ptr(w_scale),
+                                                             _ptr(group_offsets), _ptr(_u16(out)), m, n, k, g,
+                                                             _stream(a)))
+        else:
+            _check("grouped_gemm_w8a8_blockscaled_tile",
+                   _lib.grouped_gemm_w8a8_blockscaled_tile(_ptr(a), _ptr(a_scale), m_a, _ptr(a_rows), int(a_row_div),
+                                                           _ptr(w), _ptr(w_scale), _ptr(group_offsets),
+                                                           _ptr(_u16(out)), m, n, k, g, _tile_id(tile), _stream(a)))
     return out
+
+
+def check_group_offsets(group_offsets, m_total):
+    """Host check of the grouped GEMMs' offsets contract (int32 [G+1] on the
+    device: [0] = 0, non-decreasing, [G] = M_total); raises FP8BQError if it
+    is broken.  Synchronous."""
+    g = group_offsets.numel() - 1
+    _require(group_offsets, "group_offsets", torch.int32, (g + 1,))
+    with torch.cuda.device(group_offsets.device):
+        _check("fp8bq_check_group_offsets",
+               _lib.fp8bq_check_group_offsets(_ptr(group_offsets), g, int(m_total), _stream(group_offsets)))
 
 
 def encode_e4m3(v, method=1, out=None):

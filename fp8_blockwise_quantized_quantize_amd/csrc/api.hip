@@ -10,6 +10,9 @@
 #include "../../include/fp8bq.h"
 #include "launch.hpp"
 
+static_assert(FP8BQ_MAX_WEIGHT_DESCS == fp8bq::kMaxWeightDescs, "descriptor limits of the header and the launcher");
+static_assert(FP8BQ_MAX_ACT_DESCS == fp8bq::kMaxActDescs, "descriptor limits of the header and the launcher");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -29,6 +32,26 @@ fp8bq_status check_device() {
   }
   return state == 1 ? FP8BQ_OK : FP8BQ_ERR_DEVICE;
 }
+
+}  // namespace
+
+namespace fp8bq {
+
+int device_cus() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cached[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cached[dev].store(n, std::memory_order_release);
+  }
+  return n;
+}
+
+}  // namespace fp8bq
+
+namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -53,14 +76,10 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 fp8bq_status launched(hipError_t e) { return e == hipSuccess ? FP8BQ_OK : FP8BQ_ERR_LAUNCH; }
 
-// Debug mode for the grouped GEMMs' device-side precondition: with
-// FP8BQ_CHECK_OFFSETS=1 in the environment (read on every call) the offsets
-// are copied to the host on the call's stream, which waits for them, and
-// checked: [0] = 0, non-decreasing, [G] = M_total.  A violation returns
-// FP8BQ_ERR_BAD_SHAPE before anything is launched.
-fp8bq_status check_offsets_if_asked(const int32_t* offsets, int64_t G, int64_t M_total, hipStream_t stream) {
-  const char* e = std::getenv("FP8BQ_CHECK_OFFSETS");
-  if (e == nullptr || std::strcmp(e, "1") != 0) return FP8BQ_OK;
+// The grouped GEMMs' offsets contract, checked on the host: [0] = 0,
+// non-decreasing, [G] = M_total (the offsets are copied on `stream`, which
+// the call waits for).
+fp8bq_status check_offsets(const int32_t* offsets, int64_t G, int64_t M_total, hipStream_t stream) {
   std::vector<int32_t> h(static_cast<size_t>(G + 1));
   if (hipMemcpyAsync(h.data(), offsets, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
@@ -69,6 +88,17 @@ fp8bq_status check_offsets_if_asked(const int32_t* offsets, int64_t G, int64_t M
   for (int64_t g = 0; g < G; ++g)
     if (h[static_cast<size_t>(g + 1)] < h[static_cast<size_t>(g)]) return FP8BQ_ERR_BAD_SHAPE;
   return FP8BQ_OK;
+}
+
+// Debug mode for the grouped GEMMs' device-side precondition: with
+// FP8BQ_CHECK_OFFSETS=1 in the environment (read once, at the first grouped
+// GEMM call of the process) every grouped call checks its offsets first.
+fp8bq_status check_offsets_if_asked(const int32_t* offsets, int64_t G, int64_t M_total, hipStream_t stream) {
+  static const bool enabled = [] {
+    const char* e = std::getenv("FP8BQ_CHECK_OFFSETS");
+    return e != nullptr && std::strcmp(e, "1") == 0;
+  }();
+  return enabled ? check_offsets(offsets, G, M_total, stream) : FP8BQ_OK;
 }
 
 // Clears a stale runtime error so that the post-launch check reports ours.
@@ -170,10 +200,44 @@ fp8bq_status quantize_act_per_token_group(const uint16_t* x_bf16, uint8_t* x_fp8
   }
 }
 
-fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
-                                   const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
-                                   void* stream) {
+fp8bq_status quantize_acts_per_token_group_multi(const fp8bq_act_desc* descs, int64_t count, void* stream) {
   try {
+    if (count < 0 || count > FP8BQ_MAX_ACT_DESCS) return FP8BQ_ERR_BAD_SHAPE;
+    if (count == 0) return FP8BQ_OK;
+    if (!descs) return FP8BQ_ERR_NULL_PTR;
+    fp8bq::ActBatch batch{};
+    int64_t blocks = 0;
+    for (int64_t i = 0; i < count; ++i) {
+      const fp8bq_act_desc& d = descs[i];
+      if (d.M < 0 || d.K < 0) return FP8BQ_ERR_BAD_SHAPE;
+      int64_t mk, bytes;
+      if (!mul_ok(d.M, d.K, &mk) || !mul_ok(mk, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
+      if (mk == 0) continue;
+      if (!d.x_bf16 || !d.x_fp8 || !d.x_scale) return FP8BQ_ERR_NULL_PTR;
+      if (!aligned16(d.x_bf16) || !aligned16(d.x_fp8) || !aligned16(d.x_scale)) return FP8BQ_ERR_MISALIGNED;
+      const int64_t groups = d.M * ((d.K + 127) / 128);
+      batch.desc[batch.count] = fp8bq::ActDesc{d.x_bf16, d.x_fp8, d.x_scale, d.M, d.K};
+      batch.first[batch.count] = blocks;
+      blocks += (groups + fp8bq::kActGroupsPerWg - 1) / fp8bq::kActGroupsPerWg;
+      if (blocks > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+      ++batch.count;
+    }
+    batch.first[batch.count] = blocks;
+    if (batch.count == 0) return FP8BQ_OK;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_quant_act_multi(batch, blocks, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status gemm_w8a8_blockscaled_tile(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                        const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                        int tile, void* stream) {
+  try {
+    if (tile < FP8BQ_TILE_AUTO || tile > FP8BQ_TILE_PANEL192) return FP8BQ_ERR_BAD_ARG;
     if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
     int64_t mk, nk, mn, bytes;
     if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, &mn) || !mul_ok(mn, 2, &bytes))
@@ -187,11 +251,17 @@ fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, c
     fp8bq_status st = check_device();
     if (st != FP8BQ_OK) return st;
     clear_last_error();
-    return launched(
-        fp8bq::launch_gemm(a_fp8, a_scale, w_fp8, w_scale, y_bf16, M, N, K, static_cast<hipStream_t>(stream)));
+    return launched(fp8bq::launch_gemm(a_fp8, a_scale, w_fp8, w_scale, y_bf16, M, N, K, tile,
+                                       static_cast<hipStream_t>(stream)));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }
+}
+
+fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                   const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                   void* stream) {
+  return gemm_w8a8_blockscaled_tile(a_fp8, a_scale, w_fp8, w_scale, y_bf16, M, N, K, FP8BQ_TILE_AUTO, stream);
 }
 
 fp8bq_status quantize_act_per_token_group_frag(const uint16_t* x_bf16, uint8_t* x_fp8_frag, float* x_scale,
@@ -237,34 +307,75 @@ fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float*
   }
 }
 
-fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
-                                           const float* w_scale, const int32_t* group_offsets, uint16_t* y_bf16,
-                                           int64_t M_total, int64_t N, int64_t K, int64_t G, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The grouped GEMMs: plain (a_fp8 has M_total rows) or gathered (output row
+// m reads row a_rows[m] / a_row_div of the M_a rows of a_fp8).
+fp8bq_status grouped_gemm(bool gather, const uint8_t* a_fp8, const float* a_scale, int64_t M_a,
+                          const int32_t* a_rows, int64_t a_row_div, const uint8_t* w_fp8, const float* w_scale,
+                          const int32_t* group_offsets, uint16_t* y_bf16, int64_t M_total, int64_t N, int64_t K,
+                          int64_t G, int tile, void* stream) {
   try {
-    if (M_total < 0 || N < 0 || K < 0 || G < 0 || (K % 128) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
-    int64_t mk, nk, gnk, mn, bytes;
-    if (!mul_ok(M_total, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(nk, G, &gnk) || !mul_ok(M_total, N, &mn) ||
+    if (tile != FP8BQ_TILE_AUTO && tile != FP8BQ_TILE_WIDE && tile != FP8BQ_TILE_DECODE_PANEL &&
+        tile != FP8BQ_TILE_DEEP && tile != FP8BQ_TILE_DEEP_PERSISTENT)
+      return FP8BQ_ERR_BAD_ARG;
+    if (!gather) {
+      M_a = M_total;
+      a_row_div = 1;
+    }
+    if (M_a < 0 || M_total < 0 || N < 0 || K < 0 || G < 0 || (K % 128) != 0 || K > kMaxGemmK)
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (a_row_div < 1 || a_row_div > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t ak, nk, gnk, mn, bytes;
+    if (!mul_ok(M_a, K, &ak) || !mul_ok(N, K, &nk) || !mul_ok(nk, G, &gnk) || !mul_ok(M_total, N, &mn) ||
         !mul_ok(mn, 2, &bytes))
       return FP8BQ_ERR_BAD_SHAPE;
+    if (gather && ak >= (int64_t(1) << 31)) return FP8BQ_ERR_BAD_SHAPE;
     if (G > 0 && M_total + 128 * G > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
     if (mn == 0) return FP8BQ_OK;
     if (G == 0) return FP8BQ_ERR_BAD_SHAPE;  // rows to produce but no expert to own them
-    if (!y_bf16 || !group_offsets) return FP8BQ_ERR_NULL_PTR;
-    if (K > 0 && (!a_fp8 || !a_scale || !w_fp8 || !w_scale)) return FP8BQ_ERR_NULL_PTR;
-    if (!aligned16(y_bf16) || (K > 0 && (!aligned16(a_fp8) || !aligned16(a_scale) || !aligned16(w_fp8) ||
-                                         !aligned16(w_scale))))
+    if (!y_bf16 || !group_offsets || (gather && !a_rows)) return FP8BQ_ERR_NULL_PTR;
+    if (K > 0 && (!w_fp8 || !w_scale || (M_a > 0 && (!a_fp8 || !a_scale)))) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(y_bf16) || (gather && !aligned16(a_rows)) ||
+        (K > 0 && (!aligned16(w_fp8) || !aligned16(w_scale) || (M_a > 0 && (!aligned16(a_fp8) || !aligned16(a_scale))))))
       return FP8BQ_ERR_MISALIGNED;
-    if ((reinterpret_cast<uintptr_t>(group_offsets) & 3u) != 0) return FP8BQ_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(group_offsets) & (gather ? 15u : 3u)) != 0) return FP8BQ_ERR_MISALIGNED;
     fp8bq_status st = check_device();
     if (st != FP8BQ_OK) return st;
     st = check_offsets_if_asked(group_offsets, G, M_total, static_cast<hipStream_t>(stream));
     if (st != FP8BQ_OK) return st;
     clear_last_error();
-    return launched(fp8bq::launch_grouped_gemm(a_fp8, a_scale, w_fp8, w_scale, group_offsets, y_bf16, M_total, N,
-                                               K, G, static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gather)
+      return launched(fp8bq::launch_grouped_gemm_gather(a_fp8, a_scale, a_rows, a_row_div, M_a, w_fp8, w_scale,
+                                                        group_offsets, y_bf16, M_total, N, K, G, tile, s));
+    return launched(fp8bq::launch_grouped_gemm(a_fp8, a_scale, w_fp8, w_scale, group_offsets, y_bf16, M_total, N, K,
+                                               G, tile, s));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8bq_status grouped_gemm_w8a8_blockscaled_tile(const uint8_t* a_fp8, const float* a_scale, int64_t M_a,
+                                                const int32_t* a_rows, int64_t a_row_div, const uint8_t* w_fp8,
+                                                const float* w_scale, const int32_t* group_offsets,
+                                                uint16_t* y_bf16, int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                                int tile, void* stream) {
+  return grouped_gemm(a_rows != nullptr, a_fp8, a_scale, M_a, a_rows, a_row_div, w_fp8, w_scale, group_offsets,
+                      y_bf16, M_total, N, K, G, tile, stream);
+}
+
+fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                           const float* w_scale, const int32_t* group_offsets, uint16_t* y_bf16,
+                                           int64_t M_total, int64_t N, int64_t K, int64_t G, void* stream) {
+  return grouped_gemm(false, a_fp8, a_scale, M_total, nullptr, 1, w_fp8, w_scale, group_offsets, y_bf16, M_total, N,
+                      K, G, FP8BQ_TILE_AUTO, stream);
 }
 
 fp8bq_status grouped_gemm_w8a8_blockscaled_gather(const uint8_t* a_fp8, const float* a_scale, int64_t M_a,
@@ -272,30 +383,18 @@ fp8bq_status grouped_gemm_w8a8_blockscaled_gather(const uint8_t* a_fp8, const fl
                                                   const float* w_scale, const int32_t* group_offsets,
                                                   uint16_t* y_bf16, int64_t M_total, int64_t N, int64_t K, int64_t G,
                                                   void* stream) {
+  return grouped_gemm(true, a_fp8, a_scale, M_a, a_rows, a_row_div, w_fp8, w_scale, group_offsets, y_bf16, M_total,
+                      N, K, G, FP8BQ_TILE_AUTO, stream);
+}
+
+fp8bq_status fp8bq_check_group_offsets(const int32_t* group_offsets, int64_t G, int64_t M_total, void* stream) {
   try {
-    if (M_a < 0 || M_total < 0 || N < 0 || K < 0 || G < 0 || (K % 128) != 0 || K > kMaxGemmK)
-      return FP8BQ_ERR_BAD_SHAPE;
-    if (a_row_div < 1 || a_row_div > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
-    int64_t ak, nk, gnk, mn, bytes;
-    if (!mul_ok(M_a, K, &ak) || ak >= (int64_t(1) << 31) || !mul_ok(N, K, &nk) || !mul_ok(nk, G, &gnk) ||
-        !mul_ok(M_total, N, &mn) || !mul_ok(mn, 2, &bytes))
-      return FP8BQ_ERR_BAD_SHAPE;
-    if (G > 0 && M_total + 128 * G > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
-    if (mn == 0) return FP8BQ_OK;
-    if (G == 0) return FP8BQ_ERR_BAD_SHAPE;
-    if (!y_bf16 || !group_offsets || !a_rows) return FP8BQ_ERR_NULL_PTR;
-    if (K > 0 && (!w_fp8 || !w_scale || (M_a > 0 && (!a_fp8 || !a_scale)))) return FP8BQ_ERR_NULL_PTR;
-    if (!aligned16(y_bf16) || !aligned16(a_rows) || !aligned16(group_offsets) ||
-        (K > 0 && (!aligned16(w_fp8) || !aligned16(w_scale) || (M_a > 0 && (!aligned16(a_fp8) || !aligned16(a_scale))))))
-      return FP8BQ_ERR_MISALIGNED;
+    if (G < 1 || G > 0x7fffffffLL || M_total < 0) return FP8BQ_ERR_BAD_SHAPE;
+    if (!group_offsets) return FP8BQ_ERR_NULL_PTR;
+    if ((reinterpret_cast<uintptr_t>(group_offsets) & 3u) != 0) return FP8BQ_ERR_MISALIGNED;
     fp8bq_status st = check_device();
     if (st != FP8BQ_OK) return st;
-    st = check_offsets_if_asked(group_offsets, G, M_total, static_cast<hipStream_t>(stream));
-    if (st != FP8BQ_OK) return st;
-    clear_last_error();
-    return launched(fp8bq::launch_grouped_gemm_gather(a_fp8, a_scale, a_rows, a_row_div, M_a, w_fp8, w_scale,
-                                                      group_offsets, y_bf16, M_total, N, K, G,
-                                                      static_cast<hipStream_t>(stream)));
+    return check_offsets(group_offsets, G, M_total, static_cast<hipStream_t>(stream));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }

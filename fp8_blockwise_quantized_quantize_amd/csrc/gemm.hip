@@ -847,13 +847,15 @@ struct Panel {
 // ---------------------------------------------------------------------------
 // panel_afrag<BN, BM, ...>: the panel tile for activations stored in the MFMA
 // fragment order (launch_quant_act_frag): each wave loads its activation
-// fragments straight into VGPRs, one K-block ahead (two contiguous 16-byte
-// loads per lane per fragment), and only the weight rows and the scales go
-// through LDS.  That leaves room for four one-K-block weight stages in two
-// alternating pairs: the waves meet at one barrier per two K-blocks (K % 256
-// == 0).  Same per-element arithmetic and order as panel<>: bit-identical
-// outputs.  Qwen3-8B prefill (M = 8192): qkv 204-211 vs 239-249 us, o
-// 138-148 vs 153-156, down 347 vs 371-379, gate_up 882-885 vs 888-892.
+// fragments straight into VGPRs (two contiguous 16-byte loads per lane per
+// fragment), and only the weight rows and the scales go through LDS.  That
+// leaves room for four one-K-block weight stages used in two alternating
+// pairs: the waves meet at one barrier per two K-blocks (K % 256 == 0).
+// The weight and scale loads of pair p + 1 are issued during the MFMAs of
+// pair p, and the activation fragments of K-block k + 1 during those of
+// K-block k; before the barrier of pair p + 1 every wave waits for all of
+// its loads (vmcnt(0)), so the prefetch depth is one pair.  Same per-element arithmetic and order
+// as panel<>: bit-identical outputs.
 // ---------------------------------------------------------------------------
 template <int BN_, int BM_, int WGN, int WGM, int S>
 struct PanelAfrag {
@@ -863,16 +865,15 @@ struct PanelAfrag {
   static constexpr int TN = WNR / 16, TM = WMR / 16;
   static_assert(WNR % 16 == 0 && WMR % 16 == 0 && WNR <= 128, "wave tile");
   static_assert(BN % 64 == 0 && BM % 64 == 0, "each load instruction covers 8 rows of one operand, 8 waves");
-  static constexpr int kRows = BN;                      // weight rows staged per K-block (activations direct)
-  static constexpr int kLoads = kRows / 64;             // load instructions per wave per K-block
-  static constexpr int kStage = kRows * kBlock;
-  // Each stage also holds that K-block's scales, staged like the operands:
-  // 64 dwords per wave (activation scales of the tile's rows 0..BM-1, then
-  // the tile's weight scale blocks), after the S operand stages.
+  static constexpr int kLoads = BN / 64;               // weight load instructions per wave per K-block
+  static constexpr int kStage = BN * kBlock;           // one K-block of weight rows
+  // Each stage also holds that K-block's scales: 64 dwords per wave
+  // (activation scales of the tile's rows 0..BM-1, then the tile's weight
+  // scale blocks), after the S operand stages.
   static constexpr int kScaleBytes = 8 * 64 * 4;
   static_assert(BM / 64 < 8, "a wave left over for the weight scales");
   static constexpr int kLdsBytes = S * (kStage + kScaleBytes);
-  static_assert(S >= 2 && S <= 4, "stages");
+  static_assert(S == 4, "two pairs of K-block sub-stages");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
   static constexpr int kThreadsPerWg = 512;
   static constexpr int kWavesPerSimd = 2;
@@ -880,11 +881,7 @@ struct PanelAfrag {
   // multiples of 128 and the wave's share divides 128
   static constexpr bool kOneScaleBlock = (BN % kBlock == 0) && (kBlock % WNR == 0);
 
-  __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) { run_impl<false>(t, lds); }
-
-  template <bool kGather>
-  __device__ static __forceinline__ void run_impl(const Tile& t, uint8_t* lds) {
-    static_assert(!kGather, "fragment-order activations are not gathered");
+  __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) {
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wn = wave % WGN, wm = wave / WGN;
@@ -905,50 +902,26 @@ struct PanelAfrag {
     for (int i = 0; i < TN; ++i)
       if ((wrow0 + i * 16) / kBlock > nb0) hi_mask |= 1u << i;
     const auto wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
-    const auto ar = kGather ? make_rsrc(t.a, t.a_nrows * K) : make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
-    const int64_t am_lo = t.m_lo + wm * WMR;  // this wave's first activation row
-    // Source row of output row m: itself, or the gathered row (-1: none).
-    auto src_row = [&](int64_t m) -> int64_t {
-      if (m >= t.m_hi) return -1;
-      if (!kGather) return m - t.m_lo;  // relative to the tile's buffer
-      const int32_t p = t.a_rows[m];
-      const int64_t r = p >= 0 ? p / t.a_div : -1;
-      return r < t.a_nrows ? r : -1;
-    };
-    // a ragged last tile (e.g. an expert's rows past a multiple of BM) can
-    // leave whole waves without a valid activation row: they skip the MFMAs
-    const bool idle = am_lo >= t.m_hi;
+    const auto ar = make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
+    // a wave whose rows all lie past the last row skips the MFMAs
+    const bool idle = t.m_lo + wm * WMR >= t.m_hi;
     // Scale staging, one buffer_load_dword ... lds per wave and K-block into
     // the wave's 64 dwords of the stage's scale area: waves w < BM/64 load
     // the activation scales of tile rows 64 w + lane, the others the
-    // weight scale blocks nbt + lane.  As for the operands, rows and blocks
-    // past the end sit outside the buffer range and read zeros.
+    // weight scale blocks nbt + lane.  Rows and blocks past the end sit
+    // outside the buffer range and read zeros.
     const bool act_scales = wave < BM / 64;
-    const auto scr = act_scales ? (kGather ? make_rsrc(t.sa, t.a_nrows * KB * 4)
-                                           : make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4))
+    const auto scr = act_scales ? make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4)
                                 : make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
-    int scvoff = lane * KB * 4;
-    if (act_scales) {
-      const int64_t r = src_row(t.m_lo + 64 * wave + lane);
-      scvoff = kGather ? (r >= 0 ? (int)(r * KB * 4) : kOob) : (64 * wave + lane) * KB * 4;
-    }
+    const int scvoff = act_scales ? (64 * wave + lane) * KB * 4 : lane * KB * 4;
 
-    // DMA staging: load q of wave w fills stage rows R0..R0+7 with
-    // R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at physical chunk
-    // l%8, so it fetches logical chunk (l%8) ^ (l/8) (the XOR swizzle).
-    // The row offset is part of the per-lane offset, which the buffer range
-    // check covers: rows past the tile's last row read zeros, never memory.
+    // DMA staging of the weight rows: load q of wave w fills stage rows
+    // R0..R0+7 with R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at
+    // physical chunk l%8, so it fetches logical chunk (l%8) ^ (l/8) (the XOR
+    // swizzle).  The row offset is part of the per-lane offset, which the
+    // buffer range check covers: rows past the tile's last row read zeros.
     const int chunk_off = ((lane & 7) ^ (lane >> 3)) << 4;
     const int dvoff = (lane >> 3) * (int)K + chunk_off;
-    // gathered activations: the offset of this lane's row in each A load
-    int aoff[kGather ? BM / 64 : 1];
-    if constexpr (kGather) {
-#pragma unroll
-      for (int qa = 0; qa < BM / 64; ++qa) {
-        const int64_t r = src_row(t.m_lo + 8 * (8 * (BN / 64 + qa) + wave) - BN + (lane >> 3));
-        aoff[qa] = r >= 0 ? (int)(r * K) + chunk_off : kOob;
-      }
-    }
     const FragLds fl(lane);
 
     v4f acc[TN][TM];
@@ -962,17 +935,11 @@ struct PanelAfrag {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, dst, 4, scvoff, kb * 4, 0, 0);
     };
     auto dma_q = [&](int q, int kb, uint8_t* buf) {
-      const int koff = kb * kBlock;
-      const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
+      const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q: weight rows n0 + r0 ..
       auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
-      if (q < BN / 64)  // stage rows 0..BN-1: weight rows n0 + r0 ..
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, koff, 0, 0);
-      else if (kGather)  // stage rows BN..: the gathered activation rows
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, aoff[kGather ? q - BN / 64 : 0], koff, 0, 0);
-      else              // stage rows BN..: activation rows m_lo + r0 - BN ..
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff + (r0 - BN) * (int)K, koff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, kb * kBlock, 0, 0);
     };
-    // all loads of one K-block: the operand rows, then the scales
+    // all loads of one K-block: the weight rows, then the scales
     auto dma_kblock = [&](int kb, int stage) {
 #pragma unroll
       for (int q = 0; q < kLoads; ++q) dma_q(q, kb, lds + stage * kStage);
@@ -980,8 +947,6 @@ struct PanelAfrag {
     };
     constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
     auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * WNR + i * 16); };
-    // The first fragments of a phase, read right after its barrier; the
-    // first MFMA's two operands go first so that it waits for them only.
     // activation fragments in MFMA order: 2 KB per (16-row group, K-block),
     // lane l's two 16-byte halves at l * 16 and 1024 + l * 16
     u32x4 an_lo[TM], an_hi[TM];
@@ -990,6 +955,8 @@ struct PanelAfrag {
       const u32x4 v = bload16(ar, afrag_off(j, h), kb * 2048);
       if (h == 0) an_lo[j] = v; else an_hi[j] = v;
     };
+    // The first fragments of a phase; the first MFMA's weight operand goes
+    // first so that it waits for that read only.
     auto first_frags = [&](v8i (&fa)[TM], v8i (&fw)[kAhead + 1], const uint8_t* buf) {
       fw[0] = load_w(buf, 0);
 #pragma unroll
@@ -998,12 +965,11 @@ struct PanelAfrag {
 #pragma unroll
       for (int p = 1; p < kAhead && p < TN; ++p) fw[p] = load_w(buf, p);
     };
-    // One phase: the product of the K-block in stage `cur`, with the loads
-    // of K-block `kb` into stage `fill` issued after every second MFMA
-    // (after every MFMA when there are few), so that the L2 and LDS-write
-    // traffic does not arrive as one burst right after the barrier.  The
-    // scales come from the stage's scale area; their products are formed
-    // while the first MFMAs run.
+    // One K-block: the product of the K-block in stage `cur`, with the loads
+    // of weight K-block `kb` into stage `fill` and of the activation
+    // fragments of K-block `kb_a` issued after every second MFMA (after
+    // every MFMA when there are few), so that the L2 and LDS-write traffic
+    // does not arrive as one burst right after the barrier.
     constexpr int kT = TN * TM;
     constexpr int kPhaseLoads = kLoads + 1 + 2 * TM;
     constexpr int kEvery = (kT >= 2 * kPhaseLoads) ? 2 : 1;
@@ -1027,9 +993,6 @@ struct PanelAfrag {
           [&](int i, int j) { return (kOneScaleBlock || !((hi_mask >> i) & 1u)) ? c0[j] : c1[j]; },
           [&](int tt) {
             if (tt % kEvery != 0 || tt / kEvery >= kPhaseLoads) return false;
-            // activation fragments first: the end-of-phase wait leaves the
-            // newest (S - 2) phases' weight and scale loads in flight, and
-            // loads complete in issue order
             const int q = tt / kEvery;
             if (q < 2 * TM)
               load_a(q / 2, q % 2, kb_a);
@@ -1040,45 +1003,31 @@ struct PanelAfrag {
             return true;
           });
     };
-    // The compiler does not track LDS writes by buffer_load ... lds: wait
-    // for them explicitly before the barrier that publishes the stage.  With
-    // three stages the loads of the next K-block may stay in flight.
-    auto wait_stage = [&]() {
-      // weight + scale loads of the newest S - 2 phases may stay in flight
-      if constexpr (S == 2)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * (kLoads + 1)) : "memory");
-    };
-    // The workgroup barrier of a phase.  Not __syncthreads(): its fence
-    // would wait for every load in flight (vmcnt(0)), including the later
-    // K-blocks' prefetches that the ring keeps in flight on purpose.  The
-    // LDS writes this barrier publishes were waited for by wait_stage();
-    // the LDS reads of the previous phase are waited for here, so no wave
+    // The workgroup barrier of a pair.  Not __syncthreads(): its fence adds
+    // nothing here (the vmcnt(0) before it already covers every load), and
+    // the LDS reads of the previous pair are waited for here, so no wave
     // refills a stage that another is still reading.
     auto barrier = [&]() {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       order_fence();
     };
-    auto wait_all = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
     const int kb_last = KB - 1;
     auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };  // clamped prefetch
-    static_assert(S == 4, "two pairs of K-block sub-stages");
     if (KB > 0) {
       dma_kblock(0, 0);
 #pragma unroll
       for (int j = 0; j < TM; ++j) { load_a(j, 0, 0); load_a(j, 1, 0); }
       dma_kblock(nxt(1), 1);
     }
-    // Loads past the last K-block re-load it into a stage nobody reads
-    // again, keeping the loop body free of branches.
-    // K-blocks in pairs, one barrier per pair (KB even: the host uses this
-    // tile only for K % 256 == 0); sub-stages 0,1 and 2,3 alternate.
+    // K-blocks in pairs (KB even: the host uses this tile only for K % 256
+    // == 0); sub-stages 0,1 and 2,3 alternate.  Loads past the last K-block
+    // re-load it into a stage nobody reads again, keeping the loop body
+    // free of branches.
     for (int kp = 0; kp < KB; kp += 2) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      barrier();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of pair kp have landed
+      barrier();                                        // and everyone's
       const int c0 = ((kp >> 1) & 1) ? 2 : 0, f0 = 2 - c0;
       if (idle) {
         dma_kblock(nxt(kp + 2), f0);
@@ -1090,7 +1039,7 @@ struct PanelAfrag {
       }
       order_fence();
     }
-    wait_all();  // no LDS write may be in flight when the workgroup ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may be in flight when the workgroup ends
 
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
@@ -1100,7 +1049,6 @@ struct PanelAfrag {
       for (int i = 0; i < TN; ++i) store4(t.y, t.N, m, t.n0 + wn * WNR + i * 16 + g * 4, acc[i][j]);
     }
   }
-
 };
 
 using WideAfrag = PanelAfrag<256, 256, 2, 4, 4>;
@@ -1332,7 +1280,7 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
 enum class Cfg { kSkinny64x64, kSkinny48x64, kWide, kDecodePanel, kDeep, kPanel192 };
 
 // Per-workgroup cycle estimate: operand bytes through L1 (64 B/clk/CU) vs
-// FP8 MFMA (8192 FLOP/clk/CU), times the rounds of workgroups over 256 CUs.
+// FP8 MFMA (8192 FLOP/clk/CU), times the rounds of workgroups over the CUs.
 double est_cycles(int64_t M, int64_t N, int64_t K, int bn, int bm, double cus) {
   const double tiles = (double)((N + bn - 1) / bn) * (double)((M + bm - 1) / bm);
   const double rounds = std::ceil(tiles / cus);  // waves of workgroups over the CUs
@@ -1341,14 +1289,20 @@ double est_cycles(int64_t M, int64_t N, int64_t K, int bn, int bm, double cus) {
   return rounds * (l1 > mfma ? l1 : mfma);
 }
 
+// The CU count of the device (256 on MI355X; 256 if it cannot be read).
+double cu_count() {
+  const int n = device_cus();
+  return n > 0 ? (double)n : 256.0;
+}
+
 Cfg choose(int64_t M, int64_t N, int64_t K) {
-  const double cus = 256.0;
+  const double cus = cu_count();
   // Few activation rows but many weight rows: one 128 x 256 panel covers
   // every row of the activation panel, so each weight row is read once.
-  if (M <= DecodePanel::BM && (N + DecodePanel::BN - 1) / DecodePanel::BN >= 160) {
-    // the 192 x 128 panel when its tiles fill 224..256 CUs in one round
+  if (M <= DecodePanel::BM && (N + DecodePanel::BN - 1) / DecodePanel::BN >= (int64_t)(0.625 * cus)) {
+    // the 192 x 128 panel when its tiles fill 7/8 or more of the CUs in one round
     const int64_t t192 = ((N + Panel192::BN - 1) / Panel192::BN) * ((M + Panel192::BM - 1) / Panel192::BM);
-    if (t192 >= 224 && t192 <= (int64_t)cus) return Cfg::kPanel192;
+    if (t192 >= (int64_t)(0.875 * cus) && t192 <= (int64_t)cus) return Cfg::kPanel192;
     return Cfg::kDecodePanel;
   }
   double best = est_cycles(M, N, K, Wide::BN, Wide::BM, cus);
@@ -1356,7 +1310,7 @@ Cfg choose(int64_t M, int64_t N, int64_t K) {
   const double s64 = est_cycles(M, N, K, 64, 64, cus) * 1.05;  // partial-tile reduction overhead
   if (s64 < best) {
     // Skinny tiles 64 or 48 weight rows wide: whichever fills its rounds of
-    // 256 workgroups more evenly (tiles / (rounds * 256)); ties keep 64.
+    // one workgroup per CU more evenly (tiles / (rounds * CUs)); ties keep 64.
     // At M = 256 the 48-row tile gives qkv (N = 6144) 512 tiles, two per CU,
     // where the 64-row one gives 384 (19.7 vs 21.7 us); o and down (N =
     // 4096) stay at 256 tiles of 64 rows.
@@ -1380,22 +1334,18 @@ hipError_t launch_dense_cfg(const uint8_t* a, const float* sa, const uint8_t* w,
   return hipGetLastError();
 }
 
-// Tile override for tests and diagnostics: FP8BQ_GEMM_TILE = skinny64 |
-// skinny48 | wide | decode_panel | deep | panel192 forces that kernel for every dense GEMM
-// (wide | decode_panel | deep (one tile per workgroup) | deep_persistent for
-// the grouped GEMM); unset (the default) lets the cost model choose.  Read
-// on every call.
-Cfg tile_for(int64_t M, int64_t N, int64_t K) {
-  const char* e = std::getenv("FP8BQ_GEMM_TILE");
-  if (e != nullptr && *e != '\0') {
-    if (std::strcmp(e, "skinny64") == 0) return Cfg::kSkinny64x64;
-    if (std::strcmp(e, "skinny48") == 0) return Cfg::kSkinny48x64;
-    if (std::strcmp(e, "wide") == 0) return Cfg::kWide;
-    if (std::strcmp(e, "decode_panel") == 0) return Cfg::kDecodePanel;
-    if (std::strcmp(e, "deep") == 0) return Cfg::kDeep;
-    if (std::strcmp(e, "panel192") == 0) return Cfg::kPanel192;
+// A named tile kernel (FP8BQ_TILE_* of the C ABI; 0 = the cost model).
+bool tile_cfg(int tile, int64_t M, int64_t N, int64_t K, Cfg* c) {
+  switch (tile) {
+    case 0: *c = choose(M, N, K); return true;
+    case 1: *c = Cfg::kSkinny64x64; return true;
+    case 2: *c = Cfg::kSkinny48x64; return true;
+    case 3: *c = Cfg::kWide; return true;
+    case 4: *c = Cfg::kDecodePanel; return true;
+    case 5: *c = Cfg::kDeep; return true;
+    case 6: *c = Cfg::kPanel192; return true;
+    default: return false;
   }
-  return choose(M, N, K);
 }
 
 template <class Kern, bool kGather>
@@ -1418,7 +1368,8 @@ hipError_t launch_grouped_persistent(const uint8_t* a, const float* sa, const ui
                                      const int32_t* a_rows, int a_div, int64_t a_nrows, hipStream_t stream) {
   const int64_t tiles_n = (N + Kern::BN - 1) / Kern::BN;
   const int64_t bound = tiles_n * ((M + Kern::BM - 1) / Kern::BM + G);  // >= the tiles there are
-  const int64_t P = bound < 256 ? bound : 256;  // one workgroup per CU (the tile's LDS allows one)
+  const int64_t cus = (int64_t)cu_count();
+  const int64_t P = bound < cus ? bound : cus;  // one workgroup per CU (the tile's LDS allows one)
   hipLaunchKernelGGL((gemm_grouped_persistent_kernel<Kern, kGather>), dim3((unsigned)P), dim3(Kern::kThreadsPerWg),
                      (size_t)Kern::kLdsBytes, stream, a, sa, w, sw, offsets, y, M, N, K, (int)G, tiles_n, a_rows,
                      a_div, a_nrows);
@@ -1428,7 +1379,7 @@ hipError_t launch_grouped_persistent(const uint8_t* a, const float* sa, const ui
 template <bool kGather>
 hipError_t launch_grouped_any(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                               const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
-                              const int32_t* a_rows, int a_div, int64_t a_nrows, hipStream_t stream) {
+                              const int32_t* a_rows, int a_div, int64_t a_nrows, int tile, hipStream_t stream) {
   if (M == 0 || N == 0 || G == 0) return hipSuccess;
   // The expert tiles: each expert's weights are read by its own few tiles
   // only, so they stream from HBM, and the deep (three-stage) panel keeps
@@ -1437,14 +1388,14 @@ hipError_t launch_grouped_any(const uint8_t* a, const float* sa, const uint8_t* 
   // for the 256 x 256 two-stage tile.  Run persistent (one workgroup per
   // CU, the ring carried across tiles) while the expert table fits in LDS:
   // fc1 224-228 vs 240 us, fc2 131 vs 167 us (its tiles have 6 K-blocks,
-  // so the per-tile pipeline fill weighed most).  The others on override.
-  const char* e = std::getenv("FP8BQ_GEMM_TILE");
-  if (e != nullptr && std::strcmp(e, "decode_panel") == 0)
+  // so the per-tile pipeline fill weighed most).  The others when named.
+  if (tile == 4)
     return launch_grouped_cfg<DecodePanel, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows,
                                                     stream);
-  if (e != nullptr && std::strcmp(e, "wide") == 0)
+  if (tile == 3)
     return launch_grouped_cfg<Wide, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows, stream);
-  const bool per_tile = e != nullptr && std::strcmp(e, "deep") == 0;
+  if (tile != 0 && tile != 5 && tile != 7) return hipErrorInvalidValue;
+  const bool per_tile = tile == 5;
   if (per_tile || G > kMaxPersistentExperts)
     return launch_grouped_cfg<Deep, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows, stream);
   return launch_grouped_persistent<Deep, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows,
@@ -1454,9 +1405,11 @@ hipError_t launch_grouped_any(const uint8_t* a, const float* sa, const uint8_t* 
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
-                       int64_t N, int64_t K, hipStream_t stream) {
+                       int64_t N, int64_t K, int tile, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  switch (tile_for(M, N, K)) {
+  Cfg cfg;
+  if (!tile_cfg(tile, M, N, K, &cfg)) return hipErrorInvalidValue;
+  switch (cfg) {
     case Cfg::kSkinny64x64:
       return launch_dense_cfg<Skinny<64, 64, 4>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kSkinny48x64:
@@ -1481,14 +1434,15 @@ hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                                const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
-                               hipStream_t stream) {
-  return launch_grouped_any<false>(a, sa, w, sw, offsets, y, M, N, K, G, nullptr, 1, 0, stream);
+                               int tile, hipStream_t stream) {
+  return launch_grouped_any<false>(a, sa, w, sw, offsets, y, M, N, K, G, nullptr, 1, 0, tile, stream);
 }
 
 hipError_t launch_grouped_gemm_gather(const uint8_t* a, const float* sa, const int32_t* a_rows, int64_t a_div,
                                       int64_t a_nrows, const uint8_t* w, const float* sw, const int32_t* offsets,
-                                      uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G, hipStream_t stream) {
-  return launch_grouped_any<true>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, (int)a_div, a_nrows, stream);
+                                      uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G, int tile,
+                                      hipStream_t stream) {
+  return launch_grouped_any<true>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, (int)a_div, a_nrows, tile, stream);
 }
 
 }  // namespace fp8bq

@@ -7,6 +7,10 @@
 
 namespace fp8bq {
 
+// Compute units of the current device, read from its properties once per
+// device (0 when they cannot be read).
+int device_cus();
+
 // Matrices re-quantized by one launch (passed by value in the kernel
 // arguments): desc[t] is an [N][K] BF16 matrix with its outputs; its blocks
 // are workgroups first[t] .. first[t + 1] - 1.
@@ -29,6 +33,25 @@ hipError_t launch_quant_weight(const uint16_t* w, uint8_t* q, float* scale, int6
 hipError_t launch_quant_weight_multi(const WeightBatch& batch, int64_t blocks, hipStream_t stream);
 
 hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K, hipStream_t stream);
+
+// Activations quantized by one launch (descriptors by value in the kernel
+// arguments): desc[t] is an [M][K] BF16 matrix with its outputs; its groups
+// go to workgroups first[t] .. first[t + 1] - 1 (16 groups each).
+constexpr int kMaxActDescs = 16;  // FP8BQ_MAX_ACT_DESCS of the C ABI
+struct ActDesc {
+  const uint16_t* x;
+  uint8_t* q;
+  float* s;
+  int64_t M, K;
+};
+struct ActBatch {
+  ActDesc desc[kMaxActDescs];
+  int64_t first[kMaxActDescs + 1];
+  int count;
+};
+constexpr int kActGroupsPerWg = 16;
+
+hipError_t launch_quant_act_multi(const ActBatch& batch, int64_t blocks, hipStream_t stream);
 // the same codes in the MFMA fragment order of the activation operand (M % 16 == 0, K % 128 == 0)
 hipError_t launch_quant_act_frag(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K,
                                  hipStream_t stream);
@@ -36,16 +59,19 @@ hipError_t launch_quant_act_frag(const uint16_t* x, uint8_t* q, float* scale, in
 hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// `tile`: FP8BQ_TILE_* of the C ABI (0 = the cost model's choice); an
+// unknown value returns hipErrorInvalidValue.
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
-                       int64_t N, int64_t K, hipStream_t stream);
+                       int64_t N, int64_t K, int tile, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                                const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
-                               hipStream_t stream);
+                               int tile, hipStream_t stream);
 
 hipError_t launch_grouped_gemm_gather(const uint8_t* a, const float* sa, const int32_t* a_rows, int64_t a_div,
                                       int64_t a_nrows, const uint8_t* w, const float* sw, const int32_t* offsets,
-                                      uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G, hipStream_t stream);
+                                      uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G, int tile,
+                                      hipStream_t stream);
 
 hipError_t launch_encode(const float* in, uint8_t* out, int64_t n, int method, hipStream_t stream);
 

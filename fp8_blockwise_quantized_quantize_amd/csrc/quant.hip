@@ -207,6 +207,23 @@ __global__ __launch_bounds__(kQaThreads) void quant_act_kernel(const uint16_t* _
   for (int p = 0; p < kPasses; ++p) act_group_store(grp[p], q, scale, K, G, li);
 }
 
+// Several activations in one launch (the four of a decode layer step take
+// one launch instead of four latency-bound ones): workgroup b takes groups
+// 16 (b - first[t]) .. + 15 of the activation t with first[t] <= b <
+// first[t + 1], one group per quarter wave as in quant_act_kernel<1>.
+__global__ __launch_bounds__(kQaThreads) void quant_act_multi_kernel(const ActBatch batch) {
+  static_assert(kQaThreads / 16 == kActGroupsPerWg, "one group per quarter wave");
+  const int64_t b = blockIdx.x;
+  int t = 0;
+  while (t + 1 < batch.count && b >= batch.first[t + 1]) ++t;  // uniform scan over <= 16 entries
+  const ActDesc& d = batch.desc[t];
+  const int G = (int)((d.K + kBlock - 1) / kBlock);
+  const int li = threadIdx.x & 15;
+  const int64_t gid = (b - batch.first[t]) * kActGroupsPerWg + (threadIdx.x >> 4);
+  const ActGroup grp = act_group_load(d.x, d.M, d.K, G, gid, li);
+  act_group_store(grp, d.q, d.s, d.K, G, li);
+}
+
 // ---------------------------------------------------------------------------
 // Standalone encoder: method 0 = the hardware conversion exactly as the
 // quantizers apply it (valid for |v| < 464), 1 = saturating encoder (clamp
@@ -318,6 +335,13 @@ hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t
   else
     hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, x, q, scale, M, K,
                        (int)G);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_multi(const ActBatch& batch, int64_t blocks, hipStream_t stream) {
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_act_multi_kernel, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, batch);
   return hipGetLastError();
 }
 

@@ -124,6 +124,29 @@ fp8bq_status quantize_act_per_token_group(const uint16_t* x_bf16, uint8_t* x_fp8
                                           int64_t M, int64_t K, void* stream);
 
 /*
+ * quantize_acts_per_token_group_multi -- quantize_act_per_token_group of
+ * several activations of any shapes in one launch (a decode step quantizes
+ * the small inputs of several linears per layer; at a few MB each, one
+ * launch per activation is latency-bound).  Each activation gets exactly the
+ * codes and scales quantize_act_per_token_group gives it.
+ *   descs  HOST array of `count` descriptors (read during the call only):
+ *          x_bf16 [M][K] BF16, x_fp8 [M][K] E4M3, x_scale [M][ceil(K/128)]
+ *          float32, M, K >= 0, each validated as in
+ *          quantize_act_per_token_group (empty ones are skipped).
+ *   0 <= count <= FP8BQ_MAX_ACT_DESCS; outputs must not overlap.
+ */
+#define FP8BQ_MAX_ACT_DESCS 16
+typedef struct {
+  const uint16_t* x_bf16;
+  uint8_t* x_fp8;
+  float* x_scale;
+  int64_t M;
+  int64_t K;
+} fp8bq_act_desc;
+
+fp8bq_status quantize_acts_per_token_group_multi(const fp8bq_act_desc* descs, int64_t count, void* stream);
+
+/*
  * gemm_w8a8_blockscaled -- y = dequant(A) * dequant(W)^T in FP32, stored as
  * BF16 ([FP8-RL summary] §3.4.2 Phase 3: FP8 matrix multiplication,
  * accumulated in FP32, converted back to BF16).
@@ -136,13 +159,43 @@ fp8bq_status quantize_act_per_token_group(const uint16_t* x_bf16, uint8_t* x_fp8
  *   256-row operand panel with 32-bit offsets).  The summation order is
  *   unspecified (results agree with the exact value to FP32 accumulation
  *   error before the BF16 rounding).
- *   The tile kernel is chosen per shape.  For tests and diagnostics the
- *   environment variable FP8BQ_GEMM_TILE (skinny64, skinny48, wide,
- *   decode_panel, deep, panel192), read on every call, forces one of them.
+ *   The tile kernel is chosen per shape by a cost model over the device's
+ *   CU count; gemm_w8a8_blockscaled_tile runs a named one.
  */
 fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
                                    const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
                                    void* stream);
+
+/*
+ * Tile kernels of the GEMMs, for tests and diagnostics (the *_tile entry
+ * points).  FP8BQ_TILE_AUTO is the choice the plain entry points make.
+ *   dense:   SKINNY64, SKINNY48 (K split over the 4 waves of a 64 / 48 x 64
+ *            tile), WIDE (256 x 256), DECODE_PANEL (128 x 256), DEEP
+ *            (256 x 128, three stages), PANEL192 (192 x 128)
+ *   grouped: WIDE, DECODE_PANEL, DEEP (one workgroup per tile),
+ *            DEEP_PERSISTENT (one workgroup per CU; the default, used for
+ *            G <= 1024 only, above that the per-tile DEEP kernel runs)
+ */
+enum {
+  FP8BQ_TILE_AUTO = 0,
+  FP8BQ_TILE_SKINNY64 = 1,
+  FP8BQ_TILE_SKINNY48 = 2,
+  FP8BQ_TILE_WIDE = 3,
+  FP8BQ_TILE_DECODE_PANEL = 4,
+  FP8BQ_TILE_DEEP = 5,
+  FP8BQ_TILE_PANEL192 = 6,
+  FP8BQ_TILE_DEEP_PERSISTENT = 7
+};
+
+/*
+ * gemm_w8a8_blockscaled_tile -- gemm_w8a8_blockscaled with the tile kernel
+ * named by `tile` (a dense FP8BQ_TILE_* value; DEEP_PERSISTENT is grouped
+ * only).  Same contract and the same result bits for a given tile; another
+ * tile may sum in another order.  An unknown tile is FP8BQ_ERR_BAD_ARG.
+ */
+fp8bq_status gemm_w8a8_blockscaled_tile(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                        const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                        int tile, void* stream);
 
 /*
  * quantize_act_per_token_group_frag -- quantize_act_per_token_group with
@@ -199,14 +252,12 @@ fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float*
  *   K as for gemm_w8a8_blockscaled.
  *   For G <= 1024 one workgroup per CU runs the expert tiles in turn (the
  *   launch does not depend on how the rows are spread); for more experts,
- *   one workgroup per tile.  FP8BQ_GEMM_TILE (wide, decode_panel, deep,
- *   deep_persistent), read on every call, forces a tile kernel for tests
- *   and diagnostics.
- *   Debug mode: with FP8BQ_CHECK_OFFSETS=1 in the environment (read on every
- *   call) the call copies the offsets to the host, waits for them on
- *   `stream`, and returns FP8BQ_ERR_BAD_SHAPE, launching nothing, unless
- *   [0] = 0, they are non-decreasing and [G] = M_total.  This applies to
- *   grouped_gemm_w8a8_blockscaled_gather too.
+ *   one workgroup per tile.  grouped_gemm_w8a8_blockscaled_tile runs a
+ *   named tile kernel.
+ *   Debug mode: with FP8BQ_CHECK_OFFSETS=1 in the environment (read once,
+ *   at the first grouped GEMM call of the process) every grouped call first
+ *   runs fp8bq_check_group_offsets and returns its error, launching
+ *   nothing.  This applies to grouped_gemm_w8a8_blockscaled_gather too.
  */
 fp8bq_status grouped_gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
                                            const float* w_scale, const int32_t* group_offsets, uint16_t* y_bf16,
@@ -232,6 +283,30 @@ fp8bq_status grouped_gemm_w8a8_blockscaled_gather(const uint8_t* a_fp8, const fl
                                                   const float* w_scale, const int32_t* group_offsets,
                                                   uint16_t* y_bf16, int64_t M_total, int64_t N, int64_t K, int64_t G,
                                                   void* stream);
+
+/*
+ * grouped_gemm_w8a8_blockscaled_tile -- the grouped GEMM (plain when a_rows
+ * is NULL, then a_fp8 has M_total rows and M_a / a_row_div are ignored;
+ * gathered otherwise, as grouped_gemm_w8a8_blockscaled_gather) with the
+ * tile kernel named by `tile`: FP8BQ_TILE_AUTO, WIDE, DECODE_PANEL, DEEP or
+ * DEEP_PERSISTENT.  Same contract and the same result bits for a given
+ * tile.  Another tile value is FP8BQ_ERR_BAD_ARG.  For tests and
+ * diagnostics.
+ */
+fp8bq_status grouped_gemm_w8a8_blockscaled_tile(const uint8_t* a_fp8, const float* a_scale, int64_t M_a,
+                                                const int32_t* a_rows, int64_t a_row_div, const uint8_t* w_fp8,
+                                                const float* w_scale, const int32_t* group_offsets,
+                                                uint16_t* y_bf16, int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                                int tile, void* stream);
+
+/*
+ * fp8bq_check_group_offsets -- host check of the grouped GEMMs' offsets
+ * contract (the debug mode above): copies group_offsets (DEVICE int32
+ * [G+1]) to the host on `stream`, waits for the copy, and returns
+ * FP8BQ_ERR_BAD_SHAPE unless [0] = 0, the offsets are non-decreasing and
+ * [G] = M_total.  Synchronous; launches no kernel.  G >= 1.
+ */
+fp8bq_status fp8bq_check_group_offsets(const int32_t* group_offsets, int64_t G, int64_t M_total, void* stream);
 
 /*
  * fp8bq_encode_e4m3 -- the library's float32 -> E4M3 conversion on its own

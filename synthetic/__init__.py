@@ -37,6 +37,7 @@ from .gen import (
     moe_topk,
     gather_rows,
     device_bf16_normal,
+    device_activations,
     f32_to_bf16_bits,
     ROLLOUT_TRAIN_BATCH,
     rollout_batch,
@@ -51,6 +52,7 @@ __all__ = [
     "moe_topk",
     "gather_rows",
     "device_bf16_normal",
+    "device_activations",
     "f32_to_bf16_bits",
     "ROLLOUT_TRAIN_BATCH",
     "rollout_batch",

@@ -107,6 +107,25 @@ def device_bf16_normal(shape, std, seed, device="cuda", chunk_rows=4096):
     return out
 
 
+def device_activations(m, k, seed, outlier_frac=0.0, outlier_mult=1.0, device="cuda", chunk_rows=4096):
+    """BF16 activations [m][k] of N(0,1) drawn on ``device``, with
+    round(outlier_frac * k) "outlier channels" (whole K columns, chosen with
+    a seeded CPU generator) multiplied by ``outlier_mult`` in float32 before
+    the single rounding to BF16.  Returns ``(tensor, outlier_columns)``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    cols = torch.randperm(k, generator=torch.Generator().manual_seed(int(seed) + 1))[: round(outlier_frac * k)]
+    mult = torch.ones(k, dtype=torch.float32)
+    mult[cols] = float(outlier_mult)
+    mult = mult.to(device)
+    out = torch.empty((m, k), dtype=torch.bfloat16, device=device)
+    for r0 in range(0, m, chunk_rows):
+        r1 = min(m, r0 + chunk_rows)
+        z = torch.randn((r1 - r0, k), generator=g, dtype=torch.float32, device=device)
+        out[r0:r1] = (z * mult).to(torch.bfloat16)
+    return out, torch.sort(cols).values
+
+
 # Rollout batch of the FP8-RL experiments: 32 prompts x 16 responses per
 # training step, responses of up to 20,000 tokens.
 ROLLOUT_TRAIN_BATCH = {"responses": 32 * 16, "max_len": 20000}

@@ -91,3 +91,66 @@ def test_gemm_counter_summary_of_synthetic_csvs(tmp_path):
     assert len(wave) == 1
     assert [c.strip() for c in wave[0].strip("|").split("|")][1:] == [
         "0.400", "0.300", "0.050", "0.600", "0.200", "0.100", "0.020", "0.500"]
+
+
+def test_bw_counter_summary_of_synthetic_csvs(tmp_path):
+    """The bandwidth-kernel summary matches the library's dispatches to the
+    cases in launch order (other kernels skipped), scales the counters by the
+    copy calibration and divides by the algorithmic bytes: a case whose
+    counters read exactly its algorithmic bytes after a x2 fetch scale, in
+    1 ms, reads ratio 1.000 and (bytes / 1 ms) GB/s."""
+    import csv
+
+    sys.path.insert(0, ROOT)
+    import bench
+
+    cases = bench.bw_profile_cases()
+    reps = bench.BW_PROFILE_REPS
+    kib = 1 << 30
+
+    def kname(prefix):
+        return "void fp8bq::(anonymous namespace)::%s<4>(args)" % prefix
+
+    def write_counter(sub, rows):
+        d = tmp_path / sub
+        d.mkdir()
+        with open(d / "p_counter_collection.csv", "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for r in rows:
+                w.writerow(r)
+
+    def pass_rows(counter, part):
+        rows = [{"Dispatch_Id": 1, "Kernel_Name": "kv_init_kernel", "Counter_Name": counter, "Counter_Value": 5}]
+        for i in range(len(cases) * reps):
+            label, prefix, algo = cases[i // reps]
+            algo = 1_000_000 if algo is None else algo
+            v = algo * part / 1024.0
+            rows.append({"Dispatch_Id": 10 + i, "Kernel_Name": kname(prefix), "Counter_Name": counter,
+                         "Counter_Value": v / 2.0 if counter == "FETCH_SIZE" else v})
+        return rows
+
+    write_counter("fetch", pass_rows("FETCH_SIZE", 0.75))
+    write_counter("write", pass_rows("WRITE_SIZE", 0.25))
+    write_counter("copy_fetch", [{"Dispatch_Id": 1, "Kernel_Name": "copyBuffer", "Counter_Name": "FETCH_SIZE",
+                                  "Counter_Value": kib / 1024.0 / 2.0}])
+    write_counter("copy_write", [{"Dispatch_Id": 1, "Kernel_Name": "copyBuffer", "Counter_Name": "WRITE_SIZE",
+                                  "Counter_Value": kib / 1024.0}])
+    (tmp_path / "kt").mkdir()
+    with open(tmp_path / "kt" / "kt_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i in range(len(cases) * reps):
+            w.writerow({"Dispatch_Id": 10 + i, "Kernel_Name": kname(cases[i // reps][1]), "Start_Timestamp": 0,
+                        "End_Timestamp": 1_000_000})
+    r = _run("--bw-counter-summary", str(tmp_path))
+    assert r.returncode == 0, r.stderr
+    n = len(cases) * reps
+    assert "kernel trace %d, fetch %d, write %d (expected %d)" % (n, n, n, n) in r.stdout
+    assert "FETCH_SIZE x2.000, WRITE_SIZE x1.000" in r.stdout
+    label, _, algo = cases[0]
+    row = [line for line in r.stdout.splitlines() if line.startswith("| %s |" % label)]
+    assert len(row) == 1
+    cells = [c.strip() for c in row[0].strip("|").split("|")]
+    assert cells[2] == "1000.0" and cells[6] == "1.000"
+    assert cells[7] == "%.0f" % (algo / 1e6)

@@ -50,7 +50,7 @@ def test_quantizer_fragment_order_matches_row_major_prefill(fb, m, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 130, 256), (48, 384, 768), (272, 520, 512), (256, 256, 2048)])
-def test_gemm_afrag_against_oracle_and_row_major(fb, monkeypatch, m, n, k):
+def test_gemm_afrag_against_oracle_and_row_major(fb, m, n, k):
     announce("afrag gemm", m, n, k)
     x, _ = activations(m, k, (m, n, k, 0))
     w = bf16_normal((n, k), 0.02, (m, n, k, 1))
@@ -60,27 +60,25 @@ def test_gemm_afrag_against_oracle_and_row_major(fb, monkeypatch, m, n, k):
     y = fb.gemm_w8a8_blockscaled_afrag(dev(oracle.act_fragment_order(qa)), dev(sa), dev(qw), dev(sw))
     got = device_to_bits(y)
     assert_gemm_close(got, oracle.gemm_ref(qa, sa, qw, sw))
-    monkeypatch.setenv("FP8BQ_GEMM_TILE", "wide")
-    ref = device_to_bits(fb.gemm_w8a8_blockscaled(dev(qa), dev(sa), dev(qw), dev(sw)))
+    ref = device_to_bits(fb.gemm_w8a8_blockscaled(dev(qa), dev(sa), dev(qw), dev(sw), tile="wide"))
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("n,k", [(6144, 4096), (4096, 12288)])
-def test_gemm_afrag_prefill_bit_identical(fb, monkeypatch, n, k):
-    """Qwen3-8B prefill shapes (M = 8192): same bits as the row-major tile."""
+@pytest.mark.parametrize("n,k", [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)])
+def test_gemm_afrag_prefill_bit_identical(fb, n, k):
+    """The four Qwen3-8B prefill shapes (M = 8192): same bits as the row-major tile."""
     m = 8192
     announce("afrag gemm prefill", m, n, k)
     x = device_bf16_normal((m, k), 1.0, seed=11)
     wq, ws = fb.quantize_weight_blockwise(device_bf16_normal((n, k), 0.02, seed=12))
     q, s = fb.quantize_act_per_token_group(x)
     qf, _ = fb.quantize_act_per_token_group_frag(x)
-    monkeypatch.setenv("FP8BQ_GEMM_TILE", "wide")
-    y0 = fb.gemm_w8a8_blockscaled(q, s, wq, ws)
+    y0 = fb.gemm_w8a8_blockscaled(q, s, wq, ws, tile="wide")
     y1 = fb.gemm_w8a8_blockscaled_afrag(qf, s, wq, ws)
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
 
 
-def test_gemm_afrag_largest_k(fb, monkeypatch):
+def test_gemm_afrag_largest_k(fb):
     """K = 2^22: 256 rows of fragment-order codes span 2^30 bytes."""
     m, n, k = 256, 3, 1 << 22
     announce("afrag gemm largest K", m, n, k)
@@ -92,8 +90,7 @@ def test_gemm_afrag_largest_k(fb, monkeypatch):
     sa = torch.rand((m, k // 128), generator=g, device="cuda") + 0.5
     sw = torch.rand((1, k // 128), generator=g, device="cuda") + 0.5
     qf = qa.view(m // 16, 16, k // 128, 2, 4, 16).permute(0, 2, 3, 4, 1, 5).contiguous().view(m, k)
-    monkeypatch.setenv("FP8BQ_GEMM_TILE", "wide")
-    y0 = fb.gemm_w8a8_blockscaled(qa, sa, qw, sw)
+    y0 = fb.gemm_w8a8_blockscaled(qa, sa, qw, sw, tile="wide")
     del qa
     y1 = fb.gemm_w8a8_blockscaled_afrag(qf, sa, qw, sw)
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))

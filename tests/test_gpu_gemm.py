@@ -11,12 +11,15 @@ GEMM) and compare sampled outputs with the oracle's quantize-then-multiply
 of the same BF16 inputs.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from helpers import (
+    ROOT,
     announce,
     assert_gemm_close,
     bf16_bits_to_device,
@@ -40,8 +43,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def gpu_gemm(fb, qa, sa, qw, sw):
-    y = fb.gemm_w8a8_blockscaled(_dev(qa), _dev(sa), _dev(qw), _dev(sw))
+def gpu_gemm(fb, qa, sa, qw, sw, tile=None):
+    y = fb.gemm_w8a8_blockscaled(_dev(qa), _dev(sa), _dev(qw), _dev(sw), tile=tile)
     return device_to_bits(y)
 
 
@@ -73,17 +76,16 @@ TILES = ["skinny64", "skinny48", "wide", "decode_panel", "deep", "panel192"]
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("m,n,k", [(1, 1, 128), (37, 130, 256), (130, 300, 384), (257, 129, 1024), (300, 520, 2048)])
-def test_gemm_every_tile_kernel(fb, monkeypatch, tile, m, n, k):
+def test_gemm_every_tile_kernel(fb, tile, m, n, k):
     """Each tile kernel on ragged shapes and 1..16 K-blocks (odd and even
-    trip counts of the pipelined loops), forced through FP8BQ_GEMM_TILE."""
+    trip counts of the pipelined loops), named through gemm_w8a8_blockscaled_tile."""
     announce("gemm tile", tile, m, n, k)
-    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
     qa, sa, qw, sw = _oracle_inputs(m, n, k, 90 + m + n)
-    assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw), oracle.gemm_ref(qa, sa, qw, sw))
+    assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw, tile), oracle.gemm_ref(qa, sa, qw, sw))
 
 
 @pytest.mark.parametrize("tile", TILES)
-def test_gemm_every_tile_random_scales(fb, monkeypatch, tile):
+def test_gemm_every_tile_random_scales(fb, tile):
     """Each tile kernel with a different scale in every weight block,
     activation row and K-block (tiles that straddle scale blocks, a partial
     last block, zero-scale rows).  The spread (2^-3..2^3) keeps every
@@ -91,7 +93,6 @@ def test_gemm_every_tile_random_scales(fb, monkeypatch, tile):
     is checked on its own, so a scale applied to the wrong rows, block or
     K-block fails."""
     announce("gemm tile random scales", tile)
-    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
     rng = np.random.default_rng(35)
     m, n, k = 300, 520, 640
     qa = rng.integers(0, 256, (m, k)).astype(np.uint8)
@@ -102,7 +103,7 @@ def test_gemm_every_tile_random_scales(fb, monkeypatch, tile):
     sw = np.exp2(rng.uniform(-3, 3, ((n + 127) // 128, k // 128))).astype(np.float32)
     zero_rows = [0, 63, 64, 257]
     sa[zero_rows] = 0
-    y = gpu_gemm(fb, qa, sa, qw, sw)
+    y = gpu_gemm(fb, qa, sa, qw, sw, tile)
     ref = oracle.gemm_ref(qa, sa, qw, sw)
     assert np.all((y[zero_rows] & 0x7FFF) == 0)
     for r in range(m):
@@ -203,19 +204,18 @@ def _grouped_oracle_inputs(counts, n, k, seed):
     return qa, sa, qw, sw, off
 
 
-def gpu_grouped(fb, qa, sa, qw, sw, off):
-    y = fb.grouped_gemm_w8a8_blockscaled(_dev(qa), _dev(sa), _dev(qw), _dev(sw), _dev(off))
+def gpu_grouped(fb, qa, sa, qw, sw, off, tile=None):
+    y = fb.grouped_gemm_w8a8_blockscaled(_dev(qa), _dev(sa), _dev(qw), _dev(sw), _dev(off), tile=tile)
     return device_to_bits(y)
 
 
 @pytest.mark.parametrize("tile", ["wide", "decode_panel", "deep", "deep_persistent"])
 @pytest.mark.parametrize("counts", [[3, 0, 17, 1, 0], [0, 0, 300, 0], [129], [0, 128, 0, 1, 255, 0, 0, 2],
                                     [1] * 40, [257, 511, 70]])
-def test_grouped_small(fb, monkeypatch, tile, counts):
+def test_grouped_small(fb, tile, counts):
     announce("grouped small", tile, counts)
-    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
     qa, sa, qw, sw, off = _grouped_oracle_inputs(counts, 256, 384, 50 + len(counts))
-    y = gpu_grouped(fb, qa, sa, qw, sw, off)
+    y = gpu_grouped(fb, qa, sa, qw, sw, off, tile)
     ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, off)
     for e in range(len(counts)):
         lo, hi = off[e], off[e + 1]
@@ -226,11 +226,10 @@ def test_grouped_small(fb, monkeypatch, tile, counts):
 @pytest.mark.parametrize("tile", ["wide", "decode_panel", "deep", "deep_persistent"])
 @pytest.mark.parametrize("counts,div", [([3, 0, 17, 1, 0], 1), ([0, 128, 0, 1, 255, 0, 0, 2], 8), ([257, 511, 70], 3),
                                         ([1] * 40, 2)])
-def test_grouped_gather(fb, monkeypatch, tile, counts, div):
+def test_grouped_gather(fb, tile, counts, div):
     """Row m of the output uses row a_rows[m] // div of a (MoE tokens read
     through their routed pairs); rows naming no row of a give zeros."""
     announce("grouped gather", tile, counts, div)
-    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
     n, k = 256, 384
     g = len(counts)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -246,7 +245,7 @@ def test_grouped_gather(fb, monkeypatch, tile, counts, div):
         rows[1] = -5               # no row
         rows[m // 2] = m_a * div   # one past the last row
     y = device_to_bits(fb.grouped_gemm_w8a8_blockscaled_gather(_dev(qa), _dev(sa), _dev(rows), div, _dev(qw),
-                                                                _dev(sw), _dev(off)))
+                                                                _dev(sw), _dev(off), tile=tile))
     src = rows // div
     valid = (rows >= 0) & (src < m_a)
     qg = np.where(valid[:, None], qa[np.clip(src, 0, m_a - 1)], 0).astype(np.uint8)
@@ -310,25 +309,60 @@ def test_grouped_moe_full_size_sampled(fb, proj):
         assert_gemm_close(got, ref)
 
 
-def test_offsets_debug_mode(fb, monkeypatch):
-    """FP8BQ_CHECK_OFFSETS=1 rejects offsets that break the contract before
-    launching anything; valid offsets run as usual."""
-    announce("offsets debug mode")
+def test_offsets_check(fb):
+    """The offsets checker rejects offsets that break the contract; valid
+    offsets pass and the GEMM runs as usual."""
+    announce("offsets check")
     qa, sa, qw, sw, off = _grouped_oracle_inputs([5, 0, 9], 128, 256, 80)
-    monkeypatch.setenv("FP8BQ_CHECK_OFFSETS", "1")
-    y = gpu_grouped(fb, qa, sa, qw, sw, off)   # valid: runs
+    fb.check_group_offsets(_dev(off), 14)
+    y = gpu_grouped(fb, qa, sa, qw, sw, off)
     assert_gemm_close(y, oracle.grouped_gemm_ref(qa, sa, qw, sw, off))
     for bad in ([0, 9, 5, 14], [1, 5, 5, 14], [0, 5, 5, 13]):
         with pytest.raises(fb.FP8BQError, match="invalid shape"):
-            gpu_grouped(fb, qa, sa, qw, sw, np.array(bad, np.int32))
-    rows = np.arange(14, dtype=np.int32)
-    with pytest.raises(fb.FP8BQError, match="invalid shape"):
-        fb.grouped_gemm_w8a8_blockscaled_gather(_dev(qa), _dev(sa), _dev(rows), 1, _dev(qw), _dev(sw),
-                                                _dev(np.array([0, 9, 5, 14], np.int32)))
+            fb.check_group_offsets(_dev(np.array(bad, np.int32)), 14)
+
+
+_DEBUG_MODE_CHILD = """
+import numpy as np, torch
+import fp8_blockwise_quantized_quantize_amd as fb
+a = torch.zeros((14, 256), dtype=torch.uint8, device="cuda")
+sa = torch.ones((14, 2), device="cuda")
+w = torch.zeros((3, 128, 256), dtype=torch.uint8, device="cuda")
+sw = torch.ones((3, 1, 2), device="cuda")
+rows = torch.arange(14, dtype=torch.int32, device="cuda")
+good = torch.tensor([0, 5, 5, 14], dtype=torch.int32, device="cuda")
+fb.grouped_gemm_w8a8_blockscaled(a, sa, w, sw, good)
+for bad in ([0, 9, 5, 14], [1, 5, 5, 14], [0, 5, 5, 13]):
+    off = torch.tensor(bad, dtype=torch.int32, device="cuda")
+    for call in (lambda: fb.grouped_gemm_w8a8_blockscaled(a, sa, w, sw, off),
+                 lambda: fb.grouped_gemm_w8a8_blockscaled_gather(a, sa, rows, 1, w, sw, off)):
+        try:
+            call()
+        except fb.FP8BQError as e:
+            assert "invalid shape" in str(e)
+        else:
+            raise SystemExit("bad offsets accepted")
+torch.cuda.synchronize()
+print("debug mode ok", flush=True)
+"""
+
+
+def test_offsets_debug_mode_from_the_environment():
+    """FP8BQ_CHECK_OFFSETS=1 (read once per process, so in a process of its
+    own) makes every grouped call check its offsets and reject broken ones
+    before launching anything."""
+    import subprocess
+    import sys
+
+    announce("offsets debug mode (child process)")
+    env = dict(os.environ, FP8BQ_CHECK_OFFSETS="1")
+    r = subprocess.run([sys.executable, "-c", _DEBUG_MODE_CHILD], env=env, cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and "debug mode ok" in r.stdout, r.stdout + r.stderr
 
 
 @pytest.mark.parametrize("tile", TILES)
-def test_gemm_largest_k(fb, monkeypatch, tile):
+def test_gemm_largest_k(fb, tile):
     """K = 2^22, the largest K the boundary accepts: a 256-row activation
     panel then spans 2^30 bytes, still addressed with 32-bit buffer offsets
     (the 256-row tiles read rows up to 255 * 2^22 bytes in), over 32768
@@ -338,7 +372,6 @@ def test_gemm_largest_k(fb, monkeypatch, tile):
     k = 1 << 22
     m, n = 256, 3
     announce("gemm largest K", tile, m, n, k)
-    monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
     g = torch.Generator(device="cuda").manual_seed(2201)
     qa = torch.randint(0, 256, (m, k), generator=g, dtype=torch.uint8, device="cuda")
     qa[(qa & 0x7F) == 0x7F] = 0
@@ -346,7 +379,7 @@ def test_gemm_largest_k(fb, monkeypatch, tile):
     qw[(qw & 0x7F) == 0x7F] = 0
     sa = torch.rand((m, k // 128), generator=g, device="cuda") + 0.5
     sw = torch.rand((1, k // 128), generator=g, device="cuda") + 0.5
-    y = fb.gemm_w8a8_blockscaled(qa, sa, qw, sw)
+    y = fb.gemm_w8a8_blockscaled(qa, sa, qw, sw, tile=tile)
     torch.cuda.synchronize()
     rows = [0, 1, 128, 255]
     ref = oracle.gemm_ref(qa[rows].cpu().numpy(), sa[rows].cpu().numpy(), qw.cpu().numpy(), sw.cpu().numpy())
@@ -361,24 +394,20 @@ def test_gemm_largest_k(fb, monkeypatch, tile):
 
 
 @pytest.mark.parametrize("tile", [None, "deep_persistent"])
-def test_grouped_more_experts_than_the_persistent_table(fb, monkeypatch, tile):
+def test_grouped_more_experts_than_the_persistent_table(fb, tile):
     """1100 experts, most of them empty: above the 1024 experts whose tile
     prefix the persistent kernel keeps in LDS, so the default (and even a
     forced deep_persistent) runs the per-tile kernel; 1024 experts exactly
     still run persistent."""
     for g_total in (1100, 1024):
         announce("grouped many experts", tile, g_total)
-        if tile:
-            monkeypatch.setenv("FP8BQ_GEMM_TILE", tile)
-        else:
-            monkeypatch.delenv("FP8BQ_GEMM_TILE", raising=False)
         rng = np.random.default_rng(g_total)
         counts = np.zeros(g_total, np.int64)
         busy = rng.choice(g_total, 24, replace=False)
         counts[busy] = rng.integers(1, 300, 24)
         counts[-1] = 5  # the last expert's rows end the offsets
         qa, sa, qw, sw, off = _grouped_oracle_inputs(counts, 128, 256, 90 + g_total)
-        y = gpu_grouped(fb, qa, sa, qw, sw, off)
+        y = gpu_grouped(fb, qa, sa, qw, sw, off, tile)
         ref = oracle.grouped_gemm_ref(qa, sa, qw, sw, off)
         for e in np.nonzero(counts)[0]:
             lo, hi = off[e], off[e + 1]

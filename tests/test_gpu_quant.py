@@ -226,3 +226,32 @@ def test_weights_multi_matches_single():
         rq, rs = oracle.quant_weight_blockwise(b)
         assert np.array_equal(q.cpu().numpy(), rq), sh
         assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32)), sh
+
+
+def test_acts_multi_matches_oracle(fb):
+    """quantize_acts_per_token_group_multi: one launch over the four decode
+    activations of a Qwen3-8B layer (M = 256; K = 4096 x 3 and 12288) plus
+    ragged shapes (K % 8 != 0, a partial last group, one row, empty) gives
+    each one the oracle's codes and scales."""
+    shapes = [(256, k) for _, _, k in LAYER_SHAPES_QWEN3_8B] + [(7, 300), (1, 1), (33, 4100), (0, 256), (5, 8)]
+    announce("acts multi", shapes)
+    xs_bits = []
+    for i, (m, k) in enumerate(shapes):
+        if m * k == 0:
+            xs_bits.append(np.zeros((m, k), np.uint16))
+        else:
+            xs_bits.append(activations(m, k, (150 + i, 0), n_outliers=min(4, k), outlier_mult=50.0)[0])
+    xs = [bf16_bits_to_device(b) for b in xs_bits]
+    res = fb.quantize_acts_per_token_group_multi(xs)
+    torch.cuda.synchronize()
+    for (q, s), b, sh in zip(res, xs_bits, shapes):
+        if sh[0] * sh[1] == 0:
+            continue
+        assert_same((q.cpu().numpy(), s.cpu().numpy()), oracle.quant_act_per_token_group(b), ("acts multi", sh))
+
+
+def test_acts_multi_limits(fb):
+    x = torch.zeros((2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fb.quantize_acts_per_token_group_multi([x] * (fb.MAX_ACT_DESCS + 1))
+    assert fb.quantize_acts_per_token_group_multi([]) == []
