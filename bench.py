@@ -495,6 +495,9 @@ def decode_step(fb, dev, with_cpu):
         sets.append(layers)
     stream = torch.cuda.current_stream()
     ev = []
+    # one workspace serves the K-split GEMMs of a step (ordered on one stream)
+    need = max(fb.splitk_workspace_bytes(M, n, k) for _, n, k in LAYER_SHAPES_QWEN3_8B)
+    wsp = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
     def step(record, s):
         ls = sets[s % SETS]
@@ -508,7 +511,7 @@ def decode_step(fb, dev, with_cpu):
         if record:
             e[2].record(stream)
         for L in ls:
-            fb.gemm_w8a8_blockscaled(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
+            fb.gemm_w8a8_blockscaled_splitk(L["xq"], L["xs"], L["wq"], L["ws"], L["y"], workspace=wsp)
         if record:
             e[3].record(stream)
             ev.append(e)
@@ -539,8 +542,49 @@ def decode_step(fb, dev, with_cpu):
            "gemm": {"launches": 4, "bytes": gm_b, "TFLOPs": round(flops / ph["gemm"] / 1e9, 1),
                     "GBps": round(gm_b / ph["gemm"] / 1e6, 1),
                     "frac_hbm": round(gm_b / ph["gemm"] / 1e6 / HBM_PEAK_GBPS, 4)}}
+    # each GEMM on its own, as the step runs it (graph replays over the four
+    # buffer sets)
+    per = {}
+    for i, L in enumerate(layers):
+        f = 2 * M * L["n"] * L["k"]
+        byt = M * L["k"] + L["n"] * L["k"] + 2 * M * L["n"] + L["xs"].numel() * 4 + L["ws"].numel() * 4
+        us, _ = _time_graph_ms([lambda t=t[i]: fb.gemm_w8a8_blockscaled_splitk(t["xq"], t["xs"], t["wq"], t["ws"],
+                                                                               t["y"], workspace=wsp) for t in sets])
+        per[L["name"]] = {"k_pieces": max(1, fb.splitk_workspace_bytes(M, L["n"], L["k"]) // (4 * M * L["n"])),
+                          "us": round(us * 1e3, 2), "frac_hbm": round(byt / us / 1e6 / HBM_PEAK_GBPS, 4),
+                          "TFLOPs": round(f / us / 1e9, 1)}
+    res["gemm_each"] = per
+    res["splitk_small_batch"] = splitk_small_batch(fb, dev, sets[0])
+    step(False, 0)
+    torch.cuda.synchronize()
     if with_cpu:
         res["cpu_baseline"], res["parity"] = decode_cpu_and_parity(layers, M, flops)
+    return res
+
+
+def splitk_small_batch(fb, dev, layer_set):
+    """The K-split GEMM against the unsplit one at small decode batches
+    (16, 64 and 128 tokens) on the Qwen3-8B layer weights, which the split
+    rule splits where K is long against M (the down projection): graph
+    replays over four weight copies (Infinity Cache rotated)."""
+    import torch
+
+    res = {}
+    for m in (16, 64, 128):
+        for L in layer_set:
+            n, k = L["n"], L["k"]
+            need = fb.splitk_workspace_bytes(m, n, k)
+            if need == 0:
+                continue
+            wq = [L["wq"]] + [L["wq"].clone() for _ in range(3)]
+            xq, xs = L["xq"][:m].contiguous(), L["xs"][:m].contiguous()
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            wsp = torch.empty(need, dtype=torch.uint8, device=dev)
+            sk, _ = _time_graph_ms([lambda w=w: fb.gemm_w8a8_blockscaled_splitk(xq, xs, w, L["ws"], y, workspace=wsp)
+                                    for w in wq])
+            pl, _ = _time_graph_ms([lambda w=w: fb.gemm_w8a8_blockscaled(xq, xs, w, L["ws"], y) for w in wq])
+            res["%s_M%d" % (L["name"], m)] = {"k_pieces": need // (4 * m * n), "splitk_us": round(sk * 1e3, 2),
+                                               "unsplit_us": round(pl * 1e3, 2)}
     return res
 
 

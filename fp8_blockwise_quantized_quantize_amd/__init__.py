@@ -30,6 +30,8 @@ __all__ = [
     "quantize_acts_per_token_group_multi",
     "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
+    "gemm_w8a8_blockscaled_splitk",
+    "splitk_workspace_bytes",
     "gemm_w8a8_blockscaled_afrag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
@@ -61,6 +63,8 @@ EXPORTS = (
     "quantize_acts_per_token_group_multi",
     "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
+    "gemm_w8a8_blockscaled_splitk",
+    "gemm_w8a8_blockscaled_splitk_workspace",
     "gemm_w8a8_blockscaled_afrag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
@@ -116,6 +120,8 @@ def _load():
     lib.grouped_gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled_gather.argtypes = [p, p, i64, p, i64, p, p, p, p, i64, i64, i64, i64, p]
     lib.gemm_w8a8_blockscaled_tile.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
+    lib.gemm_w8a8_blockscaled_splitk.argtypes = [p, p, p, p, p, i64, i64, i64, p, i64, p]
+    lib.gemm_w8a8_blockscaled_splitk_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
     lib.grouped_gemm_w8a8_blockscaled_tile.argtypes = [p, p, i64, p, i64, p, p, p, p, i64, i64, i64, i64, i32, p]
     lib.fp8bq_check_group_offsets.argtypes = [p, i64, i64, p]
     lib.fp8bq_encode_e4m3.argtypes = [p, p, i64, i32, p]
@@ -363,6 +369,43 @@ def gemm_w8a8_blockscaled(a, a_scale, w, w_scale, out=None, tile=None):
             _check("gemm_w8a8_blockscaled_tile",
                    _lib.gemm_w8a8_blockscaled_tile(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)), m,
                                                    n, k, _tile_id(tile), _stream(a)))
+    return out
+
+
+def splitk_workspace_bytes(m, n, k):
+    """Workspace bytes gemm_w8a8_blockscaled_splitk needs for (M, N, K) on the current device (0: no split)."""
+    b = ctypes.c_int64(0)
+    _check("gemm_w8a8_blockscaled_splitk_workspace",
+           _lib.gemm_w8a8_blockscaled_splitk_workspace(int(m), int(n), int(k), ctypes.byref(b)))
+    return b.value
+
+
+def gemm_w8a8_blockscaled_splitk(a, a_scale, w, w_scale, out=None, workspace=None):
+    """gemm_w8a8_blockscaled for few activation rows (M <= 256) with K split
+    over more workgroups; ``workspace``: a uint8 device tensor of at least
+    splitk_workspace_bytes(M, N, K) bytes (allocated here when None)."""
+    m, k = a.shape
+    n = w.shape[0]
+    _require(a, "a", _U8, (m, k))
+    dev = a.device
+    _require(a_scale, "a_scale", torch.float32, (m, k // BLOCK), dev)
+    _require(w, "w", _U8, (n, k), dev)
+    _require(w_scale, "w_scale", torch.float32, (_cdiv(n, BLOCK), k // BLOCK), dev)
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", _BF16, (m, n), dev)
+    with torch.cuda.device(dev):
+        if workspace is None:
+            need = splitk_workspace_bytes(m, n, k)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the device of a")
+        _check("gemm_w8a8_blockscaled_splitk",
+               _lib.gemm_w8a8_blockscaled_splitk(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)), m,
+                                                 n, k, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                 _stream(a)))
     return out
 
 

@@ -117,6 +117,7 @@ const char* fp8bq_status_string(fp8bq_status s) {
     case FP8BQ_ERR_LAUNCH: return "kernel launch failed";
     case FP8BQ_ERR_DEVICE: return "current device is not an AMD gfx950 GPU";
     case FP8BQ_ERR_BAD_ARG: return "invalid scalar argument or option combination";
+    case FP8BQ_ERR_WORKSPACE: return "workspace missing, misaligned or too small for this call";
     default: return "unknown status";
   }
 }
@@ -262,6 +263,55 @@ fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, c
                                    const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
                                    void* stream) {
   return gemm_w8a8_blockscaled_tile(a_fp8, a_scale, w_fp8, w_scale, y_bf16, M, N, K, FP8BQ_TILE_AUTO, stream);
+}
+
+// The GEMM shape checks shared by the dense entry points.
+fp8bq_status check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t* mn) {
+  if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
+  int64_t mk, nk, bytes;
+  if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, mn) || !mul_ok(*mn, 4, &bytes))
+    return FP8BQ_ERR_BAD_SHAPE;
+  return FP8BQ_OK;
+}
+
+fp8bq_status gemm_w8a8_blockscaled_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
+  try {
+    if (!bytes) return FP8BQ_ERR_NULL_PTR;
+    int64_t mn;
+    fp8bq_status st = check_gemm_shape(M, N, K, &mn);
+    if (st != FP8BQ_OK) return st;
+    st = check_device();
+    if (st != FP8BQ_OK) return st;
+    *bytes = mn == 0 ? 0 : fp8bq::gemm_splitk_workspace_bytes(M, N, K);
+    return FP8BQ_OK;
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status gemm_w8a8_blockscaled_splitk(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                          const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                          void* workspace, int64_t workspace_bytes, void* stream) {
+  try {
+    int64_t mn;
+    fp8bq_status st = check_gemm_shape(M, N, K, &mn);
+    if (st != FP8BQ_OK) return st;
+    if (mn == 0) return FP8BQ_OK;
+    if (!y_bf16) return FP8BQ_ERR_NULL_PTR;
+    if (K > 0 && (!a_fp8 || !a_scale || !w_fp8 || !w_scale)) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(y_bf16) || (K > 0 && (!aligned16(a_fp8) || !aligned16(a_scale) || !aligned16(w_fp8) ||
+                                         !aligned16(w_scale))))
+      return FP8BQ_ERR_MISALIGNED;
+    st = check_device();
+    if (st != FP8BQ_OK) return st;
+    const int64_t need = fp8bq::gemm_splitk_workspace_bytes(M, N, K);
+    if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need)) return FP8BQ_ERR_WORKSPACE;
+    clear_last_error();
+    return launched(fp8bq::launch_gemm_splitk(a_fp8, a_scale, w_fp8, w_scale, y_bf16, M, N, K, workspace,
+                                              workspace_bytes, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
 }
 
 fp8bq_status quantize_act_per_token_group_frag(const uint16_t* x_bf16, uint8_t* x_fp8_frag, float* x_scale,

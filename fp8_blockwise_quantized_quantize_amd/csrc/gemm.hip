@@ -166,6 +166,11 @@ struct Tile {
   const float* sw;
   uint16_t* y;
   int64_t m_lo, m_hi, n0, N, K;
+  // K-blocks [kb0, kb1) of the product (the panel tile only; a K-split
+  // piece), and where that piece goes: FP32 partial rows of stride N at
+  // `part` (nullptr: the BF16 output y).
+  int kb0, kb1;
+  float* part;
   // Gathered activations (grouped GEMM only): output row m reads row
   // a_rows[m] / a_div of a (of a_nrows rows); others read zeros.
   const int32_t* a_rows;
@@ -189,6 +194,18 @@ __device__ __forceinline__ void store4(uint16_t* __restrict__ y, int64_t N, int6
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (n + r < N) dst[r] = (uint16_t)bf16_rne(v[r]);
+  }
+}
+
+// Store four consecutive n of FP32 partial row m (a K-split piece).
+__device__ __forceinline__ void store4_f32(float* __restrict__ p, int64_t N, int64_t m, int64_t n, v4f v) {
+  float* dst = p + m * N + n;
+  if (n + 4 <= N && (N & 3) == 0) {
+    *reinterpret_cast<v4f*>(dst) = v;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) dst[r] = v[r];
   }
 }
 
@@ -434,7 +451,9 @@ struct Panel {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wn = wave % WGN, wm = wave / WGN;
     const int64_t K = t.K;
-    const int KB = (int)(K / kBlock);
+    const int KB = (int)(K / kBlock);  // K-blocks of a row (strides)
+    // this tile's K-blocks: kb0 + 0 .. kb0 + NKB - 1
+    const int kb0 = t.kb0, NKB = t.kb1 - t.kb0;
     const int64_t n_hi = (t.n0 + BN < t.N) ? t.n0 + BN : t.N;
     // weight scale blocks of this wave's rows: nb0, and nb0 + 1 for the
     // fragments in hi_mask (only when a wave's rows can straddle a block);
@@ -504,10 +523,10 @@ struct Panel {
 
     auto dma_scales = [&](int kb, int stage) {
       auto* dst = (__attribute__((address_space(3))) void*)(lds + S * kStage + stage * kScaleBytes + wave * 256);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, dst, 4, scvoff, kb * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, dst, 4, scvoff, (kb0 + kb) * 4, 0, 0);
     };
     auto dma_q = [&](int q, int kb, uint8_t* buf) {
-      const int koff = kb * kBlock;
+      const int koff = (kb0 + kb) * kBlock;
       const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
       auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
       if (q < BN / 64)  // stage rows 0..BN-1: weight rows n0 + r0 ..
@@ -596,16 +615,16 @@ struct Panel {
     };
     auto wait_all = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-    const int kb_last = KB - 1;
-    auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };  // clamped prefetch
-    if (KB > 0) {
+    const int kb_last = NKB - 1;
+    auto nxt = [&](int kb) { return kb < NKB ? kb : kb_last; };  // clamped prefetch
+    if (NKB > 0) {
 #pragma unroll
       for (int st = 0; st < S - 1; ++st) dma_kblock(nxt(st), st);
     }
     // Loads past the last K-block re-load it into a stage nobody reads
     // again, keeping the loop body free of branches.
     int cur = 0;  // stage of K-block k
-    for (int k = 0; k < KB; ++k) {
+    for (int k = 0; k < NKB; ++k) {
       wait_stage();
       barrier();  // stage cur holds K-block k; stage cur - 1 is free
       const int fill = (cur == 0) ? S - 1 : cur - 1;
@@ -624,7 +643,13 @@ struct Panel {
       const int64_t m = t.m_lo + wm * WMR + j * 16 + r16;
       if (m >= t.m_hi) continue;
 #pragma unroll
-      for (int i = 0; i < TN; ++i) store4(t.y, t.N, m, t.n0 + wn * WNR + i * 16 + g * 4, acc[i][j]);
+      for (int i = 0; i < TN; ++i) {
+        const int64_t n = t.n0 + wn * WNR + i * 16 + g * 4;
+        if (t.part != nullptr)
+          store4_f32(t.part, t.N, m, n, acc[i][j]);
+        else
+          store4(t.y, t.N, m, n, acc[i][j]);
+      }
     }
   }
 
@@ -1109,7 +1134,61 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   t.n0 = tn * BN;
   t.N = N; t.K = K;
   t.a_rows = nullptr; t.a_div = 1; t.a_nrows = 0;
+  t.kb0 = 0; t.kb1 = (int)(K / kBlock); t.part = nullptr;
   Kern::run(t, smem);
+}
+
+// K split: workgroup L takes piece s = L' % S of tile L' / S (L' the
+// XCD-aware rank), the K-blocks [s KB / S, (s + 1) KB / S), and stores its
+// FP32 partial tile to part + s * M * N; splitk_reduce_kernel sums them.
+template <class Kern, int BN, int BM>
+__global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_splitk_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ w,
+    const float* __restrict__ sw, float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t tiles_m,
+    int64_t tiles_n, int S) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int64_t L = xcd_linear(blockIdx.x, tiles_m * tiles_n * S);
+  const int piece = (int)(L % S);
+  int64_t tm, tn;
+  tile_of(L / S, tiles_m, tiles_n, &tm, &tn);
+  const int KB = (int)(K / kBlock);
+  Tile t;
+  t.a = a; t.sa = sa; t.w = w; t.sw = sw; t.y = nullptr;
+  t.m_lo = tm * BM;
+  t.m_hi = (t.m_lo + BM < M) ? t.m_lo + BM : M;
+  t.n0 = tn * BN;
+  t.N = N; t.K = K;
+  t.a_rows = nullptr; t.a_div = 1; t.a_nrows = 0;
+  t.kb0 = (int)((int64_t)piece * KB / S);
+  t.kb1 = (int)((int64_t)(piece + 1) * KB / S);
+  t.part = part + (int64_t)piece * M * N;
+  Kern::run(t, smem);
+}
+
+// y = BF16_RNE(p_0 + p_1 + ... + p_{S-1}), summed in that order in FP32
+// (deterministic: the pieces and the order do not depend on timing).  One
+// thread per four consecutive outputs.
+constexpr int kReduceThreads = 256;
+__global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                                       uint16_t* __restrict__ y, int64_t M,
+                                                                       int64_t N, int S) {
+  const int64_t MN = M * N;
+  const int64_t i = ((int64_t)blockIdx.x * kReduceThreads + threadIdx.x) * 4;
+  if (i >= MN) return;
+  if ((N & 3) == 0) {
+    v4f acc = *reinterpret_cast<const v4f*>(part + i);
+    for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const v4f*>(part + (int64_t)s * MN + i);
+    u32x2 pk;
+    pk.x = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
+    pk.y = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
+    *reinterpret_cast<u32x2*>(y + i) = pk;
+  } else {
+    for (int64_t e = i; e < i + 4 && e < MN; ++e) {
+      float acc = part[e];
+      for (int s = 1; s < S; ++s) acc += part[(int64_t)s * MN + e];
+      y[e] = (uint16_t)bf16_rne(acc);
+    }
+  }
 }
 
 // Grouped form: workgroup slot s is mapped to (expert, m-tile) by a prefix
@@ -1182,6 +1261,7 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   t.n0 = tn * BN;
   t.N = N; t.K = K;
   t.a_rows = a_rows; t.a_div = a_div; t.a_nrows = a_nrows;
+  t.kb0 = 0; t.kb1 = (int)KB; t.part = nullptr;
   if constexpr (kGather)
     Kern::run_gather(t, smem);
   else
@@ -1272,6 +1352,7 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
     t.n0 = tn * BN;
     t.N = N; t.K = K;
     t.a_rows = a_rows; t.a_div = a_div; t.a_nrows = a_nrows;
+    t.kb0 = 0; t.kb1 = (int)KB; t.part = nullptr;
     return t;
   };
   Kern::template run_persistent<kGather>(ntiles, tile_at, smem);
@@ -1423,6 +1504,57 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
     default:
       return launch_dense_cfg<Wide, Wide::BN, Wide::BM>(a, sa, w, sw, y, M, N, K, stream);
   }
+}
+
+namespace {
+
+// Pieces of K for the split form.  The FP32 partials cost 2 S M N 4 bytes
+// of traffic next to the N K weight bytes, so the split pays only where K
+// is long against M and each piece keeps enough K-blocks; measured on
+// MI355X (graph replays, weights rotated past the Infinity Cache; us,
+// unsplit -> 8 pieces): M = 16, N = 4096, K = 12288: 21.6 -> 15.9; M = 128
+// same N, K: 23.4 -> 21.6; M = 16, N = 1024, K = 16384: 26.8 -> 16.2; but
+// M = 256, K = 12288: 29.2 -> 30.6 and every K = 4096 shape slower (M = 16,
+// N = 4096: 10.6 -> 11.3; M = 256: 13.5 -> 22.4), with 2 or 4 pieces slower
+// still.  Rule: 8 pieces (fewer when the 128-row weight tiles times 8 do
+// not fit one round of the CUs, at least 4) when M <= 256, 96 M <= K and
+// every piece has at least 8 K-blocks.  1 = no split.
+int splitk_pieces(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || M > DecodePanel::BM || N <= 0 || 96 * M > K) return 1;
+  const int64_t tiles = (N + DecodePanel::BN - 1) / DecodePanel::BN;
+  const int64_t cus = (int64_t)cu_count();
+  int64_t S = cus / tiles;
+  if (S > 8) S = 8;
+  if (S < 4 || K / kBlock < 8 * S) return 1;
+  return (int)S;
+}
+
+}  // namespace
+
+int64_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = splitk_pieces(M, N, K);
+  return S > 1 ? (int64_t)S * M * N * 4 : 0;
+}
+
+hipError_t launch_gemm_splitk(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
+                              int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int S = splitk_pieces(M, N, K);
+  if (S == 1) return launch_gemm(a, sa, w, sw, y, M, N, K, 0, stream);
+  if (workspace == nullptr || workspace_bytes < (int64_t)S * M * N * 4) return hipErrorInvalidValue;
+  using Kern = DecodePanel;
+  const int64_t tiles_m = (M + Kern::BM - 1) / Kern::BM, tiles_n = (N + Kern::BN - 1) / Kern::BN;
+  float* part = static_cast<float*>(workspace);
+  hipLaunchKernelGGL((gemm_splitk_kernel<Kern, Kern::BN, Kern::BM>), dim3((unsigned)(tiles_m * tiles_n * S)),
+                     dim3(threads_of<Kern>()), (size_t)Kern::kLdsBytes, stream, a, sa, w, sw, part, M, N, K, tiles_m,
+                     tiles_n, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = (M * N + 3) / 4;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((units + kReduceThreads - 1) / kReduceThreads)),
+                     dim3(kReduceThreads), 0, stream, part, y, M, N, S);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,

@@ -36,7 +36,7 @@ hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t
 
 // Activations quantized by one launch (descriptors by value in the kernel
 // arguments): desc[t] is an [M][K] BF16 matrix with its outputs; its groups
-// go to workgroups first[t] .. first[t + 1] - 1 (16 groups each).
+// go to workgroups first[t] .. first[t + 1] - 1 (32 groups each).
 constexpr int kMaxActDescs = 16;  // FP8BQ_MAX_ACT_DESCS of the C ABI
 struct ActDesc {
   const uint16_t* x;
@@ -49,7 +49,7 @@ struct ActBatch {
   int64_t first[kMaxActDescs + 1];
   int count;
 };
-constexpr int kActGroupsPerWg = 16;
+constexpr int kActGroupsPerWg = 32;
 
 hipError_t launch_quant_act_multi(const ActBatch& batch, int64_t blocks, hipStream_t stream);
 // the same codes in the MFMA fragment order of the activation operand (M % 16 == 0, K % 128 == 0)
@@ -63,6 +63,14 @@ hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w
 // unknown value returns hipErrorInvalidValue.
 hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y, int64_t M,
                        int64_t N, int64_t K, int tile, hipStream_t stream);
+
+// The K-split form for few activation rows: workspace bytes it needs for
+// this shape on the current device (0: it runs the unsplit GEMM), and the
+// launch (hipErrorInvalidValue when the workspace is smaller).
+int64_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_splitk(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
+                              int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                                const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,

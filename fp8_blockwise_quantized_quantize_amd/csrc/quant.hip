@@ -50,20 +50,13 @@ __device__ __forceinline__ void quant_weight_block(const uint16_t* __restrict__ 
     const float s = scale_from_amax_bits(m);
     if (tid == 0) *sslot = s;
     uint8_t* dst = qm + (row0 + rr) * K + col0 + cc * 8;
-    if (s != 0.0f) {
-      Divisor d(s);
-      if (d.fast) {
+    // One store loop for the three cases (the choice is uniform per block):
+    // 2% faster on the 36-layer sweep than a store loop per case.
+    const Divisor d(s != 0.0f ? s : 1.0f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          __builtin_nontemporal_store(quant8<true>(v[i], d), reinterpret_cast<u32x2*>(dst + (int64_t)16 * i * K));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<u32x2*>(dst + (int64_t)16 * i * K) = quant8<false>(v[i], d);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x2*>(dst + (int64_t)16 * i * K) = zero8(v[i]);
+    for (int i = 0; i < 8; ++i) {
+      const u32x2 o = s == 0.0f ? zero8(v[i]) : (d.fast ? quant8<true>(v[i], d) : quant8<false>(v[i], d));
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(dst + (int64_t)16 * i * K));
     }
     return;
   }
@@ -209,19 +202,25 @@ __global__ __launch_bounds__(kQaThreads) void quant_act_kernel(const uint16_t* _
 
 // Several activations in one launch (the four of a decode layer step take
 // one launch instead of four latency-bound ones): workgroup b takes groups
-// 16 (b - first[t]) .. + 15 of the activation t with first[t] <= b <
-// first[t + 1], one group per quarter wave as in quant_act_kernel<1>.
+// 32 (b - first[t]) .. + 31 of the activation t with first[t] <= b <
+// first[t + 1], two per quarter wave (both loaded before either is
+// reduced; 6.4 vs 6.6 us for one per quarter wave on the four Qwen3-8B
+// decode activations, 6.9 us with four).
+constexpr int kQaMultiPasses = 2;
 __global__ __launch_bounds__(kQaThreads) void quant_act_multi_kernel(const ActBatch batch) {
-  static_assert(kQaThreads / 16 == kActGroupsPerWg, "one group per quarter wave");
+  static_assert(kQaThreads / 16 * kQaMultiPasses == kActGroupsPerWg, "groups per workgroup");
   const int64_t b = blockIdx.x;
   int t = 0;
   while (t + 1 < batch.count && b >= batch.first[t + 1]) ++t;  // uniform scan over <= 16 entries
   const ActDesc& d = batch.desc[t];
   const int G = (int)((d.K + kBlock - 1) / kBlock);
   const int li = threadIdx.x & 15;
-  const int64_t gid = (b - batch.first[t]) * kActGroupsPerWg + (threadIdx.x >> 4);
-  const ActGroup grp = act_group_load(d.x, d.M, d.K, G, gid, li);
-  act_group_store(grp, d.q, d.s, d.K, G, li);
+  const int64_t g0 = (b - batch.first[t]) * kActGroupsPerWg + (threadIdx.x >> 4);
+  ActGroup grp[kQaMultiPasses];
+#pragma unroll
+  for (int p = 0; p < kQaMultiPasses; ++p) grp[p] = act_group_load(d.x, d.M, d.K, G, g0 + 16 * p, li);
+#pragma unroll
+  for (int p = 0; p < kQaMultiPasses; ++p) act_group_store(grp[p], d.q, d.s, d.K, G, li);
 }
 
 // ---------------------------------------------------------------------------

@@ -64,7 +64,8 @@ enum {
   FP8BQ_ERR_MISALIGNED = 3, /* a tensor pointer is not 16-byte aligned */
   FP8BQ_ERR_LAUNCH = 4,     /* the HIP runtime rejected a kernel launch */
   FP8BQ_ERR_DEVICE = 5,     /* the current device is not gfx950, or no device */
-  FP8BQ_ERR_BAD_ARG = 6     /* an invalid scalar argument or option combination */
+  FP8BQ_ERR_BAD_ARG = 6,    /* an invalid scalar argument or option combination */
+  FP8BQ_ERR_WORKSPACE = 7   /* the workspace is missing, misaligned or smaller than the call needs */
 };
 
 /* Static, human-readable text for a status code (host function). */
@@ -196,6 +197,41 @@ enum {
 fp8bq_status gemm_w8a8_blockscaled_tile(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
                                         const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
                                         int tile, void* stream);
+
+/*
+ * gemm_w8a8_blockscaled_splitk -- gemm_w8a8_blockscaled for few activation
+ * rows, with K split over more workgroups ([FP8-RL summary] §3.4.2 Phase
+ * 3: every decode step runs the FP8 GEMMs of each layer on a few hundred
+ * tokens).  With M <= 256 every activation row fits one 256-row panel, so
+ * each weight byte is read by one workgroup; when the 128-row weight tiles
+ * are too few to fill the CUs, K is split into S <= 8 pieces of whole
+ * K-blocks, each piece's FP32 partial tile goes to the workspace, and a
+ * second kernel sums the S partials in piece order and rounds once to
+ * BF16.  The result is deterministic (fixed pieces, fixed order) and meets
+ * the contract of gemm_w8a8_blockscaled (only the FP32 summation order
+ * differs).  Shapes that do not split run gemm_w8a8_blockscaled itself and
+ * need no workspace.
+ *   a_fp8 ... M, N, K  as for gemm_w8a8_blockscaled
+ *   workspace        DEVICE memory of workspace_bytes bytes, 16-byte
+ *                    aligned, owned by the caller; its contents on entry do
+ *                    not matter and are overwritten; it must not be used by
+ *                    other work until the stream has passed this call
+ *   workspace_bytes  at least what gemm_w8a8_blockscaled_splitk_workspace
+ *                    gives for (M, N, K) (S * M * N * 4 bytes; at most
+ *                    32 MiB on a 256-CU device), else FP8BQ_ERR_WORKSPACE
+ */
+fp8bq_status gemm_w8a8_blockscaled_splitk(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                          const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                          void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * gemm_w8a8_blockscaled_splitk_workspace -- the workspace bytes
+ * gemm_w8a8_blockscaled_splitk needs for (M, N, K) on the current device
+ * (the split depends on its CU count), written to *bytes (0: no split).
+ * The shape is checked as in gemm_w8a8_blockscaled.  Host only; launches
+ * nothing.
+ */
+fp8bq_status gemm_w8a8_blockscaled_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes);
 
 /*
  * quantize_act_per_token_group_frag -- quantize_act_per_token_group with

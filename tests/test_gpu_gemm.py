@@ -412,3 +412,51 @@ def test_grouped_more_experts_than_the_persistent_table(fb, tile):
         for e in np.nonzero(counts)[0]:
             lo, hi = off[e], off[e + 1]
             assert_gemm_close(y[lo:hi], ref[lo:hi])
+
+
+# ---------------------------------------------------------------- K split
+
+@pytest.mark.parametrize("m,n,k", [(16, 4096, 12288), (128, 4096, 12288), (64, 1000, 8192), (100, 300, 16384),
+                                   (65, 129, 8192), (33, 520, 9344), (1, 256, 8192)])
+def test_gemm_splitk_against_oracle(fb, m, n, k):
+    """The K-split GEMM for few activation rows and long K: the Qwen3-8B
+    down projection (K = 12288) at 16 and 128 tokens, and ragged shapes
+    (partial tiles in M and N, a K-block count the pieces divide unevenly,
+    one row) meet the 1e-2 bar against the oracle; the workspace the size
+    query names is used, a smaller one is refused, and two calls with
+    different workspace contents give the same bits (a fixed summation
+    order)."""
+    announce("gemm split-K", m, n, k)
+    qa, sa, qw, sw = _oracle_inputs(m, n, k, 140 + m + n, 4, 30.0)
+    need = fb.splitk_workspace_bytes(m, n, k)
+    assert need > 0 and need % (4 * m * n) == 0 and 2 <= need // (4 * m * n) <= 8
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    y = fb.gemm_w8a8_blockscaled_splitk(_dev(qa), _dev(sa), _dev(qw), _dev(sw), workspace=ws)
+    got = device_to_bits(y)
+    print(assert_gemm_close(got, oracle.gemm_ref(qa, sa, qw, sw)))
+    ws.fill_(0xFF)
+    y2 = fb.gemm_w8a8_blockscaled_splitk(_dev(qa), _dev(sa), _dev(qw), _dev(sw), workspace=ws)
+    assert np.array_equal(device_to_bits(y2), got)
+    with pytest.raises(fb.FP8BQError, match="workspace"):
+        fb.gemm_w8a8_blockscaled_splitk(_dev(qa), _dev(sa), _dev(qw), _dev(sw), workspace=ws[: need - 16])
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 4096, 4096), (256, 4096, 12288), (128, 4096, 8192), (512, 4096, 65536),
+                                   (64, 24576, 8192), (256, 6144, 4096)])
+def test_gemm_splitk_unsplit_shapes_run_the_plain_gemm(fb, m, n, k):
+    """Shapes the split rule leaves whole (pieces of fewer than 8 K-blocks,
+    M too large against K, M > 256, weight tiles that fill the CUs; the
+    Qwen3-8B decode shapes at M = 256) need no workspace and give the plain
+    GEMM's bits."""
+    announce("gemm split-K unsplit", m, n, k)
+    assert fb.splitk_workspace_bytes(m, n, k) == 0
+    g = torch.Generator(device="cuda").manual_seed(m + n + k)
+    qa = torch.randint(0, 256, (m, k), generator=g, dtype=torch.uint8, device="cuda")
+    qa[(qa & 0x7F) == 0x7F] = 0
+    qw = torch.randint(0, 256, (n, k), generator=g, dtype=torch.uint8, device="cuda")
+    qw[(qw & 0x7F) == 0x7F] = 0
+    sa = torch.rand((m, k // 128), generator=g, device="cuda") + 0.5
+    sw = torch.rand(((n + 127) // 128, k // 128), generator=g, device="cuda") + 0.5
+    y0 = fb.gemm_w8a8_blockscaled(qa, sa, qw, sw)
+    y1 = fb.gemm_w8a8_blockscaled_splitk(qa, sa, qw, sw, workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
