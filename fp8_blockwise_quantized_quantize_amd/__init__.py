@@ -31,6 +31,7 @@ __all__ = [
     "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
     "gemm_w8a8_blockscaled_splitk",
+    "gemm_w8a8_blockscaled_splitk_noalloc",
     "splitk_workspace_bytes",
     "gemm_w8a8_blockscaled_afrag",
     "grouped_gemm_w8a8_blockscaled",
@@ -65,6 +66,7 @@ EXPORTS = (
     "gemm_w8a8_blockscaled",
     "gemm_w8a8_blockscaled_splitk",
     "gemm_w8a8_blockscaled_splitk_workspace",
+    "gemm_w8a8_blockscaled_splitk_noalloc",
     "gemm_w8a8_blockscaled_afrag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
@@ -122,6 +124,7 @@ def _load():
     lib.gemm_w8a8_blockscaled_tile.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
     lib.gemm_w8a8_blockscaled_splitk.argtypes = [p, p, p, p, p, i64, i64, i64, p, i64, p]
     lib.gemm_w8a8_blockscaled_splitk_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
+    lib.gemm_w8a8_blockscaled_splitk_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled_tile.argtypes = [p, p, i64, p, i64, p, p, p, p, i64, i64, i64, i64, i32, p]
     lib.fp8bq_check_group_offsets.argtypes = [p, i64, i64, p]
     lib.fp8bq_encode_e4m3.argtypes = [p, p, i64, i32, p]
@@ -406,6 +409,27 @@ def gemm_w8a8_blockscaled_splitk(a, a_scale, w, w_scale, out=None, workspace=Non
                _lib.gemm_w8a8_blockscaled_splitk(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)), m,
                                                  n, k, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                                  _stream(a)))
+    return out
+
+
+def gemm_w8a8_blockscaled_splitk_noalloc(a, a_scale, w, w_scale, out):
+    """gemm_w8a8_blockscaled_splitk with the library's static scratch instead
+    of a workspace (for callers that cannot allocate: ``out`` must be given;
+    nothing is allocated here either)."""
+    m, k = a.shape
+    n = w.shape[0]
+    _require(a, "a", _U8, (m, k))
+    dev = a.device
+    _require(a_scale, "a_scale", torch.float32, (m, k // BLOCK), dev)
+    _require(w, "w", _U8, (n, k), dev)
+    _require(w_scale, "w_scale", torch.float32, (_cdiv(n, BLOCK), k // BLOCK), dev)
+    _require(out, "out", _BF16, (m, n), dev)
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    with torch.cuda.device(dev):
+        _check("gemm_w8a8_blockscaled_splitk_noalloc",
+               _lib.gemm_w8a8_blockscaled_splitk_noalloc(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale),
+                                                         _ptr(_u16(out)), m, n, k, _stream(a)))
     return out
 
 

@@ -12,6 +12,7 @@
 
 static_assert(FP8BQ_MAX_WEIGHT_DESCS == fp8bq::kMaxWeightDescs, "descriptor limits of the header and the launcher");
 static_assert(FP8BQ_MAX_ACT_DESCS == fp8bq::kMaxActDescs, "descriptor limits of the header and the launcher");
+static_assert(FP8BQ_SCRATCH_BYTES == 32 * 1024 * 1024, "static scratch size of the header and the GEMM source");
 
 namespace {
 
@@ -118,6 +119,7 @@ const char* fp8bq_status_string(fp8bq_status s) {
     case FP8BQ_ERR_DEVICE: return "current device is not an AMD gfx950 GPU";
     case FP8BQ_ERR_BAD_ARG: return "invalid scalar argument or option combination";
     case FP8BQ_ERR_WORKSPACE: return "workspace missing, misaligned or too small for this call";
+    case FP8BQ_ERR_SCRATCH: return "the call needs more than the library's static scratch (FP8BQ_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -309,6 +311,30 @@ fp8bq_status gemm_w8a8_blockscaled_splitk(const uint8_t* a_fp8, const float* a_s
     clear_last_error();
     return launched(fp8bq::launch_gemm_splitk(a_fp8, a_scale, w_fp8, w_scale, y_bf16, M, N, K, workspace,
                                               workspace_bytes, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
+fp8bq_status gemm_w8a8_blockscaled_splitk_noalloc(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                                  const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N,
+                                                  int64_t K, void* stream) {
+  try {
+    int64_t mn;
+    fp8bq_status st = check_gemm_shape(M, N, K, &mn);
+    if (st != FP8BQ_OK) return st;
+    if (mn == 0) return FP8BQ_OK;
+    if (!y_bf16) return FP8BQ_ERR_NULL_PTR;
+    if (K > 0 && (!a_fp8 || !a_scale || !w_fp8 || !w_scale)) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(y_bf16) || (K > 0 && (!aligned16(a_fp8) || !aligned16(a_scale) || !aligned16(w_fp8) ||
+                                         !aligned16(w_scale))))
+      return FP8BQ_ERR_MISALIGNED;
+    st = check_device();
+    if (st != FP8BQ_OK) return st;
+    if (fp8bq::gemm_splitk_workspace_bytes(M, N, K) > fp8bq::gemm_splitk_scratch_bytes()) return FP8BQ_ERR_SCRATCH;
+    clear_last_error();
+    return launched(fp8bq::launch_gemm_splitk_noalloc(a_fp8, a_scale, w_fp8, w_scale, y_bf16, M, N, K,
+                                                      static_cast<hipStream_t>(stream)));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }

@@ -38,6 +38,7 @@
 // Tiles are ordered so that the workgroups resident on one XCD at a time
 // (consecutive workgroup ids of the same id % 8) share weight and
 // activation panels in that XCD's L2.
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -1555,6 +1556,55 @@ hipError_t launch_gemm_splitk(const uint8_t* a, const float* sa, const uint8_t* 
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((units + kReduceThreads - 1) / kReduceThreads)),
                      dim3(kReduceThreads), 0, stream, part, y, M, N, S);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The K split without a caller workspace, for callers that cannot allocate
+// (code under graph capture, serving loops that forbid it): the partials go
+// to `scratch`, a file-scope device array of kScratchBytes that each GPU the
+// library runs on holds until the process ends.  Its device address is
+// looked up once per device (hipGetSymbolAddress, with that device
+// current) and passed to the kernels like a workspace; host code never
+// uses the array's name for its memory.  Every call on a GPU shares the
+// array: calls that overlap on one GPU race.  The partials are written in
+// full before they are read, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+
+// The device address of `scratch` on the current device.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+int64_t gemm_splitk_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_gemm_splitk_noalloc(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                                      uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (gemm_splitk_workspace_bytes(M, N, K) > kScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_gemm_splitk(a, sa, w, sw, y, M, N, K, ws, kScratchBytes, stream);
 }
 
 hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,

@@ -72,6 +72,12 @@ hipError_t launch_gemm_splitk(const uint8_t* a, const float* sa, const uint8_t* 
                               int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
                               hipStream_t stream);
 
+// The K split with the library's static scratch instead of a workspace:
+// its size, and the launch (hipErrorInvalidValue when the shape needs more).
+int64_t gemm_splitk_scratch_bytes();
+hipError_t launch_gemm_splitk_noalloc(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                                      uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                                const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
                                int tile, hipStream_t stream);

@@ -65,7 +65,8 @@ enum {
   FP8BQ_ERR_LAUNCH = 4,     /* the HIP runtime rejected a kernel launch */
   FP8BQ_ERR_DEVICE = 5,     /* the current device is not gfx950, or no device */
   FP8BQ_ERR_BAD_ARG = 6,    /* an invalid scalar argument or option combination */
-  FP8BQ_ERR_WORKSPACE = 7   /* the workspace is missing, misaligned or smaller than the call needs */
+  FP8BQ_ERR_WORKSPACE = 7,  /* the workspace is missing, misaligned or smaller than the call needs */
+  FP8BQ_ERR_SCRATCH = 8     /* the call needs more than the library's static scratch (FP8BQ_SCRATCH_BYTES) */
 };
 
 /* Static, human-readable text for a status code (host function). */
@@ -232,6 +233,28 @@ fp8bq_status gemm_w8a8_blockscaled_splitk(const uint8_t* a_fp8, const float* a_s
  * nothing.
  */
 fp8bq_status gemm_w8a8_blockscaled_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t* bytes);
+
+/*
+ * gemm_w8a8_blockscaled_splitk_noalloc -- gemm_w8a8_blockscaled_splitk for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops or harnesses that forbid hipMalloc): no workspace argument;
+ * the partial tiles go to a static device array of FP8BQ_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends.  The
+ * call itself allocates nothing (no hipMalloc / hipFree, no allocating
+ * library routine).  Same kernels and the same result bits as
+ * gemm_w8a8_blockscaled_splitk.
+ *   Arguments as for gemm_w8a8_blockscaled.  A shape whose split needs more
+ *   than FP8BQ_SCRATCH_BYTES (see gemm_w8a8_blockscaled_splitk_workspace)
+ *   returns FP8BQ_ERR_SCRATCH and enqueues nothing; with the split rule on a
+ *   256-CU device that never happens (S * M * N * 4 <= 32 MiB).
+ *   All calls on one GPU share the array: calls that overlap on one GPU (on
+ *   different streams, or from different threads without ordering) race
+ *   and give unspecified output.  Calls ordered on one stream are safe.
+ */
+#define FP8BQ_SCRATCH_BYTES (32 * 1024 * 1024)
+fp8bq_status gemm_w8a8_blockscaled_splitk_noalloc(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,
+                                                  const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N,
+                                                  int64_t K, void* stream);
 
 /*
  * quantize_act_per_token_group_frag -- quantize_act_per_token_group with

@@ -44,7 +44,7 @@ def test_status_strings():
     import fp8_blockwise_quantized_quantize_amd as fb
 
     assert fb.status_string(0) == "ok"
-    for code in range(1, 8):
+    for code in range(1, 9):
         assert fb.status_string(code) not in ("ok", "unknown status")
     assert fb.status_string(99) == "unknown status"
 
