@@ -202,11 +202,15 @@ def layer_case(T, E, k, H, F, seed, sample=None):
     rep = gemm_tolerance_report(out[toks], ref)
     print("moe layer", T, E, k, H, F, rep, flush=True)
     # The GPU's and the oracle's fc1 outputs are each within the GEMM bar but
-    # round to BF16 differently in places, so a few h codes differ by one
-    # E4M3 step (at most 1/8 of |h|) and move the fc2 output accordingly:
-    # the chain keeps the GEMM bar in Frobenius norm, and each element stays
-    # within 2^-4 of max(|ref|, rms(ref)).
-    assert rep["rel_fro"] <= 1e-2 and rep["rel_max"] <= 2.0 ** -4, rep
+    # round to BF16 differently in places (about 1% of them), so a few h
+    # codes differ by one E4M3 step (at most 1/8 of |h|).  Each such flip
+    # moves one of the F terms of an fc2 output: with F = 768 terms of
+    # similar size, one term is ~1/sqrt(F) = 3.6% of rms(ref), so a flip
+    # moves the output by ~0.45% of it, and flips are rare enough that an
+    # output rarely takes two.  The chain keeps the GEMM bar of 1e-2 in
+    # Frobenius norm and per element (measured on the full Qwen3-30B-A3B
+    # layer: 0.18% and 0.64%).
+    assert rep["rel_fro"] <= 1e-2 and rep["rel_max"] <= 1e-2, rep
 
 
 def test_moe_layer_small():

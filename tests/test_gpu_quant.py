@@ -134,14 +134,30 @@ def test_weight_qwen3_8b_layer(fb, idx):
         assert np.array_equal(gq[blk], q), (name, i, j)
 
 
+def _oracle_quant_rows(bits):
+    """oracle.quant_weight_blockwise of [N][K] bits, one 128-row block row per
+    task on a thread pool (blocks are independent)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    chunks = [(r, min(bits.shape[0], r + 128)) for r in range(0, bits.shape[0], 128)]
+    with ThreadPoolExecutor(8) as ex:
+        res = list(ex.map(lambda c: oracle.quant_weight_blockwise(bits[c[0]:c[1]]), chunks))
+    return np.concatenate([q for q, _ in res]), np.concatenate([s for _, s in res])
+
+
 def test_weight_36_layer_sweep_sampled(fb):
-    """Full-size re-quantization sweep (36 layers x 4 projections, batch = 36 per call)."""
+    """Full-size re-quantization sweep (36 layers x 4 projections, batch = 36
+    per call): the last layer of every projection in full (its bytes lie
+    past 2^31 in the batched call) and random blocks of the others."""
     rng = np.random.default_rng(6)
     for p, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
         announce("quant_weight sweep", name, 36, n, k)
         w = device_bf16_normal((36, n, k), 0.02, seed=1000 + p)
         q, s = fb.quantize_weight_blockwise(w)
         torch.cuda.synchronize()
+        oq, os_ = _oracle_quant_rows(w[35].contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+        assert np.array_equal(s[35].cpu().numpy().view(np.uint32), os_.view(np.uint32)), (name, "layer 35 scales")
+        assert np.array_equal(q[35].cpu().numpy(), oq), (name, "layer 35 codes")
         for _ in range(6):
             l, i, j = int(rng.integers(0, 36)), int(rng.integers(0, n // 128)), int(rng.integers(0, k // 128))
             blk = w[l, i * 128:(i + 1) * 128, j * 128:(j + 1) * 128].contiguous().view(torch.int16)
