@@ -204,13 +204,16 @@ def layer_case(T, E, k, H, F, seed, sample=None):
     # The GPU's and the oracle's fc1 outputs are each within the GEMM bar but
     # round to BF16 differently in places (about 1% of them), so a few h
     # codes differ by one E4M3 step (at most 1/8 of |h|).  Each such flip
-    # moves one of the F terms of an fc2 output: with F = 768 terms of
-    # similar size, one term is ~1/sqrt(F) = 3.6% of rms(ref), so a flip
-    # moves the output by ~0.45% of it, and flips are rare enough that an
-    # output rarely takes two.  The chain keeps the GEMM bar of 1e-2 in
-    # Frobenius norm and per element (measured on the full Qwen3-30B-A3B
-    # layer: 0.18% and 0.64%).
-    assert rep["rel_fro"] <= 1e-2 and rep["rel_max"] <= 1e-2, rep
+    # moves one of the F terms of an fc2 output; with F terms of similar
+    # size, one term is ~1/sqrt(F) of rms(ref), so a flip moves the output
+    # by ~1/(8 sqrt(F)) of it, and an output rarely takes more than a few.
+    # The chain keeps the GEMM bar of 1e-2 in Frobenius norm; per element
+    # it stays within 1/sqrt(F): 6.25% for F = 256 (this test's small layer
+    # measures 3.2%, so it does need more than 1e-2) and 3.6% for the
+    # Qwen3-30B-A3B layer's F = 768, which also keeps the 1e-2 bar
+    # (measured 0.64% on the full layer).
+    assert rep["rel_fro"] <= 1e-2 and rep["rel_max"] <= min(2.0 ** -4, 1.0 / np.sqrt(F)), rep
+    return rep
 
 
 def test_moe_layer_small():
@@ -219,7 +222,8 @@ def test_moe_layer_small():
 
 def test_moe_layer_qwen3_30b_a3b_sampled():
     c = MOE_QWEN3_30B_A3B
-    layer_case(T=c["tokens"], E=c["experts"], k=c["top_k"], H=c["hidden"], F=c["ffn"], seed=2, sample=4)
+    rep = layer_case(T=c["tokens"], E=c["experts"], k=c["top_k"], H=c["hidden"], F=c["ffn"], seed=2, sample=4)
+    assert rep["rel_max"] <= 1e-2, rep
 
 
 def test_silu_mul_structural_ties():
