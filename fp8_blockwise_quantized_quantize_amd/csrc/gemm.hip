@@ -872,11 +872,12 @@ struct Panel {
 
 // ---------------------------------------------------------------------------
 // panel_afrag<BN, BM, ...>: the panel tile for activations stored in the MFMA
-// fragment order (launch_quant_act_frag): each wave loads its activation
-// fragments straight into VGPRs (two contiguous 16-byte loads per lane per
-// fragment), and only the weight rows and the scales go through LDS.  That
-// leaves room for four one-K-block weight stages used in two alternating
-// pairs: the waves meet at one barrier per two K-blocks (K % 256 == 0).
+// fragment order (launch_quant_act_frag), four or eight waves: each wave
+// loads its activation fragments straight into VGPRs (two contiguous
+// 16-byte loads per lane per fragment), and only the weight rows and the
+// scales go through LDS.  That leaves room for four one-K-block weight
+// stages used in two alternating pairs: the waves meet at one barrier per
+// two K-blocks (K % 256 == 0).
 // The weight and scale loads of pair p + 1 are issued during the MFMAs of
 // pair p, and the activation fragments of K-block k + 1 during those of
 // K-block k; before the barrier of pair p + 1 every wave waits for all of
@@ -886,22 +887,27 @@ struct Panel {
 template <int BN_, int BM_, int WGN, int WGM, int S>
 struct PanelAfrag {
   static constexpr int BN = BN_, BM = BM_;
-  static_assert(WGN * WGM == 8, "eight waves");
+  static constexpr int kNW = WGN * WGM;  // waves
+  static_assert(kNW == 8 || kNW == 4, "eight waves (one workgroup per CU) or four (two per CU)");
   static constexpr int WNR = BN / WGN, WMR = BM / WGM;  // rows of a wave's tile
   static constexpr int TN = WNR / 16, TM = WMR / 16;
   static_assert(WNR % 16 == 0 && WMR % 16 == 0 && WNR <= 128, "wave tile");
-  static_assert(BN % 64 == 0 && BM % 64 == 0, "each load instruction covers 8 rows of one operand, 8 waves");
-  static constexpr int kLoads = BN / 64;               // weight load instructions per wave per K-block
+  static_assert(BN % (8 * kNW) == 0 && BM % 64 == 0, "each load instruction covers 8 weight rows");
+  static constexpr int kLoads = BN / (8 * kNW);        // weight load instructions per wave per K-block
   static constexpr int kStage = BN * kBlock;           // one K-block of weight rows
-  // Each stage also holds that K-block's scales: 64 dwords per wave
-  // (activation scales of the tile's rows 0..BM-1, then the tile's weight
-  // scale blocks), after the S operand stages.
-  static constexpr int kScaleBytes = 8 * 64 * 4;
-  static_assert(BM / 64 < 8, "a wave left over for the weight scales");
+  // Each stage also holds that K-block's scales, after the S operand
+  // stages, in slots of 64 dwords: slots 0 .. BM/64 - 1 the activation
+  // scales of the tile's rows (slot w loaded by wave w), slot BM/64 the
+  // tile's weight scale blocks (loaded by the waves left over, or by wave 0
+  // as a second load when every wave has activation rows).
+  static constexpr int kActSlots = BM / 64;
+  static_assert(kActSlots <= kNW, "one wave per 64 activation rows");
+  static constexpr bool kExtraWeightScaleLoad = kActSlots == kNW;
+  static constexpr int kScaleBytes = (kExtraWeightScaleLoad ? kNW + 1 : kNW) * 64 * 4;
   static constexpr int kLdsBytes = S * (kStage + kScaleBytes);
   static_assert(S == 4, "two pairs of K-block sub-stages");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
-  static constexpr int kThreadsPerWg = 512;
+  static constexpr int kThreadsPerWg = 64 * kNW;
   static constexpr int kWavesPerSimd = 2;
   // a wave's weight rows lie in one 128-row scale block when tiles start at
   // multiples of 128 and the wave's share divides 128
@@ -936,10 +942,11 @@ struct PanelAfrag {
     // the activation scales of tile rows 64 w + lane, the others the
     // weight scale blocks nbt + lane.  Rows and blocks past the end sit
     // outside the buffer range and read zeros.
-    const bool act_scales = wave < BM / 64;
-    const auto scr = act_scales ? make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4)
-                                : make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
+    const bool act_scales = wave < kActSlots;
+    const auto wsr = make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
+    const auto scr = act_scales ? make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4) : wsr;
     const int scvoff = act_scales ? (64 * wave + lane) * KB * 4 : lane * KB * 4;
+    const bool extra_ws = kExtraWeightScaleLoad && wave == 0;  // wave-uniform
 
     // DMA staging of the weight rows: load q of wave w fills stage rows
     // R0..R0+7 with R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at
@@ -960,8 +967,16 @@ struct PanelAfrag {
       auto* dst = (__attribute__((address_space(3))) void*)(lds + S * kStage + stage * kScaleBytes + wave * 256);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, dst, 4, scvoff, kb * 4, 0, 0);
     };
+    // the weight scales when every wave has activation rows: wave 0 loads
+    // them for both K-blocks of a pair at the pair's start (a branch inside
+    // the pipelined MFMA loop would cost the compiler its schedule)
+    const int wsvoff = lane * KB * 4;
+    auto dma_wscales = [&](int kb, int stage) {
+      auto* dst = (__attribute__((address_space(3))) void*)(lds + S * kStage + stage * kScaleBytes + kActSlots * 256);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, dst, 4, wsvoff, kb * 4, 0, 0);
+    };
     auto dma_q = [&](int q, int kb, uint8_t* buf) {
-      const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q: weight rows n0 + r0 ..
+      const int r0 = 8 * (kNW * q + wave);  // stage row of this wave's load q: weight rows n0 + r0 ..
       auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, kb * kBlock, 0, 0);
     };
@@ -1046,6 +1061,10 @@ struct PanelAfrag {
 #pragma unroll
       for (int j = 0; j < TM; ++j) { load_a(j, 0, 0); load_a(j, 1, 0); }
       dma_kblock(nxt(1), 1);
+      if (extra_ws) {
+        dma_wscales(0, 0);
+        dma_wscales(nxt(1), 1);
+      }
     }
     // K-blocks in pairs (KB even: the host uses this tile only for K % 256
     // == 0); sub-stages 0,1 and 2,3 alternate.  Loads past the last K-block
@@ -1055,6 +1074,10 @@ struct PanelAfrag {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of pair kp have landed
       barrier();                                        // and everyone's
       const int c0 = ((kp >> 1) & 1) ? 2 : 0, f0 = 2 - c0;
+      if (extra_ws) {
+        dma_wscales(nxt(kp + 2), f0);
+        dma_wscales(nxt(kp + 3), f0 + 1);
+      }
       if (idle) {
         dma_kblock(nxt(kp + 2), f0);
         dma_kblock(nxt(kp + 3), f0 + 1);
@@ -1077,7 +1100,15 @@ struct PanelAfrag {
   }
 };
 
-using WideAfrag = PanelAfrag<256, 256, 2, 4, 4>;
+// The prefill tile for fragment-order activations: the 128 x 64 wave tile
+// in four-wave 128 x 256 workgroups, two per CU (69 KB of LDS each).  Each
+// workgroup meets at its own barriers, so the two on a CU wait at
+// different times; the same wave tile in one eight-wave 256 x 256
+// workgroup per CU (same traffic per output) is slower on the Qwen3-8B
+// prefill shapes at M = 8192: 1.82 vs 1.92 PF over the four (gate_up 920
+// vs 849 us, o 171 vs 156 us, qkv 247 vs 239 us, down 400 vs 401 us),
+// bit-identical outputs.
+using WideAfrag4 = PanelAfrag<128, 256, 1, 4, 4>;
 
 using Wide = Panel<256, 256, 2, 4, 2>;
 using DecodePanel = Panel<128, 256, 2, 4, 3>;
@@ -1611,7 +1642,7 @@ hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   if (M % 16 != 0 || K % (2 * kBlock) != 0) return hipErrorInvalidValue;
-  return launch_dense_cfg<WideAfrag, WideAfrag::BN, WideAfrag::BM>(a, sa, w, sw, y, M, N, K, stream);
+  return launch_dense_cfg<WideAfrag4, WideAfrag4::BN, WideAfrag4::BM>(a, sa, w, sw, y, M, N, K, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
