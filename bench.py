@@ -469,10 +469,11 @@ def detail(fb, dev, with_cpu=True):
 
 def decode_step(fb, dev, with_cpu):
     """The Qwen3-8B decode layer step at M = 256: one launch re-quantizes the
-    four weight matrices, one launch quantizes the four activations, then
-    the four GEMMs.  Steps cycle through four copies of the layer's buffers
-    (0.6 GB each).  Phases timed with HIP events; the oracle runs the same
-    step on the same input bytes (parity and a CPU time on all its threads)."""
+    four weight matrices, one launch quantizes the four activations (codes
+    in fragment order), then the four fragment-order GEMMs.  Steps cycle
+    through four copies of the layer's buffers (0.6 GB each).  Phases timed
+    with HIP events; the oracle runs the same step on the same input bytes
+    (parity and a CPU time on all its threads)."""
     import torch
 
     from synthetic import LAYER_SHAPES_QWEN3_8B, device_bf16_normal
@@ -495,9 +496,6 @@ def decode_step(fb, dev, with_cpu):
         sets.append(layers)
     stream = torch.cuda.current_stream()
     ev = []
-    # one workspace serves the K-split GEMMs of a step (ordered on one stream)
-    need = max(fb.splitk_workspace_bytes(M, n, k) for _, n, k in LAYER_SHAPES_QWEN3_8B)
-    wsp = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
     def step(record, s):
         ls = sets[s % SETS]
@@ -507,11 +505,11 @@ def decode_step(fb, dev, with_cpu):
         fb.quantize_weights_blockwise_multi([L["w"] for L in ls], [(L["wq"], L["ws"]) for L in ls])
         if record:
             e[1].record(stream)
-        fb.quantize_acts_per_token_group_multi([L["x"] for L in ls], [(L["xq"], L["xs"]) for L in ls])
+        fb.quantize_acts_per_token_group_frag_multi([L["x"] for L in ls], [(L["xq"], L["xs"]) for L in ls])
         if record:
             e[2].record(stream)
         for L in ls:
-            fb.gemm_w8a8_blockscaled_splitk(L["xq"], L["xs"], L["wq"], L["ws"], L["y"], workspace=wsp)
+            fb.gemm_w8a8_blockscaled_afrag(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
         if record:
             e[3].record(stream)
             ev.append(e)
@@ -543,18 +541,28 @@ def decode_step(fb, dev, with_cpu):
                     "GBps": round(gm_b / ph["gemm"] / 1e6, 1),
                     "frac_hbm": round(gm_b / ph["gemm"] / 1e6 / HBM_PEAK_GBPS, 4)}}
     # each GEMM on its own, as the step runs it (graph replays over the four
-    # buffer sets)
+    # buffer sets), and the row-major GEMM on the same activations
+    for ls in sets:
+        for L in ls:
+            L["xr"], _ = fb.quantize_act_per_token_group(L["x"])
     per = {}
     for i, L in enumerate(layers):
         f = 2 * M * L["n"] * L["k"]
         byt = M * L["k"] + L["n"] * L["k"] + 2 * M * L["n"] + L["xs"].numel() * 4 + L["ws"].numel() * 4
-        us, _ = _time_graph_ms([lambda t=t[i]: fb.gemm_w8a8_blockscaled_splitk(t["xq"], t["xs"], t["wq"], t["ws"],
-                                                                               t["y"], workspace=wsp) for t in sets])
-        per[L["name"]] = {"k_pieces": max(1, fb.splitk_workspace_bytes(M, L["n"], L["k"]) // (4 * M * L["n"])),
-                          "us": round(us * 1e3, 2), "frac_hbm": round(byt / us / 1e6 / HBM_PEAK_GBPS, 4),
-                          "TFLOPs": round(f / us / 1e9, 1)}
+        us, _ = _time_graph_ms([lambda t=t[i]: fb.gemm_w8a8_blockscaled_afrag(t["xq"], t["xs"], t["wq"], t["ws"],
+                                                                              t["y"]) for t in sets])
+        y_frag = layers[i]["y"].clone()
+        rm, _ = _time_graph_ms([lambda t=t[i]: fb.gemm_w8a8_blockscaled(t["xr"], t["xs"], t["wq"], t["ws"], t["y"])
+                                for t in sets])
+        per[L["name"]] = {"us": round(us * 1e3, 2), "frac_hbm": round(byt / us / 1e6 / HBM_PEAK_GBPS, 4),
+                          "TFLOPs": round(f / us / 1e9, 1), "row_major_us": round(rm * 1e3, 2),
+                          "bit_identical": bool(torch.equal(y_frag.view(torch.int16),
+                                                            layers[i]["y"].view(torch.int16)))}
     res["gemm_each"] = per
     res["splitk_small_batch"] = splitk_small_batch(fb, dev, sets[0])
+    for ls in sets:
+        for L in ls:
+            del L["xr"]
     step(False, 0)
     torch.cuda.synchronize()
     if with_cpu:
@@ -577,7 +585,7 @@ def splitk_small_batch(fb, dev, layer_set):
             if need == 0:
                 continue
             wq = [L["wq"]] + [L["wq"].clone() for _ in range(3)]
-            xq, xs = L["xq"][:m].contiguous(), L["xs"][:m].contiguous()
+            xq, xs = L["xr"][:m].contiguous(), L["xs"][:m].contiguous()
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             wsp = torch.empty(need, dtype=torch.uint8, device=dev)
             sk, _ = _time_graph_ms([lambda w=w: fb.gemm_w8a8_blockscaled_splitk(xq, xs, w, L["ws"], y, workspace=wsp)
@@ -977,7 +985,7 @@ def decode_cpu_and_parity(layers, m, flops):
     re-quant (thread pool over block rows), act quant, FP32-accumulated GEMM
     (BLAS threads); its outputs check the GPU's bit for bit (quantizers) and
     by R14 (GEMMs)."""
-    from oracle import gemm_ref_fp32, quant_act_per_token_group
+    from oracle import act_fragment_order, gemm_ref_fp32, quant_act_per_token_group
 
     threads = host_threads()
     host = [(_bits(L["w"]), _bits(L["x"])) for L in layers]
@@ -998,8 +1006,9 @@ def decode_cpu_and_parity(layers, m, flops):
     for L, (qw, sw), (qa, sa), y_ref in zip(layers, wres, ares, yres):
         par["requant_bitexact"] &= bool(np.array_equal(L["wq"].cpu().numpy(), qw) and np.array_equal(
             L["ws"].cpu().numpy().view(np.uint32), sw.view(np.uint32)))
-        par["act_quant_bitexact"] &= bool(np.array_equal(L["xq"].cpu().numpy(), qa) and np.array_equal(
-            L["xs"].cpu().numpy().view(np.uint32), sa.view(np.uint32)))
+        par["act_quant_bitexact"] &= bool(np.array_equal(L["xq"].cpu().numpy(), act_fragment_order(qa))
+                                          and np.array_equal(L["xs"].cpu().numpy().view(np.uint32),
+                                                             sa.view(np.uint32)))
         par["gemm"][L["name"]] = _r14(_bits(L["y"]), y_ref)
     par["pass"] = par["requant_bitexact"] and par["act_quant_bitexact"] and all(g["pass"] for g in par["gemm"].values())
     return base, par

@@ -28,6 +28,7 @@ __all__ = [
     "quantize_weights_blockwise_multi",
     "quantize_act_per_token_group",
     "quantize_acts_per_token_group_multi",
+    "quantize_acts_per_token_group_frag_multi",
     "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
     "gemm_w8a8_blockscaled_splitk",
@@ -62,6 +63,7 @@ EXPORTS = (
     "quantize_weights_blockwise_multi",
     "quantize_act_per_token_group",
     "quantize_acts_per_token_group_multi",
+    "quantize_acts_per_token_group_frag_multi",
     "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
     "gemm_w8a8_blockscaled_splitk",
@@ -116,6 +118,7 @@ def _load():
     lib.quantize_act_per_token_group.argtypes = [p, p, p, i64, i64, p]
     lib.quantize_weights_blockwise_multi.argtypes = [ctypes.POINTER(_WeightDesc), i64, p]
     lib.quantize_acts_per_token_group_multi.argtypes = [ctypes.POINTER(_ActDesc), i64, p]
+    lib.quantize_acts_per_token_group_frag_multi.argtypes = [ctypes.POINTER(_ActDesc), i64, p]
     lib.gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.quantize_act_per_token_group_frag.argtypes = [p, p, p, i64, i64, p]
     lib.gemm_w8a8_blockscaled_afrag.argtypes = [p, p, p, p, p, i64, i64, i64, p]
@@ -273,10 +276,11 @@ def quantize_act_per_token_group(x, out=None, scale=None):
     return out, scale
 
 
-def quantize_acts_per_token_group_multi(xs, outs=None):
+def quantize_acts_per_token_group_multi(xs, outs=None, frag=False):
     """Several BF16 activations [M, K] (any shapes) in one launch -> list of
-    (codes, scales), each exactly what quantize_act_per_token_group gives it.
-    ``outs``: optional list of (codes, scales) to fill."""
+    (codes, scales), each exactly what quantize_act_per_token_group gives it
+    (``frag``: what quantize_act_per_token_group_frag gives it, M % 16 == 0
+    and K % 128 == 0).  ``outs``: optional list of (codes, scales) to fill."""
     xs = list(xs)
     if len(xs) > MAX_ACT_DESCS:
         raise ValueError(f"at most {MAX_ACT_DESCS} activations per call")
@@ -299,10 +303,15 @@ def quantize_acts_per_token_group_multi(xs, outs=None):
         _require(s, f"scale[{i}]", torch.float32, (m, _cdiv(k, BLOCK)), dev)
         descs[i] = _ActDesc(_ptr(_u16(x)).value, _ptr(q).value, _ptr(s).value, m, k)
         res.append((q, s))
+    name = "quantize_acts_per_token_group_frag_multi" if frag else "quantize_acts_per_token_group_multi"
     with torch.cuda.device(dev):
-        _check("quantize_acts_per_token_group_multi",
-               _lib.quantize_acts_per_token_group_multi(descs, len(xs), _stream(xs[0])))
+        _check(name, getattr(_lib, name)(descs, len(xs), _stream(xs[0])))
     return res
+
+
+def quantize_acts_per_token_group_frag_multi(xs, outs=None):
+    """quantize_acts_per_token_group_multi with codes in fragment order."""
+    return quantize_acts_per_token_group_multi(xs, outs, frag=True)
 
 
 def quantize_act_per_token_group_frag(x, out=None, scale=None):

@@ -203,7 +203,14 @@ fp8bq_status quantize_act_per_token_group(const uint16_t* x_bf16, uint8_t* x_fp8
   }
 }
 
-fp8bq_status quantize_acts_per_token_group_multi(const fp8bq_act_desc* descs, int64_t count, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The two multi-activation quantizers: row-major (32 groups per workgroup)
+// or fragment order (4 units of 16 rows x one K-block per workgroup, M % 16
+// == 0 and K % 128 == 0 for each activation).
+fp8bq_status quantize_acts_multi(const fp8bq_act_desc* descs, int64_t count, bool frag, void* stream) {
   try {
     if (count < 0 || count > FP8BQ_MAX_ACT_DESCS) return FP8BQ_ERR_BAD_SHAPE;
     if (count == 0) return FP8BQ_OK;
@@ -213,15 +220,21 @@ fp8bq_status quantize_acts_per_token_group_multi(const fp8bq_act_desc* descs, in
     for (int64_t i = 0; i < count; ++i) {
       const fp8bq_act_desc& d = descs[i];
       if (d.M < 0 || d.K < 0) return FP8BQ_ERR_BAD_SHAPE;
+      if (frag && ((d.M % 16) != 0 || (d.K % 128) != 0)) return FP8BQ_ERR_BAD_SHAPE;
       int64_t mk, bytes;
       if (!mul_ok(d.M, d.K, &mk) || !mul_ok(mk, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
       if (mk == 0) continue;
       if (!d.x_bf16 || !d.x_fp8 || !d.x_scale) return FP8BQ_ERR_NULL_PTR;
       if (!aligned16(d.x_bf16) || !aligned16(d.x_fp8) || !aligned16(d.x_scale)) return FP8BQ_ERR_MISALIGNED;
-      const int64_t groups = d.M * ((d.K + 127) / 128);
       batch.desc[batch.count] = fp8bq::ActDesc{d.x_bf16, d.x_fp8, d.x_scale, d.M, d.K};
       batch.first[batch.count] = blocks;
-      blocks += (groups + fp8bq::kActGroupsPerWg - 1) / fp8bq::kActGroupsPerWg;
+      if (frag) {
+        const int64_t units = (d.M / 16) * (d.K / 128);
+        blocks += (units + fp8bq::kActFragUnitsPerWg - 1) / fp8bq::kActFragUnitsPerWg;
+      } else {
+        const int64_t groups = d.M * ((d.K + 127) / 128);
+        blocks += (groups + fp8bq::kActGroupsPerWg - 1) / fp8bq::kActGroupsPerWg;
+      }
       if (blocks > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
       ++batch.count;
     }
@@ -230,10 +243,24 @@ fp8bq_status quantize_acts_per_token_group_multi(const fp8bq_act_desc* descs, in
     fp8bq_status st = check_device();
     if (st != FP8BQ_OK) return st;
     clear_last_error();
-    return launched(fp8bq::launch_quant_act_multi(batch, blocks, static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(frag ? fp8bq::launch_quant_act_frag_multi(batch, blocks, s)
+                         : fp8bq::launch_quant_act_multi(batch, blocks, s));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8bq_status quantize_acts_per_token_group_multi(const fp8bq_act_desc* descs, int64_t count, void* stream) {
+  return quantize_acts_multi(descs, count, false, stream);
+}
+
+fp8bq_status quantize_acts_per_token_group_frag_multi(const fp8bq_act_desc* descs, int64_t count, void* stream) {
+  return quantize_acts_multi(descs, count, true, stream);
 }
 
 fp8bq_status gemm_w8a8_blockscaled_tile(const uint8_t* a_fp8, const float* a_scale, const uint8_t* w_fp8,

@@ -220,12 +220,18 @@ __device__ __forceinline__ void store4_f32(float* __restrict__ p, int64_t N, int
 // steps arrive in one load per 16-row group (one K-block per lane group):
 // per-lane scale loads touch a cache line per row, and one per step made
 // the scale loads a fifth of the kernel's vector-memory work.
+//
+// kAfrag: the activations are in MFMA fragment order (launch_quant_act_frag)
+// and each wave loads its activation fragments straight into registers
+// with the K-block's weight rows; only the weight rows go through the
+// slice.
 // ---------------------------------------------------------------------------
-template <int BN, int BM, int NW>
+template <int BN, int BM, int NW, bool kAfrag = false>
 struct Skinny {
   static constexpr int TN = BN / 16, TM = BM / 16;
-  static constexpr int kRows = BN + BM;                 // rows staged per K-block
-  static constexpr int kLoads = kRows / 8;              // 16-byte loads per lane per K-block
+  static constexpr int kRows = kAfrag ? BN : BN + BM;   // rows staged per K-block
+  static constexpr int kLoads = BN / 8 + (kAfrag ? 2 * TM : BM / 8);  // 16-byte loads per lane per K-block
+  static constexpr int kStaged = kRows / 8;             // of which staged through the slice
   static constexpr int kSlice = kRows * kBlock;         // LDS bytes per wave
   static constexpr int kRed = NW * BN * BM * 4;         // the waves' partial tiles, FP32
   static constexpr int kLdsBytes = (NW * kSlice > kRed) ? NW * kSlice : kRed;
@@ -291,8 +297,16 @@ struct Skinny {
       const int koff = kb * kBlock;
 #pragma unroll
       for (int q = 0; q < BN / 8; ++q) s.v[q] = bload16(wr, gvoff + 8 * q * (int)K, koff);
+      if constexpr (kAfrag) {
+        // fragment j, half h of K-block kb: 1 KB at (16 j) K + 2048 kb + 1024 h
 #pragma unroll
-      for (int q = 0; q < BM / 8; ++q) s.v[BN / 8 + q] = bload16(ar, gvoff + 8 * q * (int)K, koff);
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) s.v[BN / 8 + 2 * j + h] = bload16(ar, 16 * j * (int)K + h * 1024 + lane * 16, kb * 2048);
+      } else {
+#pragma unroll
+        for (int q = 0; q < BM / 8; ++q) s.v[BN / 8 + q] = bload16(ar, gvoff + 8 * q * (int)K, koff);
+      }
       s.swa = swa_row[kb];
       s.swb = swb_row[kb];
     };
@@ -306,7 +320,7 @@ struct Skinny {
     };
     auto store_stage = [&](const Stage& s) {
 #pragma unroll
-      for (int q = 0; q < kLoads; ++q) *reinterpret_cast<u32x4*>(slice + swz(lrow + 8 * q, lchunk)) = s.v[q];
+      for (int q = 0; q < kStaged; ++q) *reinterpret_cast<u32x4*>(slice + swz(lrow + 8 * q, lchunk)) = s.v[q];
     };
     auto bperm = [](float v, int addr) {
       return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
@@ -318,7 +332,8 @@ struct Skinny {
       for (int j = 0; j < TM; ++j) sa[j] = bperm(G.sa[j], addr);
       v8i fa[TM];
 #pragma unroll
-      for (int j = 0; j < TM; ++j) fa[j] = fl(slice, BN + j * 16);
+      for (int j = 0; j < TM; ++j)
+        fa[j] = kAfrag ? to_v8i(s.v[BN / 8 + 2 * j], s.v[BN / 8 + 2 * j + 1]) : fl(slice, BN + j * 16);
       v8i fw[2];
       fw[0] = fl(slice, 0);
       tile_product<TN, TM, 4, 1>(
@@ -1638,11 +1653,24 @@ hipError_t launch_gemm_splitk_noalloc(const uint8_t* a, const float* sa, const u
   return launch_gemm_splitk(a, sa, w, sw, y, M, N, K, ws, kScratchBytes, stream);
 }
 
+// Fragment-order activations: the tile the cost model picks for row-major
+// ones, in its fragment-order form (the skinny tiles load the activation
+// fragments straight into registers; every panel choice becomes the
+// four-wave 128 x 256 panel).  Qwen3-8B decode shapes at M = 256 (us,
+// row-major -> fragment order, bit-identical): qkv 19.1 -> 17.6, o 14.0 ->
+// 12.2, down 27.8 -> 24.3; gate_up 46.0 (192 x 128 panel) -> 48.9.
 hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   if (M % 16 != 0 || K % (2 * kBlock) != 0) return hipErrorInvalidValue;
-  return launch_dense_cfg<WideAfrag4, WideAfrag4::BN, WideAfrag4::BM>(a, sa, w, sw, y, M, N, K, stream);
+  switch (choose(M, N, K)) {
+    case Cfg::kSkinny64x64:
+      return launch_dense_cfg<Skinny<64, 64, 4, true>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
+    case Cfg::kSkinny48x64:
+      return launch_dense_cfg<Skinny<48, 64, 4, true>, 48, 64>(a, sa, w, sw, y, M, N, K, stream);
+    default:
+      return launch_dense_cfg<WideAfrag4, WideAfrag4::BN, WideAfrag4::BM>(a, sa, w, sw, y, M, N, K, stream);
+  }
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,

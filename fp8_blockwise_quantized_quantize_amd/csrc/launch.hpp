@@ -52,6 +52,9 @@ struct ActBatch {
 constexpr int kActGroupsPerWg = 32;
 
 hipError_t launch_quant_act_multi(const ActBatch& batch, int64_t blocks, hipStream_t stream);
+// the same in fragment order: first[] counts workgroups of 4 units (16 rows x one K-block)
+constexpr int kActFragUnitsPerWg = 4;
+hipError_t launch_quant_act_frag_multi(const ActBatch& batch, int64_t blocks, hipStream_t stream);
 // the same codes in the MFMA fragment order of the activation operand (M % 16 == 0, K % 128 == 0)
 hipError_t launch_quant_act_frag(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K,
                                  hipStream_t stream);

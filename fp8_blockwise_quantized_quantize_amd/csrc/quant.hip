@@ -259,14 +259,10 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ i
 // pieces 32 bytes apart: 62 vs 49 us for the row-major quantizer at 8192 x
 // 12288.)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kQaThreads) void quant_act_frag_kernel(const uint16_t* __restrict__ x,
-                                                                    uint8_t* __restrict__ q,
-                                                                    float* __restrict__ scale, int64_t M,
-                                                                    int64_t K, int G) {
-  __shared__ __align__(16) uint8_t tile[kQaThreads / 64][2048];
-  const int wave = threadIdx.x >> 6;
-  const int64_t unit = (int64_t)blockIdx.x * (kQaThreads / 64) + wave;
-  if (unit >= (M / 16) * G) return;  // whole waves
+// One unit (16 rows R x K-block g, unit = R G + g) of one activation, by
+// one wave; `t` is the wave's 2 KB of LDS.
+__device__ __forceinline__ void frag_unit(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
+                                          float* __restrict__ scale, int64_t K, int G, int64_t unit, uint8_t* t) {
   const int lane = threadIdx.x & 63, cc = lane & 15, rq = lane >> 4;
   const int64_t R = unit / G;
   const int g = (int)(unit % G);
@@ -274,7 +270,6 @@ __global__ __launch_bounds__(kQaThreads) void quant_act_frag_kernel(const uint16
   u32x4 v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)4 * i * K));
-  uint8_t* t = tile[wave];
   // fragment position of this lane's 8 codes of row r = 4 i + rq, columns
   // 8 cc .. 8 cc + 7: half cc / 8, 16-byte chunk (cc % 8) / 2, byte 8 (cc % 2)
   const int pos = (cc >> 3) * 1024 + ((cc & 7) >> 1) * 256 + (cc & 1) * 8;
@@ -297,6 +292,33 @@ __global__ __launch_bounds__(kQaThreads) void quant_act_frag_kernel(const uint16
   uint8_t* dst = q + (R * G + g) * 2048 + lane * 16;
   __builtin_nontemporal_store(lo, reinterpret_cast<u32x4*>(dst));
   __builtin_nontemporal_store(hi, reinterpret_cast<u32x4*>(dst + 1024));
+}
+
+__global__ __launch_bounds__(kQaThreads) void quant_act_frag_kernel(const uint16_t* __restrict__ x,
+                                                                    uint8_t* __restrict__ q,
+                                                                    float* __restrict__ scale, int64_t M,
+                                                                    int64_t K, int G) {
+  __shared__ __align__(16) uint8_t tile[kQaThreads / 64][2048];
+  const int wave = threadIdx.x >> 6;
+  const int64_t unit = (int64_t)blockIdx.x * (kQaThreads / 64) + wave;
+  if (unit >= (M / 16) * G) return;  // whole waves
+  frag_unit(x, q, scale, K, G, unit, tile[wave]);
+}
+
+// Several activations in fragment order in one launch: workgroup b takes
+// units 4 (b - first[t]) .. + 3 (16 rows x one K-block each) of activation
+// t, one per wave, as quant_act_frag_kernel does for one activation.
+__global__ __launch_bounds__(kQaThreads) void quant_act_frag_multi_kernel(const ActBatch batch) {
+  __shared__ __align__(16) uint8_t tile[kQaThreads / 64][2048];
+  const int64_t b = blockIdx.x;
+  int t = 0;
+  while (t + 1 < batch.count && b >= batch.first[t + 1]) ++t;  // uniform scan over <= 16 entries
+  const ActDesc& d = batch.desc[t];
+  const int G = (int)(d.K / kBlock);
+  const int wave = threadIdx.x >> 6;
+  const int64_t unit = (b - batch.first[t]) * (kQaThreads / 64) + wave;
+  if (unit >= (d.M / 16) * G) return;  // whole waves
+  frag_unit(d.x, d.q, d.s, d.K, G, unit, tile[wave]);
 }
 
 }  // namespace
@@ -353,6 +375,13 @@ hipError_t launch_quant_act_multi(const ActBatch& batch, int64_t blocks, hipStre
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quant_act_multi_kernel, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_frag_multi(const ActBatch& batch, int64_t blocks, hipStream_t stream) {
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_act_frag_multi_kernel, dim3((unsigned)blocks), dim3(kQaThreads), 0, stream, batch);
   return hipGetLastError();
 }
 

@@ -149,6 +149,17 @@ typedef struct {
 fp8bq_status quantize_acts_per_token_group_multi(const fp8bq_act_desc* descs, int64_t count, void* stream);
 
 /*
+ * quantize_acts_per_token_group_frag_multi -- quantize_act_per_token_group_frag
+ * of several activations in one launch (the decode step's inputs of the
+ * fragment-order GEMMs).  Same descriptors and limits as
+ * quantize_acts_per_token_group_multi, codes in fragment order; each
+ * activation needs M % 16 == 0 and K % 128 == 0 (FP8BQ_ERR_BAD_SHAPE
+ * otherwise) and gets exactly the codes and scales
+ * quantize_act_per_token_group_frag gives it.
+ */
+fp8bq_status quantize_acts_per_token_group_frag_multi(const fp8bq_act_desc* descs, int64_t count, void* stream);
+
+/*
  * gemm_w8a8_blockscaled -- y = dequant(A) * dequant(W)^T in FP32, stored as
  * BF16 ([FP8-RL summary] §3.4.2 Phase 3: FP8 matrix multiplication,
  * accumulated in FP32, converted back to BF16).
@@ -286,11 +297,12 @@ fp8bq_status quantize_act_per_token_group_frag(const uint16_t* x_bf16, uint8_t* 
  *   w_fp8 [N][K], w_scale [ceil(N/128)][K/128], y_bf16 [M][N] as for
  *   gemm_w8a8_blockscaled.
  *   Requires M % 16 == 0 and K % 256 == 0 (K <= 2^22); FP8BQ_ERR_BAD_SHAPE
- *   otherwise.  Meant for many activation rows (prefill): it always runs
- *   128 x 256 (weight rows x activation rows) workgroup tiles, two per CU.
- *   This is the library's path for prefill-sized activations (M % 16 == 0,
- *   K % 256 == 0): at the Qwen3-8B prefill shapes (M = 8192) it is faster
- *   than gemm_w8a8_blockscaled on row-major codes.
+ *   otherwise.  The tile is chosen per shape as for gemm_w8a8_blockscaled
+ *   (few activation rows: K split over the waves of a 64- or 48-row tile;
+ *   many rows: 128 x 256 workgroup tiles, two per CU).  This is the
+ *   library's path for activations with M % 16 == 0 and K % 256 == 0: on
+ *   the Qwen3-8B layer shapes it is faster than gemm_w8a8_blockscaled on
+ *   row-major codes at both decode (M = 256) and prefill (M = 8192) sizes.
  */
 fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8,
                                          const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,

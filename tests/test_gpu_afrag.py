@@ -4,7 +4,8 @@ the codes in MFMA fragment order, and the GEMM that reads them.
 The quantizer must give the oracle's codes, permuted by the oracle's
 fragment order, and the oracle's scales, bit for bit.  The GEMM must meet
 the GEMM bar against the exact oracle and give the same bits as the
-row-major GEMM's 256 x 256 tile (same per-element arithmetic and order).
+row-major GEMM with the tile the cost model picks for the shape (same
+per-element arithmetic and order).
 """
 
 import numpy as np
@@ -13,7 +14,7 @@ import torch
 
 import oracle
 from helpers import announce, assert_gemm_close, bf16_bits_to_device, device_to_bits
-from synthetic import activations, bf16_normal, device_bf16_normal
+from synthetic import LAYER_SHAPES_QWEN3_8B, activations, bf16_normal, device_bf16_normal
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +50,32 @@ def test_quantizer_fragment_order_matches_row_major_prefill(fb, m, k):
     assert torch.equal(qf, perm) and torch.equal(sf, s)
 
 
+def test_quantizer_frag_multi_matches_oracle(fb):
+    """One launch over the four decode activations of a Qwen3-8B layer
+    (M = 256) plus small and empty ones: each gets the oracle's codes in
+    fragment order and the oracle's scales."""
+    shapes = [(256, 4096), (256, 4096), (256, 4096), (256, 12288), (16, 128), (48, 384), (0, 256), (272, 2048)]
+    announce("afrag quant multi", shapes)
+    xs_bits = [activations(m, k, (m, k, i), n_outliers=max(1, k // 100), outlier_mult=30.0)[0] if m else
+               np.zeros((m, k), np.uint16) for i, (m, k) in enumerate(shapes)]
+    res = fb.quantize_acts_per_token_group_frag_multi([bf16_bits_to_device(b) for b in xs_bits])
+    torch.cuda.synchronize()
+    for (q, s), b, (m, k) in zip(res, xs_bits, shapes):
+        if m == 0:
+            continue
+        oq, os_ = oracle.quant_act_per_token_group(b)
+        assert np.array_equal(q.cpu().numpy(), oracle.act_fragment_order(oq)), (m, k)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32)), (m, k)
+
+
+@pytest.mark.parametrize("m,k", [(24, 256), (16, 200)])
+def test_quantizer_frag_multi_shape_errors(fb, m, k):
+    ok = torch.zeros((16, 128), dtype=torch.bfloat16, device="cuda")
+    bad = torch.zeros((m, k), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fb.FP8BQError, match="shape"):
+        fb.quantize_acts_per_token_group_frag_multi([ok, bad])
+
+
 @pytest.mark.parametrize("m,n,k", [(16, 130, 256), (48, 384, 768), (272, 520, 512), (256, 256, 2048)])
 def test_gemm_afrag_against_oracle_and_row_major(fb, m, n, k):
     announce("afrag gemm", m, n, k)
@@ -60,8 +87,24 @@ def test_gemm_afrag_against_oracle_and_row_major(fb, m, n, k):
     y = fb.gemm_w8a8_blockscaled_afrag(dev(oracle.act_fragment_order(qa)), dev(sa), dev(qw), dev(sw))
     got = device_to_bits(y)
     assert_gemm_close(got, oracle.gemm_ref(qa, sa, qw, sw))
-    ref = device_to_bits(fb.gemm_w8a8_blockscaled(dev(qa), dev(sa), dev(qw), dev(sw), tile="wide"))
+    ref = device_to_bits(fb.gemm_w8a8_blockscaled(dev(qa), dev(sa), dev(qw), dev(sw)))
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("m", [256, 128, 64, 48, 16])
+def test_gemm_afrag_decode_shapes_bit_identical(fb, m):
+    """The Qwen3-8B layer shapes at decode batch sizes: the fragment-order
+    GEMM picks the row-major GEMM's tile in its fragment-order form (K split
+    over the waves of a 64- or 48-row tile, or a panel) and gives its bits."""
+    for _, n, k in LAYER_SHAPES_QWEN3_8B:
+        announce("afrag gemm decode", m, n, k)
+        x = device_bf16_normal((m, k), 1.0, seed=13)
+        wq, ws = fb.quantize_weight_blockwise(device_bf16_normal((n, k), 0.02, seed=14))
+        q, s = fb.quantize_act_per_token_group(x)
+        qf, _ = fb.quantize_act_per_token_group_frag(x)
+        y0 = fb.gemm_w8a8_blockscaled(q, s, wq, ws)
+        y1 = fb.gemm_w8a8_blockscaled_afrag(qf, s, wq, ws)
+        assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)), (m, n, k)
 
 
 @pytest.mark.parametrize("n,k", [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)])
@@ -90,7 +133,7 @@ def test_gemm_afrag_largest_k(fb):
     sa = torch.rand((m, k // 128), generator=g, device="cuda") + 0.5
     sw = torch.rand((1, k // 128), generator=g, device="cuda") + 0.5
     qf = qa.view(m // 16, 16, k // 128, 2, 4, 16).permute(0, 2, 3, 4, 1, 5).contiguous().view(m, k)
-    y0 = fb.gemm_w8a8_blockscaled(qa, sa, qw, sw, tile="wide")
+    y0 = fb.gemm_w8a8_blockscaled(qa, sa, qw, sw)
     del qa
     y1 = fb.gemm_w8a8_blockscaled_afrag(qf, sa, qw, sw)
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
