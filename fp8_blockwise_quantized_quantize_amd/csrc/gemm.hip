@@ -461,8 +461,14 @@ struct Panel {
   // activation rows gathered through t.a_rows (grouped GEMM)
   __device__ static __forceinline__ void run_gather(const Tile& t, uint8_t* lds) { run_impl<true>(t, lds); }
 
-  template <bool kGather>
+  // kAfrag: the activations are in MFMA fragment order (2 KB per 16 rows x
+  // K-block, launch_quant_act_frag) and stay in that order in LDS: each
+  // DMA load copies one contiguous 1 KB half-unit, and a fragment is two
+  // contiguous 1 KB reads (no swizzle needed, no bank conflicts).  Same
+  // values in the MFMAs, same results.
+  template <bool kGather, bool kAfrag = false>
   __device__ static __forceinline__ void run_impl(const Tile& t, uint8_t* lds) {
+    static_assert(!(kGather && kAfrag), "gathered rows are row-major");
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wn = wave % WGN, wm = wave / WGN;
@@ -549,6 +555,10 @@ struct Panel {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, koff, 0, 0);
       else if (kGather)  // stage rows BN..: the gathered activation rows
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, aoff[kGather ? q - BN / 64 : 0], koff, 0, 0);
+      else if (kAfrag)  // stage rows BN..: half (r0 - BN) / 8 % 2 of the unit of rows m_lo + (r0 - BN) / 16 16
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16,
+                                                 ((r0 - BN) >> 4) * 16 * (int)K + ((r0 - BN) & 8) * 128 + lane * 16,
+                                                 (kb0 + kb) * 16 * kBlock, 0, 0);
       else              // stage rows BN..: activation rows m_lo + r0 - BN ..
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff + (r0 - BN) * (int)K, koff, 0, 0);
     };
@@ -562,12 +572,20 @@ struct Panel {
     auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * WNR + i * 16); };
     // The first fragments of a phase, read right after its barrier; the
     // first MFMA's two operands go first so that it waits for them only.
+    auto load_a = [&](const uint8_t* buf, int j) -> v8i {
+      if constexpr (kAfrag) {  // the 2 KB unit of rows wm WMR + 16 j
+        const uint8_t* p = buf + (BN + wm * WMR + j * 16) * kBlock + lane * 16;
+        return to_v8i(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 1024));
+      } else {
+        return fl(buf, BN + wm * WMR + j * 16);
+      }
+    };
     auto first_frags = [&](v8i (&fa)[TM], v8i (&fw)[kAhead + 1], const uint8_t* buf) {
       fw[0] = load_w(buf, 0);
-      fa[0] = fl(buf, BN + wm * WMR);
+      fa[0] = load_a(buf, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 1; j < TM; ++j) fa[j] = fl(buf, BN + wm * WMR + j * 16);
+      for (int j = 1; j < TM; ++j) fa[j] = load_a(buf, j);
 #pragma unroll
       for (int p = 1; p < kAhead && p < TN; ++p) fw[p] = load_w(buf, p);
     };
@@ -1115,6 +1133,18 @@ struct PanelAfrag {
   }
 };
 
+// A panel tile reading fragment-order activations through its LDS ring.
+template <class P>
+struct PanelFragA {
+  static constexpr int BN = P::BN, BM = P::BM;
+  static constexpr int kLdsBytes = P::kLdsBytes;
+  static constexpr int kThreadsPerWg = P::kThreadsPerWg;
+  static constexpr int kWavesPerSimd = P::kWavesPerSimd;
+  __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) {
+    P::template run_impl<false, true>(t, lds);
+  }
+};
+
 // The prefill tile for fragment-order activations: the 128 x 64 wave tile
 // in four-wave 128 x 256 workgroups, two per CU (69 KB of LDS each).  Each
 // workgroup meets at its own barriers, so the two on a CU wait at
@@ -1425,9 +1455,11 @@ double cu_count() {
 
 Cfg choose(int64_t M, int64_t N, int64_t K) {
   const double cus = cu_count();
-  // Few activation rows but many weight rows: one 128 x 256 panel covers
-  // every row of the activation panel, so each weight row is read once.
-  if (M <= DecodePanel::BM && (N + DecodePanel::BN - 1) / DecodePanel::BN >= (int64_t)(0.625 * cus)) {
+  // Few activation rows (65 .. 256) but many weight rows: one 128 x 256
+  // panel covers every row of the activation panel, so each weight row is
+  // read once.  At M <= 64 the 48-row K-split tile is faster (Qwen3-8B
+  // gate_up, M = 64: 27.7 vs 33.9 us).
+  if (M > 64 && M <= DecodePanel::BM && (N + DecodePanel::BN - 1) / DecodePanel::BN >= (int64_t)(0.625 * cus)) {
     // the 192 x 128 panel when its tiles fill 7/8 or more of the CUs in one round
     const int64_t t192 = ((N + Panel192::BN - 1) / Panel192::BN) * ((M + Panel192::BM - 1) / Panel192::BM);
     if (t192 >= (int64_t)(0.875 * cus) && t192 <= (int64_t)cus) return Cfg::kPanel192;
@@ -1655,10 +1687,11 @@ hipError_t launch_gemm_splitk_noalloc(const uint8_t* a, const float* sa, const u
 
 // Fragment-order activations: the tile the cost model picks for row-major
 // ones, in its fragment-order form (the skinny tiles load the activation
-// fragments straight into registers; every panel choice becomes the
-// four-wave 128 x 256 panel).  Qwen3-8B decode shapes at M = 256 (us,
-// row-major -> fragment order, bit-identical): qkv 19.1 -> 17.6, o 14.0 ->
-// 12.2, down 27.8 -> 24.3; gate_up 46.0 (192 x 128 panel) -> 48.9.
+// fragments straight into registers; the decode panels keep them in
+// fragment order in their LDS ring; the 256 x 256 choice becomes the
+// four-wave 128 x 256 panel, two per CU).  Qwen3-8B decode shapes at M =
+// 256 (us, row-major -> fragment order, bit-identical): qkv 19.3 -> 18.0,
+// o 14.1 -> 12.5, gate_up 45.9 -> 43.5, down 28.8 -> 24.8.
 hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
@@ -1668,6 +1701,10 @@ hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w
       return launch_dense_cfg<Skinny<64, 64, 4, true>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kSkinny48x64:
       return launch_dense_cfg<Skinny<48, 64, 4, true>, 48, 64>(a, sa, w, sw, y, M, N, K, stream);
+    case Cfg::kPanel192:
+      return launch_dense_cfg<PanelFragA<Panel192>, 192, 128>(a, sa, w, sw, y, M, N, K, stream);
+    case Cfg::kDecodePanel:
+      return launch_dense_cfg<PanelFragA<DecodePanel>, 128, 256>(a, sa, w, sw, y, M, N, K, stream);
     default:
       return launch_dense_cfg<WideAfrag4, WideAfrag4::BN, WideAfrag4::BM>(a, sa, w, sw, y, M, N, K, stream);
   }

@@ -76,8 +76,13 @@ def test_quantizer_frag_multi_shape_errors(fb, m, k):
         fb.quantize_acts_per_token_group_frag_multi([ok, bad])
 
 
-@pytest.mark.parametrize("m,n,k", [(16, 130, 256), (48, 384, 768), (272, 520, 512), (256, 256, 2048)])
+@pytest.mark.parametrize("m,n,k", [(16, 130, 256), (48, 384, 768), (272, 520, 512), (256, 256, 2048),
+                                   (80, 20480, 256), (208, 24576, 256)])
 def test_gemm_afrag_against_oracle_and_row_major(fb, m, n, k):
+    """Every tile form: 64- and 48-row K-split tiles, the 256 x 256 choice
+    (four-wave 128 x 256 tiles), the 128 x 256 decode panel (M = 80: one
+    ragged tile of activation rows) and the 192 x 128 panel (M = 208: a
+    second, ragged row tile)."""
     announce("afrag gemm", m, n, k)
     x, _ = activations(m, k, (m, n, k, 0))
     w = bf16_normal((n, k), 0.02, (m, n, k, 1))
@@ -91,7 +96,7 @@ def test_gemm_afrag_against_oracle_and_row_major(fb, m, n, k):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("m", [256, 128, 64, 48, 16])
+@pytest.mark.parametrize("m", [256, 208, 144, 128, 64, 48, 16])
 def test_gemm_afrag_decode_shapes_bit_identical(fb, m):
     """The Qwen3-8B layer shapes at decode batch sizes: the fragment-order
     GEMM picks the row-major GEMM's tile in its fragment-order form (K split
