@@ -432,7 +432,7 @@ struct Skinny {
 // compute k while issuing the loads of K-block k + S - 1 into that stage
 // between the MFMAs.
 // ---------------------------------------------------------------------------
-template <int BN_, int BM_, int WGN, int WGM, int S>
+template <int BN_, int BM_, int WGN, int WGM, int S, bool kWfrag = false>
 struct Panel {
   static constexpr int BN = BN_, BM = BM_;
   static_assert(WGN * WGM == 8, "eight waves");
@@ -551,7 +551,10 @@ struct Panel {
       const int koff = (kb0 + kb) * kBlock;
       const int r0 = 8 * (8 * q + wave);  // stage row of this wave's load q
       auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
-      if (q < BN / 64)  // stage rows 0..BN-1: weight rows n0 + r0 ..
+      if (q < BN / 64 && kWfrag)  // stage rows 0..BN-1: half r0 / 8 % 2 of the weight unit of rows n0 + r0 / 16 16
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, (r0 >> 4) * 16 * (int)K + (r0 & 8) * 128 + lane * 16,
+                                                 (kb0 + kb) * 16 * kBlock, 0, 0);
+      else if (q < BN / 64)  // stage rows 0..BN-1: weight rows n0 + r0 ..
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, koff, 0, 0);
       else if (kGather)  // stage rows BN..: the gathered activation rows
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, aoff[kGather ? q - BN / 64 : 0], koff, 0, 0);
@@ -569,9 +572,14 @@ struct Panel {
       dma_scales(kb, stage);
     };
     constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
-    auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * WNR + i * 16); };
-    // The first fragments of a phase, read right after its barrier; the
-    // first MFMA's two operands go first so that it waits for them only.
+    auto load_w = [&](const uint8_t* buf, int i) -> v8i {
+      if constexpr (kWfrag) {  // the 2 KB unit of weight rows wn WNR + 16 i
+        const uint8_t* p = buf + (wn * WNR + i * 16) * kBlock + lane * 16;
+        return to_v8i(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 1024));
+      } else {
+        return fl(buf, wn * WNR + i * 16);
+      }
+    };
     auto load_a = [&](const uint8_t* buf, int j) -> v8i {
       if constexpr (kAfrag) {  // the 2 KB unit of rows wm WMR + 16 j
         const uint8_t* p = buf + (BN + wm * WMR + j * 16) * kBlock + lane * 16;
@@ -580,6 +588,8 @@ struct Panel {
         return fl(buf, BN + wm * WMR + j * 16);
       }
     };
+    // The first fragments of a phase, read right after its barrier; the
+    // first MFMA's two operands go first so that it waits for them only.
     auto first_frags = [&](v8i (&fa)[TM], v8i (&fw)[kAhead + 1], const uint8_t* buf) {
       fw[0] = load_w(buf, 0);
       fa[0] = load_a(buf, 0);
@@ -699,6 +709,7 @@ struct Panel {
   // final wait) made the prefill tiles 3-7% slower.
   template <bool kGather, class TileAt>
   __device__ static __forceinline__ void run_persistent(int ntiles, TileAt tile_at, uint8_t* lds) {
+    static_assert(!kWfrag, "the grouped tiles read row-major weights");
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wn = wave % WGN, wm = wave / WGN;
@@ -903,236 +914,6 @@ struct Panel {
   }
 };
 
-// ---------------------------------------------------------------------------
-// panel_afrag<BN, BM, ...>: the panel tile for activations stored in the MFMA
-// fragment order (launch_quant_act_frag), four or eight waves: each wave
-// loads its activation fragments straight into VGPRs (two contiguous
-// 16-byte loads per lane per fragment), and only the weight rows and the
-// scales go through LDS.  That leaves room for four one-K-block weight
-// stages used in two alternating pairs: the waves meet at one barrier per
-// two K-blocks (K % 256 == 0).
-// The weight and scale loads of pair p + 1 are issued during the MFMAs of
-// pair p, and the activation fragments of K-block k + 1 during those of
-// K-block k; before the barrier of pair p + 1 every wave waits for all of
-// its loads (vmcnt(0)), so the prefetch depth is one pair.  Same per-element arithmetic and order
-// as panel<>: bit-identical outputs.
-// ---------------------------------------------------------------------------
-template <int BN_, int BM_, int WGN, int WGM, int S>
-struct PanelAfrag {
-  static constexpr int BN = BN_, BM = BM_;
-  static constexpr int kNW = WGN * WGM;  // waves
-  static_assert(kNW == 8 || kNW == 4, "eight waves (one workgroup per CU) or four (two per CU)");
-  static constexpr int WNR = BN / WGN, WMR = BM / WGM;  // rows of a wave's tile
-  static constexpr int TN = WNR / 16, TM = WMR / 16;
-  static_assert(WNR % 16 == 0 && WMR % 16 == 0 && WNR <= 128, "wave tile");
-  static_assert(BN % (8 * kNW) == 0 && BM % 64 == 0, "each load instruction covers 8 weight rows");
-  static constexpr int kLoads = BN / (8 * kNW);        // weight load instructions per wave per K-block
-  static constexpr int kStage = BN * kBlock;           // one K-block of weight rows
-  // Each stage also holds that K-block's scales, after the S operand
-  // stages, in slots of 64 dwords: slots 0 .. BM/64 - 1 the activation
-  // scales of the tile's rows (slot w loaded by wave w), slot BM/64 the
-  // tile's weight scale blocks (loaded by the waves left over, or by wave 0
-  // as a second load when every wave has activation rows).
-  static constexpr int kActSlots = BM / 64;
-  static_assert(kActSlots <= kNW, "one wave per 64 activation rows");
-  static constexpr bool kExtraWeightScaleLoad = kActSlots == kNW;
-  static constexpr int kScaleBytes = (kExtraWeightScaleLoad ? kNW + 1 : kNW) * 64 * 4;
-  static constexpr int kLdsBytes = S * (kStage + kScaleBytes);
-  static_assert(S == 4, "two pairs of K-block sub-stages");
-  static_assert(kLdsBytes <= 160 * 1024, "LDS");
-  static constexpr int kThreadsPerWg = 64 * kNW;
-  static constexpr int kWavesPerSimd = 2;
-  // a wave's weight rows lie in one 128-row scale block when tiles start at
-  // multiples of 128 and the wave's share divides 128
-  static constexpr bool kOneScaleBlock = (BN % kBlock == 0) && (kBlock % WNR == 0);
-
-  __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) {
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wn = wave % WGN, wm = wave / WGN;
-    const int64_t K = t.K;
-    const int KB = (int)(K / kBlock);
-    const int64_t n_hi = (t.n0 + BN < t.N) ? t.n0 + BN : t.N;
-    // weight scale blocks of this wave's rows: nb0, and nb0 + 1 for the
-    // fragments in hi_mask (only when a wave's rows can straddle a block);
-    // wsl0 / wsl1 are their positions among the tile's blocks nbt, nbt + 1, ..
-    const int64_t NBm1 = (t.N - 1) / kBlock;
-    const int64_t nbt = t.n0 / kBlock;
-    const int64_t wrow0 = t.n0 + wn * WNR;
-    const int64_t nb0 = ((wrow0 < t.N) ? wrow0 : t.N - 1) / kBlock;
-    const int64_t nb1 = nb0 + 1 < NBm1 ? nb0 + 1 : NBm1;
-    const int wsl0 = (int)(nb0 - nbt), wsl1 = (int)(nb1 - nbt);
-    uint32_t hi_mask = 0;
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-      if ((wrow0 + i * 16) / kBlock > nb0) hi_mask |= 1u << i;
-    const auto wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
-    const auto ar = make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
-    // a wave whose rows all lie past the last row skips the MFMAs
-    const bool idle = t.m_lo + wm * WMR >= t.m_hi;
-    // Scale staging, one buffer_load_dword ... lds per wave and K-block into
-    // the wave's 64 dwords of the stage's scale area: waves w < BM/64 load
-    // the activation scales of tile rows 64 w + lane, the others the
-    // weight scale blocks nbt + lane.  Rows and blocks past the end sit
-    // outside the buffer range and read zeros.
-    const bool act_scales = wave < kActSlots;
-    const auto wsr = make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
-    const auto scr = act_scales ? make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4) : wsr;
-    const int scvoff = act_scales ? (64 * wave + lane) * KB * 4 : lane * KB * 4;
-    const bool extra_ws = kExtraWeightScaleLoad && wave == 0;  // wave-uniform
-
-    // DMA staging of the weight rows: load q of wave w fills stage rows
-    // R0..R0+7 with R0 = 8 (8 q + w); lane l writes LDS row R0 + l/8 at
-    // physical chunk l%8, so it fetches logical chunk (l%8) ^ (l/8) (the XOR
-    // swizzle).  The row offset is part of the per-lane offset, which the
-    // buffer range check covers: rows past the tile's last row read zeros.
-    const int chunk_off = ((lane & 7) ^ (lane >> 3)) << 4;
-    const int dvoff = (lane >> 3) * (int)K + chunk_off;
-    const FragLds fl(lane);
-
-    v4f acc[TN][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    auto dma_scales = [&](int kb, int stage) {
-      auto* dst = (__attribute__((address_space(3))) void*)(lds + S * kStage + stage * kScaleBytes + wave * 256);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, dst, 4, scvoff, kb * 4, 0, 0);
-    };
-    // the weight scales when every wave has activation rows: wave 0 loads
-    // them for both K-blocks of a pair at the pair's start (a branch inside
-    // the pipelined MFMA loop would cost the compiler its schedule)
-    const int wsvoff = lane * KB * 4;
-    auto dma_wscales = [&](int kb, int stage) {
-      auto* dst = (__attribute__((address_space(3))) void*)(lds + S * kStage + stage * kScaleBytes + kActSlots * 256);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wsr, dst, 4, wsvoff, kb * 4, 0, 0);
-    };
-    auto dma_q = [&](int q, int kb, uint8_t* buf) {
-      const int r0 = 8 * (kNW * q + wave);  // stage row of this wave's load q: weight rows n0 + r0 ..
-      auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, kb * kBlock, 0, 0);
-    };
-    // all loads of one K-block: the weight rows, then the scales
-    auto dma_kblock = [&](int kb, int stage) {
-#pragma unroll
-      for (int q = 0; q < kLoads; ++q) dma_q(q, kb, lds + stage * kStage);
-      dma_scales(kb, stage);
-    };
-    constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
-    auto load_w = [&](const uint8_t* buf, int i) { return fl(buf, wn * WNR + i * 16); };
-    // activation fragments in MFMA order: 2 KB per (16-row group, K-block),
-    // lane l's two 16-byte halves at l * 16 and 1024 + l * 16
-    u32x4 an_lo[TM], an_hi[TM];
-    auto afrag_off = [&](int j, int h) { return (wm * WMR + 16 * j) * (int)K + h * 1024 + lane * 16; };
-    auto load_a = [&](int j, int h, int kb) {
-      const u32x4 v = bload16(ar, afrag_off(j, h), kb * 2048);
-      if (h == 0) an_lo[j] = v; else an_hi[j] = v;
-    };
-    // The first fragments of a phase; the first MFMA's weight operand goes
-    // first so that it waits for that read only.
-    auto first_frags = [&](v8i (&fa)[TM], v8i (&fw)[kAhead + 1], const uint8_t* buf) {
-      fw[0] = load_w(buf, 0);
-#pragma unroll
-      for (int j = 0; j < TM; ++j) fa[j] = to_v8i(an_lo[j], an_hi[j]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int p = 1; p < kAhead && p < TN; ++p) fw[p] = load_w(buf, p);
-    };
-    // One K-block: the product of the K-block in stage `cur`, with the loads
-    // of weight K-block `kb` into stage `fill` and of the activation
-    // fragments of K-block `kb_a` issued after every second MFMA (after
-    // every MFMA when there are few), so that the L2 and LDS-write traffic
-    // does not arrive as one burst right after the barrier.
-    constexpr int kT = TN * TM;
-    constexpr int kPhaseLoads = kLoads + 1 + 2 * TM;
-    constexpr int kEvery = (kT >= 2 * kPhaseLoads) ? 2 : 1;
-    static_assert(kT >= kPhaseLoads, "enough MFMAs to carry the loads");
-    auto phase = [&](int cur, int kb, int fill, int kb_a) {
-      const uint8_t* buf = lds + cur * kStage;
-      v8i fa[TM], fw[kAhead + 1];
-      first_frags(fa, fw, buf);
-      const float* scl = reinterpret_cast<const float*>(lds + S * kStage + cur * kScaleBytes);
-      const float sw0 = scl[BM + wsl0];
-      const float sw1 = kOneScaleBlock ? sw0 : scl[BM + wsl1];
-      float c0[TM], c1[TM];
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const float sa = scl[wm * WMR + j * 16 + r16];
-        c0[j] = sa * sw0;
-        c1[j] = kOneScaleBlock ? c0[j] : sa * sw1;
-      }
-      tile_product<TN, TM, 2, kAhead>(
-          acc, fa, fw, [&](int i) { return load_w(buf, i); },
-          [&](int i, int j) { return (kOneScaleBlock || !((hi_mask >> i) & 1u)) ? c0[j] : c1[j]; },
-          [&](int tt) {
-            if (tt % kEvery != 0 || tt / kEvery >= kPhaseLoads) return false;
-            const int q = tt / kEvery;
-            if (q < 2 * TM)
-              load_a(q / 2, q % 2, kb_a);
-            else if (q < 2 * TM + kLoads)
-              dma_q(q - 2 * TM, kb, lds + fill * kStage);
-            else
-              dma_scales(kb, fill);
-            return true;
-          });
-    };
-    // The workgroup barrier of a pair.  Not __syncthreads(): its fence adds
-    // nothing here (the vmcnt(0) before it already covers every load), and
-    // the LDS reads of the previous pair are waited for here, so no wave
-    // refills a stage that another is still reading.
-    auto barrier = [&]() {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      order_fence();
-    };
-
-    const int kb_last = KB - 1;
-    auto nxt = [&](int kb) { return kb < KB ? kb : kb_last; };  // clamped prefetch
-    if (KB > 0) {
-      dma_kblock(0, 0);
-#pragma unroll
-      for (int j = 0; j < TM; ++j) { load_a(j, 0, 0); load_a(j, 1, 0); }
-      dma_kblock(nxt(1), 1);
-      if (extra_ws) {
-        dma_wscales(0, 0);
-        dma_wscales(nxt(1), 1);
-      }
-    }
-    // K-blocks in pairs (KB even: the host uses this tile only for K % 256
-    // == 0); sub-stages 0,1 and 2,3 alternate.  Loads past the last K-block
-    // re-load it into a stage nobody reads again, keeping the loop body
-    // free of branches.
-    for (int kp = 0; kp < KB; kp += 2) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of pair kp have landed
-      barrier();                                        // and everyone's
-      const int c0 = ((kp >> 1) & 1) ? 2 : 0, f0 = 2 - c0;
-      if (extra_ws) {
-        dma_wscales(nxt(kp + 2), f0);
-        dma_wscales(nxt(kp + 3), f0 + 1);
-      }
-      if (idle) {
-        dma_kblock(nxt(kp + 2), f0);
-        dma_kblock(nxt(kp + 3), f0 + 1);
-      } else {
-        phase(c0, nxt(kp + 2), f0, nxt(kp + 1));
-        order_fence();
-        phase(c0 + 1, nxt(kp + 3), f0 + 1, nxt(kp + 2));
-      }
-      order_fence();
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may be in flight when the workgroup ends
-
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int64_t m = t.m_lo + wm * WMR + j * 16 + r16;
-      if (m >= t.m_hi) continue;
-#pragma unroll
-      for (int i = 0; i < TN; ++i) store4(t.y, t.N, m, t.n0 + wn * WNR + i * 16 + g * 4, acc[i][j]);
-    }
-  }
-};
-
 // A panel tile reading fragment-order activations through its LDS ring.
 template <class P>
 struct PanelFragA {
@@ -1145,15 +926,6 @@ struct PanelFragA {
   }
 };
 
-// The prefill tile for fragment-order activations: the 128 x 64 wave tile
-// in four-wave 128 x 256 workgroups, two per CU (69 KB of LDS each).  Each
-// workgroup meets at its own barriers, so the two on a CU wait at
-// different times; the same wave tile in one eight-wave 256 x 256
-// workgroup per CU (same traffic per output) is slower on the Qwen3-8B
-// prefill shapes at M = 8192: 1.82 vs 1.92 PF over the four (gate_up 920
-// vs 849 us, o 171 vs 156 us, qkv 247 vs 239 us, down 400 vs 401 us),
-// bit-identical outputs.
-using WideAfrag4 = PanelAfrag<128, 256, 1, 4, 4>;
 
 using Wide = Panel<256, 256, 2, 4, 2>;
 using DecodePanel = Panel<128, 256, 2, 4, 3>;
@@ -1687,11 +1459,13 @@ hipError_t launch_gemm_splitk_noalloc(const uint8_t* a, const float* sa, const u
 
 // Fragment-order activations: the tile the cost model picks for row-major
 // ones, in its fragment-order form (the skinny tiles load the activation
-// fragments straight into registers; the decode panels keep them in
-// fragment order in their LDS ring; the 256 x 256 choice becomes the
-// four-wave 128 x 256 panel, two per CU).  Qwen3-8B decode shapes at M =
-// 256 (us, row-major -> fragment order, bit-identical): qkv 19.3 -> 18.0,
-// o 14.1 -> 12.5, gate_up 45.9 -> 43.5, down 28.8 -> 24.8.
+// fragments straight into registers; the panels keep them in fragment
+// order in their LDS ring).  Qwen3-8B decode shapes at M = 256 (us,
+// row-major -> fragment order, bit-identical): qkv 19.3 -> 18.0, o 14.1 ->
+// 12.5, gate_up 45.9 -> 43.5, down 28.8 -> 24.8; the four prefill shapes at
+// M = 8192 on quantized normal data: 1.77 -> 1.95 PF (the four-wave
+// 128 x 256 panel that loads activation fragments into registers, two per
+// CU: 1.90 PF).
 hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
@@ -1706,7 +1480,7 @@ hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w
     case Cfg::kDecodePanel:
       return launch_dense_cfg<PanelFragA<DecodePanel>, 128, 256>(a, sa, w, sw, y, M, N, K, stream);
     default:
-      return launch_dense_cfg<WideAfrag4, WideAfrag4::BN, WideAfrag4::BM>(a, sa, w, sw, y, M, N, K, stream);
+      return launch_dense_cfg<PanelFragA<Wide>, 256, 256>(a, sa, w, sw, y, M, N, K, stream);
   }
 }
 

@@ -298,11 +298,14 @@ fp8bq_status quantize_act_per_token_group_frag(const uint16_t* x_bf16, uint8_t* 
  *   gemm_w8a8_blockscaled.
  *   Requires M % 16 == 0 and K % 256 == 0 (K <= 2^22); FP8BQ_ERR_BAD_SHAPE
  *   otherwise.  The tile is chosen per shape as for gemm_w8a8_blockscaled
- *   (few activation rows: K split over the waves of a 64- or 48-row tile;
- *   many rows: 128 x 256 workgroup tiles, two per CU).  This is the
- *   library's path for activations with M % 16 == 0 and K % 256 == 0: on
- *   the Qwen3-8B layer shapes it is faster than gemm_w8a8_blockscaled on
- *   row-major codes at both decode (M = 256) and prefill (M = 8192) sizes.
+ *   (few activation rows: K split over the waves of a 64- or 48-row tile
+ *   that loads the fragments straight into registers; more rows: the panel
+ *   tiles, which keep the fragment order in their LDS ring), and the output
+ *   is bit-identical to gemm_w8a8_blockscaled's on the row-major codes.
+ *   This is the library's path for activations with M % 16 == 0 and
+ *   K % 256 == 0: on the Qwen3-8B layer shapes it is faster than
+ *   gemm_w8a8_blockscaled at both decode (M = 256) and prefill (M = 8192)
+ *   sizes.
  */
 fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8,
                                          const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
