@@ -6,10 +6,11 @@ the four BF16 activations (qkv 4096, o 4096, gate_up 4096, down 12288 input
 features) per token in 1x128 groups, and run the four block-scaled FP8
 GEMMs (qkv 4096->6144, o 4096->4096, gate_up 4096->24576, down
 12288->4096; FP32 accumulation, BF16 output) on E4M3 weights with
-128x128-block scales quantized beforehand (once per RL step).  The
-activation codes are written in the MFMA fragment order that the library's
-prefill GEMM reads (quantize_act_per_token_group_frag +
-gemm_w8a8_blockscaled_afrag, its path for M % 16 == 0 and K % 256 == 0).
+128x128-block scales quantized beforehand (once per RL step).  Both
+operands' codes are in the MFMA fragment order that the library's fastest
+GEMM reads (quantize_weights_blockwise_frag_multi,
+quantize_act_per_token_group_frag, gemm_w8a8_blockscaled_frag: its path for
+M % 16 == 0, N % 16 == 0 and K % 256 == 0).
 Steps cycle through four copies of every buffer (1.4 GB each), so a copy
 has left the 256 MB Infinity Cache before it is used again.  Inputs are
 seeded synthetic tensors already resident in HBM.
@@ -21,7 +22,7 @@ weight re-quantization of all 36 layers of the model (6.95 G parameters,
 checks sampled outputs of both against the CPU oracle (`parity`), times the
 oracle on the host's cores (`cpu_baseline`), and adds per-configuration
 measurements (`detail`: the decode layer step at M = 256, the prefill
-GEMMs on both activation layouts, the Qwen3-30B-A3B MoE layer, and the
+GEMMs on the three operand layouts, the Qwen3-30B-A3B MoE layer, and the
 widened operations).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail] [--no-cpu]
@@ -193,7 +194,9 @@ def main():
     # ---------------------------------------------------------------- inputs
     # Step s uses buffer set s % SETS (copies of the same inputs, 1.4 GB per
     # set): a set's bytes have left the 256 MB Infinity Cache before it is
-    # used again.  The weights are quantized once, before the timed steps.
+    # used again.  The weights are quantized once, before the timed steps,
+    # into the MFMA fragment order the GEMM reads (as the per-step
+    # re-quantization writes them).
     SETS = 4
     base = []
     for i, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
@@ -212,7 +215,7 @@ def main():
                 "xs": torch.empty((M, k // 128), dtype=torch.float32, device=dev),
                 "y": torch.empty((M, n), dtype=torch.bfloat16, device=dev),
             })
-        fb.quantize_weights_blockwise_multi([b[3] for b in base], [(L["wq"], L["ws"]) for L in layers])
+        fb.quantize_weights_blockwise_frag_multi([b[3] for b in base], [(L["wq"], L["ws"]) for L in layers])
         sets.append(layers)
     w_bf16 = {name: w for name, _, _, w, _ in base}
     del base
@@ -236,7 +239,7 @@ def main():
         if record:
             e[1].record(stream)
         for L in ls:
-            fb.gemm_w8a8_blockscaled_afrag(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
+            fb.gemm_w8a8_blockscaled_frag(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
         if record:
             e[2].record(stream)
             ev.append(e)
@@ -282,11 +285,12 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights; N(0,1) activations with 1% outlier channels x30; "
                 "Qwen3-8B layer shapes; 4 buffer sets rotated across steps)",
         "config": {
-            "workload": "qwen3-8b-prefill-layer: 1x128 act quant (fragment order) + 4 W8A8 block-scaled GEMMs "
-                        "(qkv/o/gate_up/down), M=8192",
+            "workload": "qwen3-8b-prefill-layer: 1x128 act quant + 4 W8A8 block-scaled GEMMs "
+                        "(qkv/o/gate_up/down), M=8192, operands in MFMA fragment order",
             "tokens": M,
             "gemm_flops_per_step": gemm_flops,
-            "requant_workload": "qwen3-8b 36-layer weight re-quant sweep: 6.95 G params, 4 calls with batch=36",
+            "requant_workload": "qwen3-8b 36-layer weight re-quant sweep: 6.95 G params, 4 calls with batch=36, "
+                                "codes in fragment order",
             "parallelism": "1 GPU",
         },
         "roofline": roofline,
@@ -325,12 +329,12 @@ def roof_entry(phase, ms, byt, flops):
     return e
 
 
-def requant_sweep(fb, dev):
+def requant_sweep(fb, dev, frag=True):
     """The per-step re-quantization of every quantized linear weight of the
     model: 36 layers x {qkv, o, gate_up, down} (6.95 G BF16 parameters),
-    four calls with batch = 36.  SWEEP_REPS timed sweeps (HIP events around
-    each) after two untimed ones; 21 GB per sweep, far past the Infinity
-    Cache, so no rotation is needed."""
+    four calls with batch = 36, codes in fragment order (frag) or row-major.
+    SWEEP_REPS timed sweeps (HIP events around each) after two untimed ones;
+    21 GB per sweep, far past the Infinity Cache, so no rotation is needed."""
     import torch
 
     from synthetic import LAYER_SHAPES_QWEN3_8B, device_bf16_normal
@@ -345,7 +349,7 @@ def requant_sweep(fb, dev):
 
     def run():
         for _, w, q, s in bufs:
-            fb.quantize_weight_blockwise(w, q, s)
+            fb.quantize_weight_blockwise(w, q, s, frag=frag)
 
     for _ in range(2):
         run()
@@ -360,7 +364,7 @@ def requant_sweep(fb, dev):
     torch.cuda.synchronize()
     t = sorted(a.elapsed_time(b) for a, b in evs)
     return {"ms": sum(t) / len(t), "median_ms": t[len(t) // 2], "min_ms": t[0], "reps": len(t), "bytes": byt,
-            "params": sum(w.numel() for _, w, _, _ in bufs), "tensors": bufs}
+            "params": sum(w.numel() for _, w, _, _ in bufs), "frag": frag, "tensors": bufs}
 
 
 # ---------------------------------------------------------------------------
@@ -470,7 +474,7 @@ def detail(fb, dev, with_cpu=True):
 def decode_step(fb, dev, with_cpu):
     """The Qwen3-8B decode layer step at M = 256: one launch re-quantizes the
     four weight matrices, one launch quantizes the four activations (codes
-    in fragment order), then the four fragment-order GEMMs.  Steps cycle
+    of both in fragment order), then the four fragment-order GEMMs.  Steps cycle
     through four copies of the layer's buffers (0.6 GB each).  Phases timed
     with HIP events; the oracle runs the same step on the same input bytes
     (parity and a CPU time on all its threads)."""
@@ -502,14 +506,14 @@ def decode_step(fb, dev, with_cpu):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
         if record:
             e[0].record(stream)
-        fb.quantize_weights_blockwise_multi([L["w"] for L in ls], [(L["wq"], L["ws"]) for L in ls])
+        fb.quantize_weights_blockwise_frag_multi([L["w"] for L in ls], [(L["wq"], L["ws"]) for L in ls])
         if record:
             e[1].record(stream)
         fb.quantize_acts_per_token_group_frag_multi([L["x"] for L in ls], [(L["xq"], L["xs"]) for L in ls])
         if record:
             e[2].record(stream)
         for L in ls:
-            fb.gemm_w8a8_blockscaled_afrag(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
+            fb.gemm_w8a8_blockscaled_frag(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
         if record:
             e[3].record(stream)
             ev.append(e)
@@ -541,28 +545,35 @@ def decode_step(fb, dev, with_cpu):
                     "GBps": round(gm_b / ph["gemm"] / 1e6, 1),
                     "frac_hbm": round(gm_b / ph["gemm"] / 1e6 / HBM_PEAK_GBPS, 4)}}
     # each GEMM on its own, as the step runs it (graph replays over the four
-    # buffer sets), and the row-major GEMM on the same activations
+    # buffer sets), and on the other operand layouts: fragment-order
+    # activations with row-major weights, and both row-major
     for ls in sets:
         for L in ls:
             L["xr"], _ = fb.quantize_act_per_token_group(L["x"])
+            L["wr"], _ = fb.quantize_weight_blockwise(L["w"])
     per = {}
     for i, L in enumerate(layers):
         f = 2 * M * L["n"] * L["k"]
         byt = M * L["k"] + L["n"] * L["k"] + 2 * M * L["n"] + L["xs"].numel() * 4 + L["ws"].numel() * 4
-        us, _ = _time_graph_ms([lambda t=t[i]: fb.gemm_w8a8_blockscaled_afrag(t["xq"], t["xs"], t["wq"], t["ws"],
-                                                                              t["y"]) for t in sets])
+        us, _ = _time_graph_ms([lambda t=t[i]: fb.gemm_w8a8_blockscaled_frag(t["xq"], t["xs"], t["wq"], t["ws"],
+                                                                             t["y"]) for t in sets])
         y_frag = layers[i]["y"].clone()
-        rm, _ = _time_graph_ms([lambda t=t[i]: fb.gemm_w8a8_blockscaled(t["xr"], t["xs"], t["wq"], t["ws"], t["y"])
+        af, _ = _time_graph_ms([lambda t=t[i]: fb.gemm_w8a8_blockscaled_afrag(t["xq"], t["xs"], t["wr"], t["ws"],
+                                                                              t["y"]) for t in sets])
+        y_afrag = layers[i]["y"].clone()
+        rm, _ = _time_graph_ms([lambda t=t[i]: fb.gemm_w8a8_blockscaled(t["xr"], t["xs"], t["wr"], t["ws"], t["y"])
                                 for t in sets])
+        y_row = layers[i]["y"]
+        same = torch.equal(y_frag.view(torch.int16), y_row.view(torch.int16)) and torch.equal(
+            y_afrag.view(torch.int16), y_row.view(torch.int16))
         per[L["name"]] = {"us": round(us * 1e3, 2), "frac_hbm": round(byt / us / 1e6 / HBM_PEAK_GBPS, 4),
-                          "TFLOPs": round(f / us / 1e9, 1), "row_major_us": round(rm * 1e3, 2),
-                          "bit_identical": bool(torch.equal(y_frag.view(torch.int16),
-                                                            layers[i]["y"].view(torch.int16)))}
+                          "TFLOPs": round(f / us / 1e9, 1), "afrag_us": round(af * 1e3, 2),
+                          "row_major_us": round(rm * 1e3, 2), "bit_identical": bool(same)}
     res["gemm_each"] = per
     res["splitk_small_batch"] = splitk_small_batch(fb, dev, sets[0])
     for ls in sets:
         for L in ls:
-            del L["xr"]
+            del L["xr"], L["wr"]
     step(False, 0)
     torch.cuda.synchronize()
     if with_cpu:
@@ -584,7 +595,7 @@ def splitk_small_batch(fb, dev, layer_set):
             need = fb.splitk_workspace_bytes(m, n, k)
             if need == 0:
                 continue
-            wq = [L["wq"]] + [L["wq"].clone() for _ in range(3)]
+            wq = [L["wr"]] + [L["wr"].clone() for _ in range(3)]
             xq, xs = L["xr"][:m].contiguous(), L["xs"][:m].contiguous()
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             wsp = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -597,31 +608,43 @@ def splitk_small_batch(fb, dev, layer_set):
 
 
 def prefill_gemms(fb, dev):
-    """Each prefill GEMM (M = 8192) on its own, row-major and fragment-order
-    activations, timed from graph replays over enough buffer copies (input
-    codes, weights, output) that a copy has left the Infinity Cache before
-    it comes round again; the two layouts' outputs compared bit for bit."""
+    """Each prefill GEMM (M = 8192) on its own, on three operand layouts
+    (both row-major; fragment-order activations; both in fragment order),
+    timed from graph replays over enough buffer copies (input codes,
+    weights, output) that a copy has left the Infinity Cache before it comes
+    round again; the layouts' outputs compared bit for bit."""
     import torch
 
     from synthetic import LAYER_SHAPES_QWEN3_8B, device_activations, device_bf16_normal
 
     m = PREFILL_M
-    pre, tot_f, tot_ms, tot_fr_ms = {}, 0.0, 0.0, 0.0
+    pre, tot_f = {}, 0.0
+    tot = {"row": 0.0, "afrag": 0.0, "frag": 0.0}
     for i, (name, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B):
-        wq, ws = fb.quantize_weight_blockwise(device_bf16_normal((n, k), 0.02, seed=300 + i))
+        wb = device_bf16_normal((n, k), 0.02, seed=300 + i)
+        wq, ws = fb.quantize_weight_blockwise(wb)
+        wf, _ = fb.quantize_weight_blockwise_frag(wb)
+        del wb
         x, _ = device_activations(m, k, seed=400 + 2 * i, outlier_frac=OUTLIER_FRAC, outlier_mult=OUTLIER_MULT)
         xq, xs = fb.quantize_act_per_token_group(x)
         xf, _ = fb.quantize_act_per_token_group_frag(x)
-        nsets = rotations(m * k + n * k + 2 * m * n)
-        sets = [(xq, xf, xs, wq, ws, torch.empty((m, n), dtype=torch.bfloat16, device=dev))]
-        sets += [(xq.clone(), xf.clone(), xs.clone(), wq.clone(), ws.clone(),
-                  torch.empty((m, n), dtype=torch.bfloat16, device=dev)) for _ in range(nsets - 1)]
-        ms, _ = _time_graph_ms([lambda t=t: fb.gemm_w8a8_blockscaled(t[0], t[2], t[3], t[4], t[5]) for t in sets],
-                               calls=max(4, nsets))
-        y_row = sets[0][5].clone()
-        fr_ms, _ = _time_graph_ms([lambda t=t: fb.gemm_w8a8_blockscaled_afrag(t[1], t[2], t[3], t[4], t[5])
-                                   for t in sets], calls=max(4, nsets))
-        same = bool(torch.equal(y_row.view(torch.int16), sets[0][5].view(torch.int16)))
+        nsets = rotations(2 * m * k + 2 * n * k + 2 * m * n)
+        mk = lambda c: {"xq": xq if c == 0 else xq.clone(), "xf": xf if c == 0 else xf.clone(),
+                        "xs": xs if c == 0 else xs.clone(), "wq": wq if c == 0 else wq.clone(),
+                        "wf": wf if c == 0 else wf.clone(), "ws": ws if c == 0 else ws.clone(),
+                        "y": torch.empty((m, n), dtype=torch.bfloat16, device=dev)}
+        sets = [mk(c) for c in range(nsets)]
+        calls = max(4, nsets)
+        ms = {}
+        ms["row"], _ = _time_graph_ms([lambda t=t: fb.gemm_w8a8_blockscaled(t["xq"], t["xs"], t["wq"], t["ws"], t["y"])
+                                       for t in sets], calls=calls)
+        y_row = sets[0]["y"].clone()
+        ms["afrag"], _ = _time_graph_ms([lambda t=t: fb.gemm_w8a8_blockscaled_afrag(t["xf"], t["xs"], t["wq"], t["ws"],
+                                                                                    t["y"]) for t in sets], calls=calls)
+        same = torch.equal(y_row.view(torch.int16), sets[0]["y"].view(torch.int16))
+        ms["frag"], _ = _time_graph_ms([lambda t=t: fb.gemm_w8a8_blockscaled_frag(t["xf"], t["xs"], t["wf"], t["ws"],
+                                                                                  t["y"]) for t in sets], calls=calls)
+        same = same and torch.equal(y_row.view(torch.int16), sets[0]["y"].view(torch.int16))
         del sets, y_row
         xsets = [(x, torch.empty_like(xq), torch.empty_like(xs))]
         xsets += [(x.clone(), torch.empty_like(xq), torch.empty_like(xs)) for _ in range(rotations(m * k * 3) - 1)]
@@ -630,22 +653,24 @@ def prefill_gemms(fb, dev):
         del xsets
         f = 2 * m * n * k
         tot_f += f
-        tot_ms += ms
-        tot_fr_ms += fr_ms
+        for key in tot:
+            tot[key] += ms[key]
         aq_b = m * k * 3 + m * (k // 128) * 4
-        pre[name] = {"buffer_sets": nsets, "gemm_us": round(ms * 1e3, 1), "TFLOPs": round(f / ms / 1e9, 1),
-                     "frac_fp8_peak": round(f / ms / 1e9 / FP8_PEAK_TFLOPS, 4),
-                     "afrag_gemm_us": round(fr_ms * 1e3, 1), "afrag_TFLOPs": round(f / fr_ms / 1e9, 1),
-                     "afrag_frac_fp8_peak": round(f / fr_ms / 1e9 / FP8_PEAK_TFLOPS, 4),
-                     "afrag_bit_identical": same,
-                     "act_quant_us": round(aq_ms * 1e3, 1), "afrag_act_quant_us": round(aqf_ms * 1e3, 1),
-                     "act_quant_GBps": round(aq_b / aq_ms / 1e6, 1), "afrag_act_quant_GBps": round(aq_b / aqf_ms / 1e6, 1)}
-        del wq, ws, x, xq, xs, xf
+        e = {"buffer_sets": nsets, "bit_identical": bool(same)}
+        for key, label in (("row", ""), ("afrag", "afrag_"), ("frag", "frag_")):
+            e[label + "gemm_us"] = round(ms[key] * 1e3, 1)
+            e[label + "TFLOPs"] = round(f / ms[key] / 1e9, 1)
+            e[label + "frac_fp8_peak"] = round(f / ms[key] / 1e9 / FP8_PEAK_TFLOPS, 4)
+        e.update({"act_quant_us": round(aq_ms * 1e3, 1), "afrag_act_quant_us": round(aqf_ms * 1e3, 1),
+                  "act_quant_GBps": round(aq_b / aq_ms / 1e6, 1),
+                  "afrag_act_quant_GBps": round(aq_b / aqf_ms / 1e6, 1)})
+        pre[name] = e
+        del wq, wf, ws, x, xq, xs, xf
         torch.cuda.empty_cache()
-    pre["all4"] = {"TFLOPs": round(tot_f / tot_ms / 1e9, 1),
-                   "frac_fp8_peak": round(tot_f / tot_ms / 1e9 / FP8_PEAK_TFLOPS, 4),
-                   "afrag_TFLOPs": round(tot_f / tot_fr_ms / 1e9, 1),
-                   "afrag_frac_fp8_peak": round(tot_f / tot_fr_ms / 1e9 / FP8_PEAK_TFLOPS, 4)}
+    pre["all4"] = {}
+    for key, label in (("row", ""), ("afrag", "afrag_"), ("frag", "frag_")):
+        pre["all4"][label + "TFLOPs"] = round(tot_f / tot[key] / 1e9, 1)
+        pre["all4"][label + "frac_fp8_peak"] = round(tot_f / tot[key] / 1e9 / FP8_PEAK_TFLOPS, 4)
     return pre
 
 
@@ -881,13 +906,13 @@ def _r14(y_bits, y_ref):
 def cpu_baseline_and_parity(fb, layers, w_bf16, sweep, gemm_flops):
     """Parity of the timed prefill step and of the re-quant sweep against the
     oracle, and the oracle's time for the same work on the host's cores.
+    Codes are compared bit for bit with the GPU's fragment-order codes after
+    the oracle's permutation, scales bit for bit.
 
     Prefill (the headline): per projection, 192 consecutive token rows (12
-    groups of 16, at a seeded offset) are quantized by the oracle (codes
-    compared bit for bit with the GPU's fragment-order codes after the
-    oracle's permutation, scales bit for bit) and multiplied by the
-    FP32-accumulated oracle GEMM with the oracle's own weight codes (which
-    are compared bit for bit with the GPU's).  The GPU rows meet R14
+    groups of 16, at a seeded offset) are quantized by the oracle and
+    multiplied by the FP32-accumulated oracle GEMM with the oracle's own
+    weight codes (the whole matrix quantized by the oracle).  The GPU rows meet R14
     against it.  The oracle GEMM is timed at 64 and 192 rows; its time for
     all 8192 rows is the linear fit (a fixed part that decodes the weights,
     a per-row part), plus the per-row time of its activation quantizer.
@@ -913,7 +938,8 @@ def cpu_baseline_and_parity(fb, layers, w_bf16, sweep, gemm_flops):
         n, k = L["n"], L["k"]
         gq, gs = L["wq"].cpu().numpy(), L["ws"].cpu().numpy()
         qw, sw = oracle_quant_weight(_bits(w_bf16[L["name"]]), threads)
-        pp["weights_bitexact"] &= bool(np.array_equal(gq, qw) and np.array_equal(gs.view(np.uint32), sw.view(np.uint32)))
+        pp["weights_bitexact"] &= bool(np.array_equal(gq, act_fragment_order(qw))
+                                       and np.array_equal(gs.view(np.uint32), sw.view(np.uint32)))
         xb = _bits(L["x"][r0:r0 + 192])
         t = time.perf_counter()
         qa, sa = quant_act_per_token_group(xb)
@@ -944,7 +970,8 @@ def cpu_baseline_and_parity(fb, layers, w_bf16, sweep, gemm_flops):
             oq, os_ = oracle_quant_weight(wb, threads)
             t_rq += time.perf_counter() - t
             params += wb.size
-            ps["bitexact"] &= bool(np.array_equal(q[layer].cpu().numpy(), oq) and np.array_equal(
+            want = act_fragment_order(oq) if sweep["frag"] else oq
+            ps["bitexact"] &= bool(np.array_equal(q[layer].cpu().numpy(), want) and np.array_equal(
                 s[layer].cpu().numpy().view(np.uint32), os_.view(np.uint32)))
     ps["pass"] = ps["bitexact"]
     par["requant_sweep_36_layers"] = ps
@@ -1004,8 +1031,9 @@ def decode_cpu_and_parity(layers, m, flops):
             "seconds": {"requant": round(t_rq, 3), "act_quant": round(t_aq, 3), "gemm": round(t_gm, 3)}}
     par = {"requant_bitexact": True, "act_quant_bitexact": True, "gemm": {}}
     for L, (qw, sw), (qa, sa), y_ref in zip(layers, wres, ares, yres):
-        par["requant_bitexact"] &= bool(np.array_equal(L["wq"].cpu().numpy(), qw) and np.array_equal(
-            L["ws"].cpu().numpy().view(np.uint32), sw.view(np.uint32)))
+        par["requant_bitexact"] &= bool(np.array_equal(L["wq"].cpu().numpy(), act_fragment_order(qw))
+                                        and np.array_equal(L["ws"].cpu().numpy().view(np.uint32),
+                                                           sw.view(np.uint32)))
         par["act_quant_bitexact"] &= bool(np.array_equal(L["xq"].cpu().numpy(), act_fragment_order(qa))
                                           and np.array_equal(L["xs"].cpu().numpy().view(np.uint32),
                                                              sa.view(np.uint32)))
@@ -1146,9 +1174,11 @@ def gemm_profile_cases():
     sys.path.insert(0, ROOT)
     from synthetic import LAYER_SHAPES_QWEN3_8B, MOE_QWEN3_30B_A3B
 
+    # decode and "prefill frag": both operands in fragment order (the
+    # library's path at these shapes); "prefill": both row-major
     cases = [("decode %s" % nm, 256, n, k, 0) for nm, n, k in LAYER_SHAPES_QWEN3_8B]
     cases += [("prefill %s" % nm, 8192, n, k, 0) for nm, n, k in LAYER_SHAPES_QWEN3_8B]
-    cases += [("prefill afrag %s" % nm, 8192, n, k, 0) for nm, n, k in LAYER_SHAPES_QWEN3_8B]
+    cases += [("prefill frag %s" % nm, 8192, n, k, 0) for nm, n, k in LAYER_SHAPES_QWEN3_8B]
     moe = MOE_QWEN3_30B_A3B
     mt = moe["tokens"] * moe["top_k"]
     cases.append(("MoE fc1 gate_up", mt, moe["gate_up"][0], moe["gate_up"][1], moe["experts"]))
@@ -1170,18 +1200,19 @@ def gemm_profile():
     for i, (label, m, n, k, g) in enumerate(gemm_profile_cases()):
         w = device_bf16_normal((g, n, k) if g else (n, k), 0.02, seed=700 + i)
         x = device_bf16_normal((m, k), 1.0, seed=800 + i)
-        wq, ws = fb.quantize_weight_blockwise(w)
-        afrag = label.startswith("prefill afrag")
-        if afrag:
+        frag = label.startswith("decode") or label.startswith("prefill frag")
+        if frag:
+            wq, ws = fb.quantize_weight_blockwise_frag(w)
             xq, xs = fb.quantize_act_per_token_group_frag(x)
         else:
+            wq, ws = fb.quantize_weight_blockwise(w)
             xq, xs = fb.quantize_act_per_token_group(x)
         del w, x
         y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
         torch.cuda.synchronize()
         for _ in range(GEMM_PROFILE_REPS):
-            if afrag:
-                fb.gemm_w8a8_blockscaled_afrag(xq, xs, wq, ws, y)
+            if frag:
+                fb.gemm_w8a8_blockscaled_frag(xq, xs, wq, ws, y)
             elif g:
                 fb.grouped_gemm_w8a8_blockscaled(xq, xs, wq, ws, offsets, y)
             else:
@@ -1313,16 +1344,16 @@ def bw_profile_cases():
     from synthetic import LAYER_SHAPES_QWEN3_8B, MOE_QWEN3_30B_A3B
 
     cases = []
-    for nm, n, k in LAYER_SHAPES_QWEN3_8B:  # 36-layer sweep: one call per projection
+    for nm, n, k in LAYER_SHAPES_QWEN3_8B:  # 36-layer sweep: one call per projection, fragment order
         cases.append(("requant sweep %s (batch 36)" % nm, "quant_weight_kernel",
                       SWEEP_LAYERS * (n * k * 3 + (n // 128) * (k // 128) * 4)))
     for k in (4096, 12288):
         ab = PREFILL_M * k * 3 + PREFILL_M * (k // 128) * 4
         cases.append(("prefill act quant 8192x%d" % k, "quant_act_kernel", ab))
         cases.append(("prefill act quant frag 8192x%d" % k, "quant_act_frag_kernel", ab))
-    cases.append(("decode act quant, 4 activations (one launch)", "quant_act_multi_kernel",
+    cases.append(("decode act quant frag, 4 activations (one launch)", "quant_act_frag_multi_kernel",
                   sum(256 * k * 3 + 256 * (k // 128) * 4 for _, _, k in LAYER_SHAPES_QWEN3_8B)))
-    cases.append(("decode requant, 4 matrices (one launch)", "quant_weight_multi_kernel",
+    cases.append(("decode requant frag, 4 matrices (one launch)", "quant_weight_multi_kernel",
                   sum(n * k * 3 + (n // 128) * (k // 128) * 4 for _, n, k in LAYER_SHAPES_QWEN3_8B)))
     moe = MOE_QWEN3_30B_A3B
     T, k, H, F = moe["tokens"], moe["top_k"], moe["hidden"], moe["ffn"]
@@ -1363,7 +1394,7 @@ def bw_profile():
         q = torch.empty((SWEEP_LAYERS, n, k), dtype=torch.uint8, device=dev)
         s = torch.empty((SWEEP_LAYERS, n // 128, k // 128), dtype=torch.float32, device=dev)
         for _ in range(R):
-            fb.quantize_weight_blockwise(w, q, s)
+            fb.quantize_weight_blockwise_frag(w, q, s)
         del w, q, s
         done("requant sweep " + nm)
     for k in (4096, 12288):
@@ -1379,11 +1410,11 @@ def bw_profile():
         done("prefill act quant %d" % k)
     xs = [device_bf16_normal((256, k), 1.0, seed=200 + i) for i, (_, _, k) in enumerate(LAYER_SHAPES_QWEN3_8B)]
     for _ in range(R):
-        fb.quantize_acts_per_token_group_multi(xs)
+        fb.quantize_acts_per_token_group_frag_multi(xs)
     ws = [device_bf16_normal((n, k), 0.02, seed=100 + i) for i, (_, n, k) in enumerate(LAYER_SHAPES_QWEN3_8B)]
     torch.cuda.synchronize()
     for _ in range(R):
-        fb.quantize_weights_blockwise_multi(ws)
+        fb.quantize_weights_blockwise_frag_multi(ws)
     del xs, ws
     done("decode multi")
     moe = MOE_QWEN3_30B_A3B

@@ -26,6 +26,8 @@ __all__ = [
     "FP8BQError",
     "quantize_weight_blockwise",
     "quantize_weights_blockwise_multi",
+    "quantize_weight_blockwise_frag",
+    "quantize_weights_blockwise_frag_multi",
     "quantize_act_per_token_group",
     "quantize_acts_per_token_group_multi",
     "quantize_acts_per_token_group_frag_multi",
@@ -35,6 +37,7 @@ __all__ = [
     "gemm_w8a8_blockscaled_splitk_noalloc",
     "splitk_workspace_bytes",
     "gemm_w8a8_blockscaled_afrag",
+    "gemm_w8a8_blockscaled_frag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
     "check_group_offsets",
@@ -61,11 +64,14 @@ EXPORTS = (
     "fp8bq_status_string",
     "quantize_weight_blockwise",
     "quantize_weights_blockwise_multi",
+    "quantize_weight_blockwise_frag",
+    "quantize_weights_blockwise_frag_multi",
     "quantize_act_per_token_group",
     "quantize_acts_per_token_group_multi",
     "quantize_acts_per_token_group_frag_multi",
     "quantize_act_per_token_group_frag",
     "gemm_w8a8_blockscaled",
+    "gemm_w8a8_blockscaled_frag",
     "gemm_w8a8_blockscaled_splitk",
     "gemm_w8a8_blockscaled_splitk_workspace",
     "gemm_w8a8_blockscaled_splitk_noalloc",
@@ -117,6 +123,9 @@ def _load():
     lib.quantize_weight_blockwise.argtypes = [p, p, p, i64, i64, i64, p]
     lib.quantize_act_per_token_group.argtypes = [p, p, p, i64, i64, p]
     lib.quantize_weights_blockwise_multi.argtypes = [ctypes.POINTER(_WeightDesc), i64, p]
+    lib.quantize_weight_blockwise_frag.argtypes = [p, p, p, i64, i64, i64, p]
+    lib.quantize_weights_blockwise_frag_multi.argtypes = [ctypes.POINTER(_WeightDesc), i64, p]
+    lib.gemm_w8a8_blockscaled_frag.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.quantize_acts_per_token_group_multi.argtypes = [ctypes.POINTER(_ActDesc), i64, p]
     lib.quantize_acts_per_token_group_frag_multi.argtypes = [ctypes.POINTER(_ActDesc), i64, p]
     lib.gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, p]
@@ -207,8 +216,9 @@ def _tile_id(tile):
     return TILES[tile]
 
 
-def quantize_weight_blockwise(w, out=None, scale=None):
-    """BF16 weights [N, K] or [B, N, K] -> (E4M3 codes uint8, same shape; float32 scales [.., N/128, K/128])."""
+def quantize_weight_blockwise(w, out=None, scale=None, frag=False):
+    """BF16 weights [N, K] or [B, N, K] -> (E4M3 codes uint8, same shape; float32 scales [.., N/128, K/128]).
+    ``frag``: codes in MFMA fragment order (quantize_weight_blockwise_frag; N % 16 == 0, K % 128 == 0)."""
     if w.dim() not in (2, 3):
         raise ValueError("weights must be [N, K] or [B, N, K]")
     b, n, k = (1, *w.shape) if w.dim() == 2 else tuple(w.shape)
@@ -220,16 +230,21 @@ def quantize_weight_blockwise(w, out=None, scale=None):
         scale = torch.empty(sshape, dtype=torch.float32, device=w.device)
     _require(out, "out", _U8, w.shape, w.device)
     _require(scale, "scale", torch.float32, sshape, w.device)
+    name = "quantize_weight_blockwise_frag" if frag else "quantize_weight_blockwise"
     with torch.cuda.device(w.device):
-        _check("quantize_weight_blockwise",
-               _lib.quantize_weight_blockwise(_ptr(w), _ptr(out), _ptr(scale), b, n, k, _stream(w)))
+        _check(name, getattr(_lib, name)(_ptr(w), _ptr(out), _ptr(scale), b, n, k, _stream(w)))
     return out, scale
 
 
-def quantize_weights_blockwise_multi(ws, outs=None):
+def quantize_weight_blockwise_frag(w, out=None, scale=None):
+    """quantize_weight_blockwise with the codes in MFMA fragment order (N % 16 == 0, K % 128 == 0)."""
+    return quantize_weight_blockwise(w, out, scale, frag=True)
+
+
+def quantize_weights_blockwise_multi(ws, outs=None, frag=False):
     """Several BF16 matrices [N, K] (any shapes) in one launch -> list of (codes, scales),
-    each exactly what quantize_weight_blockwise gives it.  ``outs``: optional list
-    of (codes, scales) to fill."""
+    each exactly what quantize_weight_blockwise gives it (``frag``: what
+    quantize_weight_blockwise_frag gives it).  ``outs``: optional list of (codes, scales) to fill."""
     ws = list(ws)
     if len(ws) > MAX_WEIGHT_DESCS:
         raise ValueError(f"at most {MAX_WEIGHT_DESCS} matrices per call")
@@ -252,10 +267,15 @@ def quantize_weights_blockwise_multi(ws, outs=None):
         _require(s, f"scale[{i}]", torch.float32, (_cdiv(n, BLOCK), _cdiv(k, BLOCK)), dev)
         descs[i] = _WeightDesc(_ptr(_u16(w)).value, _ptr(q).value, _ptr(s).value, n, k)
         res.append((q, s))
+    name = "quantize_weights_blockwise_frag_multi" if frag else "quantize_weights_blockwise_multi"
     with torch.cuda.device(dev):
-        _check("quantize_weights_blockwise_multi",
-               _lib.quantize_weights_blockwise_multi(descs, len(ws), _stream(ws[0])))
+        _check(name, getattr(_lib, name)(descs, len(ws), _stream(ws[0])))
     return res
+
+
+def quantize_weights_blockwise_frag_multi(ws, outs=None):
+    """quantize_weights_blockwise_multi with the codes in fragment order."""
+    return quantize_weights_blockwise_multi(ws, outs, frag=True)
 
 
 def quantize_act_per_token_group(x, out=None, scale=None):
@@ -335,9 +355,10 @@ def quantize_act_per_token_group_frag(x, out=None, scale=None):
     return out, scale
 
 
-def gemm_w8a8_blockscaled_afrag(a_frag, a_scale, w, w_scale, out=None):
+def gemm_w8a8_blockscaled_afrag(a_frag, a_scale, w, w_scale, out=None, wfrag=False):
     """gemm_w8a8_blockscaled with the activation codes in fragment order (quantize_act_per_token_group_frag);
-    M % 16 == 0 and K % 256 == 0."""
+    M % 16 == 0 and K % 256 == 0.  ``wfrag``: the weight codes in fragment order too
+    (gemm_w8a8_blockscaled_frag; N % 16 == 0)."""
     m, k = a_frag.shape
     n = w.shape[0]
     _require(a_frag, "a_frag", _U8, (m, k))
@@ -348,11 +369,17 @@ def gemm_w8a8_blockscaled_afrag(a_frag, a_scale, w, w_scale, out=None):
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     _require(out, "out", _BF16, (m, n), dev)
+    name = "gemm_w8a8_blockscaled_frag" if wfrag else "gemm_w8a8_blockscaled_afrag"
     with torch.cuda.device(dev):
-        _check("gemm_w8a8_blockscaled_afrag",
-               _lib.gemm_w8a8_blockscaled_afrag(_ptr(a_frag), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)),
-                                                m, n, k, _stream(a_frag)))
+        _check(name, getattr(_lib, name)(_ptr(a_frag), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(_u16(out)),
+                                         m, n, k, _stream(a_frag)))
     return out
+
+
+def gemm_w8a8_blockscaled_frag(a_frag, a_scale, w_frag, w_scale, out=None):
+    """The GEMM with both operands' codes in fragment order (quantize_act_per_token_group_frag,
+    quantize_weight_blockwise_frag); M % 16 == 0, N % 16 == 0, K % 256 == 0."""
+    return gemm_w8a8_blockscaled_afrag(a_frag, a_scale, w_frag, w_scale, out, wfrag=True)
 
 
 def gemm_w8a8_blockscaled(a, a_scale, w, w_scale, out=None, tile=None):

@@ -124,10 +124,17 @@ const char* fp8bq_status_string(fp8bq_status s) {
   }
 }
 
-fp8bq_status quantize_weight_blockwise(const uint16_t* w_bf16, uint8_t* w_fp8, float* w_scale, int64_t batch,
-                                       int64_t N, int64_t K, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The weight quantizers: row-major codes, or (frag) MFMA fragment order,
+// which needs N % 16 == 0 and K % 128 == 0.
+fp8bq_status quantize_weight(const uint16_t* w_bf16, uint8_t* w_fp8, float* w_scale, int64_t batch, int64_t N,
+                             int64_t K, bool frag, void* stream) {
   try {
     if (batch < 0 || N < 0 || K < 0) return FP8BQ_ERR_BAD_SHAPE;
+    if (frag && ((N % 16) != 0 || (K % 128) != 0)) return FP8BQ_ERR_BAD_SHAPE;
     int64_t nk, total, bytes;
     if (!mul_ok(N, K, &nk) || !mul_ok(nk, batch, &total) || !mul_ok(total, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
     if (total == 0) return FP8BQ_OK;
@@ -136,14 +143,14 @@ fp8bq_status quantize_weight_blockwise(const uint16_t* w_bf16, uint8_t* w_fp8, f
     fp8bq_status st = check_device();
     if (st != FP8BQ_OK) return st;
     clear_last_error();
-    return launched(fp8bq::launch_quant_weight(w_bf16, w_fp8, w_scale, batch, N, K,
+    return launched(fp8bq::launch_quant_weight(w_bf16, w_fp8, w_scale, batch, N, K, frag,
                                                static_cast<hipStream_t>(stream)));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }
 }
 
-fp8bq_status quantize_weights_blockwise_multi(const fp8bq_weight_desc* descs, int64_t count, void* stream) {
+fp8bq_status quantize_weights_multi(const fp8bq_weight_desc* descs, int64_t count, bool frag, void* stream) {
   try {
     if (count < 0 || count > FP8BQ_MAX_WEIGHT_DESCS) return FP8BQ_ERR_BAD_SHAPE;
     if (count == 0) return FP8BQ_OK;
@@ -154,6 +161,7 @@ fp8bq_status quantize_weights_blockwise_multi(const fp8bq_weight_desc* descs, in
     for (int64_t i = 0; i < count; ++i) {
       const fp8bq_weight_desc& d = descs[i];
       if (d.N < 0 || d.K < 0) return FP8BQ_ERR_BAD_SHAPE;
+      if (frag && ((d.N % 16) != 0 || (d.K % 128) != 0)) return FP8BQ_ERR_BAD_SHAPE;
       int64_t nk, bytes;
       if (!mul_ok(d.N, d.K, &nk) || !mul_ok(nk, 2, &bytes)) return FP8BQ_ERR_BAD_SHAPE;
       if (nk == 0) continue;
@@ -179,10 +187,32 @@ fp8bq_status quantize_weights_blockwise_multi(const fp8bq_weight_desc* descs, in
     fp8bq_status st = check_device();
     if (st != FP8BQ_OK) return st;
     clear_last_error();
-    return launched(fp8bq::launch_quant_weight_multi(batch, blocks, static_cast<hipStream_t>(stream)));
+    return launched(fp8bq::launch_quant_weight_multi(batch, blocks, frag, static_cast<hipStream_t>(stream)));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8bq_status quantize_weight_blockwise(const uint16_t* w_bf16, uint8_t* w_fp8, float* w_scale, int64_t batch,
+                                       int64_t N, int64_t K, void* stream) {
+  return quantize_weight(w_bf16, w_fp8, w_scale, batch, N, K, false, stream);
+}
+
+fp8bq_status quantize_weight_blockwise_frag(const uint16_t* w_bf16, uint8_t* w_fp8_frag, float* w_scale,
+                                            int64_t batch, int64_t N, int64_t K, void* stream) {
+  return quantize_weight(w_bf16, w_fp8_frag, w_scale, batch, N, K, true, stream);
+}
+
+fp8bq_status quantize_weights_blockwise_multi(const fp8bq_weight_desc* descs, int64_t count, void* stream) {
+  return quantize_weights_multi(descs, count, false, stream);
+}
+
+fp8bq_status quantize_weights_blockwise_frag_multi(const fp8bq_weight_desc* descs, int64_t count, void* stream) {
+  return quantize_weights_multi(descs, count, true, stream);
 }
 
 fp8bq_status quantize_act_per_token_group(const uint16_t* x_bf16, uint8_t* x_fp8, float* x_scale, int64_t M,
@@ -386,11 +416,17 @@ fp8bq_status quantize_act_per_token_group_frag(const uint16_t* x_bf16, uint8_t* 
   }
 }
 
-fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8,
-                                         const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
-                                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The GEMMs on fragment-order activations: weights row-major, or (wfrag)
+// in fragment order too (N % 16 == 0).
+fp8bq_status gemm_frag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8, const float* w_scale,
+                       uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, bool wfrag, void* stream) {
   try {
     if (M < 0 || N < 0 || K < 0 || (M % 16) != 0 || (K % 256) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
+    if (wfrag && (N % 16) != 0) return FP8BQ_ERR_BAD_SHAPE;
     int64_t mk, nk, mn, bytes;
     if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, &mn) || !mul_ok(mn, 2, &bytes))
       return FP8BQ_ERR_BAD_SHAPE;
@@ -403,11 +439,27 @@ fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float*
     fp8bq_status st = check_device();
     if (st != FP8BQ_OK) return st;
     clear_last_error();
-    return launched(fp8bq::launch_gemm_afrag(a_fp8_frag, a_scale, w_fp8, w_scale, y_bf16, M, N, K,
+    return launched(fp8bq::launch_gemm_afrag(a_fp8_frag, a_scale, w_fp8, w_scale, y_bf16, M, N, K, wfrag,
                                              static_cast<hipStream_t>(stream)));
   } catch (...) {
     return FP8BQ_ERR_LAUNCH;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8,
+                                         const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                         void* stream) {
+  return gemm_frag(a_fp8_frag, a_scale, w_fp8, w_scale, y_bf16, M, N, K, false, stream);
+}
+
+fp8bq_status gemm_w8a8_blockscaled_frag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8_frag,
+                                        const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                        void* stream) {
+  return gemm_frag(a_fp8_frag, a_scale, w_fp8_frag, w_scale, y_bf16, M, N, K, true, stream);
 }
 
 }  // extern "C"

@@ -224,13 +224,17 @@ __device__ __forceinline__ void store4_f32(float* __restrict__ p, int64_t N, int
 // kAfrag: the activations are in MFMA fragment order (launch_quant_act_frag)
 // and each wave loads its activation fragments straight into registers
 // with the K-block's weight rows; only the weight rows go through the
-// slice.
+// slice.  kWfrag (with kAfrag): the weights are in fragment order too and
+// their fragments are loaded straight into registers as well, so the K
+// loop uses no LDS at all.
 // ---------------------------------------------------------------------------
-template <int BN, int BM, int NW, bool kAfrag = false>
+template <int BN, int BM, int NW, bool kAfrag = false, bool kWfrag = false>
 struct Skinny {
+  static_assert(kAfrag || !kWfrag, "fragment-order weights come with fragment-order activations");
   static constexpr int TN = BN / 16, TM = BM / 16;
-  static constexpr int kRows = kAfrag ? BN : BN + BM;   // rows staged per K-block
-  static constexpr int kLoads = BN / 8 + (kAfrag ? 2 * TM : BM / 8);  // 16-byte loads per lane per K-block
+  static constexpr int kRows = kAfrag ? (kWfrag ? 0 : BN) : BN + BM;  // rows staged per K-block
+  static constexpr int kWL = kWfrag ? 2 * TN : BN / 8;  // 16-byte weight loads per lane per K-block
+  static constexpr int kLoads = kWL + (kAfrag ? 2 * TM : BM / 8);  // 16-byte loads per lane per K-block
   static constexpr int kStaged = kRows / 8;             // of which staged through the slice
   static constexpr int kSlice = kRows * kBlock;         // LDS bytes per wave
   static constexpr int kRed = NW * BN * BM * 4;         // the waves' partial tiles, FP32
@@ -295,14 +299,22 @@ struct Skinny {
 
     auto load_stage = [&](Stage& s, int kb) {
       const int koff = kb * kBlock;
+      if constexpr (kWfrag) {
+        // weight fragment i, half h: 1 KB at (16 i) K + 2048 kb + 1024 h
 #pragma unroll
-      for (int q = 0; q < BN / 8; ++q) s.v[q] = bload16(wr, gvoff + 8 * q * (int)K, koff);
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) s.v[2 * i + h] = bload16(wr, 16 * i * (int)K + h * 1024 + lane * 16, kb * 2048);
+      } else {
+#pragma unroll
+        for (int q = 0; q < BN / 8; ++q) s.v[q] = bload16(wr, gvoff + 8 * q * (int)K, koff);
+      }
       if constexpr (kAfrag) {
         // fragment j, half h of K-block kb: 1 KB at (16 j) K + 2048 kb + 1024 h
 #pragma unroll
         for (int j = 0; j < TM; ++j)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) s.v[BN / 8 + 2 * j + h] = bload16(ar, 16 * j * (int)K + h * 1024 + lane * 16, kb * 2048);
+          for (int h = 0; h < 2; ++h) s.v[kWL + 2 * j + h] = bload16(ar, 16 * j * (int)K + h * 1024 + lane * 16, kb * 2048);
       } else {
 #pragma unroll
         for (int q = 0; q < BM / 8; ++q) s.v[BN / 8 + q] = bload16(ar, gvoff + 8 * q * (int)K, koff);
@@ -333,11 +345,12 @@ struct Skinny {
       v8i fa[TM];
 #pragma unroll
       for (int j = 0; j < TM; ++j)
-        fa[j] = kAfrag ? to_v8i(s.v[BN / 8 + 2 * j], s.v[BN / 8 + 2 * j + 1]) : fl(slice, BN + j * 16);
+        fa[j] = kAfrag ? to_v8i(s.v[kWL + 2 * j], s.v[kWL + 2 * j + 1]) : fl(slice, BN + j * 16);
+      auto wfrag = [&](int i) { return kWfrag ? to_v8i(s.v[2 * i], s.v[2 * i + 1]) : fl(slice, i * 16); };
       v8i fw[2];
-      fw[0] = fl(slice, 0);
+      fw[0] = wfrag(0);
       tile_product<TN, TM, 4, 1>(
-          acc, fa, fw, [&](int i) { return fl(slice, i * 16); },
+          acc, fa, fw, wfrag,
           [&](int i, int j) { return sa[j] * (((b_mask >> i) & 1u) ? s.swb : s.swa); });
     };
 
@@ -1466,22 +1479,35 @@ hipError_t launch_gemm_splitk_noalloc(const uint8_t* a, const float* sa, const u
 // M = 8192 on quantized normal data: 1.77 -> 1.95 PF (the four-wave
 // 128 x 256 panel that loads activation fragments into registers, two per
 // CU: 1.90 PF).
-hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
-                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
-  if (M % 16 != 0 || K % (2 * kBlock) != 0) return hipErrorInvalidValue;
-  switch (choose(M, N, K)) {
+//
+// Weights in fragment order as well (wfrag): the same tiles with the weight
+// fragments loaded straight into registers (K-split tiles) or copied 1 KB at
+// a time into the LDS ring (panels); bit-identical again.  Prefill shapes on
+// quantized normal data: 1.95 -> 2.01 PF.
+template <bool kW>
+hipError_t launch_gemm_frag_cfg(Cfg cfg, const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                                uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  switch (cfg) {
     case Cfg::kSkinny64x64:
-      return launch_dense_cfg<Skinny<64, 64, 4, true>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
+      return launch_dense_cfg<Skinny<64, 64, 4, true, kW>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kSkinny48x64:
-      return launch_dense_cfg<Skinny<48, 64, 4, true>, 48, 64>(a, sa, w, sw, y, M, N, K, stream);
+      return launch_dense_cfg<Skinny<48, 64, 4, true, kW>, 48, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kPanel192:
-      return launch_dense_cfg<PanelFragA<Panel192>, 192, 128>(a, sa, w, sw, y, M, N, K, stream);
+      return launch_dense_cfg<PanelFragA<Panel<192, 128, 2, 4, 3, kW>>, 192, 128>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kDecodePanel:
-      return launch_dense_cfg<PanelFragA<DecodePanel>, 128, 256>(a, sa, w, sw, y, M, N, K, stream);
+      return launch_dense_cfg<PanelFragA<Panel<128, 256, 2, 4, 3, kW>>, 128, 256>(a, sa, w, sw, y, M, N, K, stream);
     default:
-      return launch_dense_cfg<PanelFragA<Wide>, 256, 256>(a, sa, w, sw, y, M, N, K, stream);
+      return launch_dense_cfg<PanelFragA<Panel<256, 256, 2, 4, 2, kW>>, 256, 256>(a, sa, w, sw, y, M, N, K, stream);
   }
+}
+
+hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
+                             int64_t M, int64_t N, int64_t K, bool wfrag, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (M % 16 != 0 || K % (2 * kBlock) != 0 || (wfrag && N % 16 != 0)) return hipErrorInvalidValue;
+  const Cfg cfg = choose(M, N, K);
+  return wfrag ? launch_gemm_frag_cfg<true>(cfg, a, sa, w, sw, y, M, N, K, stream)
+               : launch_gemm_frag_cfg<false>(cfg, a, sa, w, sw, y, M, N, K, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,

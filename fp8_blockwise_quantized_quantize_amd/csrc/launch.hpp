@@ -27,10 +27,11 @@ struct WeightBatch {
   int count;
 };
 
+// frag: codes in MFMA fragment order (N % 16 == 0, K % 128 == 0)
 hipError_t launch_quant_weight(const uint16_t* w, uint8_t* q, float* scale, int64_t batch, int64_t N, int64_t K,
-                               hipStream_t stream);
+                               bool frag, hipStream_t stream);
 
-hipError_t launch_quant_weight_multi(const WeightBatch& batch, int64_t blocks, hipStream_t stream);
+hipError_t launch_quant_weight_multi(const WeightBatch& batch, int64_t blocks, bool frag, hipStream_t stream);
 
 hipError_t launch_quant_act(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K, hipStream_t stream);
 
@@ -58,9 +59,10 @@ hipError_t launch_quant_act_frag_multi(const ActBatch& batch, int64_t blocks, hi
 // the same codes in the MFMA fragment order of the activation operand (M % 16 == 0, K % 128 == 0)
 hipError_t launch_quant_act_frag(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K,
                                  hipStream_t stream);
-// the GEMM on fragment-order activations (M % 16 == 0, K % 256 == 0)
+// the GEMM on fragment-order activations (M % 16 == 0, K % 256 == 0); wfrag:
+// fragment-order weights too (N % 16 == 0)
 hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
-                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                             int64_t M, int64_t N, int64_t K, bool wfrag, hipStream_t stream);
 
 // `tile`: FP8BQ_TILE_* of the C ABI (0 = the cost model's choice); an
 // unknown value returns hipErrorInvalidValue.

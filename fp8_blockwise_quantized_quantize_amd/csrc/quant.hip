@@ -23,8 +23,18 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kQwThreads = 256;
 
+// Byte offset of code (n, k) of an [N][K] matrix in MFMA fragment order
+// (N % 16 == 0, K % 128 == 0): per 16-row group and K-block one 2 KB unit,
+// in it half (k % 128) / 64, piece ((k % 64) / 16) 16 + n % 16, byte k % 16.
+__device__ __forceinline__ int64_t frag_offset(int64_t n, int64_t k, int64_t KB) {
+  return ((((n >> 4) * KB + (k >> 7)) * 2 + ((k >> 6) & 1)) << 10) + ((((k >> 4) & 3) << 4) + (n & 15)) * 16 +
+         (k & 15);
+}
+
 // Block (bn, bk) of one [N][K] matrix; its scale goes to *sslot.  `red`:
-// kQwThreads / 64 words of LDS.
+// qw_lds_words<kFrag>() words of LDS.  kFrag: codes in MFMA fragment order
+// (N % 16 == 0, K % 128 == 0, checked by the host).
+template <bool kFrag>
 __device__ __forceinline__ void quant_weight_block(const uint16_t* __restrict__ wm, uint8_t* __restrict__ qm,
                                                    float* __restrict__ sslot, int64_t N, int64_t K, int bn, int bk,
                                                    uint32_t* red) {
@@ -53,6 +63,28 @@ __device__ __forceinline__ void quant_weight_block(const uint16_t* __restrict__ 
     // One store loop for the three cases (the choice is uniform per block):
     // 2% faster on the 36-layer sweep than a store loop per case.
     const Divisor d(s != 0.0f ? s : 1.0f);
+    if constexpr (kFrag) {
+      // The block's 8 fragment units (2 KB each: rows 16 i .., 16 K bytes
+      // apart in memory) go through LDS, so that each wave then stores 1 KB
+      // contiguous pieces: code row rr + 16 i, bytes cc 8 .. sit in unit i,
+      // half cc / 8, piece ((cc % 8) / 2) 16 + rr, bytes (cc % 2) 8 ..
+      uint8_t* stage = reinterpret_cast<uint8_t*>(red + kQwThreads / 64);
+      const int loff = (cc >> 3) * 1024 + (((cc & 7) >> 1) * 16 + rr) * 16 + (cc & 1) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u32x2 o = s == 0.0f ? zero8(v[i]) : (d.fast ? quant8<true>(v[i], d) : quant8<false>(v[i], d));
+        *reinterpret_cast<u32x2*>(stage + i * 2048 + loff) = o;
+      }
+      __syncthreads();
+      uint8_t* unit0 = qm + frag_offset(row0, col0, K / kBlock);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = j * 4096 + tid * 16;  // unit b / 2048, byte b % 2048 of it
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + b),
+                                    reinterpret_cast<u32x4*>(unit0 + (int64_t)(b >> 11) * 16 * K + (b & 2047)));
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const u32x2 o = s == 0.0f ? zero8(v[i]) : (d.fast ? quant8<true>(v[i], d) : quant8<false>(v[i], d));
@@ -83,30 +115,39 @@ __device__ __forceinline__ void quant_weight_block(const uint16_t* __restrict__ 
     const int r = e >> 7, c = e & 127;
     if (r < rows && c < cols) {
       const int64_t off = (row0 + r) * K + col0 + c;
-      qm[off] = encode1(wm[off], s);
+      qm[kFrag ? frag_offset(row0 + r, col0 + c, K / kBlock) : off] = encode1(wm[off], s);
     }
   }
 }
 
 
+// LDS words of a weight workgroup: the amax reduction, then (fragment
+// order) the 16 KB block of codes
+template <bool kFrag>
+constexpr int qw_lds_words() {
+  return kQwThreads / 64 + (kFrag ? kBlock * kBlock / 4 : 0);
+}
+
+template <bool kFrag>
 __global__ __launch_bounds__(kQwThreads) void quant_weight_kernel(const uint16_t* __restrict__ w,
                                                                   uint8_t* __restrict__ q,
                                                                   float* __restrict__ scale, int64_t N,
                                                                   int64_t K, int nb, int kb) {
-  __shared__ uint32_t red[kQwThreads / 64];
+  __shared__ __align__(16) uint32_t red[qw_lds_words<kFrag>()];
   const int64_t blk = blockIdx.x;  // == index into scale[batch][nb][kb]
   const int bk = (int)(blk % kb);
   const int64_t rest = blk / kb;
   const int bn = (int)(rest % nb);
   const int64_t b = rest / nb;
-  quant_weight_block(w + b * N * K, q + b * N * K, scale + blk, N, K, bn, bk, red);
+  quant_weight_block<kFrag>(w + b * N * K, q + b * N * K, scale + blk, N, K, bn, bk, red);
 }
 
 // Several matrices in one launch: workgroup g takes block g - first[t] of
 // the matrix t with first[t] <= g < first[t + 1] (descriptors in the kernel
 // arguments, largest matrices first).
+template <bool kFrag>
 __global__ __launch_bounds__(kQwThreads) void quant_weight_multi_kernel(const WeightBatch batch) {
-  __shared__ uint32_t red[kQwThreads / 64];
+  __shared__ __align__(16) uint32_t red[qw_lds_words<kFrag>()];
   const int64_t g = blockIdx.x;
   int t = 0;
   while (t + 1 < batch.count && g >= batch.first[t + 1]) ++t;  // uniform scan over <= 64 entries
@@ -114,7 +155,7 @@ __global__ __launch_bounds__(kQwThreads) void quant_weight_multi_kernel(const We
   const int kb = (int)((d.K + kBlock - 1) / kBlock);
   const int64_t local = g - batch.first[t];
   const int bk = (int)(local % kb), bn = (int)(local / kb);
-  quant_weight_block(d.w, d.q, d.s + local, d.N, d.K, bn, bk, red);
+  quant_weight_block<kFrag>(d.w, d.q, d.s + local, d.N, d.K, bn, bk, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -324,20 +365,28 @@ __global__ __launch_bounds__(kQaThreads) void quant_act_frag_multi_kernel(const 
 }  // namespace
 
 hipError_t launch_quant_weight(const uint16_t* w, uint8_t* q, float* scale, int64_t batch, int64_t N, int64_t K,
-                               hipStream_t stream) {
+                               bool frag, hipStream_t stream) {
   const int64_t nb = (N + kBlock - 1) / kBlock, kb = (K + kBlock - 1) / kBlock;
   const int64_t blocks = batch * nb * kb;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)blocks), dim3(kQwThreads), 0, stream, w, q, scale, N, K,
-                     (int)nb, (int)kb);
+  if (frag && ((N % 16) != 0 || (K % kBlock) != 0)) return hipErrorInvalidValue;
+  if (frag)
+    hipLaunchKernelGGL(quant_weight_kernel<true>, dim3((unsigned)blocks), dim3(kQwThreads), 0, stream, w, q, scale, N,
+                       K, (int)nb, (int)kb);
+  else
+    hipLaunchKernelGGL(quant_weight_kernel<false>, dim3((unsigned)blocks), dim3(kQwThreads), 0, stream, w, q, scale,
+                       N, K, (int)nb, (int)kb);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_weight_multi(const WeightBatch& batch, int64_t blocks, hipStream_t stream) {
+hipError_t launch_quant_weight_multi(const WeightBatch& batch, int64_t blocks, bool frag, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_weight_multi_kernel, dim3((unsigned)blocks), dim3(kQwThreads), 0, stream, batch);
+  if (frag)
+    hipLaunchKernelGGL(quant_weight_multi_kernel<true>, dim3((unsigned)blocks), dim3(kQwThreads), 0, stream, batch);
+  else
+    hipLaunchKernelGGL(quant_weight_multi_kernel<false>, dim3((unsigned)blocks), dim3(kQwThreads), 0, stream, batch);
   return hipGetLastError();
 }
 

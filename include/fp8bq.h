@@ -113,6 +113,30 @@ typedef struct {
 fp8bq_status quantize_weights_blockwise_multi(const fp8bq_weight_desc* descs, int64_t count, void* stream);
 
 /*
+ * quantize_weight_blockwise_frag / quantize_weights_blockwise_frag_multi --
+ * the same re-quantization ([FP8-RL summary] §3.4.1 formula for W^, §3.4.2
+ * Phase 2 step 2), with the codes written in the MFMA fragment order that
+ * gemm_w8a8_blockscaled_frag reads (the pages fix the values and scales,
+ * not the byte layout of the quantized weights; a weight that is
+ * re-quantized every step can be stored the way the GEMM reads it).
+ *   Fragment order of an [N][K] code matrix (N % 16 == 0, K % 128 == 0):
+ *   code (n, k) at byte
+ *     ((n/16 * (K/128) + k/128) * 2 + (k%128)/64) * 1024
+ *       + (((k%64)/16) * 16 + n%16) * 16 + k%16,
+ *   i.e. one 2 KB unit per 16 rows and 128-wide K-block, in it lane
+ *   l = 16 c + r of the 16x16x128 FP8 MFMA finds its operand bytes at l*16
+ *   (k = 16 c ..) and 1024 + l*16 (k = 64 + 16 c ..).  Same layout as the
+ *   activations of quantize_act_per_token_group_frag.
+ *   Arguments, scales and errors as for quantize_weight_blockwise /
+ *   quantize_weights_blockwise_multi, plus FP8BQ_ERR_BAD_SHAPE unless every
+ *   matrix has N % 16 == 0 and K % 128 == 0.  Each matrix gets exactly the
+ *   row-major codes permuted into that order, and the same scales.
+ */
+fp8bq_status quantize_weight_blockwise_frag(const uint16_t* w_bf16, uint8_t* w_fp8_frag, float* w_scale,
+                                            int64_t batch, int64_t N, int64_t K, void* stream);
+fp8bq_status quantize_weights_blockwise_frag_multi(const fp8bq_weight_desc* descs, int64_t count, void* stream);
+
+/*
  * quantize_act_per_token_group -- dynamic per-token 1x128 quantization of
  * BF16 activations ([FP8-RL summary] §3.4.1, "1 x 128 tiles for
  * activations", and §3.4.2 Phase 3, scales computed on the fly).
@@ -310,6 +334,18 @@ fp8bq_status quantize_act_per_token_group_frag(const uint16_t* x_bf16, uint8_t* 
 fp8bq_status gemm_w8a8_blockscaled_afrag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8,
                                          const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
                                          void* stream);
+
+/*
+ * gemm_w8a8_blockscaled_frag -- gemm_w8a8_blockscaled_afrag with the weight
+ * codes in fragment order as well (quantize_weight_blockwise_frag), the
+ * library's fastest form: every operand load is a contiguous 1 KB piece of
+ * a fragment unit.  Same result, bit for bit, as gemm_w8a8_blockscaled on
+ * the row-major codes; same arguments and errors as
+ * gemm_w8a8_blockscaled_afrag, plus FP8BQ_ERR_BAD_SHAPE unless N % 16 == 0.
+ */
+fp8bq_status gemm_w8a8_blockscaled_frag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8_frag,
+                                        const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
+                                        void* stream);
 
 /*
  * grouped_gemm_w8a8_blockscaled -- the MoE expert form: rows

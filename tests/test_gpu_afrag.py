@@ -76,13 +76,14 @@ def test_quantizer_frag_multi_shape_errors(fb, m, k):
         fb.quantize_acts_per_token_group_frag_multi([ok, bad])
 
 
-@pytest.mark.parametrize("m,n,k", [(16, 130, 256), (48, 384, 768), (272, 520, 512), (256, 256, 2048),
-                                   (80, 20480, 256), (208, 24576, 256)])
+@pytest.mark.parametrize("m,n,k", [(16, 130, 256), (48, 384, 768), (272, 520, 512), (272, 528, 512),
+                                   (256, 256, 2048), (80, 20480, 256), (208, 24576, 256)])
 def test_gemm_afrag_against_oracle_and_row_major(fb, m, n, k):
-    """Every tile form: 64- and 48-row K-split tiles, the 256 x 256 choice
-    (four-wave 128 x 256 tiles), the 128 x 256 decode panel (M = 80: one
-    ragged tile of activation rows) and the 192 x 128 panel (M = 208: a
-    second, ragged row tile)."""
+    """Every tile form: 64- and 48-row K-split tiles, the 256 x 256 panel,
+    the 128 x 256 decode panel (M = 80: one ragged tile of activation rows)
+    and the 192 x 128 panel (M = 208: a second, ragged row tile).  Where
+    N % 16 == 0 the same product with the weights in fragment order too
+    (N = 528: a ragged last weight scale block of 16 rows)."""
     announce("afrag gemm", m, n, k)
     x, _ = activations(m, k, (m, n, k, 0))
     w = bf16_normal((n, k), 0.02, (m, n, k, 1))
@@ -94,6 +95,10 @@ def test_gemm_afrag_against_oracle_and_row_major(fb, m, n, k):
     assert_gemm_close(got, oracle.gemm_ref(qa, sa, qw, sw))
     ref = device_to_bits(fb.gemm_w8a8_blockscaled(dev(qa), dev(sa), dev(qw), dev(sw)))
     assert np.array_equal(got, ref)
+    if n % 16 == 0:
+        yf = fb.gemm_w8a8_blockscaled_frag(dev(oracle.act_fragment_order(qa)), dev(sa),
+                                           dev(oracle.act_fragment_order(qw)), dev(sw))
+        assert np.array_equal(device_to_bits(yf), ref)
 
 
 @pytest.mark.parametrize("m", [256, 208, 144, 128, 64, 48, 16])
@@ -104,12 +109,16 @@ def test_gemm_afrag_decode_shapes_bit_identical(fb, m):
     for _, n, k in LAYER_SHAPES_QWEN3_8B:
         announce("afrag gemm decode", m, n, k)
         x = device_bf16_normal((m, k), 1.0, seed=13)
-        wq, ws = fb.quantize_weight_blockwise(device_bf16_normal((n, k), 0.02, seed=14))
+        wb = device_bf16_normal((n, k), 0.02, seed=14)
+        wq, ws = fb.quantize_weight_blockwise(wb)
+        wqf, _ = fb.quantize_weight_blockwise_frag(wb)
         q, s = fb.quantize_act_per_token_group(x)
         qf, _ = fb.quantize_act_per_token_group_frag(x)
         y0 = fb.gemm_w8a8_blockscaled(q, s, wq, ws)
         y1 = fb.gemm_w8a8_blockscaled_afrag(qf, s, wq, ws)
+        y2 = fb.gemm_w8a8_blockscaled_frag(qf, s, wqf, ws)
         assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)), (m, n, k)
+        assert torch.equal(y0.view(torch.int16), y2.view(torch.int16)), (m, n, k)
 
 
 @pytest.mark.parametrize("n,k", [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)])
@@ -118,17 +127,22 @@ def test_gemm_afrag_prefill_bit_identical(fb, n, k):
     m = 8192
     announce("afrag gemm prefill", m, n, k)
     x = device_bf16_normal((m, k), 1.0, seed=11)
-    wq, ws = fb.quantize_weight_blockwise(device_bf16_normal((n, k), 0.02, seed=12))
+    wb = device_bf16_normal((n, k), 0.02, seed=12)
+    wq, ws = fb.quantize_weight_blockwise(wb)
+    wqf, _ = fb.quantize_weight_blockwise_frag(wb)
     q, s = fb.quantize_act_per_token_group(x)
     qf, _ = fb.quantize_act_per_token_group_frag(x)
     y0 = fb.gemm_w8a8_blockscaled(q, s, wq, ws, tile="wide")
     y1 = fb.gemm_w8a8_blockscaled_afrag(qf, s, wq, ws)
+    y2 = fb.gemm_w8a8_blockscaled_frag(qf, s, wqf, ws)
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
 
 
 def test_gemm_afrag_largest_k(fb):
-    """K = 2^22: 256 rows of fragment-order codes span 2^30 bytes."""
-    m, n, k = 256, 3, 1 << 22
+    """K = 2^22: 256 rows of fragment-order codes span 2^30 bytes (with the
+    16 weight rows in fragment order too)."""
+    m, n, k = 256, 16, 1 << 22
     announce("afrag gemm largest K", m, n, k)
     g = torch.Generator(device="cuda").manual_seed(2202)
     qa = torch.randint(0, 256, (m, k), generator=g, dtype=torch.uint8, device="cuda")
@@ -142,6 +156,54 @@ def test_gemm_afrag_largest_k(fb):
     del qa
     y1 = fb.gemm_w8a8_blockscaled_afrag(qf, sa, qw, sw)
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    qwf = qw.view(n // 16, 16, k // 128, 2, 4, 16).permute(0, 2, 3, 4, 1, 5).contiguous().view(n, k)
+    y2 = fb.gemm_w8a8_blockscaled_frag(qf, sa, qwf, sw)
+    assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (384, 512), (16, 256), (144, 384), (2, 144, 256)])
+def test_weight_quantizer_fragment_order(fb, shape):
+    """The oracle's codes permuted into fragment order and the oracle's
+    scales; (144, 384): a last block of 16 rows (element-wise path);
+    (2, 144, 256): the batched form."""
+    announce("frag weight quant", shape)
+    bits = bf16_normal(shape, 0.02, (len(shape),) + shape)
+    q, s = fb.quantize_weight_blockwise_frag(bf16_bits_to_device(bits))
+    mats = bits if len(shape) == 3 else bits[None]
+    for b in range(mats.shape[0]):
+        oq, os_ = oracle.quant_weight_blockwise(mats[b])
+        gq = q.cpu().numpy() if len(shape) == 2 else q[b].cpu().numpy()
+        gs = s.cpu().numpy() if len(shape) == 2 else s[b].cpu().numpy()
+        assert np.array_equal(gq, oracle.act_fragment_order(oq)), (shape, b)
+        assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), (shape, b)
+
+
+def test_weight_quantizer_fragment_order_multi(fb):
+    """One launch over the Qwen3-8B layer matrices and small ones: each the
+    row-major GPU codes (checked against the oracle elsewhere) permuted."""
+    shapes = [(n, k) for _, n, k in LAYER_SHAPES_QWEN3_8B] + [(144, 384), (16, 128), (0, 256)]
+    announce("frag weight quant multi", shapes)
+    ws = [device_bf16_normal(sh, 0.02, seed=30 + i) if sh[0] else torch.empty(sh, dtype=torch.bfloat16, device="cuda")
+          for i, sh in enumerate(shapes)]
+    rows = fb.quantize_weights_blockwise_multi(ws)
+    frags = fb.quantize_weights_blockwise_frag_multi(ws)
+    for (q, s), (qf, sf), (n, k) in zip(rows, frags, shapes):
+        if n == 0:
+            continue
+        perm = q.view(n // 16, 16, k // 128, 2, 4, 16).permute(0, 2, 3, 4, 1, 5).contiguous().view(n, k)
+        assert torch.equal(qf, perm) and torch.equal(sf, s), (n, k)
+
+
+def test_frag_shape_errors(fb):
+    w = torch.zeros((24, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fb.FP8BQError, match="shape"):
+        fb.quantize_weight_blockwise_frag(w)
+    with pytest.raises(fb.FP8BQError, match="shape"):
+        fb.quantize_weights_blockwise_frag_multi([torch.zeros((16, 200), dtype=torch.bfloat16, device="cuda")])
+    a = torch.zeros((16, 256), dtype=torch.uint8, device="cuda")
+    with pytest.raises(fb.FP8BQError, match="shape"):
+        fb.gemm_w8a8_blockscaled_frag(a, torch.ones((16, 2), device="cuda"), torch.zeros((24, 256), dtype=torch.uint8,
+                                      device="cuda"), torch.ones((1, 2), device="cuda"))
 
 
 def test_afrag_shape_errors(fb):
