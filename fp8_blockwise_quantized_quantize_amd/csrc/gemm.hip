@@ -445,10 +445,8 @@ struct Skinny {
 // compute k while issuing the loads of K-block k + S - 1 into that stage
 // between the MFMAs.
 // ---------------------------------------------------------------------------
-// kWfrag: the weight codes are in MFMA fragment order; kLoadEvery: issue
-// the next K-block's loads after every kLoadEvery-th MFMA (0: every second
-// MFMA when there are enough MFMAs, else every one).
-template <int BN_, int BM_, int WGN, int WGM, int S, bool kWfrag = false, int kLoadEvery = 0>
+// kWfrag: the weight codes are in MFMA fragment order.
+template <int BN_, int BM_, int WGN, int WGM, int S, bool kWfrag = false>
 struct Panel {
   static constexpr int BN = BN_, BM = BM_;
   static_assert(WGN * WGM == 8, "eight waves");
@@ -623,7 +621,7 @@ struct Panel {
     // while the first MFMAs run.
     constexpr int kT = TN * TM;
     constexpr int kPhaseLoads = kLoads + 1;
-    constexpr int kEvery = kLoadEvery > 0 ? kLoadEvery : (kT >= 2 * kPhaseLoads) ? 2 : 1;
+    constexpr int kEvery = (kT >= 2 * kPhaseLoads) ? 2 : 1;
     static_assert(kT >= kPhaseLoads, "enough MFMAs to carry the loads");
     auto phase = [&](int cur, int kb, int fill) {
       const uint8_t* buf = lds + cur * kStage;
@@ -843,7 +841,7 @@ struct Panel {
     };
     constexpr int kT = TN * TM;
     constexpr int kPhaseLoads = kLoads + 1;
-    constexpr int kEvery = kLoadEvery > 0 ? kLoadEvery : (kT >= 2 * kPhaseLoads) ? 2 : 1;
+    constexpr int kEvery = (kT >= 2 * kPhaseLoads) ? 2 : 1;
     static_assert(kT >= kPhaseLoads, "enough MFMAs to carry the loads");
     auto phase = [&](int cur, int kb, int fill) {
       const uint8_t* buf = lds + cur * kStage;
@@ -1495,9 +1493,8 @@ hipError_t launch_gemm_frag_cfg(Cfg cfg, const uint8_t* a, const float* sa, cons
       return launch_dense_cfg<Skinny<64, 64, 4, true, kW>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kSkinny48x64:
       return launch_dense_cfg<Skinny<48, 64, 4, true, kW>, 48, 64>(a, sa, w, sw, y, M, N, K, stream);
-    case Cfg::kPanel192:  // loads issued after every MFMA: 48.7 -> 46.7 us on the decode gate_up (M = 256)
-      return launch_dense_cfg<PanelFragA<Panel<192, 128, 2, 4, 3, kW, 1>>, 192, 128>(a, sa, w, sw, y, M, N, K,
-                                                                                      stream);
+    case Cfg::kPanel192:
+      return launch_dense_cfg<PanelFragA<Panel<192, 128, 2, 4, 3, kW>>, 192, 128>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kDecodePanel:
       return launch_dense_cfg<PanelFragA<Panel<128, 256, 2, 4, 3, kW>>, 128, 256>(a, sa, w, sw, y, M, N, K, stream);
     default:
