@@ -137,14 +137,15 @@ def quant_act_per_token_group(x_bits):
 
 
 def act_fragment_order(codes):
-    """Byte order of activation codes [M][K] (M % 16 == 0, K % 128 == 0) as
-    the 16x16x128 FP8 MFMA reads its activation operand: per 16-row group and
-    128-wide K-block one 2 KB block; in it, lane l = 16 c + r (r = row within
-    the group, c = 0..3) holds bytes 16 c .. 16 c + 15 of its row's K-block
-    at l * 16 and bytes 64 + 16 c .. 79 + 16 c at 1024 + l * 16.  A pure
-    permutation of the row-major codes (what the block-scaled GEMM computes
-    is unchanged; the pages leave the byte layout of the quantized operand
-    open).
+    """Byte order of codes [R][K] (R % 16 == 0, K % 128 == 0) as the
+    16x16x128 FP8 MFMA reads an operand: per 16-row group and 128-wide
+    K-block one 2 KB block; in it, lane l = 16 c + r (r = row within the
+    group, c = 0..3) holds bytes 16 c .. 16 c + 15 of its row's K-block at
+    l * 16 and bytes 64 + 16 c .. 79 + 16 c at 1024 + l * 16.  The same order
+    serves activations [M][K] and weights [N][K] (both operands are read in
+    this form).  A pure permutation of the row-major codes (what the
+    block-scaled GEMM computes is unchanged; the pages leave the byte layout
+    of the quantized operands open).
     """
     q = np.asarray(codes, np.uint8)
     m, k = q.shape
