@@ -1,8 +1,9 @@
 """The library's kernels under HIP graph capture: a decode-layer step
-(re-quant, activation quant, GEMMs), a ragged MoE grouped GEMM (plain and
-with gathered rows; the persistent expert-tile kernel by default), the
-fragment-order activation quantizer and GEMM, and a
-KV-cache calibration + write are
+(re-quant, activation quant, GEMMs) in row-major and in fragment order
+(one-launch quantizers, the fragment-order GEMM), a ragged MoE grouped GEMM
+(plain and with gathered rows; the persistent expert-tile kernel by
+default), the fragment-order activation quantizer with the activation-only
+fragment GEMM, and a KV-cache calibration + write are
 captured once and replayed several times, with eager work and
 synchronizations between replays; every replay's outputs must equal the
 eager outputs bit for bit (the kernels are deterministic and no memset is
@@ -64,6 +65,8 @@ def test_graph_replays_match_eager():
 
     L0 = layers[0]
     af = dict(xq=torch.empty_like(L0["xq"]), xs=torch.empty_like(L0["xs"]), y=torch.empty_like(L0["y"]))
+    fr = [dict(wq=torch.empty_like(L["wq"]), ws=torch.empty_like(L["ws"]), xq=torch.empty_like(L["xq"]),
+               xs=torch.empty_like(L["xs"]), y=torch.empty_like(L["y"])) for L in layers]
 
     def work():
         fb().grouped_gemm_w8a8_blockscaled(moe["xq"], moe["xs"], moe["wq"], moe["ws"], moe["off"], moe["y"])
@@ -75,11 +78,16 @@ def test_graph_replays_match_eager():
             fb().gemm_w8a8_blockscaled(L["xq"], L["xs"], L["wq"], L["ws"], L["y"])
         fb().quantize_act_per_token_group_frag(L0["x"], af["xq"], af["xs"])
         fb().gemm_w8a8_blockscaled_afrag(af["xq"], af["xs"], L0["wq"], L0["ws"], af["y"])
+        fb().quantize_weights_blockwise_frag_multi([L["w"] for L in layers], [(F["wq"], F["ws"]) for F in fr])
+        fb().quantize_acts_per_token_group_frag_multi([L["x"] for L in layers], [(F["xq"], F["xs"]) for F in fr])
+        for F in fr:
+            fb().gemm_w8a8_blockscaled_frag(F["xq"], F["xs"], F["wq"], F["ws"], F["y"])
         fb().kv_scale_calibrate(kv["k"], kv["v"], True, kv["ks"], kv["vs"])
         fb().kv_cache_write_fp8(kv["k"], kv["v"], kv["slots"], kv["ks"], kv["vs"], kv["kc"], kv["vc"])
 
     outs = ([t for L in layers for t in (L["wq"], L["ws"], L["xq"], L["xs"], L["y"])] +
-            [kv["ks"], kv["vs"], kv["kc"], kv["vc"], moe["y"], moe["yg"], af["xq"], af["xs"], af["y"]])
+            [kv["ks"], kv["vs"], kv["kc"], kv["vc"], moe["y"], moe["yg"], af["xq"], af["xs"], af["y"]] +
+            [t for F in fr for t in (F["wq"], F["ws"], F["xq"], F["xs"], F["y"])])
     announce("graph eager reference")
     work()
     ref = snapshot(outs)
@@ -100,7 +108,9 @@ def test_graph_replays_match_eager():
         got = snapshot(outs)
         for a, b in zip(got, ref):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
-    # the fragment-order GEMM agrees with the row-major GEMM (whose default
-    # tile at M = 256 sums in another order, so to the GEMM tolerance)
-    y_af, y_rm = ref[-1].float(), ref[4].float()
-    assert float((y_af - y_rm).norm() / y_rm.norm()) <= 1e-2
+    # the fragment-order GEMMs give the row-major GEMM's bits, and the
+    # fragment-order quantizers its scales
+    assert torch.equal(af["y"].view(torch.int16), layers[0]["y"].view(torch.int16))
+    for F, L in zip(fr, layers):
+        assert torch.equal(F["y"].view(torch.int16), L["y"].view(torch.int16))
+        assert torch.equal(F["ws"], L["ws"]) and torch.equal(F["xs"], L["xs"])
