@@ -357,7 +357,7 @@ def quantize_act_per_token_group_frag(x, out=None, scale=None):
 
 def gemm_w8a8_blockscaled_afrag(a_frag, a_scale, w, w_scale, out=None, wfrag=False):
     """gemm_w8a8_blockscaled with the activation codes in fragment order (quantize_act_per_token_group_frag);
-    M % 16 == 0 and K % 256 == 0.  ``wfrag``: the weight codes in fragment order too
+    M % 16 == 0 and K % 128 == 0.  ``wfrag``: the weight codes in fragment order too
     (gemm_w8a8_blockscaled_frag; N % 16 == 0)."""
     m, k = a_frag.shape
     n = w.shape[0]
@@ -378,7 +378,7 @@ def gemm_w8a8_blockscaled_afrag(a_frag, a_scale, w, w_scale, out=None, wfrag=Fal
 
 def gemm_w8a8_blockscaled_frag(a_frag, a_scale, w_frag, w_scale, out=None):
     """The GEMM with both operands' codes in fragment order (quantize_act_per_token_group_frag,
-    quantize_weight_blockwise_frag); M % 16 == 0, N % 16 == 0, K % 256 == 0."""
+    quantize_weight_blockwise_frag); M % 16 == 0, N % 16 == 0, K % 128 == 0."""
     return gemm_w8a8_blockscaled_afrag(a_frag, a_scale, w_frag, w_scale, out, wfrag=True)
 
 

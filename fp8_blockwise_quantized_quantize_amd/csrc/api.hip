@@ -425,7 +425,7 @@ namespace {
 fp8bq_status gemm_frag(const uint8_t* a_fp8_frag, const float* a_scale, const uint8_t* w_fp8, const float* w_scale,
                        uint16_t* y_bf16, int64_t M, int64_t N, int64_t K, bool wfrag, void* stream) {
   try {
-    if (M < 0 || N < 0 || K < 0 || (M % 16) != 0 || (K % 256) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
+    if (M < 0 || N < 0 || K < 0 || (M % 16) != 0 || (K % 128) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
     if (wfrag && (N % 16) != 0) return FP8BQ_ERR_BAD_SHAPE;
     int64_t mk, nk, mn, bytes;
     if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, &mn) || !mul_ok(mn, 2, &bytes))

@@ -1505,7 +1505,7 @@ hipError_t launch_gemm_frag_cfg(Cfg cfg, const uint8_t* a, const float* sa, cons
 hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, bool wfrag, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (M % 16 != 0 || K % (2 * kBlock) != 0 || (wfrag && N % 16 != 0)) return hipErrorInvalidValue;
+  if (M % 16 != 0 || K % kBlock != 0 || (wfrag && N % 16 != 0)) return hipErrorInvalidValue;
   const Cfg cfg = choose(M, N, K);
   return wfrag ? launch_gemm_frag_cfg<true>(cfg, a, sa, w, sw, y, M, N, K, stream)
                : launch_gemm_frag_cfg<false>(cfg, a, sa, w, sw, y, M, N, K, stream);

@@ -59,7 +59,7 @@ hipError_t launch_quant_act_frag_multi(const ActBatch& batch, int64_t blocks, hi
 // the same codes in the MFMA fragment order of the activation operand (M % 16 == 0, K % 128 == 0)
 hipError_t launch_quant_act_frag(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int64_t K,
                                  hipStream_t stream);
-// the GEMM on fragment-order activations (M % 16 == 0, K % 256 == 0); wfrag:
+// the GEMM on fragment-order activations (M % 16 == 0, K % 128 == 0); wfrag:
 // fragment-order weights too (N % 16 == 0)
 hipError_t launch_gemm_afrag(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, bool wfrag, hipStream_t stream);

@@ -313,21 +313,20 @@ fp8bq_status quantize_act_per_token_group_frag(const uint16_t* x_bf16, uint8_t* 
 /*
  * gemm_w8a8_blockscaled_afrag -- gemm_w8a8_blockscaled on activation codes
  * in the fragment order of quantize_act_per_token_group_frag
- * ([FP8-RL summary] §3.4.2 Phase 3).  The activation fragments go straight
- * to registers and only the weights are staged in LDS, which leaves room for
- * one workgroup barrier per two K-blocks.  Same result bits as
+ * ([FP8-RL summary] §3.4.2 Phase 3).  Each load of an activation operand is
+ * then a contiguous 1 KB piece of a fragment unit.  Same result bits as
  * gemm_w8a8_blockscaled on the row-major codes (same per-element order).
  *   a_fp8_frag  M * K bytes in fragment order; a_scale [M][K/128]
  *   w_fp8 [N][K], w_scale [ceil(N/128)][K/128], y_bf16 [M][N] as for
  *   gemm_w8a8_blockscaled.
- *   Requires M % 16 == 0 and K % 256 == 0 (K <= 2^22); FP8BQ_ERR_BAD_SHAPE
+ *   Requires M % 16 == 0 and K % 128 == 0 (K <= 2^22); FP8BQ_ERR_BAD_SHAPE
  *   otherwise.  The tile is chosen per shape as for gemm_w8a8_blockscaled
  *   (few activation rows: K split over the waves of a 64- or 48-row tile
  *   that loads the fragments straight into registers; more rows: the panel
  *   tiles, which keep the fragment order in their LDS ring), and the output
  *   is bit-identical to gemm_w8a8_blockscaled's on the row-major codes.
  *   This is the library's path for activations with M % 16 == 0 and
- *   K % 256 == 0: on the Qwen3-8B layer shapes it is faster than
+ *   K % 128 == 0: on the Qwen3-8B layer shapes it is faster than
  *   gemm_w8a8_blockscaled at both decode (M = 256) and prefill (M = 8192)
  *   sizes.
  */

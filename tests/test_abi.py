@@ -72,11 +72,13 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call("gemm_w8a8_blockscaled", good, good, good, good, good, 4, 4, (1 << 22) + 128, null) == 2
     assert _call("grouped_gemm_w8a8_blockscaled", good, good, good, good, good, good, 4, 4, (1 << 22) + 128, 2,
                  null) == 2
-    # fragment order: M % 16, K % 128 (quantizer) and K % 256 (GEMM)
+    # fragment order: M % 16 and K % 128 (quantizers and GEMMs), N % 16 (fragment-order weights)
     assert _call("quantize_act_per_token_group_frag", good, good, good, 24, 128, null) == 2
     assert _call("quantize_act_per_token_group_frag", good, good, good, 32, 200, null) == 2
     assert _call("gemm_w8a8_blockscaled_afrag", good, good, good, good, good, 24, 4, 256, null) == 2
-    assert _call("gemm_w8a8_blockscaled_afrag", good, good, good, good, good, 32, 4, 384, null) == 2
+    assert _call("gemm_w8a8_blockscaled_afrag", good, good, good, good, good, 32, 4, 200, null) == 2
+    assert _call("gemm_w8a8_blockscaled_frag", good, good, good, good, good, 32, 24, 256, null) == 2
+    assert _call("quantize_weight_blockwise_frag", good, good, good, 1, 24, 128, null) == 2
     assert _call("gemm_w8a8_blockscaled_afrag", good, good, good, good, good, 32, 4, (1 << 22) + 256, null) == 2
     assert _call("gemm_w8a8_blockscaled_afrag", good, good, null, good, good, 32, 4, 256, null) == 1
     # size overflow

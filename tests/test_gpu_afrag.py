@@ -77,13 +77,16 @@ def test_quantizer_frag_multi_shape_errors(fb, m, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 130, 256), (48, 384, 768), (272, 520, 512), (272, 528, 512),
-                                   (256, 256, 2048), (80, 20480, 256), (208, 24576, 256)])
+                                   (256, 256, 2048), (80, 20480, 256), (208, 24576, 256),
+                                   (32, 256, 384), (512, 512, 640), (144, 24576, 128), (208, 24576, 384),
+                                   (80, 20480, 384)])
 def test_gemm_afrag_against_oracle_and_row_major(fb, m, n, k):
     """Every tile form: 64- and 48-row K-split tiles, the 256 x 256 panel,
     the 128 x 256 decode panel (M = 80: one ragged tile of activation rows)
     and the 192 x 128 panel (M = 208: a second, ragged row tile).  Where
     N % 16 == 0 the same product with the weights in fragment order too
-    (N = 528: a ragged last weight scale block of 16 rows)."""
+    (N = 528: a ragged last weight scale block of 16 rows).  K = 128, 384 and
+    640: odd numbers of K-blocks on every tile form."""
     announce("afrag gemm", m, n, k)
     x, _ = activations(m, k, (m, n, k, 0))
     w = bf16_normal((n, k), 0.02, (m, n, k, 1))
@@ -121,9 +124,10 @@ def test_gemm_afrag_decode_shapes_bit_identical(fb, m):
         assert torch.equal(y0.view(torch.int16), y2.view(torch.int16)), (m, n, k)
 
 
-@pytest.mark.parametrize("n,k", [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)])
+@pytest.mark.parametrize("n,k", [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288), (2048, 384), (2048, 640)])
 def test_gemm_afrag_prefill_bit_identical(fb, n, k):
-    """The four Qwen3-8B prefill shapes (M = 8192): same bits as the row-major tile."""
+    """The four Qwen3-8B prefill shapes (M = 8192), and the 256 x 256 panel on
+    odd numbers of K-blocks: same bits as the row-major tile."""
     m = 8192
     announce("afrag gemm prefill", m, n, k)
     x = device_bf16_normal((m, k), 1.0, seed=11)
