@@ -722,30 +722,44 @@ def moe_layer(fb, dev):
                      None, 2 * R * H * F),
         "combine": ([lambda t=t: fb.moe_combine(t[0], pr, tw, t[1]) for t in comb_sets], comb_b, None),
     }
+    fused_sets = copies(rotations(w1_b), w1q, w1s, h, h_s)
+    # fc1 with SiLU(gate) * up quantized in its epilogue: replaces the
+    # fc1_gate_up + silu_mul_quant pair (not part of the separate chain's sum).
+    steps["fc1_silu_quant_fused"] = ([lambda t=t: fb.grouped_gemm_w8a8_blockscaled_gather_silu(a, a_s, sp, k, t[0], t[1], off,
+                                                                                          t[2], t[3])
+                                      for t in fused_sets], None, 2 * R * 2 * F * H)
     res, total = {}, 0.0
     for name, (fn, byt, flops) in steps.items():
         ms, _ = _time_graph_ms(fn)
-        total += ms
+        if name != "fc1_silu_quant_fused":
+            total += ms
         e = {"us": round(ms * 1e3, 1), "buffer_sets": len(fn)}
         if byt is not None:
             e.update({"bytes": byt, "GBps": round(byt / ms / 1e6, 1), "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)})
         if flops is not None:
-            n_out = 2 * F if name == "fc1_gate_up" else H
-            k_in = H if name == "fc1_gate_up" else F
-            a_rows = T if name == "fc1_gate_up" else R  # fc1 reads each token's row once (gathered)
-            byt_g = a_rows * k_in + E * n_out * k_in + 2 * R * n_out + a_rows * (k_in // 128) * 4
+            fc1 = name.startswith("fc1")
+            n_out = 2 * F if fc1 else H
+            k_in = H if fc1 else F
+            a_rows = T if fc1 else R  # fc1 reads each token's row once (gathered)
+            out_b = R * F + R * (F // 128) * 4 if name == "fc1_silu_quant_fused" else 2 * R * n_out
+            byt_g = a_rows * k_in + E * n_out * k_in + out_b + a_rows * (k_in // 128) * 4
             roof = min(FP8_PEAK_TFLOPS, flops / byt_g * HBM_PEAK_GBPS / 1e3)
             e.update({"TFLOPs": round(flops / ms / 1e9, 1), "roofline_TFLOPs": round(roof, 1),
                       "frac_roofline": round(flops / ms / 1e9 / roof, 4)})
         res[name] = e
 
     def layer():
-        fb.moe_expert_ffn(x, ids, tw, w1q, w1s, w2q, w2s)
+        fb.moe_expert_ffn(x, ids, tw, w1q, w1s, w2q, w2s, fused=True)
+
+    def layer_separate():
+        fb.moe_expert_ffn(x, ids, tw, w1q, w1s, w2q, w2s, fused=False)
 
     layer_ms, _ = _time_graph_ms(layer, calls=4)
-    del aq_sets, w1_sets, silu_sets, w2_sets, comb_sets
+    sep_ms, _ = _time_graph_ms(layer_separate, calls=4)
+    del aq_sets, w1_sets, silu_sets, w2_sets, comb_sets, fused_sets
     res["sum_of_kernels_us"] = round(total * 1e3, 1)
     res["layer_us"] = round(layer_ms * 1e3, 1)
+    res["layer_separate_fc1_silu_us"] = round(sep_ms * 1e3, 1)
     res["layer_TFLOPs"] = round((2 * R * 2 * F * H + 2 * R * H * F) / layer_ms / 1e9, 1)
     return res
 

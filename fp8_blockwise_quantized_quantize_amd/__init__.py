@@ -40,6 +40,7 @@ __all__ = [
     "gemm_w8a8_blockscaled_frag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
+    "grouped_gemm_w8a8_blockscaled_gather_silu",
     "check_group_offsets",
     "TILES",
     "encode_e4m3",
@@ -78,6 +79,7 @@ EXPORTS = (
     "gemm_w8a8_blockscaled_afrag",
     "grouped_gemm_w8a8_blockscaled",
     "grouped_gemm_w8a8_blockscaled_gather",
+    "grouped_gemm_w8a8_blockscaled_gather_silu",
     "gemm_w8a8_blockscaled_tile",
     "grouped_gemm_w8a8_blockscaled_tile",
     "fp8bq_check_group_offsets",
@@ -133,6 +135,7 @@ def _load():
     lib.gemm_w8a8_blockscaled_afrag.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, p]
     lib.grouped_gemm_w8a8_blockscaled_gather.argtypes = [p, p, i64, p, i64, p, p, p, p, i64, i64, i64, i64, p]
+    lib.grouped_gemm_w8a8_blockscaled_gather_silu.argtypes = [p, p, i64, p, i64, p, p, p, p, p, i64, i64, i64, i64, p]
     lib.gemm_w8a8_blockscaled_tile.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
     lib.gemm_w8a8_blockscaled_splitk.argtypes = [p, p, p, p, p, i64, i64, i64, p, i64, p]
     lib.gemm_w8a8_blockscaled_splitk_workspace.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
@@ -686,19 +689,56 @@ def moe_combine(y, pair_row, topk_weights, out=None):
     return out
 
 
-def moe_expert_ffn(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale):
+def grouped_gemm_w8a8_blockscaled_gather_silu(a, a_scale, a_rows, a_row_div, w, w_scale, group_offsets, h=None,
+                                              h_scale=None):
+    """MoE fc1 with SiLU(gate) * up quantized in its epilogue: w E4M3 [G, 2F, K] ([gate; up]),
+    rows gathered as in grouped_gemm_w8a8_blockscaled_gather -> (h codes uint8 [len(a_rows), F],
+    float32 scales [len(a_rows), F/128]), exactly those of silu_mul_quantize_act of the BF16 fc1 output."""
+    m_a, k = a.shape
+    g, n2, _ = w.shape
+    f = n2 // 2
+    dev = a.device
+    m = a_rows.numel()
+    _require(a, "a", _U8, (m_a, k))
+    _require(a_scale, "a_scale", torch.float32, (m_a, k // BLOCK), dev)
+    _require(a_rows, "a_rows", torch.int32, (m,), dev)
+    _require(w, "w", _U8, (g, n2, k), dev)
+    _require(w_scale, "w_scale", torch.float32, (g, _cdiv(n2, BLOCK), k // BLOCK), dev)
+    _require(group_offsets, "group_offsets", torch.int32, (g + 1,), dev)
+    if n2 % 2:
+        raise ValueError("w must hold [gate; up] rows (an even count)")
+    if h is None:
+        h = torch.empty((m, f), dtype=torch.uint8, device=dev)
+    if h_scale is None:
+        h_scale = torch.empty((m, _cdiv(f, BLOCK)), dtype=torch.float32, device=dev)
+    _require(h, "h", _U8, (m, f), dev)
+    _require(h_scale, "h_scale", torch.float32, (m, _cdiv(f, BLOCK)), dev)
+    with torch.cuda.device(dev):
+        _check("grouped_gemm_w8a8_blockscaled_gather_silu",
+               _lib.grouped_gemm_w8a8_blockscaled_gather_silu(_ptr(a), _ptr(a_scale), m_a, _ptr(a_rows), int(a_row_div),
+                                                              _ptr(w), _ptr(w_scale), _ptr(group_offsets), _ptr(h),
+                                                              _ptr(h_scale), m, f, k, g, _stream(a)))
+    return h, h_scale
+
+
+def moe_expert_ffn(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, fused=True):
     """One MoE expert FFN layer through the library's kernels only.
 
     x BF16 [T, H]; topk_ids int32 [T, k]; topk_weights float32 [T, k];
     w1 E4M3 [E, 2F, H] (fc1 = [gate; up]) with scales [E, 2F/128, H/128];
     w2 E4M3 [E, H, F] (fc2) with scales [E, H/128, F/128].  Returns BF16 [T, H].
+    ``fused``: fc1 with the SiLU * up quantization in its epilogue (same
+    result bits as the separate kernels).
     """
     E, H = w1.shape[0], x.shape[1]
     k = topk_ids.shape[1]
     offsets, sorted_pair, pair_row = moe_sort_by_expert(topk_ids, E)
     a, a_s = quantize_act_per_token_group(x)   # once per token; fc1 gathers the rows
-    y1 = grouped_gemm_w8a8_blockscaled_gather(a, a_s, sorted_pair, k, w1, w1_scale, offsets)
-    h, h_s = silu_mul_quantize_act(y1)
+    if fused:
+        h, h_s = grouped_gemm_w8a8_blockscaled_gather_silu(a, a_s, sorted_pair, k, w1, w1_scale, offsets)
+    else:
+        y1 = grouped_gemm_w8a8_blockscaled_gather(a, a_s, sorted_pair, k, w1, w1_scale, offsets)
+        h, h_s = silu_mul_quantize_act(y1)
     y2 = grouped_gemm_w8a8_blockscaled(h, h_s, w2, w2_scale, offsets)
     return moe_combine(y2, pair_row, topk_weights)
 

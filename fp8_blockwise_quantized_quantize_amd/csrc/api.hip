@@ -517,6 +517,40 @@ fp8bq_status grouped_gemm(bool gather, const uint8_t* a_fp8, const float* a_scal
 
 extern "C" {
 
+fp8bq_status grouped_gemm_w8a8_blockscaled_gather_silu(const uint8_t* a_fp8, const float* a_scale, int64_t M_a,
+                                                       const int32_t* a_rows, int64_t a_row_div, const uint8_t* w_fp8,
+                                                       const float* w_scale, const int32_t* group_offsets,
+                                                       uint8_t* h_fp8, float* h_scale, int64_t M_total, int64_t F,
+                                                       int64_t K, int64_t G, void* stream) {
+  try {
+    if (M_a < 0 || M_total < 0 || F < 0 || K <= 0 || G < 0 || (F % 128) != 0 || (K % 128) != 0 || K > kMaxGemmK)
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (a_row_div < 1 || a_row_div > 0x7fffffffLL || G > 1024) return FP8BQ_ERR_BAD_SHAPE;
+    int64_t ak, fk, gfk, mf;
+    if (!mul_ok(M_a, K, &ak) || !mul_ok(F + 128, K, &fk) || !mul_ok(2 * fk, G, &gfk) || !mul_ok(M_total, F, &mf))
+      return FP8BQ_ERR_BAD_SHAPE;
+    if (ak >= (int64_t(1) << 31) || fk >= (int64_t(1) << 31)) return FP8BQ_ERR_BAD_SHAPE;
+    if (G > 0 && M_total + 128 * G > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
+    if (mf == 0) return FP8BQ_OK;
+    if (G == 0) return FP8BQ_ERR_BAD_SHAPE;  // rows to produce but no expert to own them
+    if (!h_fp8 || !h_scale || !group_offsets || !a_rows || !w_fp8 || !w_scale) return FP8BQ_ERR_NULL_PTR;
+    if (M_a > 0 && (!a_fp8 || !a_scale)) return FP8BQ_ERR_NULL_PTR;
+    if (!aligned16(h_fp8) || !aligned16(h_scale) || !aligned16(a_rows) || !aligned16(w_fp8) || !aligned16(w_scale) ||
+        !aligned16(group_offsets) || (M_a > 0 && (!aligned16(a_fp8) || !aligned16(a_scale))))
+      return FP8BQ_ERR_MISALIGNED;
+    fp8bq_status st = check_device();
+    if (st != FP8BQ_OK) return st;
+    st = check_offsets_if_asked(group_offsets, G, M_total, static_cast<hipStream_t>(stream));
+    if (st != FP8BQ_OK) return st;
+    clear_last_error();
+    return launched(fp8bq::launch_grouped_gemm_gather_silu(a_fp8, a_scale, a_rows, a_row_div, M_a, w_fp8, w_scale,
+                                                           group_offsets, h_fp8, h_scale, M_total, F, K, G,
+                                                           static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return FP8BQ_ERR_LAUNCH;
+  }
+}
+
 fp8bq_status grouped_gemm_w8a8_blockscaled_tile(const uint8_t* a_fp8, const float* a_scale, int64_t M_a,
                                                 const int32_t* a_rows, int64_t a_row_div, const uint8_t* w_fp8,
                                                 const float* w_scale, const int32_t* group_offsets,

@@ -46,6 +46,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "silu_math.hpp"
 
 namespace fp8bq {
 
@@ -177,6 +178,10 @@ struct Tile {
   const int32_t* a_rows;
   int a_div;
   int64_t a_nrows;
+  // SiLU(gate) * up tiles (grouped fc1 only): h codes [M][N/2] and their
+  // 1x128 scales [M][N/256]
+  uint8_t* hq;
+  float* hs;
 };
 
 // A buffer offset past every record: the load returns zeros.  Buffers that
@@ -446,9 +451,17 @@ struct Skinny {
 // between the MFMAs.
 // ---------------------------------------------------------------------------
 // kWfrag: the weight codes are in MFMA fragment order.
-template <int BN_, int BM_, int WGN, int WGM, int S, bool kWfrag = false>
+// kSilu (persistent grouped tiles only): the fc1 form.  The weights are
+// [gate; up] of N = 2F rows and a tile computes 128 columns c0.. of
+// h = SiLU(gate) * up: its weight rows are gate c0..c0+63, up c0..c0+63,
+// gate c0+64..c0+127, up c0+64..c0+127, so each wave holds the gate and up
+// values of the same 64 columns in the same lanes (fragments i and i + 4),
+// and the epilogue stores h as E4M3 codes in 1x128 groups (the group amax
+// crosses the two waves of a row through LDS).
+template <int BN_, int BM_, int WGN, int WGM, int S, bool kWfrag = false, bool kSilu = false>
 struct Panel {
   static constexpr int BN = BN_, BM = BM_;
+  static constexpr bool kSiluForm = kSilu;
   static_assert(WGN * WGM == 8, "eight waves");
   static constexpr int WNR = BN / WGN, WMR = BM / WGM;  // rows of a wave's tile
   static constexpr int TN = WNR / 16, TM = WMR / 16;
@@ -462,14 +475,16 @@ struct Panel {
   // the tile's weight scale blocks), after the S operand stages.
   static constexpr int kScaleBytes = 8 * 64 * 4;
   static_assert(BM / 64 < 8, "a wave left over for the weight scales");
-  static constexpr int kLdsBytes = S * (kStage + kScaleBytes);
+  static constexpr int kAmaxOff = S * (kStage + kScaleBytes);  // kSilu: 2 x BM row maxima
+  static constexpr int kLdsBytes = kAmaxOff + (kSilu ? 2 * BM * 4 : 0);
   static_assert(S == 2 || S == 3, "stages");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
   static constexpr int kThreadsPerWg = 512;
   static constexpr int kWavesPerSimd = 2;
   // a wave's weight rows lie in one 128-row scale block when tiles start at
   // multiples of 128 and the wave's share divides 128
-  static constexpr bool kOneScaleBlock = (BN % kBlock == 0) && (kBlock % WNR == 0);
+  static constexpr bool kOneScaleBlock = (BN % kBlock == 0) && (kBlock % WNR == 0) && !kSilu;
+  static_assert(!kSilu || (BN == 256 && WGN == 2 && TN == 8 && !kWfrag), "the fc1 form's row interleave");
 
   __device__ static __forceinline__ void run(const Tile& t, uint8_t* lds) { run_impl<false>(t, lds); }
   // activation rows gathered through t.a_rows (grouped GEMM)
@@ -749,12 +764,23 @@ struct Panel {
     auto setup_load = [&](const Tile& t) {
       const int64_t n_hi = (t.n0 + BN < t.N) ? t.n0 + BN : t.N;
       const int64_t NBm1 = (t.N - 1) / kBlock, nbt = t.n0 / kBlock;
-      wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
+      if constexpr (kSilu) {
+        // gate rows n0 .. n0 + 127 and up rows F + n0 .. F + n0 + 127 (F = N / 2,
+        // n0 a multiple of 128); weight scale blocks n0 / 128 (slot 0) and
+        // (F + n0) / 128 (slot 1)
+        const int64_t F = t.N / 2;
+        wr = make_rsrc(t.w + t.n0 * K, (F + kBlock) * K);
+        scr = act_scales ? make_rsrc(t.sa, t.a_nrows * KB * 4)
+                         : make_rsrc(t.sw + nbt * KB, (F / kBlock + 1) * KB * 4);
+        scvoff = lane == 0 ? 0 : (lane == 1 ? (int)(F / kBlock) * KB * 4 : kOob);
+      } else {
+        wr = make_rsrc(t.w + t.n0 * K, (n_hi - t.n0) * K);
+        scr = act_scales ? (kGather ? make_rsrc(t.sa, t.a_nrows * KB * 4)
+                                    : make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4))
+                         : make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
+        scvoff = lane * KB * 4;
+      }
       ar = kGather ? make_rsrc(t.a, t.a_nrows * K) : make_rsrc(t.a + t.m_lo * K, (t.m_hi - t.m_lo) * K);
-      scr = act_scales ? (kGather ? make_rsrc(t.sa, t.a_nrows * KB * 4)
-                                  : make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4))
-                       : make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
-      scvoff = lane * KB * 4;
       if (act_scales) {
         const int64_t r = src_row(t, t.m_lo + 64 * wave + lane);
         scvoff = kGather ? (r >= 0 ? (int)(r * KB * 4) : kOob) : (64 * wave + lane) * KB * 4;
@@ -787,16 +813,22 @@ struct Panel {
     uint32_t hi_mask = 0;
     bool idle = false;
     auto setup_compute = [&](const Tile& t) {
-      const int64_t NBm1 = (t.N - 1) / kBlock, nbt = t.n0 / kBlock;
-      const int64_t wrow0 = t.n0 + wn * WNR;
-      const int64_t nb0 = ((wrow0 < t.N) ? wrow0 : t.N - 1) / kBlock;
-      const int64_t nb1 = nb0 + 1 < NBm1 ? nb0 + 1 : NBm1;
-      wsl0 = (int)(nb0 - nbt);
-      wsl1 = (int)(nb1 - nbt);
-      hi_mask = 0;
+      if constexpr (kSilu) {  // fragments 0..3 gate (scale slot 0), 4..7 up (slot 1)
+        wsl0 = 0;
+        wsl1 = 1;
+        hi_mask = 0xF0u;
+      } else {
+        const int64_t NBm1 = (t.N - 1) / kBlock, nbt = t.n0 / kBlock;
+        const int64_t wrow0 = t.n0 + wn * WNR;
+        const int64_t nb0 = ((wrow0 < t.N) ? wrow0 : t.N - 1) / kBlock;
+        const int64_t nb1 = nb0 + 1 < NBm1 ? nb0 + 1 : NBm1;
+        wsl0 = (int)(nb0 - nbt);
+        wsl1 = (int)(nb1 - nbt);
+        hi_mask = 0;
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
-        if ((wrow0 + i * 16) / kBlock > nb0) hi_mask |= 1u << i;
+        for (int i = 0; i < TN; ++i)
+          if ((wrow0 + i * 16) / kBlock > nb0) hi_mask |= 1u << i;
+      }
       idle = t.m_lo + wm * WMR >= t.m_hi;
     };
     setup_compute(ct);
@@ -812,11 +844,18 @@ struct Panel {
       auto* dst = (__attribute__((address_space(3))) void*)(lds + S * kStage + stage * kScaleBytes + wave * 256);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, dst, 4, scvoff, kb * 4, 0, 0);
     };
+    // kSilu: load q < 4 fills tile rows 64 q .. 64 q + 63 with gate (q even)
+    // or up (q odd) rows 64 (q / 2) .. of the tile's 128 columns
+    const int fup = kSilu ? (int)(lt.N / 2) * (int)K : 0;
     auto dma_q = [&](int q, int kb, uint8_t* buf) {
       const int koff = kb * kBlock;
       const int r0 = 8 * (8 * q + wave);
       auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
-      if (q < BN / 64)
+      if (q < BN / 64 && kSilu)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16,
+                                                 dvoff + ((q & 1) ? fup : 0) + ((q >> 1) * 64 + 8 * wave) * (int)K,
+                                                 koff, 0, 0);
+      else if (q < BN / 64)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, koff, 0, 0);
       else if (kGather)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, aoff[kGather ? q - BN / 64 : 0], koff, 0, 0);
@@ -890,6 +929,69 @@ struct Panel {
       dma_kblock(lt_kb, st);
       advance_load();
     }
+    // kSilu: lane (r16, g) holds, for rows wm WMR + 16 j + r16, the gate and
+    // up accumulators of columns 64 wn + 16 i + 4 g + r (fragments i and
+    // i + 4, i, r < 4).  Each is rounded to BF16 (the fc1 output the
+    // unfused chain would store), h = SiLU(gate) * up is rounded to BF16
+    // exactly (silu_mul_bf16), and the row's 1x128 group (the columns of
+    // both waves wn = 0, 1) is quantized: amax over the wave's lanes by
+    // shuffles, across the two waves through LDS, s = fl32(amax / 448),
+    // codes E4M3(fl32(h / s)).
+    auto silu_epilogue = [&](const Tile& t) {
+      const int64_t F = t.N / 2;
+      uint32_t hb[4][TM][4];
+      uint32_t mx[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        mx[j] = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gv = __uint_as_float(bf16_rne(acc[i][j][r]) << 16);
+            const float uv = __uint_as_float(bf16_rne(acc[i + 4][j][r]) << 16);
+            const uint32_t h = silu_mul_bf16(gv, uv);
+            hb[i][j][r] = h;
+            const uint32_t ah = h & 0x7fffu;
+            mx[j] = mx[j] > ah ? mx[j] : ah;
+          }
+        mx[j] = max(mx[j], (uint32_t)__shfl_xor((int)mx[j], 16));
+        mx[j] = max(mx[j], (uint32_t)__shfl_xor((int)mx[j], 32));
+      }
+      uint32_t* am = reinterpret_cast<uint32_t*>(lds + kAmaxOff);
+      if (g == 0) {
+#pragma unroll
+        for (int j = 0; j < TM; ++j) am[wn * BM + wm * WMR + j * 16 + r16] = mx[j];
+      }
+      barrier();
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const uint32_t other = am[(1 - wn) * BM + wm * WMR + j * 16 + r16];
+        const float sc = scale_from_amax_bits(mx[j] > other ? mx[j] : other);
+        const int64_t m = t.m_lo + wm * WMR + j * 16 + r16;
+        if (m >= t.m_hi) continue;
+        const Divisor d(sc != 0.0f ? sc : 1.0f);
+        uint8_t* dst = t.hq + m * F + t.n0 + 64 * wn + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t code;
+          if (sc == 0.0f) {  // the sign of each input zero
+            code = ((hb[i][j][0] >> 8) & 0x80u) | (hb[i][j][1] & 0x8000u) | ((hb[i][j][2] << 8) & 0x800000u) |
+                   ((hb[i][j][3] << 16) & 0x80000000u);
+          } else {
+            float q[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float x = __uint_as_float(hb[i][j][r] << 16);
+              q[r] = d.fast ? d.quotient_fast(x) : d.quotient_ieee(x);
+            }
+            code = pack4_e4m3(q[0], q[1], q[2], q[3]);
+          }
+          *reinterpret_cast<uint32_t*>(dst + 16 * i) = code;
+        }
+        if (wn == 0 && g == 0) t.hs[m * (F / kBlock) + t.n0 / kBlock] = sc;
+      }
+    };
     const int64_t steps = (int64_t)ntiles * KB;
     int cur = 0;
     for (int64_t step = 0; step < steps; ++step) {
@@ -905,12 +1007,16 @@ struct Panel {
       advance_load();
       cur = (cur + 1 == S) ? 0 : cur + 1;
       if (++ct_kb == KB) {  // the compute tile's last K-block: store it, start the next
+        if constexpr (kSilu) {
+          silu_epilogue(ct);
+        } else {
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          const int64_t m = ct.m_lo + wm * WMR + j * 16 + r16;
-          if (m >= ct.m_hi) continue;
+          for (int j = 0; j < TM; ++j) {
+            const int64_t m = ct.m_lo + wm * WMR + j * 16 + r16;
+            if (m >= ct.m_hi) continue;
 #pragma unroll
-          for (int i = 0; i < TN; ++i) store4(ct.y, ct.N, m, ct.n0 + wn * WNR + i * 16 + g * 4, acc[i][j]);
+            for (int i = 0; i < TN; ++i) store4(ct.y, ct.N, m, ct.n0 + wn * WNR + i * 16 + g * 4, acc[i][j]);
+          }
         }
 #pragma unroll
         for (int i = 0; i < TN; ++i)
@@ -1145,7 +1251,8 @@ template <class Kern, bool kGather>
 __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_grouped_persistent_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ sa, const uint8_t* __restrict__ w,
     const float* __restrict__ sw, const int32_t* __restrict__ offsets, uint16_t* __restrict__ y, int64_t M,
-    int64_t N, int64_t K, int G, int64_t tiles_n, const int32_t* __restrict__ a_rows, int a_div, int64_t a_nrows) {
+    int64_t N, int64_t K, int G, int64_t tiles_n, const int32_t* __restrict__ a_rows, int a_div, int64_t a_nrows,
+    uint8_t* __restrict__ hq, float* __restrict__ hs) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int NT = threads_of<Kern>();
   constexpr int BM = Kern::BM, BN = Kern::BN;
@@ -1212,10 +1319,11 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
     t.y = y;
     t.m_lo = (int64_t)lo + (int64_t)(slot - pre[e]) * BM;
     t.m_hi = (t.m_lo + BM < hi) ? t.m_lo + BM : hi;
-    t.n0 = tn * BN;
+    t.n0 = tn * (Kern::kSiluForm ? kBlock : BN);  // the fc1 form's tiles are 128 columns of h
     t.N = N; t.K = K;
     t.a_rows = a_rows; t.a_div = a_div; t.a_nrows = a_nrows;
     t.kb0 = 0; t.kb1 = (int)KB; t.part = nullptr;
+    t.hq = hq; t.hs = hs;
     return t;
   };
   Kern::template run_persistent<kGather>(ntiles, tile_at, smem);
@@ -1311,14 +1419,16 @@ hipError_t launch_grouped_cfg(const uint8_t* a, const float* sa, const uint8_t* 
 template <class Kern, bool kGather>
 hipError_t launch_grouped_persistent(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                                      const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
-                                     const int32_t* a_rows, int a_div, int64_t a_nrows, hipStream_t stream) {
-  const int64_t tiles_n = (N + Kern::BN - 1) / Kern::BN;
+                                     const int32_t* a_rows, int a_div, int64_t a_nrows, hipStream_t stream,
+                                     uint8_t* hq = nullptr, float* hs = nullptr) {
+  // the fc1 form: N = 2F weight rows, one tile per 128 columns of h
+  const int64_t tiles_n = Kern::kSiluForm ? N / 2 / kBlock : (N + Kern::BN - 1) / Kern::BN;
   const int64_t bound = tiles_n * ((M + Kern::BM - 1) / Kern::BM + G);  // >= the tiles there are
   const int64_t cus = (int64_t)cu_count();
   const int64_t P = bound < cus ? bound : cus;  // one workgroup per CU (the tile's LDS allows one)
   hipLaunchKernelGGL((gemm_grouped_persistent_kernel<Kern, kGather>), dim3((unsigned)P), dim3(Kern::kThreadsPerWg),
                      (size_t)Kern::kLdsBytes, stream, a, sa, w, sw, offsets, y, M, N, K, (int)G, tiles_n, a_rows,
-                     a_div, a_nrows);
+                     a_div, a_nrows, hq, hs);
   return hipGetLastError();
 }
 
@@ -1341,7 +1451,9 @@ hipError_t launch_grouped_any(const uint8_t* a, const float* sa, const uint8_t* 
   if (tile == 3)
     return launch_grouped_cfg<Wide, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows, stream);
   if (tile != 0 && tile != 5 && tile != 7) return hipErrorInvalidValue;
-  const bool per_tile = tile == 5;
+  // K = 0: the per-tile kernel stores the zero products (the persistent one
+  // has no K-block step to end a tile on)
+  const bool per_tile = tile == 5 || K == 0;
   if (per_tile || G > kMaxPersistentExperts)
     return launch_grouped_cfg<Deep, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows, stream);
   return launch_grouped_persistent<Deep, kGather>(a, sa, w, sw, offsets, y, M, N, K, G, a_rows, a_div, a_nrows,
@@ -1515,6 +1627,20 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t*
                                const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
                                int tile, hipStream_t stream) {
   return launch_grouped_any<false>(a, sa, w, sw, offsets, y, M, N, K, G, nullptr, 1, 0, tile, stream);
+}
+
+// The MoE fc1 GEMM with the SiLU(gate) * up quantization in its epilogue:
+// the persistent deep tile in its fc1 form (weights [G][2F][K], F % 128 ==
+// 0, G <= kMaxPersistentExperts), rows gathered through a_rows.
+hipError_t launch_grouped_gemm_gather_silu(const uint8_t* a, const float* sa, const int32_t* a_rows, int64_t a_div,
+                                           int64_t a_nrows, const uint8_t* w, const float* sw, const int32_t* offsets,
+                                           uint8_t* hq, float* hs, int64_t M, int64_t F, int64_t K, int64_t G,
+                                           hipStream_t stream) {
+  if (M == 0 || F == 0 || G == 0) return hipSuccess;
+  if (F % kBlock != 0 || G > kMaxPersistentExperts) return hipErrorInvalidValue;
+  using Kern = Panel<256, 128, 2, 4, 3, false, true>;
+  return launch_grouped_persistent<Kern, true>(a, sa, w, sw, offsets, nullptr, M, 2 * F, K, G, a_rows, (int)a_div,
+                                               a_nrows, stream, hq, hs);
 }
 
 hipError_t launch_grouped_gemm_gather(const uint8_t* a, const float* sa, const int32_t* a_rows, int64_t a_div,

@@ -87,6 +87,14 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* sa, const uint8_t*
                                const int32_t* offsets, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G,
                                int tile, hipStream_t stream);
 
+// The MoE fc1 GEMM (weights [G][2F][K] = [gate; up] per expert, rows
+// gathered as in launch_grouped_gemm_gather) with h = SiLU(gate) * up
+// quantized in 1x128 groups in its epilogue: codes hq [M][F], scales
+// hs [M][F/128] (F % 128 == 0, K > 0, G <= 1024).
+hipError_t launch_grouped_gemm_gather_silu(const uint8_t* a, const float* sa, const int32_t* a_rows, int64_t a_div,
+                                           int64_t a_nrows, const uint8_t* w, const float* sw, const int32_t* offsets,
+                                           uint8_t* hq, float* hs, int64_t M, int64_t F, int64_t K, int64_t G,
+                                           hipStream_t stream);
 hipError_t launch_grouped_gemm_gather(const uint8_t* a, const float* sa, const int32_t* a_rows, int64_t a_div,
                                       int64_t a_nrows, const uint8_t* w, const float* sw, const int32_t* offsets,
                                       uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t G, int tile,

@@ -397,6 +397,31 @@ fp8bq_status grouped_gemm_w8a8_blockscaled_gather(const uint8_t* a_fp8, const fl
                                                   void* stream);
 
 /*
+ * grouped_gemm_w8a8_blockscaled_gather_silu -- the MoE fc1 GEMM with the
+ * gated activation and its quantization in the epilogue ([FP8-RL summary]
+ * §3.4.1 "Quantization Scope": fc1 gives gate and up, multiplied element-wise
+ * before fc2; "Static vs. Dynamic Quantization": the nonlinearity in higher
+ * precision, the activations quantized on the fly in 1x128 tiles).  Gives
+ * exactly the codes and scales of
+ *   silu_mul_quantize_act(grouped_gemm_w8a8_blockscaled_gather(...))
+ * without storing the BF16 fc1 output [M_total][2F]: each gate and up value
+ * is rounded to BF16 as that output would be, h = SiLU(gate) * up is rounded
+ * to BF16 from its exact value, and h is quantized per row in groups of 128
+ * columns.
+ *   a_fp8, a_scale, M_a, a_rows, a_row_div, group_offsets, M_total, K, G as
+ *   in grouped_gemm_w8a8_blockscaled_gather, with K > 0 and G <= 1024;
+ *   w_fp8 [G][2F][K] E4M3 with rows [gate (F); up (F)] per expert, w_scale
+ *   [G][2F/128][K/128]; outputs h_fp8 [M_total][F] E4M3 and h_scale
+ *   [M_total][F/128] float32.  F % 128 == 0 and (F + 128) * K < 2^31;
+ *   FP8BQ_ERR_BAD_SHAPE otherwise.  All pointers 16-byte aligned.
+ */
+fp8bq_status grouped_gemm_w8a8_blockscaled_gather_silu(const uint8_t* a_fp8, const float* a_scale, int64_t M_a,
+                                                       const int32_t* a_rows, int64_t a_row_div, const uint8_t* w_fp8,
+                                                       const float* w_scale, const int32_t* group_offsets,
+                                                       uint8_t* h_fp8, float* h_scale, int64_t M_total, int64_t F,
+                                                       int64_t K, int64_t G, void* stream);
+
+/*
  * grouped_gemm_w8a8_blockscaled_tile -- the grouped GEMM (plain when a_rows
  * is NULL, then a_fp8 has M_total rows and M_a / a_row_div are ignored;
  * gathered otherwise, as grouped_gemm_w8a8_blockscaled_gather) with the

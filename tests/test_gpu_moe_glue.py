@@ -245,3 +245,91 @@ def test_silu_mul_structural_ties():
         for u in ups:
             y = np.concatenate([gg, np.full(gg.shape, u, np.uint16)], axis=1)
             silu_case(y, F, f"ties {name} u={hex(int(u))}")
+
+
+def _fused_case(T, k, E, H, F, seed, ids=None, rows=None):
+    """fc1 with the SiLU * up quantization in its epilogue against the two
+    separate kernels (gathered fc1 GEMM to BF16, then silu_mul_quantize_act):
+    the same codes and scales, bit for bit."""
+    from synthetic import device_bf16_normal
+
+    announce("fused fc1 SiLU quant", T, k, E, H, F)
+    if ids is None:
+        ids, _ = moe_topk(T, E, k, (seed, 0))
+    off, sp, _ = fb().moe_sort_by_expert(dev(ids.astype(np.int32)), E)
+    if rows is not None:
+        sp = dev(rows)
+    x = device_bf16_normal((T, H), 1.0, seed=seed + 1)
+    a, a_s = fb().quantize_act_per_token_group(x)
+    w, w_s = fb().quantize_weight_blockwise(device_bf16_normal((E, 2 * F, H), 0.02, seed=seed + 2))
+    y1 = fb().grouped_gemm_w8a8_blockscaled_gather(a, a_s, sp, k, w, w_s, off)
+    h_ref, hs_ref = fb().silu_mul_quantize_act(y1)
+    h, hs = fb().grouped_gemm_w8a8_blockscaled_gather_silu(a, a_s, sp, k, w, w_s, off)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h_ref), (T, k, E, H, F, int((h != h_ref).sum()))
+    assert torch.equal(hs.view(torch.int32), hs_ref.view(torch.int32)), (T, k, E, H, F)
+
+
+@pytest.mark.parametrize("T,k,E,H,F", [(1, 1, 2, 128, 128), (37, 4, 8, 384, 256), (300, 2, 5, 256, 384),
+                                       (513, 8, 16, 1024, 640)])
+def test_fused_fc1_silu_matches_separate_kernels(T, k, E, H, F):
+    _fused_case(T, k, E, H, F, seed=90 + T)
+
+
+def test_fused_fc1_silu_qwen3_30b_a3b():
+    """The full Qwen3-30B-A3B fc1 (4096 tokens, top-8 of 128 experts, H = 2048, F = 768)."""
+    c = MOE_QWEN3_30B_A3B
+    _fused_case(c["tokens"], c["top_k"], c["experts"], c["hidden"], c["ffn"], seed=70)
+
+
+def test_fused_fc1_silu_ragged_and_empty_experts_and_missing_rows():
+    """Experts with 0, 1, 129 and 300 rows, and gathered rows that name no
+    token (negative or past the token count: zero activation rows)."""
+    T, k, E, H, F = 250, 2, 6, 256, 256
+    counts = [0, 1, 129, 0, 300, 250 * 2 - 430]
+    ids = np.repeat(np.arange(E), counts).astype(np.int32)
+    ids = np.random.default_rng(3).permutation(ids).reshape(T, k)
+    rows = np.random.default_rng(4).integers(-3, T * k + 50, T * k).astype(np.int32)
+    _fused_case(T, k, E, H, F, seed=11, ids=ids)
+    _fused_case(T, k, E, H, F, seed=12, ids=ids, rows=rows)
+
+
+def test_fused_fc1_silu_shape_errors():
+    a = torch.zeros((4, 128), dtype=torch.uint8, device=DEV)
+    a_s = torch.ones((4, 1), device=DEV)
+    rows = torch.zeros(4, dtype=torch.int32, device=DEV)
+    off = torch.tensor([0, 4], dtype=torch.int32, device=DEV)
+    w = torch.zeros((1, 2 * 192, 128), dtype=torch.uint8, device=DEV)  # F = 192: not a multiple of 128
+    with pytest.raises(fb().FP8BQError, match="shape"):
+        fb().grouped_gemm_w8a8_blockscaled_gather_silu(a, a_s, rows, 1, w, torch.ones((1, 3, 1), device=DEV), off)
+
+
+def test_moe_layer_fused_and_separate_are_identical():
+    from synthetic import device_bf16_normal
+
+    T, E, k, H, F = 513, 16, 4, 512, 256
+    announce("MoE layer fused vs separate", T, E, k, H, F)
+    ids, tw = moe_topk(T, E, k, (5, 5))
+    x = device_bf16_normal((T, H), 1.0, seed=21)
+    w1, w1s = fb().quantize_weight_blockwise(device_bf16_normal((E, 2 * F, H), 0.02, seed=22))
+    w2, w2s = fb().quantize_weight_blockwise(device_bf16_normal((E, H, F), 0.02, seed=23))
+    y0 = fb().moe_expert_ffn(x, dev(ids), dev(tw), w1, w1s, w2, w2s, fused=False)
+    y1 = fb().moe_expert_ffn(x, dev(ids), dev(tw), w1, w1s, w2, w2s, fused=True)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
+def test_grouped_gemm_k_zero_gives_zeros():
+    """K = 0 experts: the zero products are stored (plain and gathered)."""
+    m, n, g = 40, 256, 3
+    off = torch.tensor([0, 10, 10, 40], dtype=torch.int32, device=DEV)
+    a = torch.empty((m, 0), dtype=torch.uint8, device=DEV)
+    a_s = torch.empty((m, 0), dtype=torch.float32, device=DEV)
+    w = torch.empty((g, n, 0), dtype=torch.uint8, device=DEV)
+    w_s = torch.empty((g, 2, 0), dtype=torch.float32, device=DEV)
+    y = torch.full((m, n), 1.0, dtype=torch.bfloat16, device=DEV)
+    fb().grouped_gemm_w8a8_blockscaled(a, a_s, w, w_s, off, y)
+    assert torch.count_nonzero(y.float()) == 0
+    y.fill_(1.0)
+    rows = torch.arange(m, dtype=torch.int32, device=DEV)
+    fb().grouped_gemm_w8a8_blockscaled_gather(a, a_s, rows, 1, w, w_s, off, y)
+    assert torch.count_nonzero(y.float()) == 0
