@@ -1197,6 +1197,9 @@ def gemm_profile_cases():
     mt = moe["tokens"] * moe["top_k"]
     cases.append(("MoE fc1 gate_up", mt, moe["gate_up"][0], moe["gate_up"][1], moe["experts"]))
     cases.append(("MoE fc2 down", mt, moe["down"][0], moe["down"][1], moe["experts"]))
+    # fc1 with SiLU(gate) * up quantized in its epilogue: N = 2F columns
+    # computed, F codes + F/128 scales per row stored
+    cases.append(("MoE fc1 gate_up + SiLU quant (fused)", mt, moe["gate_up"][0], moe["gate_up"][1], moe["experts"]))
     return cases
 
 
@@ -1223,10 +1226,17 @@ def gemm_profile():
             xq, xs = fb.quantize_act_per_token_group(x)
         del w, x
         y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+        fused = "fused" in label
+        if fused:
+            rows = torch.arange(m, dtype=torch.int32, device="cuda:0")
+            h = torch.empty((m, n // 2), dtype=torch.uint8, device="cuda:0")
+            hs = torch.empty((m, n // 2 // 128), dtype=torch.float32, device="cuda:0")
         torch.cuda.synchronize()
         for _ in range(GEMM_PROFILE_REPS):
             if frag:
                 fb.gemm_w8a8_blockscaled_frag(xq, xs, wq, ws, y)
+            elif fused:
+                fb.grouped_gemm_w8a8_blockscaled_gather_silu(xq, xs, rows, 1, wq, ws, offsets, h, hs)
             elif g:
                 fb.grouped_gemm_w8a8_blockscaled(xq, xs, wq, ws, offsets, y)
             else:
@@ -1307,7 +1317,8 @@ def gemm_counter_summary(d):
     for c, (label, m, n, k, g) in enumerate(cases):
         flops = 2.0 * m * n * k
         nb = -(-n // 128)
-        algo = m * k + (g or 1) * n * k + 2 * m * n + 4 * m * (k // 128) + 4 * (g or 1) * nb * (k // 128)
+        out_b = m * (n // 2) + 4 * m * (n // 256) + 4 * m if "fused" in label else 2 * m * n  # + gather index
+        algo = m * k + (g or 1) * n * k + out_b + 4 * m * (k // 128) + 4 * (g or 1) * nb * (k // 128)
         tf = flops / ns[c] / 1e3 if ns[c] else None
         ghz = grbm[c] / 8.0 / ns[c] if grbm[c] and ns[c] else None
         mb = busy[c] / (grbm[c] / 8.0 * 1024.0) if busy[c] is not None and grbm[c] else None

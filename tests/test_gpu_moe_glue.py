@@ -271,9 +271,12 @@ def _fused_case(T, k, E, H, F, seed, ids=None, rows=None):
 
 
 @pytest.mark.parametrize("T,k,E,H,F", [(1, 1, 2, 128, 128), (37, 4, 8, 384, 256), (300, 2, 5, 256, 384),
-                                       (513, 8, 16, 1024, 640)])
+                                       (513, 8, 16, 1024, 640),
+                                       # 10-16 K-blocks, one and several tiles per workgroup
+                                       (1, 1, 2, 1280, 128), (37, 4, 8, 1280, 256), (300, 2, 5, 1536, 384),
+                                       (700, 8, 6, 2048, 768), (2000, 8, 3, 1408, 256)])
 def test_fused_fc1_silu_matches_separate_kernels(T, k, E, H, F):
-    _fused_case(T, k, E, H, F, seed=90 + T)
+    _fused_case(T, k, E, H, F, seed=90 + T + H)
 
 
 def test_fused_fc1_silu_qwen3_30b_a3b():
@@ -282,10 +285,12 @@ def test_fused_fc1_silu_qwen3_30b_a3b():
     _fused_case(c["tokens"], c["top_k"], c["experts"], c["hidden"], c["ffn"], seed=70)
 
 
-def test_fused_fc1_silu_ragged_and_empty_experts_and_missing_rows():
+@pytest.mark.parametrize("H", [256, 2048])
+def test_fused_fc1_silu_ragged_and_empty_experts_and_missing_rows(H):
     """Experts with 0, 1, 129 and 300 rows, and gathered rows that name no
-    token (negative or past the token count: zero activation rows)."""
-    T, k, E, H, F = 250, 2, 6, 256, 256
+    token (negative or past the token count: zero activation rows); with
+    2 and 16 K-blocks."""
+    T, k, E, F = 250, 2, 6, 256
     counts = [0, 1, 129, 0, 300, 250 * 2 - 430]
     ids = np.repeat(np.arange(E), counts).astype(np.int32)
     ids = np.random.default_rng(3).permutation(ids).reshape(T, k)
