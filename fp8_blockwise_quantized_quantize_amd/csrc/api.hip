@@ -527,9 +527,9 @@ fp8bq_status grouped_gemm_w8a8_blockscaled_gather_silu(const uint8_t* a_fp8, con
       return FP8BQ_ERR_BAD_SHAPE;
     if (a_row_div < 1 || a_row_div > 0x7fffffffLL || G > 1024) return FP8BQ_ERR_BAD_SHAPE;
     int64_t ak, fk, gfk, mf;
-    if (!mul_ok(M_a, K, &ak) || !mul_ok(F + 128, K, &fk) || !mul_ok(2 * fk, G, &gfk) || !mul_ok(M_total, F, &mf))
-      return FP8BQ_ERR_BAD_SHAPE;
+    if (!mul_ok(M_a, K, &ak) || !mul_ok(F + 128, K, &fk) || !mul_ok(M_total, F, &mf)) return FP8BQ_ERR_BAD_SHAPE;
     if (ak >= (int64_t(1) << 31) || fk >= (int64_t(1) << 31)) return FP8BQ_ERR_BAD_SHAPE;
+    if (!mul_ok(2 * fk, G, &gfk)) return FP8BQ_ERR_BAD_SHAPE;  // 2 fk < 2^32: no overflow
     if (G > 0 && M_total + 128 * G > 0x7fffffffLL) return FP8BQ_ERR_BAD_SHAPE;
     if (mf == 0) return FP8BQ_OK;
     if (G == 0) return FP8BQ_ERR_BAD_SHAPE;  // rows to produce but no expert to own them

@@ -158,6 +158,20 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call("silu_mul_quantize_act", good, 4, 12, good, good, null, null) == 2  # F % 8
     assert _call("silu_mul_quantize_act", good, 4, 16, good, null, null, null) == 1
     assert _call("silu_mul_quantize_act", good, 4, 16, good, good, bad_align, null) == 3
+    # fc1 with the SiLU * up quantization in its epilogue: (a, a_scale, M_a, a_rows, a_row_div, w, w_scale,
+    # offsets, h, h_scale, M_total, F, K, G, stream)
+    silu = "grouped_gemm_w8a8_blockscaled_gather_silu"
+    assert _call(silu, good, good, 8, good, 1, good, good, good, good, good, 8, 256, 0, 2, null) == 2  # K = 0
+    assert _call(silu, good, good, 8, good, 1, good, good, good, good, good, 8, 192, 256, 2, null) == 2  # F % 128
+    assert _call(silu, good, good, 8, good, 1, good, good, good, good, good, 8, 256, 200, 2, null) == 2  # K % 128
+    assert _call(silu, good, good, 8, good, 1, good, good, good, good, good, 8, 256, 256, 1025, null) == 2  # G
+    assert _call(silu, good, good, 8, good, 0, good, good, good, good, good, 8, 256, 256, 2, null) == 2  # div
+    assert _call(silu, good, good, 8, good, 1, good, good, good, good, good, 8, 1 << 60, 256, 2, null) == 2
+    assert _call(silu, good, good, 8, good, 1, good, good, good, good, good, 8, 1 << 23, 256, 2, null) == 2
+    assert _call(silu, good, good, 8, good, 1, good, good, good, good, good, 8, 256, 256, 0, null) == 2  # no expert
+    assert _call(silu, good, good, 8, good, 1, good, good, good, null, good, 8, 256, 256, 2, null) == 1
+    assert _call(silu, good, good, 8, null, 1, good, good, good, good, good, 8, 256, 256, 2, null) == 1
+    assert _call(silu, good, good, 8, good, 1, good, good, good, bad_align, good, 8, 256, 256, 2, null) == 3
     assert _call("moe_combine", good, good, good, 4, 2, 12, 8, good, null) == 2  # H % 8
     assert _call("moe_combine", good, null, good, 4, 2, 16, 8, good, null) == 1
     assert _call("moe_combine", good, good, good, 4, 2, 16, 8, bad_align, null) == 3
@@ -176,6 +190,8 @@ def test_zero_sized_problems_are_no_ops():
     assert _call("moe_gather_quantize_act", null, null, 0, 5, 2, 256, null, null, null) == 0
     assert _call("silu_mul_quantize_act", null, 0, 768, null, null, null, null) == 0
     assert _call("moe_combine", null, null, null, 0, 8, 2048, 0, null, null) == 0
+    assert _call("grouped_gemm_w8a8_blockscaled_gather_silu", null, null, 0, null, 1, null, null, null, null, null,
+                 0, 768, 2048, 128, null) == 0
     assert _call("kv_cache_write_fp8", null, null, null, null, null, 1, null, null, 0, 8, 128, 0, null) == 0
 
 
