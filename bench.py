@@ -456,7 +456,7 @@ def detail(fb, dev, with_cpu=True):
     torch.cuda.empty_cache()
     # -- one MoE expert-FFN layer (Qwen3-30B-A3B: 4096 tokens, top-8 of 128
     #    experts, hidden 2048, expert FFN 768), every step on the GPU
-    res["moe_layer_qwen3_30b_a3b"] = moe_layer(fb, dev)
+    res["moe_layer_qwen3_30b_a3b"] = moe_layer(fb, dev, with_cpu)
     torch.cuda.empty_cache()
     # -- FP8 training operands (Qwen3-8B)
     res["train_operands_qwen3_8b"] = train_operands(fb, dev)
@@ -674,7 +674,7 @@ def prefill_gemms(fb, dev):
     return pre
 
 
-def moe_layer(fb, dev):
+def moe_layer(fb, dev, with_cpu=True):
     import torch
 
     from synthetic import MOE_QWEN3_30B_A3B, device_bf16_normal, moe_topk
@@ -685,8 +685,14 @@ def moe_layer(fb, dev):
     ids_h, tw_h = moe_topk(T, E, k, (70, 0))
     ids, tw = torch.from_numpy(ids_h).to(dev), torch.from_numpy(tw_h).to(dev)
     x = device_bf16_normal((T, H), 1.0, seed=700)
-    w1q, w1s = fb.quantize_weight_blockwise(device_bf16_normal((E, 2 * F, H), 0.02, seed=600))
-    w2q, w2s = fb.quantize_weight_blockwise(device_bf16_normal((E, H, F), 0.02, seed=601))
+    w1 = device_bf16_normal((E, 2 * F, H), 0.02, seed=600)
+    w2 = device_bf16_normal((E, H, F), 0.02, seed=601)
+    # the per-step re-quantization of every expert weight: both stacks in one launch
+    w1f, w2f = w1.view(E * 2 * F, H), w2.view(E * H, F)
+    (w1q, w1s), (w2q, w2s) = fb.quantize_weights_blockwise_multi([w1f, w2f])
+    req_out = [(w1q, w1s), (w2q, w2s)]
+    w1q, w1s = w1q.view(E, 2 * F, H), w1s.view(E, 2 * F // 128, H // 128)
+    w2q, w2s = w2q.view(E, H, F), w2s.view(E, H // 128, F // 128)
     off, sp, pr = fb.moe_sort_by_expert(ids, E)
     a, a_s = fb.quantize_act_per_token_group(x)
     y1 = torch.empty((R, 2 * F), dtype=torch.bfloat16, device=dev)
@@ -712,7 +718,9 @@ def moe_layer(fb, dev):
     silu_sets = copies(rotations(silu_b), y1, h, h_s)
     w2_sets = copies(rotations(w2_b), w2q, w2s, y2)
     comb_sets = copies(rotations(comb_b), y2, out)
+    req_b = (w1.numel() + w2.numel()) * 3 + (w1s.numel() + w2s.numel()) * 4
     steps = {
+        "expert_requant": ([lambda: fb.quantize_weights_blockwise_multi([w1f, w2f], req_out)], req_b, None),
         "sort": ([lambda: fb.moe_sort_by_expert(ids, E, off, sp, pr)], None, None),
         "act_quant": ([lambda t=t: fb.quantize_act_per_token_group(*t) for t in aq_sets], aq_b, None),
         "fc1_gate_up": ([lambda t=t: fb.grouped_gemm_w8a8_blockscaled_gather(a, a_s, sp, k, t[0], t[1], off, t[2])
@@ -731,7 +739,7 @@ def moe_layer(fb, dev):
     res, total = {}, 0.0
     for name, (fn, byt, flops) in steps.items():
         ms, _ = _time_graph_ms(fn)
-        if name != "fc1_silu_quant_fused":
+        if name not in ("fc1_silu_quant_fused", "expert_requant"):
             total += ms
         e = {"us": round(ms * 1e3, 1), "buffer_sets": len(fn)}
         if byt is not None:
@@ -760,7 +768,15 @@ def moe_layer(fb, dev):
     res["sum_of_kernels_us"] = round(total * 1e3, 1)
     res["layer_us"] = round(layer_ms * 1e3, 1)
     res["layer_separate_fc1_silu_us"] = round(sep_ms * 1e3, 1)
-    res["layer_TFLOPs"] = round((2 * R * 2 * F * H + 2 * R * H * F) / layer_ms / 1e9, 1)
+    layer_flops = 2 * R * 2 * F * H + 2 * R * H * F
+    res["layer_TFLOPs"] = round(layer_flops / layer_ms / 1e9, 1)
+    if with_cpu:
+        out = fb.moe_expert_ffn(x, ids, tw, w1q, w1s, w2q, w2s)
+        hq, hs = fb.grouped_gemm_w8a8_blockscaled_gather_silu(a, a_s, sp, k, w1q, w1s, off)
+        y2p = fb.grouped_gemm_w8a8_blockscaled(hq, hs, w2q, w2s, off)
+        torch.cuda.synchronize()
+        res["cpu_baseline"], res["parity"] = moe_cpu_and_parity(
+            x, ids_h, tw_h, w1, w2, w1q, w1s, w2q, w2s, off, sp, pr, out, hq, y2p, layer_flops, req_b)
     return res
 
 
@@ -1019,6 +1035,139 @@ def cpu_baseline_and_parity(fb, layers, w_bf16, sweep, gemm_flops):
     }
     par["pass"] = pp["pass"] and ps["pass"]
     return base, par
+
+
+MOE_PARITY_TOKENS = 16
+MOE_TIMING_EXPERTS = 2
+
+
+def moe_cpu_and_parity(x, ids, tw, w1, w2, w1q, w1s, w2q, w2s, off, sp, pr, out, hq, y2, layer_flops, req_bytes):
+    """The oracle on the MoE layer's input bytes.
+
+    Parity (as in the GPU tests' layer check): the routing sort of all pairs
+    (bit for bit); the weights of every expert used below, re-quantized by
+    the oracle (bit for bit against the GPU's codes and scales);
+    MOE_PARITY_TOKENS sampled tokens' whole chain (act quant, fc1,
+    SiLU(gate) * up and its 1x128 quantization, fc2, weighted combine)
+    against the GPU layer output: 1e-2 in Frobenius norm and
+    min(2^-4, 1/sqrt(F)) per element.  For all rows of MOE_TIMING_EXPERTS
+    sampled experts: the h codes (equal to the oracle's for >= 99% of them:
+    where the GPU's and the oracle's fc1 outputs, each within the GEMM bar,
+    round to BF16 differently, a code can sit one E4M3 step apart) and the
+    fc2 outputs in Frobenius norm (1e-2; a flipped code of a large h moves a
+    single fc2 row by more than the per-element bar, which holds for the
+    routing-weighted sum of a token's rows).
+
+    CPU baseline: the oracle's time for the sort, the act quant of all
+    tokens, the fc1 -> SiLU * up quant -> fc2 chain of all rows of the
+    sampled experts (scaled to all experts) and the combine of all pairs
+    (on host-drawn BF16 rows of the same shape); expert re-quant per
+    parameter, scaled to all experts."""
+    from oracle import dequant_act, dequant_weight, round_to_bf16_bits
+    from oracle.bf16 import bf16_bits_to_f64
+    from oracle.moe import combine, silu_mul_quantize, sort_by_expert
+
+    threads = host_threads()
+    T, H = x.shape
+    E, F, k = w1.shape[0], w2.shape[2], ids.shape[1]
+    bar = float(min(2.0 ** -4, 1.0 / np.sqrt(F)))
+
+    def layer_bar(y_bits, ref):
+        rep = _r14(y_bits, ref)
+        rep["pass"] = bool(rep["rel_fro"] <= 1e-2 and rep["rel_max"] <= bar)
+        rep["rel_max_bar"] = round(bar, 6)
+        return rep
+
+    t0 = time.perf_counter()
+    roff, rrows, rpr = sort_by_expert(ids, E)
+    t_sort = time.perf_counter() - t0
+    off_h, sp_h, pr_h = off.cpu().numpy(), sp.cpu().numpy(), pr.cpu().numpy()
+    sort_ok = bool(np.array_equal(off_h, roff) and np.array_equal(sp_h[:roff[-1]], rrows)
+                   and np.array_equal(pr_h, rpr))
+
+    rng = np.random.default_rng([70, 1])
+    toks = np.sort(rng.choice(T, size=MOE_PARITY_TOKENS, replace=False))
+    texp = np.sort(rng.choice(E, size=MOE_TIMING_EXPERTS, replace=False))
+    used = np.union1d(np.unique(ids[toks]), texp).astype(int)
+    t0 = time.perf_counter()
+    wo = {int(e): (oracle_quant_weight(_bits(w1[int(e)]), threads), oracle_quant_weight(_bits(w2[int(e)]), threads))
+          for e in used}
+    t_rq = time.perf_counter() - t0
+    req_ok = True
+    for e, pair in wo.items():
+        for (q, sc), gq, gs in zip(pair, (w1q[e], w2q[e]), (w1s[e], w2s[e])):
+            req_ok &= bool(np.array_equal(gq.cpu().numpy(), q)
+                           and np.array_equal(gs.cpu().numpy().view(np.uint32), sc.view(np.uint32)))
+
+    xb = _bits(x)
+    t0 = time.perf_counter()
+    aq, asc = oracle_quant_act(xb, threads)
+    t_aq = time.perf_counter() - t0
+
+    wd = {}
+
+    def fc_chain(e, rows_q, rows_s):
+        if e not in wd:
+            wd[e] = (dequant_weight(*wo[e][0]), dequant_weight(*wo[e][1]))
+        y1 = dequant_act(rows_q, rows_s) @ wd[e][0].T
+        h_q, h_s = silu_mul_quantize(round_to_bf16_bits(y1), F)
+        return h_q, round_to_bf16_bits(dequant_act(h_q, h_s) @ wd[e][1].T)
+
+    # the sampled experts: all their rows, timed
+    t0 = time.perf_counter()
+    ref_e = {}
+    for e in texp:
+        e = int(e)
+        tok = rrows[roff[e]:roff[e + 1]] // k
+        ref_e[e] = fc_chain(e, aq[tok], asc[tok])
+    t_ex = time.perf_counter() - t0
+    hq_h, y2_h = hq.cpu().numpy(), _bits(y2)
+    experts_rep = {}
+    for e, (h_ref, y_ref) in ref_e.items():
+        rep = _r14(y2_h[roff[e]:roff[e + 1]], bf16_bits_to_f64(y_ref))
+        same = float(np.mean(hq_h[roff[e]:roff[e + 1]] == h_ref))
+        rep.update({"h_codes_equal_frac": round(same, 5), "pass": bool(rep["rel_fro"] <= 1e-2 and same >= 0.99)})
+        experts_rep[str(e)] = rep
+
+    # the sampled tokens' whole chain against the layer output
+    ref = np.zeros((toks.size, H))
+    for j in range(k):
+        for t_i, t in enumerate(toks):
+            e = int(ids[t, j])
+            ref[t_i] += float(tw[t, j]) * bf16_bits_to_f64(fc_chain(e, aq[t:t + 1], asc[t:t + 1])[1][0])
+    layer_rep = layer_bar(_bits(out)[toks], ref)
+
+    # the combine of all pairs, on host-drawn BF16 rows (timing only)
+    yc = round_to_bf16_bits(np.random.default_rng([70, 2]).standard_normal((T * k, H)))
+    t0 = time.perf_counter()
+    combine(yc, rpr, tw)
+    t_comb = time.perf_counter() - t0
+
+    params_used = int(used.size) * (w1[0].numel() + w2[0].numel())
+    t_req_all = t_rq * (w1.numel() + w2.numel()) / params_used
+    t_layer = t_sort + t_aq + t_ex * E / texp.size + t_comb
+    base = {"value": round(layer_flops / t_layer / 1e12, 6), "unit": "TFLOP/s", "threads": threads,
+            "kind": "oracle",
+            "sample": ("MoE layer: sort of all %d pairs, act quant of all %d tokens, the fc1 -> SiLU*up quant -> "
+                       "fc2 chain of all rows of %d experts scaled to %d experts, combine of all pairs; expert "
+                       "re-quant of %d experts scaled to all %d by parameters"
+                       % (T * k, T, texp.size, E, used.size, E)),
+            "expert_requant_GBps": round(req_bytes / t_req_all / 1e9, 3),
+            "seconds": {"sort": round(t_sort, 3), "act_quant": round(t_aq, 3),
+                        "experts_sampled": round(t_ex, 3), "combine": round(t_comb, 3),
+                        "layer_extrapolated": round(t_layer, 3), "requant_sampled": round(t_rq, 3),
+                        "expert_requant_extrapolated": round(t_req_all, 3)}}
+    par = {"tokens": toks.tolist(), "experts": [int(e) for e in texp], "experts_requant_checked": int(used.size),
+           "sort_bitexact": sort_ok, "expert_requant_bitexact": req_ok, "fc2_rows_of_experts": experts_rep,
+           "layer_tokens": layer_rep}
+    par["pass"] = bool(sort_ok and req_ok and layer_rep["pass"] and all(r["pass"] for r in experts_rep.values()))
+    return base, par
+
+
+def torch_index(idx, device):
+    import torch
+
+    return torch.from_numpy(np.asarray(idx, np.int64)).to(device)
 
 
 def decode_cpu_and_parity(layers, m, flops):
