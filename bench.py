@@ -459,14 +459,14 @@ def detail(fb, dev, with_cpu=True):
     res["moe_layer_qwen3_30b_a3b"] = moe_layer(fb, dev, with_cpu)
     torch.cuda.empty_cache()
     # -- FP8 training operands (Qwen3-8B)
-    res["train_operands_qwen3_8b"] = train_operands(fb, dev)
+    res["train_operands_qwen3_8b"] = train_operands(fb, dev, with_cpu)
     torch.cuda.empty_cache()
     # -- FP8 KV cache, one Qwen3-8B layer (8 KV heads x 128)
-    res["kv_cache_qwen3_8b_layer"] = kv_cache(fb, dev)
+    res["kv_cache_qwen3_8b_layer"] = kv_cache(fb, dev, with_cpu)
     torch.cuda.empty_cache()
     # -- token-level TIS weights of one training batch (512 responses padded
     #    to 20,000 tokens), fused with the response mask and w * advantage
-    res["tis_weights_train_batch_512x20000"] = tis_weights(fb, dev)
+    res["tis_weights_train_batch_512x20000"] = tis_weights(fb, dev, with_cpu)
     torch.cuda.empty_cache()
     return res
 
@@ -780,7 +780,7 @@ def moe_layer(fb, dev, with_cpu=True):
     return res
 
 
-def train_operands(fb, dev):
+def train_operands(fb, dev, with_cpu=True):
     import torch
 
     from synthetic import LAYER_SHAPES_QWEN3_8B, device_bf16_normal
@@ -800,6 +800,14 @@ def train_operands(fb, dev):
     ms, _ = _time_ms(sweep, reps=5, warm=1)
     res["weight_dual_sweep_36_layers"] = {"bytes": wbytes, "ms": round(ms, 3), "GBps": round(wbytes / ms / 1e6, 1),
                                           "frac_hbm": round(wbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+    checks = []  # (label, BF16 input, GPU outputs) for the oracle leg
+    if with_cpu:
+        for (name, n, k), w in zip(LAYER_SHAPES_QWEN3_8B, bufs):
+            (q, sq), (qt, sqt) = fb.quantize_weight_blockwise_dual(w)
+            for layer in (35, 0):  # the last layer lies past 2^31 bytes into the batch
+                checks.append(("W %s layer %d" % (name, layer), _bits(w[layer]),
+                               [t[layer].cpu().numpy() for t in (q, sq, qt, sqt)]))
+            del q, sq, qt, sqt
     del bufs
     torch.cuda.empty_cache()
     M = 8192
@@ -811,11 +819,16 @@ def train_operands(fb, dev):
         del xs
         res[f"act_dual_{M}x{k}"] = {"us": round(ms * 1e3, 1), "bytes": byt, "GBps": round(byt / ms / 1e6, 1),
                                     "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        if with_cpu:
+            (q, sq), (qt, sqt) = fb.quantize_act_dual(x)
+            checks.append(("x %dx%d" % (M, k), _bits(x), [t.cpu().numpy() for t in (q, sq, qt, sqt)]))
         del x
+    if with_cpu:
+        res["cpu_baseline"], res["parity"] = train_cpu_and_parity(checks)
     return res
 
 
-def kv_cache(fb, dev):
+def kv_cache(fb, dev, with_cpu=True):
     import torch
 
     from synthetic import device_bf16_normal
@@ -847,6 +860,14 @@ def kv_cache(fb, dev):
                      "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBPS, 4)}
     # 9.4 MB per call: latency-bound, reported in microseconds only
     res["decode_write_1536"] = {"us": round(dec_ms * 1e3, 1), "bytes": 2 * B * H * D * 3 + B * 4}
+    if with_cpu:  # one calibration, the prefill write and the decode write, then the oracle
+        fb.kv_scale_calibrate(k, v, True, ks, vs)
+        fb.kv_cache_write_fp8(k, v, slots, ks, vs, kc, vc)
+        fb.kv_cache_write_fp8(kn, vn, dslots, ks, vs, kc, vc)
+        torch.cuda.synchronize()
+        res["cpu_baseline"], res["parity"] = kv_cpu_and_parity(
+            [_bits(t) for t in (k, v, kn, vn)], ks.cpu().numpy(), vs.cpu().numpy(), kc.cpu().numpy(),
+            vc.cpu().numpy(), cal_b, wr_b)
     return res
 
 
@@ -857,7 +878,7 @@ def importance_weight_bytes(slots, valid):
     return 12 * valid + 9 * slots
 
 
-def tis_weights(fb, dev):
+def tis_weights(fb, dev, with_cpu=True):
     import torch
 
     from synthetic import ROLLOUT_TRAIN_BATCH, rollout_batch
@@ -873,8 +894,12 @@ def tis_weights(fb, dev):
                                                                     advantages=t[3], out=t[4], out_adv=t[5])
                             for t in sets])
     gbps = byt / ms / 1e6
-    return {"tokens": valid, "slots": slots, "bytes": byt, "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
-            "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
+    res = {"tokens": valid, "slots": slots, "bytes": byt, "us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
+           "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
+    if with_cpu:
+        w, wa = fb.token_importance_weights(lt, lr, C=2.0, mode="tis", mask=msk, advantages=adv)
+        res["cpu_baseline"], res["parity"] = tis_cpu_and_parity(rb, w.cpu().numpy(), wa.cpu().numpy(), byt)
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -1034,6 +1059,92 @@ def cpu_baseline_and_parity(fb, layers, w_bf16, sweep, gemm_flops):
                           if i.get("user_api") == "blas"]},
     }
     par["pass"] = pp["pass"] and ps["pass"]
+    return base, par
+
+
+def train_cpu_and_parity(checks):
+    """The oracle's dual quantizers on the same input bytes: W and W^T of the
+    last and first layer of every projection from the 36-layer batch calls,
+    and both activations' x and x^T, all compared bit for bit (codes and
+    scale bits).  Its time per byte of algorithmic traffic is the baseline."""
+    from oracle.train import quant_act_dual
+
+    threads = host_threads()
+    ok, t_w, t_x, b_w, b_x = {}, 0.0, 0.0, 0, 0
+    for label, xb, gpu in checks:
+        t0 = time.perf_counter()
+        if label.startswith("W"):  # quant_weight_blockwise_dual: W and W^T, block rows on the thread pool
+            ref = oracle_quant_weight(xb, threads) + oracle_quant_weight(np.ascontiguousarray(xb.T), threads)
+            t_w += time.perf_counter() - t0
+            b_w += xb.size * 4 + sum(r.size * 4 for r in ref[1::2])
+        else:
+            ref = sum(quant_act_dual(xb), ())
+            t_x += time.perf_counter() - t0
+            b_x += xb.size * 4 + sum(r.size * 4 for r in ref[1::2])
+        ok[label] = bool(all(np.array_equal(g.view(np.uint32) if g.dtype == np.float32 else g,
+                                            r.view(np.uint32) if r.dtype == np.float32 else r)
+                             for g, r in zip(gpu, ref)))
+    base = {"kind": "oracle", "threads": threads, "unit": "GB/s",
+            "sample": "layers 35 and 0 of each projection (W and W^T), both activations (x and x^T)",
+            "weight_dual_GBps": round(b_w / t_w / 1e9, 3) if t_w else None,
+            "act_dual_GBps": round(b_x / t_x / 1e9, 3) if t_x else None,
+            "seconds": {"weights": round(t_w, 3), "activations": round(t_x, 3)}}
+    return base, {"bitexact": ok, "pass": all(ok.values())}
+
+
+def kv_cpu_and_parity(bits, ks, vs, kc, vc, cal_bytes, wr_bytes):
+    """The oracle's per-head K and V calibration over all 16,384 tokens
+    (scales bit for bit), the prefill write of those tokens into slots
+    0..T-1 and the decode write of 1,536 more tokens after them (every
+    cache byte compared, with the oracle's own scales)."""
+    from oracle.kv import kv_calibrate, kv_quantize
+
+    k, v, kn, vn = bits
+    T = k.shape[0]
+    t0 = time.perf_counter()
+    rks, rvs = kv_calibrate(k, True), kv_calibrate(v, True)
+    t_cal = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    rkc, rvc = kv_quantize(k, rks, True), kv_quantize(v, rvs, True)
+    t_wr = time.perf_counter() - t0
+    rkd, rvd = kv_quantize(kn, rks, True), kv_quantize(vn, rvs, True)
+    par = {"scales_bitexact": bool(np.array_equal(ks.view(np.uint32), rks.view(np.uint32))
+                                   and np.array_equal(vs.view(np.uint32), rvs.view(np.uint32))),
+           "prefill_write_bitexact": bool(np.array_equal(kc[:T], rkc) and np.array_equal(vc[:T], rvc)),
+           "decode_write_bitexact": bool(np.array_equal(kc[T:], rkd) and np.array_equal(vc[T:], rvd))}
+    par["pass"] = all(par.values())
+    base = {"kind": "oracle", "threads": 1, "unit": "GB/s", "sample": "the whole calibration and prefill write",
+            "calibrate_GBps": round(cal_bytes / t_cal / 1e9, 3), "write_GBps": round(wr_bytes / t_wr / 1e9, 3),
+            "seconds": {"calibrate": round(t_cal, 3), "write": round(t_wr, 3)}}
+    return base, par
+
+
+def tis_cpu_and_parity(rb, w, wa, byt):
+    """The oracle's TIS weights of the whole batch: every slot's w within
+    2 ulp and w * A within 6 ulp of the oracle's correctly rounded values,
+    NaN, zero and infinity positions identical (the GPU tests' bar)."""
+    from oracle.tis import TIS, importance_weights
+
+    t0 = time.perf_counter()
+    rw, rwa = importance_weights(rb["logp_train"], rb["logp_rollout"], C=2.0, mode=TIS, mask=rb["mask"],
+                                 advantages=rb["advantages"])
+    t = time.perf_counter() - t0
+
+    def ulps(g, r):
+        g, r = np.asarray(g, np.float32), np.asarray(r, np.float32)
+        same_special = bool(np.array_equal(np.isnan(g), np.isnan(r)) and np.array_equal(g == 0, r == 0)
+                            and np.array_equal(g[np.isinf(r)], r[np.isinf(r)]))
+        fin = np.isfinite(r) & ~np.isnan(r)
+        err = np.abs(g[fin].astype(np.float64) - r[fin]) / np.maximum(
+            np.spacing(np.abs(r[fin])).astype(np.float64), 2.0 ** -149)
+        return same_special, float(err.max()) if err.size else 0.0
+
+    sw, ew = ulps(w, rw)
+    sa, ea = ulps(wa, rwa)
+    par = {"w_max_ulp": round(ew, 3), "wA_max_ulp": round(ea, 3), "special_values_equal": sw and sa}
+    par["pass"] = bool(sw and sa and ew <= 2.0 and ea <= 6.0)
+    base = {"kind": "oracle", "threads": 1, "unit": "GB/s", "sample": "the whole batch",
+            "value": round(byt / t / 1e9, 3), "seconds": round(t, 3)}
     return base, par
 
 
