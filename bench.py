@@ -307,6 +307,11 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_detail:
         out["detail"] = detail(fb, dev, with_cpu=not args.no_cpu)
+        legs = {name: leg["parity"]["pass"] for name, leg in out["detail"].items()
+                if isinstance(leg, dict) and isinstance(leg.get("parity"), dict) and "pass" in leg["parity"]}
+        if legs and isinstance(out.get("parity"), dict):
+            out["parity"]["detail"] = legs
+            out["parity"]["pass"] = bool(out["parity"].get("pass", True) and all(legs.values()))
     print(json.dumps(out), flush=True)
 
 
@@ -671,6 +676,10 @@ def prefill_gemms(fb, dev):
     for key, label in (("row", ""), ("afrag", "afrag_"), ("frag", "frag_")):
         pre["all4"][label + "TFLOPs"] = round(tot_f / tot[key] / 1e9, 1)
         pre["all4"][label + "frac_fp8_peak"] = round(tot_f / tot[key] / 1e9 / FP8_PEAK_TFLOPS, 4)
+    # the three layouts' outputs, bit for bit (the fragment-order form is the
+    # headline's, whose outputs the headline parity checks against the oracle)
+    same = all(e["bit_identical"] for nm, e in pre.items() if nm != "all4")
+    pre["parity"] = {"layouts_bit_identical": same, "pass": same}
     return pre
 
 
