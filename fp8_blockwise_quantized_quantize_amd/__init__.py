@@ -208,7 +208,7 @@ def _cdiv(a, b):
 # Tile kernels of the GEMMs by name (FP8BQ_TILE_* of the C ABI), for tests
 # and diagnostics; None (or "auto") is the library's own choice.
 TILES = {"auto": 0, "skinny64": 1, "skinny48": 2, "wide": 3, "decode_panel": 4, "deep": 5, "panel192": 6,
-         "deep_persistent": 7}
+         "deep_persistent": 7, "skinny96": 8}
 
 
 def _tile_id(tile):

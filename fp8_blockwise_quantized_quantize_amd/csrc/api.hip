@@ -297,7 +297,8 @@ fp8bq_status gemm_w8a8_blockscaled_tile(const uint8_t* a_fp8, const float* a_sca
                                         const float* w_scale, uint16_t* y_bf16, int64_t M, int64_t N, int64_t K,
                                         int tile, void* stream) {
   try {
-    if (tile < FP8BQ_TILE_AUTO || tile > FP8BQ_TILE_PANEL192) return FP8BQ_ERR_BAD_ARG;
+    if (tile < FP8BQ_TILE_AUTO || (tile > FP8BQ_TILE_PANEL192 && tile != FP8BQ_TILE_SKINNY96))
+      return FP8BQ_ERR_BAD_ARG;
     if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || K > kMaxGemmK) return FP8BQ_ERR_BAD_SHAPE;
     int64_t mk, nk, mn, bytes;
     if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, &mn) || !mul_ok(mn, 2, &bytes))

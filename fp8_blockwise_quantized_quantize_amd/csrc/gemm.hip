@@ -1329,7 +1329,7 @@ __global__ __launch_bounds__(threads_of<Kern>(), Kern::kWavesPerSimd) void gemm_
   Kern::template run_persistent<kGather>(ntiles, tile_at, smem);
 }
 
-enum class Cfg { kSkinny64x64, kSkinny48x64, kWide, kDecodePanel, kDeep, kPanel192 };
+enum class Cfg { kSkinny64x64, kSkinny48x64, kWide, kDecodePanel, kDeep, kPanel192, kSkinny96x64 };
 
 // Per-workgroup cycle estimate: operand bytes through L1 (64 B/clk/CU) vs
 // FP8 MFMA (8192 FLOP/clk/CU), times the rounds of workgroups over the CUs.
@@ -1347,12 +1347,27 @@ double cu_count() {
   return n > 0 ? (double)n : 256.0;
 }
 
+// Skinny tiles 64 or 48 weight rows wide: whichever fills its rounds of one
+// workgroup per CU more evenly (tiles / (rounds * CUs)); ties keep 64.  At
+// M = 256 the 48-row tile gives qkv (N = 6144) 512 tiles, two per CU, where
+// the 64-row one gives 384 (19.7 vs 21.7 us); o and down (N = 4096) stay at
+// 256 tiles of 64 rows.
+Cfg skinny_narrow(int64_t M, int64_t N) {
+  const double cus = cu_count();
+  auto fill = [&](int bn) {
+    const double t = (double)((N + bn - 1) / bn) * (double)((M + 63) / 64);
+    return t / (std::ceil(t / cus) * cus);
+  };
+  return fill(48) > fill(64) ? Cfg::kSkinny48x64 : Cfg::kSkinny64x64;
+}
+
 Cfg choose(int64_t M, int64_t N, int64_t K) {
   const double cus = cu_count();
   // Few activation rows (65 .. 256) but many weight rows: one 128 x 256
   // panel covers every row of the activation panel, so each weight row is
-  // read once.  At M <= 64 the 48-row K-split tile is faster (Qwen3-8B
-  // gate_up, M = 64: 27.7 vs 33.9 us).
+  // read once.  At M <= 64 the K-split skinny tiles are faster (Qwen3-8B
+  // gate_up, M = 64: 24.2 us on the 96-row tile, 27.7 on the 48-row one,
+  // 33.9 on the panel).
   if (M > 64 && M <= DecodePanel::BM && (N + DecodePanel::BN - 1) / DecodePanel::BN >= (int64_t)(0.625 * cus)) {
     // the 192 x 128 panel when its tiles fill 7/8 or more of the CUs in one round
     const int64_t t192 = ((N + Panel192::BN - 1) / Panel192::BN) * ((M + Panel192::BM - 1) / Panel192::BM);
@@ -1363,16 +1378,19 @@ Cfg choose(int64_t M, int64_t N, int64_t K) {
   Cfg c = Cfg::kWide;
   const double s64 = est_cycles(M, N, K, 64, 64, cus) * 1.05;  // partial-tile reduction overhead
   if (s64 < best) {
-    // Skinny tiles 64 or 48 weight rows wide: whichever fills its rounds of
-    // one workgroup per CU more evenly (tiles / (rounds * CUs)); ties keep 64.
-    // At M = 256 the 48-row tile gives qkv (N = 6144) 512 tiles, two per CU,
-    // where the 64-row one gives 384 (19.7 vs 21.7 us); o and down (N =
-    // 4096) stay at 256 tiles of 64 rows.
-    auto fill = [&](int bn) {
-      const double t = (double)((N + bn - 1) / bn) * (double)((M + 63) / 64);
-      return t / (std::ceil(t / cus) * cus);
-    };
-    c = fill(48) > fill(64) ? Cfg::kSkinny48x64 : Cfg::kSkinny64x64;
+    auto tiles = [&](int bn) { return (double)((N + bn - 1) / bn) * (double)((M + 63) / 64); };
+    c = skinny_narrow(M, N);
+    // The 96-row tile moves (96 + 64) K bytes per tile against (48 + 64) K
+    // or (64 + 64) K, but runs one wave per SIMD: it pays when its tiles
+    // fill the CUs and its rounds x bytes per tile come out smaller.  At
+    // M = 256 qkv (N = 6144) takes 256 tiles of 96 rows (one round) instead
+    // of 512 of 48 (15.4 vs 19.1 us); at M = 64 gate_up (N = 24576) 256
+    // instead of 512 (24.2 vs 28.3 us).  Fewer tiles than CUs lose (M = 128,
+    // N = 6144: 14.8 vs 11.8 us).
+    const int bn = c == Cfg::kSkinny48x64 ? 48 : 64;
+    const double r96 = std::ceil(tiles(96) / cus) * (96 + 64);
+    const double rc = std::ceil(tiles(bn) / cus) * (bn + 64);
+    if (tiles(96) >= 0.875 * cus && r96 < rc) c = Cfg::kSkinny96x64;
   }
   return c;
 }
@@ -1398,6 +1416,7 @@ bool tile_cfg(int tile, int64_t M, int64_t N, int64_t K, Cfg* c) {
     case 4: *c = Cfg::kDecodePanel; return true;
     case 5: *c = Cfg::kDeep; return true;
     case 6: *c = Cfg::kPanel192; return true;
+    case 8: *c = Cfg::kSkinny96x64; return true;
     default: return false;
   }
 }
@@ -1467,11 +1486,18 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
   if (M == 0 || N == 0) return hipSuccess;
   Cfg cfg;
   if (!tile_cfg(tile, M, N, K, &cfg)) return hipErrorInvalidValue;
+  // Row-major operands stage both tiles through LDS; at 96 weight rows that
+  // form holds more than its registers (qkv at M = 256: 21.5 vs 20.0 us on
+  // the 48-row tile), so the cost model's 96-row choice runs as 48 / 64
+  // here.  Every skinny width sums in the same order: the same bits.
+  if (tile == 0 && cfg == Cfg::kSkinny96x64) cfg = skinny_narrow(M, N);
   switch (cfg) {
     case Cfg::kSkinny64x64:
       return launch_dense_cfg<Skinny<64, 64, 4>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kSkinny48x64:
       return launch_dense_cfg<Skinny<48, 64, 4>, 48, 64>(a, sa, w, sw, y, M, N, K, stream);
+    case Cfg::kSkinny96x64:
+      return launch_dense_cfg<Skinny<96, 64, 4>, 96, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kDecodePanel:
       return launch_dense_cfg<DecodePanel, DecodePanel::BN, DecodePanel::BM>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kPanel192:
@@ -1605,6 +1631,8 @@ hipError_t launch_gemm_frag_cfg(Cfg cfg, const uint8_t* a, const float* sa, cons
       return launch_dense_cfg<Skinny<64, 64, 4, true, kW>, 64, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kSkinny48x64:
       return launch_dense_cfg<Skinny<48, 64, 4, true, kW>, 48, 64>(a, sa, w, sw, y, M, N, K, stream);
+    case Cfg::kSkinny96x64:
+      return launch_dense_cfg<Skinny<96, 64, 4, true, kW>, 96, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kPanel192:
       return launch_dense_cfg<PanelFragA<Panel<192, 128, 2, 4, 3, kW>>, 192, 128>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kDecodePanel:

@@ -206,9 +206,9 @@ fp8bq_status gemm_w8a8_blockscaled(const uint8_t* a_fp8, const float* a_scale, c
 /*
  * Tile kernels of the GEMMs, for tests and diagnostics (the *_tile entry
  * points).  FP8BQ_TILE_AUTO is the choice the plain entry points make.
- *   dense:   SKINNY64, SKINNY48 (K split over the 4 waves of a 64 / 48 x 64
- *            tile), WIDE (256 x 256), DECODE_PANEL (128 x 256), DEEP
- *            (256 x 128, three stages), PANEL192 (192 x 128)
+ *   dense:   SKINNY64, SKINNY48, SKINNY96 (K split over the 4 waves of a
+ *            64 / 48 / 96 x 64 tile), WIDE (256 x 256), DECODE_PANEL
+ *            (128 x 256), DEEP (256 x 128, three stages), PANEL192 (192 x 128)
  *   grouped: WIDE, DECODE_PANEL, DEEP (one workgroup per tile),
  *            DEEP_PERSISTENT (one workgroup per CU; the default, used for
  *            G <= 1024 only, above that the per-tile DEEP kernel runs)
@@ -221,7 +221,8 @@ enum {
   FP8BQ_TILE_DECODE_PANEL = 4,
   FP8BQ_TILE_DEEP = 5,
   FP8BQ_TILE_PANEL192 = 6,
-  FP8BQ_TILE_DEEP_PERSISTENT = 7
+  FP8BQ_TILE_DEEP_PERSISTENT = 7,
+  FP8BQ_TILE_SKINNY96 = 8
 };
 
 /*

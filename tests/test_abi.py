@@ -147,6 +147,9 @@ def test_argument_errors_are_reported_before_any_launch():
     assert _call(kw, good, good, good, good, good, 1, good, good, 4, 8, 128, 1 << 31, null) == 2
     assert _call(kw, good, good, null, good, good, 1, good, good, 4, 8, 128, 16, null) == 1
     assert _call(kw, good, good, good, good, good, 1, bad_align, good, 4, 8, 128, 16, null) == 3
+    # named tile kernels: the grouped-only DEEP_PERSISTENT (7) and unknown ids are rejected for dense GEMMs
+    for tile in (-1, 7, 9):
+        assert _call("gemm_w8a8_blockscaled_tile", good, good, good, good, good, 4, 4, 128, tile, null) == 6
     # MoE glue
     assert _call("moe_sort_by_expert", good, 4, 2, 0, good, good, good, null) == 2      # no expert
     assert _call("moe_sort_by_expert", good, 1 << 20, 1 << 12, 8, good, good, good, null) == 2  # > 2^31 pairs

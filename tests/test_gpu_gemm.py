@@ -71,7 +71,7 @@ def test_gemm_ragged(fb, m, n, k):
     assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw), oracle.gemm_ref(qa, sa, qw, sw))
 
 
-TILES = ["skinny64", "skinny48", "wide", "decode_panel", "deep", "panel192"]
+TILES = ["skinny64", "skinny48", "skinny96", "wide", "decode_panel", "deep", "panel192"]
 
 
 @pytest.mark.parametrize("tile", TILES)
