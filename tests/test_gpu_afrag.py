@@ -79,14 +79,17 @@ def test_quantizer_frag_multi_shape_errors(fb, m, k):
 @pytest.mark.parametrize("m,n,k", [(16, 130, 256), (48, 384, 768), (272, 520, 512), (272, 528, 512),
                                    (256, 256, 2048), (80, 20480, 256), (208, 24576, 256),
                                    (32, 256, 384), (512, 512, 640), (144, 24576, 128), (208, 24576, 384),
-                                   (80, 20480, 384)])
+                                   (80, 20480, 384), (256, 6128, 512), (64, 24560, 384), (208, 6144, 640)])
 def test_gemm_afrag_against_oracle_and_row_major(fb, m, n, k):
-    """Every tile form: 64- and 48-row K-split tiles, the 256 x 256 panel,
-    the 128 x 256 decode panel (M = 80: one ragged tile of activation rows)
-    and the 192 x 128 panel (M = 208: a second, ragged row tile).  Where
-    N % 16 == 0 the same product with the weights in fragment order too
-    (N = 528: a ragged last weight scale block of 16 rows).  K = 128, 384 and
-    640: odd numbers of K-blocks on every tile form."""
+    """Every tile form: 64-, 48- and 96-row K-split tiles, the 256 x 256
+    panel, the 128 x 256 decode panel (M = 80: one ragged tile of activation
+    rows) and the 192 x 128 panel (M = 208: a second, ragged row tile).
+    N = 6128 and 24560 put an 80-row last tile on the 96-row skinny tile (the
+    row-major form runs the 48-row one there: the same bits), M = 208 a
+    ragged row tile on it.  Where N % 16 == 0 the same product with the
+    weights in fragment order too (N = 528: a ragged last weight scale block
+    of 16 rows).  K = 128, 384 and 640: odd numbers of K-blocks on every tile
+    form."""
     announce("afrag gemm", m, n, k)
     x, _ = activations(m, k, (m, n, k, 0))
     w = bf16_normal((n, k), 0.02, (m, n, k, 1))
