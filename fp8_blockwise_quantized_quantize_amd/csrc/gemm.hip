@@ -16,12 +16,13 @@
 //
 // Two tile kernels share that inner step:
 //
-//  * skinny<64 or 48, 64> (few activation rows, e.g. decode with M = 256):
-//    a 64 (or 48) x 64 output tile per 4-wave workgroup; the four waves split the
-//    K-blocks (wave w takes kb = w, w+4, ...).  Each wave stages its own
-//    K-blocks through a private LDS slice (coalesced 16-byte loads into
-//    registers one K-block ahead, ds_write, fragment reads), and the four
-//    partial tiles are summed through LDS at the end.
+//  * skinny<64, 48 or 96, 64> (few activation rows, e.g. decode with
+//    M = 256): a 64 (48, 96) x 64 output tile per 4-wave workgroup; the four
+//    waves split the K-blocks (wave w takes kb = w, w+4, ...).  Row-major
+//    operands are staged through each wave's private LDS slice (coalesced
+//    16-byte loads into registers one K-block ahead, ds_write, fragment
+//    reads); fragment-order operands are loaded straight into the MFMA's
+//    registers.  The four partial tiles are summed through LDS at the end.
 //
 //  * panel<BN, BM, ..., S> (many rows: prefill with a 256 x 256 tile, two
 //    stages; MoE experts with a 256 x 128 tile, three stages; decode with
