@@ -71,13 +71,23 @@ PHASE_KERNELS = {
 PHASE_LAUNCHES = {"act_quant": 4, "gemm": 4, "requant": 4}
 
 
+def _code_only(text):
+    """C++ source with its comments removed and whitespace runs collapsed
+    (what the compiler sees; the kernel sources hold no string literal
+    that contains a comment marker)."""
+    text = re.sub(r"//[^\n]*|/\*.*?\*/", " ", text, flags=re.S)
+    return " ".join(text.split())
+
+
 def source_sha(fname):
-    """SHA-256 of a kernel source plus every shared device header."""
+    """SHA-256 of a kernel source plus every shared device header, comments
+    and whitespace aside (editing a comment does not change the kernel the
+    counters were taken on)."""
     h = hashlib.sha256()
     headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
     for f in (fname, *headers):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
