@@ -1217,7 +1217,8 @@ def moe_cpu_and_parity(x, ids, tw, w1, w2, w1q, w1s, w2q, w2s, off, sp, pr, out,
 
     rng = np.random.default_rng([70, 1])
     toks = np.sort(rng.choice(T, size=MOE_PARITY_TOKENS, replace=False))
-    texp = np.sort(rng.choice(E, size=MOE_TIMING_EXPERTS, replace=False))
+    busy = np.nonzero(np.diff(roff) > 0)[0]  # experts with routed rows
+    texp = np.sort(rng.choice(busy, size=min(MOE_TIMING_EXPERTS, busy.size), replace=False))
     used = np.union1d(np.unique(ids[toks]), texp).astype(int)
     t0 = time.perf_counter()
     wo = {int(e): (oracle_quant_weight(_bits(w1[int(e)]), threads), oracle_quant_weight(_bits(w2[int(e)]), threads))
