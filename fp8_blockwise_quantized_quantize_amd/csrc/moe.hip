@@ -32,7 +32,9 @@ namespace {
 // i * 64 + l of the segment).  Pass 1 counts the pairs below e; pass 2
 // ranks e's pairs inside the segment from one ballot per load (pair order
 // is (i, l) order) and across segments from the waves' totals, so rows keep
-// pair order.  Every workgroup reads the whole id list, which stays in L2.
+// pair order.  Every workgroup reads the whole id list, which stays in L2;
+// when the pairs fit one round (up to kSortRound, e.g. 4096 tokens x top-8)
+// both passes come from one read of it.
 // ---------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
@@ -66,9 +68,55 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* _
                                                                 int32_t* __restrict__ sorted_pair,
                                                                 int32_t* __restrict__ pair_row) {
   __shared__ int32_t part[kSortWaves];
+  __shared__ int32_t part2[kSortWaves];
   const int32_t e = static_cast<int32_t>(blockIdx.x);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  if (P <= kSortRound) {  // one round: both counts and the ranks from one read of the ids
+    const int32_t seg = wave * kSortSegment;
+    int32_t id[kSortRun];
+    load_segment(ids, seg, lane, P, id);
+    uint64_t mask[kSortRun];
+    int below = 0;
+    int32_t count = 0;  // e's pairs in this wave's segment (wave-uniform)
+#pragma unroll
+    for (int i = 0; i < kSortRun; ++i) {
+      below += (id[i] >= 0 && id[i] < e) ? 1 : 0;
+      mask[i] = __ballot(id[i] == e);
+      count += __popcll(mask[i]);
+    }
+    below = wave_sum_i32(below);
+    if (lane == 0) {
+      part[wave] = below;
+      part2[wave] = count;
+    }
+    __syncthreads();
+    int32_t first = 0, before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) {
+      first += part[w];
+      before += (w < wave) ? part2[w] : 0;
+      total += part2[w];
+    }
+    int32_t r = first + before;
+#pragma unroll
+    for (int i = 0; i < kSortRun; ++i) {
+      const int32_t p = seg + i * 64 + lane;
+      if (id[i] == e) {
+        const int32_t row = r + static_cast<int32_t>(lanes_below(mask[i]));
+        sorted_pair[row] = p;
+        pair_row[p] = row;
+      }
+      if (e == 0 && p < P && (id[i] < 0 || id[i] >= E)) pair_row[p] = -1;  // no expert, no row
+      r += __popcll(mask[i]);
+    }
+    if (tid == 0) {
+      offsets[e] = first;
+      if (e == E - 1) offsets[E] = first + total;
+    }
+    return;
+  }
 
   int below = 0;
   for (int32_t base = 0; base < P; base += kSortRound) {

@@ -45,7 +45,7 @@ def bf16(a):
 
 # ---------------------------------------------------------------- sort
 @pytest.mark.parametrize("T,k,E", [(0, 8, 4), (1, 1, 1), (7, 2, 3), (513, 8, 128), (4096, 8, 128), (1000, 4, 300),
-                                   (3000, 6, 1)])
+                                   (3000, 6, 1), (5000, 8, 64), (20000, 8, 128)])
 def test_sort_router_ids(T, k, E):
     announce("moe sort", T, k, E)
     ids, _ = moe_topk(T, E, min(k, E), (90, T)) if T else (np.zeros((0, k), np.int32), None)
