@@ -950,14 +950,60 @@ struct Panel {
     // up accumulators of columns 64 wn + 16 i + 4 g + r (fragments i and
     // i + 4, i, r < 4).  Each is rounded to BF16 (the fc1 output the
     // unfused chain would store), h = SiLU(gate) * up is rounded to BF16
-    // exactly (silu_mul_bf16), and the row's 1x128 group (the columns of
-    // both waves wn = 0, 1) is quantized: amax over the wave's lanes by
-    // shuffles, across the two waves through LDS, s = fl32(amax / 448),
-    // codes E4M3(fl32(h / s)).
+    // exactly (silu_mul_bf16's result: its float32 path for all 32 values,
+    // then its float64 decision for the values that path leaves open), and
+    // the row's 1x128 group (the columns of both waves wn = 0, 1) is
+    // quantized: amax over the wave's lanes by shuffles, across the two
+    // waves through LDS, s = fl32(amax / 448), codes E4M3(fl32(h / s)).
     auto silu_epilogue = [&](const Tile& t) {
       const int64_t F = t.N / 2;
+      static_assert(4 * TM * 4 <= 32, "one deferral bit per value");
       uint32_t hb[4][TM][4];
       uint32_t mx[TM];
+      // The float32 path for every value first, with no branch; values it
+      // cannot settle are marked in `defer` (bit (i TM + j) 4 + r).
+      uint32_t defer = 0;
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gv = __uint_as_float(bf16_rne(acc[i][j][r]) << 16);
+            const float uv = __uint_as_float(bf16_rne(acc[i + 4][j][r]) << 16);
+            bool ok;
+            hb[i][j][r] = silu_mul_bf16_fast(gv, uv, &ok);
+            defer |= ok ? 0u : 1u << ((i * TM + j) * 4 + r);
+          }
+      // Then the float64 decisions: each lane hands its lowest deferred
+      // value to one call per round (values picked and written back by
+      // compile-time index), so a wave makes as many calls as its lane with
+      // the most deferred values has (usually one), not one per position.
+      while (__ballot(defer != 0u) != 0ull) {
+        const int sel = defer != 0u ? __builtin_ctz(defer) : -1;
+        float ga = 0.0f, ua = 0.0f;
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (sel == (i * TM + j) * 4 + r) {
+                ga = acc[i][j][r];
+                ua = acc[i + 4][j][r];
+              }
+        uint32_t hr = 0;
+        if (defer != 0u)
+          hr = silu_mul_bf16_f64(__uint_as_float(bf16_rne(ga) << 16), __uint_as_float(bf16_rne(ua) << 16));
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (sel == (i * TM + j) * 4 + r) hb[i][j][r] = hr;
+        defer &= defer - 1u;
+      }
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
         mx[j] = 0;
@@ -965,11 +1011,7 @@ struct Panel {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float gv = __uint_as_float(bf16_rne(acc[i][j][r]) << 16);
-            const float uv = __uint_as_float(bf16_rne(acc[i + 4][j][r]) << 16);
-            const uint32_t h = silu_mul_bf16(gv, uv);
-            hb[i][j][r] = h;
-            const uint32_t ah = h & 0x7fffu;
+            const uint32_t ah = hb[i][j][r] & 0x7fffu;
             mx[j] = mx[j] > ah ? mx[j] : ah;
           }
         mx[j] = max(mx[j], (uint32_t)__shfl_xor((int)mx[j], 16));

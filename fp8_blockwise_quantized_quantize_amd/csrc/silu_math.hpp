@@ -67,6 +67,34 @@ __device__ __noinline__ uint32_t silu_mul_bf16_f64(float g, float u) {
   return __float_as_uint(static_cast<float>(v)) >> 16;  // exact conversion
 }
 
+// silu_mul_bf16's float32 path without a branch, for a caller that takes
+// the float64 decisions of many values together (the fused fc1 epilogue):
+// the path's result, and in *ok whether it is final (false:
+// silu_mul_bf16_f64(g, u) is the result).  The exponential is taken of g
+// clamped to [-80, 80]; outside that range, and for a NaN g, *ok is false.
+// The same arithmetic as silu_mul_bf16 below, written out twice on
+// purpose: the compiler schedules each caller's kernel best from its own
+// form (one shared helper measured 4% slower on the SiLU*up quantizer and
+// 5% slower on the fused fc1).
+__device__ __forceinline__ uint32_t silu_mul_bf16_fast(float g, float u, bool* ok) {
+  constexpr float kLog2e = 1.44269502162933349609375f;      // fl32(log2 e)
+  constexpr float kLog2eLo = 1.925963033500011079e-8f;      // log2 e - kLog2e
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float gc = fminf(fmaxf(g, -80.0f), 80.0f);
+  const float xh = -gc * kLog2e;
+  const float xl = fmaf(-gc, kLog2e, -xh) + (-gc) * kLog2eLo;
+  const float p = __builtin_amdgcn_exp2f(xh);
+  const float t = fmaf(p, xl * kLn2, p);
+  const float h = (g * __builtin_amdgcn_rcpf(1.0f + t)) * u;
+  const uint32_t b = __float_as_uint(h);
+  const float ah = fabsf(h);
+  const uint32_t low = b & 0xffffu;
+  const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;
+  const bool zero = h == 0.0f;
+  *ok = fabsf(g) <= 80.0f && (zero || (ah >= 0x1p-100f && ah <= 0x1p120f && dist > 48u));
+  return zero ? b >> 16 : (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
   if (fabsf(g) <= 80.0f) {
     constexpr float kLog2e = 1.44269502162933349609375f;      // fl32(log2 e)
