@@ -299,6 +299,54 @@ def test_fused_fc1_silu_ragged_and_empty_experts_and_missing_rows(H):
     _fused_case(T, k, E, H, F, seed=12, ids=ids, rows=rows)
 
 
+def test_fused_fc1_silu_many_float64_decisions_per_lane():
+    """fc1 outputs built so that most SiLU*up values sit exactly on a BF16
+    midpoint (|gate| < 2^-20, where SiLU(g) u ~ g u / 2 and g u / 2 has nine
+    significant bits): the epilogue's float32 path leaves them open, so each
+    lane takes many of its 32 values through the float64 decision, one per
+    round.  One K-block, one nonzero code per row, so every fc1 output is an
+    exact product; the codes and scales must equal the oracle's and the two
+    separate kernels', bit for bit."""
+    T, k, E, F, K = 300, 1, 2, 128, 128
+    announce("fused fc1 SiLU quant, float64 decisions", T, E, F)
+    rng = np.random.default_rng(41)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    tok_codes = np.array([0x38, 0x30, 0x40, 0xB8, 0xC8], np.uint8)  # 1, 0.5, 2, -1, -4
+    a = np.zeros((T, K), np.uint8)
+    a[:, 0] = tok_codes[np.arange(T) % tok_codes.size]
+    a_s = np.ones((T, 1), np.float32)
+    w = np.zeros((E, 2 * F, K), np.uint8)
+    n = np.arange(F)
+    # gate rows: powers of two (midpoint products) except every third row (1.375)
+    w[:, :F, 0] = np.where(n % 3 == 0, 0x3B, np.array([0x38, 0x30, 0xC0, 0x40])[n % 4])
+    w[:, F:, 0] = np.array([0x38, 0xB8, 0x40, 0x30])[n % 4]  # up rows: 1, -1, 2, 0.5
+    w_s = np.zeros((E, 2, 1), np.float32)
+    w_s[0, :, 0] = [129 * 2.0 ** -37, 1.5]
+    w_s[1, :, 0] = [-129 * 2.0 ** -40, 0.75]
+    off, sp, _ = fb().moe_sort_by_expert(dev(ids), E)
+    h, hs = fb().grouped_gemm_w8a8_blockscaled_gather_silu(dev(a), dev(a_s), sp, k, dev(w), dev(w_s), off)
+    y1 = fb().grouped_gemm_w8a8_blockscaled_gather(dev(a), dev(a_s), sp, k, dev(w), dev(w_s), off)
+    h_sep, hs_sep = fb().silu_mul_quantize_act(y1)
+    # the exact fc1 outputs, in the sorted row order: token sp[m] // k, expert of row m
+    offs, rows = host(off).astype(np.int64), host(sp).astype(np.int64)
+    expert = np.searchsorted(offs, np.arange(T * k), side="right") - 1
+    tok = rows // k
+    e4 = {0x38: 1.0, 0x30: 0.5, 0x40: 2.0, 0xB8: -1.0, 0xC8: -4.0, 0x3B: 1.375, 0xC0: -2.0}
+    av = np.vectorize(e4.get)(a[tok, 0]).astype(np.float64)
+    wv = np.vectorize(e4.get)(w[expert, :, 0]).astype(np.float64)
+    scale = np.repeat(w_s[expert, :, 0].astype(np.float64), F, axis=1)
+    y = bf16((av[:, None] * wv * scale).astype(np.float32))  # exact in float32
+    g = bf16_bits_to_f64(y[:, :F])
+    u = bf16_bits_to_f64(y[:, F:])
+    half = np.abs(g * u / 2)
+    m9 = half / 2.0 ** (np.floor(np.log2(half)) - 8)
+    ties = np.mean((m9 == np.round(m9)) & (np.round(m9) % 2 == 1))
+    assert ties > 0.5, ties  # most values sit exactly on a midpoint
+    rq, rs = silu_mul_quantize(y, F)
+    assert np.array_equal(host(h), rq) and np.array_equal(host(hs), rs)
+    assert torch.equal(h, h_sep) and torch.equal(hs.view(torch.int32), hs_sep.view(torch.int32))
+
+
 def test_fused_fc1_silu_shape_errors():
     a = torch.zeros((4, 128), dtype=torch.uint8, device=DEV)
     a_s = torch.ones((4, 1), device=DEV)
