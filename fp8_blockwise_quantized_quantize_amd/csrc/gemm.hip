@@ -465,7 +465,9 @@ struct Skinny {
 // Phase k: wait for this wave's loads of K-block k; barrier (everyone's
 // data has landed, and everyone is done with the stage read in phase k-1);
 // compute k while issuing the loads of K-block k + S - 1 into that stage
-// between the MFMAs.
+// between the MFMAs.  Two-stage panels instead have waves 0-3 issue all
+// of those loads as one burst right after the barrier, and waves 4-7 only
+// compute (split loading, in run_impl).
 // ---------------------------------------------------------------------------
 // kWfrag: the weight codes are in MFMA fragment order.
 // kSilu (persistent grouped tiles only): the fc1 form.  The weights are
@@ -617,6 +619,53 @@ struct Panel {
       for (int q = 0; q < kLoads; ++q) dma_q(q, kb, lds + stage * kStage);
       dma_scales(kb, stage);
     };
+    // Split loading (the two-stage panels): the waves of a SIMD do not
+    // progress together.  The first-dispatched wave of each SIMD (waves 0-3)
+    // takes the MFMA pipe first and finishes its phase ~30% sooner, then
+    // waits at the barrier while the second one (waves 4-7) finishes alone.
+    // So waves 0-3 issue all of a K-block's loads, as one burst right after
+    // the barrier (operand rows 8 (kLoaders q + w) .., the activation scales
+    // of their 64-row slots, and one of them the weight scales), and waves
+    // 4-7 only compute: prefill 4.6-5.3% faster, the same bits.
+    constexpr int kLoaders = 4;
+    constexpr bool kSplit = !kGather && S == 2 && kRows % (8 * kLoaders) == 0 && BN % (8 * kLoaders) == 0 &&
+                            BM / 64 <= kLoaders;
+    constexpr int kLoadsL = kRows / (8 * kLoaders);  // operand loads per loading wave and K-block
+    const bool loader = wave < kLoaders;
+    constexpr int kWScaleWave = BM / 64 < kLoaders ? BM / 64 : 0;  // the loader that fetches the weight scales
+    const auto scr_w = make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
+    auto dma_q_split = [&](int q, int kb, uint8_t* buf) {
+      const int koff = (kb0 + kb) * kBlock;
+      const int r0 = 8 * (kLoaders * q + wave);
+      auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
+      if (q < BN / (8 * kLoaders) && kWfrag)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, (r0 >> 4) * 16 * (int)K + (r0 & 8) * 128 + lane * 16,
+                                                 (kb0 + kb) * 16 * kBlock, 0, 0);
+      else if (q < BN / (8 * kLoaders))
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, dvoff + r0 * (int)K, koff, 0, 0);
+      else if (kAfrag)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16,
+                                                 ((r0 - BN) >> 4) * 16 * (int)K + ((r0 - BN) & 8) * 128 + lane * 16,
+                                                 (kb0 + kb) * 16 * kBlock, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, dvoff + (r0 - BN) * (int)K, koff, 0, 0);
+    };
+    auto dma_scales_split = [&](int kb, int stage) {
+      uint8_t* area = lds + S * kStage + stage * kScaleBytes;
+      if (wave < BM / 64)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, (__attribute__((address_space(3))) void*)(area + wave * 256), 4,
+                                                 scvoff, (kb0 + kb) * 4, 0, 0);
+      if (wave == kWScaleWave)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(scr_w, (__attribute__((address_space(3))) void*)(area + (BM / 64) * 256),
+                                                 4, lane * KB * 4, (kb0 + kb) * 4, 0, 0);
+    };
+    auto dma_kblock_split = [&](int kb, int stage) {
+      if (loader) {
+#pragma unroll
+        for (int q = 0; q < kLoadsL; ++q) dma_q_split(q, kb, lds + stage * kStage);
+        dma_scales_split(kb, stage);
+      }
+    };
     constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
     auto load_w = [&](const uint8_t* buf, int i) -> v8i {
       if constexpr (kWfrag) {  // the 2 KB unit of weight rows wn WNR + 16 i
@@ -673,13 +722,17 @@ struct Panel {
           acc, fa, fw, [&](int i) { return load_w(buf, i); },
           [&](int i, int j) { return (kOneScaleBlock || !((hi_mask >> i) & 1u)) ? c0[j] : c1[j]; },
           [&](int tt) {
-            if (tt % kEvery != 0 || tt / kEvery >= kPhaseLoads) return false;
-            const int q = tt / kEvery;
-            if (q < kLoads)
-              dma_q(q, kb, lds + fill * kStage);
-            else
-              dma_scales(kb, fill);
-            return true;
+            if constexpr (kSplit) {
+              return false;
+            } else {
+              if (tt % kEvery != 0 || tt / kEvery >= kPhaseLoads) return false;
+              const int q = tt / kEvery;
+              if (q < kLoads)
+                dma_q(q, kb, lds + fill * kStage);
+              else
+                dma_scales(kb, fill);
+              return true;
+            }
           });
     };
     // The compiler does not track LDS writes by buffer_load ... lds: wait
@@ -709,7 +762,12 @@ struct Panel {
     auto nxt = [&](int kb) { return kb < NKB ? kb : kb_last; };  // clamped prefetch
     if (NKB > 0) {
 #pragma unroll
-      for (int st = 0; st < S - 1; ++st) dma_kblock(nxt(st), st);
+      for (int st = 0; st < S - 1; ++st) {
+        if constexpr (kSplit)
+          dma_kblock_split(nxt(st), st);
+        else
+          dma_kblock(nxt(st), st);
+      }
     }
     // Loads past the last K-block re-load it into a stage nobody reads
     // again, keeping the loop body free of branches.
@@ -718,10 +776,16 @@ struct Panel {
       wait_stage();
       barrier();  // stage cur holds K-block k; stage cur - 1 is free
       const int fill = (cur == 0) ? S - 1 : cur - 1;
-      if (idle) {  // no valid activation row: only this wave's share of the loads
-        dma_kblock(nxt(k + S - 1), fill);
+      if constexpr (kSplit) {
+        dma_kblock_split(nxt(k + S - 1), fill);  // waves 0..kLoaders-1 only
+        order_fence();
+        if (!idle) phase(cur, nxt(k + S - 1), fill);
       } else {
-        phase(cur, nxt(k + S - 1), fill);
+        if (idle) {  // no valid activation row: only this wave's share of the loads
+          dma_kblock(nxt(k + S - 1), fill);
+        } else {
+          phase(cur, nxt(k + S - 1), fill);
+        }
       }
       order_fence();
       cur = (cur + 1 == S) ? 0 : cur + 1;
