@@ -477,7 +477,8 @@ struct Skinny {
 // values of the same 64 columns in the same lanes (fragments i and i + 4),
 // and the epilogue stores h as E4M3 codes in 1x128 groups (the group amax
 // crosses the two waves of a row through LDS).
-template <int BN_, int BM_, int WGN, int WGM, int S, bool kWfrag = false, bool kSilu = false>
+// kSplit3: split loading (below, in run_impl) for a three-stage tile too.
+template <int BN_, int BM_, int WGN, int WGM, int S, bool kWfrag = false, bool kSilu = false, bool kSplit3 = false>
 struct Panel {
   static constexpr int BN = BN_, BM = BM_;
   static constexpr bool kSiluForm = kSilu;
@@ -557,14 +558,23 @@ struct Panel {
     // the activation scales of tile rows 64 w + lane, the others the
     // weight scale blocks nbt + lane.  As for the operands, rows and blocks
     // past the end sit outside the buffer range and read zeros.
-    const bool act_scales = wave < BM / 64;
+    constexpr int kLoaders = 4;
+    constexpr bool kSplit = !kGather && (S == 2 || kSplit3) && kRows % (8 * kLoaders) == 0 &&
+                            BN % (8 * kLoaders) == 0 && BM / 64 <= kLoaders;
+    // Split loading: waves 0-3 issue the loads, or waves 4-7 in a tile whose
+    // last row of waves has no valid activation row (a ragged last tile),
+    // so that the waves that skip the MFMAs are the ones that load.
+    const bool swap = kSplit && t.m_lo + (WGM - 1) * WMR >= t.m_hi;
+    const bool loader = swap ? wave >= kLoaders : wave < kLoaders;
+    const int slot = kSplit ? (wave & (kLoaders - 1)) : wave;  // a loading wave's rows and scale slot
+    const bool act_scales = slot < BM / 64;
     const auto scr = act_scales ? (kGather ? make_rsrc(t.sa, t.a_nrows * KB * 4)
                                            : make_rsrc(t.sa + t.m_lo * KB, (t.m_hi - t.m_lo) * KB * 4))
                                 : make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
     int scvoff = lane * KB * 4;
     if (act_scales) {
-      const int64_t r = src_row(t.m_lo + 64 * wave + lane);
-      scvoff = kGather ? (r >= 0 ? (int)(r * KB * 4) : kOob) : (64 * wave + lane) * KB * 4;
+      const int64_t r = src_row(t.m_lo + 64 * slot + lane);
+      scvoff = kGather ? (r >= 0 ? (int)(r * KB * 4) : kOob) : (64 * slot + lane) * KB * 4;
     }
 
     // DMA staging: load q of wave w fills stage rows R0..R0+7 with
@@ -619,24 +629,24 @@ struct Panel {
       for (int q = 0; q < kLoads; ++q) dma_q(q, kb, lds + stage * kStage);
       dma_scales(kb, stage);
     };
-    // Split loading (the two-stage panels): the waves of a SIMD do not
-    // progress together.  The first-dispatched wave of each SIMD (waves 0-3)
-    // takes the MFMA pipe first and finishes its phase ~30% sooner, then
-    // waits at the barrier while the second one (waves 4-7) finishes alone.
-    // So waves 0-3 issue all of a K-block's loads, as one burst right after
-    // the barrier (operand rows 8 (kLoaders q + w) .., the activation scales
-    // of their 64-row slots, and one of them the weight scales), and waves
-    // 4-7 only compute: prefill 4.6-5.3% faster, the same bits.
-    constexpr int kLoaders = 4;
-    constexpr bool kSplit = !kGather && S == 2 && kRows % (8 * kLoaders) == 0 && BN % (8 * kLoaders) == 0 &&
-                            BM / 64 <= kLoaders;
+    // Split loading (the two-stage panels, and kSplit3 tiles): the waves of
+    // a SIMD do not progress together.  The first-dispatched wave of each
+    // SIMD (waves 0-3) takes the MFMA pipe first and finishes its phase ~30%
+    // sooner, then waits at the barrier while the second one (waves 4-7)
+    // finishes alone.  So waves 0-3 issue all of a K-block's loads, as one
+    // burst right after the barrier (operand rows 8 (kLoaders q + w) .., the
+    // activation scales of their 64-row slots, and one of them the weight
+    // scales), and waves 4-7 only compute: prefill 4.6-5.3% faster, the same
+    // bits.  With three stages the 192 x 128 decode panel gains 4-8%
+    // (M = 192, 256); the 128 x 256 one gains only where waves 4-7 have no
+    // rows (M <= 128: they load, waves 0-3 compute) and loses 5-9% at
+    // M = 176-208, K = 2048, so it runs split only there.
     constexpr int kLoadsL = kRows / (8 * kLoaders);  // operand loads per loading wave and K-block
-    const bool loader = wave < kLoaders;
     constexpr int kWScaleWave = BM / 64 < kLoaders ? BM / 64 : 0;  // the loader that fetches the weight scales
     const auto scr_w = make_rsrc(t.sw + nbt * KB, (NBm1 - nbt + 1) * KB * 4);
     auto dma_q_split = [&](int q, int kb, uint8_t* buf) {
       const int koff = (kb0 + kb) * kBlock;
-      const int r0 = 8 * (kLoaders * q + wave);
+      const int r0 = 8 * (kLoaders * q + slot);
       auto* dst = (__attribute__((address_space(3))) void*)(buf + r0 * kBlock);
       if (q < BN / (8 * kLoaders) && kWfrag)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, (r0 >> 4) * 16 * (int)K + (r0 & 8) * 128 + lane * 16,
@@ -652,18 +662,32 @@ struct Panel {
     };
     auto dma_scales_split = [&](int kb, int stage) {
       uint8_t* area = lds + S * kStage + stage * kScaleBytes;
-      if (wave < BM / 64)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, (__attribute__((address_space(3))) void*)(area + wave * 256), 4,
+      if (slot < BM / 64)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, (__attribute__((address_space(3))) void*)(area + slot * 256), 4,
                                                  scvoff, (kb0 + kb) * 4, 0, 0);
-      if (wave == kWScaleWave)
+      if (slot == kWScaleWave)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(scr_w, (__attribute__((address_space(3))) void*)(area + (BM / 64) * 256),
                                                  4, lane * KB * 4, (kb0 + kb) * 4, 0, 0);
+    };
+    // three stages: every loading wave issues two scale loads (its own slot:
+    // activation scales below BM / 64, weight scales above; and a copy of
+    // the weight scales into slot 4 + w), so all have kLoadsL + 2 loads per
+    // K-block and one vmcnt immediate fits them
+    auto dma_scales_split3 = [&](int kb, int stage) {
+      uint8_t* area = lds + S * kStage + stage * kScaleBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, (__attribute__((address_space(3))) void*)(area + slot * 256), 4,
+                                               scvoff, (kb0 + kb) * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr_w, (__attribute__((address_space(3))) void*)(area + (kLoaders + slot) * 256),
+                                               4, lane * KB * 4, (kb0 + kb) * 4, 0, 0);
     };
     auto dma_kblock_split = [&](int kb, int stage) {
       if (loader) {
 #pragma unroll
         for (int q = 0; q < kLoadsL; ++q) dma_q_split(q, kb, lds + stage * kStage);
-        dma_scales_split(kb, stage);
+        if constexpr (S == 2)
+          dma_scales_split(kb, stage);
+        else
+          dma_scales_split3(kb, stage);
       }
     };
     constexpr int kAhead = 2;  // weight fragments are read two row groups ahead
@@ -740,10 +764,16 @@ struct Panel {
     // three stages the loads of the next K-block may stay in flight.
     auto wait_stage = [&]() {
       // the loads of K-block k + 1 have (S - 2) * kPhaseLoads loads issued after them
-      if constexpr (S == 2)
+      if constexpr (S == 2) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      else
+      } else if constexpr (kSplit) {
+        if (loader)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * (kLoadsL + 2)) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kPhaseLoads) : "memory");
+      }
     };
     // The workgroup barrier of a phase.  Not __syncthreads(): its fence
     // would wait for every load in flight (vmcnt(0)), including the later
@@ -1240,6 +1270,11 @@ struct PanelFragA {
 
 using Wide = Panel<256, 256, 2, 4, 2>;
 using DecodePanel = Panel<128, 256, 2, 4, 3>;
+// The decode panel at M <= 128 (one tile of rows, waves 4-7 without rows):
+// split loading, waves 4-7 load and waves 0-3 compute (Qwen3-8B gate_up
+// shape N = 24576, K = 4096 at M = 128: 36.8 -> 35.7 us).
+template <bool kW = false>
+using DecodePanelSplit = Panel<128, 256, 2, 4, 3, kW, false, true>;
 // Three stages of 256 weight rows: two K-blocks of weights (64 KB) in flight
 // per workgroup instead of the wide tile's one, for weights streamed from
 // HBM once (MoE experts, whose weights no other tile reads).
@@ -1247,7 +1282,7 @@ using Deep = Panel<256, 128, 2, 4, 3>;
 // Decode with exactly one round of tiles: at M = 256 and N = 24576 the
 // 192 x 128 panel gives 256 tiles (one per CU), where the 128 x 256 panel
 // leaves 64 CUs idle (48.4 vs 52.6 us on the Qwen3-8B gate_up at M = 256).
-using Panel192 = Panel<192, 128, 2, 4, 3>;
+using Panel192 = Panel<192, 128, 2, 4, 3, false, false, true>;
 
 // ---------------------------------------------------------------------------
 // Tile order: XCD-aware remap of the workgroup id, then groups of kGroupM
@@ -1690,6 +1725,8 @@ hipError_t launch_gemm(const uint8_t* a, const float* sa, const uint8_t* w, cons
     case Cfg::kSkinny96x64:
       return launch_dense_cfg<Skinny<96, 64, 4>, 96, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kDecodePanel:
+      if (2 * M <= DecodePanel::BM)
+        return launch_dense_cfg<DecodePanelSplit<>, DecodePanel::BN, DecodePanel::BM>(a, sa, w, sw, y, M, N, K, stream);
       return launch_dense_cfg<DecodePanel, DecodePanel::BN, DecodePanel::BM>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kPanel192:
       return launch_dense_cfg<Panel192, Panel192::BN, Panel192::BM>(a, sa, w, sw, y, M, N, K, stream);
@@ -1825,8 +1862,11 @@ hipError_t launch_gemm_frag_cfg(Cfg cfg, const uint8_t* a, const float* sa, cons
     case Cfg::kSkinny96x64:
       return launch_dense_cfg<Skinny<96, 64, 4, true, kW>, 96, 64>(a, sa, w, sw, y, M, N, K, stream);
     case Cfg::kPanel192:
-      return launch_dense_cfg<PanelFragA<Panel<192, 128, 2, 4, 3, kW>>, 192, 128>(a, sa, w, sw, y, M, N, K, stream);
+      return launch_dense_cfg<PanelFragA<Panel<192, 128, 2, 4, 3, kW, false, true>>, 192, 128>(a, sa, w, sw, y, M, N,
+                                                                                               K, stream);
     case Cfg::kDecodePanel:
+      if (2 * M <= DecodePanel::BM)
+        return launch_dense_cfg<PanelFragA<DecodePanelSplit<kW>>, 128, 256>(a, sa, w, sw, y, M, N, K, stream);
       return launch_dense_cfg<PanelFragA<Panel<128, 256, 2, 4, 3, kW>>, 128, 256>(a, sa, w, sw, y, M, N, K, stream);
     default:
       return launch_dense_cfg<PanelFragA<Panel<256, 256, 2, 4, 2, kW>>, 256, 256>(a, sa, w, sw, y, M, N, K, stream);
