@@ -140,7 +140,8 @@ __device__ __forceinline__ void order_fence() {
 // short delay suffices: the other wave fills the gap).  sched_group_barrier pins the
 // interleave (one MFMA, then the four FMAs of an older one).
 // fw[0 .. kAhead-1] hold the first weight fragments on entry; the rest are
-// loaded kAhead row groups ahead of their use.
+// loaded kAhead row groups ahead of their use (pinned there for kAhead >= 2:
+// prefill 2.4-3.6% faster, MoE fc2 2% faster).
 struct NoExtra {
   __device__ __forceinline__ bool operator()(int) const { return false; }
 };
@@ -156,7 +157,13 @@ __device__ __forceinline__ void tile_product(v4f (&acc)[TN][TM], const v8i (&fa)
   for (int t = 0; t < T + kDelay; ++t) {
     if (t < T) {
       const int i = t / TM, j = t % TM;
-      if (j == 0 && i + kAhead < TN) fw[(i + kAhead) % (kAhead + 1)] = load_w(i + kAhead);
+      if (j == 0 && i + kAhead < TN) {
+        fw[(i + kAhead) % (kAhead + 1)] = load_w(i + kAhead);
+        // Keep the read here, kAhead row groups ahead of its MFMAs: left free,
+        // the scheduler sinks it to just before its first use and waits on it
+        // there (one fragment register set instead of kAhead + 1).
+        if constexpr (kAhead >= 2) __builtin_amdgcn_sched_barrier(0);
+      }
       ring[t % (kDelay + 1)] = mfma_e4m3(fw[i % (kAhead + 1)], fa[j]);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       if (extra(t)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // a VMEM read
