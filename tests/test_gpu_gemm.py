@@ -84,6 +84,27 @@ def test_gemm_every_tile_kernel(fb, tile, m, n, k):
     assert_gemm_close(gpu_gemm(fb, qa, sa, qw, sw, tile), oracle.gemm_ref(qa, sa, qw, sw))
 
 
+PANEL_TILES = ["wide", "decode_panel", "deep", "panel192"]
+
+
+@pytest.mark.parametrize("m", [100, 128, 150, 200, 257])
+def test_gemm_panel_tiles_same_bits(fb, m):
+    """The panel tiles accumulate every output over the K-blocks in K order
+    with the same per-K-block scale FMA, so they give the same bits whatever
+    their shape, their number of stages, and which waves issue the loads.
+    The row counts put ragged last tiles with empty rows of waves, whose
+    waves 4-7 take the loads, into each panel: 100 and 128 rows (the 128 x
+    256 panel's split form; the 256-row panels' last row of waves empty),
+    150 (the 256 x 256 tile with one row of waves empty), 200 and 257 (the
+    192 x 128 panel's last tile of 72 or 1 rows), beside full tiles."""
+    announce("gemm panel tiles same bits", m)
+    qa, sa, qw, sw = _oracle_inputs(m, 520, 1024, 60 + m)
+    ys = {tile: gpu_gemm(fb, qa, sa, qw, sw, tile) for tile in PANEL_TILES}
+    assert_gemm_close(ys["wide"], oracle.gemm_ref(qa, sa, qw, sw))
+    for tile in PANEL_TILES[1:]:
+        assert np.array_equal(ys[tile], ys["wide"]), tile
+
+
 @pytest.mark.parametrize("tile", TILES)
 def test_gemm_every_tile_random_scales(fb, tile):
     """Each tile kernel with a different scale in every weight block,
